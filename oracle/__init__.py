@@ -1,0 +1,175 @@
+"""Python front end of the double-precision CPU oracle (oracle/liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg. The product library never imports it, and it
+imports nothing from the product library.
+
+All functions take numpy arrays in the stored input dtypes (float32, or bf16
+as uint16 bit patterns) and return float64 results computed by the plain
+definitions in oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16, F64 = 0, 1, 2
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    P, I64, I32, D, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float
+    DP = ctypes.POINTER(ctypes.c_double)
+    sig = {
+        "oracle_threads": ([], I32),
+        "oracle_set_threads": ([I32], None),
+        "oracle_round_bf16": ([D], ctypes.c_uint16),
+        "oracle_round_bf16_array": ([P, P, I64], None),
+        "oracle_decode": ([P, I32, P, I64], None),
+        "oracle_softmax": ([P, I32, I64, I64, P], None),
+        "oracle_layernorm": ([P, P, P, I32, I64, I64, F, P, P, P], None),
+        "oracle_add_rmsnorm": ([P, P, P, I32, I64, I64, F, P, P, P], None),
+        "oracle_softmax_xent": ([P, I32, P, I64, I64, P, P, P], None),
+        "oracle_online_softmax_stats": ([P, I64, DP, DP], None),
+        "oracle_softmax_stats_merge": ([D, D, D, D, DP, DP], None),
+        "oracle_welford": ([P, I64, DP, DP, DP], None),
+        "oracle_chan_merge": ([D, D, D, D, D, D, DP, DP, DP], None),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle input must be float32, bf16 bits (uint16) or float64, got {a.dtype}")
+
+
+def _c(a, dtype=None):
+    return np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def round_bf16(v) -> np.ndarray:
+    """double -> bf16 bits, round to nearest even, directly from double."""
+    a = _c(np.asarray(v, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_round_bf16_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def round_bf16_scalar(v: float) -> int:
+    return int(_load().oracle_round_bf16(float(v)))
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    """Stored input (float32 or bf16 bits) -> exact float64."""
+    a = _c(a)
+    out = np.empty(a.shape, dtype=np.float64)
+    _load().oracle_decode(_ptr(a), _dtype_code(a), _ptr(out), a.size)
+    return out
+
+
+def softmax(x: np.ndarray) -> np.ndarray:
+    x = _c(x)
+    R, C = x.shape
+    p = np.empty((R, C), dtype=np.float64)
+    _load().oracle_softmax(_ptr(x), _dtype_code(x), R, C, _ptr(p))
+    return p
+
+
+def layernorm(x, gamma, beta, eps: float):
+    x, gamma, beta = _c(x), _c(gamma), _c(beta)
+    if not (x.dtype == gamma.dtype == beta.dtype):
+        raise TypeError("x, gamma and beta share one dtype")
+    R, C = x.shape
+    y = np.empty((R, C), dtype=np.float64)
+    mean = np.empty(R, dtype=np.float64)
+    rstd = np.empty(R, dtype=np.float64)
+    _load().oracle_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _dtype_code(x), R, C,
+                             float(eps), _ptr(y), _ptr(mean), _ptr(rstd))
+    return y, mean, rstd
+
+
+def add_rmsnorm(x, residual, weight, eps: float):
+    """Returns (y, h, rstd) in float64; h = x + residual exactly."""
+    x, residual, weight = _c(x), _c(residual), _c(weight)
+    if not (x.dtype == residual.dtype == weight.dtype):
+        raise TypeError("x, residual and weight share one dtype")
+    R, C = x.shape
+    y = np.empty((R, C), dtype=np.float64)
+    h = np.empty((R, C), dtype=np.float64)
+    rstd = np.empty(R, dtype=np.float64)
+    _load().oracle_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(weight), _dtype_code(x), R, C,
+                               float(eps), _ptr(y), _ptr(h), _ptr(rstd))
+    return y, h, rstd
+
+
+def softmax_xent(logits, labels):
+    """Returns (loss[R], grad[R, C], argmax[R]) in float64 / int32."""
+    logits = _c(logits)
+    labels = _c(labels, np.int32)
+    R, C = logits.shape
+    loss = np.empty(R, dtype=np.float64)
+    grad = np.empty((R, C), dtype=np.float64)
+    am = np.empty(R, dtype=np.int32)
+    _load().oracle_softmax_xent(_ptr(logits), _dtype_code(logits), _ptr(labels), R, C,
+                                _ptr(loss), _ptr(grad), _ptr(am))
+    return loss, grad, am
+
+
+def online_softmax_stats(x: np.ndarray):
+    x = _c(x, np.float64)
+    m, d = ctypes.c_double(), ctypes.c_double()
+    _load().oracle_online_softmax_stats(_ptr(x), x.size, ctypes.byref(m), ctypes.byref(d))
+    return m.value, d.value
+
+
+def softmax_stats_merge(a, b):
+    m, d = ctypes.c_double(), ctypes.c_double()
+    _load().oracle_softmax_stats_merge(a[0], a[1], b[0], b[1], ctypes.byref(m), ctypes.byref(d))
+    return m.value, d.value
+
+
+def welford(x: np.ndarray):
+    x = _c(x, np.float64)
+    n, mu, m2 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _load().oracle_welford(_ptr(x), x.size, ctypes.byref(n), ctypes.byref(mu), ctypes.byref(m2))
+    return n.value, mu.value, m2.value
+
+
+def chan_merge(a, b):
+    n, mu, m2 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _load().oracle_chan_merge(a[0], a[1], a[2], b[0], b[1], b[2],
+                              ctypes.byref(n), ctypes.byref(mu), ctypes.byref(m2))
+    return n.value, mu.value, m2.value

@@ -1,0 +1,271 @@
+"""Python binding of libfusedrow (fused single-pass row kernels for MI355X).
+
+Argument marshalling only: every step of every operation runs in the HIP
+kernels behind the C ABI declared in include/fusedrow.h. torch supplies the
+device memory (caller-visible tensors) and the current stream; nothing here
+computes on tensor values. There is no fallback: if libfusedrow.so is missing
+or a call fails, an exception is raised.
+
+The fr_* functions mirror the C entry points one to one and take torch CUDA
+tensors; softmax / layernorm / add_rmsnorm / softmax_xent allocate the outputs
+and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "F32", "BF16", "FR_MAX_COLS", "FusedRowError", "lib", "status_str", "version",
+    "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
+    "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
+    "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
+    "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
+]
+
+F32, BF16 = 0, 1
+OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
+FR_MAX_COLS = 65536
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfusedrow.so")
+
+
+class FusedRowError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+            "python memory_bound_row_pass_amd/_build.py (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    IP = ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "fr_softmax_fwd": [P, P, I64, I64, I32, I32, P],
+        "fr_layernorm_fwd": [P, P, P, P, P, P, I64, I64, F, I32, P],
+        "fr_add_rmsnorm_fwd": [P, P, P, P, P, I64, I64, F, I32, P],
+        "fr_softmax_xent_fwd_bwd": [P, P, P, P, P, I64, I64, I32, P],
+        "fr_stream_copy": [P, P, I64, P],
+        "fr_debug_force_variant": [I32, I32, I32],
+        "fr_debug_select_variant": [I32, I64, I32, I32, I32, IP, IP, IP],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.fr_status_str.argtypes = [ctypes.c_int]
+    L.fr_status_str.restype = ctypes.c_char_p
+    L.fr_version.argtypes = []
+    L.fr_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def status_str(s: int) -> str:
+    return lib.fr_status_str(int(s)).decode()
+
+
+def version() -> str:
+    return lib.fr_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise FusedRowError(status, where)
+
+
+# ------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch  # imported lazily: the ABI can be loaded without torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; fusedrow takes float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rows_cols(t):
+    if t.dim() != 2:
+        raise ValueError(f"expected a 2-D [rows, cols] tensor, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError("row buffers must be contiguous (row-major)")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _stream(stream, t):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    torch = _torch()
+    if t is not None and t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("fusedrow operates on device (CUDA/HIP) tensors only")
+
+
+def _check_vec(t, cols, name):
+    if t.dim() != 1 or int(t.shape[0]) != cols or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [cols] vector")
+
+
+def _check_rows(t, rows, name, dtype):
+    if t.dim() != 1 or int(t.shape[0]) != rows or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name} must be a contiguous [rows] {dtype} vector")
+
+
+# ------------------------------------------------------- C entry points
+
+def fr_softmax_fwd(x, y, stream=None) -> None:
+    """y = softmax(x) over each row (C: fr_softmax_fwd)."""
+    _need_cuda(x, y)
+    R, C = _rows_cols(x)
+    if tuple(y.shape) != (R, C) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tensor of x's shape")
+    _check(lib.fr_softmax_fwd(_ptr(x), _ptr(y), R, C, _dtype_code(x), _dtype_code(y),
+                              _stream(stream, x)), "fr_softmax_fwd")
+
+
+def fr_layernorm_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, stream=None) -> None:
+    """LayerNorm of each row (C: fr_layernorm_fwd); mean/rstd optional fp32 [rows]."""
+    torch = _torch()
+    _need_cuda(x, gamma, beta, y, mean, rstd)
+    R, C = _rows_cols(x)
+    _check_vec(gamma, C, "gamma")
+    _check_vec(beta, C, "beta")
+    if tuple(y.shape) != (R, C) or not y.is_contiguous() or y.dtype != x.dtype:
+        raise ValueError("y must be a contiguous tensor of x's shape and dtype")
+    if gamma.dtype != x.dtype or beta.dtype != x.dtype:
+        raise TypeError("gamma and beta must have x's dtype")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _check_rows(t, R, n, torch.float32)
+    _check(lib.fr_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd),
+                                R, C, float(eps), _dtype_code(x), _stream(stream, x)),
+           "fr_layernorm_fwd")
+
+
+def fr_add_rmsnorm_fwd(x, residual, weight, y, residual_out=None, eps: float = 1e-6,
+                       stream=None) -> None:
+    """h = x + residual; residual_out = h; y = RMSNorm(h) * weight (C: fr_add_rmsnorm_fwd)."""
+    _need_cuda(x, residual, weight, y, residual_out)
+    R, C = _rows_cols(x)
+    for t, n in ((residual, "residual"), (y, "y"), (residual_out, "residual_out")):
+        if t is not None and (tuple(t.shape) != (R, C) or not t.is_contiguous() or t.dtype != x.dtype):
+            raise ValueError(f"{n} must be a contiguous tensor of x's shape and dtype")
+    _check_vec(weight, C, "weight")
+    if weight.dtype != x.dtype:
+        raise TypeError("weight must have x's dtype")
+    _check(lib.fr_add_rmsnorm_fwd(_ptr(x), _ptr(residual), _ptr(weight), _ptr(y), _ptr(residual_out),
+                                  R, C, float(eps), _dtype_code(x), _stream(stream, x)),
+           "fr_add_rmsnorm_fwd")
+
+
+def fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, argmax=None, stream=None) -> None:
+    """Per-row cross-entropy loss and its gradient (C: fr_softmax_xent_fwd_bwd)."""
+    torch = _torch()
+    _need_cuda(logits, labels, loss, grad, argmax)
+    R, C = _rows_cols(logits)
+    _check_rows(labels, R, "labels", torch.int32)
+    _check_rows(loss, R, "loss", torch.float32)
+    if argmax is not None:
+        _check_rows(argmax, R, "argmax", torch.int32)
+    if tuple(grad.shape) != (R, C) or not grad.is_contiguous() or grad.dtype != logits.dtype:
+        raise ValueError("grad must be a contiguous tensor of logits' shape and dtype")
+    _check(lib.fr_softmax_xent_fwd_bwd(_ptr(logits), _ptr(labels), _ptr(loss), _ptr(grad),
+                                       _ptr(argmax), R, C, _dtype_code(logits),
+                                       _stream(stream, logits)),
+           "fr_softmax_xent_fwd_bwd")
+
+
+def fr_stream_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
+    """Plain device copy of nbytes (default: all of src) — bandwidth reference."""
+    _need_cuda(src, dst)
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > dst.numel() * dst.element_size() or n > src.numel() * src.element_size():
+        raise ValueError("copy larger than a buffer")
+    _check(lib.fr_stream_copy(_ptr(src), _ptr(dst), n, _stream(stream, src)), "fr_stream_copy")
+
+
+def fr_debug_force_variant(op: int, threads: int = 0, vecs: int = 0) -> None:
+    _check(lib.fr_debug_force_variant(int(op), int(threads), int(vecs)), "fr_debug_force_variant")
+
+
+def fr_debug_select_variant(op: int, cols: int, in_dtype: int = F32, out_dtype: int | None = None,
+                            vector_path: bool = True):
+    t, v, e = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    od = in_dtype if out_dtype is None else out_dtype
+    _check(lib.fr_debug_select_variant(int(op), int(cols), int(in_dtype), int(od), int(vector_path),
+                                       ctypes.byref(t), ctypes.byref(v), ctypes.byref(e)),
+           "fr_debug_select_variant")
+    return t.value, v.value, e.value
+
+
+class forced_variant:
+    """Context manager: force (threads, vecs) for op, restore automatic selection after."""
+
+    def __init__(self, op: int, threads: int, vecs: int):
+        self.op, self.threads, self.vecs = op, threads, vecs
+
+    def __enter__(self):
+        fr_debug_force_variant(self.op, self.threads, self.vecs)
+        return self
+
+    def __exit__(self, *exc):
+        fr_debug_force_variant(self.op, 0, 0)
+        return False
+
+
+# ------------------------------------------------- allocating conveniences
+
+def softmax(x, out_dtype=None, out=None):
+    torch = _torch()
+    y = out if out is not None else torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    fr_softmax_fwd(x, y)
+    return y
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-5):
+    torch = _torch()
+    R = x.shape[0]
+    y = torch.empty_like(x)
+    mean = torch.empty(R, dtype=torch.float32, device=x.device)
+    rstd = torch.empty(R, dtype=torch.float32, device=x.device)
+    fr_layernorm_fwd(x, gamma, beta, y, mean, rstd, eps)
+    return y, mean, rstd
+
+
+def add_rmsnorm(x, residual, weight, eps: float = 1e-6, inplace: bool = False):
+    torch = _torch()
+    y = torch.empty_like(x)
+    res_out = residual if inplace else torch.empty_like(residual)
+    fr_add_rmsnorm_fwd(x, residual, weight, y, res_out, eps)
+    return y, res_out
+
+
+def softmax_xent(logits, labels, return_argmax: bool = False):
+    torch = _torch()
+    R = logits.shape[0]
+    loss = torch.empty(R, dtype=torch.float32, device=logits.device)
+    grad = torch.empty_like(logits)
+    am = torch.empty(R, dtype=torch.int32, device=logits.device) if return_argmax else None
+    fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, am)
+    return (loss, grad, am) if return_argmax else (loss, grad)

@@ -1,0 +1,279 @@
+// C-ABI front end of libfusedrow: argument validation (before any HIP call),
+// aliasing and alignment rules, kernel-variant selection and launch.
+// The contract of each entry point is documented in include/fusedrow.h.
+#include "fusedrow.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "fr_kernels.hpp"
+
+namespace {
+
+using fr::VariantSpan;
+
+// ------------------------------------------------------------ forced variant
+struct Forced {
+  std::atomic<int> threads{0};
+  std::atomic<int> vecs{0};
+};
+Forced g_forced[4];
+
+// ------------------------------------------------------------------- buffers
+struct Buf {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool row_data = false;     // [rows, cols] buffer (may be aliased in place)
+  int esize = 0;
+  bool output = false;
+  bool present = false;
+};
+
+Buf make_buf(const void* p, int64_t bytes, bool row_data, int esize, bool output) {
+  Buf b;
+  if (!p) return b;
+  b.present = true;
+  b.lo = reinterpret_cast<uintptr_t>(p);
+  b.hi = b.lo + static_cast<uintptr_t>(bytes);
+  b.row_data = row_data;
+  b.esize = esize;
+  b.output = output;
+  return b;
+}
+
+// Outputs may not overlap anything, except that an output row buffer may be
+// exactly the same range as an input row buffer of the same element size.
+fr_status_t check_alias(const Buf* bufs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!bufs[i].present) continue;
+    for (int j = i + 1; j < n; ++j) {
+      if (!bufs[j].present) continue;
+      const Buf& a = bufs[i];
+      const Buf& b = bufs[j];
+      if (!a.output && !b.output) continue;
+      const bool overlap = a.lo < b.hi && b.lo < a.hi;
+      if (!overlap) continue;
+      const bool in_place = a.output != b.output && a.row_data && b.row_data && a.lo == b.lo &&
+                            a.hi == b.hi && a.esize == b.esize;
+      if (!in_place) return FR_E_ALIAS;
+    }
+  }
+  return FR_OK;
+}
+
+bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int esize(fr_dtype_t d) { return d == FR_BF16 ? 2 : 4; }
+bool dtype_ok(fr_dtype_t d) { return d == FR_F32 || d == FR_BF16; }
+
+// rows >= 0, 1 <= cols <= FR_MAX_COLS, rows*cols*8 fits in int64.
+fr_status_t check_shape(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 1 || cols > FR_MAX_COLS) return FR_E_SHAPE;
+  if (rows > INT64_MAX / 8 / cols) return FR_E_SHAPE;
+  return FR_OK;
+}
+
+// Pick the first variant of `sp` on the requested path (epv == vector width,
+// or 1 for the scalar path) whose lanes can hold `cols` elements; honour a
+// forced (threads, vecs) pair when one is set for `op`.
+template <typename V>
+const V* select_variant(VariantSpan<V> sp, int op, int64_t cols, int epv) {
+  const int ft = g_forced[op].threads.load(std::memory_order_relaxed);
+  const int fv = g_forced[op].vecs.load(std::memory_order_relaxed);
+  for (size_t i = 0; i < sp.n; ++i) {
+    const V& v = sp.v[i];
+    if (v.epv != epv) continue;
+    if (ft && (v.threads != ft || v.nv != fv)) continue;
+    if ((int64_t)v.threads * v.nv * v.epv >= cols) return &v;
+    if (ft) return nullptr;
+  }
+  return nullptr;
+}
+
+fr_status_t launch_status(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_LAUNCH; }
+
+int vec_epv(int esz) { return 16 / esz; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fr_status_str(fr_status_t s) {
+  switch (s) {
+    case FR_OK: return "FR_OK";
+    case FR_E_NULL: return "FR_E_NULL: a required pointer is NULL";
+    case FR_E_SHAPE: return "FR_E_SHAPE: rows/cols out of range";
+    case FR_E_DTYPE: return "FR_E_DTYPE: unsupported dtype combination";
+    case FR_E_ALIAS: return "FR_E_ALIAS: an output overlaps another buffer";
+    case FR_E_LAUNCH: return "FR_E_LAUNCH: kernel launch failed";
+    case FR_E_ALIGN: return "FR_E_ALIGN: pointer not aligned to its element size";
+    case FR_E_VALUE: return "FR_E_VALUE: invalid scalar argument";
+    case FR_E_VARIANT: return "FR_E_VARIANT: forced kernel variant unavailable for this row";
+  }
+  return "unknown fr_status_t";
+}
+
+const char* fr_version(void) { return "fusedrow 0.1.0 (gfx950)"; }
+
+fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs) {
+  if (op < FR_OP_SOFTMAX || op > FR_OP_XENT) return FR_E_VALUE;
+  if (threads < 0 || vecs < 0) return FR_E_VALUE;
+  g_forced[op].vecs.store(threads ? vecs : 0);
+  g_forced[op].threads.store(threads);
+  return FR_OK;
+}
+
+fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtype,
+                                    fr_dtype_t out_dtype, int vector_path, int* threads, int* vecs,
+                                    int* elems_per_vec) {
+  if (!threads || !vecs || !elems_per_vec) return FR_E_NULL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return FR_E_DTYPE;
+  if (cols < 1 || cols > FR_MAX_COLS) return FR_E_SHAPE;
+  const int epv = vector_path ? vec_epv(esize(in_dtype)) : 1;
+  int t = 0, n = 0, e = 0;
+  switch (op) {
+    case FR_OP_SOFTMAX: {
+      auto v = select_variant(fr::softmax_variants(in_dtype == FR_BF16, out_dtype == FR_BF16), op,
+                              cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_LAYERNORM: {
+      auto v = select_variant(fr::layernorm_variants(in_dtype == FR_BF16), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_RMSNORM: {
+      auto v = select_variant(fr::rmsnorm_variants(in_dtype == FR_BF16), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_XENT: {
+      auto v = select_variant(fr::xent_variants(in_dtype == FR_BF16, 0), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    default: return FR_E_VALUE;
+  }
+  if (!t) return FR_E_VARIANT;
+  *threads = t; *vecs = n; *elems_per_vec = e;
+  return FR_OK;
+}
+
+fr_status_t fr_softmax_fwd(const void* x, void* y, int64_t rows, int64_t cols, fr_dtype_t x_dtype,
+                           fr_dtype_t y_dtype, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return FR_E_DTYPE;
+  if (rows == 0) return FR_OK;
+  if (!x || !y) return FR_E_NULL;
+  const int xs = esize(x_dtype), ys = esize(y_dtype);
+  if (!aligned(x, xs) || !aligned(y, ys)) return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(x, rows * cols * xs, true, xs, false),
+                      make_buf(y, rows * cols * ys, true, ys, true)};
+  if (fr_status_t s = check_alias(bufs, 2)) return s;
+
+  // 128-bit path: same-width rows sharing their address phase (per-row
+  // head/tail split), or mixed widths with every row 16-byte aligned.
+  const int ve = vec_epv(xs);
+  bool vec;
+  if (xs == ys) vec = (reinterpret_cast<uintptr_t>(x) % 16) == (reinterpret_cast<uintptr_t>(y) % 16);
+  else vec = aligned(x, 16) && aligned(y, 16) && cols % ve == 0;
+  auto sp = fr::softmax_variants(x_dtype == FR_BF16, y_dtype == FR_BF16);
+  const fr::SoftmaxVariant* v = select_variant(sp, FR_OP_SOFTMAX, cols, vec ? ve : 1);
+  if (!v) return g_forced[FR_OP_SOFTMAX].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  return launch_status(v->launch(x, y, rows, (int)cols, static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y,
+                             float* mean, float* rstd, int64_t rows, int64_t cols, float eps,
+                             fr_dtype_t dtype, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  if (rows == 0) return FR_OK;
+  if (!x || !gamma || !beta || !y) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, es) || !aligned(beta, es) ||
+      (mean && !aligned(mean, 4)) || (rstd && !aligned(rstd, 4)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(x, rows * cols * es, true, es, false),
+                      make_buf(gamma, cols * es, false, es, false),
+                      make_buf(beta, cols * es, false, es, false),
+                      make_buf(y, rows * cols * es, true, es, true),
+                      make_buf(mean, rows * 4, false, 4, true),
+                      make_buf(rstd, rows * 4, false, 4, true)};
+  if (fr_status_t s = check_alias(bufs, 6)) return s;
+  const bool vec = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16) &&
+                   (cols * es) % 16 == 0;
+  const fr::LayerNormVariant* v =
+      select_variant(fr::layernorm_variants(dtype == FR_BF16), FR_OP_LAYERNORM, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_LAYERNORM].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  return launch_status(v->launch(x, gamma, beta, y, mean, rstd, rows, (int)cols, eps,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_add_rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* y,
+                               void* residual_out, int64_t rows, int64_t cols, float eps,
+                               fr_dtype_t dtype, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  if (rows == 0) return FR_OK;
+  if (!x || !residual || !weight || !y) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(x, es) || !aligned(residual, es) || !aligned(weight, es) || !aligned(y, es) ||
+      (residual_out && !aligned(residual_out, es)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(x, rows * cols * es, true, es, false),
+                      make_buf(residual, rows * cols * es, true, es, false),
+                      make_buf(weight, cols * es, false, es, false),
+                      make_buf(y, rows * cols * es, true, es, true),
+                      make_buf(residual_out, rows * cols * es, true, es, true)};
+  if (fr_status_t s = check_alias(bufs, 5)) return s;
+  const bool vec = aligned(x, 16) && aligned(residual, 16) && aligned(weight, 16) &&
+                   aligned(y, 16) && (!residual_out || aligned(residual_out, 16)) &&
+                   (cols * es) % 16 == 0;
+  const fr::RmsNormVariant* v =
+      select_variant(fr::rmsnorm_variants(dtype == FR_BF16), FR_OP_RMSNORM, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_RMSNORM].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  return launch_status(v->launch(x, residual, weight, y, residual_out, rows, (int)cols, eps,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* labels, float* loss,
+                                    void* grad, int32_t* argmax, int64_t rows, int64_t cols,
+                                    fr_dtype_t dtype, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (dtype != FR_F32) return FR_E_DTYPE;
+  if (rows == 0) return FR_OK;
+  if (!logits || !labels || !loss || !grad) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(logits, es) || !aligned(grad, es) || !aligned(labels, 4) || !aligned(loss, 4) ||
+      (argmax && !aligned(argmax, 4)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(logits, rows * cols * es, true, es, false),
+                      make_buf(labels, rows * 4, false, 4, false),
+                      make_buf(loss, rows * 4, false, 4, true),
+                      make_buf(grad, rows * cols * es, true, es, true),
+                      make_buf(argmax, rows * 4, false, 4, true)};
+  if (fr_status_t s = check_alias(bufs, 5)) return s;
+  const bool vec =
+      (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
+  const fr::XentVariant* v = select_variant(fr::xent_variants(0, argmax != nullptr), FR_OP_XENT, cols,
+                                            vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  return launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0) return FR_E_SHAPE;
+  if (bytes == 0) return FR_OK;
+  if (!src || !dst) return FR_E_NULL;
+  const Buf bufs[] = {make_buf(src, bytes, false, 1, false), make_buf(dst, bytes, false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 2)) return s;
+  return launch_status(fr::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,450 @@
+// Device building blocks shared by the fused row kernels (gfx950 / CDNA4).
+//
+// Row ownership: one wavefront (64 lanes) or one workgroup owns a whole row,
+// so every reduction stays inside the owner and no cross-row exchange exists
+// ("ML Compiler Lab", Own a complete row tile; Check the graph before
+// selecting a schedule: cross-row reductions are rejected). Each lane keeps
+// its share of the row in VGPRs from the load to the store.
+//
+// Memory access: 128-bit loads/stores (global_load_dwordx4 /
+// global_store_dwordx4), consecutive lanes on consecutive 16-byte chunks
+// ("Engineering a CUDA Machine Learning Framework from Scratch", §2.3 128-Bit
+// Memory Vectorization and Register Warp Reductions). The in-wave reduction
+// uses DPP lane moves instead of shuffles through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fr {
+
+// bf16 storage (raw bits); arithmetic is always fp32.
+struct bf16_t {
+  uint16_t u;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+// log2(e), and ln(2) split in two so that t - y*ln2 is formed to ~2^-48.
+constexpr double kLog2eD = 1.4426950408889634073599;
+constexpr double kLn2D = 0.6931471805599453094172;
+constexpr float kLog2e = (float)kLog2eD;
+constexpr float kLn2 = (float)kLn2D;
+constexpr float kLn2Lo = (float)(kLn2D - (double)(float)kLn2D);
+
+// ---------------------------------------------------------------- bf16 <-> f32
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// ------------------------------------------------------------------ arithmetic
+
+// max of three, straight to v_max3_f32. Written as inline asm so that the
+// compiler does not quiet each loaded operand first (IEEE mode); a quiet NaN
+// operand is ignored here and reaches the result through the exponential sum.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// 2^y with the hardware v_exp_f32 (results below 2^-126 flush to zero).
+__device__ __forceinline__ float exp2_hw(float y) { return __builtin_amdgcn_exp2f(y); }
+
+// e^t for fp32 outputs: y = fl(t*log2e); rho = t - y*ln2 (two fmas, exact to
+// ~2^-48 relative); e^t = 2^y * e^rho ~= 2^y + 2^y*rho. Removes the rounding
+// of t*log2e from the result; what remains is v_exp_f32's own error.
+// t = -inf gives 0 (rho would be inf - inf; clamping it to -1 keeps 0 * rho
+// finite), t = NaN gives NaN (through 2^y).
+__device__ __forceinline__ float exp_acc(float t) {
+  float y = t * kLog2e;
+  float rho = __builtin_fmaf(-y, kLn2, t);
+  rho = __builtin_fmaf(-y, kLn2Lo, rho);
+  rho = __builtin_fmaxf(rho, -1.f);
+  float e = exp2_hw(y);
+  return __builtin_fmaf(e, rho, e);
+}
+
+// --------------------------------------------------------------- global access
+// Inputs are streamed once: non-temporal loads and stores keep them from
+// displacing other data in L2 / MALL.
+
+template <typename T, int EPV>
+struct Vec;  // load/store EPV consecutive elements as fp32
+
+template <>
+struct Vec<float, 4> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    f32x4 r = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+  }
+};
+
+template <>
+struct Vec<float, 8> {  // output side of bf16 -> f32 (two 16-byte stores)
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    Vec<float, 4>::load(p, v);
+    Vec<float, 4>::load(p + 4, v + 4);
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    Vec<float, 4>::store(p, v);
+    Vec<float, 4>::store(p + 4, v + 4);
+  }
+};
+
+template <>
+struct Vec<bf16_t, 8> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+    v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+    v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
+    v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    u32x4 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+  }
+};
+
+template <>
+struct Vec<bf16_t, 4> {  // output side of f32 -> bf16 (one 8-byte store)
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    u32x2 r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+    v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    u32x2 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+  }
+};
+
+template <>
+struct Vec<float, 1> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    v[0] = __builtin_nontemporal_load(p);
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    __builtin_nontemporal_store(v[0], p);
+  }
+};
+
+template <>
+struct Vec<bf16_t, 1> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    uint16_t u = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+    v[0] = __uint_as_float((uint32_t)u << 16);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    __builtin_nontemporal_store(to_bf16(v[0]), reinterpret_cast<uint16_t*>(p));
+  }
+};
+
+// Per-column parameters (gamma, beta, weight) are re-read by every row and
+// stay cache resident: ordinary loads.
+template <typename T, int EPV>
+__device__ __forceinline__ void load_param(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load_param<float, 4>(const float* p, float* v) {
+  f32x4 r = *reinterpret_cast<const f32x4*>(p);
+  v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+}
+template <>
+__device__ __forceinline__ void load_param<bf16_t, 8>(const bf16_t* p, float* v) {
+  u32x4 r = *reinterpret_cast<const u32x4*>(p);
+  v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+  v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+  v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
+  v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+}
+template <>
+__device__ __forceinline__ void load_param<float, 1>(const float* p, float* v) { v[0] = *p; }
+template <>
+__device__ __forceinline__ void load_param<bf16_t, 1>(const bf16_t* p, float* v) {
+  v[0] = __uint_as_float((uint32_t)p->u << 16);
+}
+
+// Single element of any storage type (head/tail slots, label logit).
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const bf16_t* p) { return __uint_as_float((uint32_t)p->u << 16); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store1(bf16_t* p, float v) { p->u = to_bf16(v); }
+
+// ----------------------------------------------------------------- row layout
+// A row of `cols` elements starting at `row_ptr` is cut into
+//   head: elements before the first 16-byte boundary (EPV > 1 only),
+//   body: nvec aligned chunks of EPV elements,
+//   tail: what is left (< EPV elements).
+// Lane t of a row-owner of T lanes holds body chunks t, t+T, t+2T, ...
+// (slot i -> chunk i*T + t) and at most one head/tail element in its extra
+// slot: lanes [0, head) take the head, lanes [head, head+tail) the tail.
+template <int EPV>
+struct RowGeom {
+  int head, nvec, tail;
+  template <typename T>
+  __device__ __forceinline__ RowGeom(const T* row_ptr, int cols) {
+    if constexpr (EPV == 1) {
+      head = 0; nvec = cols; tail = 0;
+    } else {
+      const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(row_ptr) / sizeof(T)) & (EPV - 1);
+      int h = (int)((EPV - mis) & (EPV - 1));
+      head = h < cols ? h : cols;
+      nvec = (cols - head) / EPV;
+      tail = cols - head - nvec * EPV;
+    }
+  }
+  // column of this lane's extra element, or -1
+  __device__ __forceinline__ int extra_col(int lane) const {
+    if (lane < head) return lane;
+    if (lane < head + tail) return head + nvec * EPV + (lane - head);
+    return -1;
+  }
+  __device__ __forceinline__ int chunk_col(int chunk) const { return head + chunk * EPV; }
+};
+
+// ------------------------------------------------------- row chunk load/store
+// `full` rows (every slot of every lane holds a chunk) use one per-lane base
+// address and compile-time slot offsets, with no masking. Ragged rows clamp
+// the chunk index into the row so every load stays in bounds, then overwrite
+// the slots past the row end with `fill`; their stores are masked.
+template <typename Ts, int T, int NV, int EPV>
+__device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV>& g, int tid, bool full,
+                                            float (&v)[NV][EPV], float fill) {
+  const Ts* base = row + g.head;                    // uniform
+  const uint32_t lo = (uint32_t)tid * EPV;          // lane offset, elements
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) Vec<Ts, EPV>::load((base + i * T * EPV) + lo, v[i]);
+  } else if (g.nvec > 0) {
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      uint32_t o = (uint32_t)(i * T * EPV) + lo;
+      o = o < last ? o : last;
+      Vec<Ts, EPV>::load(base + o, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ok = i * T + tid < g.nvec;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = ok ? v[i][k] : fill;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = fill;
+  }
+}
+
+template <typename Ts, int T, int NV, int EPV>
+__device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV>& g, int tid, bool full,
+                                             const float (&v)[NV][EPV]) {
+  Ts* base = row + g.head;
+  const uint32_t lo = (uint32_t)tid * EPV;
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) Vec<Ts, EPV>::store((base + i * T * EPV) + lo, v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i * T + tid < g.nvec) Vec<Ts, EPV>::store((base + i * T * EPV) + lo, v[i]);
+  }
+}
+
+// Per-column parameters of chunk slot i of this lane (aligned rows only,
+// where head == 0 and the columns match the parameter vector). Slots past
+// the row end read the last chunk (their results are not stored).
+template <typename Ts, int T, int EPV>
+__device__ __forceinline__ void load_param_slot(const Ts* par, const RowGeom<EPV>& g, int tid, bool full,
+                                                int i, float* w) {
+  uint32_t o = (uint32_t)(i * T * EPV) + (uint32_t)tid * EPV;
+  if (!full) {
+    if (g.nvec <= 0) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) w[k] = 0.f;
+      return;
+    }
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+    o = o < last ? o : last;
+  }
+  load_param<Ts, EPV>(par + g.head + o, w);
+}
+
+// ------------------------------------------------------- wavefront reduction
+// Reduce a state held by all 64 lanes to lane 63 with six DPP steps
+//   quad_perm [1,0,3,2], quad_perm [2,3,0,1]   -> 4-lane totals
+//   row_half_mirror, row_mirror                 -> 16-lane (row) totals
+//   row_bcast:15 (rows 1,3), row_bcast:31 (rows 2,3) -> wave total in lane 63
+// then broadcast it with v_readlane. Lanes outside a row_bcast row mask read
+// the identity. Only lane 63's value is used, so the result is the same on
+// every lane and bitwise reproducible.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float src, float identity) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, identity), __builtin_bit_cast(int, src), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float read_lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <typename S, typename Merge>
+__device__ __forceinline__ S wave_reduce(S v, Merge merge) {
+  v = merge(v, S::template move<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = merge(v, S::template move<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = merge(v, S::template move<0x141, 0xF>(v));  // row_half_mirror
+  v = merge(v, S::template move<0x140, 0xF>(v));  // row_mirror
+  v = merge(v, S::template move<0x142, 0xA>(v));  // row_bcast:15
+  v = merge(v, S::template move<0x143, 0xC>(v));  // row_bcast:31
+  return v.lane63();
+}
+
+// Sum state (RMSNorm).
+struct SumState {
+  float s;
+  template <int C, int M>
+  static __device__ __forceinline__ SumState move(const SumState& a) { return {dpp_move<C, M>(a.s, 0.f)}; }
+  __device__ __forceinline__ SumState lane63() const { return {read_lane63(s)}; }
+};
+struct SumMerge {
+  __device__ __forceinline__ SumState operator()(const SumState& a, const SumState& b) const {
+    return {a.s + b.s};
+  }
+};
+
+// Softmax state: running max m and the sum s of exponentials taken relative
+// to m ("Online FlashSoftmax" recurrence). Empty state (-inf, 0).
+struct MaxSumState {
+  float m, s;
+  template <int C, int M>
+  static __device__ __forceinline__ MaxSumState move(const MaxSumState& a) {
+    return {dpp_move<C, M>(a.m, kNegInf), dpp_move<C, M>(a.s, 0.f)};
+  }
+  __device__ __forceinline__ MaxSumState lane63() const { return {read_lane63(m), read_lane63(s)}; }
+};
+
+// (ma, sa) (+) (mb, sb) = (M, s_hi + s_lo * e^(lo - M)), M = max, lo = min.
+// The larger side is never rescaled; an empty side (or two empty sides)
+// contributes nothing. LOG2 selects base 2 (states kept in log2 units).
+template <bool LOG2>
+struct MaxSumMerge {
+  __device__ __forceinline__ MaxSumState operator()(const MaxSumState& a, const MaxSumState& b) const {
+    const bool a_hi = a.m >= b.m;
+    const float M = a_hi ? a.m : b.m;
+    const float lo = a_hi ? b.m : a.m;
+    const float s_hi = a_hi ? a.s : b.s;
+    const float s_lo = a_hi ? b.s : a.s;
+    float f;
+    if constexpr (LOG2) f = exp2_hw(lo - M);
+    else f = exp_acc(lo - M);
+    f = (lo == M) ? 1.f : f;  // equal maxima (including two empty states)
+    return {M, __builtin_fmaf(s_lo, f, s_hi)};
+  }
+};
+
+// Softmax state with the position of the maximum (cross-entropy argmax).
+// idx is a column index held as a float (exact below 2^24); empty state
+// (-inf, 0, +huge). Ties keep the smaller index.
+struct MaxSumIdxState {
+  float m, s, idx;
+  template <int C, int M>
+  static __device__ __forceinline__ MaxSumIdxState move(const MaxSumIdxState& a) {
+    return {dpp_move<C, M>(a.m, kNegInf), dpp_move<C, M>(a.s, 0.f), dpp_move<C, M>(a.idx, 3.0e38f)};
+  }
+  __device__ __forceinline__ MaxSumIdxState lane63() const {
+    return {read_lane63(m), read_lane63(s), read_lane63(idx)};
+  }
+};
+struct MaxSumIdxMerge {
+  __device__ __forceinline__ MaxSumIdxState operator()(const MaxSumIdxState& a,
+                                                       const MaxSumIdxState& b) const {
+    const MaxSumState r = MaxSumMerge<false>{}(MaxSumState{a.m, a.s}, MaxSumState{b.m, b.s});
+    const float lo_idx = a.idx < b.idx ? a.idx : b.idx;
+    const float idx = a.m > b.m ? a.idx : (b.m > a.m ? b.idx : lo_idx);
+    return {r.m, r.s, idx};
+  }
+};
+
+// Welford state: count n, mean mu, sum of squared deviations M2. Empty (0,0,0).
+struct WelfordState {
+  float n, mu, m2;
+  template <int C, int M>
+  static __device__ __forceinline__ WelfordState move(const WelfordState& a) {
+    return {dpp_move<C, M>(a.n, 0.f), dpp_move<C, M>(a.mu, 0.f), dpp_move<C, M>(a.m2, 0.f)};
+  }
+  __device__ __forceinline__ WelfordState lane63() const {
+    return {read_lane63(n), read_lane63(mu), read_lane63(m2)};
+  }
+};
+// Pairwise (Chan et al.) merge: n = na + nb, d = mub - mua,
+// mu = mua + d * nb/n, M2 = M2a + M2b + d^2 * na * nb/n.
+struct WelfordMerge {
+  __device__ __forceinline__ WelfordState operator()(const WelfordState& a, const WelfordState& b) const {
+    const float n = a.n + b.n;
+    const float wb = n > 0.f ? b.n / n : 0.f;
+    const float d = b.mu - a.mu;
+    return {n, __builtin_fmaf(d, wb, a.mu), a.m2 + b.m2 + d * d * (a.n * wb)};
+  }
+};
+
+// -------------------------------------------------------- cross-wave merge
+// Row-per-workgroup kernels: lane 0 of each wave puts the wave's state in
+// LDS, one barrier, then every lane merges the NW states in wave order, so
+// all waves see bitwise the same row state. `buf` alternates between two
+// slots across consecutive rows of a persistent loop, so a slot is never
+// rewritten while a slower wave may still read it.
+template <int NW, typename S, int NF>
+struct XWave {
+  float slot[2][NW][NF];
+};
+
+template <int NW, typename S, typename Merge>
+__device__ __forceinline__ S block_merge(S wave_state, float (*slot)[sizeof(S) / sizeof(float)],
+                                         int wave, int lane, Merge merge) {
+  constexpr int NF = sizeof(S) / sizeof(float);
+  if (lane == 0) {
+    const float* f = reinterpret_cast<const float*>(&wave_state);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) slot[wave][k] = f[k];
+  }
+  __syncthreads();
+  S acc;
+  {
+    float* f = reinterpret_cast<float*>(&acc);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) f[k] = slot[0][k];
+  }
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    S o;
+    float* f = reinterpret_cast<float*>(&o);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) f[k] = slot[w][k];
+    acc = merge(acc, o);
+  }
+  return acc;
+}
+
+}  // namespace fr

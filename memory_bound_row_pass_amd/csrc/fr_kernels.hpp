@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI front end (api.cpp) and the kernel
+// translation units: per-op variant tables of typed launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fr {
+
+// Largest grid used; row loops stride by the grid beyond it.
+constexpr int64_t kMaxGrid = int64_t(1) << 30;
+
+// A compiled kernel shape: `threads` lanes own one row, each holding `nv`
+// chunks of `epv` elements (epv == 1: scalar path).
+template <typename F>
+struct Variant {
+  int threads, nv, epv;
+  F launch;
+};
+
+template <typename V>
+struct VariantSpan {
+  const V* v;
+  size_t n;
+};
+
+typedef hipError_t (*SoftmaxLaunch)(const void* x, void* y, int64_t rows, int cols, hipStream_t s);
+typedef hipError_t (*LayerNormLaunch)(const void* x, const void* gamma, const void* beta, void* y,
+                                      float* mean, float* rstd, int64_t rows, int cols, float eps,
+                                      hipStream_t s);
+typedef hipError_t (*RmsNormLaunch)(const void* x, const void* res, const void* w, void* y,
+                                    void* res_out, int64_t rows, int cols, float eps, hipStream_t s);
+typedef hipError_t (*XentLaunch)(const void* logits, const int32_t* labels, float* loss, void* grad,
+                                 int32_t* argmax, int64_t rows, int cols, hipStream_t s);
+
+typedef Variant<SoftmaxLaunch> SoftmaxVariant;
+typedef Variant<LayerNormLaunch> LayerNormVariant;
+typedef Variant<RmsNormLaunch> RmsNormVariant;
+typedef Variant<XentLaunch> XentVariant;
+
+VariantSpan<SoftmaxVariant> softmax_variants(int in_bf16, int out_bf16);
+VariantSpan<LayerNormVariant> layernorm_variants(int bf16);
+VariantSpan<RmsNormVariant> rmsnorm_variants(int bf16);
+VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
+}  // namespace fr

@@ -1,0 +1,119 @@
+// Row softmax, one pass over memory ("Engineering a CUDA Machine Learning
+// Framework from Scratch", §3.1 Online FlashSoftmax).
+//
+// Template shape
+//   Tin/Tout  storage types (float or bf16_t); arithmetic is fp32
+//   T         lanes per row: 64 = one wavefront per row (several rows per
+//             workgroup, no barrier), 256/512/1024 = one workgroup per row
+//   NV        128-bit chunks (or scalars when EPV == 1) per lane
+//   EPV       elements per chunk: 16 / sizeof(Tin), or 1 for the scalar path
+// bf16 outputs keep the exponentials in registers (base-2, biased); fp32
+// outputs keep x and re-evaluate the compensated exponential at the store.
+#include "fr_kernels.hpp"
+#include "softmax_core.hpp"
+
+namespace fr {
+
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC))) void softmax_kernel(const Tin* x, Tout* y,
+                                                                     int64_t rows, int cols) {
+  constexpr int BLOCK = T == 64 ? 256 : T;
+  constexpr int RPB = BLOCK / T;  // rows per workgroup
+  constexpr int NW = T / 64;      // waves per row
+  constexpr bool kLog2 = sizeof(Tout) == 2;
+  using Merge = MaxSumMerge<kLog2>;
+  __shared__ float xw[2][NW][2];
+
+  // wave index made provably uniform, so per-row values live in SGPRs
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = T == 64 ? lane : (int)threadIdx.x;  // lane within the row owner
+  const int sub = T == 64 ? wib : 0;                   // row slot within the block
+  const int wave = T == 64 ? 0 : wib;                  // wave within the row owner
+  int it = 0;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
+       row += (int64_t)gridDim.x * RPB, ++it) {
+    const Tin* xr = x + row * cols;
+    Tout* yr = y + row * cols;
+    const RowGeom<EPV> g(xr, cols);
+
+    const bool full = g.nvec == T * NV;
+    float v[NV][EPV];
+    load_chunks<Tin, T, NV, EPV>(xr, g, tid, full, v, kNegInf);
+    const int ec = g.extra_col(tid);
+    float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
+
+    const float m = lane_max<NV, EPV>(v, xe);
+    MaxSumState st = kLog2 ? lane_exp_log2<NV, EPV>(v, xe, m) : lane_sum_nat<NV, EPV>(v, xe, m);
+    st = wave_reduce(st, Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
+
+    if constexpr (kLog2) {
+      const Log2Scale sc = log2_scale(m, st.m, st.s);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) v[i][k] = apply_scale(v[i][k], sc);
+      xe = apply_scale(xe, sc);
+    } else {
+      probs_nat<NV, EPV>(v, xe, st.m, st.s);
+    }
+
+    store_chunks<Tout, T, NV, EPV>(yr, g, tid, full, v);
+    if (ec >= 0) store1(yr + ec, xe);
+  }
+}
+
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC>
+static hipError_t launch_softmax(const void* x, void* y, int64_t rows, int cols, hipStream_t s) {
+  constexpr int BLOCK = T == 64 ? 256 : T;
+  constexpr int RPB = BLOCK / T;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
+  hipLaunchKernelGGL((softmax_kernel<Tin, Tout, T, NV, EPV, OCC>), dim3(grid), dim3(BLOCK), 0, s,
+                     static_cast<const Tin*>(x), static_cast<Tout*>(y), rows, cols);
+  return hipGetLastError();
+}
+
+// Variant tables, in order of preference (the first that holds the row wins).
+// OCC is the waves-per-SIMD target handed to the register allocator; the
+// last column group is the scalar path (misaligned or mixed-width rows).
+#define FR_SM(TI, TO, T, NV, EPV, OCC) {T, NV, EPV, &launch_softmax<TI, TO, T, NV, EPV, OCC>}
+#define FR_SM_SCALAR(TI, TO)                                              \
+  FR_SM(TI, TO, 64, 16, 1, 4), FR_SM(TI, TO, 256, 16, 1, 4),              \
+      FR_SM(TI, TO, 1024, 16, 1, 4), FR_SM(TI, TO, 1024, 64, 1, 4)
+
+static const SoftmaxVariant kSmF32F32[] = {
+    FR_SM(float, float, 64, 1, 4, 8),     FR_SM(float, float, 64, 2, 4, 8),
+    FR_SM(float, float, 64, 4, 4, 8),     FR_SM(float, float, 64, 8, 4, 6),
+    FR_SM(float, float, 64, 16, 4, 4),    FR_SM(float, float, 256, 8, 4, 6),
+    FR_SM(float, float, 512, 8, 4, 6),    FR_SM(float, float, 1024, 8, 4, 4),
+    FR_SM(float, float, 1024, 13, 4, 4),
+    FR_SM(float, float, 1024, 16, 4, 4),  FR_SM_SCALAR(float, float)};
+static const SoftmaxVariant kSmBf16Bf16[] = {
+    FR_SM(bf16_t, bf16_t, 64, 1, 8, 8),   FR_SM(bf16_t, bf16_t, 64, 2, 8, 8),
+    FR_SM(bf16_t, bf16_t, 64, 4, 8, 6),   FR_SM(bf16_t, bf16_t, 64, 8, 8, 4),
+    FR_SM(bf16_t, bf16_t, 256, 2, 8, 8),  FR_SM(bf16_t, bf16_t, 256, 4, 8, 6),
+    FR_SM(bf16_t, bf16_t, 512, 4, 8, 6),  FR_SM(bf16_t, bf16_t, 1024, 4, 8, 4),
+    FR_SM(bf16_t, bf16_t, 1024, 8, 8, 4), FR_SM_SCALAR(bf16_t, bf16_t)};
+static const SoftmaxVariant kSmF32Bf16[] = {
+    FR_SM(float, bf16_t, 64, 1, 4, 8),    FR_SM(float, bf16_t, 64, 2, 4, 8),
+    FR_SM(float, bf16_t, 64, 4, 4, 8),    FR_SM(float, bf16_t, 64, 8, 4, 6),
+    FR_SM(float, bf16_t, 64, 16, 4, 4),   FR_SM(float, bf16_t, 256, 8, 4, 6),
+    FR_SM(float, bf16_t, 512, 8, 4, 6),   FR_SM(float, bf16_t, 1024, 8, 4, 4),
+    FR_SM(float, bf16_t, 1024, 16, 4, 4), FR_SM_SCALAR(float, bf16_t)};
+static const SoftmaxVariant kSmBf16F32[] = {
+    FR_SM(bf16_t, float, 64, 1, 8, 8),    FR_SM(bf16_t, float, 64, 2, 8, 8),
+    FR_SM(bf16_t, float, 64, 4, 8, 6),    FR_SM(bf16_t, float, 64, 8, 8, 4),
+    FR_SM(bf16_t, float, 256, 4, 8, 6),   FR_SM(bf16_t, float, 512, 4, 8, 6),
+    FR_SM(bf16_t, float, 1024, 4, 8, 4),  FR_SM(bf16_t, float, 1024, 8, 8, 4),
+    FR_SM_SCALAR(bf16_t, float)};
+
+VariantSpan<SoftmaxVariant> softmax_variants(int in_bf16, int out_bf16) {
+  if (!in_bf16 && !out_bf16) return {kSmF32F32, sizeof(kSmF32F32) / sizeof(kSmF32F32[0])};
+  if (in_bf16 && out_bf16) return {kSmBf16Bf16, sizeof(kSmBf16Bf16) / sizeof(kSmBf16Bf16[0])};
+  if (!in_bf16) return {kSmF32Bf16, sizeof(kSmF32Bf16) / sizeof(kSmF32Bf16[0])};
+  return {kSmBf16F32, sizeof(kSmBf16F32) / sizeof(kSmBf16F32[0])};
+}
+
+}  // namespace fr

@@ -1,0 +1,177 @@
+// Softmax cross-entropy, forward and backward in one pass over memory
+// ("Engineering a CUDA Machine Learning Framework from Scratch", §2.1: loss
+// gradients fused into registers; "GPU Programming for Machine Learning",
+// Module 3: cross-entropy loss).
+//
+// Per row: the online-softmax state (M, S) of the logits (as in softmax.hip,
+// fp32 path), then
+//   loss    = M + ln S - x[label]
+//   grad_j  = exp(x_j - M) / S - [j == label]
+//   argmax  = smallest j with x_j == M (optional)
+// The label logit is taken from the registers of the lane that loaded it, by
+// the wavefront that owns that column only; the one-hot subtraction is done
+// by the same wavefront before the store. A label outside [0, cols) gives a
+// NaN loss and an unmodified softmax row.
+#include "fr_kernels.hpp"
+#include "softmax_core.hpp"
+
+namespace fr {
+
+// Where the label column sits in the register layout of the row owner.
+struct LabelPos {
+  bool valid;   // 0 <= label < cols
+  bool extra;   // held in the extra (head/tail) slot
+  int lane;     // owning lane within the row owner (0..T-1)
+  int slot;     // chunk slot (body) ...
+  int comp;     // ... and component
+};
+
+template <int T, int EPV>
+__device__ __forceinline__ LabelPos locate_label(int label, int cols, const RowGeom<EPV>& g) {
+  LabelPos p{false, false, 0, 0, 0};
+  if (label < 0 || label >= cols) return p;
+  p.valid = true;
+  const int body_end = g.head + g.nvec * EPV;
+  if (label < g.head) {
+    p.extra = true; p.lane = label;
+  } else if (label >= body_end) {
+    p.extra = true; p.lane = g.head + (label - body_end);
+  } else {
+    const int q = label - g.head;
+    const int c = q / EPV;
+    p.comp = q - c * EPV;
+    p.lane = c % T;
+    p.slot = c / T;
+  }
+  return p;
+}
+
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX>
+__global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, int32_t* argmax,
+                 int64_t rows, int cols) {
+  constexpr int BLOCK = T == 64 ? 256 : T;
+  constexpr int RPB = BLOCK / T;
+  constexpr int NW = T / 64;
+  using State = typename std::conditional<ARGMAX, MaxSumIdxState, MaxSumState>::type;
+  using Merge = typename std::conditional<ARGMAX, MaxSumIdxMerge, MaxSumMerge<false>>::type;
+  constexpr int NF = sizeof(State) / sizeof(float);
+  __shared__ float xw[2][NW][NF];
+
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = T == 64 ? lane : (int)threadIdx.x;
+  const int sub = T == 64 ? wib : 0;
+  const int wave = T == 64 ? 0 : wib;
+  int it = 0;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
+       row += (int64_t)gridDim.x * RPB, ++it) {
+    const Tin* xr = x + row * cols;
+    Tin* gr = grad + row * cols;
+    const RowGeom<EPV> g(xr, cols);
+    const bool full = g.nvec == T * NV;
+
+    float v[NV][EPV];
+    load_chunks<Tin, T, NV, EPV>(xr, g, tid, full, v, kNegInf);
+    const int ec = g.extra_col(tid);
+    float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
+
+    const int label = __builtin_amdgcn_readfirstlane(labels[row]);
+    const LabelPos lp = locate_label<T, EPV>(label, cols, g);
+    const bool owner_wave = lp.valid && (lp.lane >> 6) == wave;
+
+    // label logit, read out of the owner lane's registers
+    float x_label = 0.f;
+    if (owner_wave) {
+      float mine = xe;
+      if (!lp.extra) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int k = 0; k < EPV; ++k)
+            if (i == lp.slot && k == lp.comp) mine = v[i][k];
+      }
+      x_label = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine),
+                                                                     lp.lane & 63));
+    }
+
+    const float m = lane_max<NV, EPV>(v, xe);
+    State st;
+    {
+      const MaxSumState ms = lane_sum_nat<NV, EPV>(v, xe, m);
+      st.m = ms.m;
+      st.s = ms.s;
+    }
+    if constexpr (ARGMAX) {
+      // smallest column of this lane holding its maximum
+      float best = 3.0e38f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float col = (float)((uint32_t)g.head + (uint32_t)(i * T + tid) * EPV + k);
+          best = (v[i][k] == m && col < best) ? col : best;
+        }
+      if (ec >= 0 && xe == m && (float)ec < best) best = (float)ec;
+      st.idx = best;
+    }
+    st = wave_reduce(st, Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
+
+    probs_nat<NV, EPV>(v, xe, st.m, st.s);
+
+    if (owner_wave) {
+      const bool me = lane == (lp.lane & 63);
+      if (lp.extra) {
+        if (me) xe -= 1.f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int k = 0; k < EPV; ++k)
+            if (i == lp.slot && k == lp.comp && me) v[i][k] -= 1.f;
+      }
+      if (lane == 0) loss[row] = st.m + logf(st.s) - x_label;
+    } else if (!lp.valid && wave == 0 && lane == 0) {
+      loss[row] = __builtin_nanf("");
+    }
+    if constexpr (ARGMAX) {
+      if (wave == 0 && lane == 0) argmax[row] = (int32_t)st.idx;
+    }
+
+    store_chunks<Tin, T, NV, EPV>(gr, g, tid, full, v);
+    if (ec >= 0) store1(gr + ec, xe);
+  }
+}
+
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX>
+static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss, void* grad,
+                              int32_t* argmax, int64_t rows, int cols, hipStream_t s) {
+  constexpr int BLOCK = T == 64 ? 256 : T;
+  constexpr int RPB = BLOCK / T;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
+  hipLaunchKernelGGL((xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX>), dim3(grid), dim3(BLOCK), 0, s,
+                     static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax, rows,
+                     cols);
+  return hipGetLastError();
+}
+
+#define FR_XE(T, NV, EPV, OCC, AM) {T, NV, EPV, &launch_xent<float, T, NV, EPV, OCC, AM>}
+#define FR_XE_TABLE(AM)                                                                   \
+  {FR_XE(64, 1, 4, 8, AM),     FR_XE(64, 2, 4, 8, AM),     FR_XE(64, 4, 4, 8, AM),        \
+   FR_XE(64, 8, 4, 6, AM),     FR_XE(64, 16, 4, 4, AM),    FR_XE(256, 8, 4, 6, AM),       \
+   FR_XE(512, 8, 4, 6, AM),    FR_XE(1024, 8, 4, 4, AM),   FR_XE(1024, 13, 4, 4, AM),     \
+   FR_XE(1024, 16, 4, 4, AM),  FR_XE(64, 16, 1, 4, AM),    FR_XE(256, 16, 1, 4, AM),      \
+   FR_XE(1024, 16, 1, 4, AM),  FR_XE(1024, 64, 1, 4, AM)}
+
+static const XentVariant kXe[] = FR_XE_TABLE(false);
+static const XentVariant kXeArgmax[] = FR_XE_TABLE(true);
+
+VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax) {
+  if (bf16) return {nullptr, 0};
+  if (with_argmax) return {kXeArgmax, sizeof(kXeArgmax) / sizeof(kXeArgmax[0])};
+  return {kXe, sizeof(kXe) / sizeof(kXe[0])};
+}
+
+}  // namespace fr

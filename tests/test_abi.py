@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status codes
+before making any HIP call (so no call here launches anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_row_pass_amd as fr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fusedrow.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIAS, E_LAUNCH, E_ALIGN, E_VALUE, E_VARIANT = range(9)
+
+# fake, never dereferenced: every call below fails validation first
+A = 0x7F0000000000          # 16-byte aligned
+B = 0x7F0100000000
+P = ctypes.c_void_p
+
+
+def test_exports_every_declared_symbol():
+    names = re.findall(r"^FR_API [^;(]*?\b(fr_\w+)\s*\(", open(HEADER).read(), re.M)
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(fr.lib, n), n
+    out = os.popen(f"nm -D --defined-only {fr.LIB_PATH}").read()
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    assert set(names) == exported, (set(names) ^ exported)
+
+
+def test_status_strings_and_version():
+    for s in range(9):
+        assert fr.status_str(s).startswith("FR_")
+    assert "unknown" in fr.status_str(99)
+    assert "gfx950" in fr.version()
+
+
+def sm(x, y, rows, cols, xd=0, yd=0):
+    return fr.lib.fr_softmax_fwd(P(x), P(y), rows, cols, xd, yd, None)
+
+
+def test_softmax_validation():
+    assert sm(A, B, 0, 10) == OK                 # no-op, nothing launched
+    assert sm(0, 0, 0, 10) == OK                 # NULL allowed when rows == 0
+    assert sm(A, B, -1, 10) == E_SHAPE
+    assert sm(A, B, 4, 0) == E_SHAPE
+    assert sm(A, B, 4, fr.FR_MAX_COLS + 1) == E_SHAPE
+    assert sm(A, B, 2**62, 2**10) == E_SHAPE     # size overflow
+    assert sm(A, B, 4, 10, 2, 0) == E_DTYPE
+    assert sm(A, B, 4, 10, 0, 7) == E_DTYPE
+    assert sm(0, B, 4, 10) == E_NULL
+    assert sm(A, 0, 4, 10) == E_NULL
+    assert sm(A + 2, B, 4, 10) == E_ALIGN        # fp32 needs 4-byte alignment
+    assert sm(A, B + 1, 4, 10, 0, 1) == E_ALIGN  # bf16 needs 2-byte alignment
+    # partial overlap is rejected, exact in-place is not an alias error
+    assert sm(A, A + 4, 4, 10) == E_ALIAS
+    assert sm(A, A + 40 * 4 - 4, 4, 10) == E_ALIAS
+    # same base, different element size: rows would overlap
+    assert sm(A, A, 4, 10, 0, 1) == E_ALIAS
+
+
+def test_layernorm_validation():
+    f = fr.lib.fr_layernorm_fwd
+    G, Bt, M, R = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
+    assert f(P(A), P(G), P(Bt), P(B), P(M), P(R), 0, 8, 1e-5, 0, None) == OK
+    assert f(P(A), P(G), P(Bt), P(B), P(M), P(R), 4, 8, -1.0, 0, None) == E_VALUE
+    assert f(P(A), P(G), P(Bt), P(B), P(M), P(R), 4, 8, float("nan"), 0, None) == E_VALUE
+    assert f(P(A), P(G), P(Bt), P(B), P(M), P(R), 4, 8, float("inf"), 0, None) == E_VALUE
+    assert f(P(A), None, P(Bt), P(B), P(M), P(R), 4, 8, 1e-5, 0, None) == E_NULL
+    assert f(P(A), P(G), P(Bt), P(B), P(M), P(R), 4, 8, 1e-5, 3, None) == E_DTYPE
+    assert f(P(A), P(G), P(Bt), P(B), P(M + 2), P(R), 4, 8, 1e-5, 0, None) == E_ALIGN
+    # an output over a per-column parameter, or two outputs overlapping
+    assert f(P(A), P(G), P(Bt), P(G), P(M), P(R), 1, 8, 1e-5, 0, None) == E_ALIAS
+    assert f(P(A), P(G), P(Bt), P(B), P(M), P(M + 4), 4, 8, 1e-5, 0, None) == E_ALIAS
+    assert f(P(A), P(G), P(Bt), P(B), P(A), P(R), 4, 8, 1e-5, 0, None) == E_ALIAS
+
+
+def test_add_rmsnorm_validation():
+    f = fr.lib.fr_add_rmsnorm_fwd
+    Rz, W, Y, RO = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
+    assert f(P(A), P(Rz), P(W), P(Y), P(RO), 0, 8, 1e-6, 1, None) == OK
+    assert f(P(A), None, P(W), P(Y), P(RO), 4, 8, 1e-6, 1, None) == E_NULL
+    assert f(P(A), P(Rz), P(W), P(Y), P(RO), 4, 8, -1e-6, 1, None) == E_VALUE
+    assert f(P(A), P(Rz), P(W), P(Y), P(Y), 4, 8, 1e-6, 1, None) == E_ALIAS      # two outputs
+    assert f(P(A), P(Rz), P(W), P(Y), P(Rz + 2), 4, 8, 1e-6, 1, None) == E_ALIAS  # partial
+    assert f(P(A), P(Rz), P(W), P(Y), P(A + 1), 4, 8, 1e-6, 1, None) == E_ALIGN
+
+
+def test_xent_validation():
+    f = fr.lib.fr_softmax_xent_fwd_bwd
+    L, LS, G, AM = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
+    assert f(P(A), P(L), P(LS), P(G), P(AM), 0, 8, 0, None) == OK
+    assert f(P(A), P(L), P(LS), P(G), P(AM), 4, 8, 1, None) == E_DTYPE   # bf16 logits: not built
+    assert f(P(A), None, P(LS), P(G), None, 4, 8, 0, None) == E_NULL
+    assert f(P(A), P(L), P(LS), P(G), P(LS), 4, 8, 0, None) == E_ALIAS   # argmax over loss
+    assert f(P(A), P(L), P(L), P(G), None, 4, 8, 0, None) == E_ALIAS     # loss over labels
+    assert f(P(A), P(L), P(LS), P(A + 4), None, 4, 8, 0, None) == E_ALIAS
+
+
+def test_stream_copy_validation():
+    f = fr.lib.fr_stream_copy
+    assert f(P(A), P(B), 0, None) == OK
+    assert f(P(A), P(B), -1, None) == E_SHAPE
+    assert f(None, P(B), 16, None) == E_NULL
+    assert f(P(A), P(A + 8), 16, None) == E_ALIAS
+
+
+def test_variant_selection():
+    # one wavefront per row for short rows, a workgroup per row for long ones
+    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (64, 4, 4)
+    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 4096, fr.BF16) == (64, 8, 8)
+    t, v, e = fr.fr_debug_select_variant(fr.OP_XENT, 50257, fr.F32)
+    assert t * v * e >= 50257 and t >= 256
+    t, v, e = fr.fr_debug_select_variant(fr.OP_SOFTMAX, 50257, fr.F32, vector_path=False)
+    assert e == 1 and t * v >= 50257
+    for op in (fr.OP_SOFTMAX, fr.OP_LAYERNORM, fr.OP_RMSNORM, fr.OP_XENT):
+        for c in (1, 2, 3, 64, 1000, 4096, 8192, 50257, fr.FR_MAX_COLS):
+            for vp in (True, False):
+                t, v, e = fr.fr_debug_select_variant(op, c, fr.F32, vector_path=vp)
+                assert t * v * e >= c
+    with fr.forced_variant(fr.OP_SOFTMAX, 1024, 16):
+        assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (1024, 16, 4)
+    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (64, 4, 4)
+    with fr.forced_variant(fr.OP_SOFTMAX, 64, 1):
+        with pytest.raises(fr.FusedRowError) as ei:
+            fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32)
+        assert ei.value.status == E_VARIANT
+    with pytest.raises(fr.FusedRowError):
+        fr.fr_debug_force_variant(9, 64, 1)
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(2, 3)
+    with pytest.raises(ValueError):
+        fr.fr_softmax_fwd(x, torch.zeros(2, 3))

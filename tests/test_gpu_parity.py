@@ -1,0 +1,507 @@
+"""GPU parity: every fused row kernel against the double-precision oracle,
+through the C ABI, on seeded inputs.
+
+Outputs are pre-filled with NaN (an element the kernel fails to write fails
+the comparison) and surrounded by guard bands holding a fixed bit pattern
+(an out-of-bounds write changes them) — the poisoned-output and memory checks
+of "ML Compiler Lab" (Failures the checks caught).
+
+Covered: the five standard workloads at full size (all rows), edge widths
+from 1 to the maximum, every compiled kernel variant, misaligned rows (head /
+body / tail split and the scalar path), in-place calls, special values,
+labels out of range, bitwise determinism and a non-default stream.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_pass_amd as fr
+import oracle
+import workloads
+from parity import FLT_MIN, bf16_bits, check_bf16, check_f32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+GUARD = 1024                      # elements of guard band on each side
+CANARY16 = 0x5A5A
+TDT = {0: torch.float32, 1: torch.bfloat16}
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    oracle.set_threads(min(16, oracle.threads()))
+
+
+# ------------------------------------------------------------- buffers
+
+class Guarded:
+    """A NaN-filled device tensor of `shape` inside canary guard bands,
+    optionally starting `offset` elements past a 256-byte boundary."""
+
+    def __init__(self, shape, dtype, offset=0):
+        n = int(np.prod(shape))
+        self.dtype, self.shape, self.n, self.off = dtype, shape, n, GUARD + offset
+        self.buf = torch.empty(n + 2 * GUARD + offset + 16, dtype=dtype, device=DEV)
+        raw = self.buf.view(torch.int16) if dtype == torch.bfloat16 else self.buf.view(torch.int32)
+        raw.fill_(CANARY16 if dtype == torch.bfloat16 else 0x5A5A5A5A)
+        self.t = self.buf[self.off:self.off + n].view(shape)
+        self.t.fill_(float("nan") if dtype.is_floating_point else -7)
+
+    def canaries_intact(self):
+        raw = self.buf.view(torch.int16) if self.dtype == torch.bfloat16 else self.buf.view(torch.int32)
+        pat = CANARY16 if self.dtype == torch.bfloat16 else 0x5A5A5A5A
+        lo = raw[:self.off]
+        hi = raw[self.off + self.n:]
+        return bool((lo == pat).all()) and bool((hi == pat).all())
+
+
+def upload(a, offset=0):
+    """Copy a host array into a fresh device buffer starting `offset` elements
+    past an aligned boundary (offset 0 gives a 256-byte aligned tensor)."""
+    t = to_dev(a)
+    if offset == 0:
+        return t
+    flat = torch.empty(t.numel() + offset + 16, dtype=t.dtype, device=DEV)
+    view = flat[offset:offset + t.numel()].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.cpu().numpy()
+
+
+def ref_bf16(v):
+    return oracle.round_bf16(v)
+
+
+# ------------------------------------------------------------- runners
+
+def run_softmax(x_np, out_code, x_off=0, y_off=0):
+    x = upload(x_np, x_off)
+    R, C = x_np.shape
+    y = Guarded((R, C), TDT[out_code], y_off)
+    fr.fr_softmax_fwd(x, y.t)
+    torch.cuda.synchronize()
+    assert y.canaries_intact(), "softmax wrote outside its output"
+    return host(y.t)
+
+
+def expect_softmax(x_np, out_code, got, what):
+    p = oracle.softmax(x_np)
+    if out_code == fr.BF16:
+        return check_bf16(got, ref_bf16(p), what)
+    return check_f32(got, p, what=what)
+
+
+def run_layernorm(w_x, w_g, w_b, eps, off=0):
+    x, g, b = upload(w_x, off), upload(w_g), upload(w_b)
+    R, C = w_x.shape
+    y = Guarded((R, C), x.dtype, off)
+    mean, rstd = Guarded((R,), torch.float32), Guarded((R,), torch.float32)
+    fr.fr_layernorm_fwd(x, g, b, y.t, mean.t, rstd.t, eps)
+    torch.cuda.synchronize()
+    assert y.canaries_intact() and mean.canaries_intact() and rstd.canaries_intact()
+    return host(y.t), mean.t.cpu().numpy(), rstd.t.cpu().numpy()
+
+
+def expect_layernorm(w_x, w_g, w_b, eps, got, what):
+    y, mean, rstd = got
+    yo, mo, ro = oracle.layernorm(w_x, w_g, w_b, eps)
+    xd = oracle.decode(w_x)
+    sd = np.sqrt(np.maximum(xd.var(axis=1), 0))
+    if w_x.dtype == np.uint16:
+        hy = check_bf16(y, ref_bf16(yo), what + " y")
+    else:
+        hy = check_f32(y, yo, scale=np.maximum(np.abs(yo), 1.0), what=what + " y")
+    check_f32(mean, mo, scale=np.maximum(np.abs(mo), sd), what=what + " mean")
+    check_f32(rstd, ro, what=what + " rstd")
+    return hy
+
+
+def run_rmsnorm(w_x, w_r, w_w, eps, off=0, with_res_out=True):
+    x, r, wt = upload(w_x, off), upload(w_r, off), upload(w_w)
+    R, C = w_x.shape
+    y = Guarded((R, C), x.dtype, off)
+    ro = Guarded((R, C), x.dtype, off) if with_res_out else None
+    fr.fr_add_rmsnorm_fwd(x, r, wt, y.t, ro.t if ro else None, eps)
+    torch.cuda.synchronize()
+    assert y.canaries_intact() and (ro is None or ro.canaries_intact())
+    return host(y.t), (host(ro.t) if ro else None)
+
+
+def expect_rmsnorm(w_x, w_r, w_w, eps, got, what):
+    y, ro = got
+    yo, ho, _ = oracle.add_rmsnorm(w_x, w_r, w_w, eps)
+    if w_x.dtype == np.uint16:
+        hy = check_bf16(y, ref_bf16(yo), what + " y")
+        hr = check_bf16(ro, ref_bf16(ho), what + " residual_out") if ro is not None else None
+    else:
+        hy = check_f32(y, yo, what=what + " y")
+        hr = check_f32(ro, ho, what=what + " residual_out") if ro is not None else None
+    return hy, hr
+
+
+def run_xent(logits, labels, x_off=0, g_off=0, with_argmax=True):
+    x = upload(logits, x_off)
+    lab = upload(labels)
+    R, C = logits.shape
+    grad = Guarded((R, C), torch.float32, g_off)
+    loss = Guarded((R,), torch.float32)
+    am = Guarded((R,), torch.int32) if with_argmax else None
+    fr.fr_softmax_xent_fwd_bwd(x, lab, loss.t, grad.t, am.t if am else None)
+    torch.cuda.synchronize()
+    assert grad.canaries_intact() and loss.canaries_intact() and (am is None or am.canaries_intact())
+    return loss.t.cpu().numpy(), grad.t.cpu().numpy(), (am.t.cpu().numpy() if am else None)
+
+
+def expect_xent(logits, labels, got, what):
+    loss, grad, am = got
+    lo, go, ao = oracle.softmax_xent(logits, labels)
+    R, C = logits.shape
+    valid = (labels >= 0) & (labels < C)
+    p_at = np.abs(go).copy()
+    rows = np.nonzero(valid)[0]
+    p_at[rows, labels[rows]] = go[rows, labels[rows]] + 1.0
+    check_f32(grad, go, scale=np.maximum(np.abs(go), p_at), what=what + " grad")
+    assert np.all(np.isnan(loss[~valid])), what + ": out-of-range label must give NaN loss"
+    check_f32(loss[valid], lo[valid], scale=np.maximum(np.abs(lo[valid]), 1.0), what=what + " loss")
+    if am is not None:
+        assert np.array_equal(am, ao), what + " argmax"
+    # label sign test: exactly one negative gradient per valid row, at the label
+    for r in rows[:64]:
+        neg = np.nonzero(grad[r] < 0)[0]
+        assert list(neg) == [labels[r]], (what, r, neg[:5])
+
+
+# ------------------------------------------------- full-size workloads
+
+def test_workload_softmax_f32():
+    w = workloads.make("softmax_f32")
+    got = run_softmax(w["x"], fr.F32)
+    st = expect_softmax(w["x"], fr.F32, got, "softmax_f32 64x1000")
+    assert np.abs(got.astype(np.float64).sum(1) - 1).max() < 1e-5
+    print("softmax_f32", st)
+
+
+def test_workload_layernorm_f32():
+    w = workloads.make("layernorm_f32")
+    got = run_layernorm(w["x"], w["gamma"], w["beta"], w.eps)
+    expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps, got, "layernorm_f32 4096x1024")
+
+
+def test_workload_softmax_bf16():
+    w = workloads.make("softmax_bf16")
+    got = run_softmax(w["x"], fr.BF16)
+    p = oracle.softmax(w["x"])
+    hist = check_bf16(got, ref_bf16(p), "softmax_bf16 16384x4096")
+    sub = int(((p > 0) & (p < 2.0 ** -126)).sum())
+    print("softmax_bf16 ulp histogram", hist, "oracle values below 2^-126:", sub)
+    assert sub > 0   # the near-one-hot rows do exercise bf16 subnormals
+
+
+def test_workload_add_rmsnorm_bf16():
+    w = workloads.make("add_rmsnorm_bf16")
+    hy, hr = expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps,
+                            run_rmsnorm(w["x"], w["residual"], w["weight"], w.eps),
+                            "add_rmsnorm_bf16 8192x8192")
+    print("add_rmsnorm y ulp", hy, "residual_out ulp", hr)
+    # the updated residual is exact except where fp32 could not hold x + r
+    assert hr[">1"] == 0 and hr["1"] <= 1e-4 * (hr["0"] + hr["1"])
+
+
+def test_workload_xent_f32():
+    w = workloads.make("xent_f32")
+    got = run_xent(w["logits"], w["labels"])
+    expect_xent(w["logits"], w["labels"], got, "xent_f32 4096x50257")
+
+
+# ------------------------------------------------------- edge shapes
+
+EDGE_COLS = [1, 2, 3, 4, 5, 7, 8, 9, 63, 64, 65, 127, 255, 257, 1000, 1023, 1024, 1025,
+             2047, 4095, 4096, 4097, 8191, 8192, 12345, 16384, 32769, 50257, 65536]
+
+
+def _softmax_input(code, R, C, seed):
+    if code == fr.BF16:
+        return workloads.make("softmax_bf16", rows=R, cols=C, seed=seed)["x"]
+    return workloads.make("softmax_f32", rows=R, cols=C, seed=seed)["x"]
+
+
+@pytest.mark.parametrize("C", EDGE_COLS)
+@pytest.mark.parametrize("xin,yout", [(0, 0), (1, 1), (0, 1), (1, 0)])
+def test_softmax_edge_cols(C, xin, yout):
+    for R in (1, 3):
+        x = _softmax_input(xin, R, C, seed=C * 7 + R)
+        expect_softmax(x, yout, run_softmax(x, yout), f"softmax {xin}->{yout} {R}x{C}")
+
+
+@pytest.mark.parametrize("C", EDGE_COLS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_layernorm_edge_cols(C, dt):
+    w = workloads.make("layernorm_f32", rows=3, cols=C, seed=C, dtype=dt)
+    got = run_layernorm(w["x"], w["gamma"], w["beta"], w.eps)
+    expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps, got, f"layernorm {dt} 3x{C}")
+
+
+@pytest.mark.parametrize("C", EDGE_COLS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rmsnorm_edge_cols(C, dt):
+    w = workloads.make("add_rmsnorm_bf16", rows=3, cols=C, seed=C, dtype=dt)
+    got = run_rmsnorm(w["x"], w["residual"], w["weight"], w.eps)
+    expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, got, f"add_rmsnorm {dt} 3x{C}")
+
+
+@pytest.mark.parametrize("C", EDGE_COLS)
+def test_xent_edge_cols(C):
+    w = workloads.make("xent_f32", rows=4, cols=C, seed=C)
+    lab = w["labels"].copy()
+    lab[0], lab[-1] = 0, C - 1          # first and last column
+    expect_xent(w["logits"], lab, run_xent(w["logits"], lab), f"xent 4x{C}")
+
+
+def test_many_rows_odd_count():
+    # more rows than one grid wave, odd count (partial last workgroup)
+    x = _softmax_input(0, 4099, 300, seed=5)
+    expect_softmax(x, 0, run_softmax(x, 0), "softmax 4099x300")
+    w = workloads.make("xent_f32", rows=1031, cols=777, seed=6)
+    expect_xent(w["logits"], w["labels"], run_xent(w["logits"], w["labels"]), "xent 1031x777")
+
+
+# ----------------------------------------------------- every variant
+
+VARIANT_GRID = [(t, v) for t in (64, 256, 512, 1024) for v in (1, 2, 4, 8, 13, 16, 64)]
+
+
+def _variant_cols(op, t, v, code, vector_path):
+    try:
+        with fr.forced_variant(op, t, v):
+            tt, vv, e = fr.fr_debug_select_variant(op, 1, code, vector_path=vector_path)
+    except fr.FusedRowError:
+        return None
+    cap = tt * vv * e
+    return [cap, max(1, cap - 5 * e - 3), max(1, cap // 2 + 1)]
+
+
+@pytest.mark.parametrize("t,v", VARIANT_GRID)
+def test_every_softmax_variant(t, v):
+    ran = 0
+    for code in (fr.F32, fr.BF16):
+        cols = _variant_cols(fr.OP_SOFTMAX, t, v, code, True)
+        if not cols:
+            continue
+        with fr.forced_variant(fr.OP_SOFTMAX, t, v):
+            for C in cols:
+                x = _softmax_input(code, 3, C, seed=C)
+                expect_softmax(x, code, run_softmax(x, code), f"softmax[{t},{v}] {code} 3x{C}")
+                ran += 1
+    for code in (fr.F32, fr.BF16):
+        cols = _variant_cols(fr.OP_SOFTMAX, t, v, code, False)
+        if not cols:
+            continue
+        with fr.forced_variant(fr.OP_SOFTMAX, t, v):
+            for C in cols:
+                x = _softmax_input(code, 2, C, seed=C + 1)
+                expect_softmax(x, code, run_softmax(x, code, x_off=1, y_off=2),
+                               f"softmax scalar[{t},{v}] {code} 2x{C}")
+                ran += 1
+    if not ran:
+        pytest.skip(f"no softmax variant ({t}, {v})")
+
+
+@pytest.mark.parametrize("t,v", VARIANT_GRID)
+def test_every_norm_and_xent_variant(t, v):
+    ran = 0
+    for dt, code in (("f32", fr.F32), ("bf16", fr.BF16)):
+        for vp, off in ((True, 0), (False, 1)):
+            cols = _variant_cols(fr.OP_LAYERNORM, t, v, code, vp)
+            if cols:
+                with fr.forced_variant(fr.OP_LAYERNORM, t, v):
+                    for C in cols:
+                        w = workloads.make("layernorm_f32", rows=2, cols=C, seed=C, dtype=dt)
+                        expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps,
+                                         run_layernorm(w["x"], w["gamma"], w["beta"], w.eps, off),
+                                         f"layernorm[{t},{v},{vp}] {dt} 2x{C}")
+                        ran += 1
+            cols = _variant_cols(fr.OP_RMSNORM, t, v, code, vp)
+            if cols:
+                with fr.forced_variant(fr.OP_RMSNORM, t, v):
+                    for C in cols:
+                        w = workloads.make("add_rmsnorm_bf16", rows=2, cols=C, seed=C, dtype=dt)
+                        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps,
+                                       run_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, off),
+                                       f"rmsnorm[{t},{v},{vp}] {dt} 2x{C}")
+                        ran += 1
+    for vp, off in ((True, 0), (False, 1)):
+        cols = _variant_cols(fr.OP_XENT, t, v, fr.F32, vp)
+        if cols:
+            with fr.forced_variant(fr.OP_XENT, t, v):
+                for C in cols:
+                    w = workloads.make("xent_f32", rows=3, cols=C, seed=C)
+                    for am in (True, False):
+                        expect_xent(w["logits"], w["labels"],
+                                    run_xent(w["logits"], w["labels"], off, 2 * off, with_argmax=am),
+                                    f"xent[{t},{v},{vp}] 3x{C}")
+                    ran += 1
+    if not ran:
+        pytest.skip(f"no variant ({t}, {v})")
+
+
+# --------------------------------------------------- alignment / aliasing
+
+@pytest.mark.parametrize("xoff,yoff", [(1, 1), (2, 2), (3, 3), (1, 0), (0, 3)])
+def test_misaligned_rows(xoff, yoff):
+    # equal phases take the head/body/tail vector path, unequal the scalar path
+    for C in (5, 1000, 50257):
+        x = _softmax_input(0, 5, C, seed=C)
+        expect_softmax(x, 0, run_softmax(x, 0, xoff, yoff), f"softmax off {xoff},{yoff} 5x{C}")
+        w = workloads.make("xent_f32", rows=5, cols=C, seed=C)
+        lab = w["labels"].copy()
+        lab[:] = [0, C - 1, min(2, C - 1), C // 2, max(C - 3, 0)]
+        expect_xent(w["logits"], lab, run_xent(w["logits"], lab, xoff, yoff), f"xent off 5x{C}")
+    for off in (1, 3):
+        w = workloads.make("layernorm_f32", rows=4, cols=1000, seed=off)
+        expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps,
+                         run_layernorm(w["x"], w["gamma"], w["beta"], w.eps, off), "layernorm off")
+        w = workloads.make("add_rmsnorm_bf16", rows=4, cols=1000, seed=off)
+        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps,
+                       run_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, off), "rmsnorm off")
+
+
+def test_in_place():
+    x = _softmax_input(1, 64, 4096, seed=3)
+    t = to_dev(x)
+    fr.fr_softmax_fwd(t, t)
+    expect_softmax(x, 1, bf16_bits(t), "softmax in place")
+
+    w = workloads.make("layernorm_f32", rows=64, cols=1024, seed=4)
+    t = to_dev(w["x"])
+    mean = torch.empty(64, device=DEV)
+    rstd = torch.empty(64, device=DEV)
+    fr.fr_layernorm_fwd(t, to_dev(w["gamma"]), to_dev(w["beta"]), t, mean, rstd, w.eps)
+    expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps,
+                     (t.cpu().numpy(), mean.cpu().numpy(), rstd.cpu().numpy()), "layernorm in place")
+
+    w = workloads.make("add_rmsnorm_bf16", rows=64, cols=8192, seed=5)
+    for mode in ("res_out=res", "res_out=x", "y=x"):
+        xt, rt, wt = to_dev(w["x"]), to_dev(w["residual"]), to_dev(w["weight"])
+        if mode == "res_out=res":
+            y = torch.empty_like(xt); ro = rt
+        elif mode == "res_out=x":
+            y = torch.empty_like(xt); ro = xt
+        else:
+            y = xt; ro = torch.empty_like(xt)
+        fr.fr_add_rmsnorm_fwd(xt, rt, wt, y, ro, w.eps)
+        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, (bf16_bits(y), bf16_bits(ro)),
+                       f"rmsnorm in place {mode}")
+
+    w = workloads.make("xent_f32", rows=64, cols=50257, seed=6)
+    t = to_dev(w["logits"])
+    loss = torch.empty(64, device=DEV)
+    fr.fr_softmax_xent_fwd_bwd(t, to_dev(w["labels"]), loss, t)
+    expect_xent(w["logits"], w["labels"], (loss.cpu().numpy(), t.cpu().numpy(), None), "xent in place")
+
+
+# --------------------------------------------------------- special values
+
+def test_special_values_softmax():
+    rng = np.random.default_rng(99)
+    C = 1000
+    x = rng.normal(0, 3, size=(6, C)).astype(np.float32)
+    x[0, ::3] = -np.inf                      # masked entries
+    x[1, :] = -np.inf                        # fully masked row -> NaN
+    x[2, :] = 7.25                           # constant row -> 1/C
+    x[3] += 1000.0                           # shift
+    x[4, 5] = 100.0                          # one-hot
+    x[5, :] = np.float32(-3.0e38)            # huge negative, finite
+    for code in (fr.F32, fr.BF16):
+        got = run_softmax(x, code)
+        gotf = got.astype(np.float64) if code == fr.F32 else \
+            (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.isnan(gotf[1])), "all -inf row must be NaN"
+        keep = [0, 2, 3, 4, 5]
+        expect_softmax(x[keep], code, got[keep], f"softmax special {code}")
+        assert np.all(gotf[0, ::3] == 0.0)
+
+
+def test_special_values_norms():
+    # constant rows: LayerNorm gives beta exactly, rstd = 1/sqrt(eps)
+    C = 1024
+    x = np.full((2, C), 3.5, np.float32)
+    g = np.ones(C, np.float32)
+    b = np.linspace(-1, 1, C).astype(np.float32)
+    got = run_layernorm(x, g, b, 1e-5)
+    expect_layernorm(x, g, b, 1e-5, got, "layernorm constant")
+    assert np.array_equal(got[0], np.broadcast_to(b, (2, C)))
+    # zero input to RMSNorm: y = 0 with eps > 0
+    z = np.zeros((2, C), np.float32)
+    y, ro = run_rmsnorm(z, z, np.ones(C, np.float32), 1e-6)
+    assert np.all(y == 0) and np.all(ro == 0)
+
+
+def test_labels_out_of_range():
+    w = workloads.make("xent_f32", rows=6, cols=3000, seed=8)
+    lab = np.array([-1, 3000, 2**31 - 1, -(2**31), 0, 2999], np.int32)
+    got = run_xent(w["logits"], lab)
+    expect_xent(w["logits"], lab, got, "xent bad labels")
+    p = oracle.softmax(w["logits"])
+    check_f32(got[1][:4], p[:4], what="grad of rows with bad labels = softmax")
+
+
+# ------------------------------------------------- determinism / streams
+
+def test_bitwise_determinism():
+    w = workloads.make("xent_f32", rows=256, cols=50257, seed=10)
+    x, lab = to_dev(w["logits"]), to_dev(w["labels"])
+    outs = []
+    for _ in range(3):
+        loss, grad, am = fr.softmax_xent(x, lab, return_argmax=True)
+        outs.append((loss.cpu().numpy().tobytes(), grad.cpu().numpy().tobytes(),
+                     am.cpu().numpy().tobytes()))
+    assert outs[0] == outs[1] == outs[2]
+    w = workloads.make("softmax_bf16", rows=512, seed=11)
+    x = to_dev(w["x"])
+    r = [bf16_bits(fr.softmax(x)).tobytes() for _ in range(3)]
+    assert r[0] == r[1] == r[2]
+    w = workloads.make("layernorm_f32", rows=512, seed=12)
+    args = [to_dev(w[k]) for k in ("x", "gamma", "beta")]
+    r = [tuple(t.cpu().numpy().tobytes() for t in fr.layernorm(*args, w.eps)) for _ in range(3)]
+    assert r[0] == r[1] == r[2]
+
+
+def test_non_default_stream():
+    w = workloads.make("add_rmsnorm_bf16", rows=128, seed=13)
+    s = torch.cuda.Stream()
+    x, r, wt = to_dev(w["x"]), to_dev(w["residual"]), to_dev(w["weight"])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y, ro = fr.add_rmsnorm(x, r, wt, w.eps)
+    s.synchronize()
+    expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, (bf16_bits(y), bf16_bits(ro)),
+                   "rmsnorm on a side stream")
+
+
+def test_stream_copy():
+    src = torch.randint(0, 2**31 - 1, (1 << 20,), dtype=torch.int32, device=DEV)
+    dst = torch.zeros_like(src)
+    fr.fr_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    dst2 = torch.zeros(1000, dtype=torch.uint8, device=DEV)
+    src2 = torch.arange(1001, dtype=torch.uint8, device=DEV)[1:]
+    fr.fr_stream_copy(src2, dst2)
+    torch.cuda.synchronize()
+    assert torch.equal(src2, dst2)
+
+
+def test_rows_zero_is_noop():
+    x = torch.empty(0, 100, device=DEV)
+    fr.fr_softmax_fwd(x, torch.empty(0, 100, device=DEV))
+    loss, grad = fr.softmax_xent(torch.empty(0, 7, device=DEV),
+                                 torch.empty(0, dtype=torch.int32, device=DEV))
+    assert loss.numel() == 0 and grad.numel() == 0

@@ -158,6 +158,10 @@ typedef enum { FR_OP_SOFTMAX = 0, FR_OP_LAYERNORM = 1, FR_OP_RMSNORM = 2, FR_OP_
  * concurrent calls. */
 FR_API fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs);
 
+/* hipError_t code of the last failed kernel launch on this thread (0 if
+ * none), to explain an FR_E_LAUNCH. */
+FR_API int fr_debug_last_launch_error(void);
+
 /* Describe the variant automatic selection would pick (or the forced one)
  * for a row of `cols` elements: writes lanes per row, vectors per lane and
  * elements per vector (1 on the scalar path). in/out dtypes as for the op

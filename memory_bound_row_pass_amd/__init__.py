@@ -32,7 +32,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfusedrow
 class FusedRowError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        extra = ""
+        if status == 5:  # FR_E_LAUNCH: name the HIP error
+            extra = f", hipError_t {lib.fr_debug_last_launch_error()}"
+        super().__init__(f"{where}: {status_str(status)} (status {status}{extra})")
 
 
 def _load() -> ctypes.CDLL:
@@ -40,6 +43,14 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is not built; run __graft_entry__.build() or "
             "python memory_bound_row_pass_amd/_build.py (hipcc, gfx950)")
+    # torch bundles its own HIP runtime (same SONAME as /opt/rocm's). Loading
+    # torch first makes libfusedrow bind to that one runtime; loading the
+    # library first would put a second runtime in the process, which then
+    # reports no device to whichever side did not initialise it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     IP = ctypes.POINTER(ctypes.c_int)
@@ -60,6 +71,8 @@ def _load() -> ctypes.CDLL:
     L.fr_status_str.restype = ctypes.c_char_p
     L.fr_version.argtypes = []
     L.fr_version.restype = ctypes.c_char_p
+    L.fr_debug_last_launch_error.argtypes = []
+    L.fr_debug_last_launch_error.restype = ctypes.c_int
     return L
 
 

@@ -93,11 +93,20 @@ const V* select_variant(VariantSpan<V> sp, int op, int64_t cols, int epv) {
 
 fr_status_t launch_status(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_LAUNCH; }
 
+thread_local int t_last_launch_error = 0;
+
 int vec_epv(int esz) { return 16 / esz; }
 
 }  // namespace
 
+namespace fr {
+void note_launch_error(hipError_t e) { t_last_launch_error = static_cast<int>(e); }
+}  // namespace fr
+
 extern "C" {
+
+int fr_debug_last_launch_error(void) { return t_last_launch_error; }
+
 
 const char* fr_status_str(fr_status_t s) {
   switch (s) {

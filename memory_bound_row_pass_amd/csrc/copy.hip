@@ -37,15 +37,14 @@ hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStre
     int64_t blocks = (n16 + 1023) / 1024;
     blocks = blocks < 2048 ? blocks : 2048;
     blocks = blocks > 0 ? blocks : 1;
-    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+    return launch_kernel(&stream_copy_kernel, dim3((unsigned)blocks), dim3(256), s,
+                         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
   } else {
     int64_t blocks = (bytes + 255) / 256;
     blocks = blocks < 4096 ? blocks : 4096;
-    hipLaunchKernelGGL(byte_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), bytes);
+    return launch_kernel(&byte_copy_kernel, dim3((unsigned)blocks), dim3(256), s,
+                         static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), bytes);
   }
-  return hipGetLastError();
 }
 
 }  // namespace fr

@@ -347,7 +347,9 @@ struct MaxSumState {
 
 // (ma, sa) (+) (mb, sb) = (M, s_hi + s_lo * e^(lo - M)), M = max, lo = min.
 // The larger side is never rescaled; an empty side (or two empty sides)
-// contributes nothing. LOG2 selects base 2 (states kept in log2 units).
+// contributes nothing. States are in natural units; LOG2 selects the plain
+// hardware exponential for the rescale (bf16 outputs), otherwise the
+// compensated one.
 template <bool LOG2>
 struct MaxSumMerge {
   __device__ __forceinline__ MaxSumState operator()(const MaxSumState& a, const MaxSumState& b) const {
@@ -357,7 +359,7 @@ struct MaxSumMerge {
     const float s_hi = a_hi ? a.s : b.s;
     const float s_lo = a_hi ? b.s : a.s;
     float f;
-    if constexpr (LOG2) f = exp2_hw(lo - M);
+    if constexpr (LOG2) f = exp2_hw((lo - M) * kLog2e);
     else f = exp_acc(lo - M);
     f = (lo == M) ? 1.f : f;  // equal maxima (including two empty states)
     return {M, __builtin_fmaf(s_lo, f, s_hi)};

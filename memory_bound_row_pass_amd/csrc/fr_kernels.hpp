@@ -8,6 +8,9 @@
 
 namespace fr {
 
+// Records the HIP error of a failed launch for fr_debug_last_launch_error.
+void note_launch_error(hipError_t e);
+
 // Largest grid used; row loops stride by the grid beyond it.
 constexpr int64_t kMaxGrid = int64_t(1) << 30;
 
@@ -45,5 +48,18 @@ VariantSpan<RmsNormVariant> rmsnorm_variants(int bf16);
 VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
+// Launch `kernel` and return the status of this launch alone (not an error
+// left behind by an earlier runtime call, as hipGetLastError would).
+// Arguments must have exactly the kernel's parameter types.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                         Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+  void* argv[] = {static_cast<void*>(&args)...};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+  if (e != hipSuccess) note_launch_error(e);
+  return e;
+}
 
 }  // namespace fr

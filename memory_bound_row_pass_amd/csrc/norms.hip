@@ -171,10 +171,9 @@ static hipError_t launch_layernorm(const void* x, const void* gamma, const void*
   constexpr int RPB = BLOCK / T;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-  hipLaunchKernelGGL((layernorm_kernel<Ts, T, NV, EPV, OCC>), dim3(grid), dim3(BLOCK), 0, s,
+  return launch_kernel(&layernorm_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(BLOCK), s,
                      static_cast<const Ts*>(x), static_cast<const Ts*>(gamma),
                      static_cast<const Ts*>(beta), static_cast<Ts*>(y), mean, rstd, rows, cols, eps);
-  return hipGetLastError();
 }
 
 template <typename Ts, int T, int NV, int EPV, int OCC>
@@ -184,11 +183,10 @@ static hipError_t launch_rmsnorm(const void* x, const void* res, const void* w, 
   constexpr int RPB = BLOCK / T;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-  hipLaunchKernelGGL((add_rmsnorm_kernel<Ts, T, NV, EPV, OCC>), dim3(grid), dim3(BLOCK), 0, s,
+  return launch_kernel(&add_rmsnorm_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(BLOCK), s,
                      static_cast<const Ts*>(x), static_cast<const Ts*>(res),
                      static_cast<const Ts*>(w), static_cast<Ts*>(y), static_cast<Ts*>(res_out), rows,
                      cols, eps);
-  return hipGetLastError();
 }
 
 #define FR_LN(TS, T, NV, EPV, OCC) {T, NV, EPV, &launch_layernorm<TS, T, NV, EPV, OCC>}

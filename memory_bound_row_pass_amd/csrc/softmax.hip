@@ -70,9 +70,8 @@ static hipError_t launch_softmax(const void* x, void* y, int64_t rows, int cols,
   constexpr int RPB = BLOCK / T;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-  hipLaunchKernelGGL((softmax_kernel<Tin, Tout, T, NV, EPV, OCC>), dim3(grid), dim3(BLOCK), 0, s,
+  return launch_kernel(&softmax_kernel<Tin, Tout, T, NV, EPV, OCC>, dim3(grid), dim3(BLOCK), s,
                      static_cast<const Tin*>(x), static_cast<Tout*>(y), rows, cols);
-  return hipGetLastError();
 }
 
 // Variant tables, in order of preference (the first that holds the row wins).

@@ -43,31 +43,46 @@ __device__ __forceinline__ float lane_max(const float (&v)[NV][EPV], float xe) {
 }
 
 // ---------------------------------------------------------------- bf16 path
-// Base-2 units with a 2^64 bias: e_j = 2^(x_j*log2e - m_l*log2e + 64) lies
-// in (0, 2^64] and is normal down to x_j - m_l = -131, which covers every
-// value that can round to a non-zero bf16 (p >= 2^-134). Lane state is
-// (m_l*log2e, s_l).
+// e_j = 2^((x_j - m_l)*log2e + 64), computed as 2^(x_j*log2e + K) with
+// K = 64 - m_l*log2e: e_j lies in (0, 2^64] and is normal down to
+// x_j - m_l = -131, which covers every value that can round to a non-zero
+// bf16 (p >= 2^-134). The lane state (m_l, s_l) stays in natural units.
+// When m_l*log2e would overflow (|m_l| >= 2e38) the wave takes the slower
+// (x_j - m_l)*log2e + 64 form.
 template <int NV, int EPV>
 __device__ __forceinline__ MaxSumState lane_exp_log2(float (&v)[NV][EPV], float& xe, float m) {
   const bool empty = (m == kNegInf);
-  const float mL = m * kLog2e;
-  const float K = empty ? 0.f : 64.f - mL;
+  const bool huge = !empty && __builtin_fabsf(m) >= 2.0e38f && __builtin_fabsf(m) != __builtin_inff();
   float s0 = 0.f, s1 = 0.f;
+  if (!__any(huge)) {
+    const float K = empty ? 0.f : 64.f - m * kLog2e;
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int k = 0; k < EPV; ++k) {
-      v[i][k] = exp2_hw(__builtin_fmaf(v[i][k], kLog2e, K));
-      if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
-    }
-  xe = exp2_hw(__builtin_fmaf(xe, kLog2e, K));
-  return {empty ? kNegInf : mL, (s0 + s1) + xe};
+      for (int k = 0; k < EPV; ++k) {
+        v[i][k] = exp2_hw(__builtin_fmaf(v[i][k], kLog2e, K));
+        if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
+      }
+    xe = exp2_hw(__builtin_fmaf(xe, kLog2e, K));
+  } else {
+    const float mr = empty ? 0.f : m;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, 64.f));
+        if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
+      }
+    xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, 64.f));
+  }
+  return {m, (s0 + s1) + xe};
 }
 
-// p_j = e_j * 2^(mL - M) / S, where S carries the same 2^64 bias. The factor
-// is split as G * 2^n with G = 2^(mL - M - n) / S normal (n = floor(mL - M)),
-// and 2^n is applied with v_ldexp, so results in the bf16 subnormal range are
-// rounded from a full-precision fp32 value instead of a flushed factor.
+// p_j = e_j * 2^((m_l - M)*log2e) / S, where S carries the same 2^64 bias.
+// The factor is split as G * 2^n with G = 2^(d - n) / S normal
+// (d = (m_l - M)*log2e, n = floor(d)), and 2^n is applied with v_ldexp, so
+// results in the bf16 subnormal range are rounded from a full-precision fp32
+// value instead of a flushed factor.
 struct Log2Scale {
   float g;
   int n;
@@ -76,8 +91,7 @@ struct Log2Scale {
 __device__ __forceinline__ Log2Scale log2_scale(float m, float M, float S) {
   // d <= 0; -inf for an empty lane (its e_j are all 0); NaN if the row is
   // all -inf (the result is then NaN, as for the definition).
-  const float mL = m == kNegInf ? kNegInf : m * kLog2e;
-  const float d = mL - M;
+  const float d = (m - M) * kLog2e;
   float fl = __builtin_floorf(d);
   fl = fl < -300.f ? -300.f : fl;  // also maps -inf to -300
   return {exp2_hw(d - fl) / S, (int)fl};

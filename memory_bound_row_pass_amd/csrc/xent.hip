@@ -151,10 +151,9 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   constexpr int RPB = BLOCK / T;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-  hipLaunchKernelGGL((xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX>), dim3(grid), dim3(BLOCK), 0, s,
+  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX>, dim3(grid), dim3(BLOCK), s,
                      static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax, rows,
                      cols);
-  return hipGetLastError();
 }
 
 #define FR_XE(T, NV, EPV, OCC, AM) {T, NV, EPV, &launch_xent<float, T, NV, EPV, OCC, AM>}

@@ -11,7 +11,9 @@ fp32 outputs: |g - o| <= 1e-5 * scale + 2^-126, where scale is |o| unless a
   2^-126 is the fp32 normal threshold: below it fp32 carries no relative
   precision, so no implementation can meet a relative bound there.
 bf16 outputs: bit patterns mapped to ordered integers; pass iff within one
-  bf16 ulp of the oracle value rounded to nearest even.
+  bf16 ulp of the oracle value rounded to nearest even. LayerNorm y, which
+  crosses zero by cancellation, may instead be within 1e-5 * max(|o|, 1)
+  (the same floor as its fp32 rule); the ulp histogram is still reported.
 int32 outputs: exact.
 """
 import numpy as np
@@ -56,9 +58,20 @@ def check_f32(got, ref, scale=None, what=""):
     return stats
 
 
-def check_bf16(got_bits, ref_bits, what="", max_ulp=1):
+def bf16_value(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_bf16(got_bits, ref_bits, what="", max_ulp=1, abs_floor=None):
+    """Within max_ulp bf16 ulps of the rounded oracle. With abs_floor, an
+    element also passes if |g - o| <= abs_floor * max(|o|, 1) (outputs formed
+    by cancellation; the histogram still reports their ulp distance)."""
     d = np.abs(ordered(got_bits) - ordered(ref_bits))
     hist = {"0": int((d == 0).sum()), "1": int((d == 1).sum()), ">1": int((d > 1).sum())}
+    if abs_floor is not None and hist[">1"]:
+        g, o = bf16_value(got_bits), bf16_value(ref_bits)
+        near = np.abs(g - o) <= abs_floor * np.maximum(np.abs(o), 1.0)
+        d = np.where(near, 0, d)
     if d.max(initial=0) > max_ulp:
         i = int(np.argmax(d))
         raise AssertionError(f"{what}: max ulp {int(d.max())} at flat index {i} "

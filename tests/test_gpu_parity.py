@@ -116,7 +116,9 @@ def expect_layernorm(w_x, w_g, w_b, eps, got, what):
     xd = oracle.decode(w_x)
     sd = np.sqrt(np.maximum(xd.var(axis=1), 0))
     if w_x.dtype == np.uint16:
-        hy = check_bf16(y, ref_bf16(yo), what + " y")
+        # y crosses zero through beta: where |y| << 1 the result is a
+        # cancellation and carries the fp32 absolute error of the O(1) terms
+        hy = check_bf16(y, ref_bf16(yo), what + " y", abs_floor=1e-5)
     else:
         hy = check_f32(y, yo, scale=np.maximum(np.abs(yo), 1.0), what=what + " y")
     check_f32(mean, mo, scale=np.maximum(np.abs(mo), sd), what=what + " mean")
@@ -173,10 +175,12 @@ def expect_xent(logits, labels, got, what):
     check_f32(loss[valid], lo[valid], scale=np.maximum(np.abs(lo[valid]), 1.0), what=what + " loss")
     if am is not None:
         assert np.array_equal(am, ao), what + " argmax"
-    # label sign test: exactly one negative gradient per valid row, at the label
+    # label sign test: exactly one negative gradient per valid row, at the
+    # label (unless p_label rounds to 1 and its gradient is exactly 0)
     for r in rows[:64]:
         neg = np.nonzero(grad[r] < 0)[0]
-        assert list(neg) == [labels[r]], (what, r, neg[:5])
+        want = [labels[r]] if go[r, labels[r]] < -FLT_MIN else []
+        assert list(neg) == want, (what, r, neg[:5])
 
 
 # ------------------------------------------------- full-size workloads
@@ -285,6 +289,9 @@ def _variant_cols(op, t, v, code, vector_path):
     except fr.FusedRowError:
         return None
     cap = tt * vv * e
+    if op in (fr.OP_LAYERNORM, fr.OP_RMSNORM) and e > 1:
+        # the norms' 128-bit path needs rows that are whole 16-byte chunks
+        return [cap, cap - 5 * e, e * (cap // (2 * e) + 1)]
     return [cap, max(1, cap - 5 * e - 3), max(1, cap // 2 + 1)]
 
 

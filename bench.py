@@ -1,0 +1,296 @@
+"""Benchmark of the fused row kernels on one MI355X.
+
+One step is one pass of the whole hot path over one batch of each workload:
+five launches on the current stream, in this order
+  softmax fp32 [64, 1000]; LayerNorm fp32 [4096, 1024]; softmax bf16
+  [16384, 4096]; residual-add + RMSNorm bf16 [8192, 8192]; softmax
+  cross-entropy fwd+bwd fp32 [4096, 50257].
+Inputs are seeded synthetic data resident in HBM before timing starts. One
+step moves 2.49 GB, so by the time a workload's buffers come round again the
+256 MB last-level cache has been swept: every launch reads HBM.
+
+value = algorithmic bytes of one step (each input element read once, each
+output element written once) / wall time of one step, in GB/s; per-launch
+durations come from HIP events recorded on the stream the kernels run on.
+
+Printed: ONE JSON line (rank 0), with per-workload figures, the roofline of
+the dominant kernel (the cross-entropy launch), the streaming-copy ceiling,
+and the CPU oracle timed on the host cores as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s, fused row softmax/norm"
+DOMINANT = "xent_f32"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "xent_f32_4096x50257_traffic.json")
+KERNEL_SOURCES = ["xent.hip", "softmax_core.hpp", "fr_device.hpp"]
+
+
+def algo_bytes(name, R, C):
+    """Each input element read once, each output element written once."""
+    if name == "softmax_f32":
+        return R * C * 4 * 2
+    if name == "layernorm_f32":
+        return R * C * 4 * 2 + 2 * C * 4 + 2 * R * 4          # x, y; gamma, beta; mean, rstd
+    if name == "softmax_bf16":
+        return R * C * 2 * 2
+    if name == "add_rmsnorm_bf16":
+        return 4 * R * C * 2 + C * 2                           # x, r, y, r_out; w
+    if name == "xent_f32":
+        return 2 * R * C * 4 + R * 4 + R * 4                   # logits, grad; labels, loss
+    raise KeyError(name)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "memory_bound_row_pass_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per cross-entropy launch from the committed counter summary,
+    or None when there is none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+class Workload:
+    def __init__(self, name, w, dev, torch, fr):
+        import numpy as np
+        self.name, self.w = name, w
+        self.R, self.C = w.rows, w.cols
+        self.bytes = algo_bytes(name, self.R, self.C)
+
+        def d(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        self.torch, self.fr = torch, fr
+        if name in ("softmax_f32", "softmax_bf16"):
+            self.x = d(w["x"])
+            self.y = torch.empty_like(self.x)
+            self.run = lambda: fr.fr_softmax_fwd(self.x, self.y)
+            self.op, self.code = fr.OP_SOFTMAX, (fr.BF16 if name == "softmax_bf16" else fr.F32)
+        elif name == "layernorm_f32":
+            self.x, self.g, self.b = d(w["x"]), d(w["gamma"]), d(w["beta"])
+            self.y = torch.empty_like(self.x)
+            self.mean = torch.empty(self.R, device=dev)
+            self.rstd = torch.empty(self.R, device=dev)
+            self.run = lambda: fr.fr_layernorm_fwd(self.x, self.g, self.b, self.y, self.mean,
+                                                   self.rstd, w.eps)
+            self.op, self.code = fr.OP_LAYERNORM, fr.F32
+        elif name == "add_rmsnorm_bf16":
+            self.x, self.r, self.wt = d(w["x"]), d(w["residual"]), d(w["weight"])
+            self.y = torch.empty_like(self.x)
+            self.ro = torch.empty_like(self.x)
+            self.run = lambda: fr.fr_add_rmsnorm_fwd(self.x, self.r, self.wt, self.y, self.ro, w.eps)
+            self.op, self.code = fr.OP_RMSNORM, fr.BF16
+        elif name == "xent_f32":
+            self.x, self.lab = d(w["logits"]), d(w["labels"])
+            self.loss = torch.empty(self.R, device=dev)
+            self.grad = torch.empty_like(self.x)
+            self.run = lambda: fr.fr_softmax_xent_fwd_bwd(self.x, self.lab, self.loss, self.grad)
+            self.op, self.code = fr.OP_XENT, fr.F32
+        self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
+
+
+def copy_ceiling(torch, fr, dev, nbytes=2 << 30, reps=20):
+    """Read+write GB/s of the library's plain streaming copy over 2 GiB."""
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        fr.fr_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        fr.fr_stream_copy(src, dst)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(wls, budget_s=15.0):
+    """The oracle (plain double-precision C, OpenMP over rows) on the host
+    cores over the same inputs: full steps, repeated while within budget."""
+    import oracle
+    oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    threads = oracle.threads()
+    total_bytes = sum(w.bytes for w in wls)
+
+    def one_step():
+        for w in wls:
+            a = w.w
+            if w.name in ("softmax_f32", "softmax_bf16"):
+                oracle.softmax(a["x"])
+            elif w.name == "layernorm_f32":
+                oracle.layernorm(a["x"], a["gamma"], a["beta"], a.eps)
+            elif w.name == "add_rmsnorm_bf16":
+                y, h, _ = oracle.add_rmsnorm(a["x"], a["residual"], a["weight"], a.eps)
+                oracle.round_bf16(y)
+                oracle.round_bf16(h)
+            elif w.name == "xent_f32":
+                oracle.softmax_xent(a["logits"], a["labels"])
+
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        one_step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el > budget_s / 2 or n >= 3:
+            break
+    per_step = el / n
+    return {"value": total_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} full step(s): all rows of the five workloads, "
+                      f"{per_step:.2f} s per step, double precision, {threads} OpenMP threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true", help="no progress lines on stderr")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the row kernels own whole rows and need no "
+              "collective; multi-GPU runs are not part of this benchmark (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    import numpy as np  # noqa: F401
+    import torch
+    import memory_bound_row_pass_amd as fr
+    import workloads
+
+    dev = torch.device("cuda:0")
+    names = ["softmax_f32", "layernorm_f32", "softmax_bf16", "add_rmsnorm_bf16", "xent_f32"]
+    wls = []
+    for n in names:
+        t0 = time.perf_counter()
+        wls.append(Workload(n, workloads.make(n), dev, torch, fr))
+        log(f"generated {n} in {time.perf_counter() - t0:.1f} s")
+    step_bytes = sum(w.bytes for w in wls)
+    step_rows = sum(w.R for w in wls)
+
+    def step():
+        for w in wls:
+            w.run()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    K = args.steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in wls] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        for w, (a, b) in zip(wls, evs[k]):
+            a.record()
+            w.run()
+            b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    log(f"timed {K} steps: {ms_per_step:.3f} ms/step")
+
+    per = {}
+    for i, w in enumerate(wls):
+        us = np.array([evs[k][i][0].elapsed_time(evs[k][i][1]) * 1e3 for k in range(K)])
+        med, mean = float(np.median(us)), float(us.mean())
+        per[w.name] = {
+            "rows": w.R, "cols": w.C, "algo_bytes": w.bytes,
+            "variant": {"threads": w.variant[0], "vecs": w.variant[1], "elems_per_vec": w.variant[2]},
+            "median_us": round(med, 3), "mean_us": round(mean, 3),
+            "p10_us": round(float(np.percentile(us, 10)), 3),
+            "p90_us": round(float(np.percentile(us, 90)), 3),
+            "gbps": round(w.bytes / (med * 1e-6) / 1e9, 1),
+            "pct_peak": round(100 * w.bytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+            "rows_per_s": round(w.R / (med * 1e-6), 1),
+            "input_sha256": w.w.digest()[:16],
+        }
+
+    ceiling = copy_ceiling(torch, fr, dev)
+    log(f"copy ceiling {ceiling:.0f} GB/s")
+    dom = per[DOMINANT]
+    achieved = dom["algo_bytes"] / (dom["mean_us"] * 1e-6) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "one launch of each row-reduction workload per step: softmax fp32 64x1000, "
+                        "LayerNorm fp32 4096x1024, softmax bf16 16384x4096, residual-add+RMSNorm "
+                        "bf16 8192x8192, softmax cross-entropy fwd+bwd fp32 4096x50257",
+            "bytes_per_step": step_bytes,
+            "rows_per_step": step_rows,
+            "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
+            "pct_of_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            "copy_ceiling_gbps": round(ceiling, 1),
+            "storage": "fp32 and bf16 as listed; arithmetic fp32",
+            "seeds": [w.w.seed for w in wls],
+        },
+        "per_workload": per,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"xent_kernel<float,{dom['variant']['threads']},{dom['variant']['vecs']},"
+                      f"{dom['variant']['elems_per_vec']}> (softmax cross-entropy 4096x50257)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wls)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

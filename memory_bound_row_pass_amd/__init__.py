@@ -26,7 +26,9 @@ __all__ = [
 F32, BF16 = 0, 1
 OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
 FR_MAX_COLS = 65536
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfusedrow.so")
+# FUSEDROW_LIB may name an alternative build of the same library (A/B runs).
+LIB_PATH = os.environ.get("FUSEDROW_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfusedrow.so")
 
 
 class FusedRowError(RuntimeError):

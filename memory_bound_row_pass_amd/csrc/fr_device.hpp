@@ -81,7 +81,24 @@ __device__ __forceinline__ float exp_acc(float t) {
 
 // --------------------------------------------------------------- global access
 // Inputs are streamed once: non-temporal loads and stores keep them from
-// displacing other data in L2 / MALL.
+// displacing other data in L2 / MALL. FR_NT_LOAD / FR_NT_STORE (default 1)
+// select the hint at build time.
+#ifndef FR_NT_LOAD
+#define FR_NT_LOAD 1
+#endif
+#ifndef FR_NT_STORE
+#define FR_NT_STORE 1
+#endif
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+  if constexpr (FR_NT_LOAD) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V v, V* p) {
+  if constexpr (FR_NT_STORE) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 template <typename T, int EPV>
 struct Vec;  // load/store EPV consecutive elements as fp32
@@ -89,12 +106,12 @@ struct Vec;  // load/store EPV consecutive elements as fp32
 template <>
 struct Vec<float, 4> {
   static __device__ __forceinline__ void load(const float* p, float* v) {
-    f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    f32x4 r = ld_stream(reinterpret_cast<const f32x4*>(p));
     v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
     f32x4 r = {v[0], v[1], v[2], v[3]};
-    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+    st_stream(r, reinterpret_cast<f32x4*>(p));
   }
 };
 
@@ -113,7 +130,7 @@ struct Vec<float, 8> {  // output side of bf16 -> f32 (two 16-byte stores)
 template <>
 struct Vec<bf16_t, 8> {
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    u32x4 r = ld_stream(reinterpret_cast<const u32x4*>(p));
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
     v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
     v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
@@ -122,41 +139,41 @@ struct Vec<bf16_t, 8> {
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
     u32x4 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+    st_stream(r, reinterpret_cast<u32x4*>(p));
   }
 };
 
 template <>
 struct Vec<bf16_t, 4> {  // output side of f32 -> bf16 (one 8-byte store)
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    u32x2 r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    u32x2 r = ld_stream(reinterpret_cast<const u32x2*>(p));
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
     v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
   }
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
     u32x2 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+    st_stream(r, reinterpret_cast<u32x2*>(p));
   }
 };
 
 template <>
 struct Vec<float, 1> {
   static __device__ __forceinline__ void load(const float* p, float* v) {
-    v[0] = __builtin_nontemporal_load(p);
+    v[0] = ld_stream(p);
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
-    __builtin_nontemporal_store(v[0], p);
+    st_stream(v[0], p);
   }
 };
 
 template <>
 struct Vec<bf16_t, 1> {
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    uint16_t u = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+    uint16_t u = ld_stream(reinterpret_cast<const uint16_t*>(p));
     v[0] = __uint_as_float((uint32_t)u << 16);
   }
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
-    __builtin_nontemporal_store(to_bf16(v[0]), reinterpret_cast<uint16_t*>(p));
+    st_stream(to_bf16(v[0]), reinterpret_cast<uint16_t*>(p));
   }
 };
 
@@ -192,12 +209,19 @@ __device__ __forceinline__ void store1(bf16_t* p, float v) { p->u = to_bf16(v); 
 
 // ----------------------------------------------------------------- row layout
 // A row of `cols` elements starting at `row_ptr` is cut into
-//   head: elements before the first 16-byte boundary (EPV > 1 only),
-//   body: nvec aligned chunks of EPV elements,
+//   head: the elements before the first kHeadAlign-element boundary
+//         (EPV > 1 only; 128 bytes for fp32, 64 for bf16),
+//   body: nvec chunks of EPV elements (16 bytes), starting on that boundary,
 //   tail: what is left (< EPV elements).
+// Starting the body on a cache-line boundary makes every wavefront access
+// whole lines; rows of odd width would otherwise split a line between
+// neighbouring wavefronts on every access.
 // Lane t of a row-owner of T lanes holds body chunks t, t+T, t+2T, ...
 // (slot i -> chunk i*T + t) and at most one head/tail element in its extra
-// slot: lanes [0, head) take the head, lanes [head, head+tail) the tail.
+// slot: lanes [0, head) take the head, lanes [head, head+tail) the tail
+// (head + tail <= 31 + 7 < 64 <= T).
+constexpr int kHeadAlign = 32;  // elements
+
 template <int EPV>
 struct RowGeom {
   int head, nvec, tail;
@@ -206,8 +230,9 @@ struct RowGeom {
     if constexpr (EPV == 1) {
       head = 0; nvec = cols; tail = 0;
     } else {
-      const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(row_ptr) / sizeof(T)) & (EPV - 1);
-      int h = (int)((EPV - mis) & (EPV - 1));
+      const uint32_t mis =
+          (uint32_t)(reinterpret_cast<uintptr_t>(row_ptr) / sizeof(T)) & (kHeadAlign - 1);
+      const int h = (int)((kHeadAlign - mis) & (kHeadAlign - 1));
       head = h < cols ? h : cols;
       nvec = (cols - head) / EPV;
       tail = cols - head - nvec * EPV;
@@ -223,19 +248,17 @@ struct RowGeom {
 };
 
 // ------------------------------------------------------- row chunk load/store
-// `full` rows (every slot of every lane holds a chunk) use one per-lane base
-// address and compile-time slot offsets, with no masking. Ragged rows clamp
-// the chunk index into the row so every load stays in bounds, then overwrite
-// the slots past the row end with `fill`; their stores are masked.
+// Slot i of lane t holds chunk i*T + t. Every load is issued: a slot past
+// the end of the row re-reads the row's last chunk (always in bounds) and is
+// then overwritten with `fill`; stores of such slots are masked off. A single
+// code path keeps the register allocation tight (rows that fill every slot
+// simply never mask).
 template <typename Ts, int T, int NV, int EPV>
-__device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV>& g, int tid, bool full,
+__device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV>& g, int tid,
                                             float (&v)[NV][EPV], float fill) {
-  const Ts* base = row + g.head;                    // uniform
-  const uint32_t lo = (uint32_t)tid * EPV;          // lane offset, elements
-  if (full) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) Vec<Ts, EPV>::load((base + i * T * EPV) + lo, v[i]);
-  } else if (g.nvec > 0) {
+  if (g.nvec > 0) {
+    const Ts* base = row + g.head;                  // uniform
+    const uint32_t lo = (uint32_t)tid * EPV;        // lane offset, elements
     const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -258,18 +281,13 @@ __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV>& g
 }
 
 template <typename Ts, int T, int NV, int EPV>
-__device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV>& g, int tid, bool full,
+__device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV>& g, int tid,
                                              const float (&v)[NV][EPV]) {
   Ts* base = row + g.head;
   const uint32_t lo = (uint32_t)tid * EPV;
-  if (full) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) Vec<Ts, EPV>::store((base + i * T * EPV) + lo, v[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (i * T + tid < g.nvec) Vec<Ts, EPV>::store((base + i * T * EPV) + lo, v[i]);
-  }
+  for (int i = 0; i < NV; ++i)
+    if (i * T + tid < g.nvec) Vec<Ts, EPV>::store(base + ((uint32_t)(i * T * EPV) + lo), v[i]);
 }
 
 // Per-column parameters of chunk slot i of this lane (aligned rows only,

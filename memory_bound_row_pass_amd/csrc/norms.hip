@@ -45,7 +45,7 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
     const bool full = g.nvec == T * NV;
 
     float v[NV][EPV];
-    load_chunks<Ts, T, NV, EPV>(xr, g, tid, full, v, 0.f);
+    load_chunks<Ts, T, NV, EPV>(xr, g, tid, v, 0.f);
     const int ec = g.extra_col(tid);
     const float xe = ec >= 0 ? load1(xr + ec) : 0.f;
 
@@ -94,7 +94,7 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
 #pragma unroll
       for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf((v[i][k] - mu) * rs, ga[k], be[k]);
     }
-    store_chunks<Ts, T, NV, EPV>(yr, g, tid, full, v);
+    store_chunks<Ts, T, NV, EPV>(yr, g, tid, v);
     if (ec >= 0) store1(yr + ec, __builtin_fmaf((xe - mu) * rs, load1(gamma + ec), load1(beta + ec)));
     if (wave == 0 && lane == 0) {
       if (mean) mean[row] = mu;
@@ -125,8 +125,8 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
     const bool full = g.nvec == T * NV;
 
     float h[NV][EPV], r[NV][EPV];
-    load_chunks<Ts, T, NV, EPV>(x + off, g, tid, full, h, 0.f);
-    load_chunks<Ts, T, NV, EPV>(res + off, g, tid, full, r, 0.f);
+    load_chunks<Ts, T, NV, EPV>(x + off, g, tid, h, 0.f);
+    load_chunks<Ts, T, NV, EPV>(res + off, g, tid, r, 0.f);
     const int ec = g.extra_col(tid);
     float he = ec >= 0 ? load1(x + off + ec) + load1(res + off + ec) : 0.f;
 #pragma unroll
@@ -134,7 +134,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
 #pragma unroll
       for (int k = 0; k < EPV; ++k) h[i][k] += r[i][k];
     if (res_out) {  // updated residual, rounded once at the store
-      store_chunks<Ts, T, NV, EPV>(res_out + off, g, tid, full, h);
+      store_chunks<Ts, T, NV, EPV>(res_out + off, g, tid, h);
       if (ec >= 0) store1(res_out + off + ec, he);
     }
 
@@ -158,7 +158,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
 #pragma unroll
       for (int k = 0; k < EPV; ++k) h[i][k] = h[i][k] * rs * wt[k];
     }
-    store_chunks<Ts, T, NV, EPV>(y + off, g, tid, full, h);
+    store_chunks<Ts, T, NV, EPV>(y + off, g, tid, h);
     if (ec >= 0) store1(y + off + ec, he * rs * load1(w + ec));
   }
 }
@@ -211,7 +211,7 @@ static const RmsNormVariant kRnF32[] = {
     FR_RN(float, 1024, 64, 1, 2)};
 static const RmsNormVariant kRnBf16[] = {
     FR_RN(bf16_t, 64, 1, 8, 8),  FR_RN(bf16_t, 64, 2, 8, 8),   FR_RN(bf16_t, 64, 4, 8, 4),
-    FR_RN(bf16_t, 256, 2, 8, 8), FR_RN(bf16_t, 256, 4, 8, 4),  FR_RN(bf16_t, 512, 2, 8, 8),
+    FR_RN(bf16_t, 256, 2, 8, 8), FR_RN(bf16_t, 512, 2, 8, 8),  FR_RN(bf16_t, 256, 4, 8, 4),
     FR_RN(bf16_t, 512, 4, 8, 4), FR_RN(bf16_t, 1024, 1, 8, 8), FR_RN(bf16_t, 1024, 4, 8, 4),
     FR_RN(bf16_t, 1024, 8, 8, 2), FR_RN(bf16_t, 64, 16, 1, 4), FR_RN(bf16_t, 256, 16, 1, 4),
     FR_RN(bf16_t, 1024, 16, 1, 4), FR_RN(bf16_t, 1024, 64, 1, 2)};

@@ -7,8 +7,8 @@
 //             workgroup, no barrier), 256/512/1024 = one workgroup per row
 //   NV        128-bit chunks (or scalars when EPV == 1) per lane
 //   EPV       elements per chunk: 16 / sizeof(Tin), or 1 for the scalar path
-// bf16 outputs keep the exponentials in registers (base-2, biased); fp32
-// outputs keep x and re-evaluate the compensated exponential at the store.
+// The exponentials stay in registers between the reduction and the store:
+// base-2 with a bias for bf16 outputs, compensated natural for fp32 outputs.
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
@@ -37,14 +37,13 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_
     Tout* yr = y + row * cols;
     const RowGeom<EPV> g(xr, cols);
 
-    const bool full = g.nvec == T * NV;
     float v[NV][EPV];
-    load_chunks<Tin, T, NV, EPV>(xr, g, tid, full, v, kNegInf);
+    load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
     const int ec = g.extra_col(tid);
     float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
 
     const float m = lane_max<NV, EPV>(v, xe);
-    MaxSumState st = kLog2 ? lane_exp_log2<NV, EPV>(v, xe, m) : lane_sum_nat<NV, EPV>(v, xe, m);
+    MaxSumState st = kLog2 ? lane_exp_log2<NV, EPV>(v, xe, m) : lane_exp_nat<NV, EPV>(v, xe, m);
     st = wave_reduce(st, Merge{});
     if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
 
@@ -56,10 +55,15 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_
         for (int k = 0; k < EPV; ++k) v[i][k] = apply_scale(v[i][k], sc);
       xe = apply_scale(xe, sc);
     } else {
-      probs_nat<NV, EPV>(v, xe, st.m, st.s);
+      const float f = nat_scale(m, st.m, st.s);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) v[i][k] *= f;
+      xe *= f;
     }
 
-    store_chunks<Tout, T, NV, EPV>(yr, g, tid, full, v);
+    store_chunks<Tout, T, NV, EPV>(yr, g, tid, v);
     if (ec >= 0) store1(yr + ec, xe);
   }
 }
@@ -87,7 +91,8 @@ static const SoftmaxVariant kSmF32F32[] = {
     FR_SM(float, float, 64, 4, 4, 8),     FR_SM(float, float, 64, 8, 4, 6),
     FR_SM(float, float, 64, 16, 4, 4),    FR_SM(float, float, 256, 8, 4, 6),
     FR_SM(float, float, 512, 8, 4, 6),    FR_SM(float, float, 1024, 8, 4, 4),
-    FR_SM(float, float, 1024, 13, 4, 4),
+    FR_SM(float, float, 1024, 13, 4, 4),  FR_SM(float, float, 512, 25, 4, 4),
+    FR_SM(float, float, 256, 50, 4, 2),
     FR_SM(float, float, 1024, 16, 4, 4),  FR_SM_SCALAR(float, float)};
 static const SoftmaxVariant kSmBf16Bf16[] = {
     FR_SM(bf16_t, bf16_t, 64, 1, 8, 8),   FR_SM(bf16_t, bf16_t, 64, 2, 8, 8),

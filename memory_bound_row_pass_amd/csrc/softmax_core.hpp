@@ -10,11 +10,10 @@
 //   3. the partial states are combined with the online-normaliser merge,
 //      across the wavefront with DPP and across waves through LDS -> (M, S),
 //   4. each lane writes p_j = exp(x_j - M) / S (the only write).
-// Two ways to produce step 4 from registers:
-//   * bf16 outputs keep e_j = exp(x_j - m_l) from step 2 in place of x_j and
-//     rescale by exp(m_l - M) / S (one exponential per element);
-//   * fp32 outputs keep x_j and evaluate exp(x_j - M) again, which needs half
-//     the registers and rounds each p_j from a single exponential.
+// e_j = exp(x_j - m_l) from step 2 replaces x_j in the registers and step 4
+// rescales it by exp(m_l - M) / S: one exponential per element. bf16 outputs
+// use base-2 hardware exponentials with a bias that keeps bf16 subnormal
+// results exact; fp32 outputs use a compensated exponential.
 #pragma once
 
 #include "fr_device.hpp"
@@ -43,38 +42,23 @@ __device__ __forceinline__ float lane_max(const float (&v)[NV][EPV], float xe) {
 }
 
 // ---------------------------------------------------------------- bf16 path
-// e_j = 2^((x_j - m_l)*log2e + 64), computed as 2^(x_j*log2e + K) with
-// K = 64 - m_l*log2e: e_j lies in (0, 2^64] and is normal down to
+// e_j = 2^((x_j - m_l)*log2e + 64) lies in (0, 2^64] and is normal down to
 // x_j - m_l = -131, which covers every value that can round to a non-zero
-// bf16 (p >= 2^-134). The lane state (m_l, s_l) stays in natural units.
-// When m_l*log2e would overflow (|m_l| >= 2e38) the wave takes the slower
-// (x_j - m_l)*log2e + 64 form.
+// bf16 (p >= 2^-134). Forming x_j - m_l first keeps the argument finite for
+// any finite input (m_l*log2e alone overflows for |m_l| > 2.3e38). The lane
+// state (m_l, s_l) stays in natural units.
 template <int NV, int EPV>
 __device__ __forceinline__ MaxSumState lane_exp_log2(float (&v)[NV][EPV], float& xe, float m) {
-  const bool empty = (m == kNegInf);
-  const bool huge = !empty && __builtin_fabsf(m) >= 2.0e38f && __builtin_fabsf(m) != __builtin_inff();
+  const float mr = (m == kNegInf) ? 0.f : m;
   float s0 = 0.f, s1 = 0.f;
-  if (!__any(huge)) {
-    const float K = empty ? 0.f : 64.f - m * kLog2e;
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+  for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        v[i][k] = exp2_hw(__builtin_fmaf(v[i][k], kLog2e, K));
-        if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
-      }
-    xe = exp2_hw(__builtin_fmaf(xe, kLog2e, K));
-  } else {
-    const float mr = empty ? 0.f : m;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, 64.f));
-        if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
-      }
-    xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, 64.f));
-  }
+    for (int k = 0; k < EPV; ++k) {
+      v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, 64.f));
+      if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
+    }
+  xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, 64.f));
   return {m, (s0 + s1) + xe};
 }
 
@@ -102,30 +86,28 @@ __device__ __forceinline__ float apply_scale(float e, const Log2Scale& s) {
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Natural units with the compensated exponential; x_j is left in place.
+// Natural units with the compensated exponential: e_j = exp(x_j - m_l)
+// replaces x_j in place; p_j = e_j * exp(m_l - M) / S at the store. The two
+// compensated exponentials each contribute about one ulp, so p_j stays well
+// inside 1e-5 relative for results above the fp32 normal range.
 template <int NV, int EPV>
-__device__ __forceinline__ MaxSumState lane_sum_nat(const float (&v)[NV][EPV], float xe, float m) {
+__device__ __forceinline__ MaxSumState lane_exp_nat(float (&v)[NV][EPV], float& xe, float m) {
   const float mr = (m == kNegInf) ? 0.f : m;
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int k = 0; k < EPV; ++k) {
-      const float e = exp_acc(v[i][k] - mr);
-      if (k & 1) s1 += e; else s0 += e;
+      v[i][k] = exp_acc(v[i][k] - mr);
+      if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
     }
-  return {m, (s0 + s1) + exp_acc(xe - mr)};
+  xe = exp_acc(xe - mr);
+  return {m, (s0 + s1) + xe};
 }
 
-// p = exp(x - M) / S from the kept x.
-template <int NV, int EPV>
-__device__ __forceinline__ void probs_nat(float (&v)[NV][EPV], float& xe, float M, float S) {
-  const float inv = 1.f / S;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int k = 0; k < EPV; ++k) v[i][k] = exp_acc(v[i][k] - M) * inv;
-  xe = exp_acc(xe - M) * inv;
+// Lane factor exp(m_l - M) / S: 0 for an empty lane, NaN for an all -inf row.
+__device__ __forceinline__ float nat_scale(float m, float M, float S) {
+  return exp_acc(m - M) / S;
 }
 
 }  // namespace fr

@@ -4,46 +4,27 @@
 // Module 3: cross-entropy loss).
 //
 // Per row: the online-softmax state (M, S) of the logits (as in softmax.hip,
-// fp32 path), then
+// fp32 path, exponentials kept in registers), then
 //   loss    = M + ln S - x[label]
 //   grad_j  = exp(x_j - M) / S - [j == label]
 //   argmax  = smallest j with x_j == M (optional)
-// The label logit is taken from the registers of the lane that loaded it, by
-// the wavefront that owns that column only; the one-hot subtraction is done
-// by the same wavefront before the store. A label outside [0, cols) gives a
-// NaN loss and an unmodified softmax row.
+// The lane that owns the label column reads the label logit, writes the
+// loss, and overwrites its stored p with p - 1. A label outside [0, cols)
+// gives a NaN loss and an unmodified softmax row.
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
 namespace fr {
 
-// Where the label column sits in the register layout of the row owner.
-struct LabelPos {
-  bool valid;   // 0 <= label < cols
-  bool extra;   // held in the extra (head/tail) slot
-  int lane;     // owning lane within the row owner (0..T-1)
-  int slot;     // chunk slot (body) ...
-  int comp;     // ... and component
-};
-
+// Lane of the row owner that holds column `c` (0 <= c < cols): a head or
+// tail column sits in the extra slot of lane c or head + (c - body_end); a
+// body column in chunk (c - head) / EPV, held by lane chunk % T.
 template <int T, int EPV>
-__device__ __forceinline__ LabelPos locate_label(int label, int cols, const RowGeom<EPV>& g) {
-  LabelPos p{false, false, 0, 0, 0};
-  if (label < 0 || label >= cols) return p;
-  p.valid = true;
+__device__ __forceinline__ int owner_lane(int c, const RowGeom<EPV>& g) {
   const int body_end = g.head + g.nvec * EPV;
-  if (label < g.head) {
-    p.extra = true; p.lane = label;
-  } else if (label >= body_end) {
-    p.extra = true; p.lane = g.head + (label - body_end);
-  } else {
-    const int q = label - g.head;
-    const int c = q / EPV;
-    p.comp = q - c * EPV;
-    p.lane = c % T;
-    p.slot = c / T;
-  }
-  return p;
+  if (c < g.head) return c;
+  if (c >= body_end) return g.head + (c - body_end);
+  return ((c - g.head) / EPV) % T;
 }
 
 template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX>
@@ -69,39 +50,24 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     const Tin* xr = x + row * cols;
     Tin* gr = grad + row * cols;
     const RowGeom<EPV> g(xr, cols);
-    const bool full = g.nvec == T * NV;
 
     float v[NV][EPV];
-    load_chunks<Tin, T, NV, EPV>(xr, g, tid, full, v, kNegInf);
+    load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
     const int ec = g.extra_col(tid);
     float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
 
+    // The label column is handled by the one lane that owns it (the lane of
+    // the row owner that loads that column). It reads the label logit with
+    // its own load, before any of its stores: in-place calls (grad == logits)
+    // stay correct because a lane's accesses to one address keep their order.
     const int label = __builtin_amdgcn_readfirstlane(labels[row]);
-    const LabelPos lp = locate_label<T, EPV>(label, cols, g);
-    const bool owner_wave = lp.valid && (lp.lane >> 6) == wave;
-
-    // label logit, read out of the owner lane's registers
+    const bool valid = label >= 0 && label < cols;
+    const bool label_lane = valid && owner_lane<T, EPV>(label, g) == tid;
     float x_label = 0.f;
-    if (owner_wave) {
-      float mine = xe;
-      if (!lp.extra) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-#pragma unroll
-          for (int k = 0; k < EPV; ++k)
-            if (i == lp.slot && k == lp.comp) mine = v[i][k];
-      }
-      x_label = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine),
-                                                                     lp.lane & 63));
-    }
+    if (label_lane) x_label = load1(xr + label);
 
     const float m = lane_max<NV, EPV>(v, xe);
     State st;
-    {
-      const MaxSumState ms = lane_sum_nat<NV, EPV>(v, xe, m);
-      st.m = ms.m;
-      st.s = ms.s;
-    }
     if constexpr (ARGMAX) {
       // smallest column of this lane holding its maximum
       float best = 3.0e38f;
@@ -115,32 +81,35 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
       if (ec >= 0 && xe == m && (float)ec < best) best = (float)ec;
       st.idx = best;
     }
+    {
+      const MaxSumState ms = lane_exp_nat<NV, EPV>(v, xe, m);  // e_j replaces x_j
+      st.m = ms.m;
+      st.s = ms.s;
+    }
     st = wave_reduce(st, Merge{});
     if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
 
-    probs_nat<NV, EPV>(v, xe, st.m, st.s);
+    const float f = nat_scale(m, st.m, st.s);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] *= f;
+    xe *= f;
+    store_chunks<Tin, T, NV, EPV>(gr, g, tid, v);
+    if (ec >= 0) store1(gr + ec, xe);
 
-    if (owner_wave) {
-      const bool me = lane == (lp.lane & 63);
-      if (lp.extra) {
-        if (me) xe -= 1.f;
-      } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-#pragma unroll
-          for (int k = 0; k < EPV; ++k)
-            if (i == lp.slot && k == lp.comp && me) v[i][k] -= 1.f;
-      }
-      if (lane == 0) loss[row] = st.m + logf(st.s) - x_label;
-    } else if (!lp.valid && wave == 0 && lane == 0) {
+    if (label_lane) {
+      // overwrite the label element with p - 1 (after this lane's own store
+      // of p to the same address), and write the loss
+      const float p = exp_acc(x_label - st.m) / st.s;
+      store1(gr + label, p - 1.f);
+      loss[row] = st.m + logf(st.s) - x_label;
+    } else if (!valid && tid == 0) {
       loss[row] = __builtin_nanf("");
     }
     if constexpr (ARGMAX) {
-      if (wave == 0 && lane == 0) argmax[row] = (int32_t)st.idx;
+      if (tid == 0) argmax[row] = (int32_t)st.idx;
     }
-
-    store_chunks<Tin, T, NV, EPV>(gr, g, tid, full, v);
-    if (ec >= 0) store1(gr + ec, xe);
   }
 }
 
@@ -161,8 +130,9 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   {FR_XE(64, 1, 4, 8, AM),     FR_XE(64, 2, 4, 8, AM),     FR_XE(64, 4, 4, 8, AM),        \
    FR_XE(64, 8, 4, 6, AM),     FR_XE(64, 16, 4, 4, AM),    FR_XE(256, 8, 4, 6, AM),       \
    FR_XE(512, 8, 4, 6, AM),    FR_XE(1024, 8, 4, 4, AM),   FR_XE(1024, 13, 4, 4, AM),     \
-   FR_XE(1024, 16, 4, 4, AM),  FR_XE(64, 16, 1, 4, AM),    FR_XE(256, 16, 1, 4, AM),      \
-   FR_XE(1024, 16, 1, 4, AM),  FR_XE(1024, 64, 1, 4, AM)}
+   FR_XE(512, 25, 4, 4, AM),   FR_XE(256, 50, 4, 2, AM),   FR_XE(1024, 16, 4, 4, AM),     \
+   FR_XE(64, 16, 1, 4, AM),    FR_XE(256, 16, 1, 4, AM),   FR_XE(1024, 16, 1, 4, AM),     \
+   FR_XE(1024, 64, 1, 4, AM)}
 
 static const XentVariant kXe[] = FR_XE_TABLE(false);
 static const XentVariant kXeArgmax[] = FR_XE_TABLE(true);

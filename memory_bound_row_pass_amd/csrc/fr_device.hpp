@@ -290,23 +290,17 @@ __device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV>& g, int
     if (i * T + tid < g.nvec) Vec<Ts, EPV>::store(base + ((uint32_t)(i * T * EPV) + lo), v[i]);
 }
 
-// Per-column parameters of chunk slot i of this lane (aligned rows only,
-// where head == 0 and the columns match the parameter vector). Slots past
-// the row end read the last chunk (their results are not stored).
+// Per-column parameters of chunk slot i of this lane (rows on the 128-bit
+// path share their phase with the parameter vectors, so chunk columns map
+// to aligned parameter chunks). Only valid when g.nvec > 0 (callers test it
+// once, uniformly); slots past the row end read the last chunk.
 template <typename Ts, int T, int EPV>
-__device__ __forceinline__ void load_param_slot(const Ts* par, const RowGeom<EPV>& g, int tid, bool full,
-                                                int i, float* w) {
+__device__ __forceinline__ void load_param_slot(const Ts* par, const RowGeom<EPV>& g, int tid, int i,
+                                                float* w) {
+  const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
   uint32_t o = (uint32_t)(i * T * EPV) + (uint32_t)tid * EPV;
-  if (!full) {
-    if (g.nvec <= 0) {
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) w[k] = 0.f;
-      return;
-    }
-    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
-    o = o < last ? o : last;
-  }
-  load_param<Ts, EPV>(par + g.head + o, w);
+  o = o < last ? o : last;
+  load_param<Ts, EPV>((par + g.head) + o, w);
 }
 
 // ------------------------------------------------------- wavefront reduction

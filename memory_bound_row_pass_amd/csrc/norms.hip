@@ -86,15 +86,17 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
     const float mu = st.mu;
     const float rs = 1.f / __builtin_sqrtf(st.m2 / (float)cols + eps);
     // per-column parameters are re-read by every row: cache hits
+    if (g.nvec > 0) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float ga[EPV], be[EPV];
-      load_param_slot<Ts, T, EPV>(gamma, g, tid, full, i, ga);
-      load_param_slot<Ts, T, EPV>(beta, g, tid, full, i, be);
+      for (int i = 0; i < NV; ++i) {
+        float ga[EPV], be[EPV];
+        load_param_slot<Ts, T, EPV>(gamma, g, tid, i, ga);
+        load_param_slot<Ts, T, EPV>(beta, g, tid, i, be);
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf((v[i][k] - mu) * rs, ga[k], be[k]);
+        for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf((v[i][k] - mu) * rs, ga[k], be[k]);
+      }
+      store_chunks<Ts, T, NV, EPV>(yr, g, tid, v);
     }
-    store_chunks<Ts, T, NV, EPV>(yr, g, tid, v);
     if (ec >= 0) store1(yr + ec, __builtin_fmaf((xe - mu) * rs, load1(gamma + ec), load1(beta + ec)));
     if (wave == 0 && lane == 0) {
       if (mean) mean[row] = mu;
@@ -122,7 +124,6 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
        row += (int64_t)gridDim.x * RPB, ++it) {
     const int64_t off = row * cols;
     const RowGeom<EPV> g(x + off, cols);
-    const bool full = g.nvec == T * NV;
 
     float h[NV][EPV], r[NV][EPV];
     load_chunks<Ts, T, NV, EPV>(x + off, g, tid, h, 0.f);
@@ -151,14 +152,16 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
     if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
 
     const float rs = 1.f / __builtin_sqrtf(st.s / (float)cols + eps);
+    if (g.nvec > 0) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float wt[EPV];
-      load_param_slot<Ts, T, EPV>(w, g, tid, full, i, wt);
+      for (int i = 0; i < NV; ++i) {
+        float wt[EPV];
+        load_param_slot<Ts, T, EPV>(w, g, tid, i, wt);
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) h[i][k] = h[i][k] * rs * wt[k];
+        for (int k = 0; k < EPV; ++k) h[i][k] = h[i][k] * rs * wt[k];
+      }
+      store_chunks<Ts, T, NV, EPV>(y + off, g, tid, h);
     }
-    store_chunks<Ts, T, NV, EPV>(y + off, g, tid, h);
     if (ec >= 0) store1(y + off + ec, he * rs * load1(w + ec));
   }
 }
@@ -193,8 +196,8 @@ static hipError_t launch_rmsnorm(const void* x, const void* res, const void* w, 
 #define FR_RN(TS, T, NV, EPV, OCC) {T, NV, EPV, &launch_rmsnorm<TS, T, NV, EPV, OCC>}
 
 static const LayerNormVariant kLnF32[] = {
-    FR_LN(float, 64, 1, 4, 8),   FR_LN(float, 64, 2, 4, 8),    FR_LN(float, 64, 4, 4, 8),
-    FR_LN(float, 64, 8, 4, 4),   FR_LN(float, 256, 4, 4, 8),   FR_LN(float, 256, 8, 4, 4),
+    FR_LN(float, 64, 1, 4, 8),   FR_LN(float, 64, 2, 4, 8),    FR_LN(float, 64, 4, 4, 6),
+    FR_LN(float, 64, 8, 4, 4),   FR_LN(float, 256, 4, 4, 6),   FR_LN(float, 256, 8, 4, 4),
     FR_LN(float, 512, 8, 4, 4),  FR_LN(float, 1024, 8, 4, 4),  FR_LN(float, 1024, 16, 4, 2),
     FR_LN(float, 64, 16, 1, 4),  FR_LN(float, 256, 16, 1, 4),  FR_LN(float, 1024, 16, 1, 4),
     FR_LN(float, 1024, 64, 1, 2)};

@@ -11,7 +11,9 @@ step moves 2.49 GB, so by the time a workload's buffers come round again the
 
 value = algorithmic bytes of one step (each input element read once, each
 output element written once) / wall time of one step, in GB/s; per-launch
-durations come from HIP events recorded on the stream the kernels run on.
+durations come from a second pass with HIP events recorded around each launch
+on the stream the kernels run on. With --graph the timed steps replay one
+captured HIP graph of the five launches.
 
 Printed: ONE JSON line (rank 0), with per-workload figures, the roofline of
 the dominant kernel (the cross-entropy launch), the streaming-copy ceiling,
@@ -176,6 +178,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as one captured HIP graph (the launches are capture-safe)")
     ap.add_argument("--quiet", action="store_true", help="no progress lines on stderr")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -208,25 +212,46 @@ def main():
         for w in wls:
             w.run()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
+    graph = None
+    if args.graph:
+        # the five launches of one step captured once and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run_step = graph.replay
+    else:
+        run_step = step
 
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done ({'graph replay' if graph else 'eager launches'})")
+
+    # timed region: exactly K steps, nothing else on the stream
     K = args.steps
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in wls] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(K):
+        run_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    log(f"timed {K} steps: {ms_per_step:.3f} ms/step")
+
+    # per-launch durations: a second pass with HIP events around each launch
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in wls] for _ in range(K)]
     for k in range(K):
         for w, (a, b) in zip(wls, evs[k]):
             a.record()
             w.run()
             b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / K
-    log(f"timed {K} steps: {ms_per_step:.3f} ms/step")
 
     per = {}
     for i, w in enumerate(wls):
@@ -273,6 +298,7 @@ def main():
             "copy_ceiling_gbps": round(ceiling, 1),
             "storage": "fp32 and bf16 as listed; arithmetic fp32",
             "seeds": [w.w.seed for w in wls],
+            "launch": "hip graph replay of the five launches" if graph else "eager launches",
         },
         "per_workload": per,
         "roofline": {

@@ -512,3 +512,52 @@ def test_rows_zero_is_noop():
     loss, grad = fr.softmax_xent(torch.empty(0, 7, device=DEV),
                                  torch.empty(0, dtype=torch.int32, device=DEV))
     assert loss.numel() == 0 and grad.numel() == 0
+
+
+# ---------------------------------------------------------- graph capture
+
+def test_graph_capture_replays_match_eager():
+    # every entry point allocates nothing and never synchronises, so a step of
+    # all four ops can be captured; each replay (with eager work and
+    # synchronisations in between) must reproduce the eager result exactly
+    ws = workloads.make("softmax_bf16", rows=256)
+    wl = workloads.make("layernorm_f32", rows=256)
+    wr = workloads.make("add_rmsnorm_bf16", rows=64)
+    wx = workloads.make("xent_f32", rows=32)
+    xs = to_dev(ws["x"]); ys = torch.empty_like(xs)
+    xl, gl, bl = to_dev(wl["x"]), to_dev(wl["gamma"]), to_dev(wl["beta"])
+    yl = torch.empty_like(xl); ml = torch.empty(256, device=DEV); rl = torch.empty(256, device=DEV)
+    xr, rr, wt = to_dev(wr["x"]), to_dev(wr["residual"]), to_dev(wr["weight"])
+    yr, ror = torch.empty_like(xr), torch.empty_like(xr)
+    xx, lab = to_dev(wx["logits"]), to_dev(wx["labels"])
+    loss, grad = torch.empty(32, device=DEV), torch.empty_like(xx)
+
+    def step():
+        fr.fr_softmax_fwd(xs, ys)
+        fr.fr_layernorm_fwd(xl, gl, bl, yl, ml, rl, wl.eps)
+        fr.fr_add_rmsnorm_fwd(xr, rr, wt, yr, ror, wr.eps)
+        fr.fr_softmax_xent_fwd_bwd(xx, lab, loss, grad)
+
+    outs = (ys, yl, ml, rl, yr, ror, loss, grad)
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o.view(torch.int32),
+                               e.view(torch.int16) if e.dtype == torch.bfloat16 else e.view(torch.int32)), rep
+    # and the eager result itself is right
+    check_bf16(bf16_bits(ys), ref_bf16(oracle.softmax(ws["x"])), "graph softmax")

@@ -41,6 +41,9 @@ def _load():
         "oracle_layernorm": ([P, P, P, I32, I64, I64, F, P, P, P], None),
         "oracle_add_rmsnorm": ([P, P, P, I32, I64, I64, F, P, P, P], None),
         "oracle_softmax_xent": ([P, I32, P, I64, I64, P, P, P], None),
+        "oracle_softmax_bwd": ([P, P, I32, I64, I64, P], None),
+        "oracle_rmsnorm_bwd": ([P, P, P, I32, I64, I64, F, P, P], None),
+        "oracle_layernorm_bwd": ([P, P, P, P, P, I32, I64, I64, P, P, P], None),
         "oracle_online_softmax_stats": ([P, I64, DP, DP], None),
         "oracle_softmax_stats_merge": ([D, D, D, D, DP, DP], None),
         "oracle_welford": ([P, I64, DP, DP, DP], None),
@@ -146,6 +149,45 @@ def softmax_xent(logits, labels):
     _load().oracle_softmax_xent(_ptr(logits), _dtype_code(logits), _ptr(labels), R, C,
                                 _ptr(loss), _ptr(grad), _ptr(am))
     return loss, grad, am
+
+
+def softmax_bwd(p, dy):
+    """dx = p * (dy - <dy, p>) per row, from the stored forward output p."""
+    p, dy = _c(p), _c(dy)
+    if p.dtype != dy.dtype or p.shape != dy.shape:
+        raise TypeError("p and dy share dtype and shape")
+    R, C = p.shape
+    dx = np.empty((R, C), dtype=np.float64)
+    _load().oracle_softmax_bwd(_ptr(p), _ptr(dy), _dtype_code(p), R, C, _ptr(dx))
+    return dx
+
+
+def rmsnorm_bwd(h, dy, weight, eps: float):
+    """Returns (dh[R, C], dw[C]) for y = h * rstd * w (rstd recomputed from h)."""
+    h, dy, weight = _c(h), _c(dy), _c(weight)
+    if not (h.dtype == dy.dtype == weight.dtype):
+        raise TypeError("h, dy and weight share one dtype")
+    R, C = h.shape
+    dh = np.empty((R, C), dtype=np.float64)
+    dw = np.empty(C, dtype=np.float64)
+    _load().oracle_rmsnorm_bwd(_ptr(h), _ptr(dy), _ptr(weight), _dtype_code(h), R, C, float(eps),
+                               _ptr(dh), _ptr(dw))
+    return dh, dw
+
+
+def layernorm_bwd(x, dy, gamma, mean, rstd):
+    """Returns (dx[R, C], dgamma[C], dbeta[C]) at the given per-row mean / rstd."""
+    x, dy, gamma = _c(x), _c(dy), _c(gamma)
+    mean, rstd = _c(mean, np.float64), _c(rstd, np.float64)
+    if not (x.dtype == dy.dtype == gamma.dtype):
+        raise TypeError("x, dy and gamma share one dtype")
+    R, C = x.shape
+    dx = np.empty((R, C), dtype=np.float64)
+    dg = np.empty(C, dtype=np.float64)
+    db = np.empty(C, dtype=np.float64)
+    _load().oracle_layernorm_bwd(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd),
+                                 _dtype_code(x), R, C, _ptr(dx), _ptr(dg), _ptr(db))
+    return dx, dg, db
 
 
 def online_softmax_stats(x: np.ndarray):

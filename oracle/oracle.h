@@ -69,6 +69,28 @@ void oracle_softmax_xent(const void* logits, int dtype, const int32_t* labels,
                          int64_t rows, int64_t cols,
                          double* loss, double* grad, int32_t* argmax);
 
+/* ---- backward of the row operations (vector-Jacobian products) ---- */
+
+/* Softmax backward from the stored forward output p and the upstream
+ * gradient dy: dx_j = p_j * (dy_j - sum_k p_k dy_k). */
+void oracle_softmax_bwd(const void* p, const void* dy, int dtype, int64_t rows, int64_t cols,
+                        double* dx);
+
+/* RMSNorm backward for y = h * r * w, r = 1/sqrt(mean(h^2) + eps), from the
+ * stored h (the updated residual), w and dy:
+ * dh_j = r * (w_j dy_j - h_j r^2 mean_k(dy_k w_k h_k));  dw_j = sum_rows dy_j h_j r.
+ * dw is [cols]. */
+void oracle_rmsnorm_bwd(const void* h, const void* dy, const void* w, int dtype, int64_t rows,
+                        int64_t cols, float eps, double* dh, double* dw);
+
+/* LayerNorm backward for y = n * gamma + beta, n = (x - mean) * rstd, using
+ * the given per-row mean and rstd (as saved by the forward):
+ * g = dy * gamma;  dx_j = rstd * (g_j - mean(g) - n_j mean(g n));
+ * dgamma_j = sum_rows dy_j n_j;  dbeta_j = sum_rows dy_j. */
+void oracle_layernorm_bwd(const void* x, const void* dy, const void* gamma, const double* mean,
+                          const double* rstd, int dtype, int64_t rows, int64_t cols,
+                          double* dx, double* dgamma, double* dbeta);
+
 /* The methods' recurrences, in double, used to pin the definitions above. */
 
 /* Online normaliser: sequential running (max, rescaled sum) over x[0..n). */

@@ -42,7 +42,7 @@ def _load():
         "oracle_add_rmsnorm": ([P, P, P, I32, I64, I64, F, P, P, P], None),
         "oracle_softmax_xent": ([P, I32, P, I64, I64, P, P, P], None),
         "oracle_softmax_bwd": ([P, P, I32, I64, I64, P], None),
-        "oracle_rmsnorm_bwd": ([P, P, P, I32, I64, I64, F, P, P], None),
+        "oracle_rmsnorm_bwd": ([P, P, P, P, I32, I64, I64, F, P, P], None),
         "oracle_layernorm_bwd": ([P, P, P, P, P, I32, I64, I64, P, P, P], None),
         "oracle_online_softmax_stats": ([P, I64, DP, DP], None),
         "oracle_softmax_stats_merge": ([D, D, D, D, DP, DP], None),
@@ -162,16 +162,21 @@ def softmax_bwd(p, dy):
     return dx
 
 
-def rmsnorm_bwd(h, dy, weight, eps: float):
-    """Returns (dh[R, C], dw[C]) for y = h * rstd * w (rstd recomputed from h)."""
+def rmsnorm_bwd(h, dy, weight, eps: float, dres=None):
+    """Returns (dh[R, C], dw[C]) for y = h * rstd * w (rstd recomputed from h);
+    dres, the gradient reaching h through the updated residual, adds to dh."""
     h, dy, weight = _c(h), _c(dy), _c(weight)
     if not (h.dtype == dy.dtype == weight.dtype):
         raise TypeError("h, dy and weight share one dtype")
+    if dres is not None:
+        dres = _c(dres)
+        if dres.dtype != h.dtype or dres.shape != h.shape:
+            raise TypeError("dres shares h's dtype and shape")
     R, C = h.shape
     dh = np.empty((R, C), dtype=np.float64)
     dw = np.empty(C, dtype=np.float64)
-    _load().oracle_rmsnorm_bwd(_ptr(h), _ptr(dy), _ptr(weight), _dtype_code(h), R, C, float(eps),
-                               _ptr(dh), _ptr(dw))
+    _load().oracle_rmsnorm_bwd(_ptr(h), _ptr(dy), None if dres is None else _ptr(dres),
+                               _ptr(weight), _dtype_code(h), R, C, float(eps), _ptr(dh), _ptr(dw))
     return dh, dw
 
 

@@ -194,8 +194,8 @@ void oracle_softmax_bwd(const void* p, const void* dy, int dtype, int64_t rows, 
     }
 }
 
-void oracle_rmsnorm_bwd(const void* h, const void* dy, const void* w, int dtype, int64_t rows,
-                        int64_t cols, float eps, double* dh, double* dw) {
+void oracle_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w, int dtype,
+                        int64_t rows, int64_t cols, float eps, double* dh, double* dw) {
     const double e = (double)eps;
     double* rr = (double*)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1));
 #pragma omp parallel for schedule(static)
@@ -210,8 +210,10 @@ void oracle_rmsnorm_bwd(const void* h, const void* dy, const void* w, int dtype,
         const double rs = 1.0 / sqrt(ss / (double)cols + e);
         rr[r] = rs;
         const double c = rs * rs * sg / (double)cols;
-        for (int64_t j = 0; j < cols; ++j)
+        for (int64_t j = 0; j < cols; ++j) {
             dh[b + j] = rs * (load(w, dtype, j) * load(dy, dtype, b + j) - load(h, dtype, b + j) * c);
+            if (dres) dh[b + j] += load(dres, dtype, b + j);
+        }
     }
     for (int64_t j = 0; j < cols; ++j) dw[j] = 0.0;
     for (int64_t r = 0; r < rows; ++r)

@@ -76,12 +76,15 @@ void oracle_softmax_xent(const void* logits, int dtype, const int32_t* labels,
 void oracle_softmax_bwd(const void* p, const void* dy, int dtype, int64_t rows, int64_t cols,
                         double* dx);
 
-/* RMSNorm backward for y = h * r * w, r = 1/sqrt(mean(h^2) + eps), from the
- * stored h (the updated residual), w and dy:
- * dh_j = r * (w_j dy_j - h_j r^2 mean_k(dy_k w_k h_k));  dw_j = sum_rows dy_j h_j r.
+/* Backward of residual add + RMSNorm, y = h * r * w with h = x + residual and
+ * r = 1/sqrt(mean(h^2) + eps), from the stored h (the updated residual), w,
+ * dy, and dres, the gradient that reaches h through the updated residual
+ * (NULL: none):
+ * dh_j = r * (w_j dy_j - h_j r^2 mean_k(dy_k w_k h_k)) + dres_j;
+ * dw_j = sum_rows dy_j h_j r.  dh is the gradient of both x and residual.
  * dw is [cols]. */
-void oracle_rmsnorm_bwd(const void* h, const void* dy, const void* w, int dtype, int64_t rows,
-                        int64_t cols, float eps, double* dh, double* dw);
+void oracle_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w, int dtype,
+                        int64_t rows, int64_t cols, float eps, double* dh, double* dw);
 
 /* LayerNorm backward for y = n * gamma + beta, n = (x - mean) * rstd, using
  * the given per-row mean and rstd (as saved by the forward):

@@ -75,6 +75,31 @@ def test_rmsnorm_bwd_finite_differences(C):
         assert abs(fd(loss_w, w, (j,)) - dw[j]) <= 1e-8
 
 
+@pytest.mark.parametrize("C", [1, 4])
+def test_add_rmsnorm_bwd_residual_gradient(C):
+    """With h = x + residual also an output, L = sum(dy * y) + sum(dres * h):
+    dL/dx and dL/dresidual are both the returned dh (finite differences in x
+    and in residual separately)."""
+    x = RNG.normal(0, 1, size=(3, C))
+    res = RNG.normal(0, 1, size=(3, C))
+    w = RNG.uniform(0.5, 1.5, size=C)
+    dy = RNG.normal(0, 1, size=(3, C))
+    dres = RNG.normal(0, 1, size=(3, C))
+    eps = np.float32(1e-3)
+    dh, dw = oracle.rmsnorm_bwd(x + res, dy, w, eps, dres=dres)
+    _, dw0 = oracle.rmsnorm_bwd(x + res, dy, w, eps)
+    assert np.array_equal(dw, dw0)  # dres does not reach the weight
+
+    def loss(xx, rr):
+        y, h, _ = oracle.add_rmsnorm(xx, rr, w, eps)
+        return float(np.sum(dy * y) + np.sum(dres * h))
+
+    for r in range(3):
+        for j in range(C):
+            assert abs(fd(lambda xx: loss(xx, res), x, (r, j)) - dh[r, j]) <= 1e-8
+            assert abs(fd(lambda rr: loss(x, rr), res, (r, j)) - dh[r, j]) <= 1e-8
+
+
 def test_rmsnorm_bwd_torch():
     h = RNG.normal(0, 1, size=(12, 2048))
     w = RNG.uniform(0.8, 1.2, size=2048)

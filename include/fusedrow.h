@@ -20,8 +20,9 @@
  *            its element size. Any such alignment is accepted; 16-byte
  *            aligned rows take the 128-bit vector path, misaligned rows are
  *            split into a scalar head, a 128-bit body and a scalar tail.
- * Ownership  The caller owns every buffer. The library keeps no pointer after
- *            the call returns and allocates no memory. Inputs are read-only.
+ * Ownership  The caller owns every buffer, workspaces included. The library
+ *            keeps no pointer after the call returns and allocates no
+ *            memory. Inputs are read-only.
  *            Every output element is written.
  * Aliasing   An output may coincide exactly with a row input of the same
  *            shape and dtype (in-place): each row is read completely before
@@ -34,7 +35,9 @@
  *            FR_E_LAUNCH reports a failed kernel launch. Faults during kernel
  *            execution surface at the caller's next synchronisation.
  * Sizes      rows >= 0 (rows == 0 is a no-op returning FR_OK, pointers may
- *            then be NULL); 1 <= cols <= FR_MAX_COLS.
+ *            then be NULL; the norm backward calls still zero their
+ *            parameter gradients); 1 <= cols <= FR_MAX_COLS (less for the
+ *            backward calls).
  * Threads    Entry points are re-entrant. fr_debug_force_variant is the only
  *            global setting.
  *
@@ -56,10 +59,22 @@ extern "C" {
 
 typedef enum { FR_F32 = 0, FR_BF16 = 1 } fr_dtype_t;
 
+/* Operations, for the workspace query and the variant controls below. */
+typedef enum {
+  FR_OP_SOFTMAX = 0,
+  FR_OP_LAYERNORM = 1,
+  FR_OP_RMSNORM = 2,
+  FR_OP_XENT = 3,
+  FR_OP_SOFTMAX_BWD = 4,
+  FR_OP_RMSNORM_BWD = 5,
+  FR_OP_LAYERNORM_BWD = 6
+} fr_op_t;
+
 typedef enum {
   FR_OK = 0,
   FR_E_NULL = 1,    /* a required pointer is NULL */
-  FR_E_SHAPE = 2,   /* rows < 0, cols < 1, cols > FR_MAX_COLS, or size overflow */
+  FR_E_SHAPE = 2,   /* rows < 0, cols < 1, cols above the op's limit, size overflow,
+                       or a workspace smaller than the op needs */
   FR_E_DTYPE = 3,   /* unsupported dtype or dtype combination */
   FR_E_ALIAS = 4,   /* an output partially overlaps another buffer */
   FR_E_LAUNCH = 5,  /* the kernel launch failed (hipGetLastError) */
@@ -133,6 +148,71 @@ FR_API fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* la
                                     int64_t rows, int64_t cols, fr_dtype_t dtype,
                                     void* stream);
 
+/* ---- backward of the row operations ---- */
+
+/* Widest row of the backward entry points (their working set per element is
+ * larger: two row operands and, for the norms, per-column partial sums). */
+#define FR_BWD_MAX_COLS 16384
+/* Most partial rows a norm backward call leaves in its workspace. */
+#define FR_BWD_PARTIALS 256
+
+/* Softmax backward (vector-Jacobian product) from the stored forward output.
+ *   s = sum_k p_k dy_k,  dx_j = p_j (dy_j - s)   per row.
+ *   ("NexusGrad", Verified VJP Operators: softmax.)
+ * p, dy, dx [rows, cols] in `dtype` (FR_F32 or FR_BF16); dx may equal p or
+ * dy. cols <= FR_BWD_MAX_COLS. Rows whose p, dy and dx share their
+ * address modulo 16 take the 128-bit path. */
+FR_API fr_status_t fr_softmax_bwd(const void* p, const void* dy, void* dx, int64_t rows,
+                           int64_t cols, fr_dtype_t dtype, void* stream);
+
+/* Bytes of device workspace fr_add_rmsnorm_bwd (op FR_OP_RMSNORM_BWD) or
+ * fr_layernorm_bwd (FR_OP_LAYERNORM_BWD) needs for a [rows, cols] problem:
+ * min(rows, FR_BWD_PARTIALS) * cols * 4 per parameter gradient (one for
+ * RMSNorm, two for LayerNorm). -1 for another op or an invalid shape. */
+FR_API int64_t fr_norm_bwd_workspace_bytes(fr_op_t op, int64_t rows, int64_t cols);
+
+/* Backward of residual add + RMSNorm (fr_add_rmsnorm_fwd).
+ *   r = 1 / sqrt(mean_j h_j^2 + eps),  c = r^2 mean_k(dy_k weight_k h_k),
+ *   dh_j = r (weight_j dy_j - h_j c) + dres_j,
+ *   dweight_j = sum over rows of dy_j h_j r.
+ * h is the stored updated residual (residual_out of the forward); dres is the
+ * gradient reaching h through that output (NULL: none). dh is the gradient
+ * of both x and residual.
+ *   ("NexusGrad", Verified VJP Operators; Core Capabilities: RMSNorm,
+ *    residual blocks.)
+ * h, dy, dres, dh [rows, cols] and weight [cols] in `dtype`; dweight [cols]
+ * fp32, overwritten with the sum over all rows. dh may equal h, dy or dres.
+ * workspace: device memory of at least fr_norm_bwd_workspace_bytes bytes,
+ * 16-byte aligned, not overlapping any other buffer; its contents on entry
+ * do not matter and it holds partial sums afterwards. Both kernels run on
+ * `stream`, so a workspace may be reused by the next call on that stream.
+ * dweight is bitwise reproducible: fixed reduction order, no atomics.
+ * cols <= FR_BWD_MAX_COLS. rows == 0 sets dweight to zero (the other
+ * pointers may then be NULL). Rows on the 16-byte grid (every pointer
+ * 16-byte aligned and cols * element size a multiple of 16) take the 128-bit
+ * path. eps must be finite and >= 0. */
+FR_API fr_status_t fr_add_rmsnorm_bwd(const void* h, const void* dy, const void* dres,
+                               const void* weight, void* dh, float* dweight,
+                               void* workspace, int64_t workspace_bytes,
+                               int64_t rows, int64_t cols, float eps, fr_dtype_t dtype,
+                               void* stream);
+
+/* Backward of LayerNorm (fr_layernorm_fwd) at its saved statistics.
+ *   n_j = (x_j - mean) rstd,  g_j = dy_j gamma_j,
+ *   dx_j = rstd (g_j - mean_k g_k - n_j mean_k(g_k n_k)),
+ *   dgamma_j = sum over rows of dy_j n_j,  dbeta_j = sum over rows of dy_j.
+ *   ("NexusGrad", Verified VJP Operators; "Engineering a CUDA Machine
+ *    Learning Framework from Scratch", §3.2 for mean and rstd.)
+ * x, dy, dx [rows, cols] and gamma [cols] in `dtype`; mean, rstd [rows] fp32
+ * as written by fr_layernorm_fwd; dgamma, dbeta [cols] fp32, overwritten.
+ * dx may equal x or dy. workspace, reproducibility, rows == 0 (dgamma and
+ * dbeta set to zero), cols limit and vector path as for fr_add_rmsnorm_bwd. */
+FR_API fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* gamma,
+                             const float* mean, const float* rstd, void* dx,
+                             float* dgamma, float* dbeta, void* workspace,
+                             int64_t workspace_bytes, int64_t rows, int64_t cols,
+                             fr_dtype_t dtype, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 FR_API const char* fr_status_str(fr_status_t s);
 
@@ -147,7 +227,6 @@ FR_API const char* fr_version(void);
  * overlap. */
 FR_API fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
-typedef enum { FR_OP_SOFTMAX = 0, FR_OP_LAYERNORM = 1, FR_OP_RMSNORM = 2, FR_OP_XENT = 3 } fr_op_t;
 
 /* Force the kernel variant used by later calls of `op`: `threads` lanes per
  * row (64 = one wavefront per row, 256..1024 = one workgroup per row) and

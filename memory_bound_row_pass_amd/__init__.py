@@ -7,8 +7,8 @@ computes on tensor values. There is no fallback: if libfusedrow.so is missing
 or a call fails, an exception is raised.
 
 The fr_* functions mirror the C entry points one to one and take torch CUDA
-tensors; softmax / layernorm / add_rmsnorm / softmax_xent allocate the outputs
-and call them.
+tensors; softmax / layernorm / add_rmsnorm / softmax_xent and the *_bwd
+conveniences allocate the outputs (and the backward workspace) and call them.
 """
 from __future__ import annotations
 
@@ -19,13 +19,19 @@ __all__ = [
     "F32", "BF16", "FR_MAX_COLS", "FusedRowError", "lib", "status_str", "version",
     "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
     "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
+    "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
+    "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
+    "OP_SOFTMAX_BWD", "OP_RMSNORM_BWD", "OP_LAYERNORM_BWD", "FR_BWD_MAX_COLS", "FR_BWD_PARTIALS",
 ]
 
 F32, BF16 = 0, 1
 OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
+OP_SOFTMAX_BWD, OP_RMSNORM_BWD, OP_LAYERNORM_BWD = 4, 5, 6
 FR_MAX_COLS = 65536
+FR_BWD_MAX_COLS = 16384
+FR_BWD_PARTIALS = 256
 # FUSEDROW_LIB may name an alternative build of the same library (A/B runs).
 LIB_PATH = os.environ.get("FUSEDROW_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libfusedrow.so")
@@ -62,6 +68,9 @@ def _load() -> ctypes.CDLL:
         "fr_add_rmsnorm_fwd": [P, P, P, P, P, I64, I64, F, I32, P],
         "fr_softmax_xent_fwd_bwd": [P, P, P, P, P, I64, I64, I32, P],
         "fr_stream_copy": [P, P, I64, P],
+        "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
+        "fr_add_rmsnorm_bwd": [P, P, P, P, P, P, P, I64, I64, I64, F, I32, P],
+        "fr_layernorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, P],
         "fr_debug_force_variant": [I32, I32, I32],
         "fr_debug_select_variant": [I32, I64, I32, I32, I32, IP, IP, IP],
     }
@@ -69,6 +78,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.fr_norm_bwd_workspace_bytes.argtypes = [I32, I64, I64]
+    L.fr_norm_bwd_workspace_bytes.restype = ctypes.c_int64
     L.fr_status_str.argtypes = [ctypes.c_int]
     L.fr_status_str.restype = ctypes.c_char_p
     L.fr_version.argtypes = []
@@ -211,6 +222,87 @@ def fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, argmax=None, stream=None
            "fr_softmax_xent_fwd_bwd")
 
 
+def _check_like(t, ref, name):
+    if t is not None and (tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous()
+                          or t.dtype != ref.dtype):
+        raise ValueError(f"{name} must be a contiguous tensor of the row input's shape and dtype")
+
+
+def _check_f32_vec(t, cols, name):
+    torch = _torch()
+    _check_vec(t, cols, name)
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+
+
+def _workspace_arg(ws):
+    if ws is None:
+        return None, 0
+    _need_cuda(ws)
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def fr_softmax_bwd(p, dy, dx, stream=None) -> None:
+    """dx = p * (dy - <p, dy>) per row, from the forward output p (C: fr_softmax_bwd)."""
+    _need_cuda(p, dy, dx)
+    R, C = _rows_cols(p)
+    _check_like(dy, p, "dy")
+    _check_like(dx, p, "dx")
+    _check(lib.fr_softmax_bwd(_ptr(p), _ptr(dy), _ptr(dx), R, C, _dtype_code(p), _stream(stream, p)),
+           "fr_softmax_bwd")
+
+
+def fr_norm_bwd_workspace_bytes(op: int, rows: int, cols: int) -> int:
+    """Workspace bytes fr_add_rmsnorm_bwd / fr_layernorm_bwd need (C: same name)."""
+    n = int(lib.fr_norm_bwd_workspace_bytes(int(op), int(rows), int(cols)))
+    if n < 0:
+        raise ValueError(f"no workspace size for op {op} at [{rows}, {cols}]")
+    return n
+
+
+def fr_add_rmsnorm_bwd(h, dy, weight, dh, dweight, workspace, dres=None, eps: float = 1e-6,
+                       stream=None) -> None:
+    """Backward of residual add + RMSNorm from the stored h = x + residual
+    (C: fr_add_rmsnorm_bwd); dweight fp32 [cols] is overwritten."""
+    _need_cuda(h, dy, weight, dh, dweight, dres)
+    R, C = _rows_cols(h)
+    for t, n in ((dy, "dy"), (dh, "dh"), (dres, "dres")):
+        _check_like(t, h, n)
+    _check_vec(weight, C, "weight")
+    if weight.dtype != h.dtype:
+        raise TypeError("weight must have h's dtype")
+    _check_f32_vec(dweight, C, "dweight")
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_add_rmsnorm_bwd(_ptr(h), _ptr(dy), _ptr(dres), _ptr(weight), _ptr(dh),
+                                  _ptr(dweight), wp, wn, R, C, float(eps), _dtype_code(h),
+                                  _stream(stream, h)),
+           "fr_add_rmsnorm_bwd")
+
+
+def fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream=None) -> None:
+    """Backward of LayerNorm at the saved mean / rstd (C: fr_layernorm_bwd);
+    dgamma, dbeta fp32 [cols] are overwritten."""
+    torch = _torch()
+    _need_cuda(x, dy, gamma, mean, rstd, dx, dgamma, dbeta)
+    R, C = _rows_cols(x)
+    _check_like(dy, x, "dy")
+    _check_like(dx, x, "dx")
+    _check_vec(gamma, C, "gamma")
+    if gamma.dtype != x.dtype:
+        raise TypeError("gamma must have x's dtype")
+    _check_rows(mean, R, "mean", torch.float32)
+    _check_rows(rstd, R, "rstd", torch.float32)
+    _check_f32_vec(dgamma, C, "dgamma")
+    _check_f32_vec(dbeta, C, "dbeta")
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_layernorm_bwd(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
+                                _ptr(dgamma), _ptr(dbeta), wp, wn, R, C, _dtype_code(x),
+                                _stream(stream, x)),
+           "fr_layernorm_bwd")
+
+
 def fr_stream_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     """Plain device copy of nbytes (default: all of src) — bandwidth reference."""
     _need_cuda(src, dst)
@@ -284,3 +376,39 @@ def softmax_xent(logits, labels, return_argmax: bool = False):
     am = torch.empty(R, dtype=torch.int32, device=logits.device) if return_argmax else None
     fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, am)
     return (loss, grad, am) if return_argmax else (loss, grad)
+
+
+def _workspace(op, rows, cols, device):
+    torch = _torch()
+    n = fr_norm_bwd_workspace_bytes(op, rows, cols)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def softmax_bwd(p, dy, out=None):
+    torch = _torch()
+    dx = out if out is not None else torch.empty_like(p)
+    fr_softmax_bwd(p, dy, dx)
+    return dx
+
+
+def add_rmsnorm_bwd(h, dy, weight, eps: float = 1e-6, dres=None):
+    """Returns (dh, dweight); dh is the gradient of both x and residual."""
+    torch = _torch()
+    R, C = h.shape
+    dh = torch.empty_like(h)
+    dw = torch.empty(C, dtype=torch.float32, device=h.device)
+    ws = _workspace(OP_RMSNORM_BWD, R, C, h.device)
+    fr_add_rmsnorm_bwd(h, dy, weight, dh, dw, ws, dres=dres, eps=eps)
+    return dh, dw
+
+
+def layernorm_bwd(x, dy, gamma, mean, rstd):
+    """Returns (dx, dgamma, dbeta)."""
+    torch = _torch()
+    R, C = x.shape
+    dx = torch.empty_like(x)
+    dg = torch.empty(C, dtype=torch.float32, device=x.device)
+    db = torch.empty(C, dtype=torch.float32, device=x.device)
+    ws = _workspace(OP_LAYERNORM_BWD, R, C, x.device)
+    fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dg, db, ws)
+    return dx, dg, db

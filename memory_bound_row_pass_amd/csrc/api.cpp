@@ -20,7 +20,7 @@ struct Forced {
   std::atomic<int> threads{0};
   std::atomic<int> vecs{0};
 };
-Forced g_forced[4];
+Forced g_forced[FR_OP_LAYERNORM_BWD + 1];
 
 // ------------------------------------------------------------------- buffers
 struct Buf {
@@ -126,7 +126,7 @@ const char* fr_status_str(fr_status_t s) {
 const char* fr_version(void) { return "fusedrow 0.1.0 (gfx950)"; }
 
 fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs) {
-  if (op < FR_OP_SOFTMAX || op > FR_OP_XENT) return FR_E_VALUE;
+  if (op < FR_OP_SOFTMAX || op > FR_OP_LAYERNORM_BWD) return FR_E_VALUE;
   if (threads < 0 || vecs < 0) return FR_E_VALUE;
   g_forced[op].vecs.store(threads ? vecs : 0);
   g_forced[op].threads.store(threads);
@@ -160,6 +160,24 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
     }
     case FR_OP_XENT: {
       auto v = select_variant(fr::xent_variants(in_dtype == FR_BF16, 0), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_SOFTMAX_BWD: {
+      if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+      auto v = select_variant(fr::softmax_bwd_variants(in_dtype == FR_BF16), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_RMSNORM_BWD: {
+      if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+      auto v = select_variant(fr::rmsnorm_bwd_variants(in_dtype == FR_BF16), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_LAYERNORM_BWD: {
+      if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+      auto v = select_variant(fr::layernorm_bwd_variants(in_dtype == FR_BF16), op, cols, epv);
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -274,6 +292,124 @@ fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* labels, f
   if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
   return launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols,
                                  static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_softmax_bwd(const void* p, const void* dy, void* dx, int64_t rows, int64_t cols,
+                           fr_dtype_t dtype, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (rows == 0) return FR_OK;
+  if (!p || !dy || !dx) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(p, es) || !aligned(dy, es) || !aligned(dx, es)) return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(p, nb, true, es, false), make_buf(dy, nb, true, es, false),
+                      make_buf(dx, nb, true, es, true)};
+  if (fr_status_t s = check_alias(bufs, 3)) return s;
+  const uintptr_t ph = reinterpret_cast<uintptr_t>(p) % 16;
+  const bool vec = reinterpret_cast<uintptr_t>(dy) % 16 == ph &&
+                   reinterpret_cast<uintptr_t>(dx) % 16 == ph;
+  const fr::SoftmaxBwdVariant* v = select_variant(fr::softmax_bwd_variants(dtype == FR_BF16),
+                                                  FR_OP_SOFTMAX_BWD, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_SOFTMAX_BWD].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  return launch_status(v->launch(p, dy, dx, rows, (int)cols, static_cast<hipStream_t>(stream)));
+}
+
+int64_t fr_norm_bwd_workspace_bytes(fr_op_t op, int64_t rows, int64_t cols) {
+  if (op != FR_OP_RMSNORM_BWD && op != FR_OP_LAYERNORM_BWD) return -1;
+  if (check_shape(rows, cols) != FR_OK || cols > FR_BWD_MAX_COLS) return -1;
+  const int64_t np = op == FR_OP_LAYERNORM_BWD ? 2 : 1;
+  const int64_t parts = rows < FR_BWD_PARTIALS ? rows : FR_BWD_PARTIALS;
+  return parts * cols * 4 * np;
+}
+
+fr_status_t fr_add_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* weight,
+                               void* dh, float* dweight, void* workspace, int64_t workspace_bytes,
+                               int64_t rows, int64_t cols, float eps, fr_dtype_t dtype,
+                               void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  const int64_t need = fr_norm_bwd_workspace_bytes(FR_OP_RMSNORM_BWD, rows, cols);
+  if (workspace_bytes < need) return FR_E_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dweight) return FR_E_NULL;
+  if (!aligned(dweight, 4)) return FR_E_ALIGN;
+  if (rows == 0) return launch_status(fr::launch_colsum(nullptr, 0, (int)cols, dweight, nullptr, st));
+  if (!h || !dy || !weight || !dh || !workspace) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(h, es) || !aligned(dy, es) || !aligned(weight, es) || !aligned(dh, es) ||
+      (dres && !aligned(dres, es)) || !aligned(workspace, 16))
+    return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(h, nb, true, es, false),
+                      make_buf(dy, nb, true, es, false),
+                      make_buf(dres, nb, true, es, false),
+                      make_buf(weight, cols * es, false, es, false),
+                      make_buf(dh, nb, true, es, true),
+                      make_buf(dweight, cols * 4, false, 4, true),
+                      make_buf(workspace, need, false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 7)) return s;
+  const bool vec = aligned(h, 16) && aligned(dy, 16) && (!dres || aligned(dres, 16)) &&
+                   aligned(weight, 16) && aligned(dh, 16) && (cols * es) % 16 == 0;
+  const fr::RmsNormBwdVariant* v = select_variant(fr::rmsnorm_bwd_variants(dtype == FR_BF16),
+                                                  FR_OP_RMSNORM_BWD, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_RMSNORM_BWD].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  const int grid = fr::bwd_grid(v->threads, rows);
+  float* ws = static_cast<float*>(workspace);
+  if (fr_status_t s = launch_status(v->launch(h, dy, dres, weight, dh, ws, grid, rows, (int)cols,
+                                              eps, st)))
+    return s;
+  return launch_status(fr::launch_colsum(ws, grid, (int)cols, dweight, nullptr, st));
+}
+
+fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* gamma, const float* mean,
+                             const float* rstd, void* dx, float* dgamma, float* dbeta,
+                             void* workspace, int64_t workspace_bytes, int64_t rows, int64_t cols,
+                             fr_dtype_t dtype, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  const int64_t need = fr_norm_bwd_workspace_bytes(FR_OP_LAYERNORM_BWD, rows, cols);
+  if (workspace_bytes < need) return FR_E_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dgamma || !dbeta) return FR_E_NULL;
+  if (!aligned(dgamma, 4) || !aligned(dbeta, 4)) return FR_E_ALIGN;
+  if (rows == 0) {
+    const Buf pb[] = {make_buf(dgamma, cols * 4, false, 4, true),
+                      make_buf(dbeta, cols * 4, false, 4, true)};
+    if (fr_status_t s = check_alias(pb, 2)) return s;
+    return launch_status(fr::launch_colsum(nullptr, 0, (int)cols, dgamma, dbeta, st));
+  }
+  if (!x || !dy || !gamma || !mean || !rstd || !dx || !workspace) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(x, es) || !aligned(dy, es) || !aligned(gamma, es) || !aligned(dx, es) ||
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(workspace, 16))
+    return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(x, nb, true, es, false),
+                      make_buf(dy, nb, true, es, false),
+                      make_buf(gamma, cols * es, false, es, false),
+                      make_buf(mean, rows * 4, false, 4, false),
+                      make_buf(rstd, rows * 4, false, 4, false),
+                      make_buf(dx, nb, true, es, true),
+                      make_buf(dgamma, cols * 4, false, 4, true),
+                      make_buf(dbeta, cols * 4, false, 4, true),
+                      make_buf(workspace, need, false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 9)) return s;
+  const bool vec = aligned(x, 16) && aligned(dy, 16) && aligned(gamma, 16) && aligned(dx, 16) &&
+                   (cols * es) % 16 == 0;
+  const fr::LayerNormBwdVariant* v = select_variant(fr::layernorm_bwd_variants(dtype == FR_BF16),
+                                                    FR_OP_LAYERNORM_BWD, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_LAYERNORM_BWD].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  const int grid = fr::bwd_grid(v->threads, rows);
+  float* ws = static_cast<float*>(workspace);
+  if (fr_status_t s = launch_status(v->launch(x, dy, gamma, mean, rstd, dx, ws, grid, rows,
+                                              (int)cols, st)))
+    return s;
+  return launch_status(fr::launch_colsum(ws, grid, (int)cols, dgamma, dbeta, st));
 }
 
 fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -1,0 +1,494 @@
+// Backward passes of the row operations, each reading its row operands once.
+//
+// Softmax ("NexusGrad", Verified VJP Operators: softmax): from the stored
+// forward output p and the upstream gradient dy,
+//   s = sum_k p_k dy_k,   dx_j = p_j (dy_j - s),
+// one reduction per row and the gradient written from the same registers.
+//
+// Residual add + RMSNorm (same page, RMSNorm and residual blocks): from the
+// stored updated residual h = x + residual, the weight w, dy and the gradient
+// dres reaching h through the updated residual,
+//   r = 1/sqrt(sum h^2 / C + eps),   c = r^2 sum_k dy_k w_k h_k / C,
+//   dh_j = r (w_j dy_j - h_j c) + dres_j,   dw_j = sum_rows dy_j h_j r.
+// LayerNorm (same page; "Engineering a CUDA Machine Learning Framework from
+// Scratch", §3.2 for the saved statistics): from x, dy, gamma and the saved
+// per-row mean and rstd, with n = (x - mean) rstd and g = dy gamma,
+//   dx_j = rstd (g_j - mean(g) - n_j mean(g n)),
+//   dgamma_j = sum_rows dy_j n_j,   dbeta_j = sum_rows dy_j.
+//
+// Parameter gradients are column sums over all rows. The norm kernels run a
+// fixed grid of kBwdGrid workgroups of kBwdBlock lanes; every lane owns the
+// same columns in every row it visits (rows on the 16-byte grid, no head
+// peel), so it accumulates its columns' partial sums in registers across its
+// rows. At the end the row groups of a workgroup are summed through LDS in a
+// fixed order and the workgroup writes one partial row per parameter to the
+// workspace; colsum_kernel then adds the partial rows in a fixed order.
+// There are no atomics: results are bitwise reproducible run to run.
+#include "fr_kernels.hpp"
+#include "fr_device.hpp"
+
+namespace fr {
+
+// Clamped streaming load of chunk slot i (as load_chunks, one slot).
+template <typename Ts, int T, int EPV, int AL>
+__device__ __forceinline__ void load_slot(const Ts* row, const RowGeom<EPV, AL>& g, int tid, int i,
+                                          float* v) {
+  const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+  uint32_t o = (uint32_t)(i * T * EPV) + (uint32_t)tid * EPV;
+  o = o < last ? o : last;
+  Vec<Ts, EPV>::load(row + g.head + o, v);
+}
+
+// Ordinary (cached) fp32 vector access for partial sums, in global memory or
+// LDS: they are read back soon, unlike the streamed rows.
+template <int EPV>
+__device__ __forceinline__ void store_f32(float* p, const float* v) {
+  if constexpr (EPV == 1) {
+    *p = v[0];
+  } else {
+#pragma unroll
+    for (int k = 0; k < EPV; k += 4)
+      *reinterpret_cast<f32x4*>(p + k) = f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]};
+  }
+}
+template <int EPV>
+__device__ __forceinline__ void load_f32(const float* p, float* v) {
+  if constexpr (EPV == 1) {
+    v[0] = *p;
+  } else {
+#pragma unroll
+    for (int k = 0; k < EPV; k += 4) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(p + k);
+      v[k] = r.x; v[k + 1] = r.y; v[k + 2] = r.z; v[k + 3] = r.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------- softmax backward
+
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int cols) {
+  constexpr int BLOCK = T == 64 ? 256 : T;
+  constexpr int RPB = BLOCK / T;
+  constexpr int NW = T / 64;
+  __shared__ float xw[2][NW][1];
+
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = T == 64 ? lane : (int)threadIdx.x;
+  const int sub = T == 64 ? wib : 0;
+  const int wave = T == 64 ? 0 : wib;
+  int it = 0;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
+       row += (int64_t)gridDim.x * RPB, ++it) {
+    const int64_t off = row * cols;
+    const RowGeom<EPV> g(p + off, cols);
+
+    const int ec = g.extra_col(tid);
+    const float ae = load_extra(p + off, ec, 0.f);
+    const float de = load_extra(dy + off, ec, 0.f);
+    float a[NV][EPV], d[NV][EPV];
+    load_chunks2<Ts, T, NV, EPV>(p + off, dy + off, g, tid, a, d, 0.f);
+
+    float s0 = ae * de, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        if (k & 1) s1 = __builtin_fmaf(a[i][k], d[i][k], s1);
+        else s0 = __builtin_fmaf(a[i][k], d[i][k], s0);
+      }
+    SumState st{s0 + s1};
+    st = wave_reduce(st, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+
+    const float s = st.s;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) a[i][k] = a[i][k] * (d[i][k] - s);
+    store_chunks<Ts, T, NV, EPV>(dx + off, g, tid, a);
+    if (ec >= 0) store1(dx + off + ec, ae * (de - s));
+  }
+}
+
+// ------------------------------------------------- norm backward, partials
+
+// Sum the row groups' per-lane column partials of one parameter in row-group
+// order and write the workgroup's partial row (`cols` floats at wsrow).
+template <int T, int NV, int EPV, int RPB>
+__device__ __forceinline__ void flush_partials(const float (&acc)[NV][EPV], float* part,
+                                               float* wsrow, int nvec, int tid, int sub) {
+  if constexpr (RPB == 1) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i * T + tid < nvec) store_f32<EPV>(wsrow + (i * T + tid) * EPV, acc[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      store_f32<EPV>(part + (sub * T + tid) * EPV, acc[i]);
+      __syncthreads();
+      if (sub == 0 && i * T + tid < nvec) {
+        float s[EPV];
+        load_f32<EPV>(part + tid * EPV, s);
+#pragma unroll
+        for (int r = 1; r < RPB; ++r) {
+          float o[EPV];
+          load_f32<EPV>(part + (r * T + tid) * EPV, o);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) s[k] += o[k];
+        }
+        store_f32<EPV>(wsrow + (i * T + tid) * EPV, s);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Column slots of a lane in the norm backward kernels. Their rows start on
+// the 16-byte grid (or EPV == 1): nvec = cols / EPV >= 1 chunks, no head, no
+// tail, the same columns in every row. Slot i holds chunk i*T + tid; a slot
+// past the row end reads the last chunk (in bounds) and is masked. Offsets
+// are 32-bit element offsets from a uniform row or parameter base.
+template <int T, int NV, int EPV>
+struct Slots {
+  int nvec, tid;
+  uint32_t last;
+  __device__ __forceinline__ Slots(int cols, int tid_)
+      : nvec(cols / EPV), tid(tid_), last((uint32_t)(cols / EPV - 1) * EPV) {}
+  __device__ __forceinline__ uint32_t off(int i) const {
+    const uint32_t o = (uint32_t)((i * T + tid) * EPV);
+    return o < last ? o : last;
+  }
+  __device__ __forceinline__ bool ok(int i) const { return i * T + tid < nvec; }
+
+  template <typename Ts>
+  __device__ __forceinline__ void load2(const Ts* ra, const Ts* rb, float (&a)[NV][EPV],
+                                        float (&b)[NV][EPV]) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      Vec<Ts, EPV>::load(ra + off(i), a[i]);
+      Vec<Ts, EPV>::load(rb + off(i), b[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        a[i][k] = ok(i) ? a[i][k] : 0.f;
+        b[i][k] = ok(i) ? b[i][k] : 0.f;
+      }
+  }
+  template <typename Ts>
+  __device__ __forceinline__ void load(const Ts* r, int i, float* v) const {
+    Vec<Ts, EPV>::load(r + off(i), v);
+  }
+  template <typename Ts>
+  __device__ __forceinline__ void param(const Ts* par, int i, float* v) const {
+    load_param<Ts, EPV>(par + off(i), v);
+  }
+  template <typename Ts>
+  __device__ __forceinline__ void store(Ts* r, const float (&v)[NV][EPV]) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (ok(i)) Vec<Ts, EPV>::store(r + off(i), v[i]);
+  }
+};
+
+// The parameter pointer as a fresh uniform value in each phase of each row:
+// the loads then stay in (uniform base + 32-bit lane offset) form inside the
+// loop instead of being hoisted out as per-slot 64-bit addresses, and the
+// second phase reloads the parameters (cache hits) instead of keeping the
+// first phase's registers live across the row reduction.
+// (An opaque zero is added rather than the pointer itself laundered, which
+// would lose its global address space and turn the loads into flat ones.)
+template <typename T>
+__device__ __forceinline__ const T* fresh(const T* p) {
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  return p + z;
+}
+
+// Lane layout of the norm backward workgroup: RPB row groups of T lanes.
+// The row loop runs the same number of times in every wave of the
+// workgroup (block-wide barriers inside); a row group past the last row
+// takes part in the barriers with no data.
+template <int T>
+struct BwdLanes {
+  static constexpr int RPB = kBwdBlock / T;
+  static constexpr int NW = T / 64;
+  int lane, sub, wave, tid;
+  __device__ __forceinline__ BwdLanes() {
+    const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lane = threadIdx.x & 63;
+    sub = wib / NW;
+    wave = wib % NW;
+    tid = wave * 64 + lane;
+  }
+};
+
+// ------------------------------------------------ residual add + RMSNorm bwd
+
+template <typename Ts, int T, int NV, int EPV>
+__global__ __launch_bounds__(kBwdBlock)
+void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, Ts* dh, float* ws,
+                        int64_t rows, int cols, float eps) {
+  using L = BwdLanes<T>;
+  constexpr int RPB = L::RPB, NW = L::NW;
+  __shared__ float xw[RPB][2][NW][2];
+  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? kBwdBlock * EPV : 4];
+  const L ln;
+  const Slots<T, NV, EPV> sl(cols, ln.tid);
+
+  float acc[NV][EPV];  // dw partials
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) acc[i][k] = 0.f;
+
+  int it = 0;
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows;
+       base += (int64_t)gridDim.x * RPB, ++it) {
+    const int64_t row = base + ln.sub;
+    const bool live = row < rows;  // uniform in the wave; a dead group re-reads the last row
+    const int64_t off = (live ? row : rows - 1) * cols;
+
+    float hv[NV][EPV], d[NV][EPV];
+    sl.load2(h + off, dy + off, hv, d);
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    const Ts* w1 = fresh(w);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float wt[EPV];
+      sl.param(w1, i, wt);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const float hk = hv[i][k];
+        const float gk = d[i][k] * wt[k];
+        if (k & 1) { a1 = __builtin_fmaf(hk, hk, a1); b1 = __builtin_fmaf(gk, hk, b1); }
+        else { a0 = __builtin_fmaf(hk, hk, a0); b0 = __builtin_fmaf(gk, hk, b0); }
+      }
+    }
+    Sum2State st{a0 + a1, b0 + b1};
+    st = wave_reduce(st, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[ln.sub][it & 1], ln.wave, ln.lane, Sum2Merge{});
+
+    if (live) {
+      const float r = 1.f / __builtin_sqrtf(st.a / (float)cols + eps);
+      const float c = r * r * (st.b / (float)cols);
+      const Ts* w2 = fresh(w);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float wt[EPV];
+        sl.param(w2, i, wt);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          acc[i][k] = __builtin_fmaf(d[i][k] * hv[i][k], r, acc[i][k]);
+          hv[i][k] = r * __builtin_fmaf(-hv[i][k], c, wt[k] * d[i][k]);
+        }
+      }
+      if (dres) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          float dr[EPV];
+          sl.load(dres + off, i, dr);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) hv[i][k] += dr[k];
+        }
+      }
+      sl.store(dh + off, hv);
+    }
+  }
+  flush_partials<T, NV, EPV, RPB>(acc, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
+}
+
+// ------------------------------------------------------------ LayerNorm bwd
+
+template <typename Ts, int T, int NV, int EPV>
+__global__ __launch_bounds__(kBwdBlock)
+void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const float* mean,
+                          const float* rstd, Ts* dx, float* ws, int64_t rows, int cols) {
+  using L = BwdLanes<T>;
+  constexpr int RPB = L::RPB, NW = L::NW;
+  __shared__ float xw[RPB][2][NW][2];
+  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? kBwdBlock * EPV : 4];
+  const L ln;
+  const Slots<T, NV, EPV> sl(cols, ln.tid);
+
+  float ag[NV][EPV], ab[NV][EPV];  // dgamma, dbeta partials
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) { ag[i][k] = 0.f; ab[i][k] = 0.f; }
+
+  int it = 0;
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows;
+       base += (int64_t)gridDim.x * RPB, ++it) {
+    const int64_t row = base + ln.sub;
+    const bool live = row < rows;
+    const int64_t rr = live ? row : rows - 1;
+    const int64_t off = rr * cols;
+    const float mu = mean[rr];
+    const float rs = rstd[rr];
+
+    float n[NV][EPV], d[NV][EPV];
+    sl.load2(x + off, dy + off, n, d);
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    const Ts* g1 = fresh(gamma);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float ga[EPV];
+      sl.param(g1, i, ga);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        n[i][k] = (n[i][k] - mu) * rs;  // masked slots have dy = 0 and add nothing
+        const float gk = d[i][k] * ga[k];
+        if (k & 1) { a1 += gk; b1 = __builtin_fmaf(gk, n[i][k], b1); }
+        else { a0 += gk; b0 = __builtin_fmaf(gk, n[i][k], b0); }
+      }
+    }
+    Sum2State st{a0 + a1, b0 + b1};
+    st = wave_reduce(st, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[ln.sub][it & 1], ln.wave, ln.lane, Sum2Merge{});
+
+    if (live) {
+      const float mg = st.a / (float)cols;
+      const float mgn = st.b / (float)cols;
+      const Ts* g2 = fresh(gamma);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float ga[EPV];
+        sl.param(g2, i, ga);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          ag[i][k] = __builtin_fmaf(d[i][k], n[i][k], ag[i][k]);
+          ab[i][k] += d[i][k];
+          n[i][k] = rs * __builtin_fmaf(-n[i][k], mgn, __builtin_fmaf(d[i][k], ga[k], -mg));
+        }
+      }
+      sl.store(dx + off, n);
+    }
+  }
+  const size_t G = gridDim.x;
+  flush_partials<T, NV, EPV, RPB>(ag, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
+  flush_partials<T, NV, EPV, RPB>(ab, part, ws + (G + blockIdx.x) * cols, sl.nvec, ln.tid, ln.sub);
+}
+
+// ------------------------------------------------------------ column sums
+// out_p[c] = sum over the partial rows b = 0 .. partials-1 of ws[p][b][c],
+// parameter p = blockIdx.y. 16 waves per 64-column tile: wave ty sums rows
+// ty, ty+16, ... in order, then wave 0 adds the 16 sums in order.
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* ws, int partials, int cols,
+                                                      float* out0, float* out1) {
+  __shared__ float red[16][64];
+  const int tx = threadIdx.x & 63;
+  const int ty = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.x * 64 + tx;
+  const float* src = ws + (size_t)blockIdx.y * partials * cols;
+  float s = 0.f;
+  if (c < cols) {
+#pragma unroll 4
+    for (int b = ty; b < partials; b += 16) s += src[(size_t)b * cols + c];
+  }
+  red[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && c < cols) {
+    float t = red[0][tx];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) t += red[r][tx];
+    (blockIdx.y == 0 ? out0 : out1)[c] = t;
+  }
+}
+
+hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, float* out1,
+                         hipStream_t s) {
+  const unsigned tiles = (unsigned)((cols + 63) / 64);
+  return launch_kernel(&colsum_kernel, dim3(tiles, out1 ? 2 : 1), dim3(1024), s, ws, partials,
+                       cols, out0, out1);
+}
+
+// ------------------------------------------------------------- launchers
+
+template <typename Ts, int T, int NV, int EPV, int OCC>
+static hipError_t launch_softmax_bwd(const void* p, const void* dy, void* dx, int64_t rows, int cols,
+                                     hipStream_t s) {
+  constexpr int BLOCK = T == 64 ? 256 : T;
+  constexpr int RPB = BLOCK / T;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
+  return launch_kernel(&softmax_bwd_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(BLOCK), s,
+                       static_cast<const Ts*>(p), static_cast<const Ts*>(dy), static_cast<Ts*>(dx),
+                       rows, cols);
+}
+
+template <typename Ts, int T, int NV, int EPV>
+static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w,
+                                     void* dh, float* ws, int grid, int64_t rows, int cols,
+                                     float eps, hipStream_t s) {
+  return launch_kernel(&rmsnorm_bwd_kernel<Ts, T, NV, EPV>, dim3(grid), dim3(kBwdBlock), s,
+                       static_cast<const Ts*>(h), static_cast<const Ts*>(dy),
+                       static_cast<const Ts*>(dres), static_cast<const Ts*>(w),
+                       static_cast<Ts*>(dh), ws, rows, cols, eps);
+}
+
+template <typename Ts, int T, int NV, int EPV>
+static hipError_t launch_layernorm_bwd(const void* x, const void* dy, const void* gamma,
+                                       const float* mean, const float* rstd, void* dx, float* ws,
+                                       int grid, int64_t rows, int cols, hipStream_t s) {
+  return launch_kernel(&layernorm_bwd_kernel<Ts, T, NV, EPV>, dim3(grid), dim3(kBwdBlock), s,
+                       static_cast<const Ts*>(x), static_cast<const Ts*>(dy),
+                       static_cast<const Ts*>(gamma), mean, rstd, static_cast<Ts*>(dx), ws, rows,
+                       cols);
+}
+
+#define FR_SB(TS, T, NV, EPV, OCC) {T, NV, EPV, &launch_softmax_bwd<TS, T, NV, EPV, OCC>}
+#define FR_RB(TS, T, NV, EPV) {T, NV, EPV, &launch_rmsnorm_bwd<TS, T, NV, EPV>}
+#define FR_LB(TS, T, NV, EPV) {T, NV, EPV, &launch_layernorm_bwd<TS, T, NV, EPV>}
+
+static const SoftmaxBwdVariant kSbF32[] = {
+    FR_SB(float, 64, 1, 4, 8),    FR_SB(float, 64, 2, 4, 8),    FR_SB(float, 64, 4, 4, 6),
+    FR_SB(float, 64, 8, 4, 4),    FR_SB(float, 256, 4, 4, 6),   FR_SB(float, 256, 8, 4, 4),
+    FR_SB(float, 512, 8, 4, 4),   FR_SB(float, 64, 16, 1, 4),   FR_SB(float, 256, 16, 1, 4),
+    FR_SB(float, 1024, 16, 1, 4)};
+static const SoftmaxBwdVariant kSbBf16[] = {
+    FR_SB(bf16_t, 64, 1, 8, 8),   FR_SB(bf16_t, 64, 2, 8, 6),   FR_SB(bf16_t, 64, 4, 8, 4),
+    FR_SB(bf16_t, 256, 2, 8, 6),  FR_SB(bf16_t, 256, 4, 8, 4),  FR_SB(bf16_t, 512, 4, 8, 4),
+    FR_SB(bf16_t, 64, 16, 1, 4),  FR_SB(bf16_t, 256, 16, 1, 4), FR_SB(bf16_t, 1024, 16, 1, 4)};
+
+static const RmsNormBwdVariant kRbF32[] = {
+    FR_RB(float, 64, 1, 4),   FR_RB(float, 64, 2, 4),   FR_RB(float, 64, 4, 4),
+    FR_RB(float, 256, 2, 4),  FR_RB(float, 256, 4, 4),  FR_RB(float, 512, 4, 4),
+    FR_RB(float, 1024, 4, 4), FR_RB(float, 64, 16, 1),  FR_RB(float, 256, 16, 1),
+    FR_RB(float, 1024, 16, 1)};
+static const RmsNormBwdVariant kRbBf16[] = {
+    FR_RB(bf16_t, 64, 1, 8),   FR_RB(bf16_t, 64, 2, 8),   FR_RB(bf16_t, 256, 1, 8),
+    FR_RB(bf16_t, 256, 2, 8),  FR_RB(bf16_t, 512, 2, 8),
+    FR_RB(bf16_t, 1024, 2, 8), FR_RB(bf16_t, 64, 16, 1),  FR_RB(bf16_t, 256, 16, 1),
+    FR_RB(bf16_t, 1024, 16, 1)};
+
+static const LayerNormBwdVariant kLbF32[] = {
+    FR_LB(float, 64, 1, 4),   FR_LB(float, 64, 2, 4),   FR_LB(float, 64, 4, 4),
+    FR_LB(float, 256, 2, 4),  FR_LB(float, 256, 4, 4),  FR_LB(float, 512, 4, 4),
+    FR_LB(float, 1024, 4, 4), FR_LB(float, 64, 16, 1),  FR_LB(float, 256, 16, 1),
+    FR_LB(float, 1024, 16, 1)};
+static const LayerNormBwdVariant kLbBf16[] = {
+    FR_LB(bf16_t, 64, 1, 8),   FR_LB(bf16_t, 64, 2, 8),   FR_LB(bf16_t, 256, 1, 8),
+    FR_LB(bf16_t, 256, 2, 8),  FR_LB(bf16_t, 512, 2, 8),  FR_LB(bf16_t, 1024, 2, 8),
+    FR_LB(bf16_t, 64, 16, 1),  FR_LB(bf16_t, 256, 16, 1), FR_LB(bf16_t, 1024, 16, 1)};
+
+#define FR_SPAN(a) {a, sizeof(a) / sizeof(a[0])}
+
+VariantSpan<SoftmaxBwdVariant> softmax_bwd_variants(int bf16) {
+  if (bf16) return FR_SPAN(kSbBf16);
+  return FR_SPAN(kSbF32);
+}
+VariantSpan<RmsNormBwdVariant> rmsnorm_bwd_variants(int bf16) {
+  if (bf16) return FR_SPAN(kRbBf16);
+  return FR_SPAN(kRbF32);
+}
+VariantSpan<LayerNormBwdVariant> layernorm_bwd_variants(int bf16) {
+  if (bf16) return FR_SPAN(kLbBf16);
+  return FR_SPAN(kLbF32);
+}
+
+}  // namespace fr

@@ -222,7 +222,10 @@ __device__ __forceinline__ void store1(bf16_t* p, float v) { p->u = to_bf16(v); 
 // (head + tail <= 31 + 7 < 64 <= T).
 constexpr int kHeadAlign = 32;  // elements
 
-template <int EPV>
+// ALIGN is the element boundary the body starts on (kHeadAlign by default;
+// EPV keeps the head at 0 for rows on the 16-byte grid, so a lane owns the
+// same columns in every row — what per-column gradient sums need).
+template <int EPV, int ALIGN = kHeadAlign>
 struct RowGeom {
   int head, nvec, tail;
   template <typename T>
@@ -231,8 +234,8 @@ struct RowGeom {
       head = 0; nvec = cols; tail = 0;
     } else {
       const uint32_t mis =
-          (uint32_t)(reinterpret_cast<uintptr_t>(row_ptr) / sizeof(T)) & (kHeadAlign - 1);
-      const int h = (int)((kHeadAlign - mis) & (kHeadAlign - 1));
+          (uint32_t)(reinterpret_cast<uintptr_t>(row_ptr) / sizeof(T)) & (ALIGN - 1);
+      const int h = (int)((ALIGN - mis) & (ALIGN - 1));
       head = h < cols ? h : cols;
       nvec = (cols - head) / EPV;
       tail = cols - head - nvec * EPV;
@@ -253,8 +256,8 @@ struct RowGeom {
 // then overwritten with `fill`; stores of such slots are masked off. A single
 // code path keeps the register allocation tight (rows that fill every slot
 // simply never mask).
-template <typename Ts, int T, int NV, int EPV>
-__device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV>& g, int tid,
+template <typename Ts, int T, int NV, int EPV, int AL>
+__device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                             float (&v)[NV][EPV], float fill) {
   if (g.nvec > 0) {
     const Ts* base = row + g.head;                  // uniform
@@ -280,8 +283,49 @@ __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV>& g
   }
 }
 
-template <typename Ts, int T, int NV, int EPV>
-__device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV>& g, int tid,
+// Two row operands of the same geometry in one branch, so that the second
+// operand's loads are issued before the first operand's data is waited for.
+template <typename Ts, int T, int NV, int EPV, int AL>
+__device__ __forceinline__ void load_chunks2(const Ts* ra, const Ts* rb, const RowGeom<EPV, AL>& g,
+                                             int tid, float (&a)[NV][EPV], float (&b)[NV][EPV],
+                                             float fill) {
+  if (g.nvec > 0) {
+    const uint32_t lo = (uint32_t)tid * EPV;
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      uint32_t o = (uint32_t)(i * T * EPV) + lo;
+      o = o < last ? o : last;
+      Vec<Ts, EPV>::load(ra + g.head + o, a[i]);
+      Vec<Ts, EPV>::load(rb + g.head + o, b[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ok = i * T + tid < g.nvec;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        a[i][k] = ok ? a[i][k] : fill;
+        b[i][k] = ok ? b[i][k] : fill;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) { a[i][k] = fill; b[i][k] = fill; }
+  }
+}
+
+// The head/tail element of this lane (column `ec`, or -1: none) without a
+// divergent branch: lanes with none re-read column 0 and take `fill`.
+template <typename Ts>
+__device__ __forceinline__ float load_extra(const Ts* row, int ec, float fill) {
+  const float v = load1(row + (ec >= 0 ? ec : 0));
+  return ec >= 0 ? v : fill;
+}
+
+template <typename Ts, int T, int NV, int EPV, int AL>
+__device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                              const float (&v)[NV][EPV]) {
   Ts* base = row + g.head;
   const uint32_t lo = (uint32_t)tid * EPV;
@@ -294,8 +338,8 @@ __device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV>& g, int
 // path share their phase with the parameter vectors, so chunk columns map
 // to aligned parameter chunks). Only valid when g.nvec > 0 (callers test it
 // once, uniformly); slots past the row end read the last chunk.
-template <typename Ts, int T, int EPV>
-__device__ __forceinline__ void load_param_slot(const Ts* par, const RowGeom<EPV>& g, int tid, int i,
+template <typename Ts, int T, int EPV, int AL>
+__device__ __forceinline__ void load_param_slot(const Ts* par, const RowGeom<EPV, AL>& g, int tid, int i,
                                                 float* w) {
   const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
   uint32_t o = (uint32_t)(i * T * EPV) + (uint32_t)tid * EPV;
@@ -343,6 +387,21 @@ struct SumState {
 struct SumMerge {
   __device__ __forceinline__ SumState operator()(const SumState& a, const SumState& b) const {
     return {a.s + b.s};
+  }
+};
+
+// Two independent sums (backward kernels: e.g. sum h^2 and sum dy*w*h).
+struct Sum2State {
+  float a, b;
+  template <int C, int M>
+  static __device__ __forceinline__ Sum2State move(const Sum2State& v) {
+    return {dpp_move<C, M>(v.a, 0.f), dpp_move<C, M>(v.b, 0.f)};
+  }
+  __device__ __forceinline__ Sum2State lane63() const { return {read_lane63(a), read_lane63(b)}; }
+};
+struct Sum2Merge {
+  __device__ __forceinline__ Sum2State operator()(const Sum2State& x, const Sum2State& y) const {
+    return {x.a + y.a, x.b + y.b};
   }
 };
 

@@ -37,15 +37,49 @@ typedef hipError_t (*RmsNormLaunch)(const void* x, const void* res, const void* 
 typedef hipError_t (*XentLaunch)(const void* logits, const int32_t* labels, float* loss, void* grad,
                                  int32_t* argmax, int64_t rows, int cols, hipStream_t s);
 
+// Backward launchers. The norm backward kernels run `grid` workgroups of
+// kBwdBlock lanes and leave one fp32 partial row per workgroup and parameter
+// gradient in ws ([nparams][grid][cols]); launch_colsum reduces them.
+typedef hipError_t (*SoftmaxBwdLaunch)(const void* p, const void* dy, void* dx, int64_t rows,
+                                       int cols, hipStream_t s);
+typedef hipError_t (*RmsNormBwdLaunch)(const void* h, const void* dy, const void* dres,
+                                       const void* w, void* dh, float* ws, int grid, int64_t rows,
+                                       int cols, float eps, hipStream_t s);
+typedef hipError_t (*LayerNormBwdLaunch)(const void* x, const void* dy, const void* gamma,
+                                         const float* mean, const float* rstd, void* dx, float* ws,
+                                         int grid, int64_t rows, int cols, hipStream_t s);
+
+constexpr int kBwdBlock = 1024;  // lanes per norm-backward workgroup
+constexpr int kBwdGrid = 256;    // most norm-backward workgroups (= partial rows)
+
+// Workgroups (partial rows) of a norm backward launch whose row groups have
+// `threads` lanes each.
+inline int bwd_grid(int threads, int64_t rows) {
+  const int64_t rpb = kBwdBlock / threads;
+  const int64_t g = (rows + rpb - 1) / rpb;
+  return (int)(g < kBwdGrid ? g : kBwdGrid);
+}
+
 typedef Variant<SoftmaxLaunch> SoftmaxVariant;
 typedef Variant<LayerNormLaunch> LayerNormVariant;
 typedef Variant<RmsNormLaunch> RmsNormVariant;
 typedef Variant<XentLaunch> XentVariant;
+typedef Variant<SoftmaxBwdLaunch> SoftmaxBwdVariant;
+typedef Variant<RmsNormBwdLaunch> RmsNormBwdVariant;
+typedef Variant<LayerNormBwdLaunch> LayerNormBwdVariant;
 
 VariantSpan<SoftmaxVariant> softmax_variants(int in_bf16, int out_bf16);
 VariantSpan<LayerNormVariant> layernorm_variants(int bf16);
 VariantSpan<RmsNormVariant> rmsnorm_variants(int bf16);
 VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
+VariantSpan<SoftmaxBwdVariant> softmax_bwd_variants(int bf16);
+VariantSpan<RmsNormBwdVariant> rmsnorm_bwd_variants(int bf16);
+VariantSpan<LayerNormBwdVariant> layernorm_bwd_variants(int bf16);
+
+// out0[c] (and out1[c] when out1 != NULL) = sum over b < partials of
+// ws[p][b][c], in order of b; partials == 0 writes zeros.
+hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, float* out1,
+                         hipStream_t s);
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 

@@ -14,6 +14,9 @@ bf16 outputs: bit patterns mapped to ordered integers; pass iff within one
   bf16 ulp of the oracle value rounded to nearest even. LayerNorm y, which
   crosses zero by cancellation, may instead be within 1e-5 * max(|o|, 1)
   (the same floor as its fp32 rule); the ulp histogram is still reported.
+  Backward outputs formed by cancellation (dx = p (dy - s) and the like) may
+  instead meet the fp32 rule at a condition-aware scale, plus the final
+  rounding to bf16.
 int32 outputs: exact.
 """
 import numpy as np
@@ -62,15 +65,24 @@ def bf16_value(bits):
     return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def check_bf16(got_bits, ref_bits, what="", max_ulp=1, abs_floor=None):
+def check_bf16(got_bits, ref_bits, what="", max_ulp=1, abs_floor=None, cond=None):
     """Within max_ulp bf16 ulps of the rounded oracle. With abs_floor, an
     element also passes if |g - o| <= abs_floor * max(|o|, 1) (outputs formed
-    by cancellation; the histogram still reports their ulp distance)."""
+    by cancellation; the histogram still reports their ulp distance).
+    With cond = (ref, scale), the oracle's unrounded values and the magnitude
+    its fp32 error scales with, an element also passes if
+    |g - ref| <= 1e-5 * scale + 2^-8 * max(|g|, |ref|): the fp32 rule, plus
+    the one rounding to bf16 of the result."""
     d = np.abs(ordered(got_bits) - ordered(ref_bits))
     hist = {"0": int((d == 0).sum()), "1": int((d == 1).sum()), ">1": int((d > 1).sum())}
     if abs_floor is not None and hist[">1"]:
         g, o = bf16_value(got_bits), bf16_value(ref_bits)
         near = np.abs(g - o) <= abs_floor * np.maximum(np.abs(o), 1.0)
+        d = np.where(near, 0, d)
+    if cond is not None and hist[">1"]:
+        ref, scale = (np.asarray(a, dtype=np.float64) for a in cond)
+        g = bf16_value(got_bits)
+        near = np.abs(g - ref) <= REL * scale + 2.0 ** -8 * np.maximum(np.abs(g), np.abs(ref))
         d = np.where(near, 0, d)
     if d.max(initial=0) > max_ulp:
         i = int(np.argmax(d))

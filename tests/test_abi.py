@@ -99,6 +99,75 @@ def test_xent_validation():
     assert f(P(A), P(L), P(LS), P(A + 4), None, 4, 8, 0, None) == E_ALIAS
 
 
+def test_softmax_bwd_validation():
+    f = fr.lib.fr_softmax_bwd
+    D, X = A + 0x100000, A + 0x200000
+    assert f(P(A), P(D), P(X), 0, 8, 0, None) == OK
+    assert f(None, None, None, 0, 8, 1, None) == OK
+    assert f(P(A), P(D), P(X), 4, fr.FR_BWD_MAX_COLS + 1, 0, None) == E_SHAPE
+    assert f(P(A), None, P(X), 4, 8, 0, None) == E_NULL
+    assert f(P(A), P(D), P(X), 4, 8, 2, None) == E_DTYPE
+    assert f(P(A), P(D), P(D + 4), 4, 8, 0, None) == E_ALIAS   # partial overlap with dy
+    assert f(P(A), P(A), P(A + 4), 4, 8, 0, None) == E_ALIAS
+    assert f(P(A), P(D), P(X + 2), 4, 8, 0, None) == E_ALIGN
+
+
+def test_norm_bwd_workspace_bytes():
+    f = fr.fr_norm_bwd_workspace_bytes
+    assert f(fr.OP_RMSNORM_BWD, 8192, 8192) == fr.FR_BWD_PARTIALS * 8192 * 4
+    assert f(fr.OP_LAYERNORM_BWD, 4096, 1024) == fr.FR_BWD_PARTIALS * 1024 * 4 * 2
+    assert f(fr.OP_RMSNORM_BWD, 3, 100) == 3 * 100 * 4
+    assert f(fr.OP_LAYERNORM_BWD, 0, 100) == 0
+    for op, r, c in ((fr.OP_SOFTMAX, 4, 8), (fr.OP_RMSNORM_BWD, -1, 8),
+                     (fr.OP_RMSNORM_BWD, 4, fr.FR_BWD_MAX_COLS + 1), (fr.OP_LAYERNORM_BWD, 4, 0)):
+        with pytest.raises(ValueError):
+            f(op, r, c)
+
+
+def test_rmsnorm_bwd_validation():
+    f = fr.lib.fr_add_rmsnorm_bwd
+    DY, DR, W, DH, DW, WS = (A + k * 0x100000 for k in range(1, 7))
+    need = 4 * 8 * 4
+
+    def call(h=A, dy=DY, dres=DR, w=W, dh=DH, dw=DW, ws=WS, wsb=need, rows=4, cols=8, eps=1e-6,
+             dt=0):
+        return f(P(h), P(dy), P(dres), P(w), P(dh), P(dw), P(ws), wsb, rows, cols, eps, dt, None)
+
+    assert call(dw=0, rows=0) == E_NULL                # dweight is written even for rows == 0
+    assert call(dw=DW + 2, rows=0) == E_ALIGN
+    assert call(wsb=need - 1) == E_SHAPE
+    assert call(cols=fr.FR_BWD_MAX_COLS + 1) == E_SHAPE
+    assert call(eps=-1.0) == E_VALUE
+    assert call(dt=5) == E_DTYPE
+    assert call(ws=0) == E_NULL
+    assert call(dy=0) == E_NULL
+    assert call(ws=WS + 4) == E_ALIGN                  # workspace: 16-byte aligned
+    assert call(dres=DR + 2) == E_ALIGN
+    assert call(ws=DH + 64) == E_ALIAS                 # workspace inside dh
+    assert call(dw=W) == E_ALIAS                       # dweight over weight
+    assert call(dh=DY + 4) == E_ALIAS                  # partial overlap with dy
+
+
+def test_layernorm_bwd_validation():
+    f = fr.lib.fr_layernorm_bwd
+    DY, G, M, R, DX, DG, DB, WS = (A + k * 0x100000 for k in range(1, 9))
+    need = 4 * 8 * 4 * 2
+
+    def call(x=A, dy=DY, g=G, m=M, r=R, dx=DX, dg=DG, db=DB, ws=WS, wsb=need, rows=4, cols=8, dt=1):
+        return f(P(x), P(dy), P(g), P(m), P(r), P(dx), P(dg), P(db), P(ws), wsb, rows, cols, dt,
+                 None)
+
+    assert call(db=0, rows=0) == E_NULL
+    assert call(dg=DB, rows=0) == E_ALIAS              # the two gradients may not coincide
+    assert call(wsb=need - 4) == E_SHAPE
+    assert call(m=0) == E_NULL
+    assert call(r=R + 2) == E_ALIGN
+    assert call(x=A + 1) == E_ALIGN                    # bf16 needs 2-byte alignment
+    assert call(ws=DX) == E_ALIAS
+    assert call(dg=M) == E_ALIAS                       # an output over an input
+    assert call(dx=DY + 2) == E_ALIAS
+
+
 def test_stream_copy_validation():
     f = fr.lib.fr_stream_copy
     assert f(P(A), P(B), 0, None) == OK
@@ -120,6 +189,15 @@ def test_variant_selection():
             for vp in (True, False):
                 t, v, e = fr.fr_debug_select_variant(op, c, fr.F32, vector_path=vp)
                 assert t * v * e >= c
+    for op in (fr.OP_SOFTMAX_BWD, fr.OP_RMSNORM_BWD, fr.OP_LAYERNORM_BWD):
+        for dt in (fr.F32, fr.BF16):
+            for c in (1, 3, 8, 64, 1000, 1024, 4096, 8192, fr.FR_BWD_MAX_COLS):
+                for vp in (True, False):
+                    t, v, e = fr.fr_debug_select_variant(op, c, dt, vector_path=vp)
+                    assert t * v * e >= c
+            with pytest.raises(fr.FusedRowError) as ei:
+                fr.fr_debug_select_variant(op, fr.FR_BWD_MAX_COLS + 1, dt)
+            assert ei.value.status == E_SHAPE
     with fr.forced_variant(fr.OP_SOFTMAX, 1024, 16):
         assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (1024, 16, 4)
     assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (64, 4, 4)

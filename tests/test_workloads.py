@@ -36,6 +36,18 @@ def test_distributions():
     assert wt.min() >= 0.79 and wt.max() <= 1.21
 
 
+def test_backward_distributions():
+    def f(b):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w = workloads.make("add_rmsnorm_bwd_bf16", rows=64, cols=4096)
+    assert abs(f(w["h"]).var() - 2.0) < 0.03
+    assert abs(f(w["dy"]).std() - 1.0) < 0.01 and abs(f(w["dres"]).std() - 1.0) < 0.01
+    w = workloads.make("layernorm_bwd_f32", rows=64, cols=1024)
+    assert abs(w["x"].mean() - 3.0) < 0.03 and abs(w["dy"].std() - 1.0) < 0.01
+    w = workloads.make("softmax_bwd_bf16", rows=64, cols=4096)
+    assert set(w.arrays) == {"x", "dy"}
+
+
 def test_bf16_storage_rounding():
     v = np.array([1.0, 1 + 2**-8, 1 + 3 * 2**-8, -2.5, 3.0e38], dtype=np.float32)
     assert list(workloads.f32_to_bf16_bits(v)) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x7F62]

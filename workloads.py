@@ -26,6 +26,18 @@ variance, so N(0, 4^2) has standard deviation 4):
   xent_f32         logits ~ N(0, 2^2) fp32 [4096, 50257];
                    labels ~ U{0, ..., 50256} int32 [4096]              seed 1005
 
+Backward workloads, at the forward workloads' shapes (the per-row forward
+statistics they consume, p = softmax(x) and LayerNorm's mean / rstd, are not
+drawn here: the tests take them from the oracle, the benchmark from the
+forward kernels):
+
+  softmax_bwd_bf16    x ~ as softmax_bf16 [16384, 4096]; dy ~ N(0, 1)  seed 1006
+  layernorm_bwd_f32   x ~ N(3, 2^2) [4096, 1024]; gamma ~ U(0.5, 1.5)
+                      [1024]; dy ~ N(0, 1); eps 1e-5 (of the forward)  seed 1007
+  add_rmsnorm_bwd_bf16 h ~ N(0, 2) (the updated residual x + r of two
+                      N(0, 1) draws) [8192, 8192]; w ~ U(0.8, 1.2) [8192];
+                      dy, dres ~ N(0, 1); eps 1e-6                     seed 1008
+
 ``make(name, rows=None, cols=None)`` builds a workload with the standard
 distributions at any shape (used for edge-shape and small parity cases); the
 seed stays the workload's own unless ``seed`` is given.
@@ -66,6 +78,17 @@ WORKLOADS = {
     "xent_f32": Spec("xent_f32", "xent", 4096, 50257, 1005, "f32",
                      desc="fp32 softmax cross-entropy fwd+bwd, 4096 x 50257, "
                           "logits ~ N(0, 2^2), labels ~ U{0..50256}"),
+    "softmax_bwd_bf16": Spec("softmax_bwd_bf16", "softmax_bwd", 16384, 4096, 1006, "bf16",
+                             desc="bf16 softmax backward, 16384 x 4096, p = softmax(x) of the "
+                                  "softmax_bf16 recipe, dy ~ N(0,1)"),
+    "layernorm_bwd_f32": Spec("layernorm_bwd_f32", "layernorm_bwd", 4096, 1024, 1007, "f32",
+                              eps=1e-5,
+                              desc="fp32 LayerNorm backward, 4096 x 1024, x ~ N(3, 2^2), "
+                                   "gamma ~ U(0.5,1.5), dy ~ N(0,1)"),
+    "add_rmsnorm_bwd_bf16": Spec("add_rmsnorm_bwd_bf16", "add_rmsnorm_bwd", 8192, 8192, 1008,
+                                 "bf16", eps=1e-6,
+                                 desc="bf16 residual-add + RMSNorm backward, 8192 x 8192, "
+                                      "h ~ N(0, 2), w ~ U(0.8,1.2), dy, dres ~ N(0,1)"),
 }
 
 
@@ -148,6 +171,20 @@ def make(name: str, rows: int | None = None, cols: int | None = None,
     elif name == "xent_f32":
         arr["logits"] = _store(rng.normal(0.0, 2.0, size=(R, C)), dt)
         arr["labels"] = rng.integers(0, C, size=R, dtype=np.int64).astype(np.int32)
+    elif name == "softmax_bwd_bf16":
+        z = rng.normal(0.0, 1.0, size=(R, C))
+        z *= rng.uniform(1.0, 60.0, size=(R, 1))
+        arr["x"] = _store(z, dt)
+        arr["dy"] = _store(rng.normal(0.0, 1.0, size=(R, C)), dt)
+    elif name == "layernorm_bwd_f32":
+        arr["x"] = _store(rng.normal(3.0, 2.0, size=(R, C)), dt)
+        arr["gamma"] = _store(rng.uniform(0.5, 1.5, size=C), dt)
+        arr["dy"] = _store(rng.normal(0.0, 1.0, size=(R, C)), dt)
+    elif name == "add_rmsnorm_bwd_bf16":
+        arr["h"] = _store(rng.normal(0.0, np.sqrt(2.0), size=(R, C)), dt)
+        arr["weight"] = _store(rng.uniform(0.8, 1.2, size=C), dt)
+        arr["dy"] = _store(rng.normal(0.0, 1.0, size=(R, C)), dt)
+        arr["dres"] = _store(rng.normal(0.0, 1.0, size=(R, C)), dt)
     else:
         raise KeyError(name)
     return Workload(spec=spec, rows=R, cols=C, seed=s, arrays=arr)

@@ -19,7 +19,14 @@ Printed: ONE JSON line (rank 0), with per-workload figures, the roofline of
 the dominant kernel (the cross-entropy launch), the streaming-copy ceiling,
 and the CPU oracle timed on the host cores as a baseline.
 
+The backward entry points are measured after the step, per call, at the
+forward workloads' shapes (softmax bf16 [16384, 4096], LayerNorm fp32
+[4096, 1024], residual-add + RMSNorm bf16 [8192, 8192]); they are reported
+under "backward" and are not part of `value`. Their per-row inputs from the
+forward (p, mean, rstd) are produced by the forward kernels before timing.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                      [--no-backward] [--graph]
 """
 from __future__ import annotations
 
@@ -53,6 +60,93 @@ def algo_bytes(name, R, C):
     if name == "xent_f32":
         return 2 * R * C * 4 + R * 4 + R * 4                   # logits, grad; labels, loss
     raise KeyError(name)
+
+
+def bwd_algo_bytes(name, R, C):
+    """Backward: each row operand and parameter read once, each gradient
+    written once (the partial sums in the workspace are not counted)."""
+    if name == "softmax_bwd_bf16":
+        return 3 * R * C * 2                                   # p, dy; dx
+    if name == "layernorm_bwd_f32":
+        return 3 * R * C * 4 + C * 4 + 2 * R * 4 + 2 * C * 4   # x, dy, dx; gamma; mean, rstd; dg, db
+    if name == "add_rmsnorm_bwd_bf16":
+        return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
+    raise KeyError(name)
+
+
+class BwdWorkload:
+    def __init__(self, name, w, dev, torch, fr):
+        import numpy as np
+        self.name, self.w = name, w
+        self.R, self.C = w.rows, w.cols
+        self.bytes = bwd_algo_bytes(name, self.R, self.C)
+
+        def d(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        def ws(op):
+            n = fr.fr_norm_bwd_workspace_bytes(op, self.R, self.C)
+            return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+
+        if name == "softmax_bwd_bf16":
+            self.p = fr.softmax(d(w["x"]))
+            self.dy = d(w["dy"])
+            self.dx = torch.empty_like(self.p)
+            self.run = lambda: fr.fr_softmax_bwd(self.p, self.dy, self.dx)
+            self.op, self.code = fr.OP_SOFTMAX_BWD, fr.BF16
+        elif name == "layernorm_bwd_f32":
+            self.x, self.g, self.dy = d(w["x"]), d(w["gamma"]), d(w["dy"])
+            _, self.mean, self.rstd = fr.layernorm(self.x, self.g, torch.zeros_like(self.g), w.eps)
+            self.dx = torch.empty_like(self.x)
+            self.dg = torch.empty(self.C, device=dev)
+            self.db = torch.empty(self.C, device=dev)
+            self.ws = ws(fr.OP_LAYERNORM_BWD)
+            self.run = lambda: fr.fr_layernorm_bwd(self.x, self.dy, self.g, self.mean, self.rstd,
+                                                   self.dx, self.dg, self.db, self.ws)
+            self.op, self.code = fr.OP_LAYERNORM_BWD, fr.F32
+        elif name == "add_rmsnorm_bwd_bf16":
+            self.h, self.dy, self.dres = d(w["h"]), d(w["dy"]), d(w["dres"])
+            self.wt = d(w["weight"])
+            self.dh = torch.empty_like(self.h)
+            self.dw = torch.empty(self.C, device=dev)
+            self.ws = ws(fr.OP_RMSNORM_BWD)
+            self.run = lambda: fr.fr_add_rmsnorm_bwd(self.h, self.dy, self.wt, self.dh, self.dw,
+                                                     self.ws, dres=self.dres, eps=w.eps)
+            self.op, self.code = fr.OP_RMSNORM_BWD, fr.BF16
+        self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
+
+
+def time_calls(torch, np, runs, K):
+    """Per-call durations (us) of each callable, HIP events around each call
+    on the current stream, K rounds of all of them in turn."""
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in runs] for _ in range(K)]
+    for k in range(K):
+        for run, (a, b) in zip(runs, evs[k]):
+            a.record()
+            run()
+            b.record()
+    torch.cuda.synchronize()
+    return [np.array([evs[k][i][0].elapsed_time(evs[k][i][1]) * 1e3 for k in range(K)])
+            for i in range(len(runs))]
+
+
+def launch_stats(w, us):
+    import numpy as np
+    med, mean = float(np.median(us)), float(us.mean())
+    return {
+        "rows": w.R, "cols": w.C, "algo_bytes": w.bytes,
+        "variant": {"threads": w.variant[0], "vecs": w.variant[1], "elems_per_vec": w.variant[2]},
+        "median_us": round(med, 3), "mean_us": round(mean, 3),
+        "p10_us": round(float(np.percentile(us, 10)), 3),
+        "p90_us": round(float(np.percentile(us, 90)), 3),
+        "gbps": round(w.bytes / (med * 1e-6) / 1e9, 1),
+        "pct_peak": round(100 * w.bytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(w.R / (med * 1e-6), 1),
+        "input_sha256": w.w.digest()[:16],
+    }
 
 
 def kernel_source_digest():
@@ -178,6 +272,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurements")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph (the launches are capture-safe)")
     ap.add_argument("--quiet", action="store_true", help="no progress lines on stderr")
@@ -244,30 +339,23 @@ def main():
     log(f"timed {K} steps: {ms_per_step:.3f} ms/step")
 
     # per-launch durations: a second pass with HIP events around each launch
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in wls] for _ in range(K)]
-    for k in range(K):
-        for w, (a, b) in zip(wls, evs[k]):
-            a.record()
-            w.run()
-            b.record()
-    torch.cuda.synchronize()
+    per = {w.name: launch_stats(w, us)
+           for w, us in zip(wls, time_calls(torch, np, [w.run for w in wls], K))}
 
-    per = {}
-    for i, w in enumerate(wls):
-        us = np.array([evs[k][i][0].elapsed_time(evs[k][i][1]) * 1e3 for k in range(K)])
-        med, mean = float(np.median(us)), float(us.mean())
-        per[w.name] = {
-            "rows": w.R, "cols": w.C, "algo_bytes": w.bytes,
-            "variant": {"threads": w.variant[0], "vecs": w.variant[1], "elems_per_vec": w.variant[2]},
-            "median_us": round(med, 3), "mean_us": round(mean, 3),
-            "p10_us": round(float(np.percentile(us, 10)), 3),
-            "p90_us": round(float(np.percentile(us, 90)), 3),
-            "gbps": round(w.bytes / (med * 1e-6) / 1e9, 1),
-            "pct_peak": round(100 * w.bytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
-            "rows_per_s": round(w.R / (med * 1e-6), 1),
-            "input_sha256": w.w.digest()[:16],
-        }
+    backward = {}
+    if not args.no_backward:
+        bws = []
+        for n in ("softmax_bwd_bf16", "layernorm_bwd_f32", "add_rmsnorm_bwd_bf16"):
+            t0 = time.perf_counter()
+            bws.append(BwdWorkload(n, workloads.make(n), dev, torch, fr))
+            log(f"generated {n} in {time.perf_counter() - t0:.1f} s")
+        for _ in range(max(3, args.warmup)):
+            for b in bws:
+                b.run()
+        torch.cuda.synchronize()
+        backward = {b.name: launch_stats(b, us)
+                    for b, us in zip(bws, time_calls(torch, np, [b.run for b in bws], K))}
+        log("backward calls timed")
 
     ceiling = copy_ceiling(torch, fr, dev)
     log(f"copy ceiling {ceiling:.0f} GB/s")
@@ -301,6 +389,7 @@ def main():
             "launch": "hip graph replay of the five launches" if graph else "eager launches",
         },
         "per_workload": per,
+        "backward": backward,
         "roofline": {
             "bound": "hbm",
             "kernel": f"xent_kernel<float,{dom['variant']['threads']},{dom['variant']['vecs']},"

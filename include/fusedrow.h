@@ -154,7 +154,7 @@ FR_API fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* la
  * larger: two row operands and, for the norms, per-column partial sums). */
 #define FR_BWD_MAX_COLS 16384
 /* Most partial rows a norm backward call leaves in its workspace. */
-#define FR_BWD_PARTIALS 256
+#define FR_BWD_PARTIALS 512
 
 /* Softmax backward (vector-Jacobian product) from the stored forward output.
  *   s = sum_k p_k dy_k,  dx_j = p_j (dy_j - s)   per row.

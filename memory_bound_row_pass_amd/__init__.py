@@ -31,7 +31,7 @@ OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
 OP_SOFTMAX_BWD, OP_RMSNORM_BWD, OP_LAYERNORM_BWD = 4, 5, 6
 FR_MAX_COLS = 65536
 FR_BWD_MAX_COLS = 16384
-FR_BWD_PARTIALS = 256
+FR_BWD_PARTIALS = 512
 # FUSEDROW_LIB may name an alternative build of the same library (A/B runs).
 LIB_PATH = os.environ.get("FUSEDROW_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libfusedrow.so")

@@ -357,7 +357,7 @@ fr_status_t fr_add_rmsnorm_bwd(const void* h, const void* dy, const void* dres, 
   const fr::RmsNormBwdVariant* v = select_variant(fr::rmsnorm_bwd_variants(dtype == FR_BF16),
                                                   FR_OP_RMSNORM_BWD, cols, vec ? vec_epv(es) : 1);
   if (!v) return g_forced[FR_OP_RMSNORM_BWD].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
-  const int grid = fr::bwd_grid(v->threads, rows);
+  const int grid = fr::bwd_grid(*v, rows);
   float* ws = static_cast<float*>(workspace);
   if (fr_status_t s = launch_status(v->launch(h, dy, dres, weight, dh, ws, grid, rows, (int)cols,
                                               eps, st)))
@@ -404,7 +404,7 @@ fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* gamma, c
   const fr::LayerNormBwdVariant* v = select_variant(fr::layernorm_bwd_variants(dtype == FR_BF16),
                                                     FR_OP_LAYERNORM_BWD, cols, vec ? vec_epv(es) : 1);
   if (!v) return g_forced[FR_OP_LAYERNORM_BWD].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
-  const int grid = fr::bwd_grid(v->threads, rows);
+  const int grid = fr::bwd_grid(*v, rows);
   float* ws = static_cast<float*>(workspace);
   if (fr_status_t s = launch_status(v->launch(x, dy, gamma, mean, rstd, dx, ws, grid, rows,
                                               (int)cols, st)))

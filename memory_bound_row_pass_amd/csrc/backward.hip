@@ -17,13 +17,14 @@
 //   dgamma_j = sum_rows dy_j n_j,   dbeta_j = sum_rows dy_j.
 //
 // Parameter gradients are column sums over all rows. The norm kernels run a
-// fixed grid of kBwdGrid workgroups of kBwdBlock lanes; every lane owns the
-// same columns in every row it visits (rows on the 16-byte grid, no head
-// peel), so it accumulates its columns' partial sums in registers across its
-// rows. At the end the row groups of a workgroup are summed through LDS in a
-// fixed order and the workgroup writes one partial row per parameter to the
-// workspace; colsum_kernel then adds the partial rows in a fixed order.
-// There are no atomics: results are bitwise reproducible run to run.
+// persistent grid of at most grid_max workgroups, each of RPB row groups of
+// T lanes; every lane owns the same columns in every row it visits (rows on
+// the 16-byte grid, no head peel), so it accumulates its columns' partial
+// sums in registers across its rows. At the end the row groups of a
+// workgroup are summed through LDS in a fixed order and the workgroup writes
+// one partial row per parameter to the workspace; colsum_kernel then adds
+// the partial rows in a fixed order. There are no atomics: results are
+// bitwise reproducible run to run.
 #include "fr_kernels.hpp"
 #include "fr_device.hpp"
 
@@ -180,8 +181,23 @@ struct Slots {
       }
   }
   template <typename Ts>
-  __device__ __forceinline__ void load(const Ts* r, int i, float* v) const {
-    Vec<Ts, EPV>::load(r + off(i), v);
+  __device__ __forceinline__ void load3(const Ts* ra, const Ts* rb, const Ts* rc,
+                                        float (&a)[NV][EPV], float (&b)[NV][EPV],
+                                        float (&c)[NV][EPV]) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      Vec<Ts, EPV>::load(ra + off(i), a[i]);
+      Vec<Ts, EPV>::load(rb + off(i), b[i]);
+      Vec<Ts, EPV>::load(rc + off(i), c[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        a[i][k] = ok(i) ? a[i][k] : 0.f;
+        b[i][k] = ok(i) ? b[i][k] : 0.f;
+        c[i][k] = ok(i) ? c[i][k] : 0.f;
+      }
   }
   template <typename Ts>
   __device__ __forceinline__ void param(const Ts* par, int i, float* v) const {
@@ -213,9 +229,9 @@ __device__ __forceinline__ const T* fresh(const T* p) {
 // The row loop runs the same number of times in every wave of the
 // workgroup (block-wide barriers inside); a row group past the last row
 // takes part in the barriers with no data.
-template <int T>
+template <int T, int RPB_>
 struct BwdLanes {
-  static constexpr int RPB = kBwdBlock / T;
+  static constexpr int RPB = RPB_;
   static constexpr int NW = T / 64;
   int lane, sub, wave, tid;
   __device__ __forceinline__ BwdLanes() {
@@ -229,14 +245,16 @@ struct BwdLanes {
 
 // ------------------------------------------------ residual add + RMSNorm bwd
 
-template <typename Ts, int T, int NV, int EPV>
-__global__ __launch_bounds__(kBwdBlock)
+// DRES: the gradient through the updated residual is given; its loads are
+// issued with those of h and dy, before the row reduction.
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool DRES>
+__global__ __launch_bounds__(T * RPB) __attribute__((amdgpu_waves_per_eu(OCC)))
 void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, Ts* dh, float* ws,
                         int64_t rows, int cols, float eps) {
-  using L = BwdLanes<T>;
-  constexpr int RPB = L::RPB, NW = L::NW;
+  using L = BwdLanes<T, RPB>;
+  constexpr int NW = L::NW;
   __shared__ float xw[RPB][2][NW][2];
-  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? kBwdBlock * EPV : 4];
+  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
   const L ln;
   const Slots<T, NV, EPV> sl(cols, ln.tid);
 
@@ -253,8 +271,9 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
     const bool live = row < rows;  // uniform in the wave; a dead group re-reads the last row
     const int64_t off = (live ? row : rows - 1) * cols;
 
-    float hv[NV][EPV], d[NV][EPV];
-    sl.load2(h + off, dy + off, hv, d);
+    float hv[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
+    if constexpr (DRES) sl.load3(h + off, dy + off, dres + off, hv, d, dr);
+    else sl.load2(h + off, dy + off, hv, d);
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
     const Ts* w1 = fresh(w);
 #pragma unroll
@@ -284,16 +303,9 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           acc[i][k] = __builtin_fmaf(d[i][k] * hv[i][k], r, acc[i][k]);
-          hv[i][k] = r * __builtin_fmaf(-hv[i][k], c, wt[k] * d[i][k]);
-        }
-      }
-      if (dres) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          float dr[EPV];
-          sl.load(dres + off, i, dr);
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) hv[i][k] += dr[k];
+          const float t = r * __builtin_fmaf(-hv[i][k], c, wt[k] * d[i][k]);
+          if constexpr (DRES) hv[i][k] = t + dr[i][k];
+          else hv[i][k] = t;
         }
       }
       sl.store(dh + off, hv);
@@ -304,14 +316,14 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 
 // ------------------------------------------------------------ LayerNorm bwd
 
-template <typename Ts, int T, int NV, int EPV>
-__global__ __launch_bounds__(kBwdBlock)
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
+__global__ __launch_bounds__(T * RPB) __attribute__((amdgpu_waves_per_eu(OCC)))
 void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const float* mean,
                           const float* rstd, Ts* dx, float* ws, int64_t rows, int cols) {
-  using L = BwdLanes<T>;
-  constexpr int RPB = L::RPB, NW = L::NW;
+  using L = BwdLanes<T, RPB>;
+  constexpr int NW = L::NW;
   __shared__ float xw[RPB][2][NW][2];
-  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? kBwdBlock * EPV : 4];
+  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
   const L ln;
   const Slots<T, NV, EPV> sl(cols, ln.tid);
 
@@ -376,35 +388,47 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
 
 // ------------------------------------------------------------ column sums
 // out_p[c] = sum over the partial rows b = 0 .. partials-1 of ws[p][b][c],
-// parameter p = blockIdx.y. 16 waves per 64-column tile: wave ty sums rows
-// ty, ty+16, ... in order, then wave 0 adds the 16 sums in order.
-__global__ __launch_bounds__(1024) void colsum_kernel(const float* ws, int partials, int cols,
-                                                      float* out0, float* out1) {
-  __shared__ float red[16][64];
-  const int tx = threadIdx.x & 63;
-  const int ty = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.x * 64 + tx;
+// parameter p = blockIdx.y. A workgroup takes a 32-column tile (one 128-byte
+// line per partial row) and 32 row groups: lane group ty sums rows ty,
+// ty+32, ... in order, then the 32 group sums are added in order of ty.
+constexpr int kColTile = 32;
+constexpr int kColGroups = 32;
+
+__global__ __launch_bounds__(kColTile * kColGroups) void colsum_kernel(const float* ws, int partials,
+                                                                       int cols, float* out0,
+                                                                       float* out1) {
+  __shared__ float red[kColGroups][kColTile + 1];
+  const int tx = threadIdx.x % kColTile;
+  const int ty = threadIdx.x / kColTile;
+  const int c = blockIdx.x * kColTile + tx;
   const float* src = ws + (size_t)blockIdx.y * partials * cols;
   float s = 0.f;
   if (c < cols) {
-#pragma unroll 4
-    for (int b = ty; b < partials; b += 16) s += src[(size_t)b * cols + c];
+    // partials <= kBwdGridMax: all of a group's loads issued before the first add
+    float v[kBwdGridMax / kColGroups];
+#pragma unroll
+    for (int j = 0; j < kBwdGridMax / kColGroups; ++j) {
+      const int b = ty + kColGroups * j;
+      v[j] = b < partials ? src[(size_t)b * cols + c] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBwdGridMax / kColGroups; ++j) s += v[j];
   }
   red[ty][tx] = s;
   __syncthreads();
   if (ty == 0 && c < cols) {
     float t = red[0][tx];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) t += red[r][tx];
+    for (int r = 1; r < kColGroups; ++r) t += red[r][tx];
     (blockIdx.y == 0 ? out0 : out1)[c] = t;
   }
 }
 
 hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, float* out1,
                          hipStream_t s) {
-  const unsigned tiles = (unsigned)((cols + 63) / 64);
-  return launch_kernel(&colsum_kernel, dim3(tiles, out1 ? 2 : 1), dim3(1024), s, ws, partials,
-                       cols, out0, out1);
+  const unsigned tiles = (unsigned)((cols + kColTile - 1) / kColTile);
+  return launch_kernel(&colsum_kernel, dim3(tiles, out1 ? 2 : 1), dim3(kColTile * kColGroups), s, ws,
+                       partials, cols, out0, out1);
 }
 
 // ------------------------------------------------------------- launchers
@@ -421,29 +445,33 @@ static hipError_t launch_softmax_bwd(const void* p, const void* dy, void* dx, in
                        rows, cols);
 }
 
-template <typename Ts, int T, int NV, int EPV>
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
 static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w,
                                      void* dh, float* ws, int grid, int64_t rows, int cols,
                                      float eps, hipStream_t s) {
-  return launch_kernel(&rmsnorm_bwd_kernel<Ts, T, NV, EPV>, dim3(grid), dim3(kBwdBlock), s,
-                       static_cast<const Ts*>(h), static_cast<const Ts*>(dy),
-                       static_cast<const Ts*>(dres), static_cast<const Ts*>(w),
-                       static_cast<Ts*>(dh), ws, rows, cols, eps);
+  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true>
+                : &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, false>;
+  return launch_kernel(k, dim3(grid), dim3(T * RPB), s, static_cast<const Ts*>(h),
+                       static_cast<const Ts*>(dy), static_cast<const Ts*>(dres),
+                       static_cast<const Ts*>(w), static_cast<Ts*>(dh), ws, rows, cols, eps);
 }
 
-template <typename Ts, int T, int NV, int EPV>
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
 static hipError_t launch_layernorm_bwd(const void* x, const void* dy, const void* gamma,
                                        const float* mean, const float* rstd, void* dx, float* ws,
                                        int grid, int64_t rows, int cols, hipStream_t s) {
-  return launch_kernel(&layernorm_bwd_kernel<Ts, T, NV, EPV>, dim3(grid), dim3(kBwdBlock), s,
+  return launch_kernel(&layernorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC>, dim3(grid), dim3(T * RPB), s,
                        static_cast<const Ts*>(x), static_cast<const Ts*>(dy),
                        static_cast<const Ts*>(gamma), mean, rstd, static_cast<Ts*>(dx), ws, rows,
                        cols);
 }
 
+// Norm backward shapes: (T, NV, EPV, RPB, OCC, grid_max). The default
+// workgroup is 1024 lanes (RPB = 1024 / T) with one workgroup per CU
+// (grid_max 256, OCC 4: at most 128 VGPRs).
+#define FR_RB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC>}
+#define FR_LB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_layernorm_bwd<TS, T, NV, EPV, RPB, OCC>}
 #define FR_SB(TS, T, NV, EPV, OCC) {T, NV, EPV, &launch_softmax_bwd<TS, T, NV, EPV, OCC>}
-#define FR_RB(TS, T, NV, EPV) {T, NV, EPV, &launch_rmsnorm_bwd<TS, T, NV, EPV>}
-#define FR_LB(TS, T, NV, EPV) {T, NV, EPV, &launch_layernorm_bwd<TS, T, NV, EPV>}
 
 static const SoftmaxBwdVariant kSbF32[] = {
     FR_SB(float, 64, 1, 4, 8),    FR_SB(float, 64, 2, 4, 8),    FR_SB(float, 64, 4, 4, 6),
@@ -456,25 +484,30 @@ static const SoftmaxBwdVariant kSbBf16[] = {
     FR_SB(bf16_t, 64, 16, 1, 4),  FR_SB(bf16_t, 256, 16, 1, 4), FR_SB(bf16_t, 1024, 16, 1, 4)};
 
 static const RmsNormBwdVariant kRbF32[] = {
-    FR_RB(float, 64, 1, 4),   FR_RB(float, 64, 2, 4),   FR_RB(float, 64, 4, 4),
-    FR_RB(float, 256, 2, 4),  FR_RB(float, 256, 4, 4),  FR_RB(float, 512, 4, 4),
-    FR_RB(float, 1024, 4, 4), FR_RB(float, 64, 16, 1),  FR_RB(float, 256, 16, 1),
-    FR_RB(float, 1024, 16, 1)};
+    FR_RB(float, 64, 1, 4, 16, 4, 256),   FR_RB(float, 64, 2, 4, 16, 4, 256),
+    FR_RB(float, 64, 4, 4, 16, 4, 256),   FR_RB(float, 256, 2, 4, 4, 4, 256),
+    FR_RB(float, 256, 4, 4, 4, 4, 256),   FR_RB(float, 512, 4, 4, 2, 4, 256),
+    FR_RB(float, 1024, 4, 4, 1, 4, 256),  FR_RB(float, 64, 16, 1, 16, 4, 256),
+    FR_RB(float, 256, 16, 1, 4, 4, 256),  FR_RB(float, 1024, 16, 1, 1, 4, 256)};
 static const RmsNormBwdVariant kRbBf16[] = {
-    FR_RB(bf16_t, 64, 1, 8),   FR_RB(bf16_t, 64, 2, 8),   FR_RB(bf16_t, 256, 1, 8),
-    FR_RB(bf16_t, 256, 2, 8),  FR_RB(bf16_t, 512, 2, 8),
-    FR_RB(bf16_t, 1024, 2, 8), FR_RB(bf16_t, 64, 16, 1),  FR_RB(bf16_t, 256, 16, 1),
-    FR_RB(bf16_t, 1024, 16, 1)};
+    FR_RB(bf16_t, 64, 1, 8, 16, 4, 256),  FR_RB(bf16_t, 64, 2, 8, 16, 4, 256),
+    FR_RB(bf16_t, 256, 1, 8, 4, 4, 256),  FR_RB(bf16_t, 256, 2, 8, 4, 4, 256),
+    FR_RB(bf16_t, 512, 2, 8, 2, 4, 256),  FR_RB(bf16_t, 1024, 2, 8, 1, 4, 256),
+    FR_RB(bf16_t, 64, 16, 1, 16, 4, 256), FR_RB(bf16_t, 256, 16, 1, 4, 4, 256),
+    FR_RB(bf16_t, 1024, 16, 1, 1, 4, 256)};
 
 static const LayerNormBwdVariant kLbF32[] = {
-    FR_LB(float, 64, 1, 4),   FR_LB(float, 64, 2, 4),   FR_LB(float, 64, 4, 4),
-    FR_LB(float, 256, 2, 4),  FR_LB(float, 256, 4, 4),  FR_LB(float, 512, 4, 4),
-    FR_LB(float, 1024, 4, 4), FR_LB(float, 64, 16, 1),  FR_LB(float, 256, 16, 1),
-    FR_LB(float, 1024, 16, 1)};
+    FR_LB(float, 64, 1, 4, 16, 4, 256),   FR_LB(float, 64, 2, 4, 16, 4, 256),
+    FR_LB(float, 64, 4, 4, 16, 4, 256),   FR_LB(float, 256, 2, 4, 4, 4, 256),
+    FR_LB(float, 256, 4, 4, 4, 4, 256),   FR_LB(float, 512, 4, 4, 2, 4, 256),
+    FR_LB(float, 1024, 4, 4, 1, 4, 256),  FR_LB(float, 64, 16, 1, 16, 4, 256),
+    FR_LB(float, 256, 16, 1, 4, 4, 256),  FR_LB(float, 1024, 16, 1, 1, 4, 256)};
 static const LayerNormBwdVariant kLbBf16[] = {
-    FR_LB(bf16_t, 64, 1, 8),   FR_LB(bf16_t, 64, 2, 8),   FR_LB(bf16_t, 256, 1, 8),
-    FR_LB(bf16_t, 256, 2, 8),  FR_LB(bf16_t, 512, 2, 8),  FR_LB(bf16_t, 1024, 2, 8),
-    FR_LB(bf16_t, 64, 16, 1),  FR_LB(bf16_t, 256, 16, 1), FR_LB(bf16_t, 1024, 16, 1)};
+    FR_LB(bf16_t, 64, 1, 8, 16, 4, 256),  FR_LB(bf16_t, 64, 2, 8, 16, 4, 256),
+    FR_LB(bf16_t, 256, 1, 8, 4, 4, 256),  FR_LB(bf16_t, 256, 2, 8, 4, 4, 256),
+    FR_LB(bf16_t, 512, 2, 8, 2, 4, 256),  FR_LB(bf16_t, 1024, 2, 8, 1, 4, 256),
+    FR_LB(bf16_t, 64, 16, 1, 16, 4, 256), FR_LB(bf16_t, 256, 16, 1, 4, 4, 256),
+    FR_LB(bf16_t, 1024, 16, 1, 1, 4, 256)};
 
 #define FR_SPAN(a) {a, sizeof(a) / sizeof(a[0])}
 

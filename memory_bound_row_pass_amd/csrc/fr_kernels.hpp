@@ -49,15 +49,23 @@ typedef hipError_t (*LayerNormBwdLaunch)(const void* x, const void* dy, const vo
                                          const float* mean, const float* rstd, void* dx, float* ws,
                                          int grid, int64_t rows, int cols, hipStream_t s);
 
-constexpr int kBwdBlock = 1024;  // lanes per norm-backward workgroup
-constexpr int kBwdGrid = 256;    // most norm-backward workgroups (= partial rows)
+// Most workgroups (= partial rows in the workspace) of a norm backward launch.
+constexpr int kBwdGridMax = 512;
 
-// Workgroups (partial rows) of a norm backward launch whose row groups have
-// `threads` lanes each.
-inline int bwd_grid(int threads, int64_t rows) {
-  const int64_t rpb = kBwdBlock / threads;
-  const int64_t g = (rows + rpb - 1) / rpb;
-  return (int)(g < kBwdGrid ? g : kBwdGrid);
+// A compiled norm-backward shape: row groups of `threads` lanes, `rpb` row
+// groups per workgroup, at most `grid_max` workgroups (a fixed number, not
+// derived from the device, so the reduction order and the results do not
+// depend on it).
+template <typename F>
+struct BwdVariant {
+  int threads, nv, epv, rpb, grid_max;
+  F launch;
+};
+
+template <typename V>
+inline int bwd_grid(const V& v, int64_t rows) {
+  const int64_t g = (rows + v.rpb - 1) / v.rpb;
+  return (int)(g < v.grid_max ? g : v.grid_max);
 }
 
 typedef Variant<SoftmaxLaunch> SoftmaxVariant;
@@ -65,8 +73,8 @@ typedef Variant<LayerNormLaunch> LayerNormVariant;
 typedef Variant<RmsNormLaunch> RmsNormVariant;
 typedef Variant<XentLaunch> XentVariant;
 typedef Variant<SoftmaxBwdLaunch> SoftmaxBwdVariant;
-typedef Variant<RmsNormBwdLaunch> RmsNormBwdVariant;
-typedef Variant<LayerNormBwdLaunch> LayerNormBwdVariant;
+typedef BwdVariant<RmsNormBwdLaunch> RmsNormBwdVariant;
+typedef BwdVariant<LayerNormBwdLaunch> LayerNormBwdVariant;
 
 VariantSpan<SoftmaxVariant> softmax_variants(int in_bf16, int out_bf16);
 VariantSpan<LayerNormVariant> layernorm_variants(int bf16);

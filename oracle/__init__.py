@@ -42,6 +42,7 @@ def _load():
         "oracle_add_rmsnorm": ([P, P, P, I32, I64, I64, F, P, P, P], None),
         "oracle_softmax_xent": ([P, I32, P, I64, I64, P, P, P], None),
         "oracle_softmax_bwd": ([P, P, I32, I64, I64, P], None),
+        "oracle_softmax_xent_ex": ([P, I32, P, I64, I64, I32, I32, D, I32, D, P, P, P, P], None),
         "oracle_rmsnorm_bwd": ([P, P, P, P, I32, I64, I64, F, P, P], None),
         "oracle_layernorm_bwd": ([P, P, P, P, P, I32, I64, I64, P, P, P], None),
         "oracle_online_softmax_stats": ([P, I64, DP, DP], None),
@@ -149,6 +150,30 @@ def softmax_xent(logits, labels):
     _load().oracle_softmax_xent(_ptr(logits), _dtype_code(logits), _ptr(labels), R, C,
                                 _ptr(loss), _ptr(grad), _ptr(am))
     return loss, grad, am
+
+
+REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+
+
+def softmax_xent_ex(logits, labels, ignore_index=None, label_smoothing=0.0, reduction="none",
+                    grad_scale=1.0):
+    """Cross-entropy with options. Returns (loss[R], grad[R, C], argmax[R],
+    total) in float64 / int32; total is None for reduction "none".
+    ignore_index None: no row is ignored. label_smoothing and grad_scale are
+    used as given (pass fp32 values to match an fp32 caller)."""
+    logits = _c(logits)
+    labels = _c(labels, np.int32)
+    R, C = logits.shape
+    loss = np.empty(R, dtype=np.float64)
+    grad = np.empty((R, C), dtype=np.float64)
+    am = np.empty(R, dtype=np.int32)
+    tot = ctypes.c_double(np.nan)
+    red = REDUCTIONS[reduction]
+    _load().oracle_softmax_xent_ex(
+        _ptr(logits), _dtype_code(logits), _ptr(labels), R, C, int(ignore_index is not None),
+        int(ignore_index or 0), float(label_smoothing), red, float(grad_scale), _ptr(loss),
+        _ptr(grad), _ptr(am), ctypes.byref(tot))
+    return loss, grad, am, (tot.value if red else None)
 
 
 def softmax_bwd(p, dy):

@@ -176,6 +176,61 @@ void oracle_softmax_xent(const void* logits, int dtype, const int32_t* labels,
     }
 }
 
+/* Cross-entropy with the options of training code ("GPU Programming for
+ * Machine Learning", Module 3: cross-entropy loss; the variants of the
+ * cross-entropy row). Per row, straight from the definitions:
+ * lse = m + ln s; target q_j = (1 - eps) [j == label] + eps / C;
+ * loss_r = sum_j q_j (lse - x_j); p_j = exp(x_j - m) / s;
+ * grad_rj = g (p_j - q_j) with g = grad_scale (reduction none or sum) or
+ * grad_scale / n_valid (mean), n_valid = rows not ignored.
+ * Ignored rows (use_ignore and label == ignore_index): loss 0, grad 0.
+ * Other labels outside [0, C): loss NaN, grad_j = g (p_j - eps / C).
+ * total (sum / mean) = sum of loss_r in row order (/ n_valid). */
+void oracle_softmax_xent_ex(const void* logits, int dtype, const int32_t* labels, int64_t rows,
+                            int64_t cols, int use_ignore, int32_t ignore_index, double smoothing,
+                            int reduction, double grad_scale, double* loss, double* grad,
+                            int32_t* argmax, double* total) {
+    int64_t n_valid = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        if (!(use_ignore && labels[r] == ignore_index)) ++n_valid;
+    const double g = reduction == 2 ? grad_scale / (double)n_valid : grad_scale;
+    const double off = smoothing / (double)cols;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t b = r * cols;
+        double m = -INFINITY;
+        int64_t am = 0;
+        for (int64_t j = 0; j < cols; ++j) {
+            double v = load(logits, dtype, b + j);
+            if (v > m || j == 0) { m = v; am = j; }
+        }
+        if (argmax) argmax[r] = (int32_t)am;
+        const int32_t lab = labels[r];
+        if (use_ignore && lab == ignore_index) {
+            loss[r] = 0.0;
+            for (int64_t j = 0; j < cols; ++j) grad[b + j] = 0.0;
+            continue;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += exp(load(logits, dtype, b + j) - m);
+        const double lse = m + log(s);
+        const int valid = lab >= 0 && (int64_t)lab < cols;
+        double l = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            const double q = (valid && j == (int64_t)lab ? 1.0 - smoothing : 0.0) + off;
+            l += q * (lse - load(logits, dtype, b + j));
+            const double pj = exp(load(logits, dtype, b + j) - m) / s;
+            grad[b + j] = g * (pj - q);
+        }
+        loss[r] = valid ? l : NAN;
+    }
+    if (total && reduction != 0) {
+        double t = 0.0;
+        for (int64_t r = 0; r < rows; ++r) t += loss[r];
+        *total = reduction == 2 ? t / (double)n_valid : t;
+    }
+}
+
 /* ---------------------------------------------------------------- backward */
 /* The vector-Jacobian products of the row operations above (the backward
  * pipelines "NexusGrad" verifies against finite differences, Verified VJP

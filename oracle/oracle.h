@@ -69,6 +69,20 @@ void oracle_softmax_xent(const void* logits, int dtype, const int32_t* labels,
                          int64_t rows, int64_t cols,
                          double* loss, double* grad, int32_t* argmax);
 
+/* Cross-entropy with ignore_index, label smoothing, reduction and a gradient
+ * scale. target q_j = (1 - smoothing) [j == label] + smoothing / C;
+ * loss_r = sum_j q_j (lse - x_j), lse = m + ln s;
+ * grad_rj = g (p_j - q_j), g = grad_scale (reduction 0 none, 1 sum) or
+ * grad_scale / n_valid (2 mean), n_valid = rows not ignored.
+ * use_ignore: rows with label == ignore_index have loss 0 and grad 0.
+ * A label outside [0, cols) that is not ignored: loss NaN, grad = g (p - smoothing/C).
+ * total (reduction 1, 2; may be NULL): sum of loss_r in row order, / n_valid for mean.
+ * argmax may be NULL. */
+void oracle_softmax_xent_ex(const void* logits, int dtype, const int32_t* labels, int64_t rows,
+                            int64_t cols, int use_ignore, int32_t ignore_index, double smoothing,
+                            int reduction, double grad_scale, double* loss, double* grad,
+                            int32_t* argmax, double* total);
+
 /* ---- backward of the row operations (vector-Jacobian products) ---- */
 
 /* Softmax backward from the stored forward output p and the upstream

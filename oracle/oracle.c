@@ -185,7 +185,9 @@ void oracle_softmax_xent(const void* logits, int dtype, const int32_t* labels,
  * grad_scale / n_valid (mean), n_valid = rows not ignored.
  * Ignored rows (use_ignore and label == ignore_index): loss 0, grad 0.
  * Other labels outside [0, C): loss NaN, grad_j = g (p_j - eps / C).
- * total (sum / mean) = sum of loss_r in row order (/ n_valid). */
+ * total (sum / mean) = sum of loss_r in row order (/ n_valid).
+ * Terms of zero weight q_j are absent from the sum (a -inf logit, e.g. a
+ * masked class, would otherwise give 0 * inf). */
 void oracle_softmax_xent_ex(const void* logits, int dtype, const int32_t* labels, int64_t rows,
                             int64_t cols, int use_ignore, int32_t ignore_index, double smoothing,
                             int reduction, double grad_scale, double* loss, double* grad,
@@ -218,7 +220,7 @@ void oracle_softmax_xent_ex(const void* logits, int dtype, const int32_t* labels
         double l = 0.0;
         for (int64_t j = 0; j < cols; ++j) {
             const double q = (valid && j == (int64_t)lab ? 1.0 - smoothing : 0.0) + off;
-            l += q * (lse - load(logits, dtype, b + j));
+            if (q != 0.0) l += q * (lse - load(logits, dtype, b + j));  /* weight 0: no term */
             const double pj = exp(load(logits, dtype, b + j) - m) / s;
             grad[b + j] = g * (pj - q);
         }

@@ -107,3 +107,16 @@ def test_invalid_label_and_all_ignored():
     y = np.full(3, -100, np.int32)
     loss, g, _, tot = oracle.softmax_xent_ex(x, y, ignore_index=-100, reduction="mean")
     assert np.all(loss == 0) and np.all(g == 0) and np.isnan(tot)   # 0 / 0, as torch
+
+
+def test_masked_logits_zero_weight_terms():
+    # a -inf logit (masked class) has zero target weight without smoothing:
+    # the loss is the plain one and finite; with smoothing it is +inf
+    x = np.array([[1.0, -np.inf, 0.5, 2.0]])
+    y = np.array([0], np.int32)
+    l0, g0, _ = oracle.softmax_xent(x, y)
+    l, g, _, _ = oracle.softmax_xent_ex(x, y)
+    assert np.isfinite(l[0]) and l[0] == pytest.approx(l0[0], rel=1e-15)
+    assert np.array_equal(g, g0) and g[0, 1] == 0.0
+    l, _, _, _ = oracle.softmax_xent_ex(x, y, label_smoothing=0.1)
+    assert l[0] == np.inf

@@ -21,8 +21,10 @@ and the CPU oracle timed on the host cores as a baseline.
 
 The backward entry points are measured after the step, per call, at the
 forward workloads' shapes (softmax bf16 [16384, 4096], LayerNorm fp32
-[4096, 1024], residual-add + RMSNorm bf16 [8192, 8192]); they are reported
-under "backward" and are not part of `value`. Their per-row inputs from the
+[4096, 1024], residual-add + RMSNorm bf16 [8192, 8192]), and so are the
+cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
+logits, every 9th row ignored, label smoothing 0.1, mean reduction); they are
+reported under "backward" and "variants" and are not part of `value`. Their per-row inputs from the
 forward (p, mean, rstd) are produced by the forward kernels before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -71,6 +73,12 @@ def bwd_algo_bytes(name, R, C):
         return 3 * R * C * 4 + C * 4 + 2 * R * 4 + 2 * C * 4   # x, dy, dx; gamma; mean, rstd; dg, db
     if name == "add_rmsnorm_bwd_bf16":
         return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
+    if name in ("xent_ex_f32", "xent_ex_bf16"):
+        # logits of the rows not ignored (every 9th row is), grad of all rows;
+        # labels, loss; total
+        es = 4 if name == "xent_ex_f32" else 2
+        read_rows = R - len(range(0, R, 9))
+        return read_rows * C * es + R * C * es + 2 * R * 4 + 4
     raise KeyError(name)
 
 
@@ -106,6 +114,20 @@ class BwdWorkload:
             self.run = lambda: fr.fr_layernorm_bwd(self.x, self.dy, self.g, self.mean, self.rstd,
                                                    self.dx, self.dg, self.db, self.ws)
             self.op, self.code = fr.OP_LAYERNORM_BWD, fr.F32
+        elif name in ("xent_ex_f32", "xent_ex_bf16"):
+            # cross-entropy with options at the cross-entropy shape: every 9th
+            # row ignored, label smoothing 0.1, mean reduction
+            self.x, lab = d(w["logits"]), w["labels"].copy()
+            lab[::9] = -100
+            self.lab = d(lab)
+            self.loss = torch.empty(self.R, device=dev)
+            self.grad = torch.empty_like(self.x)
+            self.tot = torch.empty(1, device=dev)
+            self.run = lambda: fr.fr_softmax_xent_ex(self.x, self.lab, self.loss, self.grad, None,
+                                                     self.tot, ignore_index=-100,
+                                                     label_smoothing=0.1, reduction="mean")
+            self.op = fr.OP_XENT
+            self.code = fr.BF16 if name == "xent_ex_bf16" else fr.F32
         elif name == "add_rmsnorm_bwd_bf16":
             self.h, self.dy, self.dres = d(w["h"]), d(w["dy"]), d(w["dres"])
             self.wt = d(w["weight"])
@@ -342,20 +364,26 @@ def main():
     per = {w.name: launch_stats(w, us)
            for w, us in zip(wls, time_calls(torch, np, [w.run for w in wls], K))}
 
-    backward = {}
+    backward, variants = {}, {}
     if not args.no_backward:
         bws = []
         for n in ("softmax_bwd_bf16", "layernorm_bwd_f32", "add_rmsnorm_bwd_bf16"):
             t0 = time.perf_counter()
             bws.append(BwdWorkload(n, workloads.make(n), dev, torch, fr))
             log(f"generated {n} in {time.perf_counter() - t0:.1f} s")
+        nb = len(bws)
+        for n, dt in (("xent_ex_f32", "f32"), ("xent_ex_bf16", "bf16")):
+            bws.append(BwdWorkload(n, workloads.make("xent_f32", dtype=dt), dev, torch, fr))
+            log(f"generated {n}")
         for _ in range(max(3, args.warmup)):
             for b in bws:
                 b.run()
         torch.cuda.synchronize()
-        backward = {b.name: launch_stats(b, us)
-                    for b, us in zip(bws, time_calls(torch, np, [b.run for b in bws], K))}
-        log("backward calls timed")
+        timed = {b.name: launch_stats(b, us)
+                 for b, us in zip(bws, time_calls(torch, np, [b.run for b in bws], K))}
+        backward = {b.name: timed[b.name] for b in bws[:nb]}
+        variants = {b.name: timed[b.name] for b in bws[nb:]}
+        log("backward and variant calls timed")
 
     ceiling = copy_ceiling(torch, fr, dev)
     log(f"copy ceiling {ceiling:.0f} GB/s")
@@ -390,6 +418,7 @@ def main():
         },
         "per_workload": per,
         "backward": backward,
+        "variants": variants,
         "roofline": {
             "bound": "hbm",
             "kernel": f"xent_kernel<float,{dom['variant']['threads']},{dom['variant']['vecs']},"

@@ -148,6 +148,43 @@ FR_API fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* la
                                     int64_t rows, int64_t cols, fr_dtype_t dtype,
                                     void* stream);
 
+/* ---- cross-entropy variants ---- */
+
+typedef enum { FR_REDUCE_NONE = 0, FR_REDUCE_SUM = 1, FR_REDUCE_MEAN = 2 } fr_reduction_t;
+
+/* Options of fr_softmax_xent_ex (NULL: all defaults, in brackets). */
+typedef struct {
+  int32_t use_ignore_index; /* nonzero: rows whose label == ignore_index are ignored [0] */
+  int32_t ignore_index;     /* e.g. -100 [0] */
+  float label_smoothing;    /* eps in [0, 1] [0] */
+  float grad_scale;         /* finite; multiplies the gradient [1] */
+  int32_t reduction;        /* fr_reduction_t [FR_REDUCE_NONE] */
+} fr_xent_options_t;
+
+/* Softmax cross-entropy forward + backward with the options of training code.
+ *   target q_j = (1 - eps) [j == label] + eps / C,
+ *   loss_r = sum_j q_j (lse - x_j) = lse - (1 - eps) x[label] - eps mean_j x_j,
+ *   grad_rj = g (p_j - q_j),  g = grad_scale, or grad_scale / n_valid for
+ *   FR_REDUCE_MEAN (n_valid = rows not ignored),
+ *   loss_total = sum_r loss_r (SUM) or that sum / n_valid (MEAN; NaN when
+ *   every row is ignored), accumulated in double in a fixed order.
+ * Ignored rows: loss 0 and a zero gradient row. A label outside [0, cols)
+ * that is not ignored: loss NaN, grad_j = g (p_j - eps / C).
+ *   ("GPU Programming for Machine Learning", Module 3: cross-entropy loss;
+ *    "Engineering a CUDA Machine Learning Framework from Scratch", §2.1.)
+ * logits, grad [rows, cols] in `dtype` (FR_F32 or FR_BF16, grad in the
+ * logits' dtype; grad may equal logits); labels [rows] int32; loss [rows]
+ * fp32 (always written: the per-row losses the total is summed from); argmax
+ * [rows] int32 or NULL; loss_total [1] fp32, required for SUM and MEAN (NULL
+ * allowed for NONE); during a MEAN call it first holds the row count. One
+ * to three kernels on `stream` (count, row pass, total). rows == 0: SUM
+ * writes 0, MEAN writes NaN, NONE does nothing. Options out of range
+ * (eps outside [0, 1], scale not finite, unknown reduction) give FR_E_VALUE. */
+FR_API fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels, float* loss,
+                               void* grad, int32_t* argmax, float* loss_total,
+                               int64_t rows, int64_t cols, fr_dtype_t dtype,
+                               const fr_xent_options_t* options, void* stream);
+
 /* ---- backward of the row operations ---- */
 
 /* Widest row of the backward entry points (their working set per element is

@@ -20,6 +20,7 @@ __all__ = [
     "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
     "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
+    "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
     "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
@@ -32,6 +33,15 @@ OP_SOFTMAX_BWD, OP_RMSNORM_BWD, OP_LAYERNORM_BWD = 4, 5, 6
 FR_MAX_COLS = 65536
 FR_BWD_MAX_COLS = 16384
 FR_BWD_PARTIALS = 512
+REDUCE_NONE, REDUCE_SUM, REDUCE_MEAN = 0, 1, 2
+_REDUCTIONS = {"none": REDUCE_NONE, "sum": REDUCE_SUM, "mean": REDUCE_MEAN}
+
+
+class XentOptions(ctypes.Structure):
+    """fr_xent_options_t."""
+    _fields_ = [("use_ignore_index", ctypes.c_int32), ("ignore_index", ctypes.c_int32),
+                ("label_smoothing", ctypes.c_float), ("grad_scale", ctypes.c_float),
+                ("reduction", ctypes.c_int32)]
 # FUSEDROW_LIB may name an alternative build of the same library (A/B runs).
 LIB_PATH = os.environ.get("FUSEDROW_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libfusedrow.so")
@@ -69,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "fr_softmax_xent_fwd_bwd": [P, P, P, P, P, I64, I64, I32, P],
         "fr_stream_copy": [P, P, I64, P],
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
+        "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
         "fr_add_rmsnorm_bwd": [P, P, P, P, P, P, P, I64, I64, I64, F, I32, P],
         "fr_layernorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, P],
         "fr_debug_force_variant": [I32, I32, I32],
@@ -222,6 +233,30 @@ def fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, argmax=None, stream=None
            "fr_softmax_xent_fwd_bwd")
 
 
+def fr_softmax_xent_ex(logits, labels, loss, grad, argmax=None, loss_total=None,
+                       ignore_index=None, label_smoothing: float = 0.0, grad_scale: float = 1.0,
+                       reduction: str = "none", stream=None) -> None:
+    """Cross-entropy with ignore_index / label smoothing / reduction / gradient
+    scale (C: fr_softmax_xent_ex); fp32 or bf16 logits, grad in their dtype."""
+    torch = _torch()
+    _need_cuda(logits, labels, loss, grad, argmax, loss_total)
+    R, C = _rows_cols(logits)
+    _check_rows(labels, R, "labels", torch.int32)
+    _check_rows(loss, R, "loss", torch.float32)
+    if argmax is not None:
+        _check_rows(argmax, R, "argmax", torch.int32)
+    if loss_total is not None and (loss_total.numel() < 1 or loss_total.dtype != torch.float32):
+        raise ValueError("loss_total must be a float32 tensor of at least one element")
+    if tuple(grad.shape) != (R, C) or not grad.is_contiguous() or grad.dtype != logits.dtype:
+        raise ValueError("grad must be a contiguous tensor of logits' shape and dtype")
+    opts = XentOptions(int(ignore_index is not None), int(ignore_index or 0), float(label_smoothing),
+                       float(grad_scale), _REDUCTIONS[reduction])
+    _check(lib.fr_softmax_xent_ex(_ptr(logits), _ptr(labels), _ptr(loss), _ptr(grad), _ptr(argmax),
+                                  _ptr(loss_total), R, C, _dtype_code(logits), ctypes.byref(opts),
+                                  _stream(stream, logits)),
+           "fr_softmax_xent_ex")
+
+
 def _check_like(t, ref, name):
     if t is not None and (tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous()
                           or t.dtype != ref.dtype):
@@ -368,14 +403,26 @@ def add_rmsnorm(x, residual, weight, eps: float = 1e-6, inplace: bool = False):
     return y, res_out
 
 
-def softmax_xent(logits, labels, return_argmax: bool = False):
+def softmax_xent(logits, labels, return_argmax: bool = False, ignore_index=None,
+                 label_smoothing: float = 0.0, reduction: str = "none", grad_scale: float = 1.0):
+    """Returns (loss, grad[, argmax]); loss is the per-row loss [rows] for
+    reduction "none", else the scalar total (a 1-element tensor)."""
     torch = _torch()
     R = logits.shape[0]
     loss = torch.empty(R, dtype=torch.float32, device=logits.device)
     grad = torch.empty_like(logits)
     am = torch.empty(R, dtype=torch.int32, device=logits.device) if return_argmax else None
-    fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, am)
-    return (loss, grad, am) if return_argmax else (loss, grad)
+    plain = (logits.dtype == torch.float32 and ignore_index is None and label_smoothing == 0.0
+             and reduction == "none" and grad_scale == 1.0)
+    if plain:
+        fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, am)
+        out = loss
+    else:
+        total = torch.empty(1, dtype=torch.float32, device=logits.device)
+        fr_softmax_xent_ex(logits, labels, loss, grad, am, total, ignore_index, label_smoothing,
+                           grad_scale, reduction)
+        out = loss if reduction == "none" else total
+    return (out, grad, am) if return_argmax else (out, grad)
 
 
 def _workspace(op, rows, cols, device):

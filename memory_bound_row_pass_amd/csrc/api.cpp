@@ -159,7 +159,10 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
       break;
     }
     case FR_OP_XENT: {
-      auto v = select_variant(fr::xent_variants(in_dtype == FR_BF16, 0), op, cols, epv);
+      // fp32: the plain table (the options table has the same shapes); bf16
+      // logits exist only with options
+      auto v = select_variant(in_dtype == FR_BF16 ? fr::xent_ex_variants(1, 0) : fr::xent_variants(0, 0),
+                              op, cols, epv);
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -290,8 +293,62 @@ fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* labels, f
   const fr::XentVariant* v = select_variant(fr::xent_variants(0, argmax != nullptr), FR_OP_XENT, cols,
                                             vec ? vec_epv(es) : 1);
   if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
-  return launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols,
+  return launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols, nullptr,
                                  static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels, float* loss, void* grad,
+                               int32_t* argmax, float* loss_total, int64_t rows, int64_t cols,
+                               fr_dtype_t dtype, const fr_xent_options_t* options, void* stream) {
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  fr_xent_options_t o = {0, 0, 0.f, 1.f, FR_REDUCE_NONE};
+  if (options) o = *options;
+  if (!std::isfinite(o.label_smoothing) || o.label_smoothing < 0.f || o.label_smoothing > 1.f ||
+      !std::isfinite(o.grad_scale) ||
+      (o.reduction != FR_REDUCE_NONE && o.reduction != FR_REDUCE_SUM &&
+       o.reduction != FR_REDUCE_MEAN))
+    return FR_E_VALUE;
+  if (o.reduction == FR_REDUCE_MEAN && rows > (int64_t)UINT32_MAX) return FR_E_SHAPE;
+  const bool reduce = o.reduction != FR_REDUCE_NONE;
+  if (reduce && !loss_total) return FR_E_NULL;
+  if (loss_total && !aligned(loss_total, 4)) return FR_E_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* count = o.reduction == FR_REDUCE_MEAN ? reinterpret_cast<uint32_t*>(loss_total) : nullptr;
+  if (rows == 0) {
+    if (!reduce) return FR_OK;
+    if (count)
+      if (fr_status_t s = launch_status(fr::launch_xent_count(labels, 0, 0, 0, count, st))) return s;
+    return launch_status(fr::launch_xent_total(loss, 0, count, loss_total, st));
+  }
+  if (!logits || !labels || !loss || !grad) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(logits, es) || !aligned(grad, es) || !aligned(labels, 4) || !aligned(loss, 4) ||
+      (argmax && !aligned(argmax, 4)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(logits, rows * cols * es, true, es, false),
+                      make_buf(labels, rows * 4, false, 4, false),
+                      make_buf(loss, rows * 4, false, 4, true),
+                      make_buf(grad, rows * cols * es, true, es, true),
+                      make_buf(argmax, rows * 4, false, 4, true),
+                      make_buf(reduce ? loss_total : nullptr, 4, false, 4, true)};
+  if (fr_status_t s = check_alias(bufs, 6)) return s;
+  const bool vec =
+      (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
+  const fr::XentVariant* v = select_variant(fr::xent_ex_variants(dtype == FR_BF16, argmax != nullptr),
+                                            FR_OP_XENT, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  if (count)
+    if (fr_status_t s = launch_status(
+            fr::launch_xent_count(labels, rows, o.use_ignore_index != 0, o.ignore_index, count, st)))
+      return s;
+  const fr::XentOptions ko = {o.use_ignore_index != 0, o.ignore_index, o.label_smoothing,
+                              o.grad_scale, count};
+  if (fr_status_t s = launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols,
+                                              &ko, st)))
+    return s;
+  if (!reduce) return FR_OK;
+  return launch_status(fr::launch_xent_total(loss, rows, count, loss_total, st));
 }
 
 fr_status_t fr_softmax_bwd(const void* p, const void* dy, void* dx, int64_t rows, int64_t cols,

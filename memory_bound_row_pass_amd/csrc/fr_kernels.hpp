@@ -34,8 +34,18 @@ typedef hipError_t (*LayerNormLaunch)(const void* x, const void* gamma, const vo
                                       hipStream_t s);
 typedef hipError_t (*RmsNormLaunch)(const void* x, const void* res, const void* w, void* y,
                                     void* res_out, int64_t rows, int cols, float eps, hipStream_t s);
+// Cross-entropy options (kernel argument, by value). count: device pointer
+// to the number of rows not ignored (mean reduction), or NULL.
+struct XentOptions {
+  int use_ignore;
+  int ignore_index;
+  float smoothing;
+  float grad_scale;
+  const uint32_t* count;
+};
 typedef hipError_t (*XentLaunch)(const void* logits, const int32_t* labels, float* loss, void* grad,
-                                 int32_t* argmax, int64_t rows, int cols, hipStream_t s);
+                                 int32_t* argmax, int64_t rows, int cols, const XentOptions* opt,
+                                 hipStream_t s);
 
 // Backward launchers. The norm backward kernels run `grid` workgroups of
 // kBwdBlock lanes and leave one fp32 partial row per workgroup and parameter
@@ -80,6 +90,11 @@ VariantSpan<SoftmaxVariant> softmax_variants(int in_bf16, int out_bf16);
 VariantSpan<LayerNormVariant> layernorm_variants(int bf16);
 VariantSpan<RmsNormVariant> rmsnorm_variants(int bf16);
 VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
+VariantSpan<XentVariant> xent_ex_variants(int bf16, int with_argmax);
+hipError_t launch_xent_count(const int32_t* labels, int64_t rows, int use_ignore, int ignore_index,
+                             uint32_t* out, hipStream_t s);
+hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* count, float* total,
+                             hipStream_t s);
 VariantSpan<SoftmaxBwdVariant> softmax_bwd_variants(int bf16);
 VariantSpan<RmsNormBwdVariant> rmsnorm_bwd_variants(int bf16);
 VariantSpan<LayerNormBwdVariant> layernorm_bwd_variants(int bf16);

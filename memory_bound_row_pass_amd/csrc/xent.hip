@@ -11,10 +11,39 @@
 // The lane that owns the label column reads the label logit, writes the
 // loss, and overwrites its stored p with p - 1. A label outside [0, cols)
 // gives a NaN loss and an unmodified softmax row.
+//
+// With options (OPT, the cross-entropy variants of training code): rows whose
+// label is the ignore index get loss 0 and a zero gradient; label smoothing
+// eps targets q_j = (1 - eps) [j == label] + eps / C, which needs the row sum
+// of the logits t = sum_j x_j carried in the row state:
+//   loss   = lse - (1 - eps) x[label] - eps t / C,   lse = M + ln S
+//   grad_j = g (p_j - q_j),  g = grad_scale, or grad_scale / n_valid for a
+//            mean over the rows that are not ignored (n_valid counted by
+//            xent_count_kernel before the row pass).
+// Each lane stores g p_j - g eps / C with one fma; the label lane then
+// overwrites its element with g (p_label - (1 - eps) - eps / C).
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
 namespace fr {
+
+// A row state with the sum of the raw logits added (label smoothing).
+template <typename S>
+struct PlusSum {
+  S st;
+  float t;
+  template <int C, int M>
+  static __device__ __forceinline__ PlusSum move(const PlusSum& a) {
+    return {S::template move<C, M>(a.st), dpp_move<C, M>(a.t, 0.f)};
+  }
+  __device__ __forceinline__ PlusSum lane63() const { return {st.lane63(), read_lane63(t)}; }
+};
+template <typename S, typename M>
+struct PlusSumMerge {
+  __device__ __forceinline__ PlusSum<S> operator()(const PlusSum<S>& a, const PlusSum<S>& b) const {
+    return {M{}(a.st, b.st), a.t + b.t};
+  }
+};
 
 // Lane of the row owner that holds column `c` (0 <= c < cols): a head or
 // tail column sits in the extra slot of lane c or head + (c - body_end); a
@@ -27,15 +56,17 @@ __device__ __forceinline__ int owner_lane(int c, const RowGeom<EPV>& g) {
   return ((c - g.head) / EPV) % T;
 }
 
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX>
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT>
 __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
 void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, int32_t* argmax,
-                 int64_t rows, int cols) {
+                 int64_t rows, int cols, XentOptions opt) {
   constexpr int BLOCK = T == 64 ? 256 : T;
   constexpr int RPB = BLOCK / T;
   constexpr int NW = T / 64;
-  using State = typename std::conditional<ARGMAX, MaxSumIdxState, MaxSumState>::type;
-  using Merge = typename std::conditional<ARGMAX, MaxSumIdxMerge, MaxSumMerge<false>>::type;
+  using Base = typename std::conditional<ARGMAX, MaxSumIdxState, MaxSumState>::type;
+  using BaseMerge = typename std::conditional<ARGMAX, MaxSumIdxMerge, MaxSumMerge<false>>::type;
+  using State = typename std::conditional<OPT, PlusSum<Base>, Base>::type;
+  using Merge = typename std::conditional<OPT, PlusSumMerge<Base, BaseMerge>, BaseMerge>::type;
   constexpr int NF = sizeof(State) / sizeof(float);
   __shared__ float xw[2][NW][NF];
 
@@ -44,30 +75,70 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
   const int tid = T == 64 ? lane : (int)threadIdx.x;
   const int sub = T == 64 ? wib : 0;
   const int wave = T == 64 ? 0 : wib;
+
+  // gradient scale g and the smoothing offset g * eps / C (OPT only)
+  float gsc = 1.f, goff = 0.f;
+  if constexpr (OPT) {
+    gsc = opt.grad_scale;
+    if (opt.count) gsc = gsc / (float)(*opt.count);
+    goff = gsc * (opt.smoothing / (float)cols);
+  }
+
   int it = 0;
   for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
        row += (int64_t)gridDim.x * RPB, ++it) {
     const Tin* xr = x + row * cols;
     Tin* gr = grad + row * cols;
     const RowGeom<EPV> g(xr, cols);
+    const int ec = g.extra_col(tid);
+
+    const int label = __builtin_amdgcn_readfirstlane(labels[row]);
+    const bool ignored = OPT && opt.use_ignore && label == opt.ignore_index;
+    if constexpr (OPT && !ARGMAX) {
+      if (ignored) {  // uniform in the row owner: no loads, a zero row
+        float z[NV][EPV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) z[i][k] = 0.f;
+        store_chunks<Tin, T, NV, EPV>(gr, g, tid, z);
+        if (ec >= 0) store1(gr + ec, 0.f);
+        if (tid == 0) loss[row] = 0.f;
+        continue;
+      }
+    }
 
     float v[NV][EPV];
     load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
-    const int ec = g.extra_col(tid);
     float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
 
     // The label column is handled by the one lane that owns it (the lane of
     // the row owner that loads that column). It reads the label logit with
     // its own load, before any of its stores: in-place calls (grad == logits)
     // stay correct because a lane's accesses to one address keep their order.
-    const int label = __builtin_amdgcn_readfirstlane(labels[row]);
     const bool valid = label >= 0 && label < cols;
-    const bool label_lane = valid && owner_lane<T, EPV>(label, g) == tid;
+    const bool label_lane = valid && !ignored && owner_lane<T, EPV>(label, g) == tid;
     float x_label = 0.f;
     if (label_lane) x_label = load1(xr + label);
 
     const float m = lane_max<NV, EPV>(v, xe);
-    State st;
+    Base bs;
+    float tsum = 0.f;
+    if constexpr (OPT) {
+      // sum of this lane's logits (masked slots hold -inf and are skipped)
+      const bool full = g.nvec == T * NV;
+      float t0 = ec >= 0 ? xe : 0.f, t1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const bool ok = full || i * T + tid < g.nvec;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float a = ok ? v[i][k] : 0.f;
+          if (k & 1) t1 += a; else t0 += a;
+        }
+      }
+      tsum = t0 + t1;
+    }
     if constexpr (ARGMAX) {
       // smallest column of this lane holding its maximum
       float best = 3.0e38f;
@@ -79,68 +150,186 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
           best = (v[i][k] == m && col < best) ? col : best;
         }
       if (ec >= 0 && xe == m && (float)ec < best) best = (float)ec;
-      st.idx = best;
+      bs.idx = best;
     }
     {
       const MaxSumState ms = lane_exp_nat<NV, EPV>(v, xe, m);  // e_j replaces x_j
-      st.m = ms.m;
-      st.s = ms.s;
+      bs.m = ms.m;
+      bs.s = ms.s;
     }
+    State st;
+    if constexpr (OPT) st = State{bs, tsum};
+    else st = bs;
     st = wave_reduce(st, Merge{});
     if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
+    Base rs;
+    if constexpr (OPT) {
+      rs = st.st;
+      tsum = st.t;
+    } else {
+      rs = st;
+    }
 
-    const float f = nat_scale(m, st.m, st.s);
+    if constexpr (OPT) {
+      if (ignored) {  // (argmax wanted) zero row, loss 0
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] *= f;
-    xe *= f;
+          for (int k = 0; k < EPV; ++k) v[i][k] = 0.f;
+        xe = 0.f;
+      } else {
+        const float f = nat_scale(m, rs.m, rs.s) * gsc;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf(v[i][k], f, -goff);
+        xe = __builtin_fmaf(xe, f, -goff);
+      }
+    } else {
+      const float f = nat_scale(m, rs.m, rs.s);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) v[i][k] *= f;
+      xe *= f;
+    }
     store_chunks<Tin, T, NV, EPV>(gr, g, tid, v);
     if (ec >= 0) store1(gr + ec, xe);
 
     if (label_lane) {
-      // overwrite the label element with p - 1 (after this lane's own store
-      // of p to the same address), and write the loss
-      const float p = exp_acc(x_label - st.m) / st.s;
-      store1(gr + label, p - 1.f);
-      loss[row] = st.m + logf(st.s) - x_label;
-    } else if (!valid && tid == 0) {
-      loss[row] = __builtin_nanf("");
+      // overwrite the label element (after this lane's own store of it to
+      // the same address), and write the loss
+      const float p = exp_acc(x_label - rs.m) / rs.s;
+      const float lse = rs.m + logf(rs.s);
+      if constexpr (OPT) {
+        // terms with a zero weight are left out (a -inf logit would make
+        // them 0 * inf); the same reading as the definition's weighted sum
+        const float eps = opt.smoothing;
+        store1(gr + label, gsc * ((p - (1.f - eps)) - eps / (float)cols));
+        float l = lse;
+        if (eps != 1.f) l -= (1.f - eps) * x_label;
+        if (eps != 0.f) l -= eps * (tsum / (float)cols);
+        loss[row] = l;
+      } else {
+        store1(gr + label, p - 1.f);
+        loss[row] = lse - x_label;
+      }
+    } else if (tid == 0 && (ignored || !valid)) {
+      loss[row] = ignored ? 0.f : __builtin_nanf("");
     }
     if constexpr (ARGMAX) {
-      if (tid == 0) argmax[row] = (int32_t)st.idx;
+      if (tid == 0) argmax[row] = (int32_t)rs.idx;
     }
   }
 }
 
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX>
+// ------------------------------------------------- reductions over rows
+// Single-workgroup kernels (1024 lanes) for the row-count and the loss total:
+// each lane takes rows lane, lane + 1024, ... in order, then a fixed LDS tree.
+
+// n_valid = number of rows whose label is not the ignore index.
+__global__ __launch_bounds__(1024) void xent_count_kernel(const int32_t* labels, int64_t rows,
+                                                          int use_ignore, int ignore_index,
+                                                          uint32_t* out) {
+  __shared__ uint32_t red[1024];
+  uint32_t c = 0;
+  for (int64_t r = threadIdx.x; r < rows; r += 1024)
+    c += (use_ignore && labels[r] == ignore_index) ? 0u : 1u;
+  red[threadIdx.x] = c;
+  __syncthreads();
+#pragma unroll
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+// total = sum of loss[r] (double accumulation), divided by *count for a mean.
+// `total` may be the same 4 bytes as `count` (the count is read first).
+__global__ __launch_bounds__(1024) void xent_total_kernel(const float* loss, int64_t rows,
+                                                          const uint32_t* count, float* total) {
+  __shared__ double red[1024];
+  double sacc = 0.0;
+  for (int64_t r = threadIdx.x; r < rows; r += 1024) sacc += (double)loss[r];
+  red[threadIdx.x] = sacc;
+  __syncthreads();
+#pragma unroll
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double t = red[0];
+    *total = count ? (float)(t / (double)*count) : (float)t;
+  }
+}
+
+hipError_t launch_xent_count(const int32_t* labels, int64_t rows, int use_ignore, int ignore_index,
+                             uint32_t* out, hipStream_t s) {
+  return launch_kernel(&xent_count_kernel, dim3(1), dim3(1024), s, labels, rows, use_ignore,
+                       ignore_index, out);
+}
+
+hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* count, float* total,
+                             hipStream_t s) {
+  return launch_kernel(&xent_total_kernel, dim3(1), dim3(1024), s, loss, rows, count, total);
+}
+
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT>
 static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss, void* grad,
-                              int32_t* argmax, int64_t rows, int cols, hipStream_t s) {
+                              int32_t* argmax, int64_t rows, int cols, const XentOptions* opt,
+                              hipStream_t s) {
   constexpr int BLOCK = T == 64 ? 256 : T;
   constexpr int RPB = BLOCK / T;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX>, dim3(grid), dim3(BLOCK), s,
-                     static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax, rows,
-                     cols);
+  const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
+  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT>, dim3(grid), dim3(BLOCK), s,
+                       static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax,
+                       rows, cols, o);
 }
 
-#define FR_XE(T, NV, EPV, OCC, AM) {T, NV, EPV, &launch_xent<float, T, NV, EPV, OCC, AM>}
-#define FR_XE_TABLE(AM)                                                                   \
-  {FR_XE(64, 1, 4, 8, AM),     FR_XE(64, 2, 4, 8, AM),     FR_XE(64, 4, 4, 8, AM),        \
-   FR_XE(64, 8, 4, 6, AM),     FR_XE(64, 16, 4, 4, AM),    FR_XE(256, 8, 4, 6, AM),       \
-   FR_XE(512, 8, 4, 6, AM),    FR_XE(1024, 8, 4, 4, AM),   FR_XE(1024, 13, 4, 4, AM),     \
-   FR_XE(512, 25, 4, 4, AM),   FR_XE(256, 50, 4, 2, AM),   FR_XE(1024, 16, 4, 4, AM),     \
-   FR_XE(64, 16, 1, 4, AM),    FR_XE(256, 16, 1, 4, AM),   FR_XE(1024, 16, 1, 4, AM),     \
-   FR_XE(1024, 64, 1, 4, AM)}
+#define FR_XE(TS, T, NV, EPV, OCC, AM, OPT) {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT>}
+#define FR_XE_F32(AM, OPT)                                                                       \
+  {FR_XE(float, 64, 1, 4, 8, AM, OPT),    FR_XE(float, 64, 2, 4, 8, AM, OPT),                    \
+   FR_XE(float, 64, 4, 4, 8, AM, OPT),    FR_XE(float, 64, 8, 4, 6, AM, OPT),                    \
+   FR_XE(float, 64, 16, 4, 4, AM, OPT),   FR_XE(float, 256, 8, 4, 6, AM, OPT),                   \
+   FR_XE(float, 512, 8, 4, 6, AM, OPT),   FR_XE(float, 1024, 8, 4, 4, AM, OPT),                  \
+   FR_XE(float, 1024, 13, 4, 4, AM, OPT), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
+   FR_XE(float, 256, 50, 4, 2, AM, OPT),  FR_XE(float, 1024, 16, 4, 4, AM, OPT),                 \
+   FR_XE(float, 64, 16, 1, 4, AM, OPT),   FR_XE(float, 256, 16, 1, 4, AM, OPT),                  \
+   FR_XE(float, 1024, 16, 1, 4, AM, OPT), FR_XE(float, 1024, 64, 1, 4, AM, OPT)}
+#define FR_XE_BF16(AM)                                                                           \
+  {FR_XE(bf16_t, 64, 1, 8, 8, AM, true),    FR_XE(bf16_t, 64, 2, 8, 8, AM, true),                \
+   FR_XE(bf16_t, 64, 4, 8, 6, AM, true),    FR_XE(bf16_t, 64, 8, 8, 4, AM, true),                \
+   FR_XE(bf16_t, 256, 4, 8, 6, AM, true),   FR_XE(bf16_t, 512, 4, 8, 6, AM, true),               \
+   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XE(bf16_t, 1024, 7, 8, 4, AM, true),              \
+   FR_XE(bf16_t, 1024, 8, 8, 4, AM, true),  FR_XE(bf16_t, 64, 16, 1, 4, AM, true),               \
+   FR_XE(bf16_t, 256, 16, 1, 4, AM, true),  FR_XE(bf16_t, 1024, 16, 1, 4, AM, true),             \
+   FR_XE(bf16_t, 1024, 64, 1, 4, AM, true)}
 
-static const XentVariant kXe[] = FR_XE_TABLE(false);
-static const XentVariant kXeArgmax[] = FR_XE_TABLE(true);
+// plain (fr_softmax_xent_fwd_bwd, fp32) and with options (fr_softmax_xent_ex)
+static const XentVariant kXe[] = FR_XE_F32(false, false);
+static const XentVariant kXeArgmax[] = FR_XE_F32(true, false);
+static const XentVariant kXeOpt[] = FR_XE_F32(false, true);
+static const XentVariant kXeOptArgmax[] = FR_XE_F32(true, true);
+static const XentVariant kXeBf16[] = FR_XE_BF16(false);
+static const XentVariant kXeBf16Argmax[] = FR_XE_BF16(true);
+
+#define FR_SPAN(a) {a, sizeof(a) / sizeof(a[0])}
 
 VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax) {
   if (bf16) return {nullptr, 0};
-  if (with_argmax) return {kXeArgmax, sizeof(kXeArgmax) / sizeof(kXeArgmax[0])};
-  return {kXe, sizeof(kXe) / sizeof(kXe[0])};
+  if (with_argmax) return FR_SPAN(kXeArgmax);
+  return FR_SPAN(kXe);
+}
+
+VariantSpan<XentVariant> xent_ex_variants(int bf16, int with_argmax) {
+  if (bf16) return with_argmax ? VariantSpan<XentVariant>FR_SPAN(kXeBf16Argmax)
+                               : VariantSpan<XentVariant>FR_SPAN(kXeBf16);
+  return with_argmax ? VariantSpan<XentVariant>FR_SPAN(kXeOptArgmax)
+                     : VariantSpan<XentVariant>FR_SPAN(kXeOpt);
 }
 
 }  // namespace fr

@@ -168,6 +168,31 @@ def test_layernorm_bwd_validation():
     assert call(dx=DY + 2) == E_ALIAS
 
 
+def test_xent_ex_validation():
+    f = fr.lib.fr_softmax_xent_ex
+    L, LS, G, AM, T = (A + k * 0x100000 for k in range(1, 6))
+
+    def call(lg=A, lab=L, ls=LS, g=G, am=AM, tot=T, rows=4, cols=8, dt=1, **o):
+        opts = fr.XentOptions(o.get("use", 1), o.get("ign", -100), o.get("eps", 0.1),
+                              o.get("scale", 1.0), o.get("red", fr.REDUCE_MEAN))
+        return f(P(lg), P(lab), P(ls), P(g), P(am), P(tot), rows, cols, dt, ctypes.byref(opts), None)
+
+    assert call(rows=0, red=fr.REDUCE_NONE) == OK          # nothing to do, nothing launched
+    assert call(rows=0, tot=0) == E_NULL                    # a total needs somewhere to go
+    assert call(eps=-0.1) == E_VALUE
+    assert call(eps=1.5) == E_VALUE
+    assert call(eps=float("nan")) == E_VALUE
+    assert call(scale=float("inf")) == E_VALUE
+    assert call(red=7) == E_VALUE
+    assert call(dt=4) == E_DTYPE
+    assert call(tot=0) == E_NULL
+    assert call(tot=T + 2) == E_ALIGN
+    assert call(lg=A + 1) == E_ALIGN                        # bf16 needs 2-byte alignment
+    assert call(tot=LS + 4) == E_ALIAS                      # total inside the per-row losses
+    assert call(tot=L) == E_ALIAS                           # total over the labels
+    assert call(g=A + 2) == E_ALIAS
+
+
 def test_stream_copy_validation():
     f = fr.lib.fr_stream_copy
     assert f(P(A), P(B), 0, None) == OK

@@ -23,7 +23,9 @@ The backward entry points are measured after the step, per call, at the
 forward workloads' shapes (softmax bf16 [16384, 4096], LayerNorm fp32
 [4096, 1024], residual-add + RMSNorm bf16 [8192, 8192]), and so are the
 cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
-logits, every 9th row ignored, label smoothing 0.1, mean reduction); they are
+logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
+split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
+[2048, 131072], bf16 [1024, 262144]); they are
 reported under "backward" and "variants" and are not part of `value`. Their per-row inputs from the
 forward (p, mean, rstd) are produced by the forward kernels before timing.
 
@@ -73,6 +75,11 @@ def bwd_algo_bytes(name, R, C):
         return 3 * R * C * 4 + C * 4 + 2 * R * 4 + 2 * C * 4   # x, dy, dx; gamma; mean, rstd; dg, db
     if name == "add_rmsnorm_bwd_bf16":
         return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
+    if name in ("xent_split_f32", "xent_split_bf16"):
+        # one read of the logits and one write of the gradient (the split path
+        # reads the logits twice: 1.5x these bytes move); labels, loss
+        es = 4 if name == "xent_split_f32" else 2
+        return 2 * R * C * es + 2 * R * 4
     if name in ("xent_ex_f32", "xent_ex_bf16"):
         # logits of the rows not ignored (every 9th row is), grad of all rows;
         # labels, loss; total
@@ -128,6 +135,17 @@ class BwdWorkload:
                                                      label_smoothing=0.1, reduction="mean")
             self.op = fr.OP_XENT
             self.code = fr.BF16 if name == "xent_ex_bf16" else fr.F32
+        elif name in ("xent_split_f32", "xent_split_bf16"):
+            # wide vocabularies through the split-row path, no options
+            self.x, self.lab = d(w["logits"]), d(w["labels"])
+            self.loss = torch.empty(self.R, device=dev)
+            self.grad = torch.empty_like(self.x)
+            self.ws = torch.empty(fr.fr_split_workspace_bytes(self.R, self.C), dtype=torch.uint8,
+                                  device=dev)
+            self.run = lambda: fr.fr_softmax_xent_split(self.x, self.lab, self.loss, self.grad,
+                                                        self.ws)
+            self.op = fr.OP_XENT_SPLIT
+            self.code = fr.BF16 if name == "xent_split_bf16" else fr.F32
         elif name == "add_rmsnorm_bwd_bf16":
             self.h, self.dy, self.dres = d(w["h"]), d(w["dy"]), d(w["dres"])
             self.wt = d(w["weight"])
@@ -374,6 +392,11 @@ def main():
         nb = len(bws)
         for n, dt in (("xent_ex_f32", "f32"), ("xent_ex_bf16", "bf16")):
             bws.append(BwdWorkload(n, workloads.make("xent_f32", dtype=dt), dev, torch, fr))
+            log(f"generated {n}")
+        for n, dt, R, C in (("xent_split_f32", "f32", 2048, 131072),
+                            ("xent_split_bf16", "bf16", 1024, 262144)):
+            bws.append(BwdWorkload(n, workloads.make("xent_f32", rows=R, cols=C, dtype=dt), dev,
+                                   torch, fr))
             log(f"generated {n}")
         for _ in range(max(3, args.warmup)):
             for b in bws:

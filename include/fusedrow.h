@@ -67,7 +67,9 @@ typedef enum {
   FR_OP_XENT = 3,
   FR_OP_SOFTMAX_BWD = 4,
   FR_OP_RMSNORM_BWD = 5,
-  FR_OP_LAYERNORM_BWD = 6
+  FR_OP_LAYERNORM_BWD = 6,
+  FR_OP_SOFTMAX_SPLIT = 7,
+  FR_OP_XENT_SPLIT = 8
 } fr_op_t;
 
 typedef enum {
@@ -184,6 +186,45 @@ FR_API fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels,
                                void* grad, int32_t* argmax, float* loss_total,
                                int64_t rows, int64_t cols, fr_dtype_t dtype,
                                const fr_xent_options_t* options, void* stream);
+
+/* ---- split rows: any width up to FR_SPLIT_MAX_COLS ---- */
+
+/* Widest row of the split entry points (the argmax column is carried as an
+ * exact fp32 integer). */
+#define FR_SPLIT_MAX_COLS (1 << 24)
+/* Smallest segment the split kernels use (the workspace bound below). */
+#define FR_SPLIT_MIN_SEGMENT 8192
+
+/* Bytes of workspace the split entry points need for [rows, cols]:
+ * rows * ceil(cols / FR_SPLIT_MIN_SEGMENT) * 16 (one 16-byte partial state
+ * per row segment). -1 for an invalid shape. */
+FR_API int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Softmax for rows of any width (and for few rows: several workgroups share
+ * a row). Same result definition as fr_softmax_fwd. A row is cut into
+ * segments of 8192 columns (other segment shapes via fr_debug_force_variant); pass 1 writes each segment's partial state
+ * (max, exponential sum) to `workspace`, pass 2 merges a row's partials in
+ * segment order with the online normaliser merge and writes the segment's
+ * outputs. Reads x twice, writes y once.
+ *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.1:
+ *    the merge of partial (max, sum) states.)
+ * x, y as for fr_softmax_fwd (y may equal x); 1 <= cols <= FR_SPLIT_MAX_COLS.
+ * workspace: device memory of >= fr_split_workspace_bytes(rows, cols) bytes,
+ * 16-byte aligned, not overlapping any other buffer; contents on entry do not
+ * matter. Two kernels on `stream`. Results are bitwise reproducible. */
+FR_API fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t cols,
+                                 fr_dtype_t x_dtype, fr_dtype_t y_dtype, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/* Cross-entropy (with the options of fr_softmax_xent_ex) for rows of any
+ * width, split as fr_softmax_fwd_split (the partials also carry the sum of
+ * the logits and the column of the maximum). Arguments and results as
+ * fr_softmax_xent_ex, plus the workspace as fr_softmax_fwd_split. */
+FR_API fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, float* loss,
+                                  void* grad, int32_t* argmax, float* loss_total,
+                                  int64_t rows, int64_t cols, fr_dtype_t dtype,
+                                  const fr_xent_options_t* options, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
 
 /* ---- backward of the row operations ---- */
 

@@ -21,6 +21,8 @@ __all__ = [
     "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
+    "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
+    "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
     "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
@@ -30,6 +32,8 @@ __all__ = [
 F32, BF16 = 0, 1
 OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
 OP_SOFTMAX_BWD, OP_RMSNORM_BWD, OP_LAYERNORM_BWD = 4, 5, 6
+OP_SOFTMAX_SPLIT, OP_XENT_SPLIT = 7, 8
+FR_SPLIT_MAX_COLS = 1 << 24
 FR_MAX_COLS = 65536
 FR_BWD_MAX_COLS = 16384
 FR_BWD_PARTIALS = 512
@@ -80,6 +84,9 @@ def _load() -> ctypes.CDLL:
         "fr_stream_copy": [P, P, I64, P],
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
         "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
+        "fr_softmax_fwd_split": [P, P, I64, I64, I32, I32, P, I64, P],
+        "fr_softmax_xent_split": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P,
+                                  I64, P],
         "fr_add_rmsnorm_bwd": [P, P, P, P, P, P, P, I64, I64, I64, F, I32, P],
         "fr_layernorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, P],
         "fr_debug_force_variant": [I32, I32, I32],
@@ -89,6 +96,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.fr_split_workspace_bytes.argtypes = [I64, I64]
+    L.fr_split_workspace_bytes.restype = ctypes.c_int64
     L.fr_norm_bwd_workspace_bytes.argtypes = [I32, I64, I64]
     L.fr_norm_bwd_workspace_bytes.restype = ctypes.c_int64
     L.fr_status_str.argtypes = [ctypes.c_int]
@@ -257,6 +266,54 @@ def fr_softmax_xent_ex(logits, labels, loss, grad, argmax=None, loss_total=None,
            "fr_softmax_xent_ex")
 
 
+def fr_split_workspace_bytes(rows: int, cols: int) -> int:
+    """Workspace bytes of the split-row entry points (C: same name)."""
+    n = int(lib.fr_split_workspace_bytes(int(rows), int(cols)))
+    if n < 0:
+        raise ValueError(f"no split workspace size for [{rows}, {cols}]")
+    return n
+
+
+def fr_softmax_fwd_split(x, y, workspace, stream=None) -> None:
+    """Row softmax of any width, several workgroups per row (C: fr_softmax_fwd_split)."""
+    _need_cuda(x, y)
+    R, C = _rows_cols(x)
+    if tuple(y.shape) != (R, C) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tensor of x's shape")
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_softmax_fwd_split(_ptr(x), _ptr(y), R, C, _dtype_code(x), _dtype_code(y), wp, wn,
+                                    _stream(stream, x)), "fr_softmax_fwd_split")
+
+
+def fr_softmax_xent_split(logits, labels, loss, grad, workspace, argmax=None, loss_total=None,
+                          ignore_index=None, label_smoothing: float = 0.0, grad_scale: float = 1.0,
+                          reduction: str = "none", stream=None) -> None:
+    """Cross-entropy with options for rows of any width (C: fr_softmax_xent_split)."""
+    torch = _torch()
+    _need_cuda(logits, labels, loss, grad, argmax, loss_total)
+    R, C = _rows_cols(logits)
+    _check_rows(labels, R, "labels", torch.int32)
+    _check_rows(loss, R, "loss", torch.float32)
+    if argmax is not None:
+        _check_rows(argmax, R, "argmax", torch.int32)
+    if loss_total is not None and (loss_total.numel() < 1 or loss_total.dtype != torch.float32):
+        raise ValueError("loss_total must be a float32 tensor of at least one element")
+    if tuple(grad.shape) != (R, C) or not grad.is_contiguous() or grad.dtype != logits.dtype:
+        raise ValueError("grad must be a contiguous tensor of logits' shape and dtype")
+    opts = XentOptions(int(ignore_index is not None), int(ignore_index or 0), float(label_smoothing),
+                       float(grad_scale), _REDUCTIONS[reduction])
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_softmax_xent_split(_ptr(logits), _ptr(labels), _ptr(loss), _ptr(grad),
+                                     _ptr(argmax), _ptr(loss_total), R, C, _dtype_code(logits),
+                                     ctypes.byref(opts), wp, wn, _stream(stream, logits)),
+           "fr_softmax_xent_split")
+
+
+def _split_workspace(R, C, device):
+    torch = _torch()
+    return torch.empty(max(fr_split_workspace_bytes(R, C), 16), dtype=torch.uint8, device=device)
+
+
 def _check_like(t, ref, name):
     if t is not None and (tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous()
                           or t.dtype != ref.dtype):
@@ -379,9 +436,13 @@ class forced_variant:
 # ------------------------------------------------- allocating conveniences
 
 def softmax(x, out_dtype=None, out=None):
+    """Row softmax; rows wider than FR_MAX_COLS take the split-row path."""
     torch = _torch()
     y = out if out is not None else torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    fr_softmax_fwd(x, y)
+    if x.shape[1] > FR_MAX_COLS:
+        fr_softmax_fwd_split(x, y, _split_workspace(x.shape[0], x.shape[1], x.device))
+    else:
+        fr_softmax_fwd(x, y)
     return y
 
 
@@ -414,7 +475,13 @@ def softmax_xent(logits, labels, return_argmax: bool = False, ignore_index=None,
     am = torch.empty(R, dtype=torch.int32, device=logits.device) if return_argmax else None
     plain = (logits.dtype == torch.float32 and ignore_index is None and label_smoothing == 0.0
              and reduction == "none" and grad_scale == 1.0)
-    if plain:
+    if logits.shape[1] > FR_MAX_COLS:
+        total = torch.empty(1, dtype=torch.float32, device=logits.device)
+        fr_softmax_xent_split(logits, labels, loss, grad, _split_workspace(R, logits.shape[1],
+                              logits.device), am, total, ignore_index, label_smoothing, grad_scale,
+                              reduction)
+        out = loss if reduction == "none" else total
+    elif plain:
         fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, am)
         out = loss
     else:

@@ -20,7 +20,7 @@ struct Forced {
   std::atomic<int> threads{0};
   std::atomic<int> vecs{0};
 };
-Forced g_forced[FR_OP_LAYERNORM_BWD + 1];
+Forced g_forced[FR_OP_XENT_SPLIT + 1];
 
 // ------------------------------------------------------------------- buffers
 struct Buf {
@@ -93,6 +93,19 @@ const V* select_variant(VariantSpan<V> sp, int op, int64_t cols, int epv) {
 
 fr_status_t launch_status(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_LAUNCH; }
 
+// Split-row shape: a forced (threads, vecs), else the table's first shape on
+// the requested path (the smallest segment: measured fastest on MI355X).
+const fr::SplitVariant* select_split(VariantSpan<fr::SplitVariant> sp, int op, int epv) {
+  const int ft = g_forced[op].threads.load(std::memory_order_relaxed);
+  const int fv = g_forced[op].vecs.load(std::memory_order_relaxed);
+  for (size_t i = 0; i < sp.n; ++i) {
+    const fr::SplitVariant& v = sp.v[i];
+    if (v.epv != epv) continue;
+    if (!ft || (v.threads == ft && v.nv == fv)) return &v;
+  }
+  return nullptr;
+}
+
 thread_local int t_last_launch_error = 0;
 
 int vec_epv(int esz) { return 16 / esz; }
@@ -126,7 +139,7 @@ const char* fr_status_str(fr_status_t s) {
 const char* fr_version(void) { return "fusedrow 0.1.0 (gfx950)"; }
 
 fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs) {
-  if (op < FR_OP_SOFTMAX || op > FR_OP_LAYERNORM_BWD) return FR_E_VALUE;
+  if (op < FR_OP_SOFTMAX || op > FR_OP_XENT_SPLIT) return FR_E_VALUE;
   if (threads < 0 || vecs < 0) return FR_E_VALUE;
   g_forced[op].vecs.store(threads ? vecs : 0);
   g_forced[op].threads.store(threads);
@@ -138,7 +151,9 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
                                     int* elems_per_vec) {
   if (!threads || !vecs || !elems_per_vec) return FR_E_NULL;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return FR_E_DTYPE;
-  if (cols < 1 || cols > FR_MAX_COLS) return FR_E_SHAPE;
+  const int64_t maxc =
+      (op == FR_OP_SOFTMAX_SPLIT || op == FR_OP_XENT_SPLIT) ? FR_SPLIT_MAX_COLS : FR_MAX_COLS;
+  if (cols < 1 || cols > maxc) return FR_E_SHAPE;
   const int epv = vector_path ? vec_epv(esize(in_dtype)) : 1;
   int t = 0, n = 0, e = 0;
   switch (op) {
@@ -181,6 +196,15 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
     case FR_OP_LAYERNORM_BWD: {
       if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
       auto v = select_variant(fr::layernorm_bwd_variants(in_dtype == FR_BF16), op, cols, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_SOFTMAX_SPLIT:
+    case FR_OP_XENT_SPLIT: {
+      // the shape for a single row of `cols` (few rows: the smallest segment)
+      auto v = select_split(fr::split_variants(in_dtype == FR_BF16, out_dtype == FR_BF16,
+                                               op == FR_OP_XENT_SPLIT),
+                            op, epv);
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -467,6 +491,106 @@ fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* gamma, c
                                               (int)cols, st)))
     return s;
   return launch_status(fr::launch_colsum(ws, grid, (int)cols, dgamma, dbeta, st));
+}
+
+int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 1 || cols > FR_SPLIT_MAX_COLS) return -1;
+  if (rows > INT64_MAX / 8 / cols) return -1;
+  return rows * ((cols + FR_SPLIT_MIN_SEGMENT - 1) / FR_SPLIT_MIN_SEGMENT) * 16;
+}
+
+namespace {
+// Shared argument checks of the split entry points (rows, cols, workspace).
+fr_status_t check_split(int64_t rows, int64_t cols, const void* workspace, int64_t workspace_bytes) {
+  if (rows < 0 || cols < 1 || cols > FR_SPLIT_MAX_COLS) return FR_E_SHAPE;
+  if (rows > INT64_MAX / 8 / cols) return FR_E_SHAPE;
+  if (rows == 0) return FR_OK;
+  if (workspace_bytes < fr_split_workspace_bytes(rows, cols)) return FR_E_SHAPE;
+  if (!workspace) return FR_E_NULL;
+  if (!aligned(workspace, 16)) return FR_E_ALIGN;
+  return FR_OK;
+}
+}  // namespace
+
+fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t cols,
+                                 fr_dtype_t x_dtype, fr_dtype_t y_dtype, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  if (fr_status_t s = check_split(rows, cols, workspace, workspace_bytes)) return s;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return FR_E_DTYPE;
+  if (rows == 0) return FR_OK;
+  if (!x || !y) return FR_E_NULL;
+  const int xs = esize(x_dtype), ys = esize(y_dtype);
+  if (!aligned(x, xs) || !aligned(y, ys)) return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(x, rows * cols * xs, true, xs, false),
+                      make_buf(y, rows * cols * ys, true, ys, true),
+                      make_buf(workspace, fr_split_workspace_bytes(rows, cols), false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 3)) return s;
+  const int ve = vec_epv(xs);
+  bool vec;
+  if (xs == ys) vec = (reinterpret_cast<uintptr_t>(x) % 16) == (reinterpret_cast<uintptr_t>(y) % 16);
+  else vec = aligned(x, 16) && aligned(y, 16) && cols % ve == 0;
+  const fr::SplitVariant* v =
+      select_split(fr::split_variants(x_dtype == FR_BF16, y_dtype == FR_BF16, 0),
+                   FR_OP_SOFTMAX_SPLIT, vec ? ve : 1);
+  if (!v) return FR_E_VARIANT;
+  return launch_status(v->launch(x, y, rows, (int)cols, nullptr, nullptr, nullptr, nullptr,
+                                 static_cast<float4*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, float* loss,
+                                  void* grad, int32_t* argmax, float* loss_total, int64_t rows,
+                                  int64_t cols, fr_dtype_t dtype, const fr_xent_options_t* options,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  if (fr_status_t s = check_split(rows, cols, workspace, workspace_bytes)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  fr_xent_options_t o = {0, 0, 0.f, 1.f, FR_REDUCE_NONE};
+  if (options) o = *options;
+  if (!std::isfinite(o.label_smoothing) || o.label_smoothing < 0.f || o.label_smoothing > 1.f ||
+      !std::isfinite(o.grad_scale) ||
+      (o.reduction != FR_REDUCE_NONE && o.reduction != FR_REDUCE_SUM &&
+       o.reduction != FR_REDUCE_MEAN))
+    return FR_E_VALUE;
+  if (o.reduction == FR_REDUCE_MEAN && rows > (int64_t)UINT32_MAX) return FR_E_SHAPE;
+  const bool reduce = o.reduction != FR_REDUCE_NONE;
+  if (reduce && !loss_total) return FR_E_NULL;
+  if (loss_total && !aligned(loss_total, 4)) return FR_E_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* count = o.reduction == FR_REDUCE_MEAN ? reinterpret_cast<uint32_t*>(loss_total) : nullptr;
+  if (rows == 0) {
+    if (!reduce) return FR_OK;
+    if (count)
+      if (fr_status_t s = launch_status(fr::launch_xent_count(labels, 0, 0, 0, count, st))) return s;
+    return launch_status(fr::launch_xent_total(loss, 0, count, loss_total, st));
+  }
+  if (!logits || !labels || !loss || !grad) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(logits, es) || !aligned(grad, es) || !aligned(labels, 4) || !aligned(loss, 4) ||
+      (argmax && !aligned(argmax, 4)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(logits, rows * cols * es, true, es, false),
+                      make_buf(labels, rows * 4, false, 4, false),
+                      make_buf(loss, rows * 4, false, 4, true),
+                      make_buf(grad, rows * cols * es, true, es, true),
+                      make_buf(argmax, rows * 4, false, 4, true),
+                      make_buf(reduce ? loss_total : nullptr, 4, false, 4, true),
+                      make_buf(workspace, fr_split_workspace_bytes(rows, cols), false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 7)) return s;
+  const bool vec =
+      (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
+  const fr::SplitVariant* v = select_split(fr::split_variants(dtype == FR_BF16, dtype == FR_BF16, 1),
+                                           FR_OP_XENT_SPLIT, vec ? vec_epv(es) : 1);
+  if (!v) return FR_E_VARIANT;
+  if (count)
+    if (fr_status_t s = launch_status(
+            fr::launch_xent_count(labels, rows, o.use_ignore_index != 0, o.ignore_index, count, st)))
+      return s;
+  const fr::XentOptions ko = {o.use_ignore_index != 0, o.ignore_index, o.label_smoothing,
+                              o.grad_scale, count};
+  if (fr_status_t s = launch_status(v->launch(logits, grad, rows, (int)cols, labels, loss, argmax,
+                                              &ko, static_cast<float4*>(workspace), st)))
+    return s;
+  if (!reduce) return FR_OK;
+  return launch_status(fr::launch_xent_total(loss, rows, count, loss_total, st));
 }
 
 fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -78,11 +78,19 @@ inline int bwd_grid(const V& v, int64_t rows) {
   return (int)(g < v.grid_max ? g : v.grid_max);
 }
 
+// Split-row launch: pass 1 (segment partials into `part`, 16 bytes per
+// (row, segment)) then pass 2, both on `s`. Segment = threads * nv * epv
+// columns. labels / loss / argmax / opt: cross-entropy only (NULL otherwise).
+typedef hipError_t (*SplitLaunch)(const void* x, void* y, int64_t rows, int cols,
+                                  const int32_t* labels, float* loss, int32_t* argmax,
+                                  const XentOptions* opt, float4* part, hipStream_t s);
+
 typedef Variant<SoftmaxLaunch> SoftmaxVariant;
 typedef Variant<LayerNormLaunch> LayerNormVariant;
 typedef Variant<RmsNormLaunch> RmsNormVariant;
 typedef Variant<XentLaunch> XentVariant;
 typedef Variant<SoftmaxBwdLaunch> SoftmaxBwdVariant;
+typedef Variant<SplitLaunch> SplitVariant;
 typedef BwdVariant<RmsNormBwdLaunch> RmsNormBwdVariant;
 typedef BwdVariant<LayerNormBwdLaunch> LayerNormBwdVariant;
 
@@ -91,6 +99,7 @@ VariantSpan<LayerNormVariant> layernorm_variants(int bf16);
 VariantSpan<RmsNormVariant> rmsnorm_variants(int bf16);
 VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
 VariantSpan<XentVariant> xent_ex_variants(int bf16, int with_argmax);
+VariantSpan<SplitVariant> split_variants(int in_bf16, int out_bf16, int xent);
 hipError_t launch_xent_count(const int32_t* labels, int64_t rows, int use_ignore, int ignore_index,
                              uint32_t* out, hipStream_t s);
 hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* count, float* total,

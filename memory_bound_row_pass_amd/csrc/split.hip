@@ -1,0 +1,333 @@
+// Split-row softmax and softmax cross-entropy: rows of any width up to 2^24,
+// several workgroups per row.
+//
+// A row is cut into segments of `seg` columns (a multiple of 32, so every
+// segment keeps its row's address phase); workgroup (row, segment) owns one
+// segment in registers.
+//   pass 1 (split_stats_kernel): the segment's partial online-softmax state
+//     (m, s) plus the sum of its logits t and the column of its maximum,
+//     written to the workspace [rows][segments];
+//   pass 2 (split_apply_kernel): every workgroup of a row merges the row's
+//     partials in segment order (the same order, hence the same bits, in all
+//     of them), re-reads its segment and writes p (or the cross-entropy
+//     gradient, loss and argmax).
+// The merge is the online normaliser's ("Engineering a CUDA Machine Learning
+// Framework from Scratch", §3.1) applied to segment states: partials merged
+// by a second pass. Logits are read twice and the outputs written once;
+// pass 1 uses ordinary (cached) loads so the second read of a segment can
+// come from the last-level cache.
+#include "fr_kernels.hpp"
+#include "softmax_core.hpp"
+
+namespace fr {
+
+// (m, s, t, idx): max, sum of exp(x - m), sum of x, column of the max
+// (a float, exact below 2^24; empty 3e38). Empty state (-inf, 0, 0, 3e38).
+struct SplitState {
+  float m, s, t, idx;
+  template <int C, int M>
+  static __device__ __forceinline__ SplitState move(const SplitState& a) {
+    return {dpp_move<C, M>(a.m, kNegInf), dpp_move<C, M>(a.s, 0.f), dpp_move<C, M>(a.t, 0.f),
+            dpp_move<C, M>(a.idx, 3.0e38f)};
+  }
+  __device__ __forceinline__ SplitState lane63() const {
+    return {read_lane63(m), read_lane63(s), read_lane63(t), read_lane63(idx)};
+  }
+};
+struct SplitMerge {
+  __device__ __forceinline__ SplitState operator()(const SplitState& a, const SplitState& b) const {
+    const MaxSumState r = MaxSumMerge<false>{}(MaxSumState{a.m, a.s}, MaxSumState{b.m, b.s});
+    const float lo_idx = a.idx < b.idx ? a.idx : b.idx;
+    const float idx = a.m > b.m ? a.idx : (b.m > a.m ? b.idx : lo_idx);
+    return {r.m, r.s, a.t + b.t, idx};
+  }
+};
+
+// Segment `sg` of a row: [c0, c0 + len).
+struct Segment {
+  int c0, len;
+  __device__ __forceinline__ Segment(int sg, int seg, int cols)
+      : c0(sg * seg), len(cols - sg * seg < seg ? cols - sg * seg : seg) {}
+};
+
+// ------------------------------------------------------------------ pass 1
+
+// STATS bit 1: the sum of the logits (label smoothing); bit 2: the column of
+// the maximum (argmax). Without them a segment costs a max, a subtraction, a
+// multiply and one base-2 exponential per element: the sum of exponentials
+// needs no compensated exponential (its relative error is an average of the
+// terms' errors, each about |x - m| * log2e * 2^-24 for the terms that
+// matter), unlike an output p_j. x - m is formed first: folding m into an fma
+// with log2e would put the rounding of m * log2e (|m| * 2^-24) into every
+// term.
+template <typename Tin, int T, int NV, int EPV, int OCC, int STATS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
+                        const int32_t* labels, XentOptions opt, int skip_ignored, float4* part) {
+  constexpr int NW = T / 64;
+  constexpr bool WANT_T = STATS & 1;
+  constexpr bool WANT_IDX = STATS & 2;
+  __shared__ float xw[2][NW][4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t work = rows * nseg;
+  int it = 0;
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+    const int64_t row = w / nseg;
+    const int sg = (int)(w - row * nseg);
+    const Segment sgm(sg, seg, cols);
+    if (skip_ignored && labels[row] == opt.ignore_index) {  // uniform; its partial is not read
+      continue;
+    }
+    const Tin* xs = x + row * cols + sgm.c0;
+    const RowGeom<EPV> g(xs, sgm.len);
+    float v[NV][EPV];
+    load_chunks<Tin, T, NV, EPV>(xs, g, tid, v, kNegInf);
+    const int ec = g.extra_col(tid);
+    float xe = load_extra(xs, ec, kNegInf);
+
+    const float m = lane_max<NV, EPV>(v, xe);
+    float t = 0.f, best = 3.0e38f;
+    if constexpr (WANT_T) {  // masked slots hold -inf and are skipped
+      const bool full = g.nvec == T * NV;
+      float t0 = ec >= 0 ? xe : 0.f, t1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const bool ok = full || i * T + tid < g.nvec;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float a = ok ? v[i][k] : 0.f;
+          if (k & 1) t1 += a; else t0 += a;
+        }
+      }
+      t = t0 + t1;
+    }
+    if constexpr (WANT_IDX) {
+      // first slot holding the lane max: scan backwards keeping the last
+      // match; slot order is column order within a lane
+      int c = -1;
+#pragma unroll
+      for (int i = NV - 1; i >= 0; --i)
+#pragma unroll
+        for (int k = EPV - 1; k >= 0; --k) c = v[i][k] == m ? i * EPV + k : c;
+      if (c >= 0)
+        best = (float)(sgm.c0 + g.head + ((c / EPV) * T + tid) * EPV + (c % EPV));
+      if (ec >= 0 && xe == m) {
+        const float ce = (float)(sgm.c0 + ec);
+        best = ce < best ? ce : best;
+      }
+    }
+    // sum of exp(x - m) with the hardware exponential
+    const float mr = (m == kNegInf) ? 0.f : m;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const float e = exp2_hw((v[i][k] - mr) * kLog2e);
+        if (k & 1) s1 += e; else s0 += e;
+      }
+    const float se = exp2_hw((xe - mr) * kLog2e);
+    SplitState st{m, (s0 + s1) + se, t, best};
+    st = wave_reduce(st, SplitMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SplitMerge{});
+    if (tid == 0) part[w] = float4{st.m, st.s, st.t, st.idx};
+  }
+}
+
+// ------------------------------------------------------------------ pass 2
+
+// The row's merged state: lane j merges partials j, j + T, ... in order, then
+// the DPP tree and the LDS merge (a fixed order: every workgroup of the row
+// gets the same bits).
+template <int T>
+__device__ __forceinline__ SplitState merge_row(const float4* part, int64_t row, int nseg,
+                                                float (*slot)[4], int wave, int lane, int tid) {
+  constexpr int NW = T / 64;
+  SplitState st{kNegInf, 0.f, 0.f, 3.0e38f};
+  for (int j = tid; j < nseg; j += T) {
+    const float4 p = part[row * nseg + j];
+    st = SplitMerge{}(st, SplitState{p.x, p.y, p.z, p.w});
+  }
+  st = wave_reduce(st, SplitMerge{});
+  if constexpr (NW > 1) st = block_merge<NW>(st, slot, wave, lane, SplitMerge{});
+  return st;
+}
+
+// p_j = exp(x_j - M) / S into the output type. bf16 outputs: a biased base-2
+// exponential kept in fp32's normal range, scaled down by 2^-64 with ldexp so
+// that bf16 subnormal results are rounded from full-precision values.
+template <typename Tout>
+__device__ __forceinline__ float split_p(float xv, float M, float inv_s) {
+  if constexpr (sizeof(Tout) == 2) {
+    const float e = exp2_hw(__builtin_fmaf(xv - M, kLog2e, 64.f));
+    return __builtin_ldexpf(e * inv_s, -64);
+  } else {
+    return exp_acc(xv - M) * inv_s;
+  }
+}
+
+// XENT: y is the gradient (Tout == Tin); loss, argmax, labels and opt apply.
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, int nseg,
+                        const float4* part, const int32_t* labels, float* loss, int32_t* argmax,
+                        XentOptions opt) {
+  constexpr int NW = T / 64;
+  __shared__ float xw[2][NW][4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+
+  float gsc = 1.f, goff = 0.f;
+  if constexpr (XENT) {
+    gsc = opt.grad_scale;
+    if (opt.count) gsc = gsc / (float)(*opt.count);
+    goff = gsc * (opt.smoothing / (float)cols);
+  }
+
+  const int64_t work = rows * nseg;
+  int it = 0;
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+    const int64_t row = w / nseg;
+    const int sg = (int)(w - row * nseg);
+    const Segment sgm(sg, seg, cols);
+    const Tin* xs = x + row * cols + sgm.c0;
+    Tout* ys = y + row * cols + sgm.c0;
+    const RowGeom<EPV> g(xs, sgm.len);
+    const int ec = g.extra_col(tid);
+
+    int label = 0;
+    bool ignored = false;
+    if constexpr (XENT) {
+      label = __builtin_amdgcn_readfirstlane(labels[row]);
+      ignored = opt.use_ignore && label == opt.ignore_index;
+    }
+    if (ignored) {  // uniform: a zero gradient segment, loss 0
+      float z[NV][EPV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) z[i][k] = 0.f;
+      store_chunks<Tout, T, NV, EPV>(ys, g, tid, z);
+      if (ec >= 0) store1(ys + ec, 0.f);
+      if (argmax) {  // uniform: every lane takes part in the merge (it has a barrier);
+                     // pass 1 wrote this row's partials because argmax is wanted
+        const SplitState st = merge_row<T>(part, row, nseg, xw[it & 1], wave, lane, tid);
+        if (sg == 0 && tid == 0) argmax[row] = (int32_t)st.idx;
+      }
+      if (sg == 0 && tid == 0) loss[row] = 0.f;
+      continue;
+    }
+
+    const SplitState st = merge_row<T>(part, row, nseg, xw[it & 1], wave, lane, tid);
+    const float inv_s = 1.f / st.s;
+
+    float v[NV][EPV];
+    load_chunks<Tin, T, NV, EPV>(xs, g, tid, v, kNegInf);
+    float xe = load_extra(xs, ec, kNegInf);
+
+    // label column handled by the lane of this segment that owns it
+    bool label_lane = false;
+    float x_label = 0.f;
+    const bool valid = XENT && label >= 0 && label < cols;
+    if constexpr (XENT) {
+      const int lc = label - sgm.c0;
+      if (valid && lc >= 0 && lc < sgm.len) {
+        const int body_end = g.head + g.nvec * EPV;
+        const int owner = lc < g.head ? lc
+                          : lc >= body_end ? g.head + (lc - body_end)
+                                           : ((lc - g.head) / EPV) % T;
+        label_lane = owner == tid;
+      }
+      if (label_lane) x_label = load1(xs + lc);
+    }
+
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const float p = split_p<Tout>(v[i][k], st.m, inv_s);
+        v[i][k] = XENT ? __builtin_fmaf(p, gsc, -goff) : p;
+      }
+    {
+      const float p = split_p<Tout>(xe, st.m, inv_s);
+      xe = XENT ? __builtin_fmaf(p, gsc, -goff) : p;
+    }
+    store_chunks<Tout, T, NV, EPV>(ys, g, tid, v);
+    if (ec >= 0) store1(ys + ec, xe);
+
+    if constexpr (XENT) {
+      if (label_lane) {
+        const float eps = opt.smoothing;
+        const float p = exp_acc(x_label - st.m) * inv_s;
+        store1(ys + (label - sgm.c0), gsc * ((p - (1.f - eps)) - eps / (float)cols));
+        float l = st.m + logf(st.s);
+        if (eps != 1.f) l -= (1.f - eps) * x_label;
+        if (eps != 0.f) l -= eps * (st.t / (float)cols);
+        loss[row] = l;
+      } else if (!valid && sg == 0 && tid == 0) {
+        loss[row] = __builtin_nanf("");
+      }
+      if (argmax && sg == 0 && tid == 0) argmax[row] = (int32_t)st.idx;
+    }
+  }
+}
+
+// --------------------------------------------------------------- launchers
+
+static unsigned split_grid(int64_t work) {
+  return (unsigned)(work < kMaxGrid ? work : kMaxGrid);
+}
+
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT>
+static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, const int32_t* labels,
+                               float* loss, int32_t* argmax, const XentOptions* opt, float4* part,
+                               hipStream_t s) {
+  constexpr int SEG = T * NV * EPV;
+  const int nseg = (cols + SEG - 1) / SEG;
+  const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
+  const int skip = XENT && o.use_ignore && !argmax;
+  const unsigned grid = split_grid(rows * nseg);
+  const int stats = XENT ? ((o.smoothing != 0.f ? 1 : 0) | (argmax ? 2 : 0)) : 0;
+  auto k1 = stats == 0   ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 0>
+            : stats == 1 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 1>
+            : stats == 2 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 2>
+                         : &split_stats_kernel<Tin, T, NV, EPV, OCC, 3>;
+  hipError_t e = launch_kernel(k1, dim3(grid), dim3(T), s, static_cast<const Tin*>(x), rows, cols,
+                               SEG, nseg, labels, o, skip, part);
+  if (e != hipSuccess) return e;
+  return launch_kernel(&split_apply_kernel<Tin, Tout, T, NV, EPV, OCC, XENT>, dim3(grid), dim3(T), s,
+                       static_cast<const Tin*>(x), static_cast<Tout*>(y), rows, cols, SEG, nseg,
+                       static_cast<const float4*>(part), labels, loss, argmax, o);
+}
+
+#define FR_SP(TI, TO, T, NV, EPV, OCC, X) {T, NV, EPV, &launch_split<TI, TO, T, NV, EPV, OCC, X>}
+// Segment shapes, 32 elements per lane: 256 lanes (8192 columns, the
+// default: several workgroups per CU overlap one segment's loads with
+// another's arithmetic), 512 and 1024 lanes; the scalar path (unaligned
+// phases) 256 lanes x 32 elements.
+#define FR_SP_TABLE(TI, TO, E, X)                                                           \
+  {FR_SP(TI, TO, 256, 32 / E, E, 4, X),  FR_SP(TI, TO, 512, 32 / E, E, 4, X),                 \
+   FR_SP(TI, TO, 1024, 32 / E, E, 4, X), FR_SP(TI, TO, 256, 32, 1, 4, X)}
+
+static const SplitVariant kSpF32F32[] = FR_SP_TABLE(float, float, 4, false);
+static const SplitVariant kSpBf16Bf16[] = FR_SP_TABLE(bf16_t, bf16_t, 8, false);
+static const SplitVariant kSpF32Bf16[] = FR_SP_TABLE(float, bf16_t, 4, false);
+static const SplitVariant kSpBf16F32[] = FR_SP_TABLE(bf16_t, float, 8, false);
+static const SplitVariant kSpXeF32[] = FR_SP_TABLE(float, float, 4, true);
+static const SplitVariant kSpXeBf16[] = FR_SP_TABLE(bf16_t, bf16_t, 8, true);
+
+#define FR_SPAN(a) {a, sizeof(a) / sizeof(a[0])}
+
+VariantSpan<SplitVariant> split_variants(int in_bf16, int out_bf16, int xent) {
+  if (xent) return in_bf16 ? VariantSpan<SplitVariant>FR_SPAN(kSpXeBf16)
+                           : VariantSpan<SplitVariant>FR_SPAN(kSpXeF32);
+  if (in_bf16) return out_bf16 ? VariantSpan<SplitVariant>FR_SPAN(kSpBf16Bf16)
+                               : VariantSpan<SplitVariant>FR_SPAN(kSpBf16F32);
+  return out_bf16 ? VariantSpan<SplitVariant>FR_SPAN(kSpF32Bf16)
+                  : VariantSpan<SplitVariant>FR_SPAN(kSpF32F32);
+}
+
+}  // namespace fr

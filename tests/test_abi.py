@@ -193,6 +193,31 @@ def test_xent_ex_validation():
     assert call(g=A + 2) == E_ALIAS
 
 
+def test_split_validation():
+    f = fr.lib.fr_softmax_fwd_split
+    Y, WS = A + 0x100000, A + 0x200000
+    need = fr.fr_split_workspace_bytes(4, 100000)
+    assert need == 4 * 13 * 16                        # ceil(100000 / 8192) = 13 segments per row
+    assert f(P(A), P(Y), 0, 100000, 0, 0, None, 0, None) == OK
+    assert f(P(A), P(Y), 4, 100000, 0, 0, P(WS), need - 1, None) == E_SHAPE
+    assert f(P(A), P(Y), 4, fr.FR_SPLIT_MAX_COLS + 1, 0, 0, P(WS), 1 << 40, None) == E_SHAPE
+    assert f(P(A), P(Y), 4, 100000, 0, 0, None, need, None) == E_NULL
+    assert f(P(A), P(Y), 4, 100000, 0, 0, P(WS + 8), need, None) == E_ALIGN
+    assert f(P(A), P(Y), 4, 100000, 3, 0, P(WS), need, None) == E_DTYPE
+    assert f(P(A), P(A + 4), 4, 100000, 0, 0, P(WS), need, None) == E_ALIAS
+    assert f(P(A), P(Y), 4, 100000, 0, 0, P(Y + 16), need, None) == E_ALIAS   # workspace in y
+    g = fr.lib.fr_softmax_xent_split
+    L, LS, G = A + 0x300000, A + 0x400000, A + 0x500000
+    opts = fr.XentOptions(0, 0, 2.0, 1.0, 0)
+    assert g(P(A), P(L), P(LS), P(G), None, None, 4, 100000, 0, ctypes.byref(opts), P(WS), need,
+             None) == E_VALUE
+    opts = fr.XentOptions(0, 0, 0.0, 1.0, fr.REDUCE_SUM)
+    assert g(P(A), P(L), P(LS), P(G), None, None, 4, 100000, 0, ctypes.byref(opts), P(WS), need,
+             None) == E_NULL
+    with pytest.raises(ValueError):
+        fr.fr_split_workspace_bytes(4, 0)
+
+
 def test_stream_copy_validation():
     f = fr.lib.fr_stream_copy
     assert f(P(A), P(B), 0, None) == OK
@@ -223,6 +248,11 @@ def test_variant_selection():
             with pytest.raises(fr.FusedRowError) as ei:
                 fr.fr_debug_select_variant(op, fr.FR_BWD_MAX_COLS + 1, dt)
             assert ei.value.status == E_SHAPE
+    for op in (fr.OP_SOFTMAX_SPLIT, fr.OP_XENT_SPLIT):
+        for dt in (fr.F32, fr.BF16):
+            for vp in (True, False):
+                t, v, e = fr.fr_debug_select_variant(op, 262144, dt, vector_path=vp)
+                assert t * v * e >= 8192
     with fr.forced_variant(fr.OP_SOFTMAX, 1024, 16):
         assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (1024, 16, 4)
     assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (64, 4, 4)

@@ -43,6 +43,7 @@ def _load():
         "oracle_softmax_xent": ([P, I32, P, I64, I64, P, P, P], None),
         "oracle_softmax_bwd": ([P, P, I32, I64, I64, P], None),
         "oracle_softmax_xent_ex": ([P, I32, P, I64, I64, I32, I32, D, I32, D, P, P, P, P], None),
+        "oracle_attention": ([P, P, P, I32, I64, I64, I64, I64, I64, I32, D, P, P], None),
         "oracle_rmsnorm_bwd": ([P, P, P, P, I32, I64, I64, F, P, P], None),
         "oracle_layernorm_bwd": ([P, P, P, P, P, I32, I64, I64, P, P, P], None),
         "oracle_online_softmax_stats": ([P, I64, DP, DP], None),
@@ -174,6 +175,25 @@ def softmax_xent_ex(logits, labels, ignore_index=None, label_smoothing=0.0, redu
         int(ignore_index or 0), float(label_smoothing), red, float(grad_scale), _ptr(loss),
         _ptr(grad), _ptr(am), ctypes.byref(tot))
     return loss, grad, am, (tot.value if red else None)
+
+
+def attention(q, k, v, causal: bool = False, scale=None):
+    """Scaled dot-product attention. q [B, H, Sq, D], k and v [B, H, Sk, D]
+    (one dtype). Returns (o [B, H, Sq, D], lse [B, H, Sq]) in float64.
+    scale defaults to 1/sqrt(D) (pass the fp32 value an fp32 caller uses)."""
+    q, k, v = _c(q), _c(k), _c(v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v share one dtype")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != (B, H, Sk, D):
+        raise ValueError("k and v must be [B, H, Sk, D]")
+    sc = float(np.float32(1.0 / np.sqrt(D))) if scale is None else float(scale)
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, Sq, Sk, D,
+                             int(causal), sc, _ptr(o), _ptr(lse))
+    return o, lse
 
 
 def softmax_bwd(p, dy):

@@ -233,6 +233,55 @@ void oracle_softmax_xent_ex(const void* logits, int dtype, const int32_t* labels
     }
 }
 
+/* --------------------------------------------------------------- attention */
+/* Scaled dot-product attention per (batch, head), the plain definition the
+ * online softmax is fused into ("Engineering a CUDA Machine Learning
+ * Framework from Scratch", §3.1: the online normaliser inside attention):
+ * s_ij = scale * sum_d q_id k_jd over the keys j visible to query i (all j,
+ * or j <= i + (Sk - Sq) when causal: queries aligned to the end of the keys);
+ * lse_i = m_i + ln sum_j exp(s_ij - m_i); o_id = sum_j exp(s_ij - lse_i) v_jd.
+ * A query with no visible key: o = 0 and lse = -inf. q [B, H, Sq, D],
+ * k, v [B, H, Sk, D], o [B, H, Sq, D], lse [B, H, Sq] (may be NULL). */
+void oracle_attention(const void* q, const void* k, const void* v, int dtype, int64_t B, int64_t H,
+                      int64_t Sq, int64_t Sk, int64_t D, int causal, double scale, double* o,
+                      double* lse) {
+    const int64_t BH = B * H;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+#pragma omp for schedule(static) collapse(2)
+        for (int64_t bh = 0; bh < BH; ++bh)
+            for (int64_t i = 0; i < Sq; ++i) {
+                const int64_t qb = (bh * Sq + i) * D;
+                int64_t nk = Sk;
+                if (causal) {
+                    nk = i + (Sk - Sq) + 1;
+                    if (nk < 0) nk = 0;
+                    if (nk > Sk) nk = Sk;
+                }
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nk; ++j) {
+                    const int64_t kb = (bh * Sk + j) * D;
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) acc += load(q, dtype, qb + d) * load(k, dtype, kb + d);
+                    s[j] = scale * acc;
+                    if (s[j] > m) m = s[j];
+                }
+                double z = 0.0;
+                for (int64_t j = 0; j < nk; ++j) z += exp(s[j] - m);
+                const double l = nk > 0 ? m + log(z) : -INFINITY;
+                if (lse) lse[bh * Sq + i] = l;
+                for (int64_t d = 0; d < D; ++d) o[qb + d] = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    const double p = exp(s[j] - l);
+                    const int64_t vb = (bh * Sk + j) * D;
+                    for (int64_t d = 0; d < D; ++d) o[qb + d] += p * load(v, dtype, vb + d);
+                }
+            }
+        free(s);
+    }
+}
+
 /* ---------------------------------------------------------------- backward */
 /* The vector-Jacobian products of the row operations above (the backward
  * pipelines "NexusGrad" verifies against finite differences, Verified VJP

@@ -83,6 +83,15 @@ void oracle_softmax_xent_ex(const void* logits, int dtype, const int32_t* labels
                             int reduction, double grad_scale, double* loss, double* grad,
                             int32_t* argmax, double* total);
 
+/* Scaled dot-product attention per (batch, head):
+ * s_ij = scale * q_i . k_j over the visible keys (causal: j <= i + Sk - Sq);
+ * lse_i = log-sum-exp_j s_ij; o_i = sum_j exp(s_ij - lse_i) v_j.
+ * No visible key: o_i = 0, lse_i = -inf. Layouts [B, H, S, D] row-major;
+ * lse [B, H, Sq] may be NULL. */
+void oracle_attention(const void* q, const void* k, const void* v, int dtype, int64_t B, int64_t H,
+                      int64_t Sq, int64_t Sk, int64_t D, int causal, double scale, double* o,
+                      double* lse);
+
 /* ---- backward of the row operations (vector-Jacobian products) ---- */
 
 /* Softmax backward from the stored forward output p and the upstream

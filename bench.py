@@ -26,7 +26,9 @@ cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
 logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
 split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
 [2048, 131072], bf16 [1024, 262144]); they are
-reported under "backward" and "variants" and are not part of `value`. Their per-row inputs from the
+reported under "backward" and "variants" and are not part of `value`; so is the
+attention forward (bf16 B=4 H=16 S=4096 D=128, causal and not), reported
+under "attention" in matrix TFLOP/s against the bf16 peak. Their per-row inputs from the
 forward (p, mean, rstd) are produced by the forward kernels before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -187,6 +189,40 @@ def launch_stats(w, us):
         "rows_per_s": round(w.R / (med * 1e-6), 1),
         "input_sha256": w.w.digest()[:16],
     }
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+
+def attention_stats(torch, np, fr, workloads, dev, K):
+    """Attention forward, bf16, B=4 H=16 S=4096 D=128, causal and not: per
+    call duration (HIP events) and matrix TFLOP/s against the bf16 peak.
+    Flops: 4 B H Sq Sk D (two products), half of that when causal."""
+    w = workloads.make_attention(4, 16, 4096, 4096, 128)
+
+    def d(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = d(w["q"]), d(w["k"]), d(w["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty(4, 16, 4096, device=dev)
+    runs = [lambda: fr.fr_attention_fwd(q, k, v, o, lse, False),
+            lambda: fr.fr_attention_fwd(q, k, v, o, lse, True)]
+    for r in runs:
+        for _ in range(3):
+            r()
+    torch.cuda.synchronize()
+    us = time_calls(torch, np, runs, max(5, min(K, 20)))
+    out = {}
+    flops = 4.0 * 64 * 4096 * 4096 * 128
+    for name, u, f in (("attention_bf16_b4h16s4096d128", us[0], flops),
+                       ("attention_bf16_b4h16s4096d128_causal", us[1], flops / 2)):
+        med = float(np.median(u))
+        tf = f / (med * 1e-6) / 1e12
+        out[name] = {"median_us": round(med, 2), "tflops": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": f,
+                     "input_sha256": w.digest()[:16]}
+    return out
 
 
 def kernel_source_digest():
@@ -382,7 +418,7 @@ def main():
     per = {w.name: launch_stats(w, us)
            for w, us in zip(wls, time_calls(torch, np, [w.run for w in wls], K))}
 
-    backward, variants = {}, {}
+    backward, variants, attention = {}, {}, {}
     if not args.no_backward:
         bws = []
         for n in ("softmax_bwd_bf16", "layernorm_bwd_f32", "add_rmsnorm_bwd_bf16"):
@@ -407,6 +443,9 @@ def main():
         backward = {b.name: timed[b.name] for b in bws[:nb]}
         variants = {b.name: timed[b.name] for b in bws[nb:]}
         log("backward and variant calls timed")
+        del bws
+        attention = attention_stats(torch, np, fr, workloads, dev, K)
+        log("attention timed")
 
     ceiling = copy_ceiling(torch, fr, dev)
     log(f"copy ceiling {ceiling:.0f} GB/s")
@@ -442,6 +481,7 @@ def main():
         "per_workload": per,
         "backward": backward,
         "variants": variants,
+        "attention": attention,
         "roofline": {
             "bound": "hbm",
             "kernel": f"xent_kernel<float,{dom['variant']['threads']},{dom['variant']['vecs']},"

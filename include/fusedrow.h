@@ -226,6 +226,28 @@ FR_API fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labe
                                   const fr_xent_options_t* options, void* workspace,
                                   int64_t workspace_bytes, void* stream);
 
+/* ---- the online softmax inside attention ---- */
+
+/* Scaled dot-product attention forward (the online normaliser fused into
+ * attention, "Engineering a CUDA Machine Learning Framework from Scratch",
+ * §3.1), on the bf16 matrix cores:
+ *   s_ij = scale * q_i . k_j over the keys visible to query i (all, or
+ *   j <= i + seq_k - seq_q when causal: queries aligned to the end of the
+ *   keys), lse_i = ln sum_j exp(s_ij), o_i = sum_j exp(s_ij - lse_i) v_j.
+ * No score or probability is written to memory. A query with no visible key
+ * gets o = 0 and lse = -inf.
+ * q, o [batch, heads, seq_q, head_dim]; k, v [batch, heads, seq_k, head_dim];
+ * bf16 (FR_BF16 only), row-major, each pointer 16-byte aligned; lse
+ * [batch, heads, seq_q] fp32 or NULL. head_dim 64 or 128; batch * heads
+ * <= 65535. o may equal q; any other overlap with an output is FR_E_ALIAS.
+ * Arithmetic: fp32 accumulation; probabilities enter the value product
+ * rounded to bf16; o rounded to bf16 once. scale must be finite (commonly
+ * 1/sqrt(head_dim)). */
+FR_API fr_status_t fr_attention_fwd(const void* q, const void* k, const void* v, void* o,
+                             float* lse, int64_t batch, int64_t heads, int64_t seq_q,
+                             int64_t seq_k, int64_t head_dim, int causal, float scale,
+                             fr_dtype_t dtype, void* stream);
+
 /* ---- backward of the row operations ---- */
 
 /* Widest row of the backward entry points (their working set per element is

@@ -22,7 +22,7 @@ __all__ = [
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
     "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
-    "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS",
+    "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS", "fr_attention_fwd", "attention",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
     "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
@@ -85,6 +85,7 @@ def _load() -> ctypes.CDLL:
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
         "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
         "fr_softmax_fwd_split": [P, P, I64, I64, I32, I32, P, I64, P],
+        "fr_attention_fwd": [P, P, P, P, P, I64, I64, I64, I64, I64, I32, F, I32, P],
         "fr_softmax_xent_split": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P,
                                   I64, P],
         "fr_add_rmsnorm_bwd": [P, P, P, P, P, P, P, I64, I64, I64, F, I32, P],
@@ -314,6 +315,28 @@ def _split_workspace(R, C, device):
     return torch.empty(max(fr_split_workspace_bytes(R, C), 16), dtype=torch.uint8, device=device)
 
 
+def fr_attention_fwd(q, k, v, o, lse=None, causal: bool = False, scale=None, stream=None) -> None:
+    """Attention forward with the online softmax fused in (C: fr_attention_fwd).
+    q, o [B, H, Sq, D], k, v [B, H, Sk, D] bf16; lse [B, H, Sq] fp32 or None."""
+    torch = _torch()
+    _need_cuda(q, k, v, o, lse)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be a contiguous 4-D bfloat16 tensor")
+    B, H, Sq, D = (int(x) for x in q.shape)
+    Sk = int(k.shape[2])
+    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D) or \
+            tuple(o.shape) != (B, H, Sq, D):
+        raise ValueError("shapes: q, o [B, H, Sq, D]; k, v [B, H, Sk, D]")
+    if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    sc = (1.0 / D ** 0.5) if scale is None else float(scale)
+    _check(lib.fr_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, D,
+                                int(bool(causal)), sc, BF16, _stream(stream, q)),
+           "fr_attention_fwd")
+
+
 def _check_like(t, ref, name):
     if t is not None and (tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous()
                           or t.dtype != ref.dtype):
@@ -526,3 +549,12 @@ def layernorm_bwd(x, dy, gamma, mean, rstd):
     ws = _workspace(OP_LAYERNORM_BWD, R, C, x.device)
     fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dg, db, ws)
     return dx, dg, db
+
+
+def attention(q, k, v, causal: bool = False, scale=None, return_lse: bool = False):
+    """Returns o (and lse) of scaled dot-product attention (bf16)."""
+    torch = _torch()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    fr_attention_fwd(q, k, v, o, lse, causal, scale)
+    return (o, lse) if return_lse else o

@@ -593,6 +593,37 @@ fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, flo
   return launch_status(fr::launch_xent_total(loss, rows, count, loss_total, st));
 }
 
+fr_status_t fr_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                             int64_t head_dim, int causal, float scale, fr_dtype_t dtype,
+                             void* stream) {
+  if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0) return FR_E_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return FR_E_SHAPE;
+  if (seq_q > INT32_MAX / 2 || seq_k > INT32_MAX / 2) return FR_E_SHAPE;
+  const int64_t bh = batch * heads;
+  if (heads > 0 && batch > INT64_MAX / heads) return FR_E_SHAPE;
+  if (bh > 65535) return FR_E_SHAPE;
+  if (dtype != FR_BF16) return FR_E_DTYPE;
+  if (!std::isfinite(scale)) return FR_E_VALUE;
+  if (bh == 0 || seq_q == 0) return FR_OK;
+  if (!q || !o || (seq_k > 0 && (!k || !v))) return FR_E_NULL;
+  if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)) ||
+      (lse && !aligned(lse, 4)))
+    return FR_E_ALIGN;
+  const int64_t qbytes = bh * seq_q * head_dim * 2, kbytes = bh * seq_k * head_dim * 2;
+  // o may be exactly q (each workgroup reads its own queries before writing
+  // them); it may not overlap k or v, which every workgroup of a head reads
+  const Buf bufs[] = {make_buf(q, qbytes, true, 2, false),
+                      make_buf(seq_k > 0 ? k : nullptr, kbytes, false, 2, false),
+                      make_buf(seq_k > 0 ? v : nullptr, kbytes, false, 2, false),
+                      make_buf(o, qbytes, true, 2, true),
+                      make_buf(lse, bh * seq_q * 4, false, 4, true)};
+  if (fr_status_t s = check_alias(bufs, 5)) return s;
+  return launch_status(fr::launch_attention_fwd(q, k, v, o, lse, bh, (int)seq_q, (int)seq_k,
+                                                (int)head_dim, causal ? 1 : 0, scale,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (bytes < 0) return FR_E_SHAPE;
   if (bytes == 0) return FR_OK;

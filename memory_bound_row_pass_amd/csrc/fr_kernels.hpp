@@ -115,6 +115,11 @@ hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, f
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
+// Attention forward, bf16, head dim D in {64, 128}; BH = batch * heads.
+hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t BH, int Sq, int Sk, int D, int causal, float scale,
+                                hipStream_t s);
+
 // Launch `kernel` and return the status of this launch alone (not an error
 // left behind by an earlier runtime call, as hipGetLastError would).
 // Arguments must have exactly the kernel's parameter types.

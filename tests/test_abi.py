@@ -218,6 +218,24 @@ def test_split_validation():
         fr.fr_split_workspace_bytes(4, 0)
 
 
+def test_attention_validation():
+    f = fr.lib.fr_attention_fwd
+    K, V, O, LSE = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
+
+    def call(q=A, k=K, v=V, o=O, lse=LSE, b=1, h=2, sq=16, sk=16, d=64, causal=0, scale=0.125, dt=1):
+        return f(P(q), P(k), P(v), P(o), P(lse), b, h, sq, sk, d, causal, scale, dt, None)
+
+    assert call(sq=0) == OK
+    assert call(d=96) == E_SHAPE
+    assert call(b=70000) == E_SHAPE                      # batch * heads > 65535
+    assert call(dt=0) == E_DTYPE                         # bf16 only
+    assert call(scale=float("nan")) == E_VALUE
+    assert call(k=0) == E_NULL
+    assert call(o=O + 8) == E_ALIGN                      # 16-byte alignment
+    assert call(o=K) == E_ALIAS                          # output over the keys
+    assert call(lse=A + 64) == E_ALIAS                   # lse inside q
+
+
 def test_stream_copy_validation():
     f = fr.lib.fr_stream_copy
     assert f(P(A), P(B), 0, None) == OK

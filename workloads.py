@@ -38,6 +38,11 @@ forward kernels):
                       N(0, 1) draws) [8192, 8192]; w ~ U(0.8, 1.2) [8192];
                       dy, dres ~ N(0, 1); eps 1e-6                     seed 1008
 
+Attention (the online softmax inside attention):
+
+  attention_bf16      q, k, v ~ N(0, 1) bf16 [B=4, H=16, S=4096, D=128],
+                      scale 1/sqrt(128); rows = B*H*S, cols = D        seed 1009
+
 ``make(name, rows=None, cols=None)`` builds a workload with the standard
 distributions at any shape (used for edge-shape and small parity cases); the
 seed stays the workload's own unless ``seed`` is given.
@@ -85,6 +90,8 @@ WORKLOADS = {
                               eps=1e-5,
                               desc="fp32 LayerNorm backward, 4096 x 1024, x ~ N(3, 2^2), "
                                    "gamma ~ U(0.5,1.5), dy ~ N(0,1)"),
+    "attention_bf16": Spec("attention_bf16", "attention", 4 * 16 * 4096, 128, 1009, "bf16",
+                           desc="bf16 attention forward, B=4 H=16 S=4096 D=128, q,k,v ~ N(0,1)"),
     "add_rmsnorm_bwd_bf16": Spec("add_rmsnorm_bwd_bf16", "add_rmsnorm_bwd", 8192, 8192, 1008,
                                  "bf16", eps=1e-6,
                                  desc="bf16 residual-add + RMSNorm backward, 8192 x 8192, "
@@ -185,6 +192,19 @@ def make(name: str, rows: int | None = None, cols: int | None = None,
         arr["weight"] = _store(rng.uniform(0.8, 1.2, size=C), dt)
         arr["dy"] = _store(rng.normal(0.0, 1.0, size=(R, C)), dt)
         arr["dres"] = _store(rng.normal(0.0, 1.0, size=(R, C)), dt)
+    elif name == "attention_bf16":
+        raise KeyError("attention_bf16: use make_attention(B, H, Sq, Sk, D)")
     else:
         raise KeyError(name)
     return Workload(spec=spec, rows=R, cols=C, seed=s, arrays=arr)
+
+
+def make_attention(B=4, H=16, Sq=4096, Sk=None, D=128, seed=1009, dtype="bf16") -> Workload:
+    """q [B, H, Sq, D], k and v [B, H, Sk, D] (Sk defaults to Sq), N(0, 1)."""
+    Sk = Sq if Sk is None else Sk
+    rng = np.random.Generator(np.random.PCG64(seed))
+    arr = {"q": _store(rng.normal(0.0, 1.0, size=(B, H, Sq, D)), dtype),
+           "k": _store(rng.normal(0.0, 1.0, size=(B, H, Sk, D)), dtype),
+           "v": _store(rng.normal(0.0, 1.0, size=(B, H, Sk, D)), dtype)}
+    return Workload(spec=WORKLOADS["attention_bf16"], rows=B * H * Sq, cols=D, seed=seed,
+                    arrays=arr)

@@ -602,7 +602,7 @@ fr_status_t fr_attention_fwd(const void* q, const void* k, const void* v, void* 
   if (seq_q > INT32_MAX / 2 || seq_k > INT32_MAX / 2) return FR_E_SHAPE;
   const int64_t bh = batch * heads;
   if (heads > 0 && batch > INT64_MAX / heads) return FR_E_SHAPE;
-  if (bh > 65535) return FR_E_SHAPE;
+  if (bh > 65535 || bh * ((seq_q + 127) / 128) > INT32_MAX) return FR_E_SHAPE;
   if (dtype != FR_BF16) return FR_E_DTYPE;
   if (!std::isfinite(scale)) return FR_E_VALUE;
   if (bh == 0 || seq_q == 0) return FR_OK;

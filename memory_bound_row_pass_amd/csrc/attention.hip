@@ -8,7 +8,8 @@
 // matrix is written to memory.
 //
 // Workgroup: 4 waves, 128 queries (32 per wave) of one (batch, head); key
-// blocks of 32. Per key block, per wave:
+// blocks of BN (32 or 64, one or two 32-key score tiles). Per key block, per
+// wave:
 //   S^T (32 keys x 32 queries) = K_blk (A operand, from LDS) * Q^T (B operand,
 //     the wave's queries held in registers for the whole kernel);
 //   in the MFMA C layout lane l owns query l % 32 and 16 of the 32 keys (the
@@ -20,8 +21,15 @@
 //     layout gives lane half h the keys {h*4 + 0..3, 8 + h*4 + 0..3} of each
 //     16-key group, so the V^T operand is read with the same key order — the
 //     contraction over keys does not depend on their order.
-// Scores are kept in base 2 (scale * log2(e) folded in); the next key block's
-// K and V are loaded into registers while the current one is computed.
+// Scores are kept in base 2 (scale * log2(e) folded into the exponential's
+// fma); the next key block's K and V are loaded into registers while the
+// current one is computed. The running max is raised lazily: only when a
+// query's block max exceeds it by more than kLazy (base-2 units) is it
+// updated and the output accumulator rescaled — otherwise the probabilities
+// are taken against the stale max (at most 2^kLazy, exact in fp32 and bf16
+// range), which keeps the D/2 accumulator multiplies off most key blocks.
+// Masks are applied only on the key blocks that reach the causal diagonal or
+// the end of the keys. Causal query blocks are launched longest first.
 #include "fr_kernels.hpp"
 #include "fr_device.hpp"
 
@@ -31,23 +39,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAttnBlockM = 128;  // queries per workgroup (4 waves x 32)
-constexpr int kAttnBlockN = 32;   // keys per block
+constexpr float kLazy = 8.f;      // stale-max allowance, base-2 units
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int D>
+template <int D, int BN>
 __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, const bf16_t* k,
                                                             const bf16_t* v, bf16_t* o, float* lse,
-                                                            int Sq, int Sk, int causal,
+                                                            int64_t BH, int Sq, int Sk, int causal,
                                                             float scale_log2) {
+  constexpr int NT = BN / 32;               // 32-key score tiles per block
   constexpr int KP = D + 8;                 // K tile row stride (bf16), padded
-  constexpr int VP = kAttnBlockN + 8;       // V^T tile row stride (bf16), padded
+  // V^T tile row stride (bf16): BN + 4 (== 4 mod 8) spreads the transposing
+  // writes of 8 d-rows over both halves of the LDS banks and keeps the 8-byte
+  // operand reads of 16 consecutive rows on distinct banks
+  constexpr int VP = BN + 4;
   constexpr int NKK = D / 16;               // k-steps of the score product
   constexpr int NDB = D / 32;               // 32-row blocks of O^T
-  constexpr int CH = kAttnBlockN * D / 8;   // 16-byte chunks per K (or V) tile
+  constexpr int CH = BN * D / 8;            // 16-byte chunks per K (or V) tile
   constexpr int CPT = CH / 256;             // chunks per thread
   static_assert(CPT >= 1 && CH % 256 == 0, "tile");
-  __shared__ __attribute__((aligned(16))) bf16_t ks[kAttnBlockN * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t ks[BN * KP];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VP];
 
   const int tid = threadIdx.x;
@@ -55,8 +67,14 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
   const int lane = tid & 63;
   const int h = lane >> 5;      // lane half
   const int lq = lane & 31;     // the lane's query within the wave / row in A operands
-  const int64_t bh = blockIdx.y;
-  const int q0 = blockIdx.x * kAttnBlockM + wave * 32;
+  // 1-D grid, (batch, head) fastest: consecutive workgroups (dealt to
+  // different XCDs) take different heads of the same query block, so every
+  // XCD gets every query block; causal: the last query blocks (most keys) first
+  const int nqb = (Sq + kAttnBlockM - 1) / kAttnBlockM;
+  const int64_t bh = (int64_t)blockIdx.x % BH;
+  const int qidx = (int)((int64_t)blockIdx.x / BH);
+  const int qblk = causal ? nqb - 1 - qidx : qidx;
+  const int q0 = qblk * kAttnBlockM + wave * 32;
   const int qi = q0 + lq;       // this lane's query
   const bf16_t* qb = q + bh * (int64_t)Sq * D;
   const bf16_t* kb = k + bh * (int64_t)Sk * D;
@@ -79,16 +97,34 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
   float m_run = kNegInf, l_run = 0.f;
 
   // keys visible to the workgroup's last query
-  const int q_last = blockIdx.x * kAttnBlockM + kAttnBlockM - 1;
+  const int q_first = qblk * kAttnBlockM;
+  const int q_last = q_first + kAttnBlockM - 1;
   int kend = Sk;
   if (causal) {
     const int lim = q_last + (Sk - Sq) + 1;
     kend = lim < kend ? lim : kend;
   }
-  const int nblk = kend > 0 ? (kend + kAttnBlockN - 1) / kAttnBlockN : 0;
+  const int nblk = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  // tile loads: chunk c of a tile = key c / (D/8), d0 = (c % (D/8)) * 8
+  // tile loads. K: chunk c = key c / (D/8), d0 = (c % (D/8)) * 8 (row order).
+  // V: when each thread has an even number of chunks, chunk pair p holds keys
+  // 2m, 2m+1 (m = p % (BN/2)) at d0 = (p / (BN/2)) * 8, so the transposed
+  // write packs the two keys of each d into one dword (consecutive lanes,
+  // consecutive dwords); otherwise chunk c = key c % BN, d0 = (c / BN) * 8.
+  constexpr bool PAIRS = CPT % 2 == 0;
   u32x4 kreg[CPT], vreg[CPT];
+  auto vkey = [&](int i) {
+    if constexpr (PAIRS) {
+      const int pr = tid + 256 * (i >> 1);
+      return 2 * (pr % (BN / 2)) + (i & 1);
+    } else {
+      return (tid + 256 * i) % BN;
+    }
+  };
+  auto vd0 = [&](int i) {
+    if constexpr (PAIRS) return ((tid + 256 * (i >> 1)) / (BN / 2)) * 8;
+    else return ((tid + 256 * i) / BN) * 8;
+  };
   auto load_tile = [&](int n0) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -97,88 +133,160 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
       const int d0 = (c % (D / 8)) * 8;
       const int kr = key < Sk ? key : Sk - 1;
       u32x4 a = *reinterpret_cast<const u32x4*>(kb + (int64_t)kr * D + d0);
-      u32x4 b = *reinterpret_cast<const u32x4*>(vb + (int64_t)kr * D + d0);
       kreg[i] = key < Sk ? a : u32x4{0, 0, 0, 0};
-      vreg[i] = key < Sk ? b : u32x4{0, 0, 0, 0};
+      const int vk = n0 + vkey(i);
+      const int vr = vk < Sk ? vk : Sk - 1;
+      u32x4 b = *reinterpret_cast<const u32x4*>(vb + (int64_t)vr * D + vd0(i));
+      vreg[i] = vk < Sk ? b : u32x4{0, 0, 0, 0};
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
-      const int key = c / (D / 8);
-      const int d0 = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(ks + key * KP + d0) = kreg[i];
-      const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+      *reinterpret_cast<u32x4*>(ks + (c / (D / 8)) * KP + (c % (D / 8)) * 8) = kreg[i];
+    }
+    if constexpr (PAIRS) {
+      uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vt[(d0 + 2 * j) * VP + key].u = (uint16_t)(w[j] & 0xffffu);
-        vt[(d0 + 2 * j + 1) * VP + key].u = (uint16_t)(w[j] >> 16);
+      for (int i = 0; i < CPT; i += 2) {
+        const int m = vkey(i) >> 1;
+        const int d0 = vd0(i);
+        const uint32_t a[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+        const uint32_t b[4] = {vreg[i + 1].x, vreg[i + 1].y, vreg[i + 1].z, vreg[i + 1].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vt32[((d0 + 2 * j) * VP) / 2 + m] = (a[j] & 0xffffu) | (b[j] << 16);
+          vt32[((d0 + 2 * j + 1) * VP) / 2 + m] = (a[j] >> 16) | (b[j] & 0xffff0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int key = vkey(i);
+        const int d0 = vd0(i);
+        const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vt[(d0 + 2 * j) * VP + key].u = (uint16_t)(w[j] & 0xffffu);
+          vt[(d0 + 2 * j + 1) * VP + key].u = (uint16_t)(w[j] >> 16);
+        }
       }
     }
   };
 
   if (nblk > 0) load_tile(0);
   for (int blk = 0; blk < nblk; ++blk) {
-    const int n0 = blk * kAttnBlockN;
+    const int n0 = blk * BN;
     __syncthreads();  // previous block's tiles fully read
     store_tile();
     __syncthreads();
-    if (blk + 1 < nblk) load_tile(n0 + kAttnBlockN);  // in flight during the compute
+    if (blk + 1 < nblk) load_tile(n0 + BN);  // in flight during the compute
 
-    // S^T = K_blk * Q^T
-    f32x16 s = f32x16{};
+    // S^T = K_blk * Q^T, one independent accumulator per 32-key tile
+    f32x16 s[NT];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(ks + lq * KP + 16 * kk + 8 * h);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[kk]), s, 0, 0, 0);
-    }
+    for (int t = 0; t < NT; ++t) s[t] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + (32 * t + lq) * KP + 16 * kk + 8 * h);
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[kk]), s[t], 0, 0,
+                                                       0);
+      }
 
-    // online softmax for query qi over keys n0 + key(j), key(j) = (j/4)*8 + 4h + j%4
+    // online softmax for query qi over keys n0 + 32t + key(j),
+    // key(j) = (j/4)*8 + 4h + j%4; t = scale_log2 * s (base-2 units)
+    const bool need_mask =
+        n0 + BN > Sk || (causal && n0 + BN - 1 > q_first + (Sk - Sq));
     const int klim = causal ? qi + (Sk - Sq) : Sk - 1;  // last visible key
-    float mloc = kNegInf;
+    if (need_mask) {  // uniform; hidden scores take the identity of the max (or min)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = n0 + (j >> 2) * 8 + 4 * h + (j & 3);
-      const float sv = (key < Sk && key <= klim) ? s[j] * scale_log2 : kNegInf;
-      s[j] = sv;
-      mloc = sv > mloc ? sv : mloc;
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = n0 + 32 * t + (j >> 2) * 8 + 4 * h + (j & 3);
+          s[t][j] = (key < Sk && key <= klim) ? s[t][j] : (scale_log2 >= 0.f ? kNegInf : -kNegInf);
+        }
     }
-    const float mpart = __shfl_xor(mloc, 32);
-    float m_new = m_run > mloc ? m_run : mloc;
-    m_new = m_new > mpart ? m_new : mpart;
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2_hw(m_run - m_use);  // 0 while nothing was visible
+    // block max of t: the max of s for scale >= 0, else the min
+    float smax;
+    if (scale_log2 >= 0.f) {
+      smax = kNegInf;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) smax = max3(smax, s[t][j], s[t][j + 1]);
+    } else {
+      smax = -kNegInf;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) smax = s[t][j] < smax ? s[t][j] : smax;
+    }
+    float tmax = smax * scale_log2;
+    tmax = tmax != tmax ? kNegInf : tmax;  // a masked -inf * 0 scale
+    const float tpart = __shfl_xor(tmax, 32);
+    tmax = tmax > tpart ? tmax : tpart;
+    // raise the running max only past the allowance (wave-uniform decision)
+    const bool raise = tmax > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = tmax > m_run ? tmax : m_run;
+      const float alpha = m_run == kNegInf ? 0.f : exp2_hw(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) acc[b] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[t][j] = exp2_hw(__builtin_fmaf(s[t][j], scale_log2, -m_use));
+    if (need_mask) {  // hidden keys contribute exactly 0 (also when scale is 0)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = n0 + 32 * t + (j >> 2) * 8 + 4 * h + (j & 3);
+          s[t][j] = (key < Sk && key <= klim) ? s[t][j] : 0.f;
+        }
+    }
     float lsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[j] = exp2_hw(s[j] - m_use);
-      lsum += s[j];
-    }
-    lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int b = 0; b < NDB; ++b) acc[b] *= alpha;
+      for (int j = 0; j < 16; ++j) lsum += s[t][j];
+    lsum += __shfl_xor(lsum, 32);
+    l_run += lsum;
 
-    // P^T as B operands: k-step 0 = the lane's j 0..7, k-step 1 = j 8..15
-    const u32x4 p0 = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
-                      pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
-    const u32x4 p1 = {pack_bf16x2(s[8], s[9]), pack_bf16x2(s[10], s[11]),
-                      pack_bf16x2(s[12], s[13]), pack_bf16x2(s[14], s[15])};
+    // P^T as B operands: tile t, k-step 0 = the lane's j 0..7, k-step 1 = j 8..15
+    u32x4 pb[2 * NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      pb[2 * t] = {pack_bf16x2(s[t][0], s[t][1]), pack_bf16x2(s[t][2], s[t][3]),
+                   pack_bf16x2(s[t][4], s[t][5]), pack_bf16x2(s[t][6], s[t][7])};
+      pb[2 * t + 1] = {pack_bf16x2(s[t][8], s[t][9]), pack_bf16x2(s[t][10], s[t][11]),
+                       pack_bf16x2(s[t][12], s[t][13]), pack_bf16x2(s[t][14], s[t][15])};
+    }
 
     // O^T += V^T * P^T; V^T operand rows d = 32b + lq, keys in the C-layout order
 #pragma unroll
     for (int b = 0; b < NDB; ++b) {
       const bf16_t* row = vt + (32 * b + lq) * VP + 4 * h;
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(row);        // keys 4h + 0..3
-      const u32x2 a1 = *reinterpret_cast<const u32x2*>(row + 8);    // keys 8 + 4h + 0..3
-      const u32x2 a2 = *reinterpret_cast<const u32x2*>(row + 16);   // keys 16 + 4h + 0..3
-      const u32x2 a3 = *reinterpret_cast<const u32x2*>(row + 24);   // keys 24 + 4h + 0..3
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{a0.x, a0.y, a1.x, a1.y}),
-                                                       as_bf16x8(p0), acc[b], 0, 0, 0);
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{a2.x, a2.y, a3.x, a3.y}),
-                                                       as_bf16x8(p1), acc[b], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16_t* r = row + 32 * t;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(r);        // keys 4h + 0..3
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(r + 8);    // keys 8 + 4h + 0..3
+        const u32x2 a2 = *reinterpret_cast<const u32x2*>(r + 16);   // keys 16 + 4h + 0..3
+        const u32x2 a3 = *reinterpret_cast<const u32x2*>(r + 24);   // keys 24 + 4h + 0..3
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{a0.x, a0.y, a1.x, a1.y}),
+                                                         as_bf16x8(pb[2 * t]), acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{a2.x, a2.y, a3.x, a3.y}),
+                                                         as_bf16x8(pb[2 * t + 1]), acc[b], 0, 0, 0);
+      }
     }
   }
 
@@ -199,20 +307,25 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
   }
 }
 
+#ifndef FR_ATTN_BN
+#define FR_ATTN_BN 32
+#endif
+
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int64_t BH, int Sq, int Sk, int D, int causal, float scale,
                                 hipStream_t s) {
-  const dim3 grid((unsigned)((Sq + kAttnBlockM - 1) / kAttnBlockM), (unsigned)BH);
+  const int64_t nqb = (Sq + kAttnBlockM - 1) / kAttnBlockM;
+  const dim3 grid((unsigned)(nqb * BH));
   const float sl2 = scale * kLog2e;
   const bf16_t* qp = static_cast<const bf16_t*>(q);
   const bf16_t* kp = static_cast<const bf16_t*>(k);
   const bf16_t* vp = static_cast<const bf16_t*>(v);
   bf16_t* op = static_cast<bf16_t*>(o);
   if (D == 64)
-    return launch_kernel(&attention_fwd_kernel<64>, grid, dim3(256), s, qp, kp, vp, op, lse, Sq, Sk,
-                         causal, sl2);
-  return launch_kernel(&attention_fwd_kernel<128>, grid, dim3(256), s, qp, kp, vp, op, lse, Sq, Sk,
-                       causal, sl2);
+    return launch_kernel(&attention_fwd_kernel<64, FR_ATTN_BN>, grid, dim3(256), s, qp, kp, vp, op,
+                         lse, BH, Sq, Sk, causal, sl2);
+  return launch_kernel(&attention_fwd_kernel<128, FR_ATTN_BN>, grid, dim3(256), s, qp, kp, vp, op,
+                       lse, BH, Sq, Sk, causal, sl2);
 }
 
 }  // namespace fr

@@ -256,12 +256,24 @@ struct RowGeom {
 // then overwritten with `fill`; stores of such slots are masked off. A single
 // code path keeps the register allocation tight (rows that fill every slot
 // simply never mask).
+//
+// The lane offset is re-formed in every call from an opaque zero: otherwise
+// the compiler hoists the NV per-slot offsets out of a row loop, and when
+// they do not fit in registers it spills them and reloads each one right
+// before its load; a scratch reload waits on the same counter as the row's
+// loads, which then issue one at a time.
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z = 0;
+  asm volatile("" : "+s"(z));
+  return z;
+}
+
 template <typename Ts, int T, int NV, int EPV, int AL>
 __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                             float (&v)[NV][EPV], float fill) {
   if (g.nvec > 0) {
     const Ts* base = row + g.head;                  // uniform
-    const uint32_t lo = (uint32_t)tid * EPV;        // lane offset, elements
+    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();  // lane offset, elements
     const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -328,7 +340,7 @@ template <typename Ts, int T, int NV, int EPV, int AL>
 __device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                              const float (&v)[NV][EPV]) {
   Ts* base = row + g.head;
-  const uint32_t lo = (uint32_t)tid * EPV;
+  const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (i * T + tid < g.nvec) Vec<Ts, EPV>::store(base + ((uint32_t)(i * T * EPV) + lo), v[i]);

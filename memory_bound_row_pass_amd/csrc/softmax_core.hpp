@@ -47,7 +47,9 @@ __device__ __forceinline__ float lane_max(const float (&v)[NV][EPV], float xe) {
 // bf16 (p >= 2^-134). Forming x_j - m_l first keeps the argument finite for
 // any finite input (m_l*log2e alone overflows for |m_l| > 2.3e38). The lane
 // state (m_l, s_l) stays in natural units.
-template <int NV, int EPV>
+// (BIAS: the exponent offset, 64 by default; S carries the same factor, so
+// it cancels in p_j.)
+template <int NV, int EPV, int BIAS = 64>
 __device__ __forceinline__ MaxSumState lane_exp_log2(float (&v)[NV][EPV], float& xe, float m) {
   const float mr = (m == kNegInf) ? 0.f : m;
   float s0 = 0.f, s1 = 0.f;
@@ -55,10 +57,10 @@ __device__ __forceinline__ MaxSumState lane_exp_log2(float (&v)[NV][EPV], float&
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int k = 0; k < EPV; ++k) {
-      v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, 64.f));
+      v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, (float)BIAS));
       if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
     }
-  xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, 64.f));
+  xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, (float)BIAS));
   return {m, (s0 + s1) + xe};
 }
 

@@ -3,8 +3,9 @@
 // gradients fused into registers; "GPU Programming for Machine Learning",
 // Module 3: cross-entropy loss).
 //
-// Per row: the online-softmax state (M, S) of the logits (as in softmax.hip,
-// fp32 path, exponentials kept in registers), then
+// Per row: the online-softmax state (M, S) of the logits (as in softmax.hip:
+// exponentials kept in registers, natural units for fp32 logits, biased
+// base 2 for bf16 logits), then
 //   loss    = M + ln S - x[label]
 //   grad_j  = exp(x_j - M) / S - [j == label]
 //   argmax  = smallest j with x_j == M (optional)
@@ -56,6 +57,15 @@ __device__ __forceinline__ int owner_lane(int c, const RowGeom<EPV>& g) {
   return ((c - g.head) / EPV) % T;
 }
 
+// Exponentials and scaling: bf16 logits (bf16 gradient) take the biased
+// base-2 form of the bf16 softmax, so gradients in the bf16 subnormal range
+// are exact; fp32 logits take the natural form with the compensated
+// exponential. The bias here is 2^8, the least that keeps every e_j normal
+// down to p = 2^-134 (p <= 2^y with y = (x_j - m_l) log2e): a smaller bias
+// keeps more bits of y + bias, so the row sum, and with it the loss, stays
+// accurate to ~3e-7 relative (2^64 would leave ~2.6e-6).
+constexpr int kXentBias = 8;
+
 template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT>
 __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
 void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, int32_t* argmax,
@@ -63,8 +73,9 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
   constexpr int BLOCK = T == 64 ? 256 : T;
   constexpr int RPB = BLOCK / T;
   constexpr int NW = T / 64;
+  constexpr bool LOG2 = sizeof(Tin) == 2;
   using Base = typename std::conditional<ARGMAX, MaxSumIdxState, MaxSumState>::type;
-  using BaseMerge = typename std::conditional<ARGMAX, MaxSumIdxMerge, MaxSumMerge<false>>::type;
+  using BaseMerge = typename std::conditional<ARGMAX, MaxSumIdxMerge, MaxSumMerge<LOG2>>::type;
   using State = typename std::conditional<OPT, PlusSum<Base>, Base>::type;
   using Merge = typename std::conditional<OPT, PlusSumMerge<Base, BaseMerge>, BaseMerge>::type;
   constexpr int NF = sizeof(State) / sizeof(float);
@@ -84,15 +95,23 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     goff = gsc * (opt.smoothing / (float)cols);
   }
 
+  // The next row's label is read one row ahead, so that the scalar load's
+  // latency is not paid between rows (the ignore test needs the label before
+  // the row's loads are issued).
+  const int64_t stride = (int64_t)gridDim.x * RPB;
+  const int64_t first = (int64_t)blockIdx.x * RPB + sub;
+  int label_next = first < rows ? __builtin_amdgcn_readfirstlane(labels[first]) : 0;
+
   int it = 0;
-  for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
-       row += (int64_t)gridDim.x * RPB, ++it) {
+  for (int64_t row = first; row < rows; row += stride, ++it) {
     const Tin* xr = x + row * cols;
     Tin* gr = grad + row * cols;
     const RowGeom<EPV> g(xr, cols);
     const int ec = g.extra_col(tid);
+    const int64_t rn = row + stride;
 
-    const int label = __builtin_amdgcn_readfirstlane(labels[row]);
+    const int label = label_next;
+    if (rn < rows) label_next = __builtin_amdgcn_readfirstlane(labels[rn]);
     const bool ignored = OPT && opt.use_ignore && label == opt.ignore_index;
     if constexpr (OPT && !ARGMAX) {
       if (ignored) {  // uniform in the row owner: no loads, a zero row
@@ -108,16 +127,15 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
       }
     }
 
-    float v[NV][EPV];
-    load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
-    float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
-
     // The label column is handled by the one lane that owns it (the lane of
     // the row owner that loads that column). It reads the label logit with
     // its own load, before any of its stores: in-place calls (grad == logits)
     // stay correct because a lane's accesses to one address keep their order.
     const bool valid = label >= 0 && label < cols;
     const bool label_lane = valid && !ignored && owner_lane<T, EPV>(label, g) == tid;
+    float v[NV][EPV];
+    load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+    float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
     float x_label = 0.f;
     if (label_lane) x_label = load1(xr + label);
 
@@ -153,7 +171,9 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
       bs.idx = best;
     }
     {
-      const MaxSumState ms = lane_exp_nat<NV, EPV>(v, xe, m);  // e_j replaces x_j
+      // e_j replaces x_j
+      const MaxSumState ms = LOG2 ? lane_exp_log2<NV, EPV, kXentBias>(v, xe, m)
+                                  : lane_exp_nat<NV, EPV>(v, xe, m);
       bs.m = ms.m;
       bs.s = ms.s;
     }
@@ -169,22 +189,30 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     } else {
       rs = st;
     }
+    // the row sum in natural units (the base-2 form carries the 2^kXentBias bias)
+    const float s_row = LOG2 ? __builtin_ldexpf(rs.s, -kXentBias) : rs.s;
 
-    if constexpr (OPT) {
-      if (ignored) {  // (argmax wanted) zero row, loss 0
+    if (OPT && ignored) {  // (argmax wanted) zero row, loss 0
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
+      for (int i = 0; i < NV; ++i)
 #pragma unroll
-          for (int k = 0; k < EPV; ++k) v[i][k] = 0.f;
-        xe = 0.f;
-      } else {
-        const float f = nat_scale(m, rs.m, rs.s) * gsc;
+        for (int k = 0; k < EPV; ++k) v[i][k] = 0.f;
+      xe = 0.f;
+    } else if constexpr (LOG2) {
+      Log2Scale sc = log2_scale(m, rs.m, rs.s);
+      sc.g *= gsc;
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
+      for (int i = 0; i < NV; ++i)
 #pragma unroll
-          for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf(v[i][k], f, -goff);
-        xe = __builtin_fmaf(xe, f, -goff);
-      }
+        for (int k = 0; k < EPV; ++k) v[i][k] = apply_scale(v[i][k], sc) - goff;
+      xe = apply_scale(xe, sc) - goff;
+    } else if constexpr (OPT) {
+      const float f = nat_scale(m, rs.m, rs.s) * gsc;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf(v[i][k], f, -goff);
+      xe = __builtin_fmaf(xe, f, -goff);
     } else {
       const float f = nat_scale(m, rs.m, rs.s);
 #pragma unroll
@@ -199,8 +227,8 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     if (label_lane) {
       // overwrite the label element (after this lane's own store of it to
       // the same address), and write the loss
-      const float p = exp_acc(x_label - rs.m) / rs.s;
-      const float lse = rs.m + logf(rs.s);
+      const float p = exp_acc(x_label - rs.m) / s_row;
+      const float lse = rs.m + logf(s_row);
       if constexpr (OPT) {
         // terms with a zero weight are left out (a -inf logit would make
         // them 0 * inf); the same reading as the definition's weighted sum

@@ -391,6 +391,38 @@ def test_special_values_softmax():
         assert np.all(gotf[0, ::3] == 0.0)
 
 
+FAR_DELTAS = [20.0, 31.0, 33.0, 40.0, 50.0, 60.0, 70.0, 75.0, 80.0, 86.0, 88.0, 90.0, 92.0]
+
+
+def far_rows(R, C, code, seed):
+    """Rows N(0, 2^2) with a maximum of 10 and single elements 10 - d for each d
+    of FAR_DELTAS (integers, exact in bf16): probabilities from e^-20 down
+    into the subnormal range, spread over head, body and tail columns."""
+    rng = np.random.default_rng(seed)
+    x = np.clip(rng.normal(0, 2, size=(R, C)), -9, 9)
+    for r in range(R):
+        x[r, (r * 7919) % C] = 10.0
+        cols = rng.choice(C, size=min(C - 1, len(FAR_DELTAS)), replace=False)
+        cols = cols[cols != (r * 7919) % C]
+        for c, d in zip(cols, FAR_DELTAS):
+            x[r, c] = 10.0 - d
+    x = x.astype(np.float32)
+    if code == fr.BF16:
+        return oracle.round_bf16(x)
+    return x
+
+
+@pytest.mark.parametrize("C", [1000, 4096, 50257])
+def test_softmax_far_below_max(C):
+    # elements far below the row maximum: fp32 outputs keep 1e-5 relative
+    # (the compensated exponential where a lane's range needs it), bf16
+    # outputs reach the subnormal range exactly
+    for xin in (fr.F32, fr.BF16):
+        x = far_rows(16, C, xin, seed=C + xin)
+        for yout in (fr.F32, fr.BF16):
+            expect_softmax(x, yout, run_softmax(x, yout), f"softmax far {xin}->{yout} 16x{C}")
+
+
 def test_special_values_norms():
     # constant rows: LayerNorm gives beta exactly, rstd = 1/sqrt(eps)
     C = 1024

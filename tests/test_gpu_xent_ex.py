@@ -210,6 +210,21 @@ def test_labels_invalid_masked_logits_and_all_ignored():
     assert np.isnan(got[3]) and np.all(got[0] == 0) and np.all(got[1] == 0)
 
 
+@pytest.mark.parametrize("C", [1000, 4096, 50257])
+def test_far_below_max(C):
+    # logits far below the row maximum: fp32 gradients keep 1e-5 relative,
+    # bf16 gradients reach the bf16 subnormal range (p down to ~1e-40)
+    from test_gpu_parity import far_rows
+    for code in (fr.F32, fr.BF16):
+        x = far_rows(12, C, code, seed=C + 5 * code)
+        lab = np.random.default_rng(C).integers(0, C, size=12).astype(np.int32)
+        for opts in (dict(), dict(ignore_index=-100, reduction="sum"),
+                     dict(label_smoothing=0.1, reduction="mean")):
+            for am in (True, False):
+                expect(x, lab, code, opts, run(x, lab, code, opts, argmax=am),
+                       f"xent_ex far {code} 12x{C} {opts} argmax={am}")
+
+
 def test_rows_zero():
     e = torch.empty(0, 10, device=DEV)
     lab = torch.empty(0, dtype=torch.int32, device=DEV)

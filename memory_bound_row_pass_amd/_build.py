@@ -25,6 +25,12 @@ CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arc
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source flags. attention.hip: MFMA accumulators in VGPRs (the AGPR form
+# made the compiler copy the 64 output accumulators between register files on
+# every key block).
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     cand = os.path.join(rocm, "bin", "hipcc")
@@ -34,7 +40,8 @@ def _hipcc() -> str:
 def _compile(src: str, verbose: bool, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc(), *CXXFLAGS, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *CXXFLAGS, *EXTRA.get(src, []), *[f"-D{d}" for d in defines], *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -23,11 +23,12 @@
 //     contraction over keys does not depend on their order.
 // Scores are kept in base 2 (scale * log2(e) folded into the exponential's
 // fma); the next key block's K and V are loaded into registers while the
-// current one is computed. The running max is raised lazily: only when a
-// query's block max exceeds it by more than kLazy (base-2 units) is it
-// updated and the output accumulator rescaled — otherwise the probabilities
-// are taken against the stale max (at most 2^kLazy, exact in fp32 and bf16
-// range), which keeps the D/2 accumulator multiplies off most key blocks.
+// current one is computed, and written to the second LDS stage after it.
+// The running max is raised lazily: only when a query's block max exceeds
+// it by more than kLazy (base-2 units) is it updated and the output
+// accumulator rescaled — otherwise the probabilities are taken against the
+// stale max (at most 2^kLazy, exact in fp32 and bf16 range), which keeps the
+// D/2 accumulator multiplies off most key blocks.
 // Masks are applied only on the key blocks that reach the causal diagonal or
 // the end of the keys. Causal query blocks are launched longest first.
 #include "fr_kernels.hpp"
@@ -44,7 +45,7 @@ constexpr float kLazy = 8.f;      // stale-max allowance, base-2 units
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <int D, int BN>
-__global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, const bf16_t* k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attention_fwd_kernel(const bf16_t* q, const bf16_t* k,
                                                             const bf16_t* v, bf16_t* o, float* lse,
                                                             int64_t BH, int Sq, int Sk, int causal,
                                                             float scale_log2) {
@@ -59,8 +60,9 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
   constexpr int CH = BN * D / 8;            // 16-byte chunks per K (or V) tile
   constexpr int CPT = CH / 256;             // chunks per thread
   static_assert(CPT >= 1 && CH % 256 == 0, "tile");
-  __shared__ __attribute__((aligned(16))) bf16_t ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[D * VP];
+  // two stages: the next key block is written while the current one is read
+  __shared__ __attribute__((aligned(16))) bf16_t ks_st[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t vt_st[2][D * VP];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,7 +127,27 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
     if constexpr (PAIRS) return ((tid + 256 * (i >> 1)) / (BN / 2)) * 8;
     else return ((tid + 256 * i) / BN) * 8;
   };
+  // byte offsets of this thread's chunks from the tile's first key (lane
+  // constants): a full tile is read as uniform tile base + 32-bit offset
+  uint32_t koff[CPT], voff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    koff[i] = (uint32_t)(((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2);
+    voff[i] = (uint32_t)((vkey(i) * D + vd0(i)) * 2);
+  }
   auto load_tile = [&](int n0) {
+    if (n0 + BN <= Sk) {  // uniform: every key of the tile exists
+      const char* kt = reinterpret_cast<const char*>(kb + (int64_t)n0 * D);
+      const char* vtl = reinterpret_cast<const char*>(vb + (int64_t)n0 * D);
+      const uint32_t z = opaque_zero();  // keeps the offsets 32-bit (SGPR base + VGPR offset)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(kt + (koff[i] + z));
+        vreg[i] = *reinterpret_cast<const u32x4*>(vtl + (voff[i] + z));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
@@ -140,7 +162,9 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
       vreg[i] = vk < Sk ? b : u32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    bf16_t* ks = ks_st[stage];
+    bf16_t* vt = vt_st[stage];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
@@ -175,13 +199,20 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
     }
   };
 
-  if (nblk > 0) load_tile(0);
+  // Stage blk & 1 holds key block blk. Block blk + 1 is written to the other
+  // stage after this wave's compute of block blk: every wave has finished
+  // reading that stage (block blk - 1) before the barrier that ended the
+  // previous iteration. One barrier per key block.
+  if (nblk > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (nblk > 1) load_tile(BN);
+  }
+  __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int n0 = blk * BN;
-    __syncthreads();  // previous block's tiles fully read
-    store_tile();
-    __syncthreads();
-    if (blk + 1 < nblk) load_tile(n0 + BN);  // in flight during the compute
+    const bf16_t* ks = ks_st[blk & 1];
+    const bf16_t* vt = vt_st[blk & 1];
 
     // S^T = K_blk * Q^T, one independent accumulator per 32-key tile
     f32x16 s[NT];
@@ -288,6 +319,12 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(const bf16_t* q, con
                                                          as_bf16x8(pb[2 * t + 1]), acc[b], 0, 0, 0);
       }
     }
+
+    if (blk + 1 < nblk) {
+      store_tile((blk + 1) & 1);
+      if (blk + 2 < nblk) load_tile(n0 + 2 * BN);  // in flight during the next compute
+    }
+    __syncthreads();
   }
 
   // O = O^T / l, lane (query qi) writes d = 32b + 8g + 4h + 0..3 (8 bytes)

@@ -44,6 +44,11 @@ constexpr float kLazy = 8.f;      // stale-max allowance, base-2 units
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// LDS-address-space views for the transposing LDS read (ds_read_b64_tr_b16)
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) const bf16_t lds_bf16;
+
 template <int D, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attention_fwd_kernel(const bf16_t* q, const bf16_t* k,
                                                             const bf16_t* v, bf16_t* o, float* lse,
@@ -51,10 +56,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
                                                             float scale_log2) {
   constexpr int NT = BN / 32;               // 32-key score tiles per block
   constexpr int KP = D + 8;                 // K tile row stride (bf16), padded
-  // V^T tile row stride (bf16): BN + 4 (== 4 mod 8) spreads the transposing
-  // writes of 8 d-rows over both halves of the LDS banks and keeps the 8-byte
-  // operand reads of 16 consecutive rows on distinct banks
-  constexpr int VP = BN + 4;
+  // V tile row stride (bf16): row-major [key][d], padded by 64 bytes so that
+  // the transposing reads of 8 keys x 32 d spread over all LDS banks
+  constexpr int VS = D + 32;
   constexpr int NKK = D / 16;               // k-steps of the score product
   constexpr int NDB = D / 32;               // 32-row blocks of O^T
   constexpr int CH = BN * D / 8;            // 16-byte chunks per K (or V) tile
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   static_assert(CPT >= 1 && CH % 256 == 0, "tile");
   // two stages: the next key block is written while the current one is read
   __shared__ __attribute__((aligned(16))) bf16_t ks_st[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t vt_st[2][D * VP];
+  __shared__ __attribute__((aligned(16))) bf16_t vt_st[2][BN * VS];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -108,25 +112,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
   const int nblk = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  // tile loads. K: chunk c = key c / (D/8), d0 = (c % (D/8)) * 8 (row order).
-  // V: when each thread has an even number of chunks, chunk pair p holds keys
-  // 2m, 2m+1 (m = p % (BN/2)) at d0 = (p / (BN/2)) * 8, so the transposed
-  // write packs the two keys of each d into one dword (consecutive lanes,
-  // consecutive dwords); otherwise chunk c = key c % BN, d0 = (c / BN) * 8.
-  constexpr bool PAIRS = CPT % 2 == 0;
+  // tile loads: chunk c = tid + 256 i of a tile is key c / (D/8), d0 = (c % (D/8)) * 8
+  // (row order), for K and V alike
   u32x4 kreg[CPT], vreg[CPT];
-  auto vkey = [&](int i) {
-    if constexpr (PAIRS) {
-      const int pr = tid + 256 * (i >> 1);
-      return 2 * (pr % (BN / 2)) + (i & 1);
-    } else {
-      return (tid + 256 * i) % BN;
-    }
-  };
-  auto vd0 = [&](int i) {
-    if constexpr (PAIRS) return ((tid + 256 * (i >> 1)) / (BN / 2)) * 8;
-    else return ((tid + 256 * i) / BN) * 8;
-  };
   // byte offsets of this thread's chunks from the tile's first key (lane
   // constants): a full tile is read as uniform tile base + 32-bit offset
   uint32_t koff[CPT], voff[CPT];
@@ -134,7 +122,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + 256 * i;
     koff[i] = (uint32_t)(((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2);
-    voff[i] = (uint32_t)((vkey(i) * D + vd0(i)) * 2);
+    voff[i] = koff[i];
   }
   auto load_tile = [&](int n0) {
     if (n0 + BN <= Sk) {  // uniform: every key of the tile exists
@@ -156,10 +144,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int kr = key < Sk ? key : Sk - 1;
       u32x4 a = *reinterpret_cast<const u32x4*>(kb + (int64_t)kr * D + d0);
       kreg[i] = key < Sk ? a : u32x4{0, 0, 0, 0};
-      const int vk = n0 + vkey(i);
-      const int vr = vk < Sk ? vk : Sk - 1;
-      u32x4 b = *reinterpret_cast<const u32x4*>(vb + (int64_t)vr * D + vd0(i));
-      vreg[i] = vk < Sk ? b : u32x4{0, 0, 0, 0};
+      u32x4 b = *reinterpret_cast<const u32x4*>(vb + (int64_t)kr * D + d0);
+      vreg[i] = key < Sk ? b : u32x4{0, 0, 0, 0};
     }
   };
   auto store_tile = [&](int stage) {
@@ -169,33 +155,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       *reinterpret_cast<u32x4*>(ks + (c / (D / 8)) * KP + (c % (D / 8)) * 8) = kreg[i];
-    }
-    if constexpr (PAIRS) {
-      uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
-#pragma unroll
-      for (int i = 0; i < CPT; i += 2) {
-        const int m = vkey(i) >> 1;
-        const int d0 = vd0(i);
-        const uint32_t a[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-        const uint32_t b[4] = {vreg[i + 1].x, vreg[i + 1].y, vreg[i + 1].z, vreg[i + 1].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vt32[((d0 + 2 * j) * VP) / 2 + m] = (a[j] & 0xffffu) | (b[j] << 16);
-          vt32[((d0 + 2 * j + 1) * VP) / 2 + m] = (a[j] >> 16) | (b[j] & 0xffff0000u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int key = vkey(i);
-        const int d0 = vd0(i);
-        const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vt[(d0 + 2 * j) * VP + key].u = (uint16_t)(w[j] & 0xffffu);
-          vt[(d0 + 2 * j + 1) * VP + key].u = (uint16_t)(w[j] >> 16);
-        }
-      }
+      *reinterpret_cast<u32x4*>(vt + (c / (D / 8)) * VS + (c % (D / 8)) * 8) = vreg[i];
     }
   };
 
@@ -302,22 +262,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
                        pack_bf16x2(s[t][12], s[t][13]), pack_bf16x2(s[t][14], s[t][15])};
     }
 
-    // O^T += V^T * P^T; V^T operand rows d = 32b + lq, keys in the C-layout order
+    // O^T += V^T * P^T. The V^T operand (row d = 32b + lane % 32, slots i of
+    // lane half h = keys 4h + 0..3, 8 + 4h + 0..3 of each 16-key step, the
+    // C-layout order of P^T) comes from the row-major V tile through two
+    // transposing reads per MFMA: in each 16-lane group, lane t reads the 4 d
+    // values 4(t % 4) + 0..3 of key t / 4 (of the group's 4 keys and 16 d),
+    // and lane u receives d = u of all 4 keys.
+    {
+      const int g16 = lane & 15;
+      const int vrow = 4 * h + (g16 >> 2);                       // key within 8
+      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);   // d within 32
+      const lds_bf16* vl = (const lds_bf16*)vt + vrow * VS + vcol;  // generic -> LDS pointer
 #pragma unroll
-    for (int b = 0; b < NDB; ++b) {
-      const bf16_t* row = vt + (32 * b + lq) * VP + 4 * h;
+      for (int b = 0; b < NDB; ++b)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16_t* r = row + 32 * t;
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(r);        // keys 4h + 0..3
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(r + 8);    // keys 8 + 4h + 0..3
-        const u32x2 a2 = *reinterpret_cast<const u32x2*>(r + 16);   // keys 16 + 4h + 0..3
-        const u32x2 a3 = *reinterpret_cast<const u32x2*>(r + 24);   // keys 24 + 4h + 0..3
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{a0.x, a0.y, a1.x, a1.y}),
-                                                         as_bf16x8(pb[2 * t]), acc[b], 0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{a2.x, a2.y, a3.x, a3.y}),
-                                                         as_bf16x8(pb[2 * t + 1]), acc[b], 0, 0, 0);
-      }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const lds_bf16* r = vl + (32 * t + 16 * st) * VS + 32 * b;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)r);
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(r + 8 * VS));
+            const u32x4 a = {__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                             __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[2 * t + st]),
+                                                             acc[b], 0, 0, 0);
+          }
     }
 
     if (blk + 1 < nblk) {

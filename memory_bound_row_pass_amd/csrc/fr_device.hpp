@@ -295,6 +295,78 @@ __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL
   }
 }
 
+// Next-row prefetch: the first PF slots of a row loaded as raw 16-byte
+// chunks (no unpacking, no masking) ahead of time, then unpacked into the
+// register row. Slot i of lane t is chunk i*T + t, as in load_chunks.
+template <typename Ts>
+struct RawChunk;
+template <>
+struct RawChunk<float> {
+  using T = f32x4;
+  static __device__ __forceinline__ void unpack(const T& r, float* v) {
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+};
+template <>
+struct RawChunk<bf16_t> {
+  using T = u32x4;
+  static __device__ __forceinline__ void unpack(const T& r, float* v) {
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+    v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+    v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
+    v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+  }
+};
+
+template <typename Ts, int T, int PF, int EPV, int AL>
+__device__ __forceinline__ void prefetch_slots(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
+                                               typename RawChunk<Ts>::T (&r)[PF]) {
+  static_assert(EPV * sizeof(Ts) == 16, "16-byte chunks");
+  if (g.nvec > 0) {
+    const Ts* base = row + g.head;
+    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      uint32_t o = (uint32_t)(i * T * EPV) + lo;
+      o = o < last ? o : last;
+      r[i] = ld_stream(reinterpret_cast<const typename RawChunk<Ts>::T*>(base + o));
+    }
+  }
+}
+
+// The row into registers when its first PF slots were prefetched into `r`:
+// the other slots are loaded now, then all are masked as in load_chunks.
+template <typename Ts, int T, int NV, int PF, int EPV, int AL>
+__device__ __forceinline__ void load_chunks_pf(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
+                                               const typename RawChunk<Ts>::T (&r)[PF],
+                                               float (&v)[NV][EPV], float fill) {
+  if (g.nvec > 0) {
+    const Ts* base = row + g.head;
+    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+#pragma unroll
+    for (int i = PF; i < NV; ++i) {
+      uint32_t o = (uint32_t)(i * T * EPV) + lo;
+      o = o < last ? o : last;
+      Vec<Ts, EPV>::load(base + o, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) RawChunk<Ts>::unpack(r[i], v[i]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ok = i * T + tid < g.nvec;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = ok ? v[i][k] : fill;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = fill;
+  }
+}
+
 // Two row operands of the same geometry in one branch, so that the second
 // operand's loads are issued before the first operand's data is waited for.
 template <typename Ts, int T, int NV, int EPV, int AL>

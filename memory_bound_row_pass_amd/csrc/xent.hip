@@ -66,7 +66,10 @@ __device__ __forceinline__ int owner_lane(int c, const RowGeom<EPV>& g) {
 // accurate to ~3e-7 relative (2^64 would leave ~2.6e-6).
 constexpr int kXentBias = 8;
 
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT>
+// PF > 0: the first PF slots of the row owner's next row are loaded before
+// the current row's reduction, so the CU keeps reads in flight while it
+// reduces and writes (PF * 4 more VGPRs per lane).
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0>
 __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
 void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, int32_t* argmax,
                  int64_t rows, int cols, XentOptions opt) {
@@ -101,6 +104,9 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
   const int64_t stride = (int64_t)gridDim.x * RPB;
   const int64_t first = (int64_t)blockIdx.x * RPB + sub;
   int label_next = first < rows ? __builtin_amdgcn_readfirstlane(labels[first]) : 0;
+  static_assert(PF == 0 || EPV * sizeof(Tin) == 16, "prefetch of 16-byte chunks");
+  typename RawChunk<Tin>::T pre[PF > 0 ? PF : 1];
+  bool have_pre = false;  // uniform: pre holds this row's first PF slots
 
   int it = 0;
   for (int64_t row = first; row < rows; row += stride, ++it) {
@@ -123,6 +129,13 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
         store_chunks<Tin, T, NV, EPV>(gr, g, tid, z);
         if (ec >= 0) store1(gr + ec, 0.f);
         if (tid == 0) loss[row] = 0.f;
+        if constexpr (PF > 0) {
+          have_pre = rn < rows && !(opt.use_ignore && label_next == opt.ignore_index);
+          if (have_pre) {
+            const Tin* xn = x + rn * cols;
+            prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+          }
+        }
         continue;
       }
     }
@@ -134,10 +147,25 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     const bool valid = label >= 0 && label < cols;
     const bool label_lane = valid && !ignored && owner_lane<T, EPV>(label, g) == tid;
     float v[NV][EPV];
-    load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+    if constexpr (PF > 0) {
+      if (have_pre) load_chunks_pf<Tin, T, NV, PF, EPV>(xr, g, tid, pre, v, kNegInf);
+      else load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+    } else {
+      load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+    }
     float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
     float x_label = 0.f;
     if (label_lane) x_label = load1(xr + label);
+    if constexpr (PF > 0) {
+      // the next row's first slots (not when it is an ignored row that is
+      // not read)
+      have_pre = rn < rows &&
+                 !(OPT && !ARGMAX && opt.use_ignore && label_next == opt.ignore_index);
+      if (have_pre) {
+        const Tin* xn = x + rn * cols;
+        prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+      }
+    }
 
     const float m = lane_max<NV, EPV>(v, xe);
     Base bs;
@@ -304,7 +332,7 @@ hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* co
   return launch_kernel(&xent_total_kernel, dim3(1), dim3(1024), s, loss, rows, count, total);
 }
 
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT>
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0>
 static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss, void* grad,
                               int32_t* argmax, int64_t rows, int cols, const XentOptions* opt,
                               hipStream_t s) {
@@ -313,18 +341,33 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   const int64_t blocks = (rows + RPB - 1) / RPB;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
   const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
-  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT>, dim3(grid), dim3(BLOCK), s,
+  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT, PF>, dim3(grid), dim3(BLOCK), s,
                        static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax,
                        rows, cols, o);
 }
 
 #define FR_XE(TS, T, NV, EPV, OCC, AM, OPT) {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT>}
+// Prefetch depths (measured at 4096 x 50257): one slot helps the bf16 rows
+// (177 -> 170 us); fp32 rows are no faster with 2-5 slots (285 -> 290 us: the
+// reads are already at the mixed read/write ceiling) and the options
+// kernels spill with any.
+#ifndef FR_XE_PF_F32
+#define FR_XE_PF_F32 0
+#endif
+#ifndef FR_XE_PF_F32_OPT
+#define FR_XE_PF_F32_OPT 0
+#endif
+#ifndef FR_XE_PF_BF16
+#define FR_XE_PF_BF16 1
+#endif
+#define FR_XF(TS, T, NV, EPV, OCC, AM, OPT, PF) \
+  {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT, PF>}
 #define FR_XE_F32(AM, OPT)                                                                       \
   {FR_XE(float, 64, 1, 4, 8, AM, OPT),    FR_XE(float, 64, 2, 4, 8, AM, OPT),                    \
    FR_XE(float, 64, 4, 4, 8, AM, OPT),    FR_XE(float, 64, 8, 4, 6, AM, OPT),                    \
    FR_XE(float, 64, 16, 4, 4, AM, OPT),   FR_XE(float, 256, 8, 4, 6, AM, OPT),                   \
    FR_XE(float, 512, 8, 4, 6, AM, OPT),   FR_XE(float, 1024, 8, 4, 4, AM, OPT),                  \
-   FR_XE(float, 1024, 13, 4, 4, AM, OPT), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
+   FR_XF(float, 1024, 13, 4, 4, AM, OPT, (OPT ? FR_XE_PF_F32_OPT : FR_XE_PF_F32)), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
    FR_XE(float, 256, 50, 4, 2, AM, OPT),  FR_XE(float, 1024, 16, 4, 4, AM, OPT),                 \
    FR_XE(float, 64, 16, 1, 4, AM, OPT),   FR_XE(float, 256, 16, 1, 4, AM, OPT),                  \
    FR_XE(float, 1024, 16, 1, 4, AM, OPT), FR_XE(float, 1024, 64, 1, 4, AM, OPT)}
@@ -332,7 +375,7 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   {FR_XE(bf16_t, 64, 1, 8, 8, AM, true),    FR_XE(bf16_t, 64, 2, 8, 8, AM, true),                \
    FR_XE(bf16_t, 64, 4, 8, 6, AM, true),    FR_XE(bf16_t, 64, 8, 8, 4, AM, true),                \
    FR_XE(bf16_t, 256, 4, 8, 6, AM, true),   FR_XE(bf16_t, 512, 4, 8, 6, AM, true),               \
-   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XE(bf16_t, 1024, 7, 8, 4, AM, true),              \
+   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XF(bf16_t, 1024, 7, 8, 4, AM, true, FR_XE_PF_BF16),              \
    FR_XE(bf16_t, 1024, 8, 8, 4, AM, true),  FR_XE(bf16_t, 64, 16, 1, 4, AM, true),               \
    FR_XE(bf16_t, 256, 16, 1, 4, AM, true),  FR_XE(bf16_t, 1024, 16, 1, 4, AM, true),             \
    FR_XE(bf16_t, 1024, 64, 1, 4, AM, true)}

@@ -25,7 +25,8 @@ forward workloads' shapes (softmax bf16 [16384, 4096], LayerNorm fp32
 cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
 logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
 split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
-[2048, 131072], bf16 [1024, 262144]); they are
+[2048, 131072], bf16 [1024, 262144]) and the split-row norms (LayerNorm fp32
+[512, 131072], residual-add + RMSNorm bf16 [256, 262144]); they are
 reported under "backward" and "variants" and are not part of `value`; so is the
 attention forward (bf16 B=4 H=16 S=4096 D=128, causal and not), reported
 under "attention" in matrix TFLOP/s against the bf16 peak. Their per-row inputs from the
@@ -82,6 +83,12 @@ def bwd_algo_bytes(name, R, C):
         # reads the logits twice: 1.5x these bytes move); labels, loss
         es = 4 if name == "xent_split_f32" else 2
         return 2 * R * C * es + 2 * R * 4
+    if name == "layernorm_split_f32":
+        # x, y; gamma, beta; mean, rstd (the split path reads x twice)
+        return 2 * R * C * 4 + 2 * C * 4 + 2 * R * 4
+    if name == "add_rmsnorm_split_bf16":
+        # x, r, y, r_out; w (the split path reads x and r twice)
+        return 4 * R * C * 2 + C * 2
     if name in ("xent_ex_f32", "xent_ex_bf16"):
         # logits of the rows not ignored (every 9th row is), grad of all rows;
         # labels, loss; total
@@ -148,6 +155,26 @@ class BwdWorkload:
                                                         self.ws)
             self.op = fr.OP_XENT_SPLIT
             self.code = fr.BF16 if name == "xent_split_bf16" else fr.F32
+        elif name == "layernorm_split_f32":
+            # wide LayerNorm rows through the split-row path
+            self.x, self.g, self.b = d(w["x"]), d(w["gamma"]), d(w["beta"])
+            self.y = torch.empty_like(self.x)
+            self.mean = torch.empty(self.R, device=dev)
+            self.rstd = torch.empty(self.R, device=dev)
+            self.ws = torch.empty(fr.fr_split_workspace_bytes(self.R, self.C), dtype=torch.uint8,
+                                  device=dev)
+            self.run = lambda: fr.fr_layernorm_fwd_split(self.x, self.g, self.b, self.y, self.ws,
+                                                         self.mean, self.rstd, w.eps)
+            self.op, self.code = fr.OP_LAYERNORM_SPLIT, fr.F32
+        elif name == "add_rmsnorm_split_bf16":
+            self.x, self.r, self.wt = d(w["x"]), d(w["residual"]), d(w["weight"])
+            self.y = torch.empty_like(self.x)
+            self.ro = torch.empty_like(self.x)
+            self.ws = torch.empty(fr.fr_split_workspace_bytes(self.R, self.C), dtype=torch.uint8,
+                                  device=dev)
+            self.run = lambda: fr.fr_add_rmsnorm_fwd_split(self.x, self.r, self.wt, self.y, self.ws,
+                                                           self.ro, w.eps)
+            self.op, self.code = fr.OP_RMSNORM_SPLIT, fr.BF16
         elif name == "add_rmsnorm_bwd_bf16":
             self.h, self.dy, self.dres = d(w["h"]), d(w["dy"]), d(w["dres"])
             self.wt = d(w["weight"])
@@ -433,6 +460,10 @@ def main():
                             ("xent_split_bf16", "bf16", 1024, 262144)):
             bws.append(BwdWorkload(n, workloads.make("xent_f32", rows=R, cols=C, dtype=dt), dev,
                                    torch, fr))
+            log(f"generated {n}")
+        for n, base, dt, R, C in (("layernorm_split_f32", "layernorm_f32", "f32", 512, 131072),
+                                  ("add_rmsnorm_split_bf16", "add_rmsnorm_bf16", "bf16", 256, 262144)):
+            bws.append(BwdWorkload(n, workloads.make(base, rows=R, cols=C, dtype=dt), dev, torch, fr))
             log(f"generated {n}")
         for _ in range(max(3, args.warmup)):
             for b in bws:

@@ -69,7 +69,9 @@ typedef enum {
   FR_OP_RMSNORM_BWD = 5,
   FR_OP_LAYERNORM_BWD = 6,
   FR_OP_SOFTMAX_SPLIT = 7,
-  FR_OP_XENT_SPLIT = 8
+  FR_OP_XENT_SPLIT = 8,
+  FR_OP_LAYERNORM_SPLIT = 9,
+  FR_OP_RMSNORM_SPLIT = 10
 } fr_op_t;
 
 typedef enum {
@@ -225,6 +227,35 @@ FR_API fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labe
                                   int64_t rows, int64_t cols, fr_dtype_t dtype,
                                   const fr_xent_options_t* options, void* workspace,
                                   int64_t workspace_bytes, void* stream);
+
+/* LayerNorm for rows of any width, split as fr_softmax_fwd_split: pass 1
+ * writes each segment's exact (count, mean, M2) to `workspace`, pass 2 merges
+ * a row's partials in segment order with the pairwise (Chan) merge of the
+ * Welford moments and writes the segment's y (and, from the row's first
+ * segment, mean and rstd). Reads x twice, writes y once.
+ *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.2
+ *    Welford Single-Pass Normalization: partial moments merged pairwise.)
+ * Arguments and results as fr_layernorm_fwd, with 1 <= cols <=
+ * FR_SPLIT_MAX_COLS, plus the workspace as fr_softmax_fwd_split. */
+FR_API fr_status_t fr_layernorm_fwd_split(const void* x, const void* gamma, const void* beta,
+                                          void* y, float* mean, float* rstd, int64_t rows,
+                                          int64_t cols, float eps, fr_dtype_t dtype,
+                                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Residual add + RMSNorm for rows of any width, split as
+ * fr_softmax_fwd_split: pass 1 writes each segment's sum of h^2
+ * (h = x + residual in fp32) to `workspace`, pass 2 adds a row's partials in
+ * segment order, re-reads x and residual and writes residual_out and y.
+ * Reads x and residual twice, writes each output once.
+ *   ("NexusGrad", Core Capabilities: RMSNorm, residual blocks.)
+ * Arguments and results as fr_add_rmsnorm_fwd (residual_out may equal
+ * residual, y may equal x), with 1 <= cols <= FR_SPLIT_MAX_COLS, plus the
+ * workspace as fr_softmax_fwd_split. */
+FR_API fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual,
+                                            const void* weight, void* y, void* residual_out,
+                                            int64_t rows, int64_t cols, float eps,
+                                            fr_dtype_t dtype, void* workspace,
+                                            int64_t workspace_bytes, void* stream);
 
 /* ---- the online softmax inside attention ---- */
 

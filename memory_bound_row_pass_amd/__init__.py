@@ -23,6 +23,7 @@ __all__ = [
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
     "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
     "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS", "fr_attention_fwd", "attention",
+    "fr_layernorm_fwd_split", "fr_add_rmsnorm_fwd_split", "OP_LAYERNORM_SPLIT", "OP_RMSNORM_SPLIT",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
     "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
@@ -33,6 +34,7 @@ F32, BF16 = 0, 1
 OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
 OP_SOFTMAX_BWD, OP_RMSNORM_BWD, OP_LAYERNORM_BWD = 4, 5, 6
 OP_SOFTMAX_SPLIT, OP_XENT_SPLIT = 7, 8
+OP_LAYERNORM_SPLIT, OP_RMSNORM_SPLIT = 9, 10
 FR_SPLIT_MAX_COLS = 1 << 24
 FR_MAX_COLS = 65536
 FR_BWD_MAX_COLS = 16384
@@ -85,6 +87,8 @@ def _load() -> ctypes.CDLL:
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
         "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
         "fr_softmax_fwd_split": [P, P, I64, I64, I32, I32, P, I64, P],
+        "fr_layernorm_fwd_split": [P, P, P, P, P, P, I64, I64, F, I32, P, I64, P],
+        "fr_add_rmsnorm_fwd_split": [P, P, P, P, P, I64, I64, F, I32, P, I64, P],
         "fr_attention_fwd": [P, P, P, P, P, I64, I64, I64, I64, I64, I32, F, I32, P],
         "fr_softmax_xent_split": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P,
                                   I64, P],
@@ -286,6 +290,48 @@ def fr_softmax_fwd_split(x, y, workspace, stream=None) -> None:
                                     _stream(stream, x)), "fr_softmax_fwd_split")
 
 
+def fr_layernorm_fwd_split(x, gamma, beta, y, workspace, mean=None, rstd=None, eps: float = 1e-5,
+                           stream=None) -> None:
+    """LayerNorm of rows of any width, several workgroups per row
+    (C: fr_layernorm_fwd_split); arguments as fr_layernorm_fwd plus the
+    workspace."""
+    torch = _torch()
+    _need_cuda(x, gamma, beta, y, mean, rstd)
+    R, C = _rows_cols(x)
+    _check_vec(gamma, C, "gamma")
+    _check_vec(beta, C, "beta")
+    if tuple(y.shape) != (R, C) or not y.is_contiguous() or y.dtype != x.dtype:
+        raise ValueError("y must be a contiguous tensor of x's shape and dtype")
+    if gamma.dtype != x.dtype or beta.dtype != x.dtype:
+        raise TypeError("gamma and beta must have x's dtype")
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _check_rows(t, R, n, torch.float32)
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_layernorm_fwd_split(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean),
+                                      _ptr(rstd), R, C, float(eps), _dtype_code(x), wp, wn,
+                                      _stream(stream, x)), "fr_layernorm_fwd_split")
+
+
+def fr_add_rmsnorm_fwd_split(x, residual, weight, y, workspace, residual_out=None,
+                             eps: float = 1e-6, stream=None) -> None:
+    """Residual add + RMSNorm of rows of any width, several workgroups per row
+    (C: fr_add_rmsnorm_fwd_split); arguments as fr_add_rmsnorm_fwd plus the
+    workspace."""
+    _need_cuda(x, residual, weight, y, residual_out)
+    R, C = _rows_cols(x)
+    for t, n in ((residual, "residual"), (y, "y"), (residual_out, "residual_out")):
+        if t is not None and (tuple(t.shape) != (R, C) or not t.is_contiguous() or t.dtype != x.dtype):
+            raise ValueError(f"{n} must be a contiguous tensor of x's shape and dtype")
+    _check_vec(weight, C, "weight")
+    if weight.dtype != x.dtype:
+        raise TypeError("weight must have x's dtype")
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_add_rmsnorm_fwd_split(_ptr(x), _ptr(residual), _ptr(weight), _ptr(y),
+                                        _ptr(residual_out), R, C, float(eps), _dtype_code(x), wp, wn,
+                                        _stream(stream, x)), "fr_add_rmsnorm_fwd_split")
+
+
 def fr_softmax_xent_split(logits, labels, loss, grad, workspace, argmax=None, loss_total=None,
                           ignore_index=None, label_smoothing: float = 0.0, grad_scale: float = 1.0,
                           reduction: str = "none", stream=None) -> None:
@@ -470,20 +516,30 @@ def softmax(x, out_dtype=None, out=None):
 
 
 def layernorm(x, gamma, beta, eps: float = 1e-5):
+    """Returns (y, mean, rstd); rows wider than FR_MAX_COLS take the split-row path."""
     torch = _torch()
     R = x.shape[0]
     y = torch.empty_like(x)
     mean = torch.empty(R, dtype=torch.float32, device=x.device)
     rstd = torch.empty(R, dtype=torch.float32, device=x.device)
-    fr_layernorm_fwd(x, gamma, beta, y, mean, rstd, eps)
+    if x.shape[1] > FR_MAX_COLS:
+        fr_layernorm_fwd_split(x, gamma, beta, y, _split_workspace(R, x.shape[1], x.device), mean,
+                               rstd, eps)
+    else:
+        fr_layernorm_fwd(x, gamma, beta, y, mean, rstd, eps)
     return y, mean, rstd
 
 
 def add_rmsnorm(x, residual, weight, eps: float = 1e-6, inplace: bool = False):
+    """Returns (y, residual_out); rows wider than FR_MAX_COLS take the split-row path."""
     torch = _torch()
     y = torch.empty_like(x)
     res_out = residual if inplace else torch.empty_like(residual)
-    fr_add_rmsnorm_fwd(x, residual, weight, y, res_out, eps)
+    if x.shape[1] > FR_MAX_COLS:
+        fr_add_rmsnorm_fwd_split(x, residual, weight, y, _split_workspace(x.shape[0], x.shape[1],
+                                                                          x.device), res_out, eps)
+    else:
+        fr_add_rmsnorm_fwd(x, residual, weight, y, res_out, eps)
     return y, res_out
 
 

@@ -20,7 +20,7 @@ struct Forced {
   std::atomic<int> threads{0};
   std::atomic<int> vecs{0};
 };
-Forced g_forced[FR_OP_XENT_SPLIT + 1];
+Forced g_forced[FR_OP_RMSNORM_SPLIT + 1];
 
 // ------------------------------------------------------------------- buffers
 struct Buf {
@@ -95,11 +95,12 @@ fr_status_t launch_status(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_
 
 // Split-row shape: a forced (threads, vecs), else the table's first shape on
 // the requested path (the smallest segment: measured fastest on MI355X).
-const fr::SplitVariant* select_split(VariantSpan<fr::SplitVariant> sp, int op, int epv) {
+template <typename V>
+const V* select_split(VariantSpan<V> sp, int op, int epv) {
   const int ft = g_forced[op].threads.load(std::memory_order_relaxed);
   const int fv = g_forced[op].vecs.load(std::memory_order_relaxed);
   for (size_t i = 0; i < sp.n; ++i) {
-    const fr::SplitVariant& v = sp.v[i];
+    const V& v = sp.v[i];
     if (v.epv != epv) continue;
     if (!ft || (v.threads == ft && v.nv == fv)) return &v;
   }
@@ -139,7 +140,7 @@ const char* fr_status_str(fr_status_t s) {
 const char* fr_version(void) { return "fusedrow 0.1.0 (gfx950)"; }
 
 fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs) {
-  if (op < FR_OP_SOFTMAX || op > FR_OP_XENT_SPLIT) return FR_E_VALUE;
+  if (op < FR_OP_SOFTMAX || op > FR_OP_RMSNORM_SPLIT) return FR_E_VALUE;
   if (threads < 0 || vecs < 0) return FR_E_VALUE;
   g_forced[op].vecs.store(threads ? vecs : 0);
   g_forced[op].threads.store(threads);
@@ -151,8 +152,9 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
                                     int* elems_per_vec) {
   if (!threads || !vecs || !elems_per_vec) return FR_E_NULL;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return FR_E_DTYPE;
-  const int64_t maxc =
-      (op == FR_OP_SOFTMAX_SPLIT || op == FR_OP_XENT_SPLIT) ? FR_SPLIT_MAX_COLS : FR_MAX_COLS;
+  const bool split = op == FR_OP_SOFTMAX_SPLIT || op == FR_OP_XENT_SPLIT ||
+                     op == FR_OP_LAYERNORM_SPLIT || op == FR_OP_RMSNORM_SPLIT;
+  const int64_t maxc = split ? FR_SPLIT_MAX_COLS : FR_MAX_COLS;
   if (cols < 1 || cols > maxc) return FR_E_SHAPE;
   const int epv = vector_path ? vec_epv(esize(in_dtype)) : 1;
   int t = 0, n = 0, e = 0;
@@ -204,6 +206,13 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
       // the shape for a single row of `cols` (few rows: the smallest segment)
       auto v = select_split(fr::split_variants(in_dtype == FR_BF16, out_dtype == FR_BF16,
                                                op == FR_OP_XENT_SPLIT),
+                            op, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_LAYERNORM_SPLIT:
+    case FR_OP_RMSNORM_SPLIT: {
+      auto v = select_split(fr::norm_split_variants(in_dtype == FR_BF16, op == FR_OP_RMSNORM_SPLIT),
                             op, epv);
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
@@ -591,6 +600,68 @@ fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, flo
     return s;
   if (!reduce) return FR_OK;
   return launch_status(fr::launch_xent_total(loss, rows, count, loss_total, st));
+}
+
+fr_status_t fr_layernorm_fwd_split(const void* x, const void* gamma, const void* beta, void* y,
+                                   float* mean, float* rstd, int64_t rows, int64_t cols, float eps,
+                                   fr_dtype_t dtype, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
+  if (fr_status_t s = check_split(rows, cols, workspace, workspace_bytes)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  if (rows == 0) return FR_OK;
+  if (!x || !gamma || !beta || !y) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, es) || !aligned(beta, es) ||
+      (mean && !aligned(mean, 4)) || (rstd && !aligned(rstd, 4)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(x, rows * cols * es, true, es, false),
+                      make_buf(gamma, cols * es, false, es, false),
+                      make_buf(beta, cols * es, false, es, false),
+                      make_buf(y, rows * cols * es, true, es, true),
+                      make_buf(mean, rows * 4, false, 4, true),
+                      make_buf(rstd, rows * 4, false, 4, true),
+                      make_buf(workspace, fr_split_workspace_bytes(rows, cols), false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 7)) return s;
+  const bool vec = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16) &&
+                   (cols * es) % 16 == 0;
+  const fr::NormSplitVariant* v = select_split(fr::norm_split_variants(dtype == FR_BF16, 0),
+                                               FR_OP_LAYERNORM_SPLIT, vec ? vec_epv(es) : 1);
+  if (!v) return FR_E_VARIANT;
+  return launch_status(v->launch(x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, (int)cols,
+                                 eps, static_cast<float4*>(workspace),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual, const void* weight,
+                                     void* y, void* residual_out, int64_t rows, int64_t cols,
+                                     float eps, fr_dtype_t dtype, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+  if (fr_status_t s = check_split(rows, cols, workspace, workspace_bytes)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  if (rows == 0) return FR_OK;
+  if (!x || !residual || !weight || !y) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(x, es) || !aligned(residual, es) || !aligned(weight, es) || !aligned(y, es) ||
+      (residual_out && !aligned(residual_out, es)))
+    return FR_E_ALIGN;
+  const Buf bufs[] = {make_buf(x, rows * cols * es, true, es, false),
+                      make_buf(residual, rows * cols * es, true, es, false),
+                      make_buf(weight, cols * es, false, es, false),
+                      make_buf(y, rows * cols * es, true, es, true),
+                      make_buf(residual_out, rows * cols * es, true, es, true),
+                      make_buf(workspace, fr_split_workspace_bytes(rows, cols), false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 6)) return s;
+  const bool vec = aligned(x, 16) && aligned(residual, 16) && aligned(weight, 16) &&
+                   aligned(y, 16) && (!residual_out || aligned(residual_out, 16)) &&
+                   (cols * es) % 16 == 0;
+  const fr::NormSplitVariant* v = select_split(fr::norm_split_variants(dtype == FR_BF16, 1),
+                                               FR_OP_RMSNORM_SPLIT, vec ? vec_epv(es) : 1);
+  if (!v) return FR_E_VARIANT;
+  return launch_status(v->launch(x, residual, weight, nullptr, y, residual_out, nullptr, nullptr,
+                                 rows, (int)cols, eps, static_cast<float4*>(workspace),
+                                 static_cast<hipStream_t>(stream)));
 }
 
 fr_status_t fr_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

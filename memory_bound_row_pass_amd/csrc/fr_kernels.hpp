@@ -85,12 +85,21 @@ typedef hipError_t (*SplitLaunch)(const void* x, void* y, int64_t rows, int cols
                                   const int32_t* labels, float* loss, int32_t* argmax,
                                   const XentOptions* opt, float4* part, hipStream_t s);
 
+// Split-row LayerNorm / residual-add + RMSNorm (pass 1 partials into
+// `part`, then pass 2). LayerNorm: p1 = gamma, p2 = beta, res and res_out
+// NULL. RMSNorm: p1 = weight; p2, mean and rstd NULL.
+typedef hipError_t (*NormSplitLaunch)(const void* x, const void* res, const void* p1,
+                                      const void* p2, void* y, void* res_out, float* mean,
+                                      float* rstd, int64_t rows, int cols, float eps, float4* part,
+                                      hipStream_t s);
+
 typedef Variant<SoftmaxLaunch> SoftmaxVariant;
 typedef Variant<LayerNormLaunch> LayerNormVariant;
 typedef Variant<RmsNormLaunch> RmsNormVariant;
 typedef Variant<XentLaunch> XentVariant;
 typedef Variant<SoftmaxBwdLaunch> SoftmaxBwdVariant;
 typedef Variant<SplitLaunch> SplitVariant;
+typedef Variant<NormSplitLaunch> NormSplitVariant;
 typedef BwdVariant<RmsNormBwdLaunch> RmsNormBwdVariant;
 typedef BwdVariant<LayerNormBwdLaunch> LayerNormBwdVariant;
 
@@ -100,6 +109,7 @@ VariantSpan<RmsNormVariant> rmsnorm_variants(int bf16);
 VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
 VariantSpan<XentVariant> xent_ex_variants(int bf16, int with_argmax);
 VariantSpan<SplitVariant> split_variants(int in_bf16, int out_bf16, int xent);
+VariantSpan<NormSplitVariant> norm_split_variants(int bf16, int rms);
 hipError_t launch_xent_count(const int32_t* labels, int64_t rows, int use_ignore, int ignore_index,
                              uint32_t* out, hipStream_t s);
 hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* count, float* total,

@@ -218,6 +218,43 @@ def test_split_validation():
         fr.fr_split_workspace_bytes(4, 0)
 
 
+def test_split_norm_validation():
+    f = fr.lib.fr_layernorm_fwd_split
+    Gm, Bt, Y, M, RS, WS = (A + k * 0x100000 for k in range(1, 7))
+    need = fr.fr_split_workspace_bytes(4, 100000)
+
+    def ln(x=A, g=Gm, b=Bt, y=Y, m=M, r=RS, rows=4, cols=100000, eps=1e-5, dt=0, ws=WS, wn=need):
+        return f(P(x), P(g), P(b), P(y), P(m), P(r), rows, cols, eps, dt, P(ws), wn, None)
+
+    assert ln(rows=0, ws=0, wn=0) == OK
+    assert ln(wn=need - 1) == E_SHAPE
+    assert ln(cols=fr.FR_SPLIT_MAX_COLS + 1, wn=1 << 40) == E_SHAPE
+    assert ln(ws=0) == E_NULL
+    assert ln(g=0) == E_NULL
+    assert ln(ws=WS + 8) == E_ALIGN
+    assert ln(dt=3) == E_DTYPE
+    assert ln(eps=-1.0) == E_VALUE
+    assert ln(eps=float("nan")) == E_VALUE
+    assert ln(m=M + 2) == E_ALIGN
+    assert ln(y=A + 4) == E_ALIAS                       # partial overlap with x
+    assert ln(ws=Y + 16) == E_ALIAS                     # workspace inside y
+    assert ln(r=M) == E_ALIAS                           # mean and rstd the same buffer
+    g = fr.lib.fr_add_rmsnorm_fwd_split
+    R_, W_, RO = A + 0x700000, A + 0x800000, A + 0x900000
+
+    def rn(x=A, r=R_, w=W_, y=Y, ro=RO, rows=4, cols=100000, eps=1e-6, dt=1, ws=WS, wn=need):
+        return g(P(x), P(r), P(w), P(y), P(ro), rows, cols, eps, dt, P(ws), wn, None)
+
+    assert rn(rows=0, ws=0, wn=0) == OK
+    assert rn(wn=need - 1) == E_SHAPE
+    assert rn(w=0) == E_NULL
+    assert rn(dt=2) == E_DTYPE
+    assert rn(eps=float("inf")) == E_VALUE
+    assert rn(x=A + 1) == E_ALIGN                      # bf16 needs 2-byte alignment
+    assert rn(ro=R_ + 2) == E_ALIAS                    # residual_out overlapping the residual
+    assert rn(ws=RO) == E_ALIAS                        # workspace over residual_out
+
+
 def test_attention_validation():
     f = fr.lib.fr_attention_fwd
     K, V, O, LSE = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
@@ -266,7 +303,7 @@ def test_variant_selection():
             with pytest.raises(fr.FusedRowError) as ei:
                 fr.fr_debug_select_variant(op, fr.FR_BWD_MAX_COLS + 1, dt)
             assert ei.value.status == E_SHAPE
-    for op in (fr.OP_SOFTMAX_SPLIT, fr.OP_XENT_SPLIT):
+    for op in (fr.OP_SOFTMAX_SPLIT, fr.OP_XENT_SPLIT, fr.OP_LAYERNORM_SPLIT, fr.OP_RMSNORM_SPLIT):
         for dt in (fr.F32, fr.BF16):
             for vp in (True, False):
                 t, v, e = fr.fr_debug_select_variant(op, 262144, dt, vector_path=vp)
@@ -279,7 +316,7 @@ def test_variant_selection():
             fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32)
         assert ei.value.status == E_VARIANT
     with pytest.raises(fr.FusedRowError):
-        fr.fr_debug_force_variant(9, 64, 1)
+        fr.fr_debug_force_variant(11, 64, 1)
 
 
 def test_binding_rejects_host_tensors():

@@ -198,3 +198,145 @@ def test_convenience_routes_wide_rows():
     loss, grad = fr.softmax_xent(upload(xl), upload(lab))
     lo, go, _, _ = oracle.softmax_xent_ex(xl, lab)
     check_f32(loss.cpu().numpy(), lo, scale=np.maximum(np.abs(lo), 1.0), what="softmax_xent() wide")
+
+
+# ------------------------------------------------------ LayerNorm / RMSNorm
+
+from test_gpu_parity import expect_layernorm, expect_rmsnorm  # noqa: E402
+
+
+def run_ln_split(w_x, w_g, w_b, eps, offs=(0, 0), inplace=False):
+    x, g, b = upload(w_x, offs[0]), upload(w_g, offs[1]), upload(w_b, offs[1])
+    R, C = w_x.shape
+    ws = workspace(R, C)
+    mean, rstd = Guarded((R,), torch.float32), Guarded((R,), torch.float32)
+    y = None if inplace else Guarded((R, C), x.dtype, offs[0])
+    yt = x if inplace else y.t
+    fr.fr_layernorm_fwd_split(x, g, b, yt, ws.t, mean.t, rstd.t, eps)
+    torch.cuda.synchronize()
+    assert ws.canaries_intact() and mean.canaries_intact() and rstd.canaries_intact()
+    assert y is None or y.canaries_intact(), "split LayerNorm wrote out of bounds"
+    return host(yt), mean.t.cpu().numpy(), rstd.t.cpu().numpy()
+
+
+def run_rms_split(w_x, w_r, w_w, eps, offs=(0, 0), inplace=False, with_res_out=True):
+    x, r, wt = upload(w_x, offs[0]), upload(w_r, offs[0]), upload(w_w, offs[1])
+    R, C = w_x.shape
+    ws = workspace(R, C)
+    if inplace:  # y over x, residual_out over the residual
+        fr.fr_add_rmsnorm_fwd_split(x, r, wt, x, ws.t, r, eps)
+        torch.cuda.synchronize()
+        assert ws.canaries_intact()
+        return host(x), host(r)
+    y = Guarded((R, C), x.dtype, offs[0])
+    ro = Guarded((R, C), x.dtype, offs[0]) if with_res_out else None
+    fr.fr_add_rmsnorm_fwd_split(x, r, wt, y.t, ws.t, ro.t if ro else None, eps)
+    torch.cuda.synchronize()
+    assert ws.canaries_intact() and y.canaries_intact() and (ro is None or ro.canaries_intact())
+    return host(y.t), (host(ro.t) if ro else None)
+
+
+NORM_WIDTHS = [1, 5, 1000, 8191, 8192, 8193, 65536, 65537, 100000, 262144]
+
+
+@pytest.mark.parametrize("C", NORM_WIDTHS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_layernorm_split_widths(C, dt):
+    for R in (1, 3):
+        w = workloads.make("layernorm_f32", rows=R, cols=C, seed=C + R, dtype=dt)
+        got = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps)
+        expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps, got, f"split layernorm {dt} {R}x{C}")
+
+
+@pytest.mark.parametrize("C", NORM_WIDTHS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rmsnorm_split_widths(C, dt):
+    for R in (1, 3):
+        w = workloads.make("add_rmsnorm_bf16", rows=R, cols=C, seed=C + R, dtype=dt)
+        got = run_rms_split(w["x"], w["residual"], w["weight"], w.eps, with_res_out=R == 3)
+        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, got,
+                       f"split add_rmsnorm {dt} {R}x{C}")
+
+
+@pytest.mark.parametrize("t,v", SEG_SHAPES)
+def test_norm_split_every_segment_shape(t, v):
+    ran = 0
+    for dt, code in (("f32", fr.F32), ("bf16", fr.BF16)):
+        for vp, offs in ((True, (0, 0)), (False, (1, 3))):
+            for op in (fr.OP_LAYERNORM_SPLIT, fr.OP_RMSNORM_SPLIT):
+                try:
+                    with fr.forced_variant(op, t, v):
+                        tt, vv, e = fr.fr_debug_select_variant(op, 1, code, vector_path=vp)
+                except fr.FusedRowError:
+                    continue
+                seg = tt * vv * e
+                # the vector path needs every row on the 16-byte grid (the
+                # parameter vectors share the rows' phase): widths of 8k
+                widths = (seg - 8, seg, 2 * seg + 40, 5 * seg) if vp else (seg - 3, 2 * seg + 37)
+                for C in widths:
+                    with fr.forced_variant(op, t, v):
+                        if op == fr.OP_LAYERNORM_SPLIT:
+                            w = workloads.make("layernorm_f32", rows=2, cols=C, seed=C, dtype=dt)
+                            got = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps, offs)
+                        else:
+                            w = workloads.make("add_rmsnorm_bf16", rows=2, cols=C, seed=C, dtype=dt)
+                            got = run_rms_split(w["x"], w["residual"], w["weight"], w.eps, offs)
+                    what = f"split norm op {op} [{t},{v},{vp}] {dt} 2x{C}"
+                    if op == fr.OP_LAYERNORM_SPLIT:
+                        expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps, got, what)
+                    else:
+                        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, got, what)
+                    ran += 1
+    if not ran:
+        pytest.skip(f"no split norm shape ({t}, {v})")
+
+
+def test_norm_split_in_place_and_misaligned():
+    for dt in ("f32", "bf16"):
+        w = workloads.make("layernorm_f32", rows=4, cols=70001, seed=21, dtype=dt)
+        expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps,
+                         run_ln_split(w["x"], w["gamma"], w["beta"], w.eps, inplace=True),
+                         f"split layernorm in place {dt}")
+        for offs in ((1, 1), (3, 0), (0, 5)):
+            expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps,
+                             run_ln_split(w["x"], w["gamma"], w["beta"], w.eps, offs),
+                             f"split layernorm offs {offs} {dt}")
+        w = workloads.make("add_rmsnorm_bf16", rows=4, cols=131072, seed=22, dtype=dt)
+        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps,
+                       run_rms_split(w["x"], w["residual"], w["weight"], w.eps, inplace=True),
+                       f"split add_rmsnorm in place {dt}")
+        expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps,
+                       run_rms_split(w["x"], w["residual"], w["weight"], w.eps, (1, 2)),
+                       f"split add_rmsnorm misaligned {dt}")
+
+
+def test_norm_split_special_rows():
+    C = 100000
+    w = workloads.make("layernorm_f32", rows=3, cols=C, seed=23)
+    x = w["x"].copy()
+    x[0, :] = 2.5                                   # constant row: y = beta, rstd = 1/sqrt(eps)
+    x[1, :C // 2] = -7.0                            # two-valued row across the segments
+    x[1, C // 2:] = 9.0
+    got = run_ln_split(x, w["gamma"], w["beta"], w.eps)
+    expect_layernorm(x, w["gamma"], w["beta"], w.eps, got, "split layernorm special rows")
+    assert np.array_equal(got[0][0], w["beta"])
+    w = workloads.make("add_rmsnorm_bf16", rows=2, cols=C, seed=24, dtype="f32")
+    xr = w["x"].copy()
+    rr = w["residual"].copy()
+    rr[0] = -xr[0]                                  # h = 0: y = 0
+    got = run_rms_split(xr, rr, w["weight"], w.eps)
+    expect_rmsnorm(xr, rr, w["weight"], w.eps, got, "split add_rmsnorm zero row")
+    assert np.all(got[0][0] == 0)
+
+
+def test_norm_split_determinism_and_convenience():
+    w = workloads.make("layernorm_f32", rows=8, cols=200000, seed=25, dtype="bf16")
+    a = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps)
+    b = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps)
+    assert all(np.array_equal(p, q) for p, q in zip(a, b))
+    y, m, r = fr.layernorm(upload(w["x"]), upload(w["gamma"]), upload(w["beta"]), w.eps)
+    assert np.array_equal(host(y), a[0]) and np.array_equal(m.cpu().numpy(), a[1])
+    w = workloads.make("add_rmsnorm_bf16", rows=2, cols=100000, seed=26)
+    y, ro = fr.add_rmsnorm(upload(w["x"]), upload(w["residual"]), upload(w["weight"]), w.eps)
+    expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, (host(y), host(ro)),
+                   "add_rmsnorm() of a wide row")

@@ -111,3 +111,45 @@ def test_bitwise_determinism():
     w = workloads.make_attention(2, 2, 512, 512, 128, seed=12)
     r = [run(w, True, 0.0883883) for _ in range(3)]
     assert all(np.array_equal(r[0][0], x[0]) and np.array_equal(r[0][1], x[1]) for x in r)
+
+
+def test_rising_scores_rescale_every_block():
+    # scores rise by ~11 (base 2) from one 32-key block to the next, so the
+    # running max is raised and the accumulator rescaled on every block
+    B, H, S, D = 1, 2, 512, 64
+    rng = np.random.default_rng(13)
+    q = np.full((B, H, S, D), 4.0, np.float32)
+    k = np.repeat((4.0 * np.arange(S) / S).astype(np.float32)[None, None, :, None], D, axis=3)
+    k = np.broadcast_to(k, (B, H, S, D)).copy()
+    v = rng.normal(0, 1, size=(B, H, S, D)).astype(np.float32)
+    w = workloads.Workload(workloads.make_attention(1, 1, 1, 1, 64).spec, 0, 0, 0,
+                           {n: oracle.round_bf16(a) for n, a in (("q", q), ("k", k), ("v", v))})
+    for causal in (False, True):
+        expect(w, causal, 0.125, run(w, causal, 0.125), f"attn rising scores causal={causal}")
+
+
+def test_bench_shape_sampled():
+    # the benchmarked shape (B=4 H=16 S=4096 D=128): sampled queries of two
+    # heads against the oracle
+    w = workloads.make_attention(4, 16, 4096, 4096, 128)
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    for causal in (False, True):
+        ob, lg = run(w, causal, scale)
+        ob = ob.reshape(4, 16, 4096, 128)
+        rows = np.array([0, 31, 32, 127, 128, 2049, 4095])
+        for b, h in ((0, 0), (3, 15)):
+            sub = workloads.Workload(w.spec, 0, 0, 0, {"q": w["q"][b:b + 1, h:h + 1, rows],
+                                                       "k": w["k"][b:b + 1, h:h + 1],
+                                                       "v": w["v"][b:b + 1, h:h + 1]})
+            if causal:
+                # a sampled query i sees keys j <= i: compare query by query
+                for r_i, r in enumerate(rows):
+                    one = workloads.Workload(w.spec, 0, 0, 0, {
+                        "q": sub["q"][:, :, r_i:r_i + 1], "k": sub["k"][:, :, :r + 1],
+                        "v": sub["v"][:, :, :r + 1]})
+                    expect(one, False, scale, (ob[b:b + 1, h:h + 1, r:r + 1],
+                                               lg[b:b + 1, h:h + 1, r:r + 1]),
+                           f"attn bench shape causal b{b} h{h} q{r}")
+            else:
+                expect(sub, False, scale, (ob[b:b + 1, h:h + 1, rows], lg[b:b + 1, h:h + 1, rows]),
+                       f"attn bench shape b{b} h{h}")

@@ -214,6 +214,8 @@ def launch_stats(w, us):
         "gbps": round(w.bytes / (med * 1e-6) / 1e9, 1),
         "pct_peak": round(100 * w.bytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(w.R / (med * 1e-6), 1),
+        "dtype": "bf16" if w.code == 1 else "f32",
+        "seed": w.w.seed,
         "input_sha256": w.w.digest()[:16],
     }
 
@@ -334,39 +336,102 @@ def copy_ceiling(torch, fr, dev, nbytes=2 << 30, reps=20):
 
 def cpu_baseline(wls, budget_s=15.0):
     """The oracle (plain double-precision C, OpenMP over rows) on the host
-    cores over the same inputs: full steps, repeated while within budget."""
+    cores over the same inputs: full steps, repeated while within budget.
+    Returns the baseline record and the last step's oracle outputs."""
     import oracle
     oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
     threads = oracle.threads()
     total_bytes = sum(w.bytes for w in wls)
 
     def one_step():
+        out = {}
         for w in wls:
             a = w.w
             if w.name in ("softmax_f32", "softmax_bf16"):
-                oracle.softmax(a["x"])
+                out[w.name] = (oracle.softmax(a["x"]),)
             elif w.name == "layernorm_f32":
-                oracle.layernorm(a["x"], a["gamma"], a["beta"], a.eps)
+                out[w.name] = oracle.layernorm(a["x"], a["gamma"], a["beta"], a.eps)
             elif w.name == "add_rmsnorm_bf16":
                 y, h, _ = oracle.add_rmsnorm(a["x"], a["residual"], a["weight"], a.eps)
-                oracle.round_bf16(y)
-                oracle.round_bf16(h)
+                out[w.name] = (oracle.round_bf16(y), oracle.round_bf16(h))
             elif w.name == "xent_f32":
-                oracle.softmax_xent(a["logits"], a["labels"])
+                out[w.name] = oracle.softmax_xent(a["logits"], a["labels"])[:2]
+        return out
 
     t0 = time.perf_counter()
     n = 0
     while True:
-        one_step()
+        outs = one_step()
         n += 1
         el = time.perf_counter() - t0
         if el > budget_s / 2 or n >= 3:
             break
     per_step = el / n
-    return {"value": total_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} full step(s): all rows of the five workloads, "
-                      f"{per_step:.2f} s per step, double precision, {threads} OpenMP threads"}
+    return ({"value": total_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
+             "kind": "oracle",
+             "sample": f"{n} full step(s): all rows of the five workloads, "
+                       f"{per_step:.2f} s per step, double precision, {threads} OpenMP threads"},
+            outs)
+
+
+def parity_report(wls, outs):
+    """The timed step's GPU outputs (every element) against the oracle's, by
+    the tests' rules: fp32 |g - o| <= 1e-5 * scale + 2^-126 (scale |o|, or
+    max(|o|, 1) for LayerNorm y and the losses, max(|o|, row sd) for the mean,
+    max(|o|, p) at the label), bf16 within one ulp of the rounded oracle."""
+    import numpy as np
+    tiny = 2.0 ** -126
+
+    def f32(g, o, scale=None):
+        g = g.astype(np.float64)
+        sc = np.abs(o) if scale is None else scale
+        err = np.abs(g - o)
+        return {"max_abs": float(err.max()), "max_rel": float((err / np.maximum(sc, tiny)).max()),
+                "pass": bool(np.all(err <= 1e-5 * sc + tiny))}
+
+    def ordered(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+
+    def bf16(g_t, o_bits):
+        import torch
+        gb = g_t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        d = np.abs(ordered(gb) - ordered(o_bits))
+        return {"ulp_hist": {"0": int((d == 0).sum()), "1": int((d == 1).sum()),
+                             ">1": int((d > 1).sum())}, "pass": bool(d.max() <= 1)}
+
+    import oracle
+    rep = {}
+    for w in wls:
+        o = outs[w.name]
+        a = w.w
+        if w.name == "softmax_f32":
+            r = f32(w.y.cpu().numpy(), o[0])
+            r["denormal_count"] = int(((o[0] > 0) & (o[0] < tiny)).sum())
+        elif w.name == "softmax_bf16":
+            r = bf16(w.y, oracle.round_bf16(o[0]))
+            r["denormal_count"] = int(((o[0] > 0) & (o[0] < tiny)).sum())
+        elif w.name == "layernorm_f32":
+            yo, mo, ro = o
+            sd = np.sqrt(oracle.decode(a["x"]).var(axis=1))
+            r = {"y": f32(w.y.cpu().numpy(), yo, np.maximum(np.abs(yo), 1.0)),
+                 "mean": f32(w.mean.cpu().numpy(), mo, np.maximum(np.abs(mo), sd)),
+                 "rstd": f32(w.rstd.cpu().numpy(), ro)}
+            r["pass"] = all(v["pass"] for v in r.values())
+        elif w.name == "add_rmsnorm_bf16":
+            r = {"y": bf16(w.y, o[0]), "residual_out": bf16(w.ro, o[1])}
+            r["pass"] = all(v["pass"] for v in r.values())
+        elif w.name == "xent_f32":
+            lo, go = o
+            lab = a["labels"].astype(np.int64)
+            rows = np.arange(len(lab))
+            sc = np.abs(go)
+            sc[rows, lab] = np.maximum(sc[rows, lab], go[rows, lab] + 1.0)
+            r = {"loss": f32(w.loss.cpu().numpy(), lo, np.maximum(np.abs(lo), 1.0)),
+                 "grad": f32(w.grad.cpu().numpy(), go, sc)}
+            r["pass"] = all(v["pass"] for v in r.values())
+        rep[w.name] = r
+    return rep
 
 
 def main():
@@ -480,6 +545,12 @@ def main():
 
     ceiling = copy_ceiling(torch, fr, dev)
     log(f"copy ceiling {ceiling:.0f} GB/s")
+    for v in per.values():
+        v["pct_copy_ceiling"] = round(100 * v["gbps"] / ceiling, 1)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "memory_gib": round(props.total_memory / 2 ** 30, 1)}
     dom = per[DOMINANT]
     achieved = dom["algo_bytes"] / (dom["mean_us"] * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -505,6 +576,7 @@ def main():
             "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
             "pct_of_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             "copy_ceiling_gbps": round(ceiling, 1),
+            "device": device,
             "storage": "fp32 and bf16 as listed; arithmetic fp32",
             "seeds": [w.w.seed for w in wls],
             "launch": "hip graph replay of the five launches" if graph else "eager launches",
@@ -526,7 +598,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(wls)
+        result["cpu_baseline"], outs = cpu_baseline(wls)
+        log("comparing the timed step's outputs with the oracle's")
+        result["parity"] = parity_report(wls, outs)
+        del outs
     print(json.dumps(result), flush=True)
 
 

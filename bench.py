@@ -25,8 +25,9 @@ forward workloads' shapes (softmax bf16 [16384, 4096], LayerNorm fp32
 cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
 logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
 split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
-[2048, 131072], bf16 [1024, 262144]) and the split-row norms (LayerNorm fp32
-[512, 131072], residual-add + RMSNorm bf16 [256, 262144]); they are
+[2048, 131072], bf16 [1024, 262144]), the split-row norms (LayerNorm fp32
+[512, 131072], residual-add + RMSNorm bf16 [256, 262144]) and the split-row
+softmax backward (bf16 [1024, 131072]); they are
 reported under "backward" and "variants" and are not part of `value`; so is the
 attention forward (bf16 B=4 H=16 S=4096 D=128, causal and not), reported
 under "attention" in matrix TFLOP/s against the bf16 peak. Their per-row inputs from the
@@ -83,6 +84,8 @@ def bwd_algo_bytes(name, R, C):
         # reads the logits twice: 1.5x these bytes move); labels, loss
         es = 4 if name == "xent_split_f32" else 2
         return 2 * R * C * es + 2 * R * 4
+    if name == "softmax_bwd_split_bf16":
+        return 3 * R * C * 2                                   # p, dy; dx (read twice by the path)
     if name == "layernorm_split_f32":
         # x, y; gamma, beta; mean, rstd (the split path reads x twice)
         return 2 * R * C * 4 + 2 * C * 4 + 2 * R * 4
@@ -155,6 +158,15 @@ class BwdWorkload:
                                                         self.ws)
             self.op = fr.OP_XENT_SPLIT
             self.code = fr.BF16 if name == "xent_split_bf16" else fr.F32
+        elif name == "softmax_bwd_split_bf16":
+            # wide softmax backward rows through the split-row path
+            self.p = fr.softmax(d(w["x"]))
+            self.dy = d(w["dy"])
+            self.dx = torch.empty_like(self.p)
+            self.ws = torch.empty(fr.fr_split_workspace_bytes(self.R, self.C), dtype=torch.uint8,
+                                  device=dev)
+            self.run = lambda: fr.fr_softmax_bwd_split(self.p, self.dy, self.dx, self.ws)
+            self.op, self.code = fr.OP_SOFTMAX_BWD_SPLIT, fr.BF16
         elif name == "layernorm_split_f32":
             # wide LayerNorm rows through the split-row path
             self.x, self.g, self.b = d(w["x"]), d(w["gamma"]), d(w["beta"])
@@ -527,7 +539,8 @@ def main():
                                    torch, fr))
             log(f"generated {n}")
         for n, base, dt, R, C in (("layernorm_split_f32", "layernorm_f32", "f32", 512, 131072),
-                                  ("add_rmsnorm_split_bf16", "add_rmsnorm_bf16", "bf16", 256, 262144)):
+                                  ("add_rmsnorm_split_bf16", "add_rmsnorm_bf16", "bf16", 256, 262144),
+                                  ("softmax_bwd_split_bf16", "softmax_bwd_bf16", "bf16", 1024, 131072)):
             bws.append(BwdWorkload(n, workloads.make(base, rows=R, cols=C, dtype=dt), dev, torch, fr))
             log(f"generated {n}")
         for _ in range(max(3, args.warmup)):

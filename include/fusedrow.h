@@ -71,7 +71,8 @@ typedef enum {
   FR_OP_SOFTMAX_SPLIT = 7,
   FR_OP_XENT_SPLIT = 8,
   FR_OP_LAYERNORM_SPLIT = 9,
-  FR_OP_RMSNORM_SPLIT = 10
+  FR_OP_RMSNORM_SPLIT = 10,
+  FR_OP_SOFTMAX_BWD_SPLIT = 11
 } fr_op_t;
 
 typedef enum {
@@ -256,6 +257,19 @@ FR_API fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual,
                                             int64_t rows, int64_t cols, float eps,
                                             fr_dtype_t dtype, void* workspace,
                                             int64_t workspace_bytes, void* stream);
+
+/* Softmax backward for rows of any width, split as fr_softmax_fwd_split:
+ * pass 1 writes each segment's sum of p * dy to `workspace`, pass 2 adds a
+ * row's sums in segment order and writes dx = p (dy - s). Reads p and dy
+ * twice, writes dx once.
+ *   ("NexusGrad", Verified VJP Operators: the softmax vector-Jacobian
+ *    product.)
+ * Arguments and results as fr_softmax_bwd (dx may equal p or dy), with
+ * 1 <= cols <= FR_SPLIT_MAX_COLS, plus the workspace as
+ * fr_softmax_fwd_split. */
+FR_API fr_status_t fr_softmax_bwd_split(const void* p, const void* dy, void* dx, int64_t rows,
+                                        int64_t cols, fr_dtype_t dtype, void* workspace,
+                                        int64_t workspace_bytes, void* stream);
 
 /* ---- the online softmax inside attention ---- */
 

@@ -24,6 +24,7 @@ __all__ = [
     "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
     "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS", "fr_attention_fwd", "attention",
     "fr_layernorm_fwd_split", "fr_add_rmsnorm_fwd_split", "OP_LAYERNORM_SPLIT", "OP_RMSNORM_SPLIT",
+    "fr_softmax_bwd_split", "OP_SOFTMAX_BWD_SPLIT",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
     "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
@@ -34,7 +35,7 @@ F32, BF16 = 0, 1
 OP_SOFTMAX, OP_LAYERNORM, OP_RMSNORM, OP_XENT = 0, 1, 2, 3
 OP_SOFTMAX_BWD, OP_RMSNORM_BWD, OP_LAYERNORM_BWD = 4, 5, 6
 OP_SOFTMAX_SPLIT, OP_XENT_SPLIT = 7, 8
-OP_LAYERNORM_SPLIT, OP_RMSNORM_SPLIT = 9, 10
+OP_LAYERNORM_SPLIT, OP_RMSNORM_SPLIT, OP_SOFTMAX_BWD_SPLIT = 9, 10, 11
 FR_SPLIT_MAX_COLS = 1 << 24
 FR_MAX_COLS = 65536
 FR_BWD_MAX_COLS = 16384
@@ -89,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "fr_softmax_fwd_split": [P, P, I64, I64, I32, I32, P, I64, P],
         "fr_layernorm_fwd_split": [P, P, P, P, P, P, I64, I64, F, I32, P, I64, P],
         "fr_add_rmsnorm_fwd_split": [P, P, P, P, P, I64, I64, F, I32, P, I64, P],
+        "fr_softmax_bwd_split": [P, P, P, I64, I64, I32, P, I64, P],
         "fr_attention_fwd": [P, P, P, P, P, I64, I64, I64, I64, I64, I32, F, I32, P],
         "fr_softmax_xent_split": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P,
                                   I64, P],
@@ -330,6 +332,19 @@ def fr_add_rmsnorm_fwd_split(x, residual, weight, y, workspace, residual_out=Non
     _check(lib.fr_add_rmsnorm_fwd_split(_ptr(x), _ptr(residual), _ptr(weight), _ptr(y),
                                         _ptr(residual_out), R, C, float(eps), _dtype_code(x), wp, wn,
                                         _stream(stream, x)), "fr_add_rmsnorm_fwd_split")
+
+
+def fr_softmax_bwd_split(p, dy, dx, workspace, stream=None) -> None:
+    """Softmax backward for rows of any width, several workgroups per row
+    (C: fr_softmax_bwd_split)."""
+    _need_cuda(p, dy, dx)
+    R, C = _rows_cols(p)
+    for t, n in ((dy, "dy"), (dx, "dx")):
+        if tuple(t.shape) != (R, C) or not t.is_contiguous() or t.dtype != p.dtype:
+            raise ValueError(f"{n} must be a contiguous tensor of p's shape and dtype")
+    wp, wn = _workspace_arg(workspace)
+    _check(lib.fr_softmax_bwd_split(_ptr(p), _ptr(dy), _ptr(dx), R, C, _dtype_code(p), wp, wn,
+                                    _stream(stream, p)), "fr_softmax_bwd_split")
 
 
 def fr_softmax_xent_split(logits, labels, loss, grad, workspace, argmax=None, loss_total=None,
@@ -578,9 +593,13 @@ def _workspace(op, rows, cols, device):
 
 
 def softmax_bwd(p, dy, out=None):
+    """dx = p (dy - sum(p dy)); rows wider than FR_BWD_MAX_COLS take the split-row path."""
     torch = _torch()
     dx = out if out is not None else torch.empty_like(p)
-    fr_softmax_bwd(p, dy, dx)
+    if p.shape[1] > FR_BWD_MAX_COLS:
+        fr_softmax_bwd_split(p, dy, dx, _split_workspace(p.shape[0], p.shape[1], p.device))
+    else:
+        fr_softmax_bwd(p, dy, dx)
     return dx
 
 

@@ -20,7 +20,7 @@ struct Forced {
   std::atomic<int> threads{0};
   std::atomic<int> vecs{0};
 };
-Forced g_forced[FR_OP_RMSNORM_SPLIT + 1];
+Forced g_forced[FR_OP_SOFTMAX_BWD_SPLIT + 1];
 
 // ------------------------------------------------------------------- buffers
 struct Buf {
@@ -140,7 +140,7 @@ const char* fr_status_str(fr_status_t s) {
 const char* fr_version(void) { return "fusedrow 0.1.0 (gfx950)"; }
 
 fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs) {
-  if (op < FR_OP_SOFTMAX || op > FR_OP_RMSNORM_SPLIT) return FR_E_VALUE;
+  if (op < FR_OP_SOFTMAX || op > FR_OP_SOFTMAX_BWD_SPLIT) return FR_E_VALUE;
   if (threads < 0 || vecs < 0) return FR_E_VALUE;
   g_forced[op].vecs.store(threads ? vecs : 0);
   g_forced[op].threads.store(threads);
@@ -153,7 +153,8 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
   if (!threads || !vecs || !elems_per_vec) return FR_E_NULL;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return FR_E_DTYPE;
   const bool split = op == FR_OP_SOFTMAX_SPLIT || op == FR_OP_XENT_SPLIT ||
-                     op == FR_OP_LAYERNORM_SPLIT || op == FR_OP_RMSNORM_SPLIT;
+                     op == FR_OP_LAYERNORM_SPLIT || op == FR_OP_RMSNORM_SPLIT ||
+                     op == FR_OP_SOFTMAX_BWD_SPLIT;
   const int64_t maxc = split ? FR_SPLIT_MAX_COLS : FR_MAX_COLS;
   if (cols < 1 || cols > maxc) return FR_E_SHAPE;
   const int epv = vector_path ? vec_epv(esize(in_dtype)) : 1;
@@ -207,6 +208,11 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
       auto v = select_split(fr::split_variants(in_dtype == FR_BF16, out_dtype == FR_BF16,
                                                op == FR_OP_XENT_SPLIT),
                             op, epv);
+      if (v) { t = v->threads; n = v->nv; e = v->epv; }
+      break;
+    }
+    case FR_OP_SOFTMAX_BWD_SPLIT: {
+      auto v = select_split(fr::softmax_bwd_split_variants(in_dtype == FR_BF16), op, epv);
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -661,6 +667,30 @@ fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual, const 
   if (!v) return FR_E_VARIANT;
   return launch_status(v->launch(x, residual, weight, nullptr, y, residual_out, nullptr, nullptr,
                                  rows, (int)cols, eps, static_cast<float4*>(workspace),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_softmax_bwd_split(const void* p, const void* dy, void* dx, int64_t rows,
+                                 int64_t cols, fr_dtype_t dtype, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  if (fr_status_t s = check_split(rows, cols, workspace, workspace_bytes)) return s;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (rows == 0) return FR_OK;
+  if (!p || !dy || !dx) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(p, es) || !aligned(dy, es) || !aligned(dx, es)) return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(p, nb, true, es, false), make_buf(dy, nb, true, es, false),
+                      make_buf(dx, nb, true, es, true),
+                      make_buf(workspace, fr_split_workspace_bytes(rows, cols), false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 4)) return s;
+  const uintptr_t ph = reinterpret_cast<uintptr_t>(p) % 16;
+  const bool vec = reinterpret_cast<uintptr_t>(dy) % 16 == ph &&
+                   reinterpret_cast<uintptr_t>(dx) % 16 == ph;
+  const fr::SoftmaxBwdSplitVariant* v = select_split(
+      fr::softmax_bwd_split_variants(dtype == FR_BF16), FR_OP_SOFTMAX_BWD_SPLIT, vec ? vec_epv(es) : 1);
+  if (!v) return FR_E_VARIANT;
+  return launch_status(v->launch(p, dy, dx, rows, (int)cols, static_cast<float4*>(workspace),
                                  static_cast<hipStream_t>(stream)));
 }
 

@@ -93,6 +93,10 @@ typedef hipError_t (*NormSplitLaunch)(const void* x, const void* res, const void
                                       float* rstd, int64_t rows, int cols, float eps, float4* part,
                                       hipStream_t s);
 
+// Split-row softmax backward (pass 1 segment sums of p * dy into `part`).
+typedef hipError_t (*SoftmaxBwdSplitLaunch)(const void* p, const void* dy, void* dx, int64_t rows,
+                                            int cols, float4* part, hipStream_t s);
+
 typedef Variant<SoftmaxLaunch> SoftmaxVariant;
 typedef Variant<LayerNormLaunch> LayerNormVariant;
 typedef Variant<RmsNormLaunch> RmsNormVariant;
@@ -100,6 +104,7 @@ typedef Variant<XentLaunch> XentVariant;
 typedef Variant<SoftmaxBwdLaunch> SoftmaxBwdVariant;
 typedef Variant<SplitLaunch> SplitVariant;
 typedef Variant<NormSplitLaunch> NormSplitVariant;
+typedef Variant<SoftmaxBwdSplitLaunch> SoftmaxBwdSplitVariant;
 typedef BwdVariant<RmsNormBwdLaunch> RmsNormBwdVariant;
 typedef BwdVariant<LayerNormBwdLaunch> LayerNormBwdVariant;
 
@@ -110,6 +115,7 @@ VariantSpan<XentVariant> xent_variants(int bf16, int with_argmax);
 VariantSpan<XentVariant> xent_ex_variants(int bf16, int with_argmax);
 VariantSpan<SplitVariant> split_variants(int in_bf16, int out_bf16, int xent);
 VariantSpan<NormSplitVariant> norm_split_variants(int bf16, int rms);
+VariantSpan<SoftmaxBwdSplitVariant> softmax_bwd_split_variants(int bf16);
 hipError_t launch_xent_count(const int32_t* labels, int64_t rows, int use_ignore, int ignore_index,
                              uint32_t* out, hipStream_t s);
 hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* count, float* total,

@@ -1,5 +1,5 @@
-// Split-row softmax and softmax cross-entropy: rows of any width up to 2^24,
-// several workgroups per row.
+// Split-row softmax, softmax cross-entropy and softmax backward: rows of any
+// width up to 2^24, several workgroups per row.
 //
 // A row is cut into segments of `seg` columns (a multiple of 32, so every
 // segment keeps its row's address phase); workgroup (row, segment) owns one
@@ -275,6 +275,79 @@ void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, 
   }
 }
 
+// ------------------------------------------------ softmax backward, split
+// dx = p (dy - s), s = sum_j p_j dy_j: pass 1 writes each segment's sum of
+// p * dy, pass 2 adds the row's segment sums in segment order (the same bits
+// in every workgroup of the row), re-reads p and dy and writes dx.
+
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int cols, int seg,
+                                    int nseg, float4* part) {
+  constexpr int NW = T / 64;
+  __shared__ float xw[2][NW][1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t work = rows * nseg;
+  int it = 0;
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+    const int64_t row = w / nseg;
+    const Segment sgm((int)(w - row * nseg), seg, cols);
+    const int64_t off = row * cols + sgm.c0;
+    const RowGeom<EPV> g(p + off, sgm.len);
+    const int ec = g.extra_col(tid);
+    float a[NV][EPV], d[NV][EPV];
+    load_chunks2<Ts, T, NV, EPV>(p + off, dy + off, g, tid, a, d, 0.f);
+    float s0 = load_extra(p + off, ec, 0.f) * load_extra(dy + off, ec, 0.f), s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        if (k & 1) s1 = __builtin_fmaf(a[i][k], d[i][k], s1);
+        else s0 = __builtin_fmaf(a[i][k], d[i][k], s0);
+      }
+    SumState st{s0 + s1};
+    st = wave_reduce(st, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+    if (tid == 0) part[w] = float4{st.s, 0.f, 0.f, 0.f};
+  }
+}
+
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_split_apply_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int cols,
+                                    int seg, int nseg, const float4* part) {
+  constexpr int NW = T / 64;
+  __shared__ float xw[2][NW][1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t work = rows * nseg;
+  int it = 0;
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+    const int64_t row = w / nseg;
+    const Segment sgm((int)(w - row * nseg), seg, cols);
+    SumState st{0.f};
+    for (int j = tid; j < nseg; j += T) st.s += part[row * nseg + j].x;
+    st = wave_reduce(st, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+    const float s = st.s;
+    const int64_t off = row * cols + sgm.c0;
+    const RowGeom<EPV> g(p + off, sgm.len);
+    const int ec = g.extra_col(tid);
+    float a[NV][EPV], d[NV][EPV];
+    load_chunks2<Ts, T, NV, EPV>(p + off, dy + off, g, tid, a, d, 0.f);
+    const float ae = load_extra(p + off, ec, 0.f), de = load_extra(dy + off, ec, 0.f);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) a[i][k] = a[i][k] * (d[i][k] - s);
+    store_chunks<Ts, T, NV, EPV>(dx + off, g, tid, a);
+    if (ec >= 0) store1(dx + off + ec, ae * (de - s));
+  }
+}
+
 // --------------------------------------------------------------- launchers
 
 static unsigned split_grid(int64_t work) {
@@ -303,6 +376,21 @@ static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, c
                        static_cast<const float4*>(part), labels, loss, argmax, o);
 }
 
+template <typename Ts, int T, int NV, int EPV, int OCC>
+static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* dx, int64_t rows,
+                                           int cols, float4* part, hipStream_t s) {
+  constexpr int SEG = T * NV * EPV;
+  const int nseg = (cols + SEG - 1) / SEG;
+  const unsigned grid = split_grid(rows * nseg);
+  hipError_t e = launch_kernel(&softmax_bwd_split_stats_kernel<Ts, T, NV, EPV, OCC>, dim3(grid),
+                               dim3(T), s, static_cast<const Ts*>(p), static_cast<const Ts*>(dy),
+                               rows, cols, SEG, nseg, part);
+  if (e != hipSuccess) return e;
+  return launch_kernel(&softmax_bwd_split_apply_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(T), s,
+                       static_cast<const Ts*>(p), static_cast<const Ts*>(dy), static_cast<Ts*>(dx),
+                       rows, cols, SEG, nseg, static_cast<const float4*>(part));
+}
+
 #define FR_SP(TI, TO, T, NV, EPV, OCC, X) {T, NV, EPV, &launch_split<TI, TO, T, NV, EPV, OCC, X>}
 // Segment shapes, 32 elements per lane: 256 lanes (8192 columns, the
 // default: several workgroups per CU overlap one segment's loads with
@@ -319,7 +407,19 @@ static const SplitVariant kSpBf16F32[] = FR_SP_TABLE(bf16_t, float, 8, false);
 static const SplitVariant kSpXeF32[] = FR_SP_TABLE(float, float, 4, true);
 static const SplitVariant kSpXeBf16[] = FR_SP_TABLE(bf16_t, bf16_t, 8, true);
 
+#define FR_SB_SPLIT(TS, T, NV, EPV) {T, NV, EPV, &launch_softmax_bwd_split<TS, T, NV, EPV, 4>}
+#define FR_SB_SPLIT_TABLE(TS, E)                                                      \
+  {FR_SB_SPLIT(TS, 256, 32 / E, E), FR_SB_SPLIT(TS, 512, 32 / E, E),                   \
+   FR_SB_SPLIT(TS, 1024, 32 / E, E), FR_SB_SPLIT(TS, 256, 32, 1)}
+static const SoftmaxBwdSplitVariant kSbSpF32[] = FR_SB_SPLIT_TABLE(float, 4);
+static const SoftmaxBwdSplitVariant kSbSpBf16[] = FR_SB_SPLIT_TABLE(bf16_t, 8);
+
 #define FR_SPAN(a) {a, sizeof(a) / sizeof(a[0])}
+
+VariantSpan<SoftmaxBwdSplitVariant> softmax_bwd_split_variants(int bf16) {
+  return bf16 ? VariantSpan<SoftmaxBwdSplitVariant>FR_SPAN(kSbSpBf16)
+              : VariantSpan<SoftmaxBwdSplitVariant>FR_SPAN(kSbSpF32);
+}
 
 VariantSpan<SplitVariant> split_variants(int in_bf16, int out_bf16, int xent) {
   if (xent) return in_bf16 ? VariantSpan<SplitVariant>FR_SPAN(kSpXeBf16)

@@ -255,6 +255,25 @@ def test_split_norm_validation():
     assert rn(ws=RO) == E_ALIAS                        # workspace over residual_out
 
 
+def test_softmax_bwd_split_validation():
+    f = fr.lib.fr_softmax_bwd_split
+    DY, DX, WS = A + 0x100000, A + 0x200000, A + 0x300000
+    need = fr.fr_split_workspace_bytes(4, 100000)
+
+    def call(p=A, dy=DY, dx=DX, rows=4, cols=100000, dt=0, ws=WS, wn=need):
+        return f(P(p), P(dy), P(dx), rows, cols, dt, P(ws), wn, None)
+
+    assert call(rows=0, ws=0, wn=0) == OK
+    assert call(wn=need - 1) == E_SHAPE
+    assert call(cols=0) == E_SHAPE
+    assert call(dy=0) == E_NULL
+    assert call(ws=0) == E_NULL
+    assert call(dt=5) == E_DTYPE
+    assert call(dx=DX + 2) == E_ALIGN
+    assert call(dx=A + 4) == E_ALIAS
+    assert call(ws=DX + 64) == E_ALIAS
+
+
 def test_attention_validation():
     f = fr.lib.fr_attention_fwd
     K, V, O, LSE = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
@@ -303,7 +322,8 @@ def test_variant_selection():
             with pytest.raises(fr.FusedRowError) as ei:
                 fr.fr_debug_select_variant(op, fr.FR_BWD_MAX_COLS + 1, dt)
             assert ei.value.status == E_SHAPE
-    for op in (fr.OP_SOFTMAX_SPLIT, fr.OP_XENT_SPLIT, fr.OP_LAYERNORM_SPLIT, fr.OP_RMSNORM_SPLIT):
+    for op in (fr.OP_SOFTMAX_SPLIT, fr.OP_XENT_SPLIT, fr.OP_LAYERNORM_SPLIT, fr.OP_RMSNORM_SPLIT,
+               fr.OP_SOFTMAX_BWD_SPLIT):
         for dt in (fr.F32, fr.BF16):
             for vp in (True, False):
                 t, v, e = fr.fr_debug_select_variant(op, 262144, dt, vector_path=vp)
@@ -316,7 +336,7 @@ def test_variant_selection():
             fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32)
         assert ei.value.status == E_VARIANT
     with pytest.raises(fr.FusedRowError):
-        fr.fr_debug_force_variant(11, 64, 1)
+        fr.fr_debug_force_variant(12, 64, 1)
 
 
 def test_binding_rejects_host_tensors():

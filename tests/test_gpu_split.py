@@ -340,3 +340,58 @@ def test_norm_split_determinism_and_convenience():
     y, ro = fr.add_rmsnorm(upload(w["x"]), upload(w["residual"]), upload(w["weight"]), w.eps)
     expect_rmsnorm(w["x"], w["residual"], w["weight"], w.eps, (host(y), host(ro)),
                    "add_rmsnorm() of a wide row")
+
+
+# ---------------------------------------------------------- softmax backward
+
+from test_gpu_backward import expect_softmax_bwd, softmax_bwd_inputs  # noqa: E402
+
+
+def run_softmax_bwd_split(p, dy, offs=(0, 0, 0), inplace=None):
+    R, C = p.shape
+    pt, dyt = upload(p, offs[0]), upload(dy, offs[1])
+    ws = workspace(R, C)
+    if inplace:
+        tgt = pt if inplace == "p" else dyt
+        fr.fr_softmax_bwd_split(pt, dyt, tgt, ws.t)
+        torch.cuda.synchronize()
+        assert ws.canaries_intact()
+        return host(tgt)
+    dx = Guarded((R, C), pt.dtype, offs[2])
+    fr.fr_softmax_bwd_split(pt, dyt, dx.t, ws.t)
+    torch.cuda.synchronize()
+    assert dx.canaries_intact() and ws.canaries_intact(), "split softmax_bwd wrote out of bounds"
+    return host(dx.t)
+
+
+@pytest.mark.parametrize("C", [1, 7, 8192, 8193, 16385, 65537, 262144])
+@pytest.mark.parametrize("code", [fr.F32, fr.BF16])
+def test_softmax_bwd_split_widths(C, code):
+    for R in (1, 3):
+        p, dy = softmax_bwd_inputs(R, C, code, seed=C + R)
+        expect_softmax_bwd(p, dy, code, run_softmax_bwd_split(p, dy), f"split softmax_bwd {code} {R}x{C}")
+
+
+def test_softmax_bwd_split_shapes_in_place_misaligned():
+    for t, v in SEG_SHAPES:
+        for code in (fr.F32, fr.BF16):
+            for vp, offs in ((True, (0, 0, 0)), (False, (1, 2, 0))):
+                try:
+                    with fr.forced_variant(fr.OP_SOFTMAX_BWD_SPLIT, t, v):
+                        tt, vv, e = fr.fr_debug_select_variant(fr.OP_SOFTMAX_BWD_SPLIT, 1, code,
+                                                               vector_path=vp)
+                except fr.FusedRowError:
+                    continue
+                C = 2 * tt * vv * e + 37
+                p, dy = softmax_bwd_inputs(2, C, code, seed=C + t)
+                with fr.forced_variant(fr.OP_SOFTMAX_BWD_SPLIT, t, v):
+                    got = run_softmax_bwd_split(p, dy, offs)
+                expect_softmax_bwd(p, dy, code, got, f"split softmax_bwd [{t},{v},{vp}] {code} 2x{C}")
+    for code in (fr.F32, fr.BF16):
+        p, dy = softmax_bwd_inputs(3, 100003, code, seed=31)
+        for ip in ("p", "dy"):
+            expect_softmax_bwd(p, dy, code, run_softmax_bwd_split(p, dy, inplace=ip),
+                               f"split softmax_bwd in place ({ip}) {code}")
+    p, dy = softmax_bwd_inputs(2, 70000, fr.F32, seed=32)
+    dx = fr.softmax_bwd(upload(p), upload(dy))
+    expect_softmax_bwd(p, dy, fr.F32, dx.cpu().numpy(), "softmax_bwd() of a wide row")

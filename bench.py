@@ -26,8 +26,10 @@ cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
 logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
 split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
 [2048, 131072], bf16 [1024, 262144]), the split-row norms (LayerNorm fp32
-[512, 131072], residual-add + RMSNorm bf16 [256, 262144]) and the split-row
-softmax backward (bf16 [1024, 131072]); they are
+[512, 131072], residual-add + RMSNorm bf16 [256, 262144]), the split-row
+softmax backward (bf16 [1024, 131072]) and the split-row residual-add +
+RMSNorm backward (bf16 [2048, 32768], hidden size beyond the one-pass
+backward); they are
 reported under "backward" and "variants" and are not part of `value`; so is the
 attention forward (bf16 B=4 H=16 S=4096 D=128, causal and not), reported
 under "attention" in matrix TFLOP/s against the bf16 peak. Their per-row inputs from the
@@ -84,6 +86,8 @@ def bwd_algo_bytes(name, R, C):
         # reads the logits twice: 1.5x these bytes move); labels, loss
         es = 4 if name == "xent_split_f32" else 2
         return 2 * R * C * es + 2 * R * 4
+    if name == "add_rmsnorm_bwd_split_bf16":
+        return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
     if name == "softmax_bwd_split_bf16":
         return 3 * R * C * 2                                   # p, dy; dx (read twice by the path)
     if name == "layernorm_split_f32":
@@ -158,6 +162,20 @@ class BwdWorkload:
                                                         self.ws)
             self.op = fr.OP_XENT_SPLIT
             self.code = fr.BF16 if name == "xent_split_bf16" else fr.F32
+        elif name == "add_rmsnorm_bwd_split_bf16":
+            # hidden size beyond the one-pass backward: the split-row path
+            self.h, self.dy, self.dres = d(w["h"]), d(w["dy"]), d(w["dres"])
+            self.wt = d(w["weight"])
+            self.dh = torch.empty_like(self.h)
+            self.dw = torch.empty(self.C, device=dev)
+            self.ws = torch.empty(fr.fr_norm_bwd_split_workspace_bytes(fr.OP_RMSNORM_BWD, self.R,
+                                                                       self.C),
+                                  dtype=torch.uint8, device=dev)
+            self.run = lambda: fr.fr_add_rmsnorm_bwd_split(self.h, self.dy, self.wt, self.dh,
+                                                           self.dw, self.ws, dres=self.dres,
+                                                           eps=w.eps)
+            # one fixed shape (no variant table): 512 lanes x 2 x 8 per segment
+            self.op, self.code, self.variant = None, fr.BF16, (512, 2, 8)
         elif name == "softmax_bwd_split_bf16":
             # wide softmax backward rows through the split-row path
             self.p = fr.softmax(d(w["x"]))
@@ -196,7 +214,8 @@ class BwdWorkload:
             self.run = lambda: fr.fr_add_rmsnorm_bwd(self.h, self.dy, self.wt, self.dh, self.dw,
                                                      self.ws, dres=self.dres, eps=w.eps)
             self.op, self.code = fr.OP_RMSNORM_BWD, fr.BF16
-        self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
+        if self.op is not None:
+            self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
 
 
 def time_calls(torch, np, runs, K):
@@ -540,7 +559,9 @@ def main():
             log(f"generated {n}")
         for n, base, dt, R, C in (("layernorm_split_f32", "layernorm_f32", "f32", 512, 131072),
                                   ("add_rmsnorm_split_bf16", "add_rmsnorm_bf16", "bf16", 256, 262144),
-                                  ("softmax_bwd_split_bf16", "softmax_bwd_bf16", "bf16", 1024, 131072)):
+                                  ("softmax_bwd_split_bf16", "softmax_bwd_bf16", "bf16", 1024, 131072),
+                                  ("add_rmsnorm_bwd_split_bf16", "add_rmsnorm_bwd_bf16", "bf16", 2048,
+                                   32768)):
             bws.append(BwdWorkload(n, workloads.make(base, rows=R, cols=C, dtype=dt), dev, torch, fr))
             log(f"generated {n}")
         for _ in range(max(3, args.warmup)):

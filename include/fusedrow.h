@@ -358,6 +358,41 @@ FR_API fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* g
                              int64_t workspace_bytes, int64_t rows, int64_t cols,
                              fr_dtype_t dtype, void* stream);
 
+/* ---- backward of the norms for rows of any width ---- */
+
+/* Bytes of device workspace fr_add_rmsnorm_bwd_split (op FR_OP_RMSNORM_BWD)
+ * or fr_layernorm_bwd_split (FR_OP_LAYERNORM_BWD) needs for [rows, cols]:
+ * the per-segment row sums (rows * ceil(cols / 8192) * 16 bytes, padded to a
+ * multiple of 256) plus G * cols * 4 per parameter gradient, G =
+ * min(rows, max(1, min(512, 1024 / ceil(cols / 8192)))) partial rows. -1 for
+ * another op or an invalid shape (1 <= cols <= FR_SPLIT_MAX_COLS). */
+FR_API int64_t fr_norm_bwd_split_workspace_bytes(fr_op_t op, int64_t rows, int64_t cols);
+
+/* fr_add_rmsnorm_bwd for rows of any width (cols up to FR_SPLIT_MAX_COLS).
+ * A row is cut into segments of 8192 columns: pass 1 writes each segment's
+ * two partial row sums (sum h^2, sum dy weight h); pass 2 — workgroup
+ * (segment, row group) over rows g, g + G, ... — adds a row's partials in
+ * segment order, writes the segment's dh and accumulates its columns'
+ * dweight partials, one partial row per row group; a third kernel adds the
+ * G partial rows in order. Reads h, dy (and dres) twice.
+ * Arguments and results as fr_add_rmsnorm_bwd, with the workspace of
+ * fr_norm_bwd_split_workspace_bytes. Results are bitwise reproducible. */
+FR_API fr_status_t fr_add_rmsnorm_bwd_split(const void* h, const void* dy, const void* dres,
+                                            const void* weight, void* dh, float* dweight,
+                                            void* workspace, int64_t workspace_bytes,
+                                            int64_t rows, int64_t cols, float eps,
+                                            fr_dtype_t dtype, void* stream);
+
+/* fr_layernorm_bwd for rows of any width, split as
+ * fr_add_rmsnorm_bwd_split (the partial row sums are sum g and sum g n).
+ * Arguments and results as fr_layernorm_bwd, with the workspace of
+ * fr_norm_bwd_split_workspace_bytes. */
+FR_API fr_status_t fr_layernorm_bwd_split(const void* x, const void* dy, const void* gamma,
+                                          const float* mean, const float* rstd, void* dx,
+                                          float* dgamma, float* dbeta, void* workspace,
+                                          int64_t workspace_bytes, int64_t rows, int64_t cols,
+                                          fr_dtype_t dtype, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 FR_API const char* fr_status_str(fr_status_t s);
 

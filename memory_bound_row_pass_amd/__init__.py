@@ -24,7 +24,8 @@ __all__ = [
     "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
     "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS", "fr_attention_fwd", "attention",
     "fr_layernorm_fwd_split", "fr_add_rmsnorm_fwd_split", "OP_LAYERNORM_SPLIT", "OP_RMSNORM_SPLIT",
-    "fr_softmax_bwd_split", "OP_SOFTMAX_BWD_SPLIT",
+    "fr_softmax_bwd_split", "OP_SOFTMAX_BWD_SPLIT", "fr_add_rmsnorm_bwd_split",
+    "fr_layernorm_bwd_split", "fr_norm_bwd_split_workspace_bytes",
     "softmax", "layernorm", "add_rmsnorm", "softmax_xent", "forced_variant",
     "softmax_bwd", "add_rmsnorm_bwd", "layernorm_bwd",
     "OP_SOFTMAX", "OP_LAYERNORM", "OP_RMSNORM", "OP_XENT",
@@ -91,6 +92,8 @@ def _load() -> ctypes.CDLL:
         "fr_layernorm_fwd_split": [P, P, P, P, P, P, I64, I64, F, I32, P, I64, P],
         "fr_add_rmsnorm_fwd_split": [P, P, P, P, P, I64, I64, F, I32, P, I64, P],
         "fr_softmax_bwd_split": [P, P, P, I64, I64, I32, P, I64, P],
+        "fr_add_rmsnorm_bwd_split": [P, P, P, P, P, P, P, I64, I64, I64, F, I32, P],
+        "fr_layernorm_bwd_split": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, P],
         "fr_attention_fwd": [P, P, P, P, P, I64, I64, I64, I64, I64, I32, F, I32, P],
         "fr_softmax_xent_split": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P,
                                   I64, P],
@@ -107,6 +110,8 @@ def _load() -> ctypes.CDLL:
     L.fr_split_workspace_bytes.restype = ctypes.c_int64
     L.fr_norm_bwd_workspace_bytes.argtypes = [I32, I64, I64]
     L.fr_norm_bwd_workspace_bytes.restype = ctypes.c_int64
+    L.fr_norm_bwd_split_workspace_bytes.argtypes = [I32, I64, I64]
+    L.fr_norm_bwd_split_workspace_bytes.restype = ctypes.c_int64
     L.fr_status_str.argtypes = [ctypes.c_int]
     L.fr_status_str.restype = ctypes.c_char_p
     L.fr_version.argtypes = []
@@ -438,8 +443,28 @@ def fr_norm_bwd_workspace_bytes(op: int, rows: int, cols: int) -> int:
     return n
 
 
+def fr_norm_bwd_split_workspace_bytes(op: int, rows: int, cols: int) -> int:
+    """Workspace bytes of the split-row norm backward (C: same name)."""
+    n = int(lib.fr_norm_bwd_split_workspace_bytes(int(op), int(rows), int(cols)))
+    if n < 0:
+        raise ValueError(f"no split workspace size for op {op} at [{rows}, {cols}]")
+    return n
+
+
+def fr_add_rmsnorm_bwd_split(h, dy, weight, dh, dweight, workspace, dres=None, eps: float = 1e-6,
+                             stream=None) -> None:
+    """fr_add_rmsnorm_bwd for rows of any width (C: fr_add_rmsnorm_bwd_split)."""
+    fr_add_rmsnorm_bwd(h, dy, weight, dh, dweight, workspace, dres, eps, stream, _split=True)
+
+
+def fr_layernorm_bwd_split(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace,
+                           stream=None) -> None:
+    """fr_layernorm_bwd for rows of any width (C: fr_layernorm_bwd_split)."""
+    fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream, _split=True)
+
+
 def fr_add_rmsnorm_bwd(h, dy, weight, dh, dweight, workspace, dres=None, eps: float = 1e-6,
-                       stream=None) -> None:
+                       stream=None, _split: bool = False) -> None:
     """Backward of residual add + RMSNorm from the stored h = x + residual
     (C: fr_add_rmsnorm_bwd); dweight fp32 [cols] is overwritten."""
     _need_cuda(h, dy, weight, dh, dweight, dres)
@@ -451,13 +476,14 @@ def fr_add_rmsnorm_bwd(h, dy, weight, dh, dweight, workspace, dres=None, eps: fl
         raise TypeError("weight must have h's dtype")
     _check_f32_vec(dweight, C, "dweight")
     wp, wn = _workspace_arg(workspace)
-    _check(lib.fr_add_rmsnorm_bwd(_ptr(h), _ptr(dy), _ptr(dres), _ptr(weight), _ptr(dh),
-                                  _ptr(dweight), wp, wn, R, C, float(eps), _dtype_code(h),
-                                  _stream(stream, h)),
-           "fr_add_rmsnorm_bwd")
+    fn = lib.fr_add_rmsnorm_bwd_split if _split else lib.fr_add_rmsnorm_bwd
+    _check(fn(_ptr(h), _ptr(dy), _ptr(dres), _ptr(weight), _ptr(dh), _ptr(dweight), wp, wn, R, C,
+              float(eps), _dtype_code(h), _stream(stream, h)),
+           "fr_add_rmsnorm_bwd_split" if _split else "fr_add_rmsnorm_bwd")
 
 
-def fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream=None) -> None:
+def fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream=None,
+                     _split: bool = False) -> None:
     """Backward of LayerNorm at the saved mean / rstd (C: fr_layernorm_bwd);
     dgamma, dbeta fp32 [cols] are overwritten."""
     torch = _torch()
@@ -473,10 +499,10 @@ def fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, str
     _check_f32_vec(dgamma, C, "dgamma")
     _check_f32_vec(dbeta, C, "dbeta")
     wp, wn = _workspace_arg(workspace)
-    _check(lib.fr_layernorm_bwd(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
-                                _ptr(dgamma), _ptr(dbeta), wp, wn, R, C, _dtype_code(x),
-                                _stream(stream, x)),
-           "fr_layernorm_bwd")
+    fn = lib.fr_layernorm_bwd_split if _split else lib.fr_layernorm_bwd
+    _check(fn(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+              _ptr(dbeta), wp, wn, R, C, _dtype_code(x), _stream(stream, x)),
+           "fr_layernorm_bwd_split" if _split else "fr_layernorm_bwd")
 
 
 def fr_stream_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
@@ -586,9 +612,9 @@ def softmax_xent(logits, labels, return_argmax: bool = False, ignore_index=None,
     return (out, grad, am) if return_argmax else (out, grad)
 
 
-def _workspace(op, rows, cols, device):
+def _workspace(op, rows, cols, device, split=False):
     torch = _torch()
-    n = fr_norm_bwd_workspace_bytes(op, rows, cols)
+    n = (fr_norm_bwd_split_workspace_bytes if split else fr_norm_bwd_workspace_bytes)(op, rows, cols)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -604,25 +630,28 @@ def softmax_bwd(p, dy, out=None):
 
 
 def add_rmsnorm_bwd(h, dy, weight, eps: float = 1e-6, dres=None):
-    """Returns (dh, dweight); dh is the gradient of both x and residual."""
+    """Returns (dh, dweight); dh is the gradient of both x and residual. Rows
+    wider than FR_BWD_MAX_COLS take the split-row path."""
     torch = _torch()
     R, C = h.shape
     dh = torch.empty_like(h)
     dw = torch.empty(C, dtype=torch.float32, device=h.device)
-    ws = _workspace(OP_RMSNORM_BWD, R, C, h.device)
-    fr_add_rmsnorm_bwd(h, dy, weight, dh, dw, ws, dres=dres, eps=eps)
+    split = C > FR_BWD_MAX_COLS
+    ws = _workspace(OP_RMSNORM_BWD, R, C, h.device, split)
+    fr_add_rmsnorm_bwd(h, dy, weight, dh, dw, ws, dres=dres, eps=eps, _split=split)
     return dh, dw
 
 
 def layernorm_bwd(x, dy, gamma, mean, rstd):
-    """Returns (dx, dgamma, dbeta)."""
+    """Returns (dx, dgamma, dbeta); rows wider than FR_BWD_MAX_COLS take the split-row path."""
     torch = _torch()
     R, C = x.shape
     dx = torch.empty_like(x)
     dg = torch.empty(C, dtype=torch.float32, device=x.device)
     db = torch.empty(C, dtype=torch.float32, device=x.device)
-    ws = _workspace(OP_LAYERNORM_BWD, R, C, x.device)
-    fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dg, db, ws)
+    split = C > FR_BWD_MAX_COLS
+    ws = _workspace(OP_LAYERNORM_BWD, R, C, x.device, split)
+    fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dg, db, ws, _split=split)
     return dx, dg, db
 
 

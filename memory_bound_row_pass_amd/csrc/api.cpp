@@ -461,6 +461,89 @@ fr_status_t fr_add_rmsnorm_bwd(const void* h, const void* dy, const void* dres, 
   return launch_status(fr::launch_colsum(ws, grid, (int)cols, dweight, nullptr, st));
 }
 
+int64_t fr_norm_bwd_split_workspace_bytes(fr_op_t op, int64_t rows, int64_t cols) {
+  if (op != FR_OP_RMSNORM_BWD && op != FR_OP_LAYERNORM_BWD) return -1;
+  if (rows < 0 || cols < 1 || cols > FR_SPLIT_MAX_COLS || rows > INT64_MAX / 8 / cols) return -1;
+  const int nseg = (int)((cols + fr::kBwdSplitSeg - 1) / fr::kBwdSplitSeg);
+  const int64_t np = op == FR_OP_LAYERNORM_BWD ? 2 : 1;
+  return fr::norm_bwd_split_part_bytes(rows, cols) +
+         (int64_t)fr::norm_bwd_split_groups(rows, nseg) * cols * 4 * np;
+}
+
+fr_status_t fr_add_rmsnorm_bwd_split(const void* h, const void* dy, const void* dres,
+                                     const void* weight, void* dh, float* dweight, void* workspace,
+                                     int64_t workspace_bytes, int64_t rows, int64_t cols, float eps,
+                                     fr_dtype_t dtype, void* stream) {
+  const int64_t need = fr_norm_bwd_split_workspace_bytes(FR_OP_RMSNORM_BWD, rows, cols);
+  if (need < 0) return FR_E_SHAPE;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  if (workspace_bytes < need) return FR_E_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dweight) return FR_E_NULL;
+  if (!aligned(dweight, 4)) return FR_E_ALIGN;
+  if (rows == 0) return launch_status(fr::launch_colsum(nullptr, 0, (int)cols, dweight, nullptr, st));
+  if (!h || !dy || !weight || !dh || !workspace) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(h, es) || !aligned(dy, es) || !aligned(weight, es) || !aligned(dh, es) ||
+      (dres && !aligned(dres, es)) || !aligned(workspace, 16))
+    return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(h, nb, true, es, false),
+                      make_buf(dy, nb, true, es, false),
+                      make_buf(dres, nb, true, es, false),
+                      make_buf(weight, cols * es, false, es, false),
+                      make_buf(dh, nb, true, es, true),
+                      make_buf(dweight, cols * 4, false, 4, true),
+                      make_buf(workspace, need, false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 7)) return s;
+  const bool vec = aligned(h, 16) && aligned(dy, 16) && (!dres || aligned(dres, 16)) &&
+                   aligned(weight, 16) && aligned(dh, 16) && (cols * es) % 16 == 0;
+  return launch_status(fr::launch_norm_bwd_split(0, dtype == FR_BF16, vec, h, dy, dres, weight,
+                                                 nullptr, nullptr, dh, dweight, nullptr, workspace,
+                                                 rows, (int)cols, eps, st));
+}
+
+fr_status_t fr_layernorm_bwd_split(const void* x, const void* dy, const void* gamma,
+                                   const float* mean, const float* rstd, void* dx, float* dgamma,
+                                   float* dbeta, void* workspace, int64_t workspace_bytes,
+                                   int64_t rows, int64_t cols, fr_dtype_t dtype, void* stream) {
+  const int64_t need = fr_norm_bwd_split_workspace_bytes(FR_OP_LAYERNORM_BWD, rows, cols);
+  if (need < 0) return FR_E_SHAPE;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (workspace_bytes < need) return FR_E_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dgamma || !dbeta) return FR_E_NULL;
+  if (!aligned(dgamma, 4) || !aligned(dbeta, 4)) return FR_E_ALIGN;
+  if (rows == 0) {
+    const Buf pb[] = {make_buf(dgamma, cols * 4, false, 4, true),
+                      make_buf(dbeta, cols * 4, false, 4, true)};
+    if (fr_status_t s = check_alias(pb, 2)) return s;
+    return launch_status(fr::launch_colsum(nullptr, 0, (int)cols, dgamma, dbeta, st));
+  }
+  if (!x || !dy || !gamma || !mean || !rstd || !dx || !workspace) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(x, es) || !aligned(dy, es) || !aligned(gamma, es) || !aligned(dx, es) ||
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(workspace, 16))
+    return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(x, nb, true, es, false),
+                      make_buf(dy, nb, true, es, false),
+                      make_buf(gamma, cols * es, false, es, false),
+                      make_buf(mean, rows * 4, false, 4, false),
+                      make_buf(rstd, rows * 4, false, 4, false),
+                      make_buf(dx, nb, true, es, true),
+                      make_buf(dgamma, cols * 4, false, 4, true),
+                      make_buf(dbeta, cols * 4, false, 4, true),
+                      make_buf(workspace, need, false, 1, true)};
+  if (fr_status_t s = check_alias(bufs, 9)) return s;
+  const bool vec = aligned(x, 16) && aligned(dy, 16) && aligned(gamma, 16) && aligned(dx, 16) &&
+                   (cols * es) % 16 == 0;
+  return launch_status(fr::launch_norm_bwd_split(1, dtype == FR_BF16, vec, x, dy, nullptr, gamma,
+                                                 mean, rstd, dx, dgamma, dbeta, workspace, rows,
+                                                 (int)cols, 0.f, st));
+}
+
 fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* gamma, const float* mean,
                              const float* rstd, void* dx, float* dgamma, float* dbeta,
                              void* workspace, int64_t workspace_bytes, int64_t rows, int64_t cols,

@@ -386,6 +386,166 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
   flush_partials<T, NV, EPV, RPB>(ab, part, ws + (G + blockIdx.x) * cols, sl.nvec, ln.tid, ln.sub);
 }
 
+// ------------------------------------------------- split-row norm backward
+// Rows wider than one workgroup's registers: the row is cut into segments
+// of kBwdSplitSeg columns (rows on the 16-byte grid or the scalar path, so a
+// segment's lanes own fixed columns, as above).
+//   pass 1 (norm_bwd_split_sums_kernel): each (row, segment) writes its two
+//     partial row sums — sum h^2 and sum dy w h (RMSNorm), sum g and sum g n
+//     (LayerNorm) — to part[row][segment];
+//   pass 2 (norm_bwd_split_apply_kernel): workgroup (segment sg, row group
+//     rg) takes rows rg, rg + RG, ...: per row it adds the row's partials in
+//     segment order (the same bits in every workgroup of the row), writes
+//     the segment's dh / dx and accumulates its columns' parameter-gradient
+//     partials in registers; at the end it writes them to partial row rg of
+//     the workspace [params][RG][cols];
+//   colsum_kernel then adds the RG partial rows in order.
+
+template <typename Ts, int T, int NV, int EPV, bool LN>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4)))
+void norm_bwd_split_sums_kernel(const Ts* xh, const Ts* dy, const Ts* w, const float* mean,
+                                const float* rstd, int64_t rows, int cols, int nseg,
+                                float4* part) {
+  constexpr int NW = T / 64;
+  constexpr int SEG = T * NV * EPV;
+  __shared__ float xw[2][NW][2];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t work = rows * nseg;
+  int it = 0;
+  for (int64_t wk = blockIdx.x; wk < work; wk += gridDim.x, ++it) {
+    const int64_t row = wk / nseg;
+    const int c0 = (int)(wk - row * nseg) * SEG;
+    const int len = cols - c0 < SEG ? cols - c0 : SEG;
+    const Slots<T, NV, EPV> sl(len, tid);
+    const int64_t off = row * cols + c0;
+    float a[NV][EPV], d[NV][EPV];
+    sl.load2(xh + off, dy + off, a, d);
+    float mu = 0.f, rs = 1.f;
+    if constexpr (LN) {
+      mu = mean[row];
+      rs = rstd[row];
+    }
+    const Ts* w1 = fresh(w) + c0;
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float wt[EPV];
+      sl.param(w1, i, wt);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const float gk = d[i][k] * wt[k];
+        if constexpr (LN) {
+          const float nk = sl.ok(i) ? (a[i][k] - mu) * rs : 0.f;
+          if (k & 1) { a1 += gk; b1 = __builtin_fmaf(gk, nk, b1); }
+          else { a0 += gk; b0 = __builtin_fmaf(gk, nk, b0); }
+        } else {
+          const float hk = a[i][k];
+          if (k & 1) { a1 = __builtin_fmaf(hk, hk, a1); b1 = __builtin_fmaf(gk, hk, b1); }
+          else { a0 = __builtin_fmaf(hk, hk, a0); b0 = __builtin_fmaf(gk, hk, b0); }
+        }
+      }
+    }
+    Sum2State st{a0 + a1, b0 + b1};
+    st = wave_reduce(st, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Sum2Merge{});
+    if (tid == 0) part[wk] = float4{st.a, st.b, 0.f, 0.f};
+  }
+}
+
+// xh: h (RMSNorm) or x (LayerNorm); w: weight or gamma; dres: RMSNorm only
+// (may be NULL); out: dh or dx; ws: [params][RG][cols].
+template <typename Ts, int T, int NV, int EPV, bool LN, bool DRES>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4)))
+void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, const Ts* w,
+                                 const float* mean, const float* rstd, Ts* out, float* ws,
+                                 int64_t rows, int cols, int nseg, int RG, const float4* part,
+                                 float eps) {
+  constexpr int NW = T / 64;
+  constexpr int SEG = T * NV * EPV;
+  __shared__ float xw[2][NW][2];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int sg = (int)(blockIdx.x % (unsigned)nseg);
+  const int rg = (int)(blockIdx.x / (unsigned)nseg);
+  const int c0 = sg * SEG;
+  const int len = cols - c0 < SEG ? cols - c0 : SEG;
+  const Slots<T, NV, EPV> sl(len, tid);
+
+  float acc[NV][EPV], acc2[LN ? NV : 1][EPV];  // dw (dgamma) and dbeta partials
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) acc[i][k] = 0.f;
+#pragma unroll
+  for (int i = 0; i < (LN ? NV : 1); ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) acc2[i][k] = 0.f;
+
+  int it = 0;
+  for (int64_t row = rg; row < rows; row += RG, ++it) {
+    Sum2State st{0.f, 0.f};
+    for (int j = tid; j < nseg; j += T) {
+      const float4 p = part[row * nseg + j];
+      st = Sum2Merge{}(st, Sum2State{p.x, p.y});
+    }
+    st = wave_reduce(st, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Sum2Merge{});
+
+    const int64_t off = row * cols + c0;
+    float a[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
+    if constexpr (DRES) sl.load3(xh + off, dy + off, dres + off, a, d, dr);
+    else sl.load2(xh + off, dy + off, a, d);
+    const Ts* w1 = fresh(w) + c0;
+    if constexpr (LN) {
+      const float mu = mean[row], rs = rstd[row];
+      const float mg = st.a / (float)cols, mgn = st.b / (float)cols;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float ga[EPV];
+        sl.param(w1, i, ga);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float nk = (a[i][k] - mu) * rs;
+          acc[i][k] = __builtin_fmaf(d[i][k], nk, acc[i][k]);
+          acc2[i][k] += d[i][k];
+          a[i][k] = rs * __builtin_fmaf(-nk, mgn, __builtin_fmaf(d[i][k], ga[k], -mg));
+        }
+      }
+    } else {
+      const float r = 1.f / __builtin_sqrtf(st.a / (float)cols + eps);
+      const float c = r * r * (st.b / (float)cols);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float wt[EPV];
+        sl.param(w1, i, wt);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          acc[i][k] = __builtin_fmaf(d[i][k] * a[i][k], r, acc[i][k]);
+          const float t = r * __builtin_fmaf(-a[i][k], c, wt[k] * d[i][k]);
+          if constexpr (DRES) a[i][k] = t + dr[i][k];
+          else a[i][k] = t;
+        }
+      }
+    }
+    sl.store(out + off, a);
+  }
+  // this workgroup's partial row segment (slots past the segment end hold 0
+  // and are not written)
+  float* w0 = ws + (size_t)rg * cols + c0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (sl.ok(i)) store_f32<EPV>(w0 + (i * T + tid) * EPV, acc[i]);
+  if constexpr (LN) {
+    float* w1 = ws + ((size_t)RG + rg) * cols + c0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (sl.ok(i)) store_f32<EPV>(w1 + (i * T + tid) * EPV, acc2[i]);
+  }
+}
+
 // ------------------------------------------------------------ column sums
 // out_p[c] = sum over the partial rows b = 0 .. partials-1 of ws[p][b][c],
 // parameter p = blockIdx.y. A workgroup takes a 32-column tile (one 128-byte
@@ -464,6 +624,61 @@ static hipError_t launch_layernorm_bwd(const void* x, const void* dy, const void
                        static_cast<const Ts*>(x), static_cast<const Ts*>(dy),
                        static_cast<const Ts*>(gamma), mean, rstd, static_cast<Ts*>(dx), ws, rows,
                        cols);
+}
+
+template <typename Ts, int NV, int EPV, bool LN>
+static hipError_t launch_norm_bwd_split_t(const void* xh, const void* dy, const void* dres,
+                                          const void* w, const float* mean, const float* rstd,
+                                          void* out, float* dw0, float* dw1, void* workspace,
+                                          int64_t rows, int cols, float eps, hipStream_t s) {
+  constexpr int T = 512;
+  static_assert(T * NV * EPV == kBwdSplitSeg, "segment");
+  const int nseg = (cols + kBwdSplitSeg - 1) / kBwdSplitSeg;
+  const int RG = norm_bwd_split_groups(rows, nseg);
+  float4* part = static_cast<float4*>(workspace);
+  float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       norm_bwd_split_part_bytes(rows, cols));
+  const int64_t work = rows * nseg;
+  const unsigned g1 = (unsigned)(work < kMaxGrid ? work : kMaxGrid);
+  hipError_t e = launch_kernel(&norm_bwd_split_sums_kernel<Ts, T, NV, EPV, LN>, dim3(g1), dim3(T), s,
+                               static_cast<const Ts*>(xh), static_cast<const Ts*>(dy),
+                               static_cast<const Ts*>(w), mean, rstd, rows, cols, nseg, part);
+  if (e != hipSuccess) return e;
+  auto k2 = (!LN && dres) ? &norm_bwd_split_apply_kernel<Ts, T, NV, EPV, LN, true>
+                          : &norm_bwd_split_apply_kernel<Ts, T, NV, EPV, LN, false>;
+  e = launch_kernel(k2, dim3((unsigned)(nseg * RG)), dim3(T), s, static_cast<const Ts*>(xh),
+                    static_cast<const Ts*>(dy), static_cast<const Ts*>(dres),
+                    static_cast<const Ts*>(w), mean, rstd, static_cast<Ts*>(out), ws, rows, cols,
+                    nseg, RG, static_cast<const float4*>(part), eps);
+  if (e != hipSuccess) return e;
+  return launch_colsum(ws, RG, cols, dw0, dw1, s);
+}
+
+hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* xh, const void* dy,
+                                 const void* dres, const void* w, const float* mean,
+                                 const float* rstd, void* out, float* dw0, float* dw1,
+                                 void* workspace, int64_t rows, int cols, float eps,
+                                 hipStream_t s) {
+  if (layernorm) {
+    if (bf16)
+      return vec ? launch_norm_bwd_split_t<bf16_t, 2, 8, true>(xh, dy, dres, w, mean, rstd, out, dw0,
+                                                               dw1, workspace, rows, cols, eps, s)
+                 : launch_norm_bwd_split_t<bf16_t, 16, 1, true>(xh, dy, dres, w, mean, rstd, out,
+                                                                dw0, dw1, workspace, rows, cols, eps, s);
+    return vec ? launch_norm_bwd_split_t<float, 4, 4, true>(xh, dy, dres, w, mean, rstd, out, dw0, dw1,
+                                                            workspace, rows, cols, eps, s)
+               : launch_norm_bwd_split_t<float, 16, 1, true>(xh, dy, dres, w, mean, rstd, out, dw0,
+                                                             dw1, workspace, rows, cols, eps, s);
+  }
+  if (bf16)
+    return vec ? launch_norm_bwd_split_t<bf16_t, 2, 8, false>(xh, dy, dres, w, mean, rstd, out, dw0,
+                                                              dw1, workspace, rows, cols, eps, s)
+               : launch_norm_bwd_split_t<bf16_t, 16, 1, false>(xh, dy, dres, w, mean, rstd, out, dw0,
+                                                               dw1, workspace, rows, cols, eps, s);
+  return vec ? launch_norm_bwd_split_t<float, 4, 4, false>(xh, dy, dres, w, mean, rstd, out, dw0, dw1,
+                                                           workspace, rows, cols, eps, s)
+             : launch_norm_bwd_split_t<float, 16, 1, false>(xh, dy, dres, w, mean, rstd, out, dw0,
+                                                            dw1, workspace, rows, cols, eps, s);
 }
 
 // Norm backward shapes: (T, NV, EPV, RPB, OCC, grid_max). The default

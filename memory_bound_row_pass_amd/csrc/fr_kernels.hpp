@@ -124,6 +124,26 @@ VariantSpan<SoftmaxBwdVariant> softmax_bwd_variants(int bf16);
 VariantSpan<RmsNormBwdVariant> rmsnorm_bwd_variants(int bf16);
 VariantSpan<LayerNormBwdVariant> layernorm_bwd_variants(int bf16);
 
+// Split-row norm backward (rows wider than FR_BWD_MAX_COLS): segments of
+// kBwdSplitSeg columns; workspace = the row-sum partials (16 bytes per row
+// segment, padded to 256 bytes) then [params][RG][cols] fp32 partial rows,
+// RG = norm_bwd_split_groups(rows, segments) <= kBwdGridMax.
+constexpr int kBwdSplitSeg = 8192;
+inline int norm_bwd_split_groups(int64_t rows, int nseg) {
+  int g = 1024 / nseg;
+  g = g < 1 ? 1 : (g > kBwdGridMax ? kBwdGridMax : g);
+  return (int)(rows < g ? rows : g);
+}
+inline int64_t norm_bwd_split_part_bytes(int64_t rows, int64_t cols) {
+  const int64_t nseg = (cols + kBwdSplitSeg - 1) / kBwdSplitSeg;
+  return (rows * nseg * 16 + 255) / 256 * 256;
+}
+hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* xh, const void* dy,
+                                 const void* dres, const void* w, const float* mean,
+                                 const float* rstd, void* out, float* dw0, float* dw1,
+                                 void* workspace, int64_t rows, int cols, float eps,
+                                 hipStream_t s);
+
 // out0[c] (and out1[c] when out1 != NULL) = sum over b < partials of
 // ws[p][b][c], in order of b; partials == 0 writes zeros.
 hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, float* out1,

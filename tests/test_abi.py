@@ -274,6 +274,49 @@ def test_softmax_bwd_split_validation():
     assert call(ws=DX + 64) == E_ALIAS
 
 
+def test_norm_bwd_split_validation():
+    n = fr.fr_norm_bwd_split_workspace_bytes
+    assert n(fr.OP_RMSNORM_BWD, 4, 100000) == 1024 + 4 * 100000 * 4  # 13 segments, 4 row groups
+    assert n(fr.OP_LAYERNORM_BWD, 1000, 32768) == 64000 + 256 * 32768 * 4 * 2
+    with pytest.raises(ValueError):
+        n(fr.OP_SOFTMAX, 4, 100000)
+    with pytest.raises(ValueError):
+        n(fr.OP_RMSNORM_BWD, 4, fr.FR_SPLIT_MAX_COLS + 1)
+    f = fr.lib.fr_add_rmsnorm_bwd_split
+    DY, DR, W, DH, DW, WS = (A + k * 0x1000000 for k in range(1, 7))
+    need = n(fr.OP_RMSNORM_BWD, 4, 100000)
+
+    def rn(h=A, dy=DY, dres=DR, w=W, dh=DH, dw=DW, ws=WS, wn=need, rows=4, cols=100000, eps=1e-6,
+           dt=1):
+        return f(P(h), P(dy), P(dres), P(w), P(dh), P(dw), P(ws), wn, rows, cols, eps, dt, None)
+
+    assert rn(wn=need - 1) == E_SHAPE
+    assert rn(cols=0) == E_SHAPE
+    assert rn(dw=0) == E_NULL
+    assert rn(ws=0) == E_NULL
+    assert rn(dt=3) == E_DTYPE
+    assert rn(eps=-1.0) == E_VALUE
+    assert rn(ws=WS + 8) == E_ALIGN
+    assert rn(dh=A + 2) == E_ALIAS
+    assert rn(ws=DW) == E_ALIAS
+    g = fr.lib.fr_layernorm_bwd_split
+    M, RS, DG, DB = A + 0x8000000, A + 0x9000000, A + 0xA000000, A + 0xB000000
+    need = n(fr.OP_LAYERNORM_BWD, 4, 100000)
+
+    def ln(x=A, dy=DY, gm=W, m=M, r=RS, dx=DH, dg=DG, db=DB, ws=WS, wn=need, rows=4, cols=100000,
+           dt=0):
+        return g(P(x), P(dy), P(gm), P(m), P(r), P(dx), P(dg), P(db), P(ws), wn, rows, cols, dt,
+                 None)
+
+    assert ln(wn=need - 1) == E_SHAPE
+    assert ln(m=0) == E_NULL
+    assert ln(db=0) == E_NULL
+    assert ln(dt=9) == E_DTYPE
+    assert ln(r=RS + 2) == E_ALIGN
+    assert ln(db=DG) == E_ALIAS
+    assert ln(dx=DY + 4) == E_ALIAS
+
+
 def test_attention_validation():
     f = fr.lib.fr_attention_fwd
     K, V, O, LSE = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000

@@ -395,3 +395,113 @@ def test_softmax_bwd_split_shapes_in_place_misaligned():
     p, dy = softmax_bwd_inputs(2, 70000, fr.F32, seed=32)
     dx = fr.softmax_bwd(upload(p), upload(dy))
     expect_softmax_bwd(p, dy, fr.F32, dx.cpu().numpy(), "softmax_bwd() of a wide row")
+
+
+# ------------------------------------------------------- norm backward, split
+
+from test_gpu_backward import (expect_ln_bwd, expect_rms_bwd, ln_bwd_inputs,  # noqa: E402
+                               rms_bwd_inputs)
+from parity import to_dev  # noqa: E402
+
+
+def bwd_workspace(op, R, C):
+    return Guarded((max(fr.fr_norm_bwd_split_workspace_bytes(op, R, C) // 4, 4),), torch.float32)
+
+
+def run_rms_bwd_split(w, code, with_dres=True, off=0, inplace=None):
+    R, C = w["h"].shape
+    h, dy, wt = upload(w["h"], off), upload(w["dy"], off), upload(w["weight"], off)
+    dres = upload(w["dres"], off) if with_dres else None
+    dw = Guarded((C,), torch.float32)
+    ws = bwd_workspace(fr.OP_RMSNORM_BWD, R, C)
+    if inplace:
+        dh, dh_t = None, {"dy": dy, "h": h, "dres": dres}[inplace]
+    else:
+        dh = Guarded((R, C), TDT[code], off)
+        dh_t = dh.t
+    fr.fr_add_rmsnorm_bwd_split(h, dy, wt, dh_t, dw.t, ws.t, dres=dres, eps=w.eps)
+    torch.cuda.synchronize()
+    assert dw.canaries_intact() and ws.canaries_intact() and (dh is None or dh.canaries_intact())
+    return host(dh_t), dw.t.cpu().numpy()
+
+
+def run_ln_bwd_split(w, mean, rstd, code, off=0, inplace=None):
+    R, C = w["x"].shape
+    x, dy, g = upload(w["x"], off), upload(w["dy"], off), upload(w["gamma"], off)
+    m, r = to_dev(mean), to_dev(rstd)
+    dg, db = Guarded((C,), torch.float32), Guarded((C,), torch.float32)
+    ws = bwd_workspace(fr.OP_LAYERNORM_BWD, R, C)
+    if inplace:
+        dx, dx_t = None, {"x": x, "dy": dy}[inplace]
+    else:
+        dx = Guarded((R, C), TDT[code], off)
+        dx_t = dx.t
+    fr.fr_layernorm_bwd_split(x, dy, g, m, r, dx_t, dg.t, db.t, ws.t)
+    torch.cuda.synchronize()
+    assert dg.canaries_intact() and db.canaries_intact() and ws.canaries_intact()
+    assert dx is None or dx.canaries_intact()
+    return host(dx_t), dg.t.cpu().numpy(), db.t.cpu().numpy()
+
+
+BWD_WIDTHS = [16385, 24576, 65537, 100000]
+
+
+@pytest.mark.parametrize("C", BWD_WIDTHS)
+@pytest.mark.parametrize("code", [fr.F32, fr.BF16])
+def test_rms_bwd_split_widths(C, code):
+    for R, dres in ((1, True), (5, False)):
+        w = rms_bwd_inputs(R, C, code, seed=C + R)
+        expect_rms_bwd(w, code, run_rms_bwd_split(w, code, with_dres=dres),
+                       f"split rms_bwd {code} {R}x{C} dres={dres}", with_dres=dres)
+
+
+@pytest.mark.parametrize("C", BWD_WIDTHS)
+@pytest.mark.parametrize("code", [fr.F32, fr.BF16])
+def test_ln_bwd_split_widths(C, code):
+    for R in (1, 5):
+        w, mean, rstd = ln_bwd_inputs(R, C, code, seed=C + R)
+        expect_ln_bwd(w, mean, rstd, code, run_ln_bwd_split(w, mean, rstd, code),
+                      f"split ln_bwd {code} {R}x{C}")
+
+
+def test_norm_bwd_split_many_rows_in_place_misaligned():
+    # more rows than row groups (each workgroup takes several rows), the
+    # scalar path (misaligned), and outputs over their inputs
+    for code in (fr.F32, fr.BF16):
+        w = rms_bwd_inputs(700, 32768, code, seed=41)
+        expect_rms_bwd(w, code, run_rms_bwd_split(w, code), f"split rms_bwd {code} 700x32768")
+        w = rms_bwd_inputs(3, 40000, code, seed=42)
+        expect_rms_bwd(w, code, run_rms_bwd_split(w, code, off=1), f"split rms_bwd {code} misaligned")
+        for ip in ("h", "dy", "dres"):
+            expect_rms_bwd(w, code, run_rms_bwd_split(w, code, inplace=ip),
+                           f"split rms_bwd {code} in place ({ip})")
+        w, mean, rstd = ln_bwd_inputs(600, 32768, code, seed=43)
+        expect_ln_bwd(w, mean, rstd, code, run_ln_bwd_split(w, mean, rstd, code),
+                      f"split ln_bwd {code} 600x32768")
+        w, mean, rstd = ln_bwd_inputs(3, 40001, code, seed=44)
+        expect_ln_bwd(w, mean, rstd, code, run_ln_bwd_split(w, mean, rstd, code, off=1),
+                      f"split ln_bwd {code} misaligned")
+        for ip in ("x", "dy"):
+            expect_ln_bwd(w, mean, rstd, code, run_ln_bwd_split(w, mean, rstd, code, inplace=ip),
+                          f"split ln_bwd {code} in place ({ip})")
+
+
+def test_norm_bwd_split_determinism_rows_zero_and_convenience():
+    w = rms_bwd_inputs(64, 50000, fr.BF16, seed=45)
+    a = run_rms_bwd_split(w, fr.BF16)
+    b = run_rms_bwd_split(w, fr.BF16)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    dw = torch.full((30000,), 5.0, device=DEV)
+    e = torch.empty(0, 30000, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    fr.fr_add_rmsnorm_bwd_split(e, e, torch.ones(30000, device=DEV), e, dw, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw).item() == 0
+    dh, dwc = fr.add_rmsnorm_bwd(upload(w["h"]), upload(w["dy"]), upload(w["weight"]), w.eps,
+                                 dres=upload(w["dres"]))
+    assert np.array_equal(host(dh), a[0]) and np.array_equal(dwc.cpu().numpy(), a[1])
+    w, mean, rstd = ln_bwd_inputs(4, 30000, fr.F32, seed=46)
+    dx, dg, db = fr.layernorm_bwd(upload(w["x"]), upload(w["dy"]), upload(w["gamma"]),
+                                  to_dev(mean), to_dev(rstd))
+    expect_ln_bwd(w, mean, rstd, fr.F32, (host(dx), dg.cpu().numpy(), db.cpu().numpy()),
+                  "layernorm_bwd() of a wide row")

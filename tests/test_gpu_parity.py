@@ -250,7 +250,21 @@ def _variant_cols(op, t, v, code, vector_path):
     return [cap, max(1, cap - 5 * e - 3), max(1, cap // 2 + 1)]
 
 
-@pytest.mark.parametrize("t,v", VARIANT_GRID)
+def _grid(uses):
+    """The (threads, vecs) pairs of VARIANT_GRID for which the library holds a
+    kernel for at least one (op, dtype, vector path) in `uses`; the selection
+    call runs on the host, so collection needs no GPU."""
+    return [(t, v) for t, v in VARIANT_GRID
+            if any(_variant_cols(op, t, v, code, vp) for op, code, vp in uses)]
+
+
+_BOTH = [(c, vp) for c in (fr.F32, fr.BF16) for vp in (True, False)]
+SOFTMAX_GRID = _grid([(fr.OP_SOFTMAX, c, vp) for c, vp in _BOTH])
+NORM_XENT_GRID = _grid([(op, c, vp) for op in (fr.OP_LAYERNORM, fr.OP_RMSNORM) for c, vp in _BOTH]
+                       + [(fr.OP_XENT, fr.F32, vp) for vp in (True, False)])
+
+
+@pytest.mark.parametrize("t,v", SOFTMAX_GRID)
 def test_every_softmax_variant(t, v):
     ran = 0
     for code in (fr.F32, fr.BF16):
@@ -276,7 +290,7 @@ def test_every_softmax_variant(t, v):
         pytest.skip(f"no softmax variant ({t}, {v})")
 
 
-@pytest.mark.parametrize("t,v", VARIANT_GRID)
+@pytest.mark.parametrize("t,v", NORM_XENT_GRID)
 def test_every_norm_and_xent_variant(t, v):
     ran = 0
     for dt, code in (("f32", fr.F32), ("bf16", fr.BF16)):

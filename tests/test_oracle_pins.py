@@ -423,8 +423,8 @@ def test_round_bf16_all_exponents_and_tie_patterns():
     _check_f32_range(RNG.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32))
 
 
-@pytest.mark.skipif(os.environ.get("FR_EXHAUSTIVE_BF16", "0") != "1",
-                    reason="all 2^32 fp32 inputs: set FR_EXHAUSTIVE_BF16=1 (about a minute)")
+@pytest.mark.skipif(os.environ.get("FR_EXHAUSTIVE_BF16", "1") == "0",
+                    reason="all 2^32 fp32 inputs (about two minutes): FR_EXHAUSTIVE_BF16=0 set")
 def test_round_bf16_exhaustive_fp32():
     step = 1 << 24
     for start in range(0, 1 << 32, step):

@@ -38,8 +38,8 @@
  *            then be NULL; the norm backward calls still zero their
  *            parameter gradients); 1 <= cols <= FR_MAX_COLS (less for the
  *            backward calls).
- * Threads    Entry points are re-entrant. fr_debug_force_variant is the only
- *            global setting.
+ * Threads    Entry points are re-entrant. fr_debug_force_variant and
+ *            fr_debug_set_split_batch_bytes are the only global settings.
  *
  * Arithmetic is fp32 throughout (bf16 inputs are widened exactly, bf16
  * outputs are rounded to nearest-even once, at the store).
@@ -214,7 +214,10 @@ FR_API int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols);
  * x, y as for fr_softmax_fwd (y may equal x); 1 <= cols <= FR_SPLIT_MAX_COLS.
  * workspace: device memory of >= fr_split_workspace_bytes(rows, cols) bytes,
  * 16-byte aligned, not overlapping any other buffer; contents on entry do not
- * matter. Two kernels on `stream`. Results are bitwise reproducible. */
+ * matter. Two kernels on `stream` per batch of rows (both passes run over
+ * one batch of rows, at most 256 MiB of input, before the next, so the second
+ * read can come from the last-level cache; fr_debug_set_split_batch_bytes).
+ * Results are bitwise reproducible. */
 FR_API fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t cols,
                                  fr_dtype_t x_dtype, fr_dtype_t y_dtype, void* workspace,
                                  int64_t workspace_bytes, void* stream);
@@ -416,6 +419,15 @@ FR_API fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, voi
  * Process-wide setting meant for tests and tuning; not synchronised with
  * concurrent calls. */
 FR_API fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs);
+
+/* Row batching of the two-pass (split) entry points: both passes run over
+ * one batch of rows before the next, a batch holding at most `bytes` of the
+ * rows' inputs (at least one row), so that the second read of a batch can be
+ * served by the memory-side last-level cache. bytes == 0: no batching (one
+ * batch of all rows); bytes < 0: the built-in default (256 MiB). Results do
+ * not depend on it. Returns the previous setting. Process-wide setting meant
+ * for tests and tuning; not synchronised with concurrent calls. */
+FR_API int64_t fr_debug_set_split_batch_bytes(int64_t bytes);
 
 /* hipError_t code of the last failed kernel launch on this thread (0 if
  * none), to explain an FR_E_LAUNCH. */

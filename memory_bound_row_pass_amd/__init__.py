@@ -19,6 +19,7 @@ __all__ = [
     "F32", "BF16", "FR_MAX_COLS", "FusedRowError", "lib", "status_str", "version",
     "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
     "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
+    "fr_debug_set_split_batch_bytes", "split_batch_bytes",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
     "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
@@ -116,6 +117,8 @@ def _load() -> ctypes.CDLL:
     L.fr_status_str.restype = ctypes.c_char_p
     L.fr_version.argtypes = []
     L.fr_version.restype = ctypes.c_char_p
+    L.fr_debug_set_split_batch_bytes.argtypes = [I64]
+    L.fr_debug_set_split_batch_bytes.restype = ctypes.c_int64
     L.fr_debug_last_launch_error.argtypes = []
     L.fr_debug_last_launch_error.restype = ctypes.c_int
     return L
@@ -540,6 +543,27 @@ class forced_variant:
 
     def __exit__(self, *exc):
         fr_debug_force_variant(self.op, 0, 0)
+        return False
+
+
+def fr_debug_set_split_batch_bytes(nbytes: int) -> int:
+    """C: fr_debug_set_split_batch_bytes; returns the previous setting."""
+    return int(lib.fr_debug_set_split_batch_bytes(int(nbytes)))
+
+
+class split_batch_bytes:
+    """Context manager: set the split entry points' row-batch bound (bytes of
+    input per batch; 0 = unbatched), restore the previous setting after."""
+
+    def __init__(self, nbytes: int):
+        self.nbytes = nbytes
+
+    def __enter__(self):
+        self.prev = fr_debug_set_split_batch_bytes(self.nbytes)
+        return self
+
+    def __exit__(self, *exc):
+        fr_debug_set_split_batch_bytes(self.prev)
         return False
 
 

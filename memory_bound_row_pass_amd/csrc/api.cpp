@@ -113,13 +113,24 @@ int vec_epv(int esz) { return 16 / esz; }
 
 }  // namespace
 
+namespace {
+std::atomic<int64_t> g_split_batch_bytes{FR_SPLIT_BATCH_BYTES};
+}  // namespace
+
 namespace fr {
 void note_launch_error(hipError_t e) { t_last_launch_error = static_cast<int>(e); }
+int64_t split_batch_bytes() { return g_split_batch_bytes.load(std::memory_order_relaxed); }
 }  // namespace fr
 
 extern "C" {
 
 int fr_debug_last_launch_error(void) { return t_last_launch_error; }
+
+int64_t fr_debug_set_split_batch_bytes(int64_t bytes) {
+  const int64_t prev = g_split_batch_bytes.load();
+  g_split_batch_bytes.store(bytes < 0 ? FR_SPLIT_BATCH_BYTES : bytes);
+  return prev;
+}
 
 
 const char* fr_status_str(fr_status_t s) {

@@ -89,9 +89,12 @@ __device__ __forceinline__ float exp_acc(float t) {
 #ifndef FR_NT_STORE
 #define FR_NT_STORE 1
 #endif
-template <typename V>
+// ld_stream: NT == true is the non-temporal hint; NT == false an ordinary
+// cached load, for data that is read again soon (the first pass of a
+// two-pass kernel).
+template <bool NT = (FR_NT_LOAD != 0), typename V>
 __device__ __forceinline__ V ld_stream(const V* p) {
-  if constexpr (FR_NT_LOAD) return __builtin_nontemporal_load(p);
+  if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
 template <typename V>
@@ -105,8 +108,9 @@ struct Vec;  // load/store EPV consecutive elements as fp32
 
 template <>
 struct Vec<float, 4> {
+  template <bool NT = (FR_NT_LOAD != 0)>
   static __device__ __forceinline__ void load(const float* p, float* v) {
-    f32x4 r = ld_stream(reinterpret_cast<const f32x4*>(p));
+    f32x4 r = ld_stream<NT>(reinterpret_cast<const f32x4*>(p));
     v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
@@ -117,9 +121,10 @@ struct Vec<float, 4> {
 
 template <>
 struct Vec<float, 8> {  // output side of bf16 -> f32 (two 16-byte stores)
+  template <bool NT = (FR_NT_LOAD != 0)>
   static __device__ __forceinline__ void load(const float* p, float* v) {
-    Vec<float, 4>::load(p, v);
-    Vec<float, 4>::load(p + 4, v + 4);
+    Vec<float, 4>::load<NT>(p, v);
+    Vec<float, 4>::load<NT>(p + 4, v + 4);
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
     Vec<float, 4>::store(p, v);
@@ -129,8 +134,9 @@ struct Vec<float, 8> {  // output side of bf16 -> f32 (two 16-byte stores)
 
 template <>
 struct Vec<bf16_t, 8> {
+  template <bool NT = (FR_NT_LOAD != 0)>
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    u32x4 r = ld_stream(reinterpret_cast<const u32x4*>(p));
+    u32x4 r = ld_stream<NT>(reinterpret_cast<const u32x4*>(p));
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
     v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
     v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
@@ -145,8 +151,9 @@ struct Vec<bf16_t, 8> {
 
 template <>
 struct Vec<bf16_t, 4> {  // output side of f32 -> bf16 (one 8-byte store)
+  template <bool NT = (FR_NT_LOAD != 0)>
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    u32x2 r = ld_stream(reinterpret_cast<const u32x2*>(p));
+    u32x2 r = ld_stream<NT>(reinterpret_cast<const u32x2*>(p));
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
     v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
   }
@@ -158,8 +165,9 @@ struct Vec<bf16_t, 4> {  // output side of f32 -> bf16 (one 8-byte store)
 
 template <>
 struct Vec<float, 1> {
+  template <bool NT = (FR_NT_LOAD != 0)>
   static __device__ __forceinline__ void load(const float* p, float* v) {
-    v[0] = ld_stream(p);
+    v[0] = ld_stream<NT>(p);
   }
   static __device__ __forceinline__ void store(float* p, const float* v) {
     st_stream(v[0], p);
@@ -168,8 +176,9 @@ struct Vec<float, 1> {
 
 template <>
 struct Vec<bf16_t, 1> {
+  template <bool NT = (FR_NT_LOAD != 0)>
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    uint16_t u = ld_stream(reinterpret_cast<const uint16_t*>(p));
+    uint16_t u = ld_stream<NT>(reinterpret_cast<const uint16_t*>(p));
     v[0] = __uint_as_float((uint32_t)u << 16);
   }
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
@@ -268,7 +277,7 @@ __device__ __forceinline__ uint32_t opaque_zero() {
   return z;
 }
 
-template <typename Ts, int T, int NV, int EPV, int AL>
+template <typename Ts, int T, int NV, int EPV, int AL, bool NT = (FR_NT_LOAD != 0)>
 __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                             float (&v)[NV][EPV], float fill) {
   if (g.nvec > 0) {
@@ -279,7 +288,7 @@ __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL
     for (int i = 0; i < NV; ++i) {
       uint32_t o = (uint32_t)(i * T * EPV) + lo;
       o = o < last ? o : last;
-      Vec<Ts, EPV>::load(base + o, v[i]);
+      Vec<Ts, EPV>::template load<NT>(base + o, v[i]);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -369,7 +378,7 @@ __device__ __forceinline__ void load_chunks_pf(const Ts* row, const RowGeom<EPV,
 
 // Two row operands of the same geometry in one branch, so that the second
 // operand's loads are issued before the first operand's data is waited for.
-template <typename Ts, int T, int NV, int EPV, int AL>
+template <typename Ts, int T, int NV, int EPV, int AL, bool NT = (FR_NT_LOAD != 0)>
 __device__ __forceinline__ void load_chunks2(const Ts* ra, const Ts* rb, const RowGeom<EPV, AL>& g,
                                              int tid, float (&a)[NV][EPV], float (&b)[NV][EPV],
                                              float fill) {
@@ -380,8 +389,8 @@ __device__ __forceinline__ void load_chunks2(const Ts* ra, const Ts* rb, const R
     for (int i = 0; i < NV; ++i) {
       uint32_t o = (uint32_t)(i * T * EPV) + lo;
       o = o < last ? o : last;
-      Vec<Ts, EPV>::load(ra + g.head + o, a[i]);
-      Vec<Ts, EPV>::load(rb + g.head + o, b[i]);
+      Vec<Ts, EPV>::template load<NT>(ra + g.head + o, a[i]);
+      Vec<Ts, EPV>::template load<NT>(rb + g.head + o, b[i]);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {

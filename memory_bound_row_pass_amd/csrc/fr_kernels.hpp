@@ -14,6 +14,30 @@ void note_launch_error(hipError_t e);
 // Largest grid used; row loops stride by the grid beyond it.
 constexpr int64_t kMaxGrid = int64_t(1) << 30;
 
+// Two-pass (split-row) launches run both passes over one batch of rows before
+// the next batch, so that the second pass re-reads input the first pass has
+// just brought through the memory-side last-level cache (256 MB on MI355X)
+// instead of from HBM. The batch holds at most split_batch_bytes() of input
+// (0: one batch of all rows); FR_SPLIT_BATCH_BYTES is the default, measured
+// best among 32 MB .. 512 MB and unbatched.
+#ifndef FR_SPLIT_BATCH_BYTES
+#define FR_SPLIT_BATCH_BYTES (int64_t(256) << 20)
+#endif
+int64_t split_batch_bytes();  // the current setting (fr_debug_set_split_batch_bytes)
+// Pass-1 loads of the two-pass kernels: ordinary cached loads (0) so that the
+// data stays in the last-level cache for pass 2, or non-temporal (1).
+#ifndef FR_SPLIT_PASS1_NT
+#define FR_SPLIT_PASS1_NT 0
+#endif
+constexpr bool kPass1NT = FR_SPLIT_PASS1_NT != 0;
+inline int64_t split_batch_rows(int64_t rows, int64_t input_bytes_per_row) {
+  const int64_t bytes = split_batch_bytes();
+  if (bytes <= 0) return rows;
+  int64_t b = bytes / input_bytes_per_row;
+  b = b < 1 ? 1 : b;
+  return b < rows ? b : rows;
+}
+
 // A compiled kernel shape: `threads` lanes own one row, each holding `nv`
 // chunks of `epv` elements (epv == 1: scalar path).
 template <typename F>

@@ -14,8 +14,9 @@
 // The merge is the online normaliser's ("Engineering a CUDA Machine Learning
 // Framework from Scratch", §3.1) applied to segment states: partials merged
 // by a second pass. Logits are read twice and the outputs written once;
-// pass 1 uses ordinary (cached) loads so the second read of a segment can
-// come from the last-level cache.
+// pass 1 uses ordinary (cached) loads and the launcher runs both passes over
+// one batch of rows at a time, so that the second read of a segment can come
+// from the last-level cache.
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
@@ -83,7 +84,7 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
     const Tin* xs = x + row * cols + sgm.c0;
     const RowGeom<EPV> g(xs, sgm.len);
     float v[NV][EPV];
-    load_chunks<Tin, T, NV, EPV>(xs, g, tid, v, kNegInf);
+    load_chunks<Tin, T, NV, EPV, kHeadAlign, kPass1NT>(xs, g, tid, v, kNegInf);
     const int ec = g.extra_col(tid);
     float xe = load_extra(xs, ec, kNegInf);
 
@@ -298,7 +299,7 @@ void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int
     const RowGeom<EPV> g(p + off, sgm.len);
     const int ec = g.extra_col(tid);
     float a[NV][EPV], d[NV][EPV];
-    load_chunks2<Ts, T, NV, EPV>(p + off, dy + off, g, tid, a, d, 0.f);
+    load_chunks2<Ts, T, NV, EPV, kHeadAlign, kPass1NT>(p + off, dy + off, g, tid, a, d, 0.f);
     float s0 = load_extra(p + off, ec, 0.f) * load_extra(dy + off, ec, 0.f), s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -362,18 +363,29 @@ static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, c
   const int nseg = (cols + SEG - 1) / SEG;
   const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
   const int skip = XENT && o.use_ignore && !argmax;
-  const unsigned grid = split_grid(rows * nseg);
   const int stats = XENT ? ((o.smoothing != 0.f ? 1 : 0) | (argmax ? 2 : 0)) : 0;
   auto k1 = stats == 0   ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 0>
             : stats == 1 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 1>
             : stats == 2 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 2>
                          : &split_stats_kernel<Tin, T, NV, EPV, OCC, 3>;
-  hipError_t e = launch_kernel(k1, dim3(grid), dim3(T), s, static_cast<const Tin*>(x), rows, cols,
-                               SEG, nseg, labels, o, skip, part);
-  if (e != hipSuccess) return e;
-  return launch_kernel(&split_apply_kernel<Tin, Tout, T, NV, EPV, OCC, XENT>, dim3(grid), dim3(T), s,
-                       static_cast<const Tin*>(x), static_cast<Tout*>(y), rows, cols, SEG, nseg,
-                       static_cast<const float4*>(part), labels, loss, argmax, o);
+  const Tin* xi = static_cast<const Tin*>(x);
+  Tout* yo = static_cast<Tout*>(y);
+  const int64_t batch = split_batch_rows(rows, (int64_t)cols * sizeof(Tin));
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    const unsigned grid = split_grid(nr * nseg);
+    const int64_t e0 = r0 * cols;
+    const int32_t* lb = labels ? labels + r0 : nullptr;
+    hipError_t e = launch_kernel(k1, dim3(grid), dim3(T), s, xi + e0, nr, cols, SEG, nseg, lb, o,
+                                 skip, part + r0 * nseg);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(&split_apply_kernel<Tin, Tout, T, NV, EPV, OCC, XENT>, dim3(grid), dim3(T), s,
+                      xi + e0, yo + e0, nr, cols, SEG, nseg,
+                      static_cast<const float4*>(part + r0 * nseg), lb, loss ? loss + r0 : nullptr,
+                      argmax ? argmax + r0 : nullptr, o);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename Ts, int T, int NV, int EPV, int OCC>
@@ -381,14 +393,24 @@ static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* 
                                            int cols, float4* part, hipStream_t s) {
   constexpr int SEG = T * NV * EPV;
   const int nseg = (cols + SEG - 1) / SEG;
-  const unsigned grid = split_grid(rows * nseg);
-  hipError_t e = launch_kernel(&softmax_bwd_split_stats_kernel<Ts, T, NV, EPV, OCC>, dim3(grid),
-                               dim3(T), s, static_cast<const Ts*>(p), static_cast<const Ts*>(dy),
-                               rows, cols, SEG, nseg, part);
-  if (e != hipSuccess) return e;
-  return launch_kernel(&softmax_bwd_split_apply_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(T), s,
-                       static_cast<const Ts*>(p), static_cast<const Ts*>(dy), static_cast<Ts*>(dx),
-                       rows, cols, SEG, nseg, static_cast<const float4*>(part));
+  const Ts* pi = static_cast<const Ts*>(p);
+  const Ts* di = static_cast<const Ts*>(dy);
+  Ts* xo = static_cast<Ts*>(dx);
+  const int64_t batch = split_batch_rows(rows, (int64_t)cols * 2 * sizeof(Ts));
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    const unsigned grid = split_grid(nr * nseg);
+    const int64_t e0 = r0 * cols;
+    hipError_t e = launch_kernel(&softmax_bwd_split_stats_kernel<Ts, T, NV, EPV, OCC>, dim3(grid),
+                                 dim3(T), s, pi + e0, di + e0, nr, cols, SEG, nseg,
+                                 part + r0 * nseg);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(&softmax_bwd_split_apply_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(T), s,
+                      pi + e0, di + e0, xo + e0, nr, cols, SEG, nseg,
+                      static_cast<const float4*>(part + r0 * nseg));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 #define FR_SP(TI, TO, T, NV, EPV, OCC, X) {T, NV, EPV, &launch_split<TI, TO, T, NV, EPV, OCC, X>}

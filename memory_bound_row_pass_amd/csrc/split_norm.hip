@@ -93,7 +93,7 @@ void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols,
     float v[NV][EPV];
     if constexpr (RMS) {
       float r[NV][EPV];
-      load_chunks2<Ts, T, NV, EPV>(x + off, res + off, g, tid, v, r, 0.f);
+      load_chunks2<Ts, T, NV, EPV, kHeadAlign, kPass1NT>(x + off, res + off, g, tid, v, r, 0.f);
       float he = load_extra(x + off, ec, 0.f) + load_extra(res + off, ec, 0.f);
       float q0 = he * he, q1 = 0.f;
 #pragma unroll
@@ -108,7 +108,7 @@ void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols,
       if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
       if (tid == 0) part[w] = float4{st.s, 0.f, 0.f, 0.f};
     } else {
-      load_chunks<Ts, T, NV, EPV>(x + off, g, tid, v, 0.f);
+      load_chunks<Ts, T, NV, EPV, kHeadAlign, kPass1NT>(x + off, g, tid, v, 0.f);
       const float xe = load_extra(x + off, ec, 0.f);
       WelfordState st = lane_moments<T, NV, EPV>(v, xe, ec, g, tid);
       st = wave_reduce(st, WelfordMerge{});
@@ -222,17 +222,28 @@ static hipError_t launch_norm_split(const void* x, const void* res, const void* 
                                     int cols, float eps, float4* part, hipStream_t s) {
   constexpr int SEG = T * NV * EPV;
   const int nseg = (cols + SEG - 1) / SEG;
-  const int64_t work = rows * nseg;
-  const unsigned grid = (unsigned)(work < kMaxGrid ? work : kMaxGrid);
-  hipError_t e = launch_kernel(&norm_split_stats_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid),
-                               dim3(T), s, static_cast<const Ts*>(x), static_cast<const Ts*>(res),
-                               rows, cols, SEG, nseg, part);
-  if (e != hipSuccess) return e;
-  return launch_kernel(&norm_split_apply_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid), dim3(T), s,
-                       static_cast<const Ts*>(x), static_cast<const Ts*>(res),
-                       static_cast<const Ts*>(p1), static_cast<const Ts*>(p2), static_cast<Ts*>(y),
-                       static_cast<Ts*>(res_out), mean, rstd, rows, cols, SEG, nseg,
-                       static_cast<const float4*>(part), eps);
+  const Ts* xi = static_cast<const Ts*>(x);
+  const Ts* ri = static_cast<const Ts*>(res);
+  Ts* yo = static_cast<Ts*>(y);
+  Ts* ro = static_cast<Ts*>(res_out);
+  const int64_t batch = split_batch_rows(rows, (int64_t)cols * (RMS ? 2 : 1) * sizeof(Ts));
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    const int64_t work = nr * nseg;
+    const unsigned grid = (unsigned)(work < kMaxGrid ? work : kMaxGrid);
+    const int64_t e0 = r0 * cols;
+    hipError_t e = launch_kernel(&norm_split_stats_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid),
+                                 dim3(T), s, xi + e0, ri ? ri + e0 : nullptr, nr, cols, SEG, nseg,
+                                 part + r0 * nseg);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(&norm_split_apply_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid), dim3(T), s,
+                      xi + e0, ri ? ri + e0 : nullptr, static_cast<const Ts*>(p1),
+                      static_cast<const Ts*>(p2), yo + e0, ro ? ro + e0 : nullptr,
+                      mean ? mean + r0 : nullptr, rstd ? rstd + r0 : nullptr, nr, cols, SEG, nseg,
+                      static_cast<const float4*>(part + r0 * nseg), eps);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 #define FR_NS(TS, T, NV, EPV, R) {T, NV, EPV, &launch_norm_split<TS, T, NV, EPV, 4, R>}

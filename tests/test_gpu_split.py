@@ -505,3 +505,53 @@ def test_norm_bwd_split_determinism_rows_zero_and_convenience():
                                   to_dev(mean), to_dev(rstd))
     expect_ln_bwd(w, mean, rstd, fr.F32, (host(dx), dg.cpu().numpy(), db.cpu().numpy()),
                   "layernorm_bwd() of a wide row")
+
+
+# ------------------------------------------------------------ row batches
+
+def _bits(*arrays):
+    return tuple(None if a is None else np.ascontiguousarray(a).tobytes() for a in arrays)
+
+
+@pytest.mark.parametrize("batch_rows", [1, 3, 64])
+def test_split_row_batches(batch_rows):
+    """The two-pass launches run both passes over one batch of rows at a time
+    (bounded by input bytes): batches of 1 and 3 rows (a ragged last batch of
+    7 rows) and one batch of all of them, for every split entry point. Each
+    result matches the oracle and has the same bits as the unbatched call."""
+    R = 7
+    cases = []
+    x = softmax_input(fr.F32, R, 20000, seed=31)
+    cases.append(("softmax f32", 20000 * 4, lambda: (run_softmax_split(x, fr.F32),),
+                  lambda got: expect_softmax(x, fr.F32, got[0], "split softmax batches")))
+    xb = softmax_input(fr.BF16, R, 70001, seed=32)
+    cases.append(("softmax bf16", 70001 * 2, lambda: (run_softmax_split(xb, fr.BF16, offs=(1, 1)),),
+                  lambda got: expect_softmax(xb, fr.BF16, got[0], "split softmax bf16 batches")))
+    opts = dict(ignore_index=-100, label_smoothing=0.1, reduction="mean")
+    for code, es in ((fr.F32, 4), (fr.BF16, 2)):
+        xl, lab = xent_inputs(R, 70000, code, seed=33 + code, ignore_every=3)
+        cases.append((f"xent {code}", 70000 * es,
+                      lambda xl=xl, lab=lab, code=code: run_xent_split(xl, lab, code, opts),
+                      lambda got, xl=xl, lab=lab, code=code: expect_xent(
+                          xl, lab, code, opts, got, f"split xent {code} batches")))
+    wl = workloads.make("layernorm_f32", rows=R, cols=20000, seed=35)
+    cases.append(("layernorm f32", 20000 * 4,
+                  lambda: run_ln_split(wl["x"], wl["gamma"], wl["beta"], wl.eps),
+                  lambda got: expect_layernorm(wl["x"], wl["gamma"], wl["beta"], wl.eps, got,
+                                               "split layernorm batches")))
+    wr = workloads.make("add_rmsnorm_bf16", rows=R, cols=20000, seed=36)
+    cases.append(("rmsnorm bf16", 20000 * 2 * 2,
+                  lambda: run_rms_split(wr["x"], wr["residual"], wr["weight"], wr.eps),
+                  lambda got: expect_rmsnorm(wr["x"], wr["residual"], wr["weight"], wr.eps, got,
+                                             "split rmsnorm batches")))
+    p, dy = softmax_bwd_inputs(R, 20000, fr.BF16, seed=37)
+    cases.append(("softmax bwd bf16", 20000 * 2 * 2, lambda: (run_softmax_bwd_split(p, dy),),
+                  lambda got: expect_softmax_bwd(p, dy, fr.BF16, got[0], "split softmax_bwd batches")))
+    for name, row_bytes, run, expect in cases:
+        print(f"row batches of {batch_rows}: {name}", flush=True)
+        with fr.split_batch_bytes(batch_rows * row_bytes):
+            got = run()
+        with fr.split_batch_bytes(0):
+            whole = run()
+        expect(got)
+        assert _bits(*got) == _bits(*whole), f"{name}: batched and unbatched results differ"

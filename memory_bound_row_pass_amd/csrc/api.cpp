@@ -120,6 +120,19 @@ std::atomic<int64_t> g_split_batch_bytes{FR_SPLIT_BATCH_BYTES};
 namespace fr {
 void note_launch_error(hipError_t e) { t_last_launch_error = static_cast<int>(e); }
 int64_t split_batch_bytes() { return g_split_batch_bytes.load(std::memory_order_relaxed); }
+int device_cu_count() {
+  static std::atomic<int> cache[64];  // 0: not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 }  // namespace fr
 
 extern "C" {

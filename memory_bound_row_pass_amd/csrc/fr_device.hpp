@@ -292,6 +292,7 @@ __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+      if ((i + 1) * T <= g.nvec) continue;  // uniform: the whole slot lies in the row
       const bool ok = i * T + tid < g.nvec;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) v[i][k] = ok ? v[i][k] : fill;
@@ -364,6 +365,91 @@ __device__ __forceinline__ void load_chunks_pf(const Ts* row, const RowGeom<EPV,
     for (int i = 0; i < PF; ++i) RawChunk<Ts>::unpack(r[i], v[i]);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+      if ((i + 1) * T <= g.nvec) continue;  // uniform: the whole slot lies in the row
+      const bool ok = i * T + tid < g.nvec;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = ok ? v[i][k] : fill;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = fill;
+  }
+}
+
+// Next-row staging: LDS slots and register slots. Slot i < LPF of lane t is
+// copied from global memory straight into LDS by global_load_lds_dwordx4,
+// which holds no VGPRs while in flight and writes lane l of a wave at that
+// wave's LDS base + 16 l (checked on gfx950 for both cache policies); with
+// the base of wave w at slot i set to 16 (i T + 64 w), lane t's chunk lands
+// at 16 (i T + t) and is read back by lane t itself, so no barrier is
+// needed. Slots LPF .. LPF + PF - 1 are loaded into registers (`pre`), raw.
+// The compiler does not order these copies against LDS reads:
+// wait_lds_copies() precedes reading staged data, and wait_lds_reads()
+// precedes staging over data that was read.
+__device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <typename Ts, int T, int LPF, int PF, int EPV, int AL>
+__device__ __forceinline__ void stage_row(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
+                                          int wave, uint32_t* stage,
+                                          typename RawChunk<Ts>::T (&pre)[PF > 0 ? PF : 1]) {
+  static_assert(EPV * sizeof(Ts) == 16, "16-byte chunks");
+  if (g.nvec > 0) {
+    const Ts* base = row + g.head;
+    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+#pragma unroll
+    for (int i = 0; i < LPF; ++i) {
+      uint32_t o = (uint32_t)(i * T * EPV) + lo;
+      o = o < last ? o : last;
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(base + o),
+          (__attribute__((address_space(3))) void*)(stage + (i * T + wave * 64) * 4), 16, 0,
+          FR_NT_LOAD ? 2 : 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      uint32_t o = (uint32_t)((LPF + i) * T * EPV) + lo;
+      o = o < last ? o : last;
+      pre[i] = ld_stream(reinterpret_cast<const typename RawChunk<Ts>::T*>(base + o));
+    }
+  }
+}
+
+// The row into registers when its first LPF + PF slots were staged by
+// stage_row: the remaining slots are loaded from global memory, the staged
+// ones taken from LDS (after waiting for the copies unless `copies_done`)
+// and from `pre`; all are masked as in load_chunks.
+template <typename Ts, int T, int NV, int LPF, int PF, int EPV, int AL>
+__device__ __forceinline__ void load_staged(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
+                                            const uint32_t* stage,
+                                            const typename RawChunk<Ts>::T (&pre)[PF > 0 ? PF : 1],
+                                            bool copies_done, float (&v)[NV][EPV], float fill) {
+  static_assert(LPF + PF <= NV, "staged slots");
+  if (g.nvec > 0) {
+    const Ts* base = row + g.head;
+    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
+    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
+#pragma unroll
+    for (int i = LPF + PF; i < NV; ++i) {
+      uint32_t o = (uint32_t)(i * T * EPV) + lo;
+      o = o < last ? o : last;
+      Vec<Ts, EPV>::load(base + o, v[i]);
+    }
+    if (!copies_done) wait_lds_copies();
+#pragma unroll
+    for (int i = 0; i < LPF; ++i) {
+      const typename RawChunk<Ts>::T r =
+          *reinterpret_cast<const typename RawChunk<Ts>::T*>(stage + (i * T + tid) * 4);
+      RawChunk<Ts>::unpack(r, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) RawChunk<Ts>::unpack(pre[i], v[LPF + i]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if ((i + 1) * T <= g.nvec) continue;  // uniform: the whole slot lies in the row
       const bool ok = i * T + tid < g.nvec;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) v[i][k] = ok ? v[i][k] : fill;
@@ -394,6 +480,7 @@ __device__ __forceinline__ void load_chunks2(const Ts* ra, const Ts* rb, const R
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+      if ((i + 1) * T <= g.nvec) continue;  // uniform: the whole slot lies in the row
       const bool ok = i * T + tid < g.nvec;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) {
@@ -423,8 +510,11 @@ __device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV, AL>& g,
   Ts* base = row + g.head;
   const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (i * T + tid < g.nvec) Vec<Ts, EPV>::store(base + ((uint32_t)(i * T * EPV) + lo), v[i]);
+  for (int i = 0; i < NV; ++i) {
+    Ts* p = base + ((uint32_t)(i * T * EPV) + lo);
+    if ((i + 1) * T <= g.nvec) Vec<Ts, EPV>::store(p, v[i]);  // uniform: the whole slot
+    else if (i * T + tid < g.nvec) Vec<Ts, EPV>::store(p, v[i]);
+  }
 }
 
 // Per-column parameters of chunk slot i of this lane (rows on the 128-bit

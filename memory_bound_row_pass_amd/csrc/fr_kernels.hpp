@@ -24,6 +24,7 @@ constexpr int64_t kMaxGrid = int64_t(1) << 30;
 #define FR_SPLIT_BATCH_BYTES (int64_t(256) << 20)
 #endif
 int64_t split_batch_bytes();  // the current setting (fr_debug_set_split_batch_bytes)
+int device_cu_count();        // compute units of the current device (cached per device)
 // Pass-1 loads of the two-pass kernels: ordinary cached loads (0) so that the
 // data stays in the last-level cache for pass 2, or non-temporal (1).
 #ifndef FR_SPLIT_PASS1_NT

@@ -69,7 +69,16 @@ constexpr int kXentBias = 8;
 // PF > 0: the first PF slots of the row owner's next row are loaded before
 // the current row's reduction, so the CU keeps reads in flight while it
 // reduces and writes (PF * 4 more VGPRs per lane).
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0>
+// LPF > 0 (one row per workgroup): the next row is staged while the current
+// one is reduced and written: its first LPF slots in LDS (16 T bytes of LDS
+// per slot, no VGPRs), the next PF slots in registers, and its head/tail
+// element, all issued right after the current row is in registers. The wait
+// for these copies comes before the current row's stores: vector memory
+// operations retire in order, so a wait at the next row's start would also
+// wait for the stores just issued. The grid is then one workgroup per
+// compute unit, each looping over rows.
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0,
+          int LPF = 0>
 __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
 void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, int32_t* argmax,
                  int64_t rows, int cols, XentOptions opt) {
@@ -83,6 +92,8 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
   using Merge = typename std::conditional<OPT, PlusSumMerge<Base, BaseMerge>, BaseMerge>::type;
   constexpr int NF = sizeof(State) / sizeof(float);
   __shared__ float xw[2][NW][NF];
+  static_assert(LPF == 0 || (RPB == 1 && LPF + PF <= NV), "LDS staging: one row per block");
+  __shared__ __attribute__((aligned(16))) uint32_t stage[LPF > 0 ? LPF * T * 4 : 4];
 
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -106,7 +117,19 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
   int label_next = first < rows ? __builtin_amdgcn_readfirstlane(labels[first]) : 0;
   static_assert(PF == 0 || EPV * sizeof(Tin) == 16, "prefetch of 16-byte chunks");
   typename RawChunk<Tin>::T pre[PF > 0 ? PF : 1];
-  bool have_pre = false;  // uniform: pre holds this row's first PF slots
+  bool have_pre = false;     // uniform: pre (and stage) hold this row's first slots
+  bool copies_done = false;  // uniform (LPF): the staging copies were waited for
+  float xe_next = kNegInf;   // LPF: the staged row's head/tail element
+  if constexpr (LPF > 0) {
+    have_pre = first < rows && !(OPT && !ARGMAX && opt.use_ignore && label_next == opt.ignore_index);
+    if (have_pre) {
+      const Tin* x0 = x + first * cols;
+      const RowGeom<EPV> g0(x0, cols);
+      stage_row<Tin, T, LPF, PF, EPV>(x0, g0, tid, wave, stage, pre);
+      const int e0 = g0.extra_col(tid);
+      if (e0 >= 0) xe_next = load1(x0 + e0);
+    }
+  }
 
   int it = 0;
   for (int64_t row = first; row < rows; row += stride, ++it) {
@@ -129,11 +152,20 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
         store_chunks<Tin, T, NV, EPV>(gr, g, tid, z);
         if (ec >= 0) store1(gr + ec, 0.f);
         if (tid == 0) loss[row] = 0.f;
-        if constexpr (PF > 0) {
+        if constexpr (PF > 0 || LPF > 0) {
           have_pre = rn < rows && !(opt.use_ignore && label_next == opt.ignore_index);
           if (have_pre) {
             const Tin* xn = x + rn * cols;
-            prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+            if constexpr (LPF > 0) {
+              wait_lds_reads();
+              const RowGeom<EPV> gn(xn, cols);
+              stage_row<Tin, T, LPF, PF, EPV>(xn, gn, tid, wave, stage, pre);
+              const int en = gn.extra_col(tid);
+              xe_next = en >= 0 ? load1(xn + en) : kNegInf;
+              copies_done = false;
+            } else {
+              prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+            }
           }
         }
         continue;
@@ -147,23 +179,43 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     const bool valid = label >= 0 && label < cols;
     const bool label_lane = valid && !ignored && owner_lane<T, EPV>(label, g) == tid;
     float v[NV][EPV];
-    if constexpr (PF > 0) {
-      if (have_pre) load_chunks_pf<Tin, T, NV, PF, EPV>(xr, g, tid, pre, v, kNegInf);
-      else load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+    float xe;
+    if constexpr (LPF > 0) {
+      if (have_pre) {
+        load_staged<Tin, T, NV, LPF, PF, EPV>(xr, g, tid, stage, pre, copies_done, v, kNegInf);
+        xe = xe_next;
+      } else {
+        load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+        xe = ec >= 0 ? load1(xr + ec) : kNegInf;
+      }
     } else {
-      load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+      if constexpr (PF > 0) {
+        if (have_pre) load_chunks_pf<Tin, T, NV, PF, EPV>(xr, g, tid, pre, v, kNegInf);
+        else load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+      } else {
+        load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
+      }
+      xe = ec >= 0 ? load1(xr + ec) : kNegInf;
     }
-    float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
     float x_label = 0.f;
     if (label_lane) x_label = load1(xr + label);
-    if constexpr (PF > 0) {
+    if constexpr (PF > 0 || LPF > 0) {
       // the next row's first slots (not when it is an ignored row that is
       // not read)
       have_pre = rn < rows &&
                  !(OPT && !ARGMAX && opt.use_ignore && label_next == opt.ignore_index);
       if (have_pre) {
         const Tin* xn = x + rn * cols;
-        prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+        if constexpr (LPF > 0) {
+          wait_lds_reads();  // this row's staged slots are in registers
+          const RowGeom<EPV> gn(xn, cols);
+          stage_row<Tin, T, LPF, PF, EPV>(xn, gn, tid, wave, stage, pre);
+          const int en = gn.extra_col(tid);
+          xe_next = en >= 0 ? load1(xn + en) : kNegInf;
+          copies_done = false;
+        } else {
+          prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+        }
       }
     }
 
@@ -171,16 +223,23 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
     Base bs;
     float tsum = 0.f;
     if constexpr (OPT) {
-      // sum of this lane's logits (masked slots hold -inf and are skipped)
-      const bool full = g.nvec == T * NV;
+      // sum of this lane's logits (masked slots hold -inf and are skipped;
+      // only a slot that runs past the row's end can hold any)
       float t0 = ec >= 0 ? xe : 0.f, t1 = 0.f;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const bool ok = full || i * T + tid < g.nvec;
+        if ((i + 1) * T <= g.nvec) {  // uniform: the whole slot lies in the row
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          const float a = ok ? v[i][k] : 0.f;
-          if (k & 1) t1 += a; else t0 += a;
+          for (int k = 0; k < EPV; ++k) {
+            if (k & 1) t1 += v[i][k]; else t0 += v[i][k];
+          }
+        } else {
+          const bool ok = i * T + tid < g.nvec;
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) {
+            const float a = ok ? v[i][k] : 0.f;
+            if (k & 1) t1 += a; else t0 += a;
+          }
         }
       }
       tsum = t0 + t1;
@@ -227,13 +286,18 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
         for (int k = 0; k < EPV; ++k) v[i][k] = 0.f;
       xe = 0.f;
     } else if constexpr (LOG2) {
-      Log2Scale sc = log2_scale(m, rs.m, rs.s);
-      sc.g *= gsc;
+      // One factor f = g 2^n per lane and one fma per element. With the 2^8
+      // bias every e_j <= 2^8, so where f is subnormal its rounding (at most
+      // 2^-150) moves p_j by at most 2^-142, a 2^-9 fraction of the finest
+      // bf16 step; where f is normal, f = g 2^n exactly and the fma rounds
+      // p_j - offset once.
+      const Log2Scale sc = log2_scale(m, rs.m, rs.s);
+      const float f = __builtin_ldexpf(sc.g * gsc, sc.n);
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) v[i][k] = apply_scale(v[i][k], sc) - goff;
-      xe = apply_scale(xe, sc) - goff;
+        for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf(v[i][k], f, -goff);
+      xe = __builtin_fmaf(xe, f, -goff);
     } else if constexpr (OPT) {
       const float f = nat_scale(m, rs.m, rs.s) * gsc;
 #pragma unroll
@@ -248,6 +312,14 @@ void xent_kernel(const Tin* x, const int32_t* labels, float* loss, Tin* grad, in
 #pragma unroll
         for (int k = 0; k < EPV; ++k) v[i][k] *= f;
       xe *= f;
+    }
+    if constexpr (LPF > 0) {
+      // the next row's copies have had the reduction to arrive; waiting here
+      // keeps the next row's start from waiting for this row's stores
+      if (have_pre) {
+        wait_lds_copies();
+        copies_done = true;
+      }
     }
     store_chunks<Tin, T, NV, EPV>(gr, g, tid, v);
     if (ec >= 0) store1(gr + ec, xe);
@@ -332,16 +404,21 @@ hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* co
   return launch_kernel(&xent_total_kernel, dim3(1), dim3(1024), s, loss, rows, count, total);
 }
 
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0>
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0,
+          int LPF = 0>
 static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss, void* grad,
                               int32_t* argmax, int64_t rows, int cols, const XentOptions* opt,
                               hipStream_t s) {
   constexpr int BLOCK = T == 64 ? 256 : T;
   constexpr int RPB = BLOCK / T;
-  const int64_t blocks = (rows + RPB - 1) / RPB;
+  int64_t blocks = (rows + RPB - 1) / RPB;
+  if (LPF > 0) {  // one resident workgroup per compute unit, looping over rows
+    const int64_t ncu = device_cu_count();
+    blocks = blocks < ncu ? blocks : ncu;
+  }
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
   const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
-  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT, PF>, dim3(grid), dim3(BLOCK), s,
+  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT, PF, LPF>, dim3(grid), dim3(BLOCK), s,
                        static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax,
                        rows, cols, o);
 }
@@ -360,14 +437,27 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
 #ifndef FR_XE_PF_BF16
 #define FR_XE_PF_BF16 1
 #endif
-#define FR_XF(TS, T, NV, EPV, OCC, AM, OPT, PF) \
-  {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT, PF>}
+// LDS staging of the next row (measured at 4096 x 50257): the whole bf16 row
+// (7 slots, 112 KiB) takes the options kernel from 170 to 165 us and the
+// argmax kernel from 284 to 200 us; fp32 rows (9 slots in LDS, the other 4
+// in registers) measured 287 -> 295 us and stay unstaged.
+#ifndef FR_XE_LPF_F32
+#define FR_XE_LPF_F32 0
+#endif
+#ifndef FR_XE_LPF_F32_OPT
+#define FR_XE_LPF_F32_OPT 0
+#endif
+#ifndef FR_XE_LPF_BF16
+#define FR_XE_LPF_BF16 7
+#endif
+#define FR_XF(TS, T, NV, EPV, OCC, AM, OPT, PF, LPF) \
+  {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT, PF, LPF>}
 #define FR_XE_F32(AM, OPT)                                                                       \
   {FR_XE(float, 64, 1, 4, 8, AM, OPT),    FR_XE(float, 64, 2, 4, 8, AM, OPT),                    \
    FR_XE(float, 64, 4, 4, 8, AM, OPT),    FR_XE(float, 64, 8, 4, 6, AM, OPT),                    \
    FR_XE(float, 64, 16, 4, 4, AM, OPT),   FR_XE(float, 256, 8, 4, 6, AM, OPT),                   \
    FR_XE(float, 512, 8, 4, 6, AM, OPT),   FR_XE(float, 1024, 8, 4, 4, AM, OPT),                  \
-   FR_XF(float, 1024, 13, 4, 4, AM, OPT, (OPT ? FR_XE_PF_F32_OPT : FR_XE_PF_F32)), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
+   FR_XF(float, 1024, 13, 4, 4, AM, OPT, (OPT ? FR_XE_PF_F32_OPT : FR_XE_PF_F32), (OPT ? FR_XE_LPF_F32_OPT : FR_XE_LPF_F32)), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
    FR_XE(float, 256, 50, 4, 2, AM, OPT),  FR_XE(float, 1024, 16, 4, 4, AM, OPT),                 \
    FR_XE(float, 64, 16, 1, 4, AM, OPT),   FR_XE(float, 256, 16, 1, 4, AM, OPT),                  \
    FR_XE(float, 1024, 16, 1, 4, AM, OPT), FR_XE(float, 1024, 64, 1, 4, AM, OPT)}
@@ -375,7 +465,7 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   {FR_XE(bf16_t, 64, 1, 8, 8, AM, true),    FR_XE(bf16_t, 64, 2, 8, 8, AM, true),                \
    FR_XE(bf16_t, 64, 4, 8, 6, AM, true),    FR_XE(bf16_t, 64, 8, 8, 4, AM, true),                \
    FR_XE(bf16_t, 256, 4, 8, 6, AM, true),   FR_XE(bf16_t, 512, 4, 8, 6, AM, true),               \
-   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XF(bf16_t, 1024, 7, 8, 4, AM, true, FR_XE_PF_BF16),              \
+   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XF(bf16_t, 1024, 7, 8, 4, AM, true, (FR_XE_LPF_BF16 ? 0 : FR_XE_PF_BF16), FR_XE_LPF_BF16),              \
    FR_XE(bf16_t, 1024, 8, 8, 4, AM, true),  FR_XE(bf16_t, 64, 16, 1, 4, AM, true),               \
    FR_XE(bf16_t, 256, 16, 1, 4, AM, true),  FR_XE(bf16_t, 1024, 16, 1, 4, AM, true),             \
    FR_XE(bf16_t, 1024, 64, 1, 4, AM, true)}

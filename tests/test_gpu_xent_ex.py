@@ -300,3 +300,27 @@ def test_non_default_stream():
     torch.cuda.synchronize()
     opts = dict(ignore_index=-100, label_smoothing=0.1, reduction="mean")
     expect(x, lab, fr.F32, opts, run(x, lab, fr.F32, opts, stream=s.cuda_stream), "xent_ex side stream")
+
+
+# ------------------------------------------- several rows per workgroup
+
+@pytest.mark.parametrize("C", [50257, 40001])
+def test_many_rows_per_workgroup(C):
+    """More rows than compute units, so each workgroup of the 1024-lane
+    kernels loops over several rows; the bf16 kernel stages the next row in
+    LDS while it reduces and writes the current one. Ignored rows are
+    interleaved (the first row among them), with and without argmax,
+    misaligned and in place."""
+    R = 700
+    assert fr.fr_debug_select_variant(fr.OP_XENT, C, fr.BF16) == (1024, 7, 8)
+    opts = dict(ignore_index=-100, label_smoothing=0.1, reduction="mean")
+    for code in (fr.BF16, fr.F32):
+        x, lab = inputs(R, C, code, seed=C + code, ignore_every=3)
+        print(f"many rows: {code} {R}x{C}", flush=True)
+        for am in (True, False):
+            expect(x, lab, code, opts, run(x, lab, code, opts, argmax=am),
+                   f"xent_ex {code} {R}x{C} argmax={am}")
+        expect(x, lab, code, opts, run(x, lab, code, opts, argmax=False, offs=(1, 1)),
+               f"xent_ex {code} {R}x{C} misaligned")
+        expect(x, lab, code, dict(), run(x, lab, code, dict(), argmax=False, inplace=True),
+               f"xent_ex {code} {R}x{C} in place")

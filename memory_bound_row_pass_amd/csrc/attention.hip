@@ -41,6 +41,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAttnBlockM = 128;  // queries per workgroup (4 waves x 32)
 constexpr float kLazy = 8.f;      // stale-max allowance, base-2 units
+// FR_ATTN_PRIO: raise the wave's issue priority over its matrix-core chains,
+// so that the other waves of the SIMD fill the gaps with their softmax work
+// (measured 594 -> 585 us and 320 -> 317 us at B=4 H=16 S=4096 D=128)
+#ifndef FR_ATTN_PRIO
+#define FR_ATTN_PRIO 1
+#endif
+__device__ __forceinline__ void mfma_prio_hi() {
+  if constexpr (FR_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void mfma_prio_lo() {
+  if constexpr (FR_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -178,6 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     f32x16 s[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) s[t] = f32x16{};
+    mfma_prio_hi();
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -186,6 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[kk]), s[t], 0, 0,
                                                        0);
       }
+    mfma_prio_lo();
 
     // online softmax for query qi over keys n0 + 32t + key(j),
     // key(j) = (j/4)*8 + 4h + j%4; t = scale_log2 * s (base-2 units)
@@ -273,6 +287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int vrow = 4 * h + (g16 >> 2);                       // key within 8
       const int vcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);   // d within 32
       const lds_bf16* vl = (const lds_bf16*)vt + vrow * VS + vcol;  // generic -> LDS pointer
+      mfma_prio_hi();
 #pragma unroll
       for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -287,6 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[2 * t + st]),
                                                              acc[b], 0, 0, 0);
           }
+      mfma_prio_lo();
     }
 
     if (blk + 1 < nblk) {

@@ -387,3 +387,21 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(2, 3)
     with pytest.raises(ValueError):
         fr.fr_softmax_fwd(x, torch.zeros(2, 3))
+
+
+def test_split_batch_setting():
+    # host-side setting only: returns the previous value; < 0 restores the
+    # built-in 256 MiB bound; 0 means one batch of all rows
+    L = fr.lib
+    default = 256 << 20
+    prev = L.fr_debug_set_split_batch_bytes(12345)
+    try:
+        assert prev == default
+        assert L.fr_debug_set_split_batch_bytes(0) == 12345
+        assert L.fr_debug_set_split_batch_bytes(-7) == 0
+        assert L.fr_debug_set_split_batch_bytes(-1) == default
+        with fr.split_batch_bytes(1):
+            assert L.fr_debug_set_split_batch_bytes(1) == 1
+        assert L.fr_debug_set_split_batch_bytes(-1) == default
+    finally:
+        L.fr_debug_set_split_batch_bytes(-1)

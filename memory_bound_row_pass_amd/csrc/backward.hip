@@ -247,16 +247,59 @@ struct BwdLanes {
 
 // DRES: the gradient through the updated residual is given; its loads are
 // issued with those of h and dy, before the row reduction.
-template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool DRES>
+// STG: the row operands of the workgroup's next rows are staged in LDS
+// (global_load_lds_dwordx4, 16 bytes per lane and slot, read back by the
+// lane that requested them) while the current rows are reduced and written;
+// the wait for them comes before the current rows' stores (vector memory
+// operations retire in order).
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool DRES, bool STG = false>
 __global__ __launch_bounds__(T * RPB) __attribute__((amdgpu_waves_per_eu(OCC)))
 void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, Ts* dh, float* ws,
                         int64_t rows, int cols, float eps) {
   using L = BwdLanes<T, RPB>;
   constexpr int NW = L::NW;
+  constexpr int NOP = DRES ? 3 : 2;  // staged row operands
+  static_assert(!STG || EPV * sizeof(Ts) == 16, "staging: 16-byte chunks");
   __shared__ float xw[RPB][2][NW][2];
   __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[STG ? NOP * NV * T * RPB * 4 : 4];
   const L ln;
   const Slots<T, NV, EPV> sl(cols, ln.tid);
+  using Raw = typename RawChunk<Ts>::T;
+  const int wib = ln.sub * NW + ln.wave;  // wave index in the workgroup
+  // stage operand `op` of the row at element offset `o`: slot i of lane
+  // (wib, l) lands at 16 ((op NV + i) T RPB + 64 wib + l)
+  auto stage_op = [&](const Ts* src, int op) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(src + sl.off(i)),
+          (__attribute__((address_space(3))) void*)(stage + ((op * NV + i) * T * RPB + 64 * wib) * 4),
+          16, 0, FR_NT_LOAD ? 2 : 0);
+  };
+  auto stage_rows = [&](int64_t b) {  // the rows of iteration base b (uniform)
+    const int64_t rw = b + ln.sub;
+    const int64_t o = (rw < rows ? rw : rows - 1) * cols;
+    stage_op(h + o, 0);
+    stage_op(dy + o, 1);
+    if constexpr (DRES) stage_op(dres + o, 2);
+  };
+  auto unstage_op = [&](int op, float (&v)[NV][EPV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const Raw r = *reinterpret_cast<const Raw*>(stage + ((op * NV + i) * T * RPB + threadIdx.x) * 4);
+      RawChunk<Ts>::unpack(r, v[i]);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = sl.ok(i) ? v[i][k] : 0.f;
+    }
+  };
+  bool staged = false, copies_done = false;  // uniform in the workgroup
+  if constexpr (STG) {
+    if ((int64_t)blockIdx.x * RPB < rows) {
+      stage_rows((int64_t)blockIdx.x * RPB);
+      staged = true;
+    }
+  }
 
   float acc[NV][EPV];  // dw partials
 #pragma unroll
@@ -272,8 +315,22 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
     const int64_t off = (live ? row : rows - 1) * cols;
 
     float hv[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
-    if constexpr (DRES) sl.load3(h + off, dy + off, dres + off, hv, d, dr);
-    else sl.load2(h + off, dy + off, hv, d);
+    if constexpr (STG) {
+      if (!copies_done) wait_lds_copies();
+      unstage_op(0, hv);
+      unstage_op(1, d);
+      if constexpr (DRES) unstage_op(2, dr);
+      const int64_t nb = base + (int64_t)gridDim.x * RPB;
+      staged = nb < rows;
+      if (staged) {
+        wait_lds_reads();  // this iteration's staged rows are in registers
+        stage_rows(nb);
+        copies_done = false;
+      }
+    } else {
+      if constexpr (DRES) sl.load3(h + off, dy + off, dres + off, hv, d, dr);
+      else sl.load2(h + off, dy + off, hv, d);
+    }
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
     const Ts* w1 = fresh(w);
 #pragma unroll
@@ -308,8 +365,14 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
           else hv[i][k] = t;
         }
       }
-      sl.store(dh + off, hv);
     }
+    if constexpr (STG) {
+      if (staged) {  // uniform: before this iteration's stores
+        wait_lds_copies();
+        copies_done = true;
+      }
+    }
+    if (live) sl.store(dh + off, hv);
   }
   flush_partials<T, NV, EPV, RPB>(acc, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
 }
@@ -605,12 +668,15 @@ static hipError_t launch_softmax_bwd(const void* p, const void* dy, void* dx, in
                        rows, cols);
 }
 
-template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool STG = false>
 static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w,
                                      void* dh, float* ws, int grid, int64_t rows, int cols,
                                      float eps, hipStream_t s) {
-  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true>
-                : &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, false>;
+  // staging only without dres: three staged operands (96 KiB through LDS per
+  // iteration) measured slower (100.0 -> 102.7 us at 8192^2), two faster
+  // (90.8 -> 83.1 us)
+  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true, false>
+                : &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, false, STG>;
   return launch_kernel(k, dim3(grid), dim3(T * RPB), s, static_cast<const Ts*>(h),
                        static_cast<const Ts*>(dy), static_cast<const Ts*>(dres),
                        static_cast<const Ts*>(w), static_cast<Ts*>(dh), ws, rows, cols, eps);
@@ -685,6 +751,13 @@ hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* x
 // workgroup is 1024 lanes (RPB = 1024 / T) with one workgroup per CU
 // (grid_max 256, OCC 4: at most 128 VGPRs).
 #define FR_RB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC>}
+// The 8192-column bf16 shape stages its next rows (h and dy, 64 KiB) in LDS
+// when no dres is given.
+#ifndef FR_RB_STG
+#define FR_RB_STG 1
+#endif
+#define FR_RBS(TS, T, NV, EPV, RPB, OCC, G) \
+  {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC, (FR_RB_STG != 0)>}
 #define FR_LB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_layernorm_bwd<TS, T, NV, EPV, RPB, OCC>}
 #define FR_SB(TS, T, NV, EPV, OCC) {T, NV, EPV, &launch_softmax_bwd<TS, T, NV, EPV, OCC>}
 
@@ -707,7 +780,7 @@ static const RmsNormBwdVariant kRbF32[] = {
 static const RmsNormBwdVariant kRbBf16[] = {
     FR_RB(bf16_t, 64, 1, 8, 16, 4, 256),  FR_RB(bf16_t, 64, 2, 8, 16, 4, 256),
     FR_RB(bf16_t, 256, 1, 8, 4, 4, 256),  FR_RB(bf16_t, 256, 2, 8, 4, 4, 256),
-    FR_RB(bf16_t, 512, 2, 8, 2, 4, 256),  FR_RB(bf16_t, 1024, 2, 8, 1, 4, 256),
+    FR_RBS(bf16_t, 512, 2, 8, 2, 4, 256), FR_RB(bf16_t, 1024, 2, 8, 1, 4, 256),
     FR_RB(bf16_t, 64, 16, 1, 16, 4, 256), FR_RB(bf16_t, 256, 16, 1, 4, 4, 256),
     FR_RB(bf16_t, 1024, 16, 1, 1, 4, 256)};
 

@@ -441,3 +441,21 @@ def test_graph_capture_replays_match_eager():
             iv = torch.int16 if o.dtype == torch.bfloat16 else torch.int32
             assert torch.equal(o.view(iv), e.view(iv)), rep
     expect_rms_bwd(wr, fr.BF16, (bf16_bits(eager[1]), eager[2].cpu().numpy()), "graph rms_bwd")
+
+
+@pytest.mark.parametrize("C", [8192, 5000])
+def test_rms_bwd_several_sweeps(C):
+    """More rows than one sweep of the persistent grid (256 workgroups x 2 row
+    groups): every workgroup walks several rows; without dres the bf16
+    8192-column shape stages its next rows in LDS. Rows past the last sweep's
+    end (a partial sweep) take part with no data."""
+    code = fr.BF16
+    assert fr.fr_debug_select_variant(fr.OP_RMSNORM_BWD, C, code) == (512, 2, 8)
+    R = 1100
+    w = rms_bwd_inputs(R, C, code, seed=C + 3)
+    print(f"rms_bwd sweeps bf16 {R}x{C}", flush=True)
+    for with_dres in (False, True):
+        expect_rms_bwd(w, code, run_rms_bwd(w, code, with_dres=with_dres),
+                       f"rms_bwd bf16 {R}x{C} dres={with_dres}", with_dres=with_dres)
+    expect_rms_bwd(w, code, run_rms_bwd(w, code, with_dres=False, inplace="dy"),
+                   f"rms_bwd bf16 {R}x{C} in place", with_dres=False)

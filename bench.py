@@ -21,7 +21,8 @@ and the CPU oracle timed on the host cores as a baseline.
 
 The backward entry points are measured after the step, per call, at the
 forward workloads' shapes (softmax bf16 [16384, 4096], LayerNorm fp32
-[4096, 1024], residual-add + RMSNorm bf16 [8192, 8192]), and so are the
+[4096, 1024], residual-add + RMSNorm bf16 [8192, 8192] with the residual's
+gradient and the plain RMSNorm backward without it), and so are the
 cross-entropy variants (fr_softmax_xent_ex at [4096, 50257], fp32 and bf16
 logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
 split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
@@ -81,6 +82,8 @@ def bwd_algo_bytes(name, R, C):
         return 3 * R * C * 4 + C * 4 + 2 * R * 4 + 2 * C * 4   # x, dy, dx; gamma; mean, rstd; dg, db
     if name == "add_rmsnorm_bwd_bf16":
         return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
+    if name == "rmsnorm_bwd_bf16":
+        return 3 * R * C * 2 + C * 2 + C * 4                   # h, dy, dh; w; dw
     if name in ("xent_split_f32", "xent_split_bf16"):
         # one read of the logits and one write of the gradient (the split path
         # reads the logits twice: 1.5x these bytes move); labels, loss
@@ -205,14 +208,17 @@ class BwdWorkload:
             self.run = lambda: fr.fr_add_rmsnorm_fwd_split(self.x, self.r, self.wt, self.y, self.ws,
                                                            self.ro, w.eps)
             self.op, self.code = fr.OP_RMSNORM_SPLIT, fr.BF16
-        elif name == "add_rmsnorm_bwd_bf16":
+        elif name in ("add_rmsnorm_bwd_bf16", "rmsnorm_bwd_bf16"):
+            # with the gradient through the updated residual (dres), and the
+            # plain RMSNorm backward without it
             self.h, self.dy, self.dres = d(w["h"]), d(w["dy"]), d(w["dres"])
             self.wt = d(w["weight"])
             self.dh = torch.empty_like(self.h)
             self.dw = torch.empty(self.C, device=dev)
             self.ws = ws(fr.OP_RMSNORM_BWD)
+            dres = self.dres if name == "add_rmsnorm_bwd_bf16" else None
             self.run = lambda: fr.fr_add_rmsnorm_bwd(self.h, self.dy, self.wt, self.dh, self.dw,
-                                                     self.ws, dres=self.dres, eps=w.eps)
+                                                     self.ws, dres=dres, eps=w.eps)
             self.op, self.code = fr.OP_RMSNORM_BWD, fr.BF16
         if self.op is not None:
             self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
@@ -548,6 +554,8 @@ def main():
             t0 = time.perf_counter()
             bws.append(BwdWorkload(n, workloads.make(n), dev, torch, fr))
             log(f"generated {n} in {time.perf_counter() - t0:.1f} s")
+            if n == "add_rmsnorm_bwd_bf16":  # the same inputs, no dres
+                bws.append(BwdWorkload("rmsnorm_bwd_bf16", bws[-1].w, dev, torch, fr))
         nb = len(bws)
         for n, dt in (("xent_ex_f32", "f32"), ("xent_ex_bf16", "bf16")):
             bws.append(BwdWorkload(n, workloads.make("xent_f32", dtype=dt), dev, torch, fr))

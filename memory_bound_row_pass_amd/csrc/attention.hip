@@ -14,7 +14,8 @@
 //     the wave's queries held in registers for the whole kernel);
 //   in the MFMA C layout lane l owns query l % 32 and 16 of the 32 keys (the
 //     other 16 are in lane l ^ 32), so the per-query max and sum take the
-//     lane's 16 values and one exchange with lane l ^ 32, and the rescale of
+//     lane's 16 values and one exchange with lane l ^ 32 (v_permlane32_swap,
+//     no LDS round trip: 604 -> 588 us), and the rescale of
 //     the output accumulator is one per-lane factor;
 //   O^T (D x 32 queries) += V_blk^T (A operand, from a transposed V tile in
 //     LDS) * P^T (B operand: the lane's 16 probabilities as they are). The C
@@ -55,6 +56,18 @@ __device__ __forceinline__ void mfma_prio_lo() {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// The values of lanes l % 32 and l % 32 + 32 in every lane l, through
+// v_permlane32_swap (a VALU exchange of the two wave halves) instead of an
+// LDS permute: with both operands x, one result holds the low half's value
+// and the other the high half's, in every lane.
+struct HalfPair {
+  float lo, hi;
+};
+__device__ __forceinline__ HalfPair half_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 
 // LDS-address-space views for the transposing LDS read (ds_read_b64_tr_b16)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -232,8 +245,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     }
     float tmax = smax * scale_log2;
     tmax = tmax != tmax ? kNegInf : tmax;  // a masked -inf * 0 scale
-    const float tpart = __shfl_xor(tmax, 32);
-    tmax = tmax > tpart ? tmax : tpart;
+    {
+      const HalfPair t2 = half_pair(tmax);
+      tmax = t2.lo > t2.hi ? t2.lo : t2.hi;
+    }
     // raise the running max only past the allowance (wave-uniform decision)
     const bool raise = tmax > m_run + kLazy;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -263,7 +278,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) lsum += s[t][j];
-    lsum += __shfl_xor(lsum, 32);
+    {
+      const HalfPair l2 = half_pair(lsum);
+      lsum = l2.lo + l2.hi;
+    }
     l_run += lsum;
 
     // P^T as B operands: tile t, k-step 0 = the lane's j 0..7, k-step 1 = j 8..15

@@ -28,7 +28,9 @@ logits, every 9th row ignored, label smoothing 0.1, mean reduction) and the
 split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
 [2048, 131072], bf16 [1024, 262144]), the split-row norms (LayerNorm fp32
 [512, 131072], residual-add + RMSNorm bf16 [256, 262144]), the split-row
-softmax backward (bf16 [1024, 131072]) and the split-row residual-add +
+softmax backward (bf16 [1024, 131072]), one GPU's share of an 8-way
+row-sharded cross-entropy step (fp32 [512, 50257], one-pass and split-row
+kernels) and the split-row residual-add +
 RMSNorm backward (bf16 [2048, 32768], hidden size beyond the one-pass
 backward); they are
 reported under "backward" and "variants" and are not part of `value`; so is the
@@ -84,6 +86,8 @@ def bwd_algo_bytes(name, R, C):
         return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
     if name == "rmsnorm_bwd_bf16":
         return 3 * R * C * 2 + C * 2 + C * 4                   # h, dy, dh; w; dw
+    if name in ("xent_shard_f32", "xent_shard_split_f32"):
+        return 2 * R * C * 4 + 2 * R * 4                       # logits, grad; labels, loss
     if name in ("xent_split_f32", "xent_split_bf16"):
         # one read of the logits and one write of the gradient (the split path
         # reads the logits twice: 1.5x these bytes move); labels, loss
@@ -154,7 +158,14 @@ class BwdWorkload:
                                                      label_smoothing=0.1, reduction="mean")
             self.op = fr.OP_XENT
             self.code = fr.BF16 if name == "xent_ex_bf16" else fr.F32
-        elif name in ("xent_split_f32", "xent_split_bf16"):
+        elif name == "xent_shard_f32":
+            # one GPU's share of an 8-way row-sharded cross-entropy step
+            self.x, self.lab = d(w["logits"]), d(w["labels"])
+            self.loss = torch.empty(self.R, device=dev)
+            self.grad = torch.empty_like(self.x)
+            self.run = lambda: fr.fr_softmax_xent_fwd_bwd(self.x, self.lab, self.loss, self.grad)
+            self.op, self.code = fr.OP_XENT, fr.F32
+        elif name in ("xent_split_f32", "xent_split_bf16", "xent_shard_split_f32"):
             # wide vocabularies through the split-row path, no options
             self.x, self.lab = d(w["logits"]), d(w["labels"])
             self.loss = torch.empty(self.R, device=dev)
@@ -221,7 +232,7 @@ class BwdWorkload:
                                                      self.ws, dres=dres, eps=w.eps)
             self.op, self.code = fr.OP_RMSNORM_BWD, fr.BF16
         if self.op is not None:
-            self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
+            self.variant = fr.fr_debug_select_variant_for(self.op, self.R, self.C, self.code)
 
 
 def time_calls(torch, np, runs, K):
@@ -350,7 +361,7 @@ class Workload:
             self.grad = torch.empty_like(self.x)
             self.run = lambda: fr.fr_softmax_xent_fwd_bwd(self.x, self.lab, self.loss, self.grad)
             self.op, self.code = fr.OP_XENT, fr.F32
-        self.variant = fr.fr_debug_select_variant(self.op, self.C, self.code)
+        self.variant = fr.fr_debug_select_variant_for(self.op, self.R, self.C, self.code)
 
 
 def copy_ceiling(torch, fr, dev, nbytes=2 << 30, reps=20):
@@ -561,7 +572,9 @@ def main():
             bws.append(BwdWorkload(n, workloads.make("xent_f32", dtype=dt), dev, torch, fr))
             log(f"generated {n}")
         for n, dt, R, C in (("xent_split_f32", "f32", 2048, 131072),
-                            ("xent_split_bf16", "bf16", 1024, 262144)):
+                            ("xent_split_bf16", "bf16", 1024, 262144),
+                            ("xent_shard_f32", "f32", 512, 50257),
+                            ("xent_shard_split_f32", "f32", 512, 50257)):
             bws.append(BwdWorkload(n, workloads.make("xent_f32", rows=R, cols=C, dtype=dt), dev,
                                    torch, fr))
             log(f"generated {n}")

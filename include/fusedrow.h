@@ -442,6 +442,15 @@ FR_API fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t 
                                     fr_dtype_t out_dtype, int vector_path,
                                     int* threads, int* vecs, int* elems_per_vec);
 
+/* As fr_debug_select_variant, for a call over `rows` rows (>= 0): the
+ * cross-entropy entry points may then take a 256-lane shape instead of a
+ * 1024-lane one when the rows fill the device's compute units once but not
+ * twice (two rows per compute unit resident instead of one). */
+FR_API fr_status_t fr_debug_select_variant_for(fr_op_t op, int64_t rows, int64_t cols,
+                                        fr_dtype_t in_dtype, fr_dtype_t out_dtype,
+                                        int vector_path, int* threads, int* vecs,
+                                        int* elems_per_vec);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ __all__ = [
     "F32", "BF16", "FR_MAX_COLS", "FusedRowError", "lib", "status_str", "version",
     "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
     "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
+    "fr_debug_select_variant_for",
     "fr_debug_set_split_batch_bytes", "split_batch_bytes",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
@@ -102,6 +103,7 @@ def _load() -> ctypes.CDLL:
         "fr_layernorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, P],
         "fr_debug_force_variant": [I32, I32, I32],
         "fr_debug_select_variant": [I32, I64, I32, I32, I32, IP, IP, IP],
+        "fr_debug_select_variant_for": [I32, I64, I64, I32, I32, I32, IP, IP, IP],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -528,6 +530,19 @@ def fr_debug_select_variant(op: int, cols: int, in_dtype: int = F32, out_dtype: 
     _check(lib.fr_debug_select_variant(int(op), int(cols), int(in_dtype), int(od), int(vector_path),
                                        ctypes.byref(t), ctypes.byref(v), ctypes.byref(e)),
            "fr_debug_select_variant")
+    return t.value, v.value, e.value
+
+
+def fr_debug_select_variant_for(op: int, rows: int, cols: int, in_dtype: int = F32,
+                                out_dtype: int | None = None, vector_path: bool = True):
+    """C: fr_debug_select_variant_for (the shape a call over `rows` rows takes;
+    queries the current device's compute-unit count)."""
+    t, v, e = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    od = in_dtype if out_dtype is None else out_dtype
+    _check(lib.fr_debug_select_variant_for(int(op), int(rows), int(cols), int(in_dtype), int(od),
+                                           int(vector_path), ctypes.byref(t), ctypes.byref(v),
+                                           ctypes.byref(e)),
+           "fr_debug_select_variant_for")
     return t.value, v.value, e.value
 
 

@@ -93,6 +93,28 @@ const V* select_variant(VariantSpan<V> sp, int op, int64_t cols, int epv) {
 
 fr_status_t launch_status(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_LAUNCH; }
 
+// Rows that fill the chip once but not twice (ncu < rows <= 2 ncu, such as
+// one GPU's share of a row-sharded batch): where the width-chosen shape is a
+// 1024-lane one (one resident row per CU: two rounds), a 256-lane shape that
+// holds the row keeps two rows per CU resident and runs them all in one
+// round. Measured, cross-entropy fp32 [512, 50257]: 38.8 -> 34.3 us (at 256
+// and at 1024+ rows the 1024-lane shape stays faster). Not with a forced
+// variant. Queries the device's CU count (a HIP call), so only after the
+// argument checks.
+template <typename V>
+const V* few_rows_variant(VariantSpan<V> sp, int op, int64_t rows, int64_t cols, int epv,
+                          const V* dflt) {
+  if (!dflt || dflt->threads != 1024 || g_forced[op].threads.load(std::memory_order_relaxed))
+    return dflt;
+  const int64_t ncu = fr::device_cu_count();
+  if (rows <= ncu || rows > 2 * ncu) return dflt;
+  for (size_t i = 0; i < sp.n; ++i) {
+    const V& v = sp.v[i];
+    if (v.epv == epv && v.threads == 256 && (int64_t)v.threads * v.nv * v.epv >= cols) return &v;
+  }
+  return dflt;
+}
+
 // Split-row shape: a forced (threads, vecs), else the table's first shape on
 // the requested path (the smallest segment: measured fastest on MI355X).
 template <typename V>
@@ -171,9 +193,11 @@ fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs) {
   return FR_OK;
 }
 
-fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtype,
-                                    fr_dtype_t out_dtype, int vector_path, int* threads, int* vecs,
-                                    int* elems_per_vec) {
+namespace {
+// rows < 0: the width-only choice (fr_debug_select_variant)
+fr_status_t describe_variant(fr_op_t op, int64_t rows, int64_t cols, fr_dtype_t in_dtype,
+                             fr_dtype_t out_dtype, int vector_path, int* threads, int* vecs,
+                             int* elems_per_vec) {
   if (!threads || !vecs || !elems_per_vec) return FR_E_NULL;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return FR_E_DTYPE;
   const bool split = op == FR_OP_SOFTMAX_SPLIT || op == FR_OP_XENT_SPLIT ||
@@ -203,8 +227,9 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
     case FR_OP_XENT: {
       // fp32: the plain table (the options table has the same shapes); bf16
       // logits exist only with options
-      auto v = select_variant(in_dtype == FR_BF16 ? fr::xent_ex_variants(1, 0) : fr::xent_variants(0, 0),
-                              op, cols, epv);
+      const auto sp = in_dtype == FR_BF16 ? fr::xent_ex_variants(1, 0) : fr::xent_variants(0, 0);
+      auto v = select_variant(sp, op, cols, epv);
+      if (rows >= 0) v = few_rows_variant(sp, op, rows, cols, epv, v);
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -252,6 +277,22 @@ fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtyp
   if (!t) return FR_E_VARIANT;
   *threads = t; *vecs = n; *elems_per_vec = e;
   return FR_OK;
+}
+}  // namespace
+
+fr_status_t fr_debug_select_variant(fr_op_t op, int64_t cols, fr_dtype_t in_dtype,
+                                    fr_dtype_t out_dtype, int vector_path, int* threads, int* vecs,
+                                    int* elems_per_vec) {
+  return describe_variant(op, -1, cols, in_dtype, out_dtype, vector_path, threads, vecs,
+                          elems_per_vec);
+}
+
+fr_status_t fr_debug_select_variant_for(fr_op_t op, int64_t rows, int64_t cols, fr_dtype_t in_dtype,
+                                        fr_dtype_t out_dtype, int vector_path, int* threads,
+                                        int* vecs, int* elems_per_vec) {
+  if (rows < 0) return FR_E_SHAPE;
+  return describe_variant(op, rows, cols, in_dtype, out_dtype, vector_path, threads, vecs,
+                          elems_per_vec);
 }
 
 fr_status_t fr_softmax_fwd(const void* x, void* y, int64_t rows, int64_t cols, fr_dtype_t x_dtype,
@@ -353,8 +394,10 @@ fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* labels, f
   if (fr_status_t s = check_alias(bufs, 5)) return s;
   const bool vec =
       (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
-  const fr::XentVariant* v = select_variant(fr::xent_variants(0, argmax != nullptr), FR_OP_XENT, cols,
-                                            vec ? vec_epv(es) : 1);
+  const auto sp = fr::xent_variants(0, argmax != nullptr);
+  const int epv = vec ? vec_epv(es) : 1;
+  const fr::XentVariant* v =
+      few_rows_variant(sp, FR_OP_XENT, rows, cols, epv, select_variant(sp, FR_OP_XENT, cols, epv));
   if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
   return launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols, nullptr,
                                  static_cast<hipStream_t>(stream)));
@@ -398,8 +441,10 @@ fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels, float*
   if (fr_status_t s = check_alias(bufs, 6)) return s;
   const bool vec =
       (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
-  const fr::XentVariant* v = select_variant(fr::xent_ex_variants(dtype == FR_BF16, argmax != nullptr),
-                                            FR_OP_XENT, cols, vec ? vec_epv(es) : 1);
+  const auto sp = fr::xent_ex_variants(dtype == FR_BF16, argmax != nullptr);
+  const int epv = vec ? vec_epv(es) : 1;
+  const fr::XentVariant* v =
+      few_rows_variant(sp, FR_OP_XENT, rows, cols, epv, select_variant(sp, FR_OP_XENT, cols, epv));
   if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
   if (count)
     if (fr_status_t s = launch_status(

@@ -562,3 +562,25 @@ def test_graph_capture_replays_match_eager():
                                e.view(torch.int16) if e.dtype == torch.bfloat16 else e.view(torch.int32)), rep
     # and the eager result itself is right
     check_bf16(bf16_bits(ys), ref_bf16(oracle.softmax(ws["x"])), "graph softmax")
+
+
+def test_xent_few_rows_shape():
+    """Rows that fill the compute units once but not twice (one GPU's share
+    of a row-sharded batch) take the 256-lane cross-entropy shape, two rows
+    per compute unit: parity with the oracle and the same bits as that shape
+    forced; one row per CU, or more than two, keeps the 1024-lane shape."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    C = 50257
+    assert fr.fr_debug_select_variant_for(fr.OP_XENT, ncu, C, fr.F32) == (1024, 13, 4)
+    assert fr.fr_debug_select_variant_for(fr.OP_XENT, 2 * ncu + 1, C, fr.F32) == (1024, 13, 4)
+    for R, C in ((2 * ncu, 50257), (ncu + 37, 40001)):
+        assert fr.fr_debug_select_variant_for(fr.OP_XENT, R, C, fr.F32) == (256, 50, 4)
+        w = workloads.make("xent_f32", rows=R, cols=C, seed=R)
+        print(f"xent few rows {R}x{C}", flush=True)
+        for am in (True, False):
+            got = run_xent(w["logits"], w["labels"], with_argmax=am)
+            expect_xent(w["logits"], w["labels"], got, f"xent {R}x{C} argmax={am}")
+            with fr.forced_variant(fr.OP_XENT, 256, 50):
+                forced = run_xent(w["logits"], w["labels"], with_argmax=am)
+            assert all(np.array_equal(a, b) for a, b in zip(got, forced) if a is not None), \
+                f"xent {R}x{C}: not the 256-lane shape"

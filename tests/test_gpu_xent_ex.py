@@ -324,3 +324,17 @@ def test_many_rows_per_workgroup(C):
                f"xent_ex {code} {R}x{C} misaligned")
         expect(x, lab, code, dict(), run(x, lab, code, dict(), argmax=False, inplace=True),
                f"xent_ex {code} {R}x{C} in place")
+
+
+def test_few_rows_shape_with_options():
+    # two rows per compute unit (256-lane shape) with options, fp32 logits
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    R, C = 2 * ncu - 3, 50257
+    assert fr.fr_debug_select_variant_for(fr.OP_XENT, R, C, fr.F32) == (256, 50, 4)
+    x, lab = inputs(R, C, fr.F32, seed=77, ignore_every=5)
+    opts = dict(ignore_index=-100, label_smoothing=0.1, reduction="mean")
+    got = run(x, lab, fr.F32, opts, argmax=False)
+    expect(x, lab, fr.F32, opts, got, f"xent_ex f32 {R}x{C} few rows")
+    with fr.forced_variant(fr.OP_XENT, 256, 50):
+        forced = run(x, lab, fr.F32, opts, argmax=False)
+    assert np.array_equal(got[0], forced[0]) and np.array_equal(got[1], forced[1])

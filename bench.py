@@ -391,10 +391,13 @@ def cpu_baseline(wls, budget_s=15.0):
     threads = oracle.threads()
     total_bytes = sum(w.bytes for w in wls)
 
+    per_ms = {w.name: [] for w in wls}
+
     def one_step():
         out = {}
         for w in wls:
             a = w.w
+            t1 = time.perf_counter()
             if w.name in ("softmax_f32", "softmax_bf16"):
                 out[w.name] = (oracle.softmax(a["x"]),)
             elif w.name == "layernorm_f32":
@@ -404,6 +407,7 @@ def cpu_baseline(wls, budget_s=15.0):
                 out[w.name] = (oracle.round_bf16(y), oracle.round_bf16(h))
             elif w.name == "xent_f32":
                 out[w.name] = oracle.softmax_xent(a["logits"], a["labels"])[:2]
+            per_ms[w.name].append((time.perf_counter() - t1) * 1e3)
         return out
 
     t0 = time.perf_counter()
@@ -415,11 +419,31 @@ def cpu_baseline(wls, budget_s=15.0):
         if el > budget_s / 2 or n >= 3:
             break
     per_step = el / n
+    per_workload = {}
+    for w in wls:
+        ms = sorted(per_ms[w.name])[len(per_ms[w.name]) // 2]
+        per_workload[w.name] = {"oracle_ms": round(ms, 2),
+                                "gbps": round(w.bytes / (ms * 1e-3) / 1e9, 2),
+                                "rows_per_s": round(w.R / (ms * 1e-3), 1)}
     return ({"value": total_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
              "kind": "oracle",
              "sample": f"{n} full step(s): all rows of the five workloads, "
-                       f"{per_step:.2f} s per step, double precision, {threads} OpenMP threads"},
+                       f"{per_step:.2f} s per step, double precision, {threads} OpenMP threads",
+             "host_cpu": host_cpu(), "nproc": os.cpu_count(),
+             "per_workload": per_workload},
             outs)
+
+
+def host_cpu():
+    """CPU model name of the host (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def parity_report(wls, outs):

@@ -70,7 +70,9 @@ def expect(w, causal, scale, got, what):
 
 
 SHAPES = [(1, 2, 128, 128, 64), (2, 3, 200, 333, 128), (1, 1, 1, 1, 64), (1, 2, 300, 300, 128),
-          (1, 1, 257, 129, 64), (1, 1, 129, 500, 128), (2, 2, 64, 31, 128), (1, 1, 1000, 1000, 64)]
+          (1, 1, 257, 129, 64), (1, 1, 129, 500, 128), (2, 2, 64, 31, 128), (1, 1, 1000, 1000, 64),
+          # batch x heads a multiple of 8: workgroups grouped by head per XCD
+          (2, 4, 300, 300, 128), (1, 8, 129, 200, 64), (4, 4, 256, 100, 128)]
 
 
 @pytest.mark.parametrize("B,H,Sq,Sk,D", SHAPES)

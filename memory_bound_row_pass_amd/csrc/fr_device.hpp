@@ -389,6 +389,13 @@ __device__ __forceinline__ void load_chunks_pf(const Ts* row, const RowGeom<EPV,
 // wait_lds_copies() precedes reading staged data, and wait_lds_reads()
 // precedes staging over data that was read.
 __device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// All but the K most recently issued vector memory operations of this wave
+// have completed (they retire in issue order).
+template <int K>
+__device__ __forceinline__ void wait_vmcnt_upto() {
+  static_assert(K >= 0 && K < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"I"(K) : "memory");
+}
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <typename Ts, int T, int LPF, int PF, int EPV, int AL>

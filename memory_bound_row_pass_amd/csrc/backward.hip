@@ -249,9 +249,10 @@ struct BwdLanes {
 // issued with those of h and dy, before the row reduction.
 // STG: the row operands of the workgroup's next rows are staged in LDS
 // (global_load_lds_dwordx4, 16 bytes per lane and slot, read back by the
-// lane that requested them) while the current rows are reduced and written;
-// the wait for them comes before the current rows' stores (vector memory
-// operations retire in order).
+// lane that requested them) while the current rows are reduced and written.
+// Vector memory operations retire in issue order: the next iteration's wait
+// leaves this iteration's whole-slot stores outstanding, and the weight is
+// read from LDS, so no wait inside the row loop waits for the staging.
 template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool DRES, bool STG = false>
 __global__ __launch_bounds__(T * RPB) __attribute__((amdgpu_waves_per_eu(OCC)))
 void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, Ts* dh, float* ws,
@@ -263,6 +264,9 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
   __shared__ float xw[RPB][2][NW][2];
   __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
   __shared__ __attribute__((aligned(16))) uint32_t stage[STG ? NOP * NV * T * RPB * 4 : 4];
+  // STG: the weight's chunks of this lane's slots, loaded once (no weight
+  // loads inside the row loop, whose waits would also wait for the staging)
+  __shared__ __attribute__((aligned(16))) uint32_t wlds[STG ? NV * T * 4 : 4];
   const L ln;
   const Slots<T, NV, EPV> sl(cols, ln.tid);
   using Raw = typename RawChunk<Ts>::T;
@@ -293,8 +297,27 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
       for (int k = 0; k < EPV; ++k) v[i][k] = sl.ok(i) ? v[i][k] : 0.f;
     }
   };
-  bool staged = false, copies_done = false;  // uniform in the workgroup
+  // the weight slot i of this lane: from LDS (STG) or from global memory
+  auto wparam = [&](const Ts* wp, int i, float* wt) {
+    if constexpr (STG) {
+      RawChunk<Ts>::unpack(*reinterpret_cast<const Raw*>(wlds + (i * T + ln.tid) * 4), wt);
+    } else {
+      sl.param(wp, i, wt);
+    }
+  };
+  bool staged = false;  // uniform in the workgroup: the next rows are being staged
+  // uniform: whole-slot stores issued after the latest staging; with NV of
+  // them, a wait leaving NV operations outstanding has seen the staging
+  // complete (vector memory operations retire in issue order)
+  int stores_after = 0;
   if constexpr (STG) {
+    if (ln.sub == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        *reinterpret_cast<Raw*>(wlds + (i * T + ln.tid) * 4) =
+            *reinterpret_cast<const Raw*>(w + sl.off(i));
+    }
+    __syncthreads();
     if ((int64_t)blockIdx.x * RPB < rows) {
       stage_rows((int64_t)blockIdx.x * RPB);
       staged = true;
@@ -316,7 +339,8 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 
     float hv[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
     if constexpr (STG) {
-      if (!copies_done) wait_lds_copies();
+      if (stores_after >= NV) wait_vmcnt_upto<NV>();
+      else wait_lds_copies();
       unstage_op(0, hv);
       unstage_op(1, d);
       if constexpr (DRES) unstage_op(2, dr);
@@ -325,7 +349,6 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
       if (staged) {
         wait_lds_reads();  // this iteration's staged rows are in registers
         stage_rows(nb);
-        copies_done = false;
       }
     } else {
       if constexpr (DRES) sl.load3(h + off, dy + off, dres + off, hv, d, dr);
@@ -336,7 +359,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float wt[EPV];
-      sl.param(w1, i, wt);
+      wparam(w1, i, wt);
 #pragma unroll
       for (int k = 0; k < EPV; ++k) {
         const float hk = hv[i][k];
@@ -356,7 +379,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         float wt[EPV];
-        sl.param(w2, i, wt);
+        wparam(w2, i, wt);
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           acc[i][k] = __builtin_fmaf(d[i][k] * hv[i][k], r, acc[i][k]);
@@ -366,13 +389,8 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
         }
       }
     }
-    if constexpr (STG) {
-      if (staged) {  // uniform: before this iteration's stores
-        wait_lds_copies();
-        copies_done = true;
-      }
-    }
     if (live) sl.store(dh + off, hv);
+    if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
   flush_partials<T, NV, EPV, RPB>(acc, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
 }
@@ -668,14 +686,17 @@ static hipError_t launch_softmax_bwd(const void* p, const void* dy, void* dx, in
                        rows, cols);
 }
 
+// Staging with dres as well (three staged operands, 96 KiB).
+#ifndef FR_RB_STG_DRES
+#define FR_RB_STG_DRES 1
+#endif
 template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool STG = false>
 static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w,
                                      void* dh, float* ws, int grid, int64_t rows, int cols,
                                      float eps, hipStream_t s) {
-  // staging only without dres: three staged operands (96 KiB through LDS per
-  // iteration) measured slower (100.0 -> 102.7 us at 8192^2), two faster
-  // (90.8 -> 83.1 us)
-  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true, false>
+  // measured at 8192^2 (weight in LDS, counted waits): with dres
+  // 100.1 -> 96.2 us, without 89.9 -> 80.2 us
+  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true, STG && (FR_RB_STG_DRES != 0)>
                 : &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, false, STG>;
   return launch_kernel(k, dim3(grid), dim3(T * RPB), s, static_cast<const Ts*>(h),
                        static_cast<const Ts*>(dy), static_cast<const Ts*>(dres),
@@ -751,8 +772,7 @@ hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* x
 // workgroup is 1024 lanes (RPB = 1024 / T) with one workgroup per CU
 // (grid_max 256, OCC 4: at most 128 VGPRs).
 #define FR_RB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC>}
-// The 8192-column bf16 shape stages its next rows (h and dy, 64 KiB) in LDS
-// when no dres is given.
+// The 8192-column bf16 shape stages its next rows (h, dy and dres) in LDS.
 #ifndef FR_RB_STG
 #define FR_RB_STG 1
 #endif

@@ -405,3 +405,22 @@ def test_split_batch_setting():
         assert L.fr_debug_set_split_batch_bytes(-1) == default
     finally:
         L.fr_debug_set_split_batch_bytes(-1)
+
+
+def test_row_aware_selection():
+    # the cross-entropy takes the 256-lane shape (two rows per compute unit)
+    # when the rows fill the compute units once but not twice; without a GPU
+    # the compute-unit count falls back to 256
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("compute-unit count of the host without a GPU")
+    sel = fr.fr_debug_select_variant_for
+    for R, want in ((100, (1024, 13, 4)), (256, (1024, 13, 4)), (257, (256, 50, 4)),
+                    (512, (256, 50, 4)), (513, (1024, 13, 4)), (4096, (1024, 13, 4))):
+        assert sel(fr.OP_XENT, R, 50257, fr.F32) == want, R
+    assert sel(fr.OP_XENT, 300, 50257, fr.BF16) == (1024, 7, 8)   # no 256-lane bf16 shape holds it
+    assert sel(fr.OP_SOFTMAX, 300, 50257, fr.F32) == fr.fr_debug_select_variant(fr.OP_SOFTMAX, 50257)
+    with fr.forced_variant(fr.OP_XENT, 1024, 13):                    # a forced shape is kept
+        assert sel(fr.OP_XENT, 300, 50257, fr.F32) == (1024, 13, 4)
+    with pytest.raises(fr.FusedRowError):
+        sel(fr.OP_XENT, -1, 50257, fr.F32)

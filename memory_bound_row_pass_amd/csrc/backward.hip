@@ -397,16 +397,61 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 
 // ------------------------------------------------------------ LayerNorm bwd
 
-template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
+// STG: as the RMSNorm backward, the next rows' x and dy are staged in LDS
+// (and their mean and rstd read) while the current rows are reduced and
+// written, under counted waits; gamma is held in registers (loaded once), so
+// no load inside the row loop waits for the staging.
+template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool STG = false>
 __global__ __launch_bounds__(T * RPB) __attribute__((amdgpu_waves_per_eu(OCC)))
 void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const float* mean,
                           const float* rstd, Ts* dx, float* ws, int64_t rows, int cols) {
   using L = BwdLanes<T, RPB>;
   constexpr int NW = L::NW;
+  static_assert(!STG || EPV * sizeof(Ts) == 16, "staging: 16-byte chunks");
   __shared__ float xw[RPB][2][NW][2];
   __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[STG ? 2 * NV * T * RPB * 4 : 4];
   const L ln;
   const Slots<T, NV, EPV> sl(cols, ln.tid);
+  using Raw = typename RawChunk<Ts>::T;
+  const int wib = ln.sub * NW + ln.wave;  // wave index in the workgroup
+  auto stage_op = [&](const Ts* src, int op) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(src + sl.off(i)),
+          (__attribute__((address_space(3))) void*)(stage + ((op * NV + i) * T * RPB + 64 * wib) * 4),
+          16, 0, FR_NT_LOAD ? 2 : 0);
+  };
+  auto unstage_op = [&](int op, float (&v)[NV][EPV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const Raw r = *reinterpret_cast<const Raw*>(stage + ((op * NV + i) * T * RPB + threadIdx.x) * 4);
+      RawChunk<Ts>::unpack(r, v[i]);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = sl.ok(i) ? v[i][k] : 0.f;
+    }
+  };
+  float gam[STG ? NV : 1][EPV];
+  float mu_next = 0.f, rs_next = 0.f;
+  bool staged = false;  // uniform in the workgroup: the next rows are being staged
+  int stores_after = 0;  // uniform: whole-slot stores issued after the latest staging
+  auto stage_rows = [&](int64_t b) {
+    const int64_t rw = b + ln.sub;
+    const int64_t rr = rw < rows ? rw : rows - 1;
+    stage_op(x + rr * cols, 0);
+    stage_op(dy + rr * cols, 1);
+    mu_next = mean[rr];
+    rs_next = rstd[rr];
+  };
+  if constexpr (STG) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sl.param(gamma, i, gam[i]);
+    if ((int64_t)blockIdx.x * RPB < rows) {
+      stage_rows((int64_t)blockIdx.x * RPB);
+      staged = true;
+    }
+  }
 
   float ag[NV][EPV], ab[NV][EPV];  // dgamma, dbeta partials
 #pragma unroll
@@ -421,17 +466,37 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
     const bool live = row < rows;
     const int64_t rr = live ? row : rows - 1;
     const int64_t off = rr * cols;
-    const float mu = mean[rr];
-    const float rs = rstd[rr];
-
+    float mu, rs;
     float n[NV][EPV], d[NV][EPV];
-    sl.load2(x + off, dy + off, n, d);
+    if constexpr (STG) {
+      if (stores_after >= NV) wait_vmcnt_upto<NV>();
+      else wait_lds_copies();
+      unstage_op(0, n);
+      unstage_op(1, d);
+      mu = mu_next;
+      rs = rs_next;
+      const int64_t nb = base + (int64_t)gridDim.x * RPB;
+      staged = nb < rows;
+      if (staged) {
+        wait_lds_reads();  // this iteration's staged rows are in registers
+        stage_rows(nb);
+      }
+    } else {
+      mu = mean[rr];
+      rs = rstd[rr];
+      sl.load2(x + off, dy + off, n, d);
+    }
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
     const Ts* g1 = fresh(gamma);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float ga[EPV];
-      sl.param(g1, i, ga);
+      if constexpr (STG) {
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) ga[k] = gam[i][k];
+      } else {
+        sl.param(g1, i, ga);
+      }
 #pragma unroll
       for (int k = 0; k < EPV; ++k) {
         n[i][k] = (n[i][k] - mu) * rs;  // masked slots have dy = 0 and add nothing
@@ -451,7 +516,12 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         float ga[EPV];
-        sl.param(g2, i, ga);
+        if constexpr (STG) {
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) ga[k] = gam[i][k];
+        } else {
+          sl.param(g2, i, ga);
+        }
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           ag[i][k] = __builtin_fmaf(d[i][k], n[i][k], ag[i][k]);
@@ -461,6 +531,7 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
       }
       sl.store(dx + off, n);
     }
+    if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
   const size_t G = gridDim.x;
   flush_partials<T, NV, EPV, RPB>(ag, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
@@ -703,11 +774,21 @@ static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* 
                        static_cast<const Ts*>(w), static_cast<Ts*>(dh), ws, rows, cols, eps);
 }
 
+// Staging of the LayerNorm backward rows (x, dy: 2 NV 16 T RPB bytes of LDS)
+// on the 16-byte vector path, below 1024 lanes per row (the 1024-lane shapes
+// spill with gamma held in registers). Measured: bf16 16384 x 4096
+// 89.6 -> 74.0 us; fp32 16384 x 4096 150.8 -> 145.7 us, 8192 x 8192
+// 154.2 -> 148.9 us, 16384 x 1024 43.4 -> 42.4 us, 4096 x 1024 18.1 -> 17.8 us.
+#ifndef FR_LB_STG
+#define FR_LB_STG 1
+#endif
 template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
 static hipError_t launch_layernorm_bwd(const void* x, const void* dy, const void* gamma,
                                        const float* mean, const float* rstd, void* dx, float* ws,
                                        int grid, int64_t rows, int cols, hipStream_t s) {
-  return launch_kernel(&layernorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC>, dim3(grid), dim3(T * RPB), s,
+  constexpr bool STG =
+      FR_LB_STG && T < 1024 && EPV * sizeof(Ts) == 16 && 2 * NV * T * RPB * 16 <= 128 * 1024;
+  return launch_kernel(&layernorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, STG>, dim3(grid), dim3(T * RPB), s,
                        static_cast<const Ts*>(x), static_cast<const Ts*>(dy),
                        static_cast<const Ts*>(gamma), mean, rstd, static_cast<Ts*>(dx), ws, rows,
                        cols);

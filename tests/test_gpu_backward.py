@@ -459,3 +459,19 @@ def test_rms_bwd_several_sweeps(C):
                        f"rms_bwd bf16 {R}x{C} dres={with_dres}", with_dres=with_dres)
     expect_rms_bwd(w, code, run_rms_bwd(w, code, with_dres=False, inplace="dy"),
                    f"rms_bwd bf16 {R}x{C} in place", with_dres=False)
+
+
+@pytest.mark.parametrize("code,C", [(fr.F32, 4096), (fr.BF16, 4096), (fr.F32, 1024), (fr.BF16, 1000)])
+def test_ln_bwd_several_sweeps(code, C):
+    """More rows than one sweep of the persistent grid: every workgroup walks
+    several rows, staging the next rows' x and dy (and their mean and rstd)
+    while it reduces and writes the current ones, with gamma in registers;
+    the last sweep is partial (row groups with no row take part with no
+    data). Also misaligned (scalar path) and in place."""
+    t, v, e = fr.fr_debug_select_variant(fr.OP_LAYERNORM_BWD, C, code)
+    R = 256 * (1024 // t) * 2 + 77
+    w, m, r = ln_bwd_inputs(R, C, code, seed=C + R)
+    print(f"ln_bwd sweeps {code} {R}x{C} variant {(t, v, e)}", flush=True)
+    expect_ln_bwd(w, m, r, code, run_ln_bwd(w, m, r, code), f"ln_bwd {code} {R}x{C}")
+    expect_ln_bwd(w, m, r, code, run_ln_bwd(w, m, r, code, off=1), f"ln_bwd {code} {R}x{C} misaligned")
+    expect_ln_bwd(w, m, r, code, run_ln_bwd(w, m, r, code, inplace="x"), f"ln_bwd {code} {R}x{C} in place")

@@ -636,8 +636,34 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
 #pragma unroll
     for (int k = 0; k < EPV; ++k) acc2[i][k] = 0.f;
 
+  // the weight (gamma) of this workgroup's columns, the same in every row:
+  // held in registers on the vector path (the scalar path, 16 values per
+  // lane, re-reads it per row instead of spilling)
+  constexpr bool WREG = EPV > 1;
+  float wv[WREG ? NV : 1][EPV];
+  if constexpr (WREG) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sl.param(w + c0, i, wv[i]);
+  }
+  auto weight = [&](const Ts* wp, int i, float* t) {
+    if constexpr (WREG) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) t[k] = wv[i][k];
+    } else {
+      sl.param(wp, i, t);
+    }
+  };
+
   int it = 0;
   for (int64_t row = rg; row < rows; row += RG, ++it) {
+    // the segment's row operands first: they do not depend on the row sums,
+    // so their loads are in flight while the partials are merged (the merge's
+    // barrier would otherwise keep them behind it)
+    const int64_t off = row * cols + c0;
+    float a[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
+    if constexpr (DRES) sl.load3(xh + off, dy + off, dres + off, a, d, dr);
+    else sl.load2(xh + off, dy + off, a, d);
+
     Sum2State st{0.f, 0.f};
     for (int j = tid; j < nseg; j += T) {
       const float4 p = part[row * nseg + j];
@@ -646,10 +672,6 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
     st = wave_reduce(st, Sum2Merge{});
     if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Sum2Merge{});
 
-    const int64_t off = row * cols + c0;
-    float a[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
-    if constexpr (DRES) sl.load3(xh + off, dy + off, dres + off, a, d, dr);
-    else sl.load2(xh + off, dy + off, a, d);
     const Ts* w1 = fresh(w) + c0;
     if constexpr (LN) {
       const float mu = mean[row], rs = rstd[row];
@@ -657,7 +679,7 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         float ga[EPV];
-        sl.param(w1, i, ga);
+        weight(w1, i, ga);
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           const float nk = (a[i][k] - mu) * rs;
@@ -672,7 +694,7 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         float wt[EPV];
-        sl.param(w1, i, wt);
+        weight(w1, i, wt);
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           acc[i][k] = __builtin_fmaf(d[i][k] * a[i][k], r, acc[i][k]);

@@ -156,16 +156,19 @@ __device__ __forceinline__ SplitState merge_row(const float4* part, int64_t row,
   return st;
 }
 
-// p_j = exp(x_j - M) / S into the output type. bf16 outputs: a biased base-2
-// exponential kept in fp32's normal range, scaled down by 2^-64 with ldexp so
-// that bf16 subnormal results are rounded from full-precision values.
+// p_j = exp(x_j - M) / S into the output type, times a scale a, minus b
+// (cross-entropy: a = g, b = g eps / C; softmax: a = 1, b = 0). bf16 outputs:
+// a base-2 exponential with a 2^8 bias, e_j = 2^((x_j - M) log2e + 8) <= 2^8,
+// normal for every p_j that can round to a non-zero bf16 (p_j >= 2^-134 needs
+// e_j >= 2^-126, as 1/S <= 1), and one fma with the factor 2^-8 a / S (a
+// normal number: an exact power-of-two scaling of a/S), rounding p_j once.
 template <typename Tout>
-__device__ __forceinline__ float split_p(float xv, float M, float inv_s) {
+__device__ __forceinline__ float split_p(float xv, float M, float fac, float b) {
   if constexpr (sizeof(Tout) == 2) {
-    const float e = exp2_hw(__builtin_fmaf(xv - M, kLog2e, 64.f));
-    return __builtin_ldexpf(e * inv_s, -64);
+    const float e = exp2_hw(__builtin_fmaf(xv - M, kLog2e, 8.f));
+    return __builtin_fmaf(e, fac, -b);
   } else {
-    return exp_acc(xv - M) * inv_s;
+    return __builtin_fmaf(exp_acc(xv - M), fac, -b);
   }
 }
 
@@ -245,17 +248,14 @@ void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, 
       if (label_lane) x_label = load1(xs + lc);
     }
 
+    // the factor a / S (2^-8 a / S for the biased bf16 exponentials)
+    const float fac = (sizeof(Tout) == 2 ? 0x1p-8f : 1.f) * (XENT ? inv_s * gsc : inv_s);
+    const float off = XENT ? goff : 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const float p = split_p<Tout>(v[i][k], st.m, inv_s);
-        v[i][k] = XENT ? __builtin_fmaf(p, gsc, -goff) : p;
-      }
-    {
-      const float p = split_p<Tout>(xe, st.m, inv_s);
-      xe = XENT ? __builtin_fmaf(p, gsc, -goff) : p;
-    }
+      for (int k = 0; k < EPV; ++k) v[i][k] = split_p<Tout>(v[i][k], st.m, fac, off);
+    xe = split_p<Tout>(xe, st.m, fac, off);
     store_chunks<Tout, T, NV, EPV>(ys, g, tid, v);
     if (ec >= 0) store1(ys + ec, xe);
 

@@ -475,3 +475,18 @@ def test_ln_bwd_several_sweeps(code, C):
     expect_ln_bwd(w, m, r, code, run_ln_bwd(w, m, r, code), f"ln_bwd {code} {R}x{C}")
     expect_ln_bwd(w, m, r, code, run_ln_bwd(w, m, r, code, off=1), f"ln_bwd {code} {R}x{C} misaligned")
     expect_ln_bwd(w, m, r, code, run_ln_bwd(w, m, r, code, inplace="x"), f"ln_bwd {code} {R}x{C} in place")
+
+
+@pytest.mark.parametrize("R,C,code", [(600, 4104, fr.BF16), (1100, 6000, fr.BF16),
+                                      (1025, 8192, fr.BF16), (520, 7000, fr.F32)])
+def test_staged_norm_bwd_shapes(R, C, code):
+    """The staged norm backward shapes at widths with and without a partial
+    slot (a full wait instead of the counted one) and row counts that end in
+    a partial sweep: RMSNorm with and without dres, LayerNorm."""
+    w = rms_bwd_inputs(R, C, code, seed=R + C)
+    print(f"staged norm bwd {code} {R}x{C}", flush=True)
+    for with_dres in (True, False):
+        expect_rms_bwd(w, code, run_rms_bwd(w, code, with_dres=with_dres),
+                       f"rms_bwd {code} {R}x{C} dres={with_dres}", with_dres=with_dres)
+    wl, m, r = ln_bwd_inputs(R, C, code, seed=R + C + 1)
+    expect_ln_bwd(wl, m, r, code, run_ln_bwd(wl, m, r, code), f"ln_bwd {code} {R}x{C}")

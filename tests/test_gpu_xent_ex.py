@@ -338,3 +338,21 @@ def test_few_rows_shape_with_options():
     with fr.forced_variant(fr.OP_XENT, 256, 50):
         forced = run(x, lab, fr.F32, opts, argmax=False)
     assert np.array_equal(got[0], forced[0]) and np.array_equal(got[1], forced[1])
+
+
+@pytest.mark.parametrize("R,C", [(300, 32769), (513, 40000), (1000, 57344), (257, 50257),
+                                 (1537, 33000)])
+def test_staged_row_widths_and_counts(R, C):
+    """bf16 logits on the staged 1024-lane shape: widths whose whole slots
+    number fewer than NV - 1 (a full wait before a staged row) and NV - 1 or
+    NV (the counted wait), row counts from one to several rows per compute
+    unit; options, argmax, misaligned rows."""
+    assert fr.fr_debug_select_variant(fr.OP_XENT, C, fr.BF16) == (1024, 7, 8)
+    rng = np.random.default_rng(R * 7 + C)
+    x, lab = inputs(R, C, fr.BF16, seed=R + C, ignore_every=int(rng.integers(2, 6)))
+    opts = dict(ignore_index=-100, label_smoothing=float(rng.choice([0.0, 0.05])),
+                reduction=str(rng.choice(["none", "mean"])))
+    print(f"staged bf16 {R}x{C} {opts}", flush=True)
+    for am, offs in ((False, (0, 0)), (True, (1, 1))):
+        expect(x, lab, fr.BF16, opts, run(x, lab, fr.BF16, opts, argmax=am, offs=offs),
+               f"xent_ex bf16 {R}x{C} argmax={am} offs={offs}")

@@ -118,31 +118,40 @@ void softmax_bwd_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int col
 
 // Sum the row groups' per-lane column partials of one parameter in row-group
 // order and write the workgroup's partial row (`cols` floats at wsrow).
+// RPB > 1: every row group writes all its slots to buf (NV RPB T EPV floats;
+// row group r's slot i of lane t at ((i RPB + r) T + t) EPV), then after one
+// barrier every lane of the workgroup takes columns lid, lid + T RPB, ... and
+// adds their RPB values in row-group order (the same order, and bits, as one
+// row group adding them slot by slot, in one round instead of NV). The
+// barrier on entry lets buf reuse LDS that the row loop read (the staging
+// buffer) or that a previous call read.
 template <int T, int NV, int EPV, int RPB>
-__device__ __forceinline__ void flush_partials(const float (&acc)[NV][EPV], float* part,
+__device__ __forceinline__ void flush_partials(const float (&acc)[NV][EPV], float* buf,
                                                float* wsrow, int nvec, int tid, int sub) {
   if constexpr (RPB == 1) {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       if (i * T + tid < nvec) store_f32<EPV>(wsrow + (i * T + tid) * EPV, acc[i]);
   } else {
+    constexpr int L = T * RPB;  // lanes of the workgroup
+    constexpr int W = T * EPV;  // columns per slot
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      store_f32<EPV>(part + (sub * T + tid) * EPV, acc[i]);
-      __syncthreads();
-      if (sub == 0 && i * T + tid < nvec) {
-        float s[EPV];
-        load_f32<EPV>(part + tid * EPV, s);
+    for (int i = 0; i < NV; ++i) store_f32<EPV>(buf + ((i * RPB + sub) * T + tid) * EPV, acc[i]);
+    __syncthreads();
+    const int lid = sub * T + tid;  // threadIdx.x
+    const int ncol = nvec * EPV;
 #pragma unroll
-        for (int r = 1; r < RPB; ++r) {
-          float o[EPV];
-          load_f32<EPV>(part + (r * T + tid) * EPV, o);
+    for (int j = 0; j < (NV * W + L - 1) / L; ++j) {
+      const int g = lid + j * L;  // column (slot g / W, lane (g % W) / EPV)
+      if (g < NV * W && g < ncol) {
+        const int i = g / W;
+        const float* p = buf + i * RPB * W + (g - i * W);
+        float sum = p[0];
 #pragma unroll
-          for (int k = 0; k < EPV; ++k) s[k] += o[k];
-        }
-        store_f32<EPV>(wsrow + (i * T + tid) * EPV, s);
+        for (int r = 1; r < RPB; ++r) sum += p[r * W];
+        wsrow[g] = sum;
       }
-      __syncthreads();
     }
   }
 }
@@ -262,8 +271,11 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
   constexpr int NOP = DRES ? 3 : 2;  // staged row operands
   static_assert(!STG || EPV * sizeof(Ts) == 16, "staging: 16-byte chunks");
   __shared__ float xw[RPB][2][NW][2];
-  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
+  // the partial-row buffer of flush_partials: the staging buffer when staged
+  // (read for the last time before it), else its own
+  __shared__ __attribute__((aligned(16))) float part[RPB > 1 && !STG ? NV * T * RPB * EPV : 4];
   __shared__ __attribute__((aligned(16))) uint32_t stage[STG ? NOP * NV * T * RPB * 4 : 4];
+  static_assert(!STG || RPB == 1 || NOP * 4 >= EPV, "partials fit in the staging buffer");
   // STG: the weight's chunks of this lane's slots, loaded once (no weight
   // loads inside the row loop, whose waits would also wait for the staging)
   __shared__ __attribute__((aligned(16))) uint32_t wlds[STG ? NV * T * 4 : 4];
@@ -392,7 +404,8 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
     if (live) sl.store(dh + off, hv);
     if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
-  flush_partials<T, NV, EPV, RPB>(acc, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
+  float* pbuf = STG ? reinterpret_cast<float*>(stage) : part;
+  flush_partials<T, NV, EPV, RPB>(acc, pbuf, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
 }
 
 // ------------------------------------------------------------ LayerNorm bwd
@@ -409,8 +422,10 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
   constexpr int NW = L::NW;
   static_assert(!STG || EPV * sizeof(Ts) == 16, "staging: 16-byte chunks");
   __shared__ float xw[RPB][2][NW][2];
-  __shared__ __attribute__((aligned(16))) float part[RPB > 1 ? T * RPB * EPV : 4];
+  // the partial-row buffer of flush_partials: the staging buffer when staged
+  __shared__ __attribute__((aligned(16))) float part[RPB > 1 && !STG ? NV * T * RPB * EPV : 4];
   __shared__ __attribute__((aligned(16))) uint32_t stage[STG ? 2 * NV * T * RPB * 4 : 4];
+  static_assert(!STG || RPB == 1 || 8 >= EPV, "partials fit in the staging buffer");
   const L ln;
   const Slots<T, NV, EPV> sl(cols, ln.tid);
   using Raw = typename RawChunk<Ts>::T;
@@ -534,8 +549,9 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
     if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
   const size_t G = gridDim.x;
-  flush_partials<T, NV, EPV, RPB>(ag, part, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
-  flush_partials<T, NV, EPV, RPB>(ab, part, ws + (G + blockIdx.x) * cols, sl.nvec, ln.tid, ln.sub);
+  float* pbuf = STG ? reinterpret_cast<float*>(stage) : part;
+  flush_partials<T, NV, EPV, RPB>(ag, pbuf, ws + (size_t)blockIdx.x * cols, sl.nvec, ln.tid, ln.sub);
+  flush_partials<T, NV, EPV, RPB>(ab, pbuf, ws + (G + blockIdx.x) * cols, sl.nvec, ln.tid, ln.sub);
 }
 
 // ------------------------------------------------- split-row norm backward

@@ -300,13 +300,25 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
     stage_op(dy + o, 1);
     if constexpr (DRES) stage_op(dres + o, 2);
   };
-  auto unstage_op = [&](int op, float (&v)[NV][EPV]) {
+  // this lane's staged operands (NOP x NV chunks), read past the compiler's
+  // LDS-copy wait (the counted wait has covered them)
+  auto unstage = [&](float (&v0)[NV][EPV], float (&v1)[NV][EPV], float (&v2)[DRES ? NV : 1][EPV]) {
+    uint32_t a[NOP * NV];
+    u32x4 r[NOP * NV];
+#pragma unroll
+    for (int j = 0; j < NOP * NV; ++j) a[j] = lds_offset(stage + (j * T * RPB + threadIdx.x) * 4);
+    read_staged(a, r);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const Raw r = *reinterpret_cast<const Raw*>(stage + ((op * NV + i) * T * RPB + threadIdx.x) * 4);
-      RawChunk<Ts>::unpack(r, v[i]);
+      RawChunk<Ts>::unpack(__builtin_bit_cast(Raw, r[i]), v0[i]);
+      RawChunk<Ts>::unpack(__builtin_bit_cast(Raw, r[NV + i]), v1[i]);
+      if constexpr (DRES) RawChunk<Ts>::unpack(__builtin_bit_cast(Raw, r[2 * NV + i]), v2[i]);
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] = sl.ok(i) ? v[i][k] : 0.f;
+      for (int k = 0; k < EPV; ++k) {
+        v0[i][k] = sl.ok(i) ? v0[i][k] : 0.f;
+        v1[i][k] = sl.ok(i) ? v1[i][k] : 0.f;
+        if constexpr (DRES) v2[i][k] = sl.ok(i) ? v2[i][k] : 0.f;
+      }
     }
   };
   // the weight slot i of this lane: from LDS (STG) or from global memory
@@ -353,9 +365,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
     if constexpr (STG) {
       if (stores_after >= NV) wait_vmcnt_upto<NV>();
       else wait_lds_copies();
-      unstage_op(0, hv);
-      unstage_op(1, d);
-      if constexpr (DRES) unstage_op(2, dr);
+      unstage(hv, d, dr);
       const int64_t nb = base + (int64_t)gridDim.x * RPB;
       staged = nb < rows;
       if (staged) {
@@ -416,8 +426,12 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 // no load inside the row loop waits for the staging.
 template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool STG = false>
 __global__ __launch_bounds__(T * RPB) __attribute__((amdgpu_waves_per_eu(OCC)))
-void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const float* mean,
-                          const float* rstd, Ts* dx, float* ws, int64_t rows, int cols) {
+void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma,
+                          // no output overlaps them (the entry points reject it), so the
+                          // next rows' values come through scalar loads, which the counted
+                          // wait of the staged path does not have to cover
+                          const float* __restrict__ mean, const float* __restrict__ rstd, Ts* dx,
+                          float* ws, int64_t rows, int cols) {
   using L = BwdLanes<T, RPB>;
   constexpr int NW = L::NW;
   static_assert(!STG || EPV * sizeof(Ts) == 16, "staging: 16-byte chunks");
@@ -438,13 +452,23 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
           (__attribute__((address_space(3))) void*)(stage + ((op * NV + i) * T * RPB + 64 * wib) * 4),
           16, 0, FR_NT_LOAD ? 2 : 0);
   };
-  auto unstage_op = [&](int op, float (&v)[NV][EPV]) {
+  // this lane's staged x and dy chunks, read past the compiler's LDS-copy
+  // wait (the counted wait has covered them)
+  auto unstage = [&](float (&v0)[NV][EPV], float (&v1)[NV][EPV]) {
+    uint32_t a[2 * NV];
+    u32x4 r[2 * NV];
+#pragma unroll
+    for (int j = 0; j < 2 * NV; ++j) a[j] = lds_offset(stage + (j * T * RPB + threadIdx.x) * 4);
+    read_staged(a, r);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const Raw r = *reinterpret_cast<const Raw*>(stage + ((op * NV + i) * T * RPB + threadIdx.x) * 4);
-      RawChunk<Ts>::unpack(r, v[i]);
+      RawChunk<Ts>::unpack(__builtin_bit_cast(Raw, r[i]), v0[i]);
+      RawChunk<Ts>::unpack(__builtin_bit_cast(Raw, r[NV + i]), v1[i]);
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] = sl.ok(i) ? v[i][k] : 0.f;
+      for (int k = 0; k < EPV; ++k) {
+        v0[i][k] = sl.ok(i) ? v0[i][k] : 0.f;
+        v1[i][k] = sl.ok(i) ? v1[i][k] : 0.f;
+      }
     }
   };
   float gam[STG ? NV : 1][EPV];
@@ -486,8 +510,7 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma, const floa
     if constexpr (STG) {
       if (stores_after >= NV) wait_vmcnt_upto<NV>();
       else wait_lds_copies();
-      unstage_op(0, n);
-      unstage_op(1, d);
+      unstage(n, d);
       mu = mu_next;
       rs = rs_next;
       const int64_t nb = base + (int64_t)gridDim.x * RPB;

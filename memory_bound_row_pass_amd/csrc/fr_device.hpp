@@ -398,6 +398,47 @@ __device__ __forceinline__ void wait_vmcnt_upto() {
 }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Reads of staged chunks back from LDS, out of the compiler's sight: it
+// cannot tell which LDS bytes an outstanding global_load_lds writes, so it
+// puts a full vmcnt(0) before every read of a staging buffer — which also
+// waits for earlier stores and for copies staged further ahead, defeating
+// the counted waits. The caller has waited for the copies these reads
+// return; the reads complete inside the asm (lgkmcnt(0)), so no output
+// register is still in flight when it ends. Addresses: LDS byte offsets.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void read_staged4(const uint32_t* a, u32x4* r) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+__device__ __forceinline__ void read_staged2(const uint32_t* a, u32x4* r) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(a[0]), "v"(a[1])
+      : "memory");
+}
+__device__ __forceinline__ void read_staged1(const uint32_t* a, u32x4* r) {
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a[0]) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void read_staged(const uint32_t (&a)[N], u32x4 (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) read_staged4(a + 4 * i, r + 4 * i);
+  if constexpr (N % 4 >= 2) read_staged2(a + N / 4 * 4, r + N / 4 * 4);
+  if constexpr (N % 2 == 1) read_staged1(a + N - 1, r + N - 1);
+}
+
 template <typename Ts, int T, int LPF, int PF, int EPV, int AL>
 __device__ __forceinline__ void stage_row(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                           int wave, uint32_t* stage,
@@ -683,6 +724,20 @@ struct XWave {
   float slot[2][NW][NF];
 };
 
+// The barrier of the cross-wave merge orders LDS only: the slots are LDS,
+// and no wave reads global memory, or LDS copied from it by another wave,
+// through this barrier. (__syncthreads() is a workgroup fence as well, which
+// here waits for every outstanding vector memory operation of the wave: the
+// previous row's stores and the next row's staged copies, which would then
+// stop overlapping the rest of the row.) FR_LDS_BARRIER = 0 restores it.
+#ifndef FR_LDS_BARRIER
+#define FR_LDS_BARRIER 1
+#endif
+__device__ __forceinline__ void lds_barrier() {
+  if constexpr (FR_LDS_BARRIER) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else __syncthreads();
+}
+
 template <int NW, typename S, typename Merge>
 __device__ __forceinline__ S block_merge(S wave_state, float (*slot)[sizeof(S) / sizeof(float)],
                                          int wave, int lane, Merge merge) {
@@ -692,7 +747,7 @@ __device__ __forceinline__ S block_merge(S wave_state, float (*slot)[sizeof(S) /
 #pragma unroll
     for (int k = 0; k < NF; ++k) slot[wave][k] = f[k];
   }
-  __syncthreads();
+  lds_barrier();
   S acc;
   {
     float* f = reinterpret_cast<float*>(&acc);

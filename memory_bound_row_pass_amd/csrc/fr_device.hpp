@@ -213,6 +213,25 @@ __device__ __forceinline__ void load_param<bf16_t, 1>(const bf16_t* p, float* v)
 // Single element of any storage type (head/tail slots, label logit).
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const bf16_t* p) { return __uint_as_float((uint32_t)p->u << 16); }
+// One element as its storage bits, converted later (raw_value): a value
+// converted right after its load makes the compiler wait for the load there,
+// and that wait (vmcnt) also waits for every vector memory operation issued
+// before it — stores, staged copies — where the value is only needed later.
+__device__ __forceinline__ uint32_t load1_raw(const float* p) { return __float_as_uint(*p); }
+__device__ __forceinline__ uint32_t load1_raw(const bf16_t* p) { return (uint32_t)p->u; }
+template <typename Ts>
+__device__ __forceinline__ float raw_value(uint32_t r) {
+  return sizeof(Ts) == 2 ? __uint_as_float(r << 16) : __uint_as_float(r);
+}
+template <typename Ts>
+constexpr uint32_t kRawNegInf = sizeof(Ts) == 2 ? 0xff80u : 0xff800000u;
+// The raw value at this point of the program: the conversion after it cannot
+// be moved up to the load, and the memory clobber keeps it behind the
+// memory operations before it (the compiler's wait for the load lands here).
+__device__ __forceinline__ uint32_t raw_here(uint32_t r) {
+  asm volatile("" : "+v"(r) : : "memory");
+  return r;
+}
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store1(bf16_t* p, float v) { p->u = to_bf16(v); }
 
@@ -470,7 +489,7 @@ __device__ __forceinline__ void stage_row(const Ts* row, const RowGeom<EPV, AL>&
 // stage_row: the remaining slots are loaded from global memory, the staged
 // ones taken from LDS (after waiting for the copies unless `copies_done`)
 // and from `pre`; all are masked as in load_chunks.
-template <typename Ts, int T, int NV, int LPF, int PF, int EPV, int AL>
+template <typename Ts, int T, int NV, int LPF, int PF, int EPV, bool HIDDEN, int AL>
 __device__ __forceinline__ void load_staged(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                             const uint32_t* stage,
                                             const typename RawChunk<Ts>::T (&pre)[PF > 0 ? PF : 1],
@@ -487,8 +506,28 @@ __device__ __forceinline__ void load_staged(const Ts* row, const RowGeom<EPV, AL
       Vec<Ts, EPV>::load(base + o, v[i]);
     }
     if (!copies_done) wait_lds_copies();
+    // HIDDEN: read past the compiler's LDS-copy wait (read_staged), two
+    // chunks at a time, each pair unpacked at once; the lane's LDS offset is
+    // formed anew in every row (opaque zero), so no per-slot address is kept
+    // — and spilled — across the row loop. Else plain reads (the compiler
+    // waits for all outstanding copies and stores first).
+    const uint32_t sb = lds_offset(stage) + (uint32_t)tid * 16u + opaque_zero();
 #pragma unroll
-    for (int i = 0; i < LPF; ++i) {
+    for (int i = 0; i < (HIDDEN ? LPF : 0); i += 2) {
+      uint32_t a[2];
+      u32x4 r[2];
+      a[0] = sb + (uint32_t)(i * T * 16);
+      if (i + 1 < LPF) {
+        a[1] = sb + (uint32_t)((i + 1) * T * 16);
+        read_staged2(a, r);
+        RawChunk<Ts>::unpack(__builtin_bit_cast(typename RawChunk<Ts>::T, r[1]), v[i + 1]);
+      } else {
+        read_staged1(a, r);
+      }
+      RawChunk<Ts>::unpack(__builtin_bit_cast(typename RawChunk<Ts>::T, r[0]), v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < (HIDDEN ? 0 : LPF); ++i) {
       const typename RawChunk<Ts>::T r =
           *reinterpret_cast<const typename RawChunk<Ts>::T*>(stage + (i * T + tid) * 4);
       RawChunk<Ts>::unpack(r, v[i]);

@@ -356,3 +356,31 @@ def test_staged_row_widths_and_counts(R, C):
     for am, offs in ((False, (0, 0)), (True, (1, 1))):
         expect(x, lab, fr.BF16, opts, run(x, lab, fr.BF16, opts, argmax=am, offs=offs),
                f"xent_ex bf16 {R}x{C} argmax={am} offs={offs}")
+
+
+def test_staged_bf16_plain_and_ignored_runs():
+    """The staged bf16 1024-lane kernel looping over many rows per workgroup:
+    without options (out of place, misaligned), and with runs of consecutive
+    ignored rows — the first and last rows among them — so that a row staged
+    after an ignored row's zero stores, a staged row followed by an ignored
+    one, and ignored rows with nothing to stage all occur."""
+    R, C = 1500, 50257  # a workgroup takes rows w, w + ncu, ...: ~6 rows each
+    assert fr.fr_debug_select_variant(fr.OP_XENT, C, fr.BF16) == (1024, 7, 8)
+    x, lab = inputs(R, C, fr.BF16, seed=4242)
+    print(f"staged bf16 plain {R}x{C}", flush=True)
+    for am, offs in ((False, (0, 0)), (False, (3, 1)), (True, (0, 0))):
+        expect(x, lab, fr.BF16, dict(), run(x, lab, fr.BF16, dict(), argmax=am, offs=offs),
+               f"xent_ex bf16 plain {R}x{C} argmax={am} offs={offs}")
+    rng = np.random.default_rng(4243)
+    runs = lab.copy()
+    r = 0
+    while r < R:  # alternate runs of 1-400 kept rows and 1-400 ignored rows
+        n_keep, n_ign = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+        runs[r + n_keep:r + n_keep + n_ign] = -100
+        r += n_keep + n_ign
+    runs[0] = runs[-1] = -100
+    opts = dict(ignore_index=-100, label_smoothing=0.1, reduction="mean")
+    print(f"staged bf16 ignored runs: {int((runs == -100).sum())} of {R} rows ignored", flush=True)
+    for am in (False, True):
+        expect(x, runs, fr.BF16, opts, run(x, runs, fr.BF16, opts, argmax=am),
+               f"xent_ex bf16 ignored runs argmax={am}")

@@ -144,14 +144,14 @@ FR_API fr_status_t fr_add_rmsnorm_fwd(const void* x, const void* residual, const
  *   ("Engineering a CUDA Machine Learning Framework from Scratch", §2.1:
  *    loss gradients fused into registers; "GPU Programming for Machine
  *    Learning", Module 3: Cross-entropy loss.)
- * logits, grad [rows, cols] in `dtype` (FR_F32); labels [rows] int32;
- * loss [rows] fp32; argmax [rows] int32 or NULL. grad may equal logits.
+ * logits, grad [rows, cols] fp32; labels [rows] int32; loss [rows] fp32;
+ * argmax [rows] int32 or NULL. grad may equal logits. bf16 logits, and the
+ * options of training code, are fr_softmax_xent_ex's.
  * A label outside [0, cols) is a data error, not an API error: that row's
  * loss is NaN and its grad is the softmax row; no out-of-bounds access. */
-FR_API fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* labels,
-                                    float* loss, void* grad, int32_t* argmax,
-                                    int64_t rows, int64_t cols, fr_dtype_t dtype,
-                                    void* stream);
+FR_API fr_status_t fr_softmax_xent_fwd_bwd(const float* logits, const int32_t* labels,
+                                           float* loss, float* grad, int32_t* argmax,
+                                           int64_t rows, int64_t cols, void* stream);
 
 /* ---- cross-entropy variants ---- */
 
@@ -404,11 +404,54 @@ FR_API const char* fr_version(void);
 
 /* ---- measurement and tuning (not part of the row-operation contract) ---- */
 
-/* Plain device-to-device streaming copy of `bytes` bytes (128-bit accesses
- * where aligned). Used as the bandwidth ceiling and as the known-size
- * reference when scaling hardware byte counters. src and dst must not
- * overlap. */
+/* Memory-system probes: what HBM sustains for reads alone, writes alone and
+ * a copy, with the access pattern of the row kernels and no arithmetic (the
+ * ceilings the row kernels' bandwidth is compared with, "Engineering a CUDA
+ * Machine Learning Framework from Scratch", §2.1 The Memory Bandwidth
+ * Bottleneck; also the known-size references for scaling hardware byte
+ * counters). A workgroup of `threads` lanes owns a contiguous row of
+ * threads * vecs 16-byte chunks (lane t: chunks t, t + threads, ...; 64 lanes
+ * = one row per wavefront, four per workgroup); a copy issues a row's loads
+ * before its stores. The compiled shapes (threads, vecs) are 64 x {2, 4, 8,
+ * 16}, 256 x {1, 2, 4, 8, 16}, 512 x {1, 2, 4, 8} and 1024 x {1, 2, 4, 8, 13,
+ * 16}. The cache policy is a mask: FR_PROBE_NT_LOADS makes the loads
+ * non-temporal, FR_PROBE_NT_STORES the stores (else ordinary cached ones). */
+typedef enum { FR_PROBE_READ = 0, FR_PROBE_WRITE = 1, FR_PROBE_COPY = 2 } fr_probe_t;
+#define FR_PROBE_NT_LOADS 1
+#define FR_PROBE_NT_STORES 2
+/* Shape and policy of fr_stream_read, fr_stream_write and fr_stream_copy. */
+#define FR_STREAM_THREADS 256
+#define FR_STREAM_VECS 8
+#define FR_STREAM_POLICY (FR_PROBE_NT_LOADS | FR_PROBE_NT_STORES)
+
+/* Device-to-device copy of `bytes` bytes: the probe's copy in its default
+ * shape and policy when both pointers are 16-byte aligned and bytes is a
+ * multiple of 16; a plain byte loop otherwise. src and dst must not overlap. */
 FR_API fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* Read `bytes` bytes of src (16-byte aligned, bytes a multiple of 16), in the
+ * default shape and policy; each row's XOR of its 32-bit words goes to
+ * sink[row] (fr_stream_probe_rows(bytes, FR_STREAM_THREADS, FR_STREAM_VECS)
+ * words, 4-byte aligned, not overlapping src): the only writes. */
+FR_API fr_status_t fr_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/* Set every 32-bit word of dst (16-byte aligned, bytes a multiple of 16) to
+ * `value`, in the default shape and policy; reads nothing. */
+FR_API fr_status_t fr_stream_write(void* dst, int64_t bytes, uint32_t value, void* stream);
+
+/* Rows of the probe shape (threads, vecs) over `bytes` bytes: the sink words a
+ * read probe writes. -1 for a shape that is not compiled or bytes < 0. */
+FR_API int64_t fr_stream_probe_rows(int64_t bytes, int threads, int vecs);
+
+/* Any probe in any compiled shape: FR_PROBE_READ reads src and writes sink,
+ * FR_PROBE_WRITE writes `value` to every word of dst, FR_PROBE_COPY copies
+ * src to dst (no overlap). policy: a mask of FR_PROBE_NT_LOADS and
+ * FR_PROBE_NT_STORES (FR_E_VALUE otherwise). Pointers 16-byte aligned (sink
+ * 4-byte), bytes a multiple of 16; unused pointers may be NULL. FR_E_VARIANT
+ * for a shape that is not compiled. */
+FR_API fr_status_t fr_stream_probe(fr_probe_t kind, const void* src, void* dst, int64_t bytes,
+                                   uint32_t value, uint32_t* sink, int threads, int vecs,
+                                   int policy, void* stream);
 
 
 /* Force the kernel variant used by later calls of `op`: `threads` lanes per

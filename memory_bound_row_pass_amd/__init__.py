@@ -18,7 +18,9 @@ import os
 __all__ = [
     "F32", "BF16", "FR_MAX_COLS", "FusedRowError", "lib", "status_str", "version",
     "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
-    "fr_stream_copy", "fr_debug_force_variant", "fr_debug_select_variant",
+    "fr_stream_copy", "fr_stream_read", "fr_stream_write", "fr_stream_probe",
+    "fr_stream_probe_rows", "PROBE_READ", "PROBE_WRITE", "PROBE_COPY", "PROBE_NT_LOADS",
+    "PROBE_NT_STORES", "fr_debug_force_variant", "fr_debug_select_variant",
     "fr_debug_select_variant_for",
     "fr_debug_set_split_batch_bytes", "split_batch_bytes",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
@@ -86,8 +88,11 @@ def _load() -> ctypes.CDLL:
         "fr_softmax_fwd": [P, P, I64, I64, I32, I32, P],
         "fr_layernorm_fwd": [P, P, P, P, P, P, I64, I64, F, I32, P],
         "fr_add_rmsnorm_fwd": [P, P, P, P, P, I64, I64, F, I32, P],
-        "fr_softmax_xent_fwd_bwd": [P, P, P, P, P, I64, I64, I32, P],
+        "fr_softmax_xent_fwd_bwd": [P, P, P, P, P, I64, I64, P],
         "fr_stream_copy": [P, P, I64, P],
+        "fr_stream_read": [P, I64, P, P],
+        "fr_stream_write": [P, I64, ctypes.c_uint32, P],
+        "fr_stream_probe": [I32, P, P, I64, ctypes.c_uint32, P, I32, I32, I32, P],
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
         "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
         "fr_softmax_fwd_split": [P, P, I64, I64, I32, I32, P, I64, P],
@@ -109,6 +114,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.fr_stream_probe_rows.argtypes = [I64, I32, I32]
+    L.fr_stream_probe_rows.restype = ctypes.c_int64
     L.fr_split_workspace_bytes.argtypes = [I64, I64]
     L.fr_split_workspace_bytes.restype = ctypes.c_int64
     L.fr_norm_bwd_workspace_bytes.argtypes = [I32, I64, I64]
@@ -251,11 +258,13 @@ def fr_softmax_xent_fwd_bwd(logits, labels, loss, grad, argmax=None, stream=None
     _check_rows(loss, R, "loss", torch.float32)
     if argmax is not None:
         _check_rows(argmax, R, "argmax", torch.int32)
+    if logits.dtype != torch.float32:
+        raise TypeError("fr_softmax_xent_fwd_bwd takes float32 logits "
+                        "(bf16 logits: fr_softmax_xent_ex)")
     if tuple(grad.shape) != (R, C) or not grad.is_contiguous() or grad.dtype != logits.dtype:
         raise ValueError("grad must be a contiguous tensor of logits' shape and dtype")
     _check(lib.fr_softmax_xent_fwd_bwd(_ptr(logits), _ptr(labels), _ptr(loss), _ptr(grad),
-                                       _ptr(argmax), R, C, _dtype_code(logits),
-                                       _stream(stream, logits)),
+                                       _ptr(argmax), R, C, _stream(stream, logits)),
            "fr_softmax_xent_fwd_bwd")
 
 
@@ -517,6 +526,61 @@ def fr_stream_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     if n > dst.numel() * dst.element_size() or n > src.numel() * src.element_size():
         raise ValueError("copy larger than a buffer")
     _check(lib.fr_stream_copy(_ptr(src), _ptr(dst), n, _stream(stream, src)), "fr_stream_copy")
+
+
+PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
+PROBE_NT_LOADS, PROBE_NT_STORES = 1, 2
+STREAM_THREADS, STREAM_VECS, STREAM_POLICY = 256, 8, 3
+
+
+def fr_stream_probe_rows(nbytes: int, threads: int = STREAM_THREADS,
+                         vecs: int = STREAM_VECS) -> int:
+    """Rows of a probe shape over nbytes (the sink words of a read probe)."""
+    n = lib.fr_stream_probe_rows(int(nbytes), int(threads), int(vecs))
+    if n < 0:
+        raise ValueError(f"no probe shape {threads} x {vecs}")
+    return n
+
+
+def fr_stream_probe(kind: int, src=None, dst=None, nbytes: int | None = None, value: int = 0,
+                    sink=None, threads: int = STREAM_THREADS, vecs: int = STREAM_VECS,
+                    policy: int = STREAM_POLICY, stream=None) -> None:
+    """Memory-system probe (C: fr_stream_probe): PROBE_READ reads src into the
+    per-row XOR words of sink (uint32 viewed as int32), PROBE_WRITE fills dst
+    with `value`, PROBE_COPY copies src to dst. policy: a mask of
+    PROBE_NT_LOADS and PROBE_NT_STORES."""
+    _need_cuda(src, dst, sink)
+    ref = src if src is not None else dst
+    n = ref.numel() * ref.element_size() if nbytes is None else int(nbytes)
+    for t in (src, dst):
+        if t is not None and n > t.numel() * t.element_size():
+            raise ValueError("probe larger than a buffer")
+    if sink is not None and sink.numel() * sink.element_size() < 4 * fr_stream_probe_rows(n, threads, vecs):
+        raise ValueError("sink smaller than one word per row")
+    _check(lib.fr_stream_probe(int(kind), _ptr(src), _ptr(dst), n, ctypes.c_uint32(value & 0xFFFFFFFF),
+                               _ptr(sink), int(threads), int(vecs), int(policy),
+                               _stream(stream, ref)), "fr_stream_probe")
+
+
+def fr_stream_read(src, sink, nbytes: int | None = None, stream=None) -> None:
+    """Read-only probe in the default shape (C: fr_stream_read)."""
+    _need_cuda(src, sink)
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size():
+        raise ValueError("read larger than the buffer")
+    if sink.numel() * sink.element_size() < 4 * fr_stream_probe_rows(n):
+        raise ValueError("sink smaller than one word per row")
+    _check(lib.fr_stream_read(_ptr(src), n, _ptr(sink), _stream(stream, src)), "fr_stream_read")
+
+
+def fr_stream_write(dst, value: int, nbytes: int | None = None, stream=None) -> None:
+    """Write-only probe in the default shape (C: fr_stream_write)."""
+    _need_cuda(dst)
+    n = dst.numel() * dst.element_size() if nbytes is None else int(nbytes)
+    if n > dst.numel() * dst.element_size():
+        raise ValueError("write larger than the buffer")
+    _check(lib.fr_stream_write(_ptr(dst), n, ctypes.c_uint32(value & 0xFFFFFFFF),
+                               _stream(stream, dst)), "fr_stream_write")
 
 
 def fr_debug_force_variant(op: int, threads: int = 0, vecs: int = 0) -> None:

@@ -136,7 +136,7 @@ int vec_epv(int esz) { return 16 / esz; }
 }  // namespace
 
 namespace {
-std::atomic<int64_t> g_split_batch_bytes{FR_SPLIT_BATCH_BYTES};
+std::atomic<int64_t> g_split_batch_bytes{fr::kSplitBatchBytes};
 }  // namespace
 
 namespace fr {
@@ -163,7 +163,7 @@ int fr_debug_last_launch_error(void) { return t_last_launch_error; }
 
 int64_t fr_debug_set_split_batch_bytes(int64_t bytes) {
   const int64_t prev = g_split_batch_bytes.load();
-  g_split_batch_bytes.store(bytes < 0 ? FR_SPLIT_BATCH_BYTES : bytes);
+  g_split_batch_bytes.store(bytes < 0 ? fr::kSplitBatchBytes : bytes);
   return prev;
 }
 
@@ -375,14 +375,13 @@ fr_status_t fr_add_rmsnorm_fwd(const void* x, const void* residual, const void* 
                                  static_cast<hipStream_t>(stream)));
 }
 
-fr_status_t fr_softmax_xent_fwd_bwd(const void* logits, const int32_t* labels, float* loss,
-                                    void* grad, int32_t* argmax, int64_t rows, int64_t cols,
-                                    fr_dtype_t dtype, void* stream) {
+fr_status_t fr_softmax_xent_fwd_bwd(const float* logits, const int32_t* labels, float* loss,
+                                    float* grad, int32_t* argmax, int64_t rows, int64_t cols,
+                                    void* stream) {
   if (fr_status_t s = check_shape(rows, cols)) return s;
-  if (dtype != FR_F32) return FR_E_DTYPE;
   if (rows == 0) return FR_OK;
   if (!logits || !labels || !loss || !grad) return FR_E_NULL;
-  const int es = esize(dtype);
+  const int es = 4;
   if (!aligned(logits, es) || !aligned(grad, es) || !aligned(labels, 4) || !aligned(loss, 4) ||
       (argmax && !aligned(argmax, 4)))
     return FR_E_ALIGN;
@@ -853,8 +852,8 @@ fr_status_t fr_attention_fwd(const void* q, const void* k, const void* v, void* 
   if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0) return FR_E_SHAPE;
   if (head_dim != 64 && head_dim != 128) return FR_E_SHAPE;
   if (seq_q > INT32_MAX / 2 || seq_k > INT32_MAX / 2) return FR_E_SHAPE;
+  if (heads > 0 && batch > INT64_MAX / heads) return FR_E_SHAPE;  // before the product
   const int64_t bh = batch * heads;
-  if (heads > 0 && batch > INT64_MAX / heads) return FR_E_SHAPE;
   if (bh > 65535 || bh * ((seq_q + 127) / 128) > INT32_MAX) return FR_E_SHAPE;
   if (dtype != FR_BF16) return FR_E_DTYPE;
   if (!std::isfinite(scale)) return FR_E_VALUE;
@@ -884,6 +883,46 @@ fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stre
   const Buf bufs[] = {make_buf(src, bytes, false, 1, false), make_buf(dst, bytes, false, 1, true)};
   if (fr_status_t s = check_alias(bufs, 2)) return s;
   return launch_status(fr::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+int64_t fr_stream_probe_rows(int64_t bytes, int threads, int vecs) {
+  if (bytes < 0 || !fr::stream_probe_shape_exists(threads, vecs)) return -1;
+  return fr::stream_probe_rows(bytes, threads, vecs);
+}
+
+fr_status_t fr_stream_probe(fr_probe_t kind, const void* src, void* dst, int64_t bytes,
+                            uint32_t value, uint32_t* sink, int threads, int vecs, int policy,
+                            void* stream) {
+  if (kind != FR_PROBE_READ && kind != FR_PROBE_WRITE && kind != FR_PROBE_COPY) return FR_E_VALUE;
+  if (!fr::stream_probe_shape_exists(threads, vecs)) return FR_E_VARIANT;
+  if (policy < 0 || policy > (FR_PROBE_NT_LOADS | FR_PROBE_NT_STORES)) return FR_E_VALUE;
+  if (bytes < 0 || bytes % 16 != 0) return FR_E_SHAPE;
+  if (bytes == 0) return FR_OK;
+  const bool reads = kind != FR_PROBE_WRITE, writes = kind != FR_PROBE_READ;
+  if ((reads && !src) || (writes && !dst) || (kind == FR_PROBE_READ && !sink)) return FR_E_NULL;
+  if ((reads && !aligned(src, 16)) || (writes && !aligned(dst, 16)) ||
+      (kind == FR_PROBE_READ && !aligned(sink, 4)))
+    return FR_E_ALIGN;
+  const int64_t rows = fr::stream_probe_rows(bytes, threads, vecs);
+  const Buf bufs[] = {make_buf(reads ? src : nullptr, bytes, false, 1, false),
+                      make_buf(writes ? dst : nullptr, bytes, false, 1, true),
+                      make_buf(kind == FR_PROBE_READ ? sink : nullptr, rows * 4, false, 4, true)};
+  if (fr_status_t s = check_alias(bufs, 3)) return s;
+  return launch_status(fr::launch_stream_probe((int)kind, reads ? src : nullptr,
+                                               writes ? dst : nullptr, bytes, threads, vecs,
+                                               policy, value,
+                                               kind == FR_PROBE_READ ? sink : nullptr,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+fr_status_t fr_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  return fr_stream_probe(FR_PROBE_READ, src, nullptr, bytes, 0, sink, FR_STREAM_THREADS,
+                         FR_STREAM_VECS, FR_STREAM_POLICY, stream);
+}
+
+fr_status_t fr_stream_write(void* dst, int64_t bytes, uint32_t value, void* stream) {
+  return fr_stream_probe(FR_PROBE_WRITE, nullptr, dst, bytes, value, nullptr, FR_STREAM_THREADS,
+                         FR_STREAM_VECS, FR_STREAM_POLICY, stream);
 }
 
 }  // extern "C"

@@ -42,24 +42,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAttnBlockM = 128;  // queries per workgroup (4 waves x 32)
 constexpr float kLazy = 8.f;      // stale-max allowance, base-2 units
-// FR_ATTN_XCD: group the workgroups of whole heads on one XCD (when batch x
-// heads is a multiple of 8): 574 -> 564 us non-causal, the slowest tenth of
-// the calls 690 -> 580 us; causal unchanged (305 us)
-#ifndef FR_ATTN_XCD
-#define FR_ATTN_XCD 1
-#endif
-// FR_ATTN_PRIO: raise the wave's issue priority over its matrix-core chains,
-// so that the other waves of the SIMD fill the gaps with their softmax work
-// (measured 594 -> 585 us and 320 -> 317 us at B=4 H=16 S=4096 D=128)
-#ifndef FR_ATTN_PRIO
-#define FR_ATTN_PRIO 1
-#endif
-__device__ __forceinline__ void mfma_prio_hi() {
-  if constexpr (FR_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
-}
-__device__ __forceinline__ void mfma_prio_lo() {
-  if constexpr (FR_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
-}
+// The wave's issue priority is raised over its matrix-core chains, so that
+// the other waves of the SIMD fill the gaps with their softmax work
+// (measured 594 -> 585 us and 320 -> 317 us at B=4 H=16 S=4096 D=128).
+__device__ __forceinline__ void mfma_prio_hi() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_prio_lo() { __builtin_amdgcn_s_setprio(0); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -107,14 +94,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int nqb = (Sq + kAttnBlockM - 1) / kAttnBlockM;
   int64_t bh;
   int qidx;
-  if (FR_ATTN_XCD && BH % 8 == 0) {
+  if (BH % 8 == 0) {
     // Workgroups are dealt to the 8 XCDs round-robin: XCD x receives
     // blockIdx x, x + 8, ...; give it the heads x BH/8 .. (x + 1) BH/8 - 1
     // with all their query blocks, so the K/V tiles of those heads are shared
-    // in its own L2 and every XCD gets the same mix of query blocks
+    // in its own L2 and every XCD gets the same mix of query blocks (measured
+    // at B=4 H=16 S=4096 D=128: 574 -> 564 us, the slowest tenth of the calls
+    // 690 -> 580 us; causal unchanged)
     const int64_t hx = BH / 8;
     const int64_t slot = blockIdx.x / 8, x = blockIdx.x % 8;
-    if (causal || FR_ATTN_XCD == 2) {  // query block slowest: most keys first across the heads
+    if (causal) {  // query block slowest: most keys first across the heads
       bh = x * hx + slot % hx;
       qidx = (int)(slot / hx);
     } else {  // head by head
@@ -371,9 +360,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
 }
 
-#ifndef FR_ATTN_BN
-#define FR_ATTN_BN 32
-#endif
+// Key blocks of 32 (64-key blocks measured no faster: 580 -> 597 us, 239
+// VGPRs and two waves per SIMD instead of three).
+constexpr int kAttnBlockN = 32;
 
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int64_t BH, int Sq, int Sk, int D, int causal, float scale,
@@ -386,9 +375,9 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
   const bf16_t* vp = static_cast<const bf16_t*>(v);
   bf16_t* op = static_cast<bf16_t*>(o);
   if (D == 64)
-    return launch_kernel(&attention_fwd_kernel<64, FR_ATTN_BN>, grid, dim3(256), s, qp, kp, vp, op,
+    return launch_kernel(&attention_fwd_kernel<64, kAttnBlockN>, grid, dim3(256), s, qp, kp, vp, op,
                          lse, BH, Sq, Sk, causal, sl2);
-  return launch_kernel(&attention_fwd_kernel<128, FR_ATTN_BN>, grid, dim3(256), s, qp, kp, vp, op,
+  return launch_kernel(&attention_fwd_kernel<128, kAttnBlockN>, grid, dim3(256), s, qp, kp, vp, op,
                        lse, BH, Sq, Sk, causal, sl2);
 }
 

@@ -80,9 +80,9 @@ void softmax_bwd_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int col
   const int tid = T == 64 ? lane : (int)threadIdx.x;
   const int sub = T == 64 ? wib : 0;
   const int wave = T == 64 ? 0 : wib;
-  int it = 0;
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
-       row += (int64_t)gridDim.x * RPB, ++it) {
+       row += (int64_t)gridDim.x * RPB) {
     const int64_t off = row * cols;
     const RowGeom<EPV> g(p + off, cols);
 
@@ -102,14 +102,14 @@ void softmax_bwd_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int col
       }
     SumState st{s0 + s1};
     st = wave_reduce(st, SumMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SumMerge{});
 
     const float s = st.s;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int k = 0; k < EPV; ++k) a[i][k] = a[i][k] * (d[i][k] - s);
-    store_chunks<Ts, T, NV, EPV>(dx + off, g, tid, a);
+    store_chunks<Ts, T, NV, EPV, false>(dx + off, g, tid, a);  // cached stores (st_stream)
     if (ec >= 0) store1(dx + off + ec, ae * (de - s));
   }
 }
@@ -212,11 +212,12 @@ struct Slots {
   __device__ __forceinline__ void param(const Ts* par, int i, float* v) const {
     load_param<Ts, EPV>(par + off(i), v);
   }
-  template <typename Ts>
+  // NTS: non-temporal stores (the kernel's store policy, see st_stream)
+  template <bool NTS, typename Ts>
   __device__ __forceinline__ void store(Ts* r, const float (&v)[NV][EPV]) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (ok(i)) Vec<Ts, EPV>::store(r + off(i), v[i]);
+      if (ok(i)) Vec<Ts, EPV>::template store<NTS>(r + off(i), v[i]);
   }
 };
 
@@ -291,7 +292,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
       __builtin_amdgcn_global_load_lds(
           static_cast<const void*>(src + sl.off(i)),
           (__attribute__((address_space(3))) void*)(stage + ((op * NV + i) * T * RPB + 64 * wib) * 4),
-          16, 0, FR_NT_LOAD ? 2 : 0);
+          16, 0, kCopyNT);
   };
   auto stage_rows = [&](int64_t b) {  // the rows of iteration base b (uniform)
     const int64_t rw = b + ln.sub;
@@ -354,9 +355,9 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
 #pragma unroll
     for (int k = 0; k < EPV; ++k) acc[i][k] = 0.f;
 
-  int it = 0;
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows;
-       base += (int64_t)gridDim.x * RPB, ++it) {
+       base += (int64_t)gridDim.x * RPB) {
     const int64_t row = base + ln.sub;
     const bool live = row < rows;  // uniform in the wave; a dead group re-reads the last row
     const int64_t off = (live ? row : rows - 1) * cols;
@@ -392,7 +393,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
     }
     Sum2State st{a0 + a1, b0 + b1};
     st = wave_reduce(st, Sum2Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[ln.sub][it & 1], ln.wave, ln.lane, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[ln.sub][merges++ & 1], ln.wave, ln.lane, Sum2Merge{});
 
     if (live) {
       const float r = 1.f / __builtin_sqrtf(st.a / (float)cols + eps);
@@ -411,7 +412,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
         }
       }
     }
-    if (live) sl.store(dh + off, hv);
+    if (live) sl.template store<false>(dh + off, hv);  // cached stores (st_stream)
     if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
   float* pbuf = STG ? reinterpret_cast<float*>(stage) : part;
@@ -450,7 +451,7 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma,
       __builtin_amdgcn_global_load_lds(
           static_cast<const void*>(src + sl.off(i)),
           (__attribute__((address_space(3))) void*)(stage + ((op * NV + i) * T * RPB + 64 * wib) * 4),
-          16, 0, FR_NT_LOAD ? 2 : 0);
+          16, 0, kCopyNT);
   };
   // this lane's staged x and dy chunks, read past the compiler's LDS-copy
   // wait (the counted wait has covered them)
@@ -498,9 +499,9 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma,
 #pragma unroll
     for (int k = 0; k < EPV; ++k) { ag[i][k] = 0.f; ab[i][k] = 0.f; }
 
-  int it = 0;
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows;
-       base += (int64_t)gridDim.x * RPB, ++it) {
+       base += (int64_t)gridDim.x * RPB) {
     const int64_t row = base + ln.sub;
     const bool live = row < rows;
     const int64_t rr = live ? row : rows - 1;
@@ -545,7 +546,7 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma,
     }
     Sum2State st{a0 + a1, b0 + b1};
     st = wave_reduce(st, Sum2Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[ln.sub][it & 1], ln.wave, ln.lane, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[ln.sub][merges++ & 1], ln.wave, ln.lane, Sum2Merge{});
 
     if (live) {
       const float mg = st.a / (float)cols;
@@ -567,7 +568,7 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma,
           n[i][k] = rs * __builtin_fmaf(-n[i][k], mgn, __builtin_fmaf(d[i][k], ga[k], -mg));
         }
       }
-      sl.store(dx + off, n);
+      sl.template store<false>(dx + off, n);  // cached stores (st_stream)
     }
     if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
@@ -604,8 +605,8 @@ void norm_bwd_split_sums_kernel(const Ts* xh, const Ts* dy, const Ts* w, const f
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t wk = blockIdx.x; wk < work; wk += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t wk = blockIdx.x; wk < work; wk += gridDim.x) {
     const int64_t row = wk / nseg;
     const int c0 = (int)(wk - row * nseg) * SEG;
     const int len = cols - c0 < SEG ? cols - c0 : SEG;
@@ -640,7 +641,7 @@ void norm_bwd_split_sums_kernel(const Ts* xh, const Ts* dy, const Ts* w, const f
     }
     Sum2State st{a0 + a1, b0 + b1};
     st = wave_reduce(st, Sum2Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, Sum2Merge{});
     if (tid == 0) part[wk] = float4{st.a, st.b, 0.f, 0.f};
   }
 }
@@ -693,8 +694,8 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
     }
   };
 
-  int it = 0;
-  for (int64_t row = rg; row < rows; row += RG, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t row = rg; row < rows; row += RG) {
     // the segment's row operands first: they do not depend on the row sums,
     // so their loads are in flight while the partials are merged (the merge's
     // barrier would otherwise keep them behind it)
@@ -709,7 +710,7 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
       st = Sum2Merge{}(st, Sum2State{p.x, p.y});
     }
     st = wave_reduce(st, Sum2Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Sum2Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, Sum2Merge{});
 
     const Ts* w1 = fresh(w) + c0;
     if constexpr (LN) {
@@ -743,7 +744,7 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
         }
       }
     }
-    sl.store(out + off, a);
+    sl.template store<true>(out + off, a);  // split pass: non-temporal (st_stream)
   }
   // this workgroup's partial row segment (slots past the segment end hold 0
   // and are not written)
@@ -818,17 +819,14 @@ static hipError_t launch_softmax_bwd(const void* p, const void* dy, void* dx, in
                        rows, cols);
 }
 
-// Staging with dres as well (three staged operands, 96 KiB).
-#ifndef FR_RB_STG_DRES
-#define FR_RB_STG_DRES 1
-#endif
 template <typename Ts, int T, int NV, int EPV, int RPB, int OCC, bool STG = false>
 static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* dres, const void* w,
                                      void* dh, float* ws, int grid, int64_t rows, int cols,
                                      float eps, hipStream_t s) {
-  // measured at 8192^2 (weight in LDS, counted waits): with dres
-  // 100.1 -> 96.2 us, without 89.9 -> 80.2 us
-  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true, STG && (FR_RB_STG_DRES != 0)>
+  // staged with dres as well (three operands, 96 KiB): measured at 8192^2
+  // (weight in LDS, counted waits) with dres 100.1 -> 96.2 us, without
+  // 89.9 -> 80.2 us
+  auto k = dres ? &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, true, STG>
                 : &rmsnorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, false, STG>;
   return launch_kernel(k, dim3(grid), dim3(T * RPB), s, static_cast<const Ts*>(h),
                        static_cast<const Ts*>(dy), static_cast<const Ts*>(dres),
@@ -840,15 +838,12 @@ static hipError_t launch_rmsnorm_bwd(const void* h, const void* dy, const void* 
 // spill with gamma held in registers). Measured: bf16 16384 x 4096
 // 89.6 -> 74.0 us; fp32 16384 x 4096 150.8 -> 145.7 us, 8192 x 8192
 // 154.2 -> 148.9 us, 16384 x 1024 43.4 -> 42.4 us, 4096 x 1024 18.1 -> 17.8 us.
-#ifndef FR_LB_STG
-#define FR_LB_STG 1
-#endif
 template <typename Ts, int T, int NV, int EPV, int RPB, int OCC>
 static hipError_t launch_layernorm_bwd(const void* x, const void* dy, const void* gamma,
                                        const float* mean, const float* rstd, void* dx, float* ws,
                                        int grid, int64_t rows, int cols, hipStream_t s) {
   constexpr bool STG =
-      FR_LB_STG && T < 1024 && EPV * sizeof(Ts) == 16 && 2 * NV * T * RPB * 16 <= 128 * 1024;
+      T < 1024 && EPV * sizeof(Ts) == 16 && 2 * NV * T * RPB * 16 <= 128 * 1024;
   return launch_kernel(&layernorm_bwd_kernel<Ts, T, NV, EPV, RPB, OCC, STG>, dim3(grid), dim3(T * RPB), s,
                        static_cast<const Ts*>(x), static_cast<const Ts*>(dy),
                        static_cast<const Ts*>(gamma), mean, rstd, static_cast<Ts*>(dx), ws, rows,
@@ -915,11 +910,8 @@ hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* x
 // (grid_max 256, OCC 4: at most 128 VGPRs).
 #define FR_RB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC>}
 // The 8192-column bf16 shape stages its next rows (h, dy and dres) in LDS.
-#ifndef FR_RB_STG
-#define FR_RB_STG 1
-#endif
 #define FR_RBS(TS, T, NV, EPV, RPB, OCC, G) \
-  {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC, (FR_RB_STG != 0)>}
+  {T, NV, EPV, RPB, G, &launch_rmsnorm_bwd<TS, T, NV, EPV, RPB, OCC, true>}
 #define FR_LB(TS, T, NV, EPV, RPB, OCC, G) {T, NV, EPV, RPB, G, &launch_layernorm_bwd<TS, T, NV, EPV, RPB, OCC>}
 #define FR_SB(TS, T, NV, EPV, OCC) {T, NV, EPV, &launch_softmax_bwd<TS, T, NV, EPV, OCC>}
 

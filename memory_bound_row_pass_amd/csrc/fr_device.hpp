@@ -80,61 +80,66 @@ __device__ __forceinline__ float exp_acc(float t) {
 }
 
 // --------------------------------------------------------------- global access
-// Inputs are streamed once: non-temporal loads and stores keep them from
-// displacing other data in L2 / MALL. FR_NT_LOAD / FR_NT_STORE (default 1)
-// select the hint at build time.
-#ifndef FR_NT_LOAD
-#define FR_NT_LOAD 1
-#endif
-#ifndef FR_NT_STORE
-#define FR_NT_STORE 1
-#endif
-// ld_stream: NT == true is the non-temporal hint; NT == false an ordinary
-// cached load, for data that is read again soon (the first pass of a
-// two-pass kernel).
-template <bool NT = (FR_NT_LOAD != 0), typename V>
+// Inputs are streamed once with non-temporal loads (measured on MI355X: the
+// fastest load policy for every row kernel; the read-only probe reaches
+// 6.9-7.3 TB/s with them against 6.0-6.7 TB/s with cached loads).
+// ld_stream<false> is an ordinary cached load, for data that is read again
+// soon (the first pass of a two-pass kernel).
+// Stores: the policy is the kernel's (st_stream<NT>). Measured per kernel on
+// MI355X: ordinary cached stores are faster for the softmax, LayerNorm,
+// bf16 RMSNorm and backward kernels (residual-add + RMSNorm bf16 8192^2
+// 89.5 -> 80.5 us, softmax bf16 16384 x 4096 46.8 -> 43.8 us), non-temporal
+// ones for the cross-entropy (fp32 4096 x 50257 311 -> 285 us), the split-row
+// passes (whose second read of a row batch comes from the cache that cached
+// stores would fill) and fp32 RMSNorm (183 -> 174 us at 8192^2).
+template <bool NT = true, typename V>
 __device__ __forceinline__ V ld_stream(const V* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
-template <typename V>
+template <bool NT = true, typename V>
 __device__ __forceinline__ void st_stream(V v, V* p) {
-  if constexpr (FR_NT_STORE) __builtin_nontemporal_store(v, p);
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
   else *p = v;
 }
+// Cache-policy bits of global_load_lds for streamed data: the non-temporal
+// hint, as ld_stream.
+constexpr int kCopyNT = 2;
 
 template <typename T, int EPV>
 struct Vec;  // load/store EPV consecutive elements as fp32
 
 template <>
 struct Vec<float, 4> {
-  template <bool NT = (FR_NT_LOAD != 0)>
+  template <bool NT = true>
   static __device__ __forceinline__ void load(const float* p, float* v) {
     f32x4 r = ld_stream<NT>(reinterpret_cast<const f32x4*>(p));
     v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
   }
+  template <bool NT = true>
   static __device__ __forceinline__ void store(float* p, const float* v) {
     f32x4 r = {v[0], v[1], v[2], v[3]};
-    st_stream(r, reinterpret_cast<f32x4*>(p));
+    st_stream<NT>(r, reinterpret_cast<f32x4*>(p));
   }
 };
 
 template <>
 struct Vec<float, 8> {  // output side of bf16 -> f32 (two 16-byte stores)
-  template <bool NT = (FR_NT_LOAD != 0)>
+  template <bool NT = true>
   static __device__ __forceinline__ void load(const float* p, float* v) {
     Vec<float, 4>::load<NT>(p, v);
     Vec<float, 4>::load<NT>(p + 4, v + 4);
   }
+  template <bool NT = true>
   static __device__ __forceinline__ void store(float* p, const float* v) {
-    Vec<float, 4>::store(p, v);
-    Vec<float, 4>::store(p + 4, v + 4);
+    Vec<float, 4>::store<NT>(p, v);
+    Vec<float, 4>::store<NT>(p + 4, v + 4);
   }
 };
 
 template <>
 struct Vec<bf16_t, 8> {
-  template <bool NT = (FR_NT_LOAD != 0)>
+  template <bool NT = true>
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
     u32x4 r = ld_stream<NT>(reinterpret_cast<const u32x4*>(p));
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
@@ -142,47 +147,51 @@ struct Vec<bf16_t, 8> {
     v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
     v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
   }
+  template <bool NT = true>
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
     u32x4 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-    st_stream(r, reinterpret_cast<u32x4*>(p));
+    st_stream<NT>(r, reinterpret_cast<u32x4*>(p));
   }
 };
 
 template <>
 struct Vec<bf16_t, 4> {  // output side of f32 -> bf16 (one 8-byte store)
-  template <bool NT = (FR_NT_LOAD != 0)>
+  template <bool NT = true>
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
     u32x2 r = ld_stream<NT>(reinterpret_cast<const u32x2*>(p));
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
     v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
   }
+  template <bool NT = true>
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
     u32x2 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    st_stream(r, reinterpret_cast<u32x2*>(p));
+    st_stream<NT>(r, reinterpret_cast<u32x2*>(p));
   }
 };
 
 template <>
 struct Vec<float, 1> {
-  template <bool NT = (FR_NT_LOAD != 0)>
+  template <bool NT = true>
   static __device__ __forceinline__ void load(const float* p, float* v) {
     v[0] = ld_stream<NT>(p);
   }
+  template <bool NT = true>
   static __device__ __forceinline__ void store(float* p, const float* v) {
-    st_stream(v[0], p);
+    st_stream<NT>(v[0], p);
   }
 };
 
 template <>
 struct Vec<bf16_t, 1> {
-  template <bool NT = (FR_NT_LOAD != 0)>
+  template <bool NT = true>
   static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
     uint16_t u = ld_stream<NT>(reinterpret_cast<const uint16_t*>(p));
     v[0] = __uint_as_float((uint32_t)u << 16);
   }
+  template <bool NT = true>
   static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
-    st_stream(to_bf16(v[0]), reinterpret_cast<uint16_t*>(p));
+    st_stream<NT>(to_bf16(v[0]), reinterpret_cast<uint16_t*>(p));
   }
 };
 
@@ -296,7 +305,7 @@ __device__ __forceinline__ uint32_t opaque_zero() {
   return z;
 }
 
-template <typename Ts, int T, int NV, int EPV, int AL, bool NT = (FR_NT_LOAD != 0)>
+template <typename Ts, int T, int NV, int EPV, int AL, bool NT = true>
 __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                             float (&v)[NV][EPV], float fill) {
   if (g.nvec > 0) {
@@ -324,9 +333,7 @@ __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL
   }
 }
 
-// Next-row prefetch: the first PF slots of a row loaded as raw 16-byte
-// chunks (no unpacking, no masking) ahead of time, then unpacked into the
-// register row. Slot i of lane t is chunk i*T + t, as in load_chunks.
+// A 16-byte chunk as loaded (raw), and its unpacking into fp32 values.
 template <typename Ts>
 struct RawChunk;
 template <>
@@ -347,66 +354,15 @@ struct RawChunk<bf16_t> {
   }
 };
 
-template <typename Ts, int T, int PF, int EPV, int AL>
-__device__ __forceinline__ void prefetch_slots(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
-                                               typename RawChunk<Ts>::T (&r)[PF]) {
-  static_assert(EPV * sizeof(Ts) == 16, "16-byte chunks");
-  if (g.nvec > 0) {
-    const Ts* base = row + g.head;
-    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
-    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      uint32_t o = (uint32_t)(i * T * EPV) + lo;
-      o = o < last ? o : last;
-      r[i] = ld_stream(reinterpret_cast<const typename RawChunk<Ts>::T*>(base + o));
-    }
-  }
-}
-
-// The row into registers when its first PF slots were prefetched into `r`:
-// the other slots are loaded now, then all are masked as in load_chunks.
-template <typename Ts, int T, int NV, int PF, int EPV, int AL>
-__device__ __forceinline__ void load_chunks_pf(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
-                                               const typename RawChunk<Ts>::T (&r)[PF],
-                                               float (&v)[NV][EPV], float fill) {
-  if (g.nvec > 0) {
-    const Ts* base = row + g.head;
-    const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
-    const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
-#pragma unroll
-    for (int i = PF; i < NV; ++i) {
-      uint32_t o = (uint32_t)(i * T * EPV) + lo;
-      o = o < last ? o : last;
-      Vec<Ts, EPV>::load(base + o, v[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < PF; ++i) RawChunk<Ts>::unpack(r[i], v[i]);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if ((i + 1) * T <= g.nvec) continue;  // uniform: the whole slot lies in the row
-      const bool ok = i * T + tid < g.nvec;
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] = ok ? v[i][k] : fill;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] = fill;
-  }
-}
-
-// Next-row staging: LDS slots and register slots. Slot i < LPF of lane t is
-// copied from global memory straight into LDS by global_load_lds_dwordx4,
-// which holds no VGPRs while in flight and writes lane l of a wave at that
-// wave's LDS base + 16 l (checked on gfx950 for both cache policies); with
-// the base of wave w at slot i set to 16 (i T + 64 w), lane t's chunk lands
-// at 16 (i T + t) and is read back by lane t itself, so no barrier is
-// needed. Slots LPF .. LPF + PF - 1 are loaded into registers (`pre`), raw.
+// Next-row staging in LDS: slot i < LPF of lane t is copied from global
+// memory straight into LDS by global_load_lds_dwordx4, which holds no VGPRs
+// while in flight and writes lane l of a wave at that wave's LDS base + 16 l
+// (checked on gfx950 for both cache policies); with the base of wave w at
+// slot i set to 16 (i T + 64 w), lane t's chunk lands at 16 (i T + t) and is
+// read back by lane t itself, so no barrier is needed.
 // The compiler does not order these copies against LDS reads:
-// wait_lds_copies() precedes reading staged data, and wait_lds_reads()
-// precedes staging over data that was read.
+// wait_lds_copies() (or a counted wait) precedes reading staged data, and
+// wait_lds_reads() precedes staging over data that was read.
 __device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // All but the K most recently issued vector memory operations of this wave
 // have completed (they retire in issue order).
@@ -458,10 +414,9 @@ __device__ __forceinline__ void read_staged(const uint32_t (&a)[N], u32x4 (&r)[N
   if constexpr (N % 2 == 1) read_staged1(a + N - 1, r + N - 1);
 }
 
-template <typename Ts, int T, int LPF, int PF, int EPV, int AL>
+template <typename Ts, int T, int LPF, int EPV, int AL>
 __device__ __forceinline__ void stage_row(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
-                                          int wave, uint32_t* stage,
-                                          typename RawChunk<Ts>::T (&pre)[PF > 0 ? PF : 1]) {
+                                          int wave, uint32_t* stage) {
   static_assert(EPV * sizeof(Ts) == 16, "16-byte chunks");
   if (g.nvec > 0) {
     const Ts* base = row + g.head;
@@ -474,38 +429,30 @@ __device__ __forceinline__ void stage_row(const Ts* row, const RowGeom<EPV, AL>&
       __builtin_amdgcn_global_load_lds(
           static_cast<const void*>(base + o),
           (__attribute__((address_space(3))) void*)(stage + (i * T + wave * 64) * 4), 16, 0,
-          FR_NT_LOAD ? 2 : 0);
-    }
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      uint32_t o = (uint32_t)((LPF + i) * T * EPV) + lo;
-      o = o < last ? o : last;
-      pre[i] = ld_stream(reinterpret_cast<const typename RawChunk<Ts>::T*>(base + o));
+          kCopyNT);
     }
   }
 }
 
-// The row into registers when its first LPF + PF slots were staged by
-// stage_row: the remaining slots are loaded from global memory, the staged
-// ones taken from LDS (after waiting for the copies unless `copies_done`)
-// and from `pre`; all are masked as in load_chunks.
-template <typename Ts, int T, int NV, int LPF, int PF, int EPV, bool HIDDEN, int AL>
+// The row into registers when its first LPF slots were staged by stage_row
+// and the caller has waited for the copies: the remaining slots are loaded
+// from global memory, the staged ones taken from LDS; all are masked as in
+// load_chunks.
+template <typename Ts, int T, int NV, int LPF, int EPV, bool HIDDEN, int AL>
 __device__ __forceinline__ void load_staged(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
-                                            const uint32_t* stage,
-                                            const typename RawChunk<Ts>::T (&pre)[PF > 0 ? PF : 1],
-                                            bool copies_done, float (&v)[NV][EPV], float fill) {
-  static_assert(LPF + PF <= NV, "staged slots");
+                                            const uint32_t* stage, float (&v)[NV][EPV],
+                                            float fill) {
+  static_assert(LPF <= NV, "staged slots");
   if (g.nvec > 0) {
     const Ts* base = row + g.head;
     const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
     const uint32_t last = (uint32_t)(g.nvec - 1) * EPV;
 #pragma unroll
-    for (int i = LPF + PF; i < NV; ++i) {
+    for (int i = LPF; i < NV; ++i) {
       uint32_t o = (uint32_t)(i * T * EPV) + lo;
       o = o < last ? o : last;
       Vec<Ts, EPV>::load(base + o, v[i]);
     }
-    if (!copies_done) wait_lds_copies();
     // HIDDEN: read past the compiler's LDS-copy wait (read_staged), two
     // chunks at a time, each pair unpacked at once; the lane's LDS offset is
     // formed anew in every row (opaque zero), so no per-slot address is kept
@@ -533,8 +480,6 @@ __device__ __forceinline__ void load_staged(const Ts* row, const RowGeom<EPV, AL
       RawChunk<Ts>::unpack(r, v[i]);
     }
 #pragma unroll
-    for (int i = 0; i < PF; ++i) RawChunk<Ts>::unpack(pre[i], v[LPF + i]);
-#pragma unroll
     for (int i = 0; i < NV; ++i) {
       if ((i + 1) * T <= g.nvec) continue;  // uniform: the whole slot lies in the row
       const bool ok = i * T + tid < g.nvec;
@@ -551,7 +496,7 @@ __device__ __forceinline__ void load_staged(const Ts* row, const RowGeom<EPV, AL
 
 // Two row operands of the same geometry in one branch, so that the second
 // operand's loads are issued before the first operand's data is waited for.
-template <typename Ts, int T, int NV, int EPV, int AL, bool NT = (FR_NT_LOAD != 0)>
+template <typename Ts, int T, int NV, int EPV, int AL, bool NT = true>
 __device__ __forceinline__ void load_chunks2(const Ts* ra, const Ts* rb, const RowGeom<EPV, AL>& g,
                                              int tid, float (&a)[NV][EPV], float (&b)[NV][EPV],
                                              float fill) {
@@ -591,7 +536,8 @@ __device__ __forceinline__ float load_extra(const Ts* row, int ec, float fill) {
   return ec >= 0 ? v : fill;
 }
 
-template <typename Ts, int T, int NV, int EPV, int AL>
+// NTS: non-temporal stores (the kernel's store policy, see st_stream).
+template <typename Ts, int T, int NV, int EPV, bool NTS = true, int AL>
 __device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                              const float (&v)[NV][EPV]) {
   Ts* base = row + g.head;
@@ -599,8 +545,8 @@ __device__ __forceinline__ void store_chunks(Ts* row, const RowGeom<EPV, AL>& g,
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     Ts* p = base + ((uint32_t)(i * T * EPV) + lo);
-    if ((i + 1) * T <= g.nvec) Vec<Ts, EPV>::store(p, v[i]);  // uniform: the whole slot
-    else if (i * T + tid < g.nvec) Vec<Ts, EPV>::store(p, v[i]);
+    if ((i + 1) * T <= g.nvec) Vec<Ts, EPV>::template store<NTS>(p, v[i]);  // uniform: whole slot
+    else if (i * T + tid < g.nvec) Vec<Ts, EPV>::template store<NTS>(p, v[i]);
   }
 }
 
@@ -755,9 +701,13 @@ struct WelfordMerge {
 // -------------------------------------------------------- cross-wave merge
 // Row-per-workgroup kernels: lane 0 of each wave puts the wave's state in
 // LDS, one barrier, then every lane merges the NW states in wave order, so
-// all waves see bitwise the same row state. `buf` alternates between two
-// slots across consecutive rows of a persistent loop, so a slot is never
-// rewritten while a slower wave may still read it.
+// all waves see bitwise the same row state. A kernel that merges more than
+// once passes the two slot buffers alternately, switching with every merge
+// it performs (a counter of merges, not of rows: a row that skips its merge
+// must not switch). Each merge has one barrier, so a buffer is written again
+// only after the barrier of the merge in between, which every wave reaches
+// after its reads of that buffer have completed (the barrier waits for the
+// wave's LDS reads): no wave overwrites a state a slower wave still reads.
 template <int NW, typename S, int NF>
 struct XWave {
   float slot[2][NW][NF];
@@ -768,13 +718,9 @@ struct XWave {
 // through this barrier. (__syncthreads() is a workgroup fence as well, which
 // here waits for every outstanding vector memory operation of the wave: the
 // previous row's stores and the next row's staged copies, which would then
-// stop overlapping the rest of the row.) FR_LDS_BARRIER = 0 restores it.
-#ifndef FR_LDS_BARRIER
-#define FR_LDS_BARRIER 1
-#endif
+// stop overlapping the rest of the row.)
 __device__ __forceinline__ void lds_barrier() {
-  if constexpr (FR_LDS_BARRIER) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int NW, typename S, typename Merge>

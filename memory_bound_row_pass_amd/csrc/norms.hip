@@ -36,9 +36,9 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
   const int tid = T == 64 ? lane : (int)threadIdx.x;
   const int sub = T == 64 ? wib : 0;
   const int wave = T == 64 ? 0 : wib;
-  int it = 0;
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
-       row += (int64_t)gridDim.x * RPB, ++it) {
+       row += (int64_t)gridDim.x * RPB) {
     const Ts* xr = x + row * cols;
     Ts* yr = y + row * cols;
     const RowGeom<EPV> g(xr, cols);
@@ -81,7 +81,7 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
     }
     WelfordState st{(float)n_l, mu_l, q0 + q1};
     st = wave_reduce(st, WelfordMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, WelfordMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, WelfordMerge{});
 
     const float mu = st.mu;
     const float rs = 1.f / __builtin_sqrtf(st.m2 / (float)cols + eps);
@@ -95,7 +95,7 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
 #pragma unroll
         for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf((v[i][k] - mu) * rs, ga[k], be[k]);
       }
-      store_chunks<Ts, T, NV, EPV>(yr, g, tid, v);
+      store_chunks<Ts, T, NV, EPV, false>(yr, g, tid, v);  // cached stores (st_stream)
     }
     if (ec >= 0) store1(yr + ec, __builtin_fmaf((xe - mu) * rs, load1(gamma + ec), load1(beta + ec)));
     if (wave == 0 && lane == 0) {
@@ -112,6 +112,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
   constexpr int BLOCK = T == 64 ? 256 : T;
   constexpr int RPB = BLOCK / T;
   constexpr int NW = T / 64;
+  constexpr bool kNts = sizeof(Ts) == 4;  // store policy: non-temporal for fp32 (st_stream)
   __shared__ float xw[2][NW][1];
 
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -119,9 +120,9 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
   const int tid = T == 64 ? lane : (int)threadIdx.x;
   const int sub = T == 64 ? wib : 0;
   const int wave = T == 64 ? 0 : wib;
-  int it = 0;
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
-       row += (int64_t)gridDim.x * RPB, ++it) {
+       row += (int64_t)gridDim.x * RPB) {
     const int64_t off = row * cols;
     const RowGeom<EPV> g(x + off, cols);
 
@@ -135,7 +136,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
 #pragma unroll
       for (int k = 0; k < EPV; ++k) h[i][k] += r[i][k];
     if (res_out) {  // updated residual, rounded once at the store
-      store_chunks<Ts, T, NV, EPV>(res_out + off, g, tid, h);
+      store_chunks<Ts, T, NV, EPV, kNts>(res_out + off, g, tid, h);
       if (ec >= 0) store1(res_out + off + ec, he);
     }
 
@@ -149,7 +150,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
       }
     SumState st{q0 + q1};
     st = wave_reduce(st, SumMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SumMerge{});
 
     const float rs = 1.f / __builtin_sqrtf(st.s / (float)cols + eps);
     if (g.nvec > 0) {
@@ -160,7 +161,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
 #pragma unroll
         for (int k = 0; k < EPV; ++k) h[i][k] = h[i][k] * rs * wt[k];
       }
-      store_chunks<Ts, T, NV, EPV>(y + off, g, tid, h);
+      store_chunks<Ts, T, NV, EPV, kNts>(y + off, g, tid, h);
     }
     if (ec >= 0) store1(y + off + ec, he * rs * load1(w + ec));
   }

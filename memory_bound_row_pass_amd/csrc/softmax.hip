@@ -14,17 +14,10 @@
 
 namespace fr {
 
-// bf16 outputs: FR_SOFTMAX_BIAS8 takes the exponentials with a 2^8 bias (every
-// e_j <= 2^8) and applies one factor f = g 2^n per lane with one multiply per
-// element: where f is subnormal its rounding (<= 2^-150) moves p_j by at most
-// 2^-142, a 2^-9 fraction of the finest bf16 step; where f is normal the
-// product is exactly the two-step ldexp(e_j g, n) value. Otherwise the 2^64
-// bias and the two-step scaling. Measured at 16384 x 4096: 48.1 -> 46.7 us.
-#ifndef FR_SOFTMAX_BIAS8
-#define FR_SOFTMAX_BIAS8 1
-#endif
-constexpr int kSoftmaxBias = FR_SOFTMAX_BIAS8 ? 8 : 64;
-
+// bf16 outputs: exponentials with the 2^8 bias (every e_j <= 2^8) and one
+// factor f = G 2^n per lane, applied with one multiply per element (the
+// rounding argument is log2_scale's). Measured at 16384 x 4096 against a
+// 2^64 bias with a two-step ldexp scaling: 48.1 -> 46.7 us.
 template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC>
 __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC))) void softmax_kernel(const Tin* x, Tout* y,
                                                                      int64_t rows, int cols) {
@@ -41,9 +34,9 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_
   const int tid = T == 64 ? lane : (int)threadIdx.x;  // lane within the row owner
   const int sub = T == 64 ? wib : 0;                   // row slot within the block
   const int wave = T == 64 ? 0 : wib;                  // wave within the row owner
-  int it = 0;
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows;
-       row += (int64_t)gridDim.x * RPB, ++it) {
+       row += (int64_t)gridDim.x * RPB) {
     const Tin* xr = x + row * cols;
     Tout* yr = y + row * cols;
     const RowGeom<EPV> g(xr, cols);
@@ -55,26 +48,18 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_
 
     const float m = lane_max<NV, EPV>(v, xe);
     MaxSumState st =
-        kLog2 ? lane_exp_log2<NV, EPV, kSoftmaxBias>(v, xe, m) : lane_exp_nat<NV, EPV>(v, xe, m);
+        kLog2 ? lane_exp_log2<NV, EPV>(v, xe, m) : lane_exp_nat<NV, EPV>(v, xe, m);
     st = wave_reduce(st, Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, Merge{});
 
     if constexpr (kLog2) {
       const Log2Scale sc = log2_scale(m, st.m, st.s);
-      if constexpr (FR_SOFTMAX_BIAS8) {
-        const float f = __builtin_ldexpf(sc.g, sc.n);
+      const float f = __builtin_ldexpf(sc.g, sc.n);
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
+      for (int i = 0; i < NV; ++i)
 #pragma unroll
-          for (int k = 0; k < EPV; ++k) v[i][k] *= f;
-        xe *= f;
-      } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) v[i][k] = apply_scale(v[i][k], sc);
-        xe = apply_scale(xe, sc);
-      }
+        for (int k = 0; k < EPV; ++k) v[i][k] *= f;
+      xe *= f;
     } else {
       const float f = nat_scale(m, st.m, st.s);
 #pragma unroll
@@ -84,7 +69,7 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_
       xe *= f;
     }
 
-    store_chunks<Tout, T, NV, EPV>(yr, g, tid, v);
+    store_chunks<Tout, T, NV, EPV, false>(yr, g, tid, v);  // cached stores (st_stream)
     if (ec >= 0) store1(yr + ec, xe);
   }
 }
@@ -120,7 +105,8 @@ static const SoftmaxVariant kSmBf16Bf16[] = {
     FR_SM(bf16_t, bf16_t, 64, 4, 8, 6),   FR_SM(bf16_t, bf16_t, 64, 8, 8, 4),
     FR_SM(bf16_t, bf16_t, 256, 2, 8, 8),  FR_SM(bf16_t, bf16_t, 256, 4, 8, 6),
     FR_SM(bf16_t, bf16_t, 512, 4, 8, 6),  FR_SM(bf16_t, bf16_t, 1024, 4, 8, 4),
-    FR_SM(bf16_t, bf16_t, 1024, 8, 8, 4), FR_SM_SCALAR(bf16_t, bf16_t)};
+    FR_SM(bf16_t, bf16_t, 1024, 8, 8, 4), FR_SM(bf16_t, bf16_t, 128, 4, 8, 8),
+    FR_SM(bf16_t, bf16_t, 512, 1, 8, 8),  FR_SM_SCALAR(bf16_t, bf16_t)};
 static const SoftmaxVariant kSmF32Bf16[] = {
     FR_SM(float, bf16_t, 64, 1, 4, 8),    FR_SM(float, bf16_t, 64, 2, 4, 8),
     FR_SM(float, bf16_t, 64, 4, 4, 8),    FR_SM(float, bf16_t, 64, 8, 4, 6),

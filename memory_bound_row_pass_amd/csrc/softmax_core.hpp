@@ -42,14 +42,18 @@ __device__ __forceinline__ float lane_max(const float (&v)[NV][EPV], float xe) {
 }
 
 // ---------------------------------------------------------------- bf16 path
-// e_j = 2^((x_j - m_l)*log2e + 64) lies in (0, 2^64] and is normal down to
-// x_j - m_l = -131, which covers every value that can round to a non-zero
-// bf16 (p >= 2^-134). Forming x_j - m_l first keeps the argument finite for
-// any finite input (m_l*log2e alone overflows for |m_l| > 2.3e38). The lane
-// state (m_l, s_l) stays in natural units.
-// (BIAS: the exponent offset, 64 by default; S carries the same factor, so
-// it cancels in p_j.)
-template <int NV, int EPV, int BIAS = 64>
+// e_j = 2^(y_j + kExpBias) with y_j = (x_j - m_l)*log2e <= 0, so e_j lies in
+// (0, 2^8]. p_j <= 2^y_j (m_l <= M and the row sum is >= 1 in natural
+// units), so every e_j whose p_j can round to a non-zero bf16 (p_j >= 2^-134)
+// is >= 2^-126: a normal fp32 value at full precision. 8 is the least bias
+// that does this; a larger one would keep fewer bits of y_j + bias and make
+// the row sum (which the cross-entropy loss takes) less accurate. Forming
+// x_j - m_l first keeps the argument finite for any finite input (m_l*log2e
+// alone overflows for |m_l| > 2.3e38). The lane state (m_l, s_l) keeps m_l in
+// natural units; s_l carries the 2^8 factor, which cancels in p_j.
+constexpr int kExpBias = 8;
+
+template <int NV, int EPV>
 __device__ __forceinline__ MaxSumState lane_exp_log2(float (&v)[NV][EPV], float& xe, float m) {
   const float mr = (m == kNegInf) ? 0.f : m;
   float s0 = 0.f, s1 = 0.f;
@@ -57,18 +61,21 @@ __device__ __forceinline__ MaxSumState lane_exp_log2(float (&v)[NV][EPV], float&
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int k = 0; k < EPV; ++k) {
-      v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, (float)BIAS));
+      v[i][k] = exp2_hw(__builtin_fmaf(v[i][k] - mr, kLog2e, (float)kExpBias));
       if (k & 1) s1 += v[i][k]; else s0 += v[i][k];
     }
-  xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, (float)BIAS));
+  xe = exp2_hw(__builtin_fmaf(xe - mr, kLog2e, (float)kExpBias));
   return {m, (s0 + s1) + xe};
 }
 
-// p_j = e_j * 2^((m_l - M)*log2e) / S, where S carries the same 2^64 bias.
-// The factor is split as G * 2^n with G = 2^(d - n) / S normal
-// (d = (m_l - M)*log2e, n = floor(d)), and 2^n is applied with v_ldexp, so
-// results in the bf16 subnormal range are rounded from a full-precision fp32
-// value instead of a flushed factor.
+// p_j = e_j * 2^((m_l - M)*log2e) / S, where S carries the same 2^8 factor.
+// The lane factor is split as G * 2^n with G = 2^(d - n) / S normal
+// (d = (m_l - M)*log2e, n = floor(d)); callers form f = ldexp(G, n) once per
+// lane and take one multiply (or fma) per element. Where f is normal the
+// product rounds the exact e_j * G * 2^n once. Where f is subnormal (a lane
+// whose maximum lies ~80 below the row's) its own rounding, at most 2^-150,
+// moves p_j by at most e_j * 2^-150 <= 2^-142: a 2^-9 fraction of the finest
+// bf16 step, so bf16 subnormal results stay within one ulp.
 struct Log2Scale {
   float g;
   int n;
@@ -81,10 +88,6 @@ __device__ __forceinline__ Log2Scale log2_scale(float m, float M, float S) {
   float fl = __builtin_floorf(d);
   fl = fl < -300.f ? -300.f : fl;  // also maps -inf to -300
   return {exp2_hw(d - fl) / S, (int)fl};
-}
-
-__device__ __forceinline__ float apply_scale(float e, const Log2Scale& s) {
-  return __builtin_ldexpf(e * s.g, s.n);
 }
 
 // ---------------------------------------------------------------- fp32 path

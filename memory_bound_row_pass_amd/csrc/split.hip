@@ -73,8 +73,8 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const Segment sgm(sg, seg, cols);
@@ -132,7 +132,7 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
     const float se = exp2_hw((xe - mr) * kLog2e);
     SplitState st{m, (s0 + s1) + se, t, best};
     st = wave_reduce(st, SplitMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SplitMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SplitMerge{});
     if (tid == 0) part[w] = float4{st.m, st.s, st.t, st.idx};
   }
 }
@@ -192,8 +192,8 @@ void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, 
   }
 
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const Segment sgm(sg, seg, cols);
@@ -218,14 +218,14 @@ void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, 
       if (ec >= 0) store1(ys + ec, 0.f);
       if (argmax) {  // uniform: every lane takes part in the merge (it has a barrier);
                      // pass 1 wrote this row's partials because argmax is wanted
-        const SplitState st = merge_row<T>(part, row, nseg, xw[it & 1], wave, lane, tid);
+        const SplitState st = merge_row<T>(part, row, nseg, xw[merges++ & 1], wave, lane, tid);
         if (sg == 0 && tid == 0) argmax[row] = (int32_t)st.idx;
       }
       if (sg == 0 && tid == 0) loss[row] = 0.f;
       continue;
     }
 
-    const SplitState st = merge_row<T>(part, row, nseg, xw[it & 1], wave, lane, tid);
+    const SplitState st = merge_row<T>(part, row, nseg, xw[merges++ & 1], wave, lane, tid);
     const float inv_s = 1.f / st.s;
 
     float v[NV][EPV];
@@ -291,8 +291,8 @@ void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
     const int64_t row = w / nseg;
     const Segment sgm((int)(w - row * nseg), seg, cols);
     const int64_t off = row * cols + sgm.c0;
@@ -310,7 +310,7 @@ void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int
       }
     SumState st{s0 + s1};
     st = wave_reduce(st, SumMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SumMerge{});
     if (tid == 0) part[w] = float4{st.s, 0.f, 0.f, 0.f};
   }
 }
@@ -325,14 +325,14 @@ void softmax_bwd_split_apply_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t r
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
     const int64_t row = w / nseg;
     const Segment sgm((int)(w - row * nseg), seg, cols);
     SumState st{0.f};
     for (int j = tid; j < nseg; j += T) st.s += part[row * nseg + j].x;
     st = wave_reduce(st, SumMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SumMerge{});
     const float s = st.s;
     const int64_t off = row * cols + sgm.c0;
     const RowGeom<EPV> g(p + off, sgm.len);

@@ -82,8 +82,8 @@ void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols,
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const NormSegment sgm(sg, seg, cols);
@@ -105,14 +105,14 @@ void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols,
         }
       SumState st{q0 + q1};
       st = wave_reduce(st, SumMerge{});
-      if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, SumMerge{});
+      if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SumMerge{});
       if (tid == 0) part[w] = float4{st.s, 0.f, 0.f, 0.f};
     } else {
       load_chunks<Ts, T, NV, EPV, kHeadAlign, kPass1NT>(x + off, g, tid, v, 0.f);
       const float xe = load_extra(x + off, ec, 0.f);
       WelfordState st = lane_moments<T, NV, EPV>(v, xe, ec, g, tid);
       st = wave_reduce(st, WelfordMerge{});
-      if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, WelfordMerge{});
+      if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, WelfordMerge{});
       if (tid == 0) part[w] = float4{st.n, st.mu, st.m2, 0.f};
     }
   }
@@ -147,8 +147,8 @@ void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts*
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
-  int it = 0;
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const NormSegment sgm(sg, seg, cols);
@@ -160,7 +160,7 @@ void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts*
     if constexpr (RMS) {
       const SumState st = merge_partials<T>(
           part, row, nseg, SumState{0.f}, [](float4 p) { return SumState{p.x}; },
-          xw[it & 1], wave, lane, tid, SumMerge{});
+          xw[merges++ & 1], wave, lane, tid, SumMerge{});
       const float rs = 1.f / __builtin_sqrtf(st.s / (float)cols + eps);
       float r[NV][EPV];
       load_chunks2<Ts, T, NV, EPV>(x + off, res + off, g, tid, v, r, 0.f);
@@ -187,7 +187,7 @@ void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts*
     } else {
       const WelfordState st = merge_partials<T>(
           part, row, nseg, WelfordState{0.f, 0.f, 0.f},
-          [](float4 p) { return WelfordState{p.x, p.y, p.z}; }, xw[it & 1], wave, lane, tid,
+          [](float4 p) { return WelfordState{p.x, p.y, p.z}; }, xw[merges++ & 1], wave, lane, tid,
           WelfordMerge{});
       const float mu = st.mu;
       const float rs = 1.f / __builtin_sqrtf(st.m2 / (float)cols + eps);

@@ -58,37 +58,23 @@ __device__ __forceinline__ int owner_lane(int c, const RowGeom<EPV>& g) {
 }
 
 // Exponentials and scaling: bf16 logits (bf16 gradient) take the biased
-// base-2 form of the bf16 softmax, so gradients in the bf16 subnormal range
-// are exact; fp32 logits take the natural form with the compensated
-// exponential. The bias here is 2^8, the least that keeps every e_j normal
-// down to p = 2^-134 (p <= 2^y with y = (x_j - m_l) log2e): a smaller bias
-// keeps more bits of y + bias, so the row sum, and with it the loss, stays
-// accurate to ~3e-7 relative (2^64 would leave ~2.6e-6).
-constexpr int kXentBias = 8;
+// base-2 form of the bf16 softmax (lane_exp_log2, 2^8 bias), so gradients in
+// the bf16 subnormal range are computed within one ulp and the row sum, and
+// with it the loss, stays accurate to ~3e-7 relative (a 2^64 bias would leave
+// ~2.6e-6); fp32 logits take the natural form with the compensated
+// exponential.
 
-// LDS staging waits: 0 waits for the next row's copies before the current
-// row's stores; 1 waits at the next row's start for all but the current
-// row's whole-slot stores (vector memory operations retire in issue order),
-// so the stores are not held back: bf16 4096 x 50257 with options
-// 166 -> 159 us, plain 170 -> 163 us.
-#ifndef FR_XE_LPF_COUNTED
-#define FR_XE_LPF_COUNTED 1
-#endif
-
-// PF > 0: the first PF slots of the row owner's next row are loaded before
-// the current row's reduction, so the CU keeps reads in flight while it
-// reduces and writes (PF * 4 more VGPRs per lane).
 // LPF > 0 (one row per workgroup): the next row is staged while the current
 // one is reduced and written: its first LPF slots in LDS (16 T bytes of LDS
-// per slot, no VGPRs), the next PF slots in registers, and its head/tail
-// element, all issued right after the current row is in registers. Vector
-// memory operations retire in issue order: at the next row's start, a wait
-// that leaves the current row's whole-slot stores outstanding has seen every
-// copy complete (FR_XE_LPF_COUNTED), so neither the stores nor the next row
-// wait for each other (a plain wait there would wait for the stores too).
-// The grid is then one workgroup per compute unit, each looping over rows.
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0,
-          int LPF = 0>
+// per slot, no VGPRs) and its head/tail element, issued right after the
+// current row is in registers. The grid is then one workgroup per compute
+// unit, each looping over rows. Vector memory operations retire in issue
+// order: at the next row's start, a wait that leaves the current row's
+// whole-slot stores outstanding has seen every copy complete, so neither the
+// stores nor the next row wait for each other (bf16 4096 x 50257 with
+// options 166 -> 159 us, plain 170 -> 163 us, against a full wait for the
+// copies before the current row's stores).
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int LPF = 0>
 __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_eu(OCC)))
 void xent_kernel(const Tin* x,
                  // no output overlaps the labels (the entry points reject it), so the
@@ -106,7 +92,7 @@ void xent_kernel(const Tin* x,
   using Merge = typename std::conditional<OPT, PlusSumMerge<Base, BaseMerge>, BaseMerge>::type;
   constexpr int NF = sizeof(State) / sizeof(float);
   __shared__ float xw[2][NW][NF];
-  static_assert(LPF == 0 || (RPB == 1 && LPF + PF <= NV), "LDS staging: one row per block");
+  static_assert(LPF == 0 || (RPB == 1 && LPF <= NV), "LDS staging: one row per block");
   __shared__ __attribute__((aligned(16))) uint32_t stage[LPF > 0 ? LPF * T * 4 : 4];
 
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -129,13 +115,11 @@ void xent_kernel(const Tin* x,
   const int64_t stride = (int64_t)gridDim.x * RPB;
   const int64_t first = (int64_t)blockIdx.x * RPB + sub;
   int label_next = first < rows ? __builtin_amdgcn_readfirstlane(labels[first]) : 0;
-  static_assert(PF == 0 || EPV * sizeof(Tin) == 16, "prefetch of 16-byte chunks");
-  typename RawChunk<Tin>::T pre[PF > 0 ? PF : 1];
-  bool have_pre = false;     // uniform: pre (and stage) hold this row's first slots
-  bool copies_done = false;  // uniform (LPF): the staging copies were waited for
-  // uniform (LPF, counted waits): whole-slot stores issued after the latest
-  // staging; with at least NV - 1 of them a wait that leaves that many
-  // operations outstanding has seen every staging copy complete
+  static_assert(LPF == 0 || EPV * sizeof(Tin) == 16, "staging of 16-byte chunks");
+  bool have_pre = false;  // uniform: the LDS stage holds this row's first slots
+  // uniform (LPF): whole-slot stores issued after the latest staging; with at
+  // least NV - 1 of them a wait that leaves that many operations outstanding
+  // has seen every staging copy complete
   int stores_after = 0;
   // LPF: the staged row's head/tail element. Its load is issued before the
   // row's copies and converted before the current row's stores, and the
@@ -155,13 +139,13 @@ void xent_kernel(const Tin* x,
       const RowGeom<EPV> g0(x0, cols);
       const int e0 = g0.extra_col(tid);
       if (e0 >= 0) xe_raw = load1_raw(x0 + e0);
-      stage_row<Tin, T, LPF, PF, EPV>(x0, g0, tid, wave, stage, pre);
+      stage_row<Tin, T, LPF, EPV>(x0, g0, tid, wave, stage);
       xe_next = raw_value<Tin>(raw_here(xe_raw));
     }
   }
 
-  int it = 0;
-  for (int64_t row = first; row < rows; row += stride, ++it) {
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t row = first; row < rows; row += stride) {
     const Tin* xr = x + row * cols;
     Tin* gr = grad + row * cols;
     const RowGeom<EPV> g(xr, cols);
@@ -181,22 +165,17 @@ void xent_kernel(const Tin* x,
         store_chunks<Tin, T, NV, EPV>(gr, g, tid, z);
         if (ec >= 0) store1(gr + ec, 0.f);
         if (tid == 0) loss[row] = 0.f;
-        if constexpr (PF > 0 || LPF > 0) {
+        if constexpr (LPF > 0) {
           have_pre = rn < rows && !(opt.use_ignore && label_next == opt.ignore_index);
           if (have_pre) {
             const Tin* xn = x + rn * cols;
-            if constexpr (LPF > 0) {
-              wait_lds_reads();
-              const RowGeom<EPV> gn(xn, cols);
-              const int en = gn.extra_col(tid);
-              xe_raw = en >= 0 ? load1_raw(xn + en) : kRawNegInf<Tin>;
-              stage_row<Tin, T, LPF, PF, EPV>(xn, gn, tid, wave, stage, pre);
-              xe_next = raw_value<Tin>(raw_here(xe_raw));
-              copies_done = false;
-              stores_after = 0;  // staged after this row's stores
-            } else {
-              prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
-            }
+            wait_lds_reads();
+            const RowGeom<EPV> gn(xn, cols);
+            const int en = gn.extra_col(tid);
+            xe_raw = en >= 0 ? load1_raw(xn + en) : kRawNegInf<Tin>;
+            stage_row<Tin, T, LPF, EPV>(xn, gn, tid, wave, stage);
+            xe_next = raw_value<Tin>(raw_here(xe_raw));
+            stores_after = 0;  // staged after this row's stores
           }
         }
         continue;
@@ -213,51 +192,38 @@ void xent_kernel(const Tin* x,
     float xe;
     if constexpr (LPF > 0) {
       if (have_pre) {
-        if constexpr (FR_XE_LPF_COUNTED) {
-          if (stores_after >= NV - 1) wait_vmcnt_upto<NV - 1>();
-          else wait_lds_copies();
-          copies_done = true;
-        }
-        load_staged<Tin, T, NV, LPF, PF, EPV, kLate>(xr, g, tid, stage, pre, copies_done, v, kNegInf);
+        if (stores_after >= NV - 1) wait_vmcnt_upto<NV - 1>();
+        else wait_lds_copies();
+        load_staged<Tin, T, NV, LPF, EPV, kLate>(xr, g, tid, stage, v, kNegInf);
         xe = xe_next;
       } else {
         load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
         xe = ec >= 0 ? load1(xr + ec) : kNegInf;
       }
     } else {
-      if constexpr (PF > 0) {
-        if (have_pre) load_chunks_pf<Tin, T, NV, PF, EPV>(xr, g, tid, pre, v, kNegInf);
-        else load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
-      } else {
-        load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
-      }
+      load_chunks<Tin, T, NV, EPV>(xr, g, tid, v, kNegInf);
       xe = ec >= 0 ? load1(xr + ec) : kNegInf;
     }
     uint32_t x_label_raw = 0;  // converted where it is used, after the row's reduction
     if (label_lane) x_label_raw = load1_raw(xr + label);
-    if constexpr (PF > 0 || LPF > 0) {
+    if constexpr (LPF > 0) {
       // the next row's first slots (not when it is an ignored row that is
       // not read)
       have_pre = rn < rows &&
                  !(OPT && !ARGMAX && opt.use_ignore && label_next == opt.ignore_index);
       if (have_pre) {
         const Tin* xn = x + rn * cols;
-        if constexpr (LPF > 0) {
-          wait_lds_reads();  // this row's staged slots are in registers
-          const RowGeom<EPV> gn(xn, cols);
-          const int en = gn.extra_col(tid);
-          if constexpr (kLate) {
-            xe_raw = en >= 0 ? load1_raw(xn + en) : kRawNegInf<Tin>;  // converted before the stores
-            stage_row<Tin, T, LPF, PF, EPV>(xn, gn, tid, wave, stage, pre);
-          } else {
-            stage_row<Tin, T, LPF, PF, EPV>(xn, gn, tid, wave, stage, pre);
-            xe_next = en >= 0 ? load1(xn + en) : kNegInf;
-          }
-          copies_done = false;
-          stores_after = 0;
+        wait_lds_reads();  // this row's staged slots are in registers
+        const RowGeom<EPV> gn(xn, cols);
+        const int en = gn.extra_col(tid);
+        if constexpr (kLate) {
+          xe_raw = en >= 0 ? load1_raw(xn + en) : kRawNegInf<Tin>;  // converted before the stores
+          stage_row<Tin, T, LPF, EPV>(xn, gn, tid, wave, stage);
         } else {
-          prefetch_slots<Tin, T, PF, EPV>(xn, RowGeom<EPV>(xn, cols), tid, pre);
+          stage_row<Tin, T, LPF, EPV>(xn, gn, tid, wave, stage);
+          xe_next = en >= 0 ? load1(xn + en) : kNegInf;
         }
+        stores_after = 0;
       }
     }
 
@@ -301,7 +267,7 @@ void xent_kernel(const Tin* x,
     }
     {
       // e_j replaces x_j
-      const MaxSumState ms = LOG2 ? lane_exp_log2<NV, EPV, kXentBias>(v, xe, m)
+      const MaxSumState ms = LOG2 ? lane_exp_log2<NV, EPV>(v, xe, m)
                                   : lane_exp_nat<NV, EPV>(v, xe, m);
       bs.m = ms.m;
       bs.s = ms.s;
@@ -310,7 +276,7 @@ void xent_kernel(const Tin* x,
     if constexpr (OPT) st = State{bs, tsum};
     else st = bs;
     st = wave_reduce(st, Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[it & 1], wave, lane, Merge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, Merge{});
     Base rs;
     if constexpr (OPT) {
       rs = st.st;
@@ -318,8 +284,8 @@ void xent_kernel(const Tin* x,
     } else {
       rs = st;
     }
-    // the row sum in natural units (the base-2 form carries the 2^kXentBias bias)
-    const float s_row = LOG2 ? __builtin_ldexpf(rs.s, -kXentBias) : rs.s;
+    // the row sum in natural units (the base-2 form carries the 2^kExpBias bias)
+    const float s_row = LOG2 ? __builtin_ldexpf(rs.s, -kExpBias) : rs.s;
 
     if (OPT && ignored) {  // (argmax wanted) zero row, loss 0
 #pragma unroll
@@ -355,19 +321,11 @@ void xent_kernel(const Tin* x,
         for (int k = 0; k < EPV; ++k) v[i][k] *= f;
       xe *= f;
     }
-    if constexpr (LPF > 0 && !FR_XE_LPF_COUNTED) {
-      // the next row's copies have had the reduction to arrive; waiting here
-      // keeps the next row's start from waiting for this row's stores
-      if (have_pre) {
-        wait_lds_copies();
-        copies_done = true;
-      }
-    }
     // the next row's head/tail element, before this row's stores (its wait
     // leaves the next row's copies in flight)
     if constexpr (LPF > 0 && kLate) xe_next = raw_value<Tin>(raw_here(xe_raw));
     store_chunks<Tin, T, NV, EPV>(gr, g, tid, v);
-    if constexpr (LPF > 0 && FR_XE_LPF_COUNTED) stores_after = g.nvec / T;  // whole slots
+    if constexpr (LPF > 0) stores_after = g.nvec / T;  // whole slots
     if (ec >= 0) store1(gr + ec, xe);
 
     if (label_lane) {
@@ -451,8 +409,7 @@ hipError_t launch_xent_total(const float* loss, int64_t rows, const uint32_t* co
   return launch_kernel(&xent_total_kernel, dim3(1), dim3(1024), s, loss, rows, count, total);
 }
 
-template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int PF = 0,
-          int LPF = 0>
+template <typename Tin, int T, int NV, int EPV, int OCC, bool ARGMAX, bool OPT, int LPF = 0>
 static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss, void* grad,
                               int32_t* argmax, int64_t rows, int cols, const XentOptions* opt,
                               hipStream_t s) {
@@ -465,46 +422,25 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   }
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
   const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
-  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT, PF, LPF>, dim3(grid), dim3(BLOCK), s,
+  return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT, LPF>, dim3(grid), dim3(BLOCK), s,
                        static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax,
                        rows, cols, o);
 }
 
 #define FR_XE(TS, T, NV, EPV, OCC, AM, OPT) {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT>}
-// Prefetch depths (measured at 4096 x 50257): one slot helps the bf16 rows
-// (177 -> 170 us); fp32 rows are no faster with 2-5 slots (285 -> 290 us: the
-// reads are already at the mixed read/write ceiling) and the options
-// kernels spill with any.
-#ifndef FR_XE_PF_F32
-#define FR_XE_PF_F32 0
-#endif
-#ifndef FR_XE_PF_F32_OPT
-#define FR_XE_PF_F32_OPT 0
-#endif
-#ifndef FR_XE_PF_BF16
-#define FR_XE_PF_BF16 1
-#endif
 // LDS staging of the next row (measured at 4096 x 50257): the whole bf16 row
 // (7 slots, 112 KiB) takes the options kernel from 170 to 165 us and the
-// argmax kernel from 284 to 200 us; fp32 rows (9 slots in LDS, the other 4
-// in registers) measured 287 -> 295 us and stay unstaged.
-#ifndef FR_XE_LPF_F32
-#define FR_XE_LPF_F32 0
-#endif
-#ifndef FR_XE_LPF_F32_OPT
-#define FR_XE_LPF_F32_OPT 0
-#endif
-#ifndef FR_XE_LPF_BF16
-#define FR_XE_LPF_BF16 7
-#endif
-#define FR_XF(TS, T, NV, EPV, OCC, AM, OPT, PF, LPF) \
-  {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT, PF, LPF>}
+// argmax kernel from 284 to 200 us (a one-slot register prefetch had taken
+// the options kernel from 177 to 170 us before). fp32 rows stay unstaged:
+// 9 slots in LDS measured 287 -> 295 us, 2-5 register slots 285 -> 290 us.
+#define FR_XE_STAGED(TS, T, NV, EPV, OCC, AM, OPT, LPF) \
+  {T, NV, EPV, &launch_xent<TS, T, NV, EPV, OCC, AM, OPT, LPF>}
 #define FR_XE_F32(AM, OPT)                                                                       \
   {FR_XE(float, 64, 1, 4, 8, AM, OPT),    FR_XE(float, 64, 2, 4, 8, AM, OPT),                    \
    FR_XE(float, 64, 4, 4, 8, AM, OPT),    FR_XE(float, 64, 8, 4, 6, AM, OPT),                    \
    FR_XE(float, 64, 16, 4, 4, AM, OPT),   FR_XE(float, 256, 8, 4, 6, AM, OPT),                   \
    FR_XE(float, 512, 8, 4, 6, AM, OPT),   FR_XE(float, 1024, 8, 4, 4, AM, OPT),                  \
-   FR_XF(float, 1024, 13, 4, 4, AM, OPT, (OPT ? FR_XE_PF_F32_OPT : FR_XE_PF_F32), (OPT ? FR_XE_LPF_F32_OPT : FR_XE_LPF_F32)), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
+   FR_XE(float, 1024, 13, 4, 4, AM, OPT), FR_XE(float, 512, 25, 4, 4, AM, OPT),                  \
    FR_XE(float, 256, 50, 4, 2, AM, OPT),  FR_XE(float, 1024, 16, 4, 4, AM, OPT),                 \
    FR_XE(float, 64, 16, 1, 4, AM, OPT),   FR_XE(float, 256, 16, 1, 4, AM, OPT),                  \
    FR_XE(float, 1024, 16, 1, 4, AM, OPT), FR_XE(float, 1024, 64, 1, 4, AM, OPT)}
@@ -512,7 +448,7 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
   {FR_XE(bf16_t, 64, 1, 8, 8, AM, true),    FR_XE(bf16_t, 64, 2, 8, 8, AM, true),                \
    FR_XE(bf16_t, 64, 4, 8, 6, AM, true),    FR_XE(bf16_t, 64, 8, 8, 4, AM, true),                \
    FR_XE(bf16_t, 256, 4, 8, 6, AM, true),   FR_XE(bf16_t, 512, 4, 8, 6, AM, true),               \
-   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XF(bf16_t, 1024, 7, 8, 4, AM, true, (FR_XE_LPF_BF16 ? 0 : FR_XE_PF_BF16), FR_XE_LPF_BF16),              \
+   FR_XE(bf16_t, 1024, 4, 8, 4, AM, true),  FR_XE_STAGED(bf16_t, 1024, 7, 8, 4, AM, true, 7),    \
    FR_XE(bf16_t, 1024, 8, 8, 4, AM, true),  FR_XE(bf16_t, 64, 16, 1, 4, AM, true),               \
    FR_XE(bf16_t, 256, 16, 1, 4, AM, true),  FR_XE(bf16_t, 1024, 16, 1, 4, AM, true),             \
    FR_XE(bf16_t, 1024, 64, 1, 4, AM, true)}

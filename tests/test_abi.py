@@ -88,15 +88,68 @@ def test_add_rmsnorm_validation():
     assert f(P(A), P(Rz), P(W), P(Y), P(A + 1), 4, 8, 1e-6, 1, None) == E_ALIGN
 
 
+# The interface of the four row operations and the status string, as the
+# contract fixes it (whitespace aside): a caller compiled against these
+# prototypes must find exactly them in the header.
+CONTRACT = [
+    "fr_status_t fr_softmax_fwd(const void* x, void* y, int64_t rows, int64_t cols, "
+    "fr_dtype_t x_dtype, fr_dtype_t y_dtype, void* stream);",
+    "fr_status_t fr_layernorm_fwd(const void* x, const void* gamma, const void* beta, "
+    "void* y, float* mean, float* rstd, int64_t rows, int64_t cols, float eps, "
+    "fr_dtype_t dtype, void* stream);",
+    "fr_status_t fr_add_rmsnorm_fwd(const void* x, const void* residual, const void* weight, "
+    "void* y, void* residual_out, int64_t rows, int64_t cols, float eps, fr_dtype_t dtype, "
+    "void* stream);",
+    "fr_status_t fr_softmax_xent_fwd_bwd(const float* logits, const int32_t* labels, "
+    "float* loss, float* grad, int32_t* argmax, int64_t rows, int64_t cols, void* stream);",
+    "const char* fr_status_str(fr_status_t s);",
+]
+
+
+def _declarations():
+    """Every FR_API declaration of the header, comments removed, FR_API
+    dropped and whitespace collapsed (one space, none inside parentheses)."""
+    text = re.sub(r"/\*.*?\*/", " ", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^FR_API\s+([^;]*;)", text, re.M):
+        d = re.sub(r"\s+", " ", m.group(1)).replace("( ", "(").replace(" )", ")")
+        out[re.search(r"\b(fr_\w+)\s*\(", d).group(1)] = d
+    return out
+
+
+def test_contract_prototypes():
+    decl = _declarations()
+    for proto in CONTRACT:
+        name = re.search(r"\b(fr_\w+)\(", proto).group(1)
+        assert name in decl, name
+        assert decl[name] == proto, f"{name}:\n header   {decl[name]}\n contract {proto}"
+    # the enums' values are part of the binary interface
+    text = open(HEADER).read()
+    for name, value in [("FR_F32", 0), ("FR_BF16", 1), ("FR_OK", 0), ("FR_E_NULL", 1),
+                        ("FR_E_SHAPE", 2), ("FR_E_DTYPE", 3), ("FR_E_ALIAS", 4),
+                        ("FR_E_LAUNCH", 5)]:
+        assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
+
+
 def test_xent_validation():
+    # the contract's argument list: logits, labels, loss, grad, argmax, rows,
+    # cols, stream (fp32 logits and gradient; no dtype argument)
     f = fr.lib.fr_softmax_xent_fwd_bwd
     L, LS, G, AM = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
-    assert f(P(A), P(L), P(LS), P(G), P(AM), 0, 8, 0, None) == OK
-    assert f(P(A), P(L), P(LS), P(G), P(AM), 4, 8, 1, None) == E_DTYPE   # bf16 logits: not built
-    assert f(P(A), None, P(LS), P(G), None, 4, 8, 0, None) == E_NULL
-    assert f(P(A), P(L), P(LS), P(G), P(LS), 4, 8, 0, None) == E_ALIAS   # argmax over loss
-    assert f(P(A), P(L), P(L), P(G), None, 4, 8, 0, None) == E_ALIAS     # loss over labels
-    assert f(P(A), P(L), P(LS), P(A + 4), None, 4, 8, 0, None) == E_ALIAS
+    assert f(P(A), P(L), P(LS), P(G), P(AM), 0, 8, None) == OK
+    assert f(None, None, None, None, None, 0, 8, None) == OK    # rows == 0: nothing read
+    assert f(P(A), P(L), P(LS), P(G), P(AM), -1, 8, None) == E_SHAPE
+    assert f(P(A), P(L), P(LS), P(G), P(AM), 4, 0, None) == E_SHAPE
+    assert f(P(A), P(L), P(LS), P(G), P(AM), 4, fr.FR_MAX_COLS + 1, None) == E_SHAPE
+    assert f(P(A), None, P(LS), P(G), None, 4, 8, None) == E_NULL
+    assert f(P(A), P(L), P(LS), None, None, 4, 8, None) == E_NULL
+    assert f(P(A + 2), P(L), P(LS), P(G), None, 4, 8, None) == E_ALIGN   # fp32 logits
+    assert f(P(A), P(L), P(LS), P(G + 2), None, 4, 8, None) == E_ALIGN
+    assert f(P(A), P(L), P(LS), P(G), P(LS), 4, 8, None) == E_ALIAS   # argmax over loss
+    assert f(P(A), P(L), P(L), P(G), None, 4, 8, None) == E_ALIAS     # loss over labels
+    assert f(P(A), P(L), P(LS), P(A + 4), None, 4, 8, None) == E_ALIAS
+    # a non-NULL stream is the last argument, not a dtype: still validated first
+    assert f(P(A), P(L), P(LS), P(A + 4), None, 4, 8, P(0x1234)) == E_ALIAS
 
 
 def test_softmax_bwd_validation():
@@ -327,6 +380,7 @@ def test_attention_validation():
     assert call(sq=0) == OK
     assert call(d=96) == E_SHAPE
     assert call(b=70000) == E_SHAPE                      # batch * heads > 65535
+    assert call(b=2**62, h=2**40) == E_SHAPE             # batch * heads overflows int64
     assert call(dt=0) == E_DTYPE                         # bf16 only
     assert call(scale=float("nan")) == E_VALUE
     assert call(k=0) == E_NULL
@@ -341,6 +395,30 @@ def test_stream_copy_validation():
     assert f(P(A), P(B), -1, None) == E_SHAPE
     assert f(None, P(B), 16, None) == E_NULL
     assert f(P(A), P(A + 8), 16, None) == E_ALIAS
+
+
+def test_stream_probe_validation():
+    f = fr.lib.fr_stream_probe
+    S = A + 0x100000
+    READ, WRITE, COPY = fr.PROBE_READ, fr.PROBE_WRITE, fr.PROBE_COPY
+    assert f(READ, P(A), None, 0, 0, P(S), 256, 8, 1, None) == OK        # nothing to do
+    assert f(3, P(A), P(B), 16, 0, None, 256, 8, 1, None) == E_VALUE     # unknown probe
+    assert f(COPY, P(A), P(B), 16, 0, None, 256, 7, 1, None) == E_VARIANT  # no such shape
+    assert f(COPY, P(A), P(B), 16, 0, None, 256, 8, 4, None) == E_VALUE    # unknown policy bit
+    assert f(COPY, P(A), P(B), 24, 0, None, 256, 8, 1, None) == E_SHAPE  # not whole chunks
+    assert f(COPY, P(A), P(B), -16, 0, None, 256, 8, 1, None) == E_SHAPE
+    assert f(READ, P(A), None, 16, 0, None, 256, 8, 1, None) == E_NULL   # read needs a sink
+    assert f(WRITE, None, None, 16, 7, None, 256, 8, 1, None) == E_NULL
+    assert f(COPY, P(A + 4), P(B), 16, 0, None, 256, 8, 1, None) == E_ALIGN
+    assert f(READ, P(A), None, 16, 0, P(S + 2), 256, 8, 1, None) == E_ALIGN
+    assert f(COPY, P(A), P(A + 16), 32, 0, None, 256, 8, 1, None) == E_ALIAS
+    assert f(READ, P(A), None, 64, 0, P(A + 32), 64, 4, 1, None) == E_ALIAS  # sink in src
+    assert fr.lib.fr_stream_read(P(A), 24, P(S), None) == E_SHAPE
+    assert fr.lib.fr_stream_write(P(A + 8), 16, 1, None) == E_ALIGN
+    # rows of a shape: one sink word per row, partial last row included
+    assert fr.fr_stream_probe_rows(1 << 20, 256, 8) == 32
+    assert fr.fr_stream_probe_rows((1 << 20) + 16, 1024, 13) == (1 << 20) // (1024 * 13 * 16) + 1
+    assert fr.lib.fr_stream_probe_rows(16, 256, 7) == -1
 
 
 def test_variant_selection():

@@ -345,6 +345,24 @@ FR_API fr_status_t fr_add_rmsnorm_bwd(const void* h, const void* dy, const void*
                                int64_t rows, int64_t cols, float eps, fr_dtype_t dtype,
                                void* stream);
 
+/* fr_add_rmsnorm_bwd without a workspace: for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The dweight partial rows go to a device array the library
+ * holds, FR_NOALLOC_SCRATCH_BYTES per GPU (allocated with the library's code
+ * on each GPU it runs on, kept until the process ends); a call whose partial
+ * rows (min(rows, 256) or fewer, times cols * 4 bytes) exceed it returns
+ * FR_E_SHAPE — any row count up to 8192 columns fits. Nothing is allocated
+ * and nothing has to be cleared: each call overwrites the partials it reads.
+ * All calls on one GPU share its array, so calls that overlap in time on one
+ * GPU (on different streams) race and give wrong dweight: serialise them.
+ * Arguments, results and errors otherwise as fr_add_rmsnorm_bwd (the same
+ * kernels, so the results are bitwise those of fr_add_rmsnorm_bwd). */
+#define FR_NOALLOC_SCRATCH_BYTES (8 << 20)
+FR_API fr_status_t fr_add_rmsnorm_bwd_noalloc(const void* h, const void* dy, const void* dres,
+                                              const void* weight, void* dh, float* dweight,
+                                              int64_t rows, int64_t cols, float eps,
+                                              fr_dtype_t dtype, void* stream);
+
 /* Backward of LayerNorm (fr_layernorm_fwd) at its saved statistics.
  *   n_j = (x_j - mean) rstd,  g_j = dy_j gamma_j,
  *   dx_j = rstd (g_j - mean_k g_k - n_j mean_k(g_k n_k)),

@@ -24,6 +24,7 @@ __all__ = [
     "fr_debug_select_variant_for",
     "fr_debug_set_split_batch_bytes", "split_batch_bytes",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
+    "fr_add_rmsnorm_bwd_noalloc", "FR_NOALLOC_SCRATCH_BYTES",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
     "fr_softmax_fwd_split", "fr_softmax_xent_split", "fr_split_workspace_bytes",
     "OP_SOFTMAX_SPLIT", "OP_XENT_SPLIT", "FR_SPLIT_MAX_COLS", "fr_attention_fwd", "attention",
@@ -106,6 +107,7 @@ def _load() -> ctypes.CDLL:
                                   I64, P],
         "fr_add_rmsnorm_bwd": [P, P, P, P, P, P, P, I64, I64, I64, F, I32, P],
         "fr_layernorm_bwd": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, P],
+        "fr_add_rmsnorm_bwd_noalloc": [P, P, P, P, P, P, I64, I64, F, I32, P],
         "fr_debug_force_variant": [I32, I32, I32],
         "fr_debug_select_variant": [I32, I64, I32, I32, I32, IP, IP, IP],
         "fr_debug_select_variant_for": [I32, I64, I64, I32, I32, I32, IP, IP, IP],
@@ -494,6 +496,27 @@ def fr_add_rmsnorm_bwd(h, dy, weight, dh, dweight, workspace, dres=None, eps: fl
     _check(fn(_ptr(h), _ptr(dy), _ptr(dres), _ptr(weight), _ptr(dh), _ptr(dweight), wp, wn, R, C,
               float(eps), _dtype_code(h), _stream(stream, h)),
            "fr_add_rmsnorm_bwd_split" if _split else "fr_add_rmsnorm_bwd")
+
+
+FR_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def fr_add_rmsnorm_bwd_noalloc(h, dy, weight, dh, dweight, dres=None, eps: float = 1e-6,
+                               stream=None) -> None:
+    """fr_add_rmsnorm_bwd with the library's own device array in place of a
+    workspace (C: fr_add_rmsnorm_bwd_noalloc): allocates nothing; calls that
+    overlap in time on one GPU race."""
+    _need_cuda(h, dy, weight, dh, dweight, dres)
+    R, C = _rows_cols(h)
+    for t, n in ((dy, "dy"), (dh, "dh"), (dres, "dres")):
+        _check_like(t, h, n)
+    _check_vec(weight, C, "weight")
+    if weight.dtype != h.dtype:
+        raise TypeError("weight must have h's dtype")
+    _check_f32_vec(dweight, C, "dweight")
+    _check(lib.fr_add_rmsnorm_bwd_noalloc(_ptr(h), _ptr(dy), _ptr(dres), _ptr(weight), _ptr(dh),
+                                          _ptr(dweight), R, C, float(eps), _dtype_code(h),
+                                          _stream(stream, h)), "fr_add_rmsnorm_bwd_noalloc")
 
 
 def fr_layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream=None,

@@ -529,6 +529,42 @@ fr_status_t fr_add_rmsnorm_bwd(const void* h, const void* dy, const void* dres, 
   return launch_status(fr::launch_colsum(ws, grid, (int)cols, dweight, nullptr, st));
 }
 
+fr_status_t fr_add_rmsnorm_bwd_noalloc(const void* h, const void* dy, const void* dres,
+                                       const void* weight, void* dh, float* dweight, int64_t rows,
+                                       int64_t cols, float eps, fr_dtype_t dtype, void* stream) {
+  static_assert(FR_NOALLOC_SCRATCH_BYTES == fr::kNoallocScratchBytes, "scratch size");
+  if (fr_status_t s = check_shape(rows, cols)) return s;
+  if (cols > FR_BWD_MAX_COLS) return FR_E_SHAPE;
+  if (!dtype_ok(dtype)) return FR_E_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return FR_E_VALUE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dweight) return FR_E_NULL;
+  if (!aligned(dweight, 4)) return FR_E_ALIGN;
+  if (rows == 0) return launch_status(fr::launch_colsum(nullptr, 0, (int)cols, dweight, nullptr, st));
+  if (!h || !dy || !weight || !dh) return FR_E_NULL;
+  const int es = esize(dtype);
+  if (!aligned(h, es) || !aligned(dy, es) || !aligned(weight, es) || !aligned(dh, es) ||
+      (dres && !aligned(dres, es)))
+    return FR_E_ALIGN;
+  const int64_t nb = rows * cols * es;
+  const Buf bufs[] = {make_buf(h, nb, true, es, false),
+                      make_buf(dy, nb, true, es, false),
+                      make_buf(dres, nb, true, es, false),
+                      make_buf(weight, cols * es, false, es, false),
+                      make_buf(dh, nb, true, es, true),
+                      make_buf(dweight, cols * 4, false, 4, true)};
+  if (fr_status_t s = check_alias(bufs, 6)) return s;
+  const bool vec = aligned(h, 16) && aligned(dy, 16) && (!dres || aligned(dres, 16)) &&
+                   aligned(weight, 16) && aligned(dh, 16) && (cols * es) % 16 == 0;
+  const fr::RmsNormBwdVariant* v = select_variant(fr::rmsnorm_bwd_variants(dtype == FR_BF16),
+                                                  FR_OP_RMSNORM_BWD, cols, vec ? vec_epv(es) : 1);
+  if (!v) return g_forced[FR_OP_RMSNORM_BWD].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  // the partial rows must fit the library's array (checked before any HIP call)
+  if ((int64_t)fr::bwd_grid(*v, rows) * cols * 4 > fr::kNoallocScratchBytes) return FR_E_SHAPE;
+  return launch_status(fr::launch_rmsnorm_bwd_noalloc(v, h, dy, dres, weight, dh, dweight, rows,
+                                                      (int)cols, eps, st));
+}
+
 int64_t fr_norm_bwd_split_workspace_bytes(fr_op_t op, int64_t rows, int64_t cols) {
   if (op != FR_OP_RMSNORM_BWD && op != FR_OP_LAYERNORM_BWD) return -1;
   if (rows < 0 || cols < 1 || cols > FR_SPLIT_MAX_COLS || rows > INT64_MAX / 8 / cols) return -1;

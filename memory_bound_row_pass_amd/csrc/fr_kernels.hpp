@@ -165,6 +165,13 @@ hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* x
                                  void* workspace, int64_t rows, int cols, float eps,
                                  hipStream_t s);
 
+// Allocation-free RMSNorm backward (noalloc.hip): the partial rows go to a
+// library-held device array of kNoallocScratchBytes per GPU.
+constexpr int64_t kNoallocScratchBytes = int64_t(8) << 20;
+hipError_t launch_rmsnorm_bwd_noalloc(const RmsNormBwdVariant* v, const void* h, const void* dy,
+                                      const void* dres, const void* w, void* dh, float* dweight,
+                                      int64_t rows, int cols, float eps, hipStream_t s);
+
 // out0[c] (and out1[c] when out1 != NULL) = sum over b < partials of
 // ws[p][b][c], in order of b; partials == 0 writes zeros.
 hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, float* out1,

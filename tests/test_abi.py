@@ -165,6 +165,21 @@ def test_softmax_bwd_validation():
     assert f(P(A), P(D), P(X + 2), 4, 8, 0, None) == E_ALIGN
 
 
+def test_rmsnorm_bwd_noalloc_validation():
+    f = fr.lib.fr_add_rmsnorm_bwd_noalloc
+    D, W, DH, DW = A + 0x10000000, A + 0x20000000, A + 0x30000000, A + 0x40000000
+    assert f(P(A), P(D), None, P(W), P(DH), None, 4, 8, 1e-6, 1, None) == E_NULL  # dweight
+    assert f(P(A), P(D), None, P(W), P(DH), P(DW), 4, fr.FR_BWD_MAX_COLS + 1, 1e-6, 1,
+             None) == E_SHAPE
+    assert f(P(A), P(D), None, P(W), P(DH), P(DW), 4, 8, -1.0, 1, None) == E_VALUE
+    assert f(P(A), P(D), None, P(W), P(DH), P(DW), 4, 8, 1e-6, 5, None) == E_DTYPE
+    assert f(P(A), P(D), None, P(W), P(A + 2), P(DW), 4, 8, 1e-6, 1, None) == E_ALIAS
+    # partial rows beyond the library's array: 256 rows x 16384 columns x 4 B
+    assert f(P(A), P(D), None, P(W), P(DH), P(DW), 4096, 16384, 1e-6, 1, None) == E_SHAPE
+    assert fr.FR_NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert re.search(r"#define FR_NOALLOC_SCRATCH_BYTES \(8 << 20\)", open(HEADER).read())
+
+
 def test_norm_bwd_workspace_bytes():
     f = fr.fr_norm_bwd_workspace_bytes
     assert f(fr.OP_RMSNORM_BWD, 8192, 8192) == fr.FR_BWD_PARTIALS * 8192 * 4

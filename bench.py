@@ -16,7 +16,9 @@ on the stream the kernels run on. With --graph the timed steps replay one
 captured HIP graph of the five launches.
 
 Printed: ONE JSON line (rank 0), with per-workload figures, the roofline of
-the dominant kernel (the cross-entropy launch), the streaming-copy ceiling,
+the dominant kernel (the cross-entropy launch), the memory ceilings measured
+in the same run with the library's probes (the best read-only, write-only and
+copy patterns, and for each large workload the copy of its own row geometry),
 and the CPU oracle timed on the host cores as a baseline.
 
 The backward entry points are measured after the step, per call, at the
@@ -364,28 +366,77 @@ class Workload:
         self.variant = fr.fr_debug_select_variant_for(self.op, self.R, self.C, self.code)
 
 
-def copy_ceiling(torch, fr, dev, nbytes=2 << 30, reps=20):
-    """Read+write GB/s of the library's plain streaming copy over 2 GiB."""
-    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+# Memory ceilings, from the library's probes (fr_stream_probe: the row
+# kernels' access pattern with no arithmetic; a copy waits for a row's loads
+# before its stores, as a row kernel's reduction does). General patterns over
+# 2 GiB: the best read-only, write-only and copy (read + write) rates among
+# the shapes and cache policies swept on MI355X. (threads, vecs, policy):
+# policy 1 = non-temporal loads and cached stores, 3 = both non-temporal,
+# 0 = cached.
+GENERAL_PROBES = {
+    "copy": [(256, 1, 1), (256, 1, 3), (512, 1, 1), (64, 4, 3)],
+    "read": [(512, 2, 1), (256, 2, 1)],
+    "write": [(256, 1, 0), (512, 1, 0)],
+}
+# Each large workload's own row geometry and cache policy (non-temporal loads
+# and stores, as the kernels use): (threads, vecs, policy, row bytes, bytes
+# copied). The residual-add + RMSNorm row has two inputs and two outputs:
+# twice the rows of one 16 KiB operand. The cross-entropy row of 201,028 B is
+# probed at 201,040 B (whole 16-byte chunks).
+PATTERN_PROBES = {
+    "layernorm_f32": (64, 4, 3, 4096, 4096 * 4096),
+    "softmax_bf16": (128, 4, 3, 8192, 16384 * 8192),
+    "add_rmsnorm_bf16": (512, 2, 3, 16384, 2 * 8192 * 16384),
+    "xent_f32": (1024, 13, 3, 201040, 4096 * 201040),
+}
+
+
+def memory_ceilings(torch, np, fr, dev, K):
+    """GB/s of the general probe patterns (best of each kind) and of each
+    workload's same-geometry copy: median per-launch time over K rounds of all
+    probes in turn (each probe's buffers are cold, as the workloads' are)."""
+    nb = 2 << 30
+    src = torch.empty(nb // 4, dtype=torch.int32, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        fr.fr_stream_copy(src, dst)
+    sink = torch.empty(nb // 4096 + 16, dtype=torch.int32, device=dev)
+    runs, names, nbytes = [], [], []
+
+    def add(name, mode, t, v, pol, n, row_bytes=0):
+        runs.append(lambda: fr.fr_stream_probe(mode, src=src if mode != fr.PROBE_WRITE else None,
+                                               dst=dst if mode != fr.PROBE_READ else None,
+                                               nbytes=n, value=1,
+                                               sink=sink if mode == fr.PROBE_READ else None,
+                                               threads=t, vecs=v, policy=pol,
+                                               row_bytes=row_bytes))
+        names.append(name)
+        nbytes.append(2 * n if mode == fr.PROBE_COPY else n)
+
+    modes = {"copy": fr.PROBE_COPY, "read": fr.PROBE_READ, "write": fr.PROBE_WRITE}
+    for kind, shapes in GENERAL_PROBES.items():
+        for (t, v, pol) in shapes:
+            add(f"{kind} {t}x{v} policy {pol}", modes[kind], t, v, pol, nb)
+    for wl, (t, v, pol, rb, n) in PATTERN_PROBES.items():
+        add(f"pattern {wl}", fr.PROBE_COPY, t, v, pol, n, rb)
+    for r in runs:
+        r()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    for _ in range(reps):
-        fr.fr_stream_copy(src, dst)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / reps
-    del src, dst
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    us = time_calls(torch, np, runs, max(5, min(K, 20)))
+    rates = {n: b / (float(np.median(u)) * 1e-6) / 1e9 for n, u, b in zip(names, us, nbytes)}
+    del src, dst, sink
+    best = {}
+    for kind in GENERAL_PROBES:
+        name = max((n for n in rates if n.startswith(kind + " ")), key=rates.get)
+        best[kind] = {"gbps": round(rates[name], 1), "probe": name + " (2 GiB)"}
+    pattern = {wl: round(rates[f"pattern {wl}"], 1) for wl in PATTERN_PROBES}
+    return best, pattern, {n: round(r, 1) for n, r in rates.items()}
 
 
 def cpu_baseline(wls, budget_s=15.0):
     """The oracle (plain double-precision C, OpenMP over rows) on the host
-    cores over the same inputs: full steps, repeated while within budget.
-    Returns the baseline record and the last step's oracle outputs."""
+    cores over the same inputs: full steps, repeated while within budget;
+    then the two small workloads (softmax fp32 64x1000, LayerNorm fp32
+    4096x1024) again on one thread. Returns the baseline record and the last
+    step's oracle outputs."""
     import oracle
     oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
     threads = oracle.threads()
@@ -422,9 +473,28 @@ def cpu_baseline(wls, budget_s=15.0):
     per_workload = {}
     for w in wls:
         ms = sorted(per_ms[w.name])[len(per_ms[w.name]) // 2]
-        per_workload[w.name] = {"oracle_ms": round(ms, 2),
+        per_workload[w.name] = {"oracle_ms": round(ms, 2), "threads": threads,
                                 "gbps": round(w.bytes / (ms * 1e-3) / 1e9, 2),
                                 "rows_per_s": round(w.R / (ms * 1e-3), 1)}
+    # one thread, the small workloads: median of 3 runs
+    oracle.set_threads(1)
+    for w in wls:
+        if w.name not in ("softmax_f32", "layernorm_f32"):
+            continue
+        a, ts = w.w, []
+        for _ in range(3):
+            t1 = time.perf_counter()
+            if w.name == "softmax_f32":
+                oracle.softmax(a["x"])
+            else:
+                oracle.layernorm(a["x"], a["gamma"], a["beta"], a.eps)
+            ts.append((time.perf_counter() - t1) * 1e3)
+        ms = sorted(ts)[1]
+        per_workload[w.name]["one_thread"] = {
+            "oracle_ms": round(ms, 3), "threads": 1,
+            "gbps": round(w.bytes / (ms * 1e-3) / 1e9, 3),
+            "rows_per_s": round(w.R / (ms * 1e-3), 1)}
+    oracle.set_threads(threads)
     return ({"value": total_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
              "kind": "oracle",
              "sample": f"{n} full step(s): all rows of the five workloads, "
@@ -622,10 +692,15 @@ def main():
         attention = attention_stats(torch, np, fr, workloads, dev, K)
         log("attention timed")
 
-    ceiling = copy_ceiling(torch, fr, dev)
-    log(f"copy ceiling {ceiling:.0f} GB/s")
-    for v in per.values():
+    best, pattern, probes = memory_ceilings(torch, np, fr, dev, K)
+    ceiling = best["copy"]["gbps"]
+    log(f"memory ceilings: read {best['read']['gbps']:.0f}, write {best['write']['gbps']:.0f}, "
+        f"copy {ceiling:.0f} GB/s")
+    for name, v in per.items():
         v["pct_copy_ceiling"] = round(100 * v["gbps"] / ceiling, 1)
+        if name in pattern:
+            v["pattern_ceiling_gbps"] = pattern[name]
+            v["pct_pattern_ceiling"] = round(100 * v["gbps"] / pattern[name], 1)
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
               "compute_units": props.multi_processor_count,
@@ -655,6 +730,12 @@ def main():
             "rows_per_s": round(step_rows / (ms_per_step * 1e-3), 1),
             "pct_of_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             "copy_ceiling_gbps": round(ceiling, 1),
+            "read_ceiling_gbps": best["read"]["gbps"],
+            "write_ceiling_gbps": best["write"]["gbps"],
+            "ceilings": {"best": best, "probes_gbps": probes,
+                         "note": "fr_stream_probe rates; copy = best mixed read+write pattern; "
+                                 "per_workload pattern_ceiling_gbps = the copy of that "
+                                 "workload's own row geometry and cache policy"},
             "device": device,
             "storage": "fp32 and bf16 as listed; arithmetic fp32",
             "seeds": [w.w.seed for w in wls],

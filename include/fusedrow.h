@@ -427,12 +427,14 @@ FR_API const char* fr_version(void);
  * ceilings the row kernels' bandwidth is compared with, "Engineering a CUDA
  * Machine Learning Framework from Scratch", §2.1 The Memory Bandwidth
  * Bottleneck; also the known-size references for scaling hardware byte
- * counters). A workgroup of `threads` lanes owns a contiguous row of
+ * counters). A workgroup of `threads` lanes owns a contiguous row of up to
  * threads * vecs 16-byte chunks (lane t: chunks t, t + threads, ...; 64 lanes
- * = one row per wavefront, four per workgroup); a copy issues a row's loads
- * before its stores. The compiled shapes (threads, vecs) are 64 x {2, 4, 8,
- * 16}, 256 x {1, 2, 4, 8, 16}, 512 x {1, 2, 4, 8} and 1024 x {1, 2, 4, 8, 13,
- * 16}. The cache policy is a mask: FR_PROBE_NT_LOADS makes the loads
+ * = one row per wavefront, four per workgroup); rows follow each other
+ * without gaps. A copy issues all of a row's loads and waits for them (and
+ * for the workgroup barrier) before its first store, as a row kernel's
+ * stores wait for the row's reduction. The compiled shapes (threads, vecs) are 64 x {2, 4, 8,
+ * 16}, 128 x 4, 256 x {1, 2, 4, 8, 16}, 512 x {1, 2, 4, 8} and 1024 x {1, 2, 4,
+ * 8, 13, 16}. The cache policy is a mask: FR_PROBE_NT_LOADS makes the loads
  * non-temporal, FR_PROBE_NT_STORES the stores (else ordinary cached ones). */
 typedef enum { FR_PROBE_READ = 0, FR_PROBE_WRITE = 1, FR_PROBE_COPY = 2 } fr_probe_t;
 #define FR_PROBE_NT_LOADS 1
@@ -449,27 +451,31 @@ FR_API fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, voi
 
 /* Read `bytes` bytes of src (16-byte aligned, bytes a multiple of 16), in the
  * default shape and policy; each row's XOR of its 32-bit words goes to
- * sink[row] (fr_stream_probe_rows(bytes, FR_STREAM_THREADS, FR_STREAM_VECS)
- * words, 4-byte aligned, not overlapping src): the only writes. */
+ * sink[row] (fr_stream_probe_rows(bytes, FR_STREAM_THREADS * FR_STREAM_VECS
+ * * 16) words, 4-byte aligned, not overlapping src): the only writes. */
 FR_API fr_status_t fr_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
 /* Set every 32-bit word of dst (16-byte aligned, bytes a multiple of 16) to
  * `value`, in the default shape and policy; reads nothing. */
 FR_API fr_status_t fr_stream_write(void* dst, int64_t bytes, uint32_t value, void* stream);
 
-/* Rows of the probe shape (threads, vecs) over `bytes` bytes: the sink words a
- * read probe writes. -1 for a shape that is not compiled or bytes < 0. */
-FR_API int64_t fr_stream_probe_rows(int64_t bytes, int threads, int vecs);
+/* Rows of row_bytes over `bytes` bytes (the last one may be partial): the
+ * sink words a read probe writes. -1 for bytes < 0 or row_bytes not a
+ * positive multiple of 16. */
+FR_API int64_t fr_stream_probe_rows(int64_t bytes, int64_t row_bytes);
 
 /* Any probe in any compiled shape: FR_PROBE_READ reads src and writes sink,
  * FR_PROBE_WRITE writes `value` to every word of dst, FR_PROBE_COPY copies
- * src to dst (no overlap). policy: a mask of FR_PROBE_NT_LOADS and
- * FR_PROBE_NT_STORES (FR_E_VALUE otherwise). Pointers 16-byte aligned (sink
- * 4-byte), bytes a multiple of 16; unused pointers may be NULL. FR_E_VARIANT
- * for a shape that is not compiled. */
+ * src to dst (no overlap). row_bytes: the row each row owner handles, a
+ * multiple of 16 up to threads * vecs * 16 (0: exactly that; FR_E_SHAPE
+ * otherwise), so that a probe can take a workload's own row length.
+ * policy: a mask of FR_PROBE_NT_LOADS and FR_PROBE_NT_STORES (FR_E_VALUE
+ * otherwise). Pointers 16-byte aligned (sink 4-byte), bytes a multiple of
+ * 16; unused pointers may be NULL. FR_E_VARIANT for a shape that is not
+ * compiled. */
 FR_API fr_status_t fr_stream_probe(fr_probe_t kind, const void* src, void* dst, int64_t bytes,
-                                   uint32_t value, uint32_t* sink, int threads, int vecs,
-                                   int policy, void* stream);
+                                   int64_t row_bytes, uint32_t value, uint32_t* sink, int threads,
+                                   int vecs, int policy, void* stream);
 
 
 /* Force the kernel variant used by later calls of `op`: `threads` lanes per

@@ -93,7 +93,7 @@ def _load() -> ctypes.CDLL:
         "fr_stream_copy": [P, P, I64, P],
         "fr_stream_read": [P, I64, P, P],
         "fr_stream_write": [P, I64, ctypes.c_uint32, P],
-        "fr_stream_probe": [I32, P, P, I64, ctypes.c_uint32, P, I32, I32, I32, P],
+        "fr_stream_probe": [I32, P, P, I64, I64, ctypes.c_uint32, P, I32, I32, I32, P],
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
         "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
         "fr_softmax_fwd_split": [P, P, I64, I64, I32, I32, P, I64, P],
@@ -116,7 +116,7 @@ def _load() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    L.fr_stream_probe_rows.argtypes = [I64, I32, I32]
+    L.fr_stream_probe_rows.argtypes = [I64, I64]
     L.fr_stream_probe_rows.restype = ctypes.c_int64
     L.fr_split_workspace_bytes.argtypes = [I64, I64]
     L.fr_split_workspace_bytes.restype = ctypes.c_int64
@@ -556,31 +556,33 @@ PROBE_NT_LOADS, PROBE_NT_STORES = 1, 2
 STREAM_THREADS, STREAM_VECS, STREAM_POLICY = 256, 8, 3
 
 
-def fr_stream_probe_rows(nbytes: int, threads: int = STREAM_THREADS,
-                         vecs: int = STREAM_VECS) -> int:
-    """Rows of a probe shape over nbytes (the sink words of a read probe)."""
-    n = lib.fr_stream_probe_rows(int(nbytes), int(threads), int(vecs))
+def fr_stream_probe_rows(nbytes: int, row_bytes: int = STREAM_THREADS * STREAM_VECS * 16) -> int:
+    """Rows of row_bytes over nbytes (the sink words of a read probe)."""
+    n = lib.fr_stream_probe_rows(int(nbytes), int(row_bytes))
     if n < 0:
-        raise ValueError(f"no probe shape {threads} x {vecs}")
+        raise ValueError(f"bad probe row length {row_bytes}")
     return n
 
 
 def fr_stream_probe(kind: int, src=None, dst=None, nbytes: int | None = None, value: int = 0,
                     sink=None, threads: int = STREAM_THREADS, vecs: int = STREAM_VECS,
-                    policy: int = STREAM_POLICY, stream=None) -> None:
+                    policy: int = STREAM_POLICY, row_bytes: int = 0, stream=None) -> None:
     """Memory-system probe (C: fr_stream_probe): PROBE_READ reads src into the
     per-row XOR words of sink (uint32 viewed as int32), PROBE_WRITE fills dst
     with `value`, PROBE_COPY copies src to dst. policy: a mask of
-    PROBE_NT_LOADS and PROBE_NT_STORES."""
+    PROBE_NT_LOADS and PROBE_NT_STORES; row_bytes: the row length (0: the
+    shape's threads * vecs * 16)."""
     _need_cuda(src, dst, sink)
     ref = src if src is not None else dst
     n = ref.numel() * ref.element_size() if nbytes is None else int(nbytes)
     for t in (src, dst):
         if t is not None and n > t.numel() * t.element_size():
             raise ValueError("probe larger than a buffer")
-    if sink is not None and sink.numel() * sink.element_size() < 4 * fr_stream_probe_rows(n, threads, vecs):
+    rb = int(row_bytes) or threads * vecs * 16
+    if sink is not None and sink.numel() * sink.element_size() < 4 * fr_stream_probe_rows(n, rb):
         raise ValueError("sink smaller than one word per row")
-    _check(lib.fr_stream_probe(int(kind), _ptr(src), _ptr(dst), n, ctypes.c_uint32(value & 0xFFFFFFFF),
+    _check(lib.fr_stream_probe(int(kind), _ptr(src), _ptr(dst), n, int(row_bytes),
+                               ctypes.c_uint32(value & 0xFFFFFFFF),
                                _ptr(sink), int(threads), int(vecs), int(policy),
                                _stream(stream, ref)), "fr_stream_probe")
 

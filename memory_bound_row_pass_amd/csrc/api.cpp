@@ -921,44 +921,47 @@ fr_status_t fr_stream_copy(const void* src, void* dst, int64_t bytes, void* stre
   return launch_status(fr::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
 }
 
-int64_t fr_stream_probe_rows(int64_t bytes, int threads, int vecs) {
-  if (bytes < 0 || !fr::stream_probe_shape_exists(threads, vecs)) return -1;
-  return fr::stream_probe_rows(bytes, threads, vecs);
+int64_t fr_stream_probe_rows(int64_t bytes, int64_t row_bytes) {
+  if (bytes < 0 || row_bytes < 16 || row_bytes % 16 != 0) return -1;
+  return fr::stream_probe_rows(bytes, row_bytes);
 }
 
 fr_status_t fr_stream_probe(fr_probe_t kind, const void* src, void* dst, int64_t bytes,
-                            uint32_t value, uint32_t* sink, int threads, int vecs, int policy,
-                            void* stream) {
+                            int64_t row_bytes, uint32_t value, uint32_t* sink, int threads,
+                            int vecs, int policy, void* stream) {
   if (kind != FR_PROBE_READ && kind != FR_PROBE_WRITE && kind != FR_PROBE_COPY) return FR_E_VALUE;
   if (!fr::stream_probe_shape_exists(threads, vecs)) return FR_E_VARIANT;
   if (policy < 0 || policy > (FR_PROBE_NT_LOADS | FR_PROBE_NT_STORES)) return FR_E_VALUE;
   if (bytes < 0 || bytes % 16 != 0) return FR_E_SHAPE;
+  if (row_bytes == 0) row_bytes = (int64_t)threads * vecs * 16;
+  if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > (int64_t)threads * vecs * 16)
+    return FR_E_SHAPE;
   if (bytes == 0) return FR_OK;
   const bool reads = kind != FR_PROBE_WRITE, writes = kind != FR_PROBE_READ;
   if ((reads && !src) || (writes && !dst) || (kind == FR_PROBE_READ && !sink)) return FR_E_NULL;
   if ((reads && !aligned(src, 16)) || (writes && !aligned(dst, 16)) ||
       (kind == FR_PROBE_READ && !aligned(sink, 4)))
     return FR_E_ALIGN;
-  const int64_t rows = fr::stream_probe_rows(bytes, threads, vecs);
+  const int64_t rows = fr::stream_probe_rows(bytes, row_bytes);
   const Buf bufs[] = {make_buf(reads ? src : nullptr, bytes, false, 1, false),
                       make_buf(writes ? dst : nullptr, bytes, false, 1, true),
                       make_buf(kind == FR_PROBE_READ ? sink : nullptr, rows * 4, false, 4, true)};
   if (fr_status_t s = check_alias(bufs, 3)) return s;
   return launch_status(fr::launch_stream_probe((int)kind, reads ? src : nullptr,
-                                               writes ? dst : nullptr, bytes, threads, vecs,
-                                               policy, value,
+                                               writes ? dst : nullptr, bytes, row_bytes, threads,
+                                               vecs, policy, value,
                                                kind == FR_PROBE_READ ? sink : nullptr,
                                                static_cast<hipStream_t>(stream)));
 }
 
 fr_status_t fr_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
-  return fr_stream_probe(FR_PROBE_READ, src, nullptr, bytes, 0, sink, FR_STREAM_THREADS,
+  return fr_stream_probe(FR_PROBE_READ, src, nullptr, bytes, 0, 0, sink, FR_STREAM_THREADS,
                          FR_STREAM_VECS, FR_STREAM_POLICY, stream);
 }
 
 fr_status_t fr_stream_write(void* dst, int64_t bytes, uint32_t value, void* stream) {
-  return fr_stream_probe(FR_PROBE_WRITE, nullptr, dst, bytes, value, nullptr, FR_STREAM_THREADS,
-                         FR_STREAM_VECS, FR_STREAM_POLICY, stream);
+  return fr_stream_probe(FR_PROBE_WRITE, nullptr, dst, bytes, 0, value, nullptr,
+                         FR_STREAM_THREADS, FR_STREAM_VECS, FR_STREAM_POLICY, stream);
 }
 
 }  // extern "C"

@@ -109,7 +109,7 @@ void softmax_bwd_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int col
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int k = 0; k < EPV; ++k) a[i][k] = a[i][k] * (d[i][k] - s);
-    store_chunks<Ts, T, NV, EPV, false>(dx + off, g, tid, a);  // cached stores (st_stream)
+    store_chunks<Ts, T, NV, EPV>(dx + off, g, tid, a);
     if (ec >= 0) store1(dx + off + ec, ae * (de - s));
   }
 }
@@ -212,12 +212,11 @@ struct Slots {
   __device__ __forceinline__ void param(const Ts* par, int i, float* v) const {
     load_param<Ts, EPV>(par + off(i), v);
   }
-  // NTS: non-temporal stores (the kernel's store policy, see st_stream)
-  template <bool NTS, typename Ts>
+  template <typename Ts>
   __device__ __forceinline__ void store(Ts* r, const float (&v)[NV][EPV]) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (ok(i)) Vec<Ts, EPV>::template store<NTS>(r + off(i), v[i]);
+      if (ok(i)) Vec<Ts, EPV>::store(r + off(i), v[i]);
   }
 };
 
@@ -412,7 +411,7 @@ void rmsnorm_bwd_kernel(const Ts* h, const Ts* dy, const Ts* dres, const Ts* w, 
         }
       }
     }
-    if (live) sl.template store<false>(dh + off, hv);  // cached stores (st_stream)
+    if (live) sl.store(dh + off, hv);
     if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
   float* pbuf = STG ? reinterpret_cast<float*>(stage) : part;
@@ -568,7 +567,7 @@ void layernorm_bwd_kernel(const Ts* x, const Ts* dy, const Ts* gamma,
           n[i][k] = rs * __builtin_fmaf(-n[i][k], mgn, __builtin_fmaf(d[i][k], ga[k], -mg));
         }
       }
-      sl.template store<false>(dx + off, n);  // cached stores (st_stream)
+      sl.store(dx + off, n);
     }
     if constexpr (STG) stores_after = (staged && live && sl.nvec >= NV * T) ? NV : 0;
   }
@@ -744,7 +743,7 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
         }
       }
     }
-    sl.template store<true>(out + off, a);  // split pass: non-temporal (st_stream)
+    sl.store(out + off, a);
   }
   // this workgroup's partial row segment (slots past the segment end hold 0
   // and are not written)

@@ -6,12 +6,13 @@
 // bound by memory traffic, not arithmetic), and the known-size references
 // for scaling the hardware byte counters.
 //
-// Access pattern: a workgroup of T lanes owns a contiguous "row" of T * NV
-// 16-byte chunks; lane t holds chunks t, t + T, ..., so consecutive lanes
-// touch consecutive chunks (one wave instruction covers 1 KiB). A copy issues
-// all NV loads of the row before any of its stores, as a row kernel holds the
-// whole row in registers between its load and its store. T == 64 runs four
-// rows per 256-lane workgroup (one per wavefront), as the wave-per-row
+// Access pattern: a workgroup of T lanes owns a contiguous "row" of up to
+// T * NV 16-byte chunks (rows follow each other without gaps); lane t holds
+// chunks t, t + T, ..., so consecutive lanes touch consecutive chunks (one
+// wave instruction covers 1 KiB). A copy issues all loads of its row, waits
+// for all of them and for the workgroup barrier, then stores: the dependency
+// of a row kernel, whose stores need the whole row's reduction. T == 64 runs
+// four rows per 256-lane workgroup (one per wavefront), as the wave-per-row
 // kernels do. One workgroup per row group; the dispatcher hands them out.
 #include "fusedrow.h"
 
@@ -47,26 +48,28 @@ struct XorMerge {
 
 // MODE: 0 read (each row's XOR of its words goes to sink[row]), 1 write
 // (every 32-bit word set to `value`), 2 copy. n16: 16-byte chunks in the
-// buffer(s); the last row may be partial (its lanes past the end neither
-// load nor store). Every wave reaches the read mode's barriers.
+// buffer(s); rc: chunks per row (<= T * NV); the last row may be partial
+// (lanes past the end of the row or buffer neither load nor store). Every
+// wave reaches the barriers.
 // POL bit 0: non-temporal loads; bit 1: non-temporal stores (else ordinary
 // cached accesses).
 template <int MODE, int T, int NV, int POL>
 __global__ __launch_bounds__(T == 64 ? 256 : T) void stream_probe_kernel(
-    const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16, uint32_t value,
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16, int rc, uint32_t value,
     uint32_t* __restrict__ sink) {
   constexpr int RPB = T == 64 ? 4 : 1;
   const int sub = T == 64 ? (int)(threadIdx.x >> 6) : 0;
   const int tid = T == 64 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * RPB + sub;
-  const int64_t c0 = row * (T * NV);
-  const bool whole = c0 + T * NV <= n16;  // uniform in the row owner
+  const int64_t c0 = row * rc;
+  const int64_t end = c0 + rc < n16 ? c0 + rc : n16;  // the row's end (chunks)
+  const bool whole = rc == T * NV && c0 + T * NV <= n16;  // uniform in the row owner
   u32x4 v[NV];
   if constexpr (MODE != 1) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t c = c0 + i * T + tid;
-      v[i] = (whole || c < n16) ? probe_load<(POL & 1) != 0>(src + c) : u32x4{0, 0, 0, 0};
+      v[i] = (whole || c < end) ? probe_load<(POL & 1) != 0>(src + c) : u32x4{0, 0, 0, 0};
     }
   } else {
 #pragma unroll
@@ -84,10 +87,14 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) void stream_probe_kernel(
     __syncthreads();
     if (tid == 0 && c0 < n16) sink[row] = acc[sub];
   } else {
+    if constexpr (MODE == 2) {  // every load of the row has arrived, in every wave
+      if constexpr (T == 64) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t c = c0 + i * T + tid;
-      if (whole || c < n16) probe_store<(POL & 2) != 0>(v[i], dst + c);
+      if (whole || c < end) probe_store<(POL & 2) != 0>(v[i], dst + c);
     }
   }
 }
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(256) void byte_copy_kernel(const uint8_t* src, uint
 
 namespace {
 
-typedef void (*ProbeKernel)(const u32x4*, u32x4*, int64_t, uint32_t, uint32_t*);
+typedef void (*ProbeKernel)(const u32x4*, u32x4*, int64_t, int, uint32_t, uint32_t*);
 
 struct ProbeShape {
   int threads, vecs;
@@ -113,12 +120,13 @@ struct ProbeShape {
 #define FR_PROBE_SHAPE(T, NV) \
   {T, NV, {FR_PROBE_MODE(0, T, NV), FR_PROBE_MODE(1, T, NV), FR_PROBE_MODE(2, T, NV)}}
 
-// The shapes of the row kernels: 64 x 8 (wave per row, bf16 16384 x 4096),
+// The shapes of the row kernels: 64 x 8 and 128 x 4 (bf16 16384 x 4096),
 // 512 x 2 (add + RMSNorm 8192^2, per operand), 1024 x 13 (cross-entropy
 // 4096 x 50257), and neighbours.
 const ProbeShape kProbeShapes[] = {
     FR_PROBE_SHAPE(64, 2),    FR_PROBE_SHAPE(64, 4),    FR_PROBE_SHAPE(64, 8),
-    FR_PROBE_SHAPE(64, 16),   FR_PROBE_SHAPE(256, 1),   FR_PROBE_SHAPE(256, 2),
+    FR_PROBE_SHAPE(64, 16),   FR_PROBE_SHAPE(128, 4),   FR_PROBE_SHAPE(256, 1),
+    FR_PROBE_SHAPE(256, 2),
     FR_PROBE_SHAPE(256, 4),   FR_PROBE_SHAPE(256, 8),   FR_PROBE_SHAPE(256, 16),
     FR_PROBE_SHAPE(512, 1),   FR_PROBE_SHAPE(512, 2),   FR_PROBE_SHAPE(512, 4),
     FR_PROBE_SHAPE(512, 8),   FR_PROBE_SHAPE(1024, 1),  FR_PROBE_SHAPE(1024, 2),
@@ -135,29 +143,31 @@ const ProbeShape* find_shape(int threads, int vecs) {
 
 bool stream_probe_shape_exists(int threads, int vecs) { return find_shape(threads, vecs) != nullptr; }
 
-int64_t stream_probe_rows(int64_t bytes, int threads, int vecs) {
-  const int64_t per_row = (int64_t)threads * vecs * 16;
-  return (bytes + per_row - 1) / per_row;
+int64_t stream_probe_rows(int64_t bytes, int64_t row_bytes) {
+  return (bytes + row_bytes - 1) / row_bytes;
 }
 
-hipError_t launch_stream_probe(int mode, const void* src, void* dst, int64_t bytes, int threads,
-                               int vecs, int policy, uint32_t value, uint32_t* sink, hipStream_t s) {
+hipError_t launch_stream_probe(int mode, const void* src, void* dst, int64_t bytes,
+                               int64_t row_bytes, int threads, int vecs, int policy,
+                               uint32_t value, uint32_t* sink, hipStream_t s) {
   const ProbeShape* sh = find_shape(threads, vecs);
-  if (!sh || mode < 0 || mode > 2) return hipErrorInvalidValue;
-  const int64_t rows = stream_probe_rows(bytes, threads, vecs);
+  if (!sh || mode < 0 || mode > 2 || row_bytes < 16 || row_bytes % 16 != 0 ||
+      row_bytes > (int64_t)threads * vecs * 16)
+    return hipErrorInvalidValue;
+  const int64_t rows = stream_probe_rows(bytes, row_bytes);
   const int64_t rpb = threads == 64 ? 4 : 1;
   const int64_t blocks = (rows + rpb - 1) / rpb;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   return launch_kernel(sh->k[mode][policy & 3], dim3((unsigned)blocks),
                        dim3(threads == 64 ? 256 : threads), s, static_cast<const u32x4*>(src),
-                       static_cast<u32x4*>(dst), bytes / 16, value, sink);
+                       static_cast<u32x4*>(dst), bytes / 16, (int)(row_bytes / 16), value, sink);
 }
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
   if (a % 16 == 0 && b % 16 == 0 && bytes % 16 == 0)
-    return launch_stream_probe(2, src, dst, bytes, FR_STREAM_THREADS, FR_STREAM_VECS,
-                               FR_STREAM_POLICY, 0, nullptr, s);
+    return launch_stream_probe(2, src, dst, bytes, FR_STREAM_THREADS * FR_STREAM_VECS * 16,
+                               FR_STREAM_THREADS, FR_STREAM_VECS, FR_STREAM_POLICY, 0, nullptr, s);
   int64_t blocks = (bytes + 255) / 256;
   blocks = blocks < 4096 ? blocks : 4096;
   return launch_kernel(&byte_copy_kernel, dim3((unsigned)blocks), dim3(256), s,

@@ -85,13 +85,17 @@ __device__ __forceinline__ float exp_acc(float t) {
 // 6.9-7.3 TB/s with them against 6.0-6.7 TB/s with cached loads).
 // ld_stream<false> is an ordinary cached load, for data that is read again
 // soon (the first pass of a two-pass kernel).
-// Stores: the policy is the kernel's (st_stream<NT>). Measured per kernel on
-// MI355X: ordinary cached stores are faster for the softmax, LayerNorm,
-// bf16 RMSNorm and backward kernels (residual-add + RMSNorm bf16 8192^2
-// 89.5 -> 80.5 us, softmax bf16 16384 x 4096 46.8 -> 43.8 us), non-temporal
-// ones for the cross-entropy (fp32 4096 x 50257 311 -> 285 us), the split-row
-// passes (whose second read of a row batch comes from the cache that cached
-// stores would fill) and fp32 RMSNorm (183 -> 174 us at 8192^2).
+// Stores are non-temporal too, except where a kernel asks otherwise
+// (st_stream<false>). Measured on MI355X with cold buffers (rotating sets
+// of >= 1.5 GB, so that neither inputs nor outputs survive in the 256 MB
+// memory-side cache between uses, as in a real sequence of kernels): cached
+// stores were 2-9% slower for every row kernel and 8-24% slower for the
+// cross-entropy and the split-row passes; the one exception is a softmax
+// with bf16 input and fp32 output, whose lanes write their 32 bytes as two
+// 16-byte stores, so each store instruction covers every other 16 bytes of
+// its lines: cached stores let the cache merge the halves (112 -> 83 us at
+// 16384 x 4096). (Timed with the same buffers call after call, an output of
+// up to 256 MB stays dirty in that cache and cached stores look faster.)
 template <bool NT = true, typename V>
 __device__ __forceinline__ V ld_stream(const V* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);

@@ -178,13 +178,15 @@ hipError_t launch_colsum(const float* ws, int partials, int cols, float* out0, f
                          hipStream_t s);
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
-// Memory-system probes (copy.hip): mode 0 read, 1 write, 2 copy; a compiled
-// (threads, vecs) row shape; policy bit 0: non-temporal loads, bit 1:
+// Memory-system probes (copy.hip): mode 0 read, 1 write, 2 copy; rows of
+// row_bytes (a multiple of 16, at most threads * vecs * 16) on a compiled
+// (threads, vecs) shape; policy bit 0: non-temporal loads, bit 1:
 // non-temporal stores.
 bool stream_probe_shape_exists(int threads, int vecs);
-int64_t stream_probe_rows(int64_t bytes, int threads, int vecs);
-hipError_t launch_stream_probe(int mode, const void* src, void* dst, int64_t bytes, int threads,
-                               int vecs, int policy, uint32_t value, uint32_t* sink, hipStream_t s);
+int64_t stream_probe_rows(int64_t bytes, int64_t row_bytes);
+hipError_t launch_stream_probe(int mode, const void* src, void* dst, int64_t bytes,
+                               int64_t row_bytes, int threads, int vecs, int policy,
+                               uint32_t value, uint32_t* sink, hipStream_t s);
 
 // Attention forward, bf16, head dim D in {64, 128}; BH = batch * heads.
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -95,7 +95,7 @@ void layernorm_kernel(const Ts* x, const Ts* gamma, const Ts* beta, Ts* y, float
 #pragma unroll
         for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf((v[i][k] - mu) * rs, ga[k], be[k]);
       }
-      store_chunks<Ts, T, NV, EPV, false>(yr, g, tid, v);  // cached stores (st_stream)
+      store_chunks<Ts, T, NV, EPV>(yr, g, tid, v);
     }
     if (ec >= 0) store1(yr + ec, __builtin_fmaf((xe - mu) * rs, load1(gamma + ec), load1(beta + ec)));
     if (wave == 0 && lane == 0) {
@@ -112,7 +112,6 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
   constexpr int BLOCK = T == 64 ? 256 : T;
   constexpr int RPB = BLOCK / T;
   constexpr int NW = T / 64;
-  constexpr bool kNts = sizeof(Ts) == 4;  // store policy: non-temporal for fp32 (st_stream)
   __shared__ float xw[2][NW][1];
 
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -136,7 +135,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
 #pragma unroll
       for (int k = 0; k < EPV; ++k) h[i][k] += r[i][k];
     if (res_out) {  // updated residual, rounded once at the store
-      store_chunks<Ts, T, NV, EPV, kNts>(res_out + off, g, tid, h);
+      store_chunks<Ts, T, NV, EPV>(res_out + off, g, tid, h);
       if (ec >= 0) store1(res_out + off + ec, he);
     }
 
@@ -161,7 +160,7 @@ void add_rmsnorm_kernel(const Ts* x, const Ts* res, const Ts* w, Ts* y, Ts* res_
 #pragma unroll
         for (int k = 0; k < EPV; ++k) h[i][k] = h[i][k] * rs * wt[k];
       }
-      store_chunks<Ts, T, NV, EPV, kNts>(y + off, g, tid, h);
+      store_chunks<Ts, T, NV, EPV>(y + off, g, tid, h);
     }
     if (ec >= 0) store1(y + off + ec, he * rs * load1(w + ec));
   }

@@ -416,30 +416,34 @@ def test_stream_probe_validation():
     f = fr.lib.fr_stream_probe
     S = A + 0x100000
     READ, WRITE, COPY = fr.PROBE_READ, fr.PROBE_WRITE, fr.PROBE_COPY
-    assert f(READ, P(A), None, 0, 0, P(S), 256, 8, 1, None) == OK        # nothing to do
-    assert f(3, P(A), P(B), 16, 0, None, 256, 8, 1, None) == E_VALUE     # unknown probe
-    assert f(COPY, P(A), P(B), 16, 0, None, 256, 7, 1, None) == E_VARIANT  # no such shape
-    assert f(COPY, P(A), P(B), 16, 0, None, 256, 8, 4, None) == E_VALUE    # unknown policy bit
-    assert f(COPY, P(A), P(B), 24, 0, None, 256, 8, 1, None) == E_SHAPE  # not whole chunks
-    assert f(COPY, P(A), P(B), -16, 0, None, 256, 8, 1, None) == E_SHAPE
-    assert f(READ, P(A), None, 16, 0, None, 256, 8, 1, None) == E_NULL   # read needs a sink
-    assert f(WRITE, None, None, 16, 7, None, 256, 8, 1, None) == E_NULL
-    assert f(COPY, P(A + 4), P(B), 16, 0, None, 256, 8, 1, None) == E_ALIGN
-    assert f(READ, P(A), None, 16, 0, P(S + 2), 256, 8, 1, None) == E_ALIGN
-    assert f(COPY, P(A), P(A + 16), 32, 0, None, 256, 8, 1, None) == E_ALIAS
-    assert f(READ, P(A), None, 64, 0, P(A + 32), 64, 4, 1, None) == E_ALIAS  # sink in src
+    assert f(READ, P(A), None, 0, 0, 0, P(S), 256, 8, 1, None) == OK        # nothing to do
+    assert f(3, P(A), P(B), 16, 0, 0, None, 256, 8, 1, None) == E_VALUE     # unknown probe
+    assert f(COPY, P(A), P(B), 16, 0, 0, None, 256, 7, 1, None) == E_VARIANT  # no such shape
+    assert f(COPY, P(A), P(B), 16, 0, 0, None, 256, 8, 4, None) == E_VALUE    # unknown policy bit
+    assert f(COPY, P(A), P(B), 24, 0, 0, None, 256, 8, 1, None) == E_SHAPE  # not whole chunks
+    assert f(COPY, P(A), P(B), -16, 0, 0, None, 256, 8, 1, None) == E_SHAPE
+    assert f(COPY, P(A), P(B), 32, 24, 0, None, 256, 8, 1, None) == E_SHAPE  # row not chunks
+    assert f(COPY, P(A), P(B), 32, 256 * 8 * 16 + 16, 0, None, 256, 8, 1, None) == E_SHAPE
+    assert f(READ, P(A), None, 16, 0, 0, None, 256, 8, 1, None) == E_NULL   # read needs a sink
+    assert f(WRITE, None, None, 16, 0, 7, None, 256, 8, 1, None) == E_NULL
+    assert f(COPY, P(A + 4), P(B), 16, 0, 0, None, 256, 8, 1, None) == E_ALIGN
+    assert f(READ, P(A), None, 16, 0, 0, P(S + 2), 256, 8, 1, None) == E_ALIGN
+    assert f(COPY, P(A), P(A + 16), 32, 0, 0, None, 256, 8, 1, None) == E_ALIAS
+    assert f(READ, P(A), None, 64, 0, 0, P(A + 32), 64, 4, 1, None) == E_ALIAS  # sink in src
     assert fr.lib.fr_stream_read(P(A), 24, P(S), None) == E_SHAPE
     assert fr.lib.fr_stream_write(P(A + 8), 16, 1, None) == E_ALIGN
-    # rows of a shape: one sink word per row, partial last row included
-    assert fr.fr_stream_probe_rows(1 << 20, 256, 8) == 32
-    assert fr.fr_stream_probe_rows((1 << 20) + 16, 1024, 13) == (1 << 20) // (1024 * 13 * 16) + 1
-    assert fr.lib.fr_stream_probe_rows(16, 256, 7) == -1
+    # rows of a length: one sink word per row, partial last row included
+    assert fr.fr_stream_probe_rows(1 << 20) == 32
+    assert fr.fr_stream_probe_rows((1 << 20) + 16, 201040) == (1 << 20) // 201040 + 1
+    assert fr.lib.fr_stream_probe_rows(16, 24) == -1
 
 
 def test_variant_selection():
     # one wavefront per row for short rows, a workgroup per row for long ones
     assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (64, 4, 4)
-    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 4096, fr.BF16) == (64, 8, 8)
+    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 2048, fr.BF16) == (64, 4, 8)
+    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 4096, fr.BF16) == (128, 4, 8)
+    assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 4096, fr.F32) == (64, 16, 4)
     t, v, e = fr.fr_debug_select_variant(fr.OP_XENT, 50257, fr.F32)
     assert t * v * e >= 50257 and t >= 256
     t, v, e = fr.fr_debug_select_variant(fr.OP_SOFTMAX, 50257, fr.F32, vector_path=False)

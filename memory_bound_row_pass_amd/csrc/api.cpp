@@ -419,9 +419,10 @@ fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels, float*
   if (reduce && !loss_total) return FR_E_NULL;
   if (loss_total && !aligned(loss_total, 4)) return FR_E_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint32_t* count = o.reduction == FR_REDUCE_MEAN ? reinterpret_cast<uint32_t*>(loss_total) : nullptr;
+  const bool mean = o.reduction == FR_REDUCE_MEAN;
   if (rows == 0) {
     if (!reduce) return FR_OK;
+    uint32_t* count = mean ? reinterpret_cast<uint32_t*>(loss_total) : nullptr;
     if (count)
       if (fr_status_t s = launch_status(fr::launch_xent_count(labels, 0, 0, 0, count, st))) return s;
     return launch_status(fr::launch_xent_total(loss, 0, count, loss_total, st));
@@ -445,17 +446,23 @@ fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels, float*
   const fr::XentVariant* v =
       few_rows_variant(sp, FR_OP_XENT, rows, cols, epv, select_variant(sp, FR_OP_XENT, cols, epv));
   if (!v) return g_forced[FR_OP_XENT].threads.load() ? FR_E_VARIANT : FR_E_SHAPE;
+  // A mean needs the rows not ignored before any gradient is scaled: the row
+  // kernel's workgroups count them themselves over few rows, a count kernel
+  // writes them to loss_total first over many. The total itself is added up
+  // by the row kernel's last workgroup (a completion counter of the pool).
+  const bool count_inline = mean && rows <= fr::kXentInlineCountRows;
+  uint32_t* count = mean && !count_inline ? reinterpret_cast<uint32_t*>(loss_total) : nullptr;
+  uint32_t* done = nullptr;
+  if (reduce)
+    if (fr_status_t s = launch_status(fr::xent_done_counter(&done))) return s;
   if (count)
     if (fr_status_t s = launch_status(
             fr::launch_xent_count(labels, rows, o.use_ignore_index != 0, o.ignore_index, count, st)))
       return s;
   const fr::XentOptions ko = {o.use_ignore_index != 0, o.ignore_index, o.label_smoothing,
-                              o.grad_scale, count};
-  if (fr_status_t s = launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols,
-                                              &ko, st)))
-    return s;
-  if (!reduce) return FR_OK;
-  return launch_status(fr::launch_xent_total(loss, rows, count, loss_total, st));
+                              o.grad_scale, count, count_inline ? 1 : 0, (int)o.reduction, done,
+                              reduce ? loss_total : nullptr};
+  return launch_status(v->launch(logits, labels, loss, grad, argmax, rows, (int)cols, &ko, st));
 }
 
 fr_status_t fr_softmax_bwd(const void* p, const void* dy, void* dx, int64_t rows, int64_t cols,
@@ -787,7 +794,7 @@ fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, flo
             fr::launch_xent_count(labels, rows, o.use_ignore_index != 0, o.ignore_index, count, st)))
       return s;
   const fr::XentOptions ko = {o.use_ignore_index != 0, o.ignore_index, o.label_smoothing,
-                              o.grad_scale, count};
+                              o.grad_scale, count, 0, 0, nullptr, nullptr};
   if (fr_status_t s = launch_status(v->launch(logits, grad, rows, (int)cols, labels, loss, argmax,
                                               &ko, static_cast<float4*>(workspace), st)))
     return s;

@@ -625,6 +625,20 @@ struct Sum2Merge {
   }
 };
 
+// Exact unsigned integer sum (counts): the words travel as float bit
+// patterns through the DPP moves, unchanged, and are added as integers.
+struct CountState {
+  float b;
+  template <int C, int M>
+  static __device__ __forceinline__ CountState move(const CountState& a) { return {dpp_move<C, M>(a.b, 0.f)}; }
+  __device__ __forceinline__ CountState lane63() const { return {read_lane63(b)}; }
+};
+struct CountMerge {
+  __device__ __forceinline__ CountState operator()(const CountState& a, const CountState& b) const {
+    return {__uint_as_float(__float_as_uint(a.b) + __float_as_uint(b.b))};
+  }
+};
+
 // Softmax state: running max m and the sum s of exponentials taken relative
 // to m ("Online FlashSoftmax" recurrence). Empty state (-inf, 0).
 struct MaxSumState {

@@ -55,15 +55,32 @@ typedef hipError_t (*LayerNormLaunch)(const void* x, const void* gamma, const vo
                                       hipStream_t s);
 typedef hipError_t (*RmsNormLaunch)(const void* x, const void* res, const void* w, void* y,
                                     void* res_out, int64_t rows, int cols, float eps, hipStream_t s);
-// Cross-entropy options (kernel argument, by value). count: device pointer
-// to the number of rows not ignored (mean reduction), or NULL.
+// Cross-entropy options (kernel argument, by value).
+//   count: device pointer to the number of rows not ignored, counted by
+//          xent_count_kernel before the row pass (mean reduction), or NULL;
+//   count_inline: instead, every workgroup counts the rows not ignored itself
+//          (mean reduction over few enough rows, kXentInlineCountRows);
+//   reduction: 1 sum, 2 mean: the last workgroup to finish (completion
+//          counter `done`, zero on entry and left zero) adds the per-row
+//          losses in a fixed order and writes `total` (one-pass kernels;
+//          the split-row path keeps xent_total_kernel).
 struct XentOptions {
   int use_ignore;
   int ignore_index;
   float smoothing;
   float grad_scale;
   const uint32_t* count;
+  int count_inline;
+  int reduction;
+  uint32_t* done;
+  float* total;
 };
+// Rows up to which a mean's row count is taken inside the row kernel (each
+// workgroup reads all labels once: at most 32 KiB).
+constexpr int64_t kXentInlineCountRows = 8192;
+// A completion counter of the library's per-device pool (zero when idle;
+// successive calls take successive counters).
+hipError_t xent_done_counter(uint32_t** out);
 typedef hipError_t (*XentLaunch)(const void* logits, const int32_t* labels, float* loss, void* grad,
                                  int32_t* argmax, int64_t rows, int cols, const XentOptions* opt,
                                  hipStream_t s);

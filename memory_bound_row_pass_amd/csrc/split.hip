@@ -361,7 +361,7 @@ static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, c
                                hipStream_t s) {
   constexpr int SEG = T * NV * EPV;
   const int nseg = (cols + SEG - 1) / SEG;
-  const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
+  const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr, 0, 0, nullptr, nullptr};
   const int skip = XENT && o.use_ignore && !argmax;
   const int stats = XENT ? ((o.smoothing != 0.f ? 1 : 0) | (argmax ? 2 : 0)) : 0;
   auto k1 = stats == 0   ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 0>

@@ -23,10 +23,98 @@
 //            xent_count_kernel before the row pass).
 // Each lane stores g p_j - g eps / C with one fma; the label lane then
 // overwrites its element with g (p_label - (1 - eps) - eps / C).
+#include <atomic>
+#include <mutex>
+
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
 namespace fr {
+
+// Rows whose label is not the ignore index, counted by every thread of the
+// workgroup (labels tid, tid + BLOCK, ...), summed exactly per wavefront into
+// one LDS word per wave (`slots`, written once and kept for the kernel's
+// lifetime), then over the waves in order: the same value in every lane.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t sum_count_slots(const uint32_t* slots) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < BLOCK / 64; ++i) t += slots[i];
+  return t;
+}
+template <int BLOCK>
+__device__ __forceinline__ uint32_t count_valid_rows(const int32_t* labels, int64_t rows,
+                                                     const XentOptions& opt, uint32_t* slots) {
+  uint32_t c = 0;
+  for (int64_t r = threadIdx.x; r < rows; r += BLOCK)
+    c += (opt.use_ignore && labels[r] == opt.ignore_index) ? 0u : 1u;
+  const CountState w = wave_reduce(CountState{__uint_as_float(c)}, CountMerge{});
+  if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = __float_as_uint(w.b);
+  __syncthreads();
+  return sum_count_slots<BLOCK>(slots);
+}
+
+// The per-row losses of a call with a sum or mean reduction are written with
+// device-scope stores: written through to the level where all XCDs see them
+// (each XCD has its own L2), without the whole-L2 write-back and invalidate
+// of a device-scope fence, which measured 285 -> 3250 us when every
+// workgroup did it.
+__device__ __forceinline__ void store_loss(float* p, float v, bool device_scope) {
+  if (device_scope) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+// The loss total of a sum or mean reduction, in the same launch: every
+// workgroup, once its loss stores have completed (each wave waits for its
+// own), increments the completion counter; the workgroup that takes it to
+// gridDim.x (the last) reads loss[0 .. rows) with device-scope loads, adds
+// them in double in a fixed order — 1024 partial sums over rows v, v + 1024,
+// ..., then a halving tree — writes the sum (or the sum / n_valid) and sets
+// the counter back to zero for the next call. No workgroup waits for
+// another, and no float atomics: the total is bitwise reproducible and does
+// not depend on the kernel shape. (n_valid is taken again here, from the
+// count or the LDS count slots, so that it is not held in a register across
+// the row loop.)
+template <int BLOCK>
+__device__ __forceinline__ void finish_total(const float* loss, int64_t rows,
+                                             const XentOptions& opt, const uint32_t* count_slots,
+                                             double* red, int* last) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loss stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(opt.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!*last) return;  // uniform
+  for (int v = threadIdx.x; v < 1024; v += BLOCK) {
+    double a = 0.0;
+    for (int64_t r = v; r < rows; r += 1024)
+      a += (double)__hip_atomic_load(loss + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    red[v] = a;
+  }
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    for (int i = threadIdx.x; i < w; i += BLOCK) red[i] += red[i + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double t = red[0];
+    const uint32_t n_valid = opt.count ? *opt.count : sum_count_slots<BLOCK>(count_slots);
+    *opt.total = opt.reduction == 2 ? (float)(t / (double)n_valid) : (float)t;
+    __hip_atomic_store(opt.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// An uniform value the compiler cannot see through: computations from it in a
+// branch stay in the branch instead of being hoisted out of the row loop
+// (and kept live, or spilled, across it).
+__device__ __forceinline__ float opaque(float v) {
+  int b = __builtin_amdgcn_readfirstlane(__float_as_int(v));
+  asm volatile("" : "+s"(b));
+  return __int_as_float(b);
+}
 
 // A row state with the sum of the raw logits added (label smoothing).
 template <typename S>
@@ -94,20 +182,19 @@ void xent_kernel(const Tin* x,
   __shared__ float xw[2][NW][NF];
   static_assert(LPF == 0 || (RPB == 1 && LPF <= NV), "LDS staging: one row per block");
   __shared__ __attribute__((aligned(16))) uint32_t stage[LPF > 0 ? LPF * T * 4 : 4];
+  __shared__ uint32_t count_slots[OPT ? BLOCK / 64 : 1];
+  // the total's partial sums: the staging buffer once the rows are done, else
+  // an array of their own
+  __shared__ double red_own[OPT && LPF == 0 ? 1024 : 1];
+  double* const red = LPF > 0 ? reinterpret_cast<double*>(stage) : red_own;
+  static_assert(LPF == 0 || LPF * T * 4 * sizeof(uint32_t) >= 1024 * sizeof(double), "total");
+  __shared__ int last_wg;
 
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tid = T == 64 ? lane : (int)threadIdx.x;
   const int sub = T == 64 ? wib : 0;
   const int wave = T == 64 ? 0 : wib;
-
-  // gradient scale g and the smoothing offset g * eps / C (OPT only)
-  float gsc = 1.f, goff = 0.f;
-  if constexpr (OPT) {
-    gsc = opt.grad_scale;
-    if (opt.count) gsc = gsc / (float)(*opt.count);
-    goff = gsc * (opt.smoothing / (float)cols);
-  }
 
   // The next row's label is read one row ahead, so that the scalar load's
   // latency is not paid between rows (the ignore test needs the label before
@@ -144,6 +231,23 @@ void xent_kernel(const Tin* x,
     }
   }
 
+  // gradient scale g and the smoothing offset g * eps / C (OPT only); the
+  // rows not ignored are counted after the first row's copies are issued
+  // (staged kernels). Counting inside the row loop, after a one-row
+  // workgroup's loads, measured slower (fp32 4096 x 50257 mean 283 -> 324
+  // us: the count's state stayed live across the loop and spilled).
+  float gsc = 1.f, goff = 0.f;
+  if constexpr (OPT) {
+    gsc = opt.grad_scale;
+    if (opt.count) gsc = gsc / (float)(*opt.count);
+    else if (opt.count_inline) gsc = gsc / (float)count_valid_rows<BLOCK>(labels, rows, opt, count_slots);
+    goff = gsc * (opt.smoothing / (float)cols);
+    // uniform: held in scalar registers (as vector registers they were
+    // spilled and reloaded in every row)
+    gsc = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gsc)));
+    goff = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(goff)));
+  }
+
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
   for (int64_t row = first; row < rows; row += stride) {
     const Tin* xr = x + row * cols;
@@ -157,14 +261,17 @@ void xent_kernel(const Tin* x,
     const bool ignored = OPT && opt.use_ignore && label == opt.ignore_index;
     if constexpr (OPT && !ARGMAX) {
       if (ignored) {  // uniform in the row owner: no loads, a zero row
+        // (zeros from an opaque value: a zero vector hoisted out of the row
+        // loop was spilled and reloaded in every row)
+        const float zf = opaque(0.f);
         float z[NV][EPV];
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
-          for (int k = 0; k < EPV; ++k) z[i][k] = 0.f;
+          for (int k = 0; k < EPV; ++k) z[i][k] = zf;
         store_chunks<Tin, T, NV, EPV>(gr, g, tid, z);
-        if (ec >= 0) store1(gr + ec, 0.f);
-        if (tid == 0) loss[row] = 0.f;
+        if (ec >= 0) store1(gr + ec, zf);
+        if (tid == 0) store_loss(loss + row, 0.f, opt.reduction != 0);
         if constexpr (LPF > 0) {
           have_pre = rn < rows && !(opt.use_ignore && label_next == opt.ignore_index);
           if (have_pre) {
@@ -336,24 +443,66 @@ void xent_kernel(const Tin* x,
       const float lse = rs.m + logf(s_row);
       if constexpr (OPT) {
         // terms with a zero weight are left out (a -inf logit would make
-        // them 0 * inf); the same reading as the definition's weighted sum
-        const float eps = opt.smoothing;
-        store1(gr + label, gsc * ((p - (1.f - eps)) - eps / (float)cols));
+        // them 0 * inf); the same reading as the definition's weighted sum.
+        // The constants are formed here from opaque copies, so they are not
+        // hoisted out of the row loop and held (or spilled) across it.
+        const float eps = opaque(opt.smoothing);
+        const float fc = (float)cols;
+        store1(gr + label, opaque(gsc) * ((p - (1.f - eps)) - eps / fc));
         float l = lse;
         if (eps != 1.f) l -= (1.f - eps) * x_label;
-        if (eps != 0.f) l -= eps * (tsum / (float)cols);
-        loss[row] = l;
+        if (eps != 0.f) l -= eps * (tsum / fc);
+        store_loss(loss + row, l, opt.reduction != 0);
       } else {
         store1(gr + label, p - 1.f);
         loss[row] = lse - x_label;
       }
     } else if (tid == 0 && (ignored || !valid)) {
-      loss[row] = ignored ? 0.f : __builtin_nanf("");
+      store_loss(loss + row, ignored ? 0.f : __builtin_nanf(""), OPT && opt.reduction != 0);
     }
     if constexpr (ARGMAX) {
       if (tid == 0) argmax[row] = (int32_t)rs.idx;
     }
   }
+  if constexpr (OPT) {
+    if (opt.reduction) finish_total<BLOCK>(loss, rows, opt, count_slots, red, &last_wg);
+  }
+}
+
+// ------------------------------------------- completion counters (sum / mean)
+// A pool of counters per GPU, zero at load; every call that reduces over
+// rows takes the next one and its last workgroup sets it back to zero. Calls
+// in flight at the same time on one GPU (on different streams) take
+// different counters unless more than kXentDoneSlots of them overlap.
+constexpr int kXentDoneSlots = 256;
+static __device__ uint32_t xent_done[kXentDoneSlots];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_done_mu;
+uint32_t* g_done_ptr[kMaxDevices] = {};
+std::atomic<uint32_t> g_done_next{0};
+}  // namespace
+
+hipError_t xent_done_counter(uint32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t* base;
+  {
+    std::lock_guard<std::mutex> lock(g_done_mu);
+    if (!g_done_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(xent_done));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_done_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    base = g_done_ptr[dev];
+  }
+  *out = base + g_done_next.fetch_add(1, std::memory_order_relaxed) % kXentDoneSlots;
+  return hipSuccess;
 }
 
 // ------------------------------------------------- reductions over rows
@@ -421,7 +570,7 @@ static hipError_t launch_xent(const void* x, const int32_t* labels, float* loss,
     blocks = blocks < ncu ? blocks : ncu;
   }
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
-  const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr};
+  const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr, 0, 0, nullptr, nullptr};
   return launch_kernel(&xent_kernel<Tin, T, NV, EPV, OCC, ARGMAX, OPT, LPF>, dim3(grid), dim3(BLOCK), s,
                        static_cast<const Tin*>(x), labels, loss, static_cast<Tin*>(grad), argmax,
                        rows, cols, o);

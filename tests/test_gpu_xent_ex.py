@@ -384,3 +384,48 @@ def test_staged_bf16_plain_and_ignored_runs():
     for am in (False, True):
         expect(x, runs, fr.BF16, opts, run(x, runs, fr.BF16, opts, argmax=am),
                f"xent_ex bf16 ignored runs argmax={am}")
+
+
+# --------------------------------------------- totals in the row kernel
+
+@pytest.mark.parametrize("code", [fr.F32, fr.BF16])
+def test_mean_over_many_rows_counted_first(code):
+    """Past 8192 rows the rows not ignored are counted by a kernel of their
+    own before the row pass (below, every workgroup counts them itself); the
+    sum / mean is added up by the row kernel's last workgroup either way."""
+    for R in (8192, 8193, 20000):
+        x, lab = inputs(R, 300, code, seed=R, ignore_every=5)
+        for opts in (dict(ignore_index=-100, reduction="mean", label_smoothing=0.05),
+                     dict(ignore_index=-100, reduction="sum")):
+            print(f"many-row total {code} {R}x300 {opts['reduction']}", flush=True)
+            expect(x, lab, code, opts, run(x, lab, code, opts, argmax=False),
+                   f"xent_ex {code} {R}x300 {opts['reduction']}")
+
+
+def test_completion_counters_reused():
+    """More calls than the pool has completion counters (256), alternating
+    sum and mean and two row counts: every call's total matches its first
+    call's bitwise (each counter is back at zero when its call ends)."""
+    shapes = [(300, 1000, 21), (4100, 64, 22)]
+    data = []
+    for R, C, seed in shapes:
+        x, lab = inputs(R, C, fr.F32, seed=seed, ignore_every=4)
+        xt, lt = upload(x), upload(lab)
+        data.append((xt, lt, torch.empty(R, device=DEV), torch.empty_like(xt)))
+    tot = torch.empty(1, device=DEV)
+    first = {}
+    for i in range(300):
+        xt, lt, loss, grad = data[i % 2]
+        red = "mean" if (i // 2) % 2 else "sum"
+        fr.fr_softmax_xent_ex(xt, lt, loss, grad, None, tot, ignore_index=-100, reduction=red)
+        torch.cuda.synchronize()
+        key = (i % 2, red)
+        v = float(tot.cpu()[0])
+        if key not in first:
+            first[key] = v
+            x = data[i % 2][0].cpu().numpy()
+            lab = data[i % 2][1].cpu().numpy()
+            to = oracle.softmax_xent_ex(x, lab, ignore_index=-100, reduction=red)[3]
+            assert abs(v - to) <= 1e-5 * abs(to) + 1e-30, (key, v, to)
+        else:
+            assert v == first[key], (i, key, v, first[key])

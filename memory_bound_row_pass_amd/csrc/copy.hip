@@ -121,8 +121,8 @@ struct ProbeShape {
   {T, NV, {FR_PROBE_MODE(0, T, NV), FR_PROBE_MODE(1, T, NV), FR_PROBE_MODE(2, T, NV)}}
 
 // The shapes of the row kernels: 64 x 8 and 128 x 4 (bf16 16384 x 4096),
-// 512 x 2 (add + RMSNorm 8192^2, per operand), 1024 x 13 (cross-entropy
-// 4096 x 50257), and neighbours.
+// 512 x 2 (add + RMSNorm 8192^2, per operand), 1024 x 13 and 1024 x 7
+// (cross-entropy 4096 x 50257, fp32 and bf16), and neighbours.
 const ProbeShape kProbeShapes[] = {
     FR_PROBE_SHAPE(64, 2),    FR_PROBE_SHAPE(64, 4),    FR_PROBE_SHAPE(64, 8),
     FR_PROBE_SHAPE(64, 16),   FR_PROBE_SHAPE(128, 4),   FR_PROBE_SHAPE(256, 1),
@@ -130,8 +130,8 @@ const ProbeShape kProbeShapes[] = {
     FR_PROBE_SHAPE(256, 4),   FR_PROBE_SHAPE(256, 8),   FR_PROBE_SHAPE(256, 16),
     FR_PROBE_SHAPE(512, 1),   FR_PROBE_SHAPE(512, 2),   FR_PROBE_SHAPE(512, 4),
     FR_PROBE_SHAPE(512, 8),   FR_PROBE_SHAPE(1024, 1),  FR_PROBE_SHAPE(1024, 2),
-    FR_PROBE_SHAPE(1024, 4),  FR_PROBE_SHAPE(1024, 8),  FR_PROBE_SHAPE(1024, 13),
-    FR_PROBE_SHAPE(1024, 16)};
+    FR_PROBE_SHAPE(1024, 4),  FR_PROBE_SHAPE(1024, 7),  FR_PROBE_SHAPE(1024, 8),
+    FR_PROBE_SHAPE(1024, 13), FR_PROBE_SHAPE(1024, 16)};
 
 const ProbeShape* find_shape(int threads, int vecs) {
   for (const ProbeShape& s : kProbeShapes)

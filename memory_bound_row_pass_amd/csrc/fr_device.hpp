@@ -639,6 +639,43 @@ struct CountMerge {
   }
 };
 
+// Maximum over a wavefront (the DPP tree above with max): no exponential,
+// one move and one max per step. -inf is the identity; a NaN lane value is
+// passed over here and reaches the result through the exponential sums.
+struct MaxState {
+  float m;
+  template <int C, int M>
+  static __device__ __forceinline__ MaxState move(const MaxState& a) { return {dpp_move<C, M>(a.m, kNegInf)}; }
+  __device__ __forceinline__ MaxState lane63() const { return {read_lane63(m)}; }
+};
+struct MaxMerge {
+  __device__ __forceinline__ MaxState operator()(const MaxState& a, const MaxState& b) const {
+    return {__builtin_fmaxf(a.m, b.m)};
+  }
+};
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(MaxState{v}, MaxMerge{}).m; }
+
+// Two sums and a minimum over a wavefront, in one DPP tree: the row sums of a
+// softmax lane state taken relative to the wave's maximum (exponentials s,
+// logits t) and the smallest column holding that maximum (idx, a float;
+// empty 3e38). Fields a kernel does not read cost nothing (dead moves are
+// dropped).
+struct WaveSums {
+  float s, t, idx;
+  template <int C, int M>
+  static __device__ __forceinline__ WaveSums move(const WaveSums& a) {
+    return {dpp_move<C, M>(a.s, 0.f), dpp_move<C, M>(a.t, 0.f), dpp_move<C, M>(a.idx, 3.0e38f)};
+  }
+  __device__ __forceinline__ WaveSums lane63() const {
+    return {read_lane63(s), read_lane63(t), read_lane63(idx)};
+  }
+};
+struct WaveSumsMerge {
+  __device__ __forceinline__ WaveSums operator()(const WaveSums& a, const WaveSums& b) const {
+    return {a.s + b.s, a.t + b.t, __builtin_fminf(a.idx, b.idx)};
+  }
+};
+
 // Softmax state: running max m and the sum s of exponentials taken relative
 // to m ("Online FlashSoftmax" recurrence). Empty state (-inf, 0).
 struct MaxSumState {
@@ -766,6 +803,52 @@ __device__ __forceinline__ S block_merge(S wave_state, float (*slot)[sizeof(S) /
     acc = merge(acc, o);
   }
   return acc;
+}
+
+// Row-per-workgroup kernels, merged through a DPP tree: lane 0 of each wave
+// puts the wave's state in LDS, one barrier, then lane j < NW of every
+// 16-lane row loads wave j's state (the other lanes hold `empty`) and
+// log2(NW) DPP steps (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror) leave the merge of all NW states in lane 0: NW - 1 merges on
+// a fixed tree of depth log2(NW) instead of a chain of NW - 1. Every wave runs
+// the same steps on the same values, so all of them get bitwise the same
+// state; it is read from lane 0 into scalar registers. NW is a power of two
+// up to 16. The LDS slots follow block_merge's alternation rule.
+template <typename S>
+__device__ __forceinline__ S read_lane0(const S& v) {
+  constexpr int NF = sizeof(S) / sizeof(float);
+  S r;
+  const float* a = reinterpret_cast<const float*>(&v);
+  float* b = reinterpret_cast<float*>(&r);
+#pragma unroll
+  for (int k = 0; k < NF; ++k)
+    b[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[k]), 0));
+  return r;
+}
+
+template <int NW, typename S, typename Merge>
+__device__ __forceinline__ S block_merge_tree(S wave_state, float (*slot)[sizeof(S) / sizeof(float)],
+                                              int wave, int lane, Merge merge, const S& empty) {
+  static_assert(NW >= 2 && NW <= 16 && (NW & (NW - 1)) == 0, "2 to 16 waves, a power of two");
+  constexpr int NF = sizeof(S) / sizeof(float);
+  if (lane == 0) {
+    const float* f = reinterpret_cast<const float*>(&wave_state);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) slot[wave][k] = f[k];
+  }
+  lds_barrier();
+  const int j = lane & 15;
+  S acc = empty;
+  if (j < NW) {
+    float* f = reinterpret_cast<float*>(&acc);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) f[k] = slot[j][k];
+  }
+  acc = merge(acc, S::template move<0xB1, 0xF>(acc));                         // pairs
+  if constexpr (NW > 2) acc = merge(acc, S::template move<0x4E, 0xF>(acc));   // quads
+  if constexpr (NW > 4) acc = merge(acc, S::template move<0x141, 0xF>(acc));  // 8 lanes
+  if constexpr (NW > 8) acc = merge(acc, S::template move<0x140, 0xF>(acc));  // 16 lanes
+  return read_lane0(acc);
 }
 
 }  // namespace fr

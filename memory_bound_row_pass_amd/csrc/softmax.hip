@@ -46,11 +46,13 @@ __global__ __launch_bounds__(T == 64 ? 256 : T) __attribute__((amdgpu_waves_per_
     const int ec = g.extra_col(tid);
     float xe = ec >= 0 ? load1(xr + ec) : kNegInf;
 
-    const float m = lane_max<NV, EPV>(v, xe);
+    // the wave's maximum first: exponentials relative to it, plain sums
+    const float m = wave_max(lane_max<NV, EPV>(v, xe));
     MaxSumState st =
         kLog2 ? lane_exp_log2<NV, EPV>(v, xe, m) : lane_exp_nat<NV, EPV>(v, xe, m);
-    st = wave_reduce(st, Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, Merge{});
+    st.s = wave_reduce(SumState{st.s}, SumMerge{}).s;
+    if constexpr (NW > 1)
+      st = block_merge_tree<NW>(st, xw[merges++ & 1], wave, lane, Merge{}, MaxSumState{kNegInf, 0.f});
 
     if constexpr (kLog2) {
       const Log2Scale sc = log2_scale(m, st.m, st.s);

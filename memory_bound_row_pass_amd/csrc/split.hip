@@ -88,7 +88,8 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
     const int ec = g.extra_col(tid);
     float xe = load_extra(xs, ec, kNegInf);
 
-    const float m = lane_max<NV, EPV>(v, xe);
+    // the wave's maximum first: exponentials relative to it, plain sums
+    const float m = wave_max(lane_max<NV, EPV>(v, xe));
     float t = 0.f, best = 3.0e38f;
     if constexpr (WANT_T) {  // masked slots hold -inf and are skipped
       const bool full = g.nvec == T * NV;
@@ -105,7 +106,7 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
       t = t0 + t1;
     }
     if constexpr (WANT_IDX) {
-      // first slot holding the lane max: scan backwards keeping the last
+      // first slot holding the wave's max: scan backwards keeping the last
       // match; slot order is column order within a lane
       int c = -1;
 #pragma unroll
@@ -130,9 +131,11 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
         if (k & 1) s1 += e; else s0 += e;
       }
     const float se = exp2_hw((xe - mr) * kLog2e);
-    SplitState st{m, (s0 + s1) + se, t, best};
-    st = wave_reduce(st, SplitMerge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, SplitMerge{});
+    const WaveSums ws = wave_reduce(WaveSums{(s0 + s1) + se, t, best}, WaveSumsMerge{});
+    SplitState st{m, ws.s, ws.t, ws.idx};
+    if constexpr (NW > 1)
+      st = block_merge_tree<NW>(st, xw[merges++ & 1], wave, lane, SplitMerge{},
+                                SplitState{kNegInf, 0.f, 0.f, 3.0e38f});
     if (tid == 0) part[w] = float4{st.m, st.s, st.t, st.idx};
   }
 }
@@ -414,12 +417,13 @@ static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* 
 }
 
 #define FR_SP(TI, TO, T, NV, EPV, OCC, X) {T, NV, EPV, &launch_split<TI, TO, T, NV, EPV, OCC, X>}
-// Segment shapes, 32 elements per lane: 256 lanes (8192 columns, the
-// default: several workgroups per CU overlap one segment's loads with
-// another's arithmetic), 512 and 1024 lanes; the scalar path (unaligned
-// phases) 256 lanes x 32 elements.
+// Segment shapes: 256 lanes x 8 chunks (32 KiB segments, 8192 fp32 or 16384
+// bf16 columns, the default: several workgroups per CU overlap one segment's
+// loads with another's arithmetic; bf16 1024 x 262144 with 8 KiB-column
+// segments of 16 KiB measured 286 -> 270 us), 512 and 1024 lanes x 32
+// elements; the scalar path (unaligned phases) 256 lanes x 32 elements.
 #define FR_SP_TABLE(TI, TO, E, X)                                                           \
-  {FR_SP(TI, TO, 256, 32 / E, E, 4, X),  FR_SP(TI, TO, 512, 32 / E, E, 4, X),                 \
+  {FR_SP(TI, TO, 256, 8, E, 4, X),       FR_SP(TI, TO, 512, 32 / E, E, 4, X),                 \
    FR_SP(TI, TO, 1024, 32 / E, E, 4, X), FR_SP(TI, TO, 256, 32, 1, 4, X)}
 
 static const SplitVariant kSpF32F32[] = FR_SP_TABLE(float, float, 4, false);

@@ -334,7 +334,8 @@ void xent_kernel(const Tin* x,
       }
     }
 
-    const float m = lane_max<NV, EPV>(v, xe);
+    // the wave's maximum first: exponentials relative to it, plain sums
+    const float m = wave_max(lane_max<NV, EPV>(v, xe));
     Base bs;
     float tsum = 0.f;
     if constexpr (OPT) {
@@ -359,9 +360,9 @@ void xent_kernel(const Tin* x,
       }
       tsum = t0 + t1;
     }
+    float best = 3.0e38f;
     if constexpr (ARGMAX) {
-      // smallest column of this lane holding its maximum
-      float best = 3.0e38f;
+      // smallest column of this lane holding the wave's maximum
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -370,20 +371,30 @@ void xent_kernel(const Tin* x,
           best = (v[i][k] == m && col < best) ? col : best;
         }
       if (ec >= 0 && xe == m && (float)ec < best) best = (float)ec;
-      bs.idx = best;
     }
     {
-      // e_j replaces x_j
+      // e_j replaces x_j; the wave's sums and first column of its maximum
       const MaxSumState ms = LOG2 ? lane_exp_log2<NV, EPV>(v, xe, m)
                                   : lane_exp_nat<NV, EPV>(v, xe, m);
-      bs.m = ms.m;
-      bs.s = ms.s;
+      const WaveSums ws = wave_reduce(WaveSums{ms.s, tsum, best}, WaveSumsMerge{});
+      bs.m = m;
+      bs.s = ws.s;
+      if constexpr (ARGMAX) bs.idx = ws.idx;
+      tsum = ws.t;
     }
     State st;
     if constexpr (OPT) st = State{bs, tsum};
     else st = bs;
-    st = wave_reduce(st, Merge{});
-    if constexpr (NW > 1) st = block_merge<NW>(st, xw[merges++ & 1], wave, lane, Merge{});
+    if constexpr (NW > 1) {
+      Base eb;  // the empty state
+      eb.m = kNegInf;
+      eb.s = 0.f;
+      if constexpr (ARGMAX) eb.idx = 3.0e38f;
+      State empty;
+      if constexpr (OPT) empty = State{eb, 0.f};
+      else empty = eb;
+      st = block_merge_tree<NW>(st, xw[merges++ & 1], wave, lane, Merge{}, empty);
+    }
     Base rs;
     if constexpr (OPT) {
       rs = st.st;

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SHAPES = [(64, 2), (64, 4), (64, 8), (64, 16), (128, 4), (256, 1), (256, 2), (256, 4), (256, 8),
           (256, 16), (512, 1), (512, 2), (512, 4), (512, 8), (1024, 1), (1024, 2), (1024, 4),
-          (1024, 8), (1024, 13), (1024, 16)]
+          (1024, 7), (1024, 8), (1024, 13), (1024, 16)]
 GUARD = 64            # int32 words on each side
 CANARY = 0x5A5A5A5A
 

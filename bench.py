@@ -381,13 +381,15 @@ GENERAL_PROBES = {
 # Each large workload's own row geometry and cache policy (non-temporal loads
 # and stores, as the kernels use): (threads, vecs, policy, row bytes, bytes
 # copied). The residual-add + RMSNorm row has two inputs and two outputs:
-# twice the rows of one 16 KiB operand. The cross-entropy row of 201,028 B is
-# probed at 201,040 B (whole 16-byte chunks).
+# twice the rows of one 16 KiB operand. The cross-entropy rows of 201,028 B
+# (fp32) and 100,514 B (bf16, the options variant) are probed at 201,040 B
+# and 100,512 B (whole 16-byte chunks).
 PATTERN_PROBES = {
     "layernorm_f32": (64, 4, 3, 4096, 4096 * 4096),
     "softmax_bf16": (128, 4, 3, 8192, 16384 * 8192),
     "add_rmsnorm_bf16": (512, 2, 3, 16384, 2 * 8192 * 16384),
     "xent_f32": (1024, 13, 3, 201040, 4096 * 201040),
+    "xent_ex_bf16": (1024, 7, 3, 100512, 4096 * 100512),
 }
 
 
@@ -696,7 +698,7 @@ def main():
     ceiling = best["copy"]["gbps"]
     log(f"memory ceilings: read {best['read']['gbps']:.0f}, write {best['write']['gbps']:.0f}, "
         f"copy {ceiling:.0f} GB/s")
-    for name, v in per.items():
+    for name, v in list(per.items()) + list((variants or {}).items()):
         v["pct_copy_ceiling"] = round(100 * v["gbps"] / ceiling, 1)
         if name in pattern:
             v["pattern_ceiling_gbps"] = pattern[name]

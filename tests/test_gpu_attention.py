@@ -131,27 +131,36 @@ def test_rising_scores_rescale_every_block():
 
 
 def test_bench_shape_sampled():
-    # the benchmarked shape (B=4 H=16 S=4096 D=128): sampled queries of two
-    # heads against the oracle
+    # the benchmarked shape (B=4 H=16 S=4096 D=128), every one of the 64
+    # (batch, head) pairs (the head-to-XCD grouping deals them out in groups
+    # of 8): queries of the first, a middle and the last 128-query block —
+    # both ends of each block and one seeded query per block in another
+    # wave — against the oracle, causal and not
     w = workloads.make_attention(4, 16, 4096, 4096, 128)
     scale = float(np.float32(1.0 / np.sqrt(128)))
+    rng = np.random.default_rng(4096)
     for causal in (False, True):
         ob, lg = run(w, causal, scale)
         ob = ob.reshape(4, 16, 4096, 128)
-        rows = np.array([0, 31, 32, 127, 128, 2049, 4095])
-        for b, h in ((0, 0), (3, 15)):
-            sub = workloads.Workload(w.spec, 0, 0, 0, {"q": w["q"][b:b + 1, h:h + 1, rows],
-                                                       "k": w["k"][b:b + 1, h:h + 1],
-                                                       "v": w["v"][b:b + 1, h:h + 1]})
-            if causal:
-                # a sampled query i sees keys j <= i: compare query by query
-                for r_i, r in enumerate(rows):
-                    one = workloads.Workload(w.spec, 0, 0, 0, {
-                        "q": sub["q"][:, :, r_i:r_i + 1], "k": sub["k"][:, :, :r + 1],
-                        "v": sub["v"][:, :, :r + 1]})
-                    expect(one, False, scale, (ob[b:b + 1, h:h + 1, r:r + 1],
-                                               lg[b:b + 1, h:h + 1, r:r + 1]),
-                           f"attn bench shape causal b{b} h{h} q{r}")
-            else:
-                expect(sub, False, scale, (ob[b:b + 1, h:h + 1, rows], lg[b:b + 1, h:h + 1, rows]),
-                       f"attn bench shape b{b} h{h}")
+        for b in range(4):
+            for h in range(16):
+                rows = []
+                for blk in (0, 16, 31):
+                    q0 = 128 * blk
+                    rows += [q0, q0 + 127, q0 + 32 * int(rng.integers(1, 3)) + int(rng.integers(0, 32))]
+                rows = np.array(sorted(set(rows)))
+                sub = workloads.Workload(w.spec, 0, 0, 0, {"q": w["q"][b:b + 1, h:h + 1, rows],
+                                                           "k": w["k"][b:b + 1, h:h + 1],
+                                                           "v": w["v"][b:b + 1, h:h + 1]})
+                if causal:
+                    # a sampled query i sees keys j <= i: compare query by query
+                    for r_i, r in enumerate(rows):
+                        one = workloads.Workload(w.spec, 0, 0, 0, {
+                            "q": sub["q"][:, :, r_i:r_i + 1], "k": sub["k"][:, :, :r + 1],
+                            "v": sub["v"][:, :, :r + 1]})
+                        expect(one, False, scale, (ob[b:b + 1, h:h + 1, r:r + 1],
+                                                   lg[b:b + 1, h:h + 1, r:r + 1]),
+                               f"attn bench shape causal b{b} h{h} q{r}")
+                else:
+                    expect(sub, False, scale, (ob[b:b + 1, h:h + 1, rows], lg[b:b + 1, h:h + 1, rows]),
+                           f"attn bench shape b{b} h{h}")

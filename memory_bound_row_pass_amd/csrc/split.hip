@@ -61,10 +61,12 @@ struct Segment {
 // matter), unlike an output p_j. x - m is formed first: folding m into an fma
 // with log2e would put the rounding of m * log2e (|m| * 2^-24) into every
 // term.
-template <typename Tin, int T, int NV, int EPV, int OCC, int STATS>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
-void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
-                        const int32_t* labels, XentOptions opt, int skip_ignored, float4* part) {
+// The body: work items w0, w0 + wstride, ... of rows * nseg.
+template <typename Tin, int T, int NV, int EPV, int STATS>
+__device__ __forceinline__ void split_stats_body(const Tin* x, int64_t rows, int cols, int seg,
+                                                 int nseg, const int32_t* labels, XentOptions opt,
+                                                 int skip_ignored, float4* part, int64_t w0,
+                                                 int64_t wstride) {
   constexpr int NW = T / 64;
   constexpr bool WANT_T = STATS & 1;
   constexpr bool WANT_IDX = STATS & 2;
@@ -74,7 +76,7 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+  for (int64_t w = w0; w < work; w += wstride) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const Segment sgm(sg, seg, cols);
@@ -140,6 +142,14 @@ void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
   }
 }
 
+template <typename Tin, int T, int NV, int EPV, int OCC, int STATS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void split_stats_kernel(const Tin* x, int64_t rows, int cols, int seg, int nseg,
+                        const int32_t* labels, XentOptions opt, int skip_ignored, float4* part) {
+  split_stats_body<Tin, T, NV, EPV, STATS>(x, rows, cols, seg, nseg, labels, opt, skip_ignored, part,
+                                           blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------------------------------------ pass 2
 
 // The row's merged state: lane j merges partials j, j + T, ... in order, then
@@ -176,11 +186,13 @@ __device__ __forceinline__ float split_p(float xv, float M, float fac, float b) 
 }
 
 // XENT: y is the gradient (Tout == Tin); loss, argmax, labels and opt apply.
-template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
-void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, int nseg,
-                        const float4* part, const int32_t* labels, float* loss, int32_t* argmax,
-                        XentOptions opt) {
+// The body: work items w0, w0 + wstride, ... of rows * nseg.
+template <typename Tin, typename Tout, int T, int NV, int EPV, bool XENT>
+__device__ __forceinline__ void split_apply_body(const Tin* x, Tout* y, int64_t rows, int cols,
+                                                 int seg, int nseg, const float4* part,
+                                                 const int32_t* labels, float* loss,
+                                                 int32_t* argmax, XentOptions opt, int64_t w0,
+                                                 int64_t wstride) {
   constexpr int NW = T / 64;
   __shared__ float xw[2][NW][4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -196,7 +208,7 @@ void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, 
 
   const int64_t work = rows * nseg;
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+  for (int64_t w = w0; w < work; w += wstride) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const Segment sgm(sg, seg, cols);
@@ -279,15 +291,52 @@ void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, 
   }
 }
 
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void split_apply_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, int nseg,
+                        const float4* part, const int32_t* labels, float* loss, int32_t* argmax,
+                        XentOptions opt) {
+  split_apply_body<Tin, Tout, T, NV, EPV, XENT>(x, y, rows, cols, seg, nseg, part, labels, loss,
+                                                argmax, opt, blockIdx.x, gridDim.x);
+}
+
+// Pass 2 of one row batch and pass 1 of the next in one launch (they touch
+// different rows): workgroups [0, n_apply) take the first batch's segments,
+// the rest the next batch's.
+struct SplitBatch {
+  const void* x;
+  void* y;
+  int64_t rows;
+  float4* part;
+  const int32_t* labels;
+  float* loss;
+  int32_t* argmax;
+};
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT, int STATS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void split_apply_stats_kernel(SplitBatch a, SplitBatch n, int cols, int seg, int nseg,
+                              XentOptions opt, int skip_ignored, unsigned n_apply) {
+  if (blockIdx.x < n_apply)
+    split_apply_body<Tin, Tout, T, NV, EPV, XENT>(
+        static_cast<const Tin*>(a.x), static_cast<Tout*>(a.y), a.rows, cols, seg, nseg, a.part,
+        a.labels, a.loss, a.argmax, opt, blockIdx.x, n_apply);
+  else
+    split_stats_body<Tin, T, NV, EPV, STATS>(static_cast<const Tin*>(n.x), n.rows, cols, seg, nseg,
+                                             n.labels, opt, skip_ignored, n.part, blockIdx.x - n_apply,
+                                             gridDim.x - n_apply);
+}
+
 // ------------------------------------------------ softmax backward, split
 // dx = p (dy - s), s = sum_j p_j dy_j: pass 1 writes each segment's sum of
 // p * dy, pass 2 adds the row's segment sums in segment order (the same bits
 // in every workgroup of the row), re-reads p and dy and writes dx.
 
-template <typename Ts, int T, int NV, int EPV, int OCC>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
-void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int cols, int seg,
-                                    int nseg, float4* part) {
+// (the bodies: work items w0, w0 + wstride, ... of rows * nseg)
+template <typename Ts, int T, int NV, int EPV>
+__device__ __forceinline__ void softmax_bwd_split_stats_body(const Ts* p, const Ts* dy, int64_t rows,
+                                                             int cols, int seg, int nseg,
+                                                             float4* part, int64_t w0,
+                                                             int64_t wstride) {
   constexpr int NW = T / 64;
   __shared__ float xw[2][NW][1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -295,7 +344,7 @@ void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+  for (int64_t w = w0; w < work; w += wstride) {
     const int64_t row = w / nseg;
     const Segment sgm((int)(w - row * nseg), seg, cols);
     const int64_t off = row * cols + sgm.c0;
@@ -318,10 +367,11 @@ void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int
   }
 }
 
-template <typename Ts, int T, int NV, int EPV, int OCC>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
-void softmax_bwd_split_apply_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int cols,
-                                    int seg, int nseg, const float4* part) {
+template <typename Ts, int T, int NV, int EPV>
+__device__ __forceinline__ void softmax_bwd_split_apply_body(const Ts* p, const Ts* dy, Ts* dx,
+                                                             int64_t rows, int cols, int seg,
+                                                             int nseg, const float4* part,
+                                                             int64_t w0, int64_t wstride) {
   constexpr int NW = T / 64;
   __shared__ float xw[2][NW][1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -329,7 +379,7 @@ void softmax_bwd_split_apply_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t r
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+  for (int64_t w = w0; w < work; w += wstride) {
     const int64_t row = w / nseg;
     const Segment sgm((int)(w - row * nseg), seg, cols);
     SumState st{0.f};
@@ -352,6 +402,37 @@ void softmax_bwd_split_apply_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t r
   }
 }
 
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_split_stats_kernel(const Ts* p, const Ts* dy, int64_t rows, int cols, int seg,
+                                    int nseg, float4* part) {
+  softmax_bwd_split_stats_body<Ts, T, NV, EPV>(p, dy, rows, cols, seg, nseg, part, blockIdx.x,
+                                               gridDim.x);
+}
+
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_split_apply_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int cols,
+                                    int seg, int nseg, const float4* part) {
+  softmax_bwd_split_apply_body<Ts, T, NV, EPV>(p, dy, dx, rows, cols, seg, nseg, part, blockIdx.x,
+                                               gridDim.x);
+}
+
+// Pass 2 of one row batch (rows ra at offset ea) and pass 1 of the next (rows
+// rn at en) in one launch, as split_apply_stats_kernel.
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_split_apply_stats_kernel(const Ts* p, const Ts* dy, Ts* dx, int cols, int seg,
+                                          int nseg, int64_t ea, int64_t ra, const float4* pa,
+                                          int64_t en, int64_t rn, float4* pn, unsigned n_apply) {
+  if (blockIdx.x < n_apply)
+    softmax_bwd_split_apply_body<Ts, T, NV, EPV>(p + ea, dy + ea, dx + ea, ra, cols, seg, nseg, pa,
+                                                 blockIdx.x, n_apply);
+  else
+    softmax_bwd_split_stats_body<Ts, T, NV, EPV>(p + en, dy + en, rn, cols, seg, nseg, pn,
+                                                 blockIdx.x - n_apply, gridDim.x - n_apply);
+}
+
 // --------------------------------------------------------------- launchers
 
 static unsigned split_grid(int64_t work) {
@@ -371,24 +452,36 @@ static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, c
             : stats == 1 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 1>
             : stats == 2 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 2>
                          : &split_stats_kernel<Tin, T, NV, EPV, OCC, 3>;
+  auto kf = !XENT || stats == 0 ? &split_apply_stats_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, 0>
+            : stats == 1 ? &split_apply_stats_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, XENT ? 1 : 0>
+            : stats == 2 ? &split_apply_stats_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, XENT ? 2 : 0>
+                         : &split_apply_stats_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, XENT ? 3 : 0>;
   const Tin* xi = static_cast<const Tin*>(x);
   Tout* yo = static_cast<Tout*>(y);
   const int64_t batch = split_batch_rows(rows, (int64_t)cols * sizeof(Tin));
-  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+  auto view = [&](int64_t r0) {
     const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
-    const unsigned grid = split_grid(nr * nseg);
-    const int64_t e0 = r0 * cols;
-    const int32_t* lb = labels ? labels + r0 : nullptr;
-    hipError_t e = launch_kernel(k1, dim3(grid), dim3(T), s, xi + e0, nr, cols, SEG, nseg, lb, o,
-                                 skip, part + r0 * nseg);
+    return SplitBatch{xi + r0 * cols, yo + r0 * cols, nr, part + r0 * nseg,
+                      labels ? labels + r0 : nullptr, loss ? loss + r0 : nullptr,
+                      argmax ? argmax + r0 : nullptr};
+  };
+  // pass 1 of the first batch; then, per further batch, pass 2 of the one
+  // before and pass 1 of this one in one launch; then pass 2 of the last
+  SplitBatch cur = view(0);
+  hipError_t e = launch_kernel(k1, dim3(split_grid(cur.rows * nseg)), dim3(T), s, xi, cur.rows, cols,
+                               SEG, nseg, cur.labels, o, skip, cur.part);
+  if (e != hipSuccess) return e;
+  for (int64_t r0 = batch; r0 < rows; r0 += batch) {
+    const SplitBatch nxt = view(r0);
+    const unsigned na = split_grid(cur.rows * nseg), ns = split_grid(nxt.rows * nseg);
+    e = launch_kernel(kf, dim3(na + ns), dim3(T), s, cur, nxt, cols, SEG, nseg, o, skip, na);
     if (e != hipSuccess) return e;
-    e = launch_kernel(&split_apply_kernel<Tin, Tout, T, NV, EPV, OCC, XENT>, dim3(grid), dim3(T), s,
-                      xi + e0, yo + e0, nr, cols, SEG, nseg,
-                      static_cast<const float4*>(part + r0 * nseg), lb, loss ? loss + r0 : nullptr,
-                      argmax ? argmax + r0 : nullptr, o);
-    if (e != hipSuccess) return e;
+    cur = nxt;
   }
-  return hipSuccess;
+  return launch_kernel(&split_apply_kernel<Tin, Tout, T, NV, EPV, OCC, XENT>,
+                       dim3(split_grid(cur.rows * nseg)), dim3(T), s,
+                       static_cast<const Tin*>(cur.x), static_cast<Tout*>(cur.y), cur.rows, cols, SEG,
+                       nseg, static_cast<const float4*>(cur.part), cur.labels, cur.loss, cur.argmax, o);
 }
 
 template <typename Ts, int T, int NV, int EPV, int OCC>
@@ -400,20 +493,28 @@ static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* 
   const Ts* di = static_cast<const Ts*>(dy);
   Ts* xo = static_cast<Ts*>(dx);
   const int64_t batch = split_batch_rows(rows, (int64_t)cols * 2 * sizeof(Ts));
-  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
-    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
-    const unsigned grid = split_grid(nr * nseg);
-    const int64_t e0 = r0 * cols;
-    hipError_t e = launch_kernel(&softmax_bwd_split_stats_kernel<Ts, T, NV, EPV, OCC>, dim3(grid),
-                                 dim3(T), s, pi + e0, di + e0, nr, cols, SEG, nseg,
-                                 part + r0 * nseg);
+  // pass 1 of the first batch; per further batch, pass 2 of the one before
+  // with pass 1 of this one; then pass 2 of the last
+  int64_t r0 = 0, nr = rows < batch ? rows : batch;
+  hipError_t e = launch_kernel(&softmax_bwd_split_stats_kernel<Ts, T, NV, EPV, OCC>,
+                               dim3(split_grid(nr * nseg)), dim3(T), s, pi, di, nr, cols, SEG, nseg,
+                               part);
+  if (e != hipSuccess) return e;
+  for (int64_t r1 = batch; r1 < rows; r1 += batch) {
+    const int64_t n1 = rows - r1 < batch ? rows - r1 : batch;
+    const unsigned na = split_grid(nr * nseg), ns = split_grid(n1 * nseg);
+    e = launch_kernel(&softmax_bwd_split_apply_stats_kernel<Ts, T, NV, EPV, OCC>, dim3(na + ns),
+                      dim3(T), s, pi, di, xo, cols, SEG, nseg, r0 * cols, nr,
+                      static_cast<const float4*>(part + r0 * nseg), r1 * cols, n1, part + r1 * nseg,
+                      na);
     if (e != hipSuccess) return e;
-    e = launch_kernel(&softmax_bwd_split_apply_kernel<Ts, T, NV, EPV, OCC>, dim3(grid), dim3(T), s,
-                      pi + e0, di + e0, xo + e0, nr, cols, SEG, nseg,
-                      static_cast<const float4*>(part + r0 * nseg));
-    if (e != hipSuccess) return e;
+    r0 = r1;
+    nr = n1;
   }
-  return hipSuccess;
+  return launch_kernel(&softmax_bwd_split_apply_kernel<Ts, T, NV, EPV, OCC>,
+                       dim3(split_grid(nr * nseg)), dim3(T), s, pi + r0 * cols, di + r0 * cols,
+                       xo + r0 * cols, nr, cols, SEG, nseg,
+                       static_cast<const float4*>(part + r0 * nseg));
 }
 
 #define FR_SP(TI, TO, T, NV, EPV, OCC, X) {T, NV, EPV, &launch_split<TI, TO, T, NV, EPV, OCC, X>}

@@ -72,10 +72,11 @@ __device__ __forceinline__ WelfordState lane_moments(const float (&v)[NV][EPV], 
 
 // ------------------------------------------------------------------ pass 1
 
-template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
-void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols, int seg,
-                             int nseg, float4* part) {
+// (the bodies: work items w0, w0 + wstride, ... of rows * nseg)
+template <typename Ts, int T, int NV, int EPV, bool RMS>
+__device__ __forceinline__ void norm_split_stats_body(const Ts* x, const Ts* res, int64_t rows,
+                                                      int cols, int seg, int nseg, float4* part,
+                                                      int64_t w0, int64_t wstride) {
   constexpr int NW = T / 64;
   __shared__ float xw[2][NW][RMS ? 1 : 3];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -83,7 +84,7 @@ void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols,
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+  for (int64_t w = w0; w < work; w += wstride) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const NormSegment sgm(sg, seg, cols);
@@ -136,11 +137,12 @@ __device__ __forceinline__ S merge_partials(const float4* part, int64_t row, int
 
 // LayerNorm: p1 = gamma, p2 = beta, res / res_out unused. RMSNorm: p1 = the
 // weight, p2 / mean / rstd unused.
-template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
-void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts* p2, Ts* y,
-                             Ts* res_out, float* mean, float* rstd, int64_t rows, int cols,
-                             int seg, int nseg, const float4* part, float eps) {
+template <typename Ts, int T, int NV, int EPV, bool RMS>
+__device__ __forceinline__ void norm_split_apply_body(const Ts* x, const Ts* res, const Ts* p1,
+                                                      const Ts* p2, Ts* y, Ts* res_out, float* mean,
+                                                      float* rstd, int64_t rows, int cols, int seg,
+                                                      int nseg, const float4* part, float eps,
+                                                      int64_t w0, int64_t wstride) {
   constexpr int NW = T / 64;
   __shared__ float xw[2][NW][RMS ? 1 : 3];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,7 +150,7 @@ void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts*
   const int tid = threadIdx.x;
   const int64_t work = rows * nseg;
   int merges = 0;  // cross-wave merges so far: picks the LDS slot
-  for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+  for (int64_t w = w0; w < work; w += wstride) {
     const int64_t row = w / nseg;
     const int sg = (int)(w - row * nseg);
     const NormSegment sgm(sg, seg, cols);
@@ -214,6 +216,46 @@ void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts*
   }
 }
 
+template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void norm_split_stats_kernel(const Ts* x, const Ts* res, int64_t rows, int cols, int seg,
+                             int nseg, float4* part) {
+  norm_split_stats_body<Ts, T, NV, EPV, RMS>(x, res, rows, cols, seg, nseg, part, blockIdx.x,
+                                             gridDim.x);
+}
+
+template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void norm_split_apply_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts* p2, Ts* y,
+                             Ts* res_out, float* mean, float* rstd, int64_t rows, int cols,
+                             int seg, int nseg, const float4* part, float eps) {
+  norm_split_apply_body<Ts, T, NV, EPV, RMS>(x, res, p1, p2, y, res_out, mean, rstd, rows, cols,
+                                             seg, nseg, part, eps, blockIdx.x, gridDim.x);
+}
+
+// Pass 2 of one row batch (rows ra from row r_a) and pass 1 of the next (rows
+// rn from row r_n) in one launch: they touch different rows; workgroups
+// [0, n_apply) take the first batch's segments, the rest the next batch's.
+template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void norm_split_apply_stats_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts* p2, Ts* y,
+                                   Ts* res_out, float* mean, float* rstd, int cols, int seg,
+                                   int nseg, float4* part, float eps, int64_t r_a, int64_t ra,
+                                   int64_t r_n, int64_t rn, unsigned n_apply) {
+  if (blockIdx.x < n_apply) {
+    const int64_t e0 = r_a * cols;
+    norm_split_apply_body<Ts, T, NV, EPV, RMS>(
+        x + e0, res ? res + e0 : nullptr, p1, p2, y + e0, res_out ? res_out + e0 : nullptr,
+        mean ? mean + r_a : nullptr, rstd ? rstd + r_a : nullptr, ra, cols, seg, nseg,
+        part + r_a * nseg, eps, blockIdx.x, n_apply);
+  } else {
+    const int64_t e0 = r_n * cols;
+    norm_split_stats_body<Ts, T, NV, EPV, RMS>(x + e0, res ? res + e0 : nullptr, rn, cols, seg,
+                                               nseg, part + r_n * nseg, blockIdx.x - n_apply,
+                                               gridDim.x - n_apply);
+  }
+}
+
 // --------------------------------------------------------------- launchers
 
 template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
@@ -227,23 +269,32 @@ static hipError_t launch_norm_split(const void* x, const void* res, const void* 
   Ts* yo = static_cast<Ts*>(y);
   Ts* ro = static_cast<Ts*>(res_out);
   const int64_t batch = split_batch_rows(rows, (int64_t)cols * (RMS ? 2 : 1) * sizeof(Ts));
-  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
-    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+  auto grid_of = [&](int64_t nr) {
     const int64_t work = nr * nseg;
-    const unsigned grid = (unsigned)(work < kMaxGrid ? work : kMaxGrid);
-    const int64_t e0 = r0 * cols;
-    hipError_t e = launch_kernel(&norm_split_stats_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid),
-                                 dim3(T), s, xi + e0, ri ? ri + e0 : nullptr, nr, cols, SEG, nseg,
-                                 part + r0 * nseg);
+    return (unsigned)(work < kMaxGrid ? work : kMaxGrid);
+  };
+  // pass 1 of the first batch; per further batch, pass 2 of the one before
+  // with pass 1 of this one; then pass 2 of the last
+  int64_t r0 = 0, nr = rows < batch ? rows : batch;
+  hipError_t e = launch_kernel(&norm_split_stats_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid_of(nr)),
+                               dim3(T), s, xi, ri, nr, cols, SEG, nseg, part);
+  if (e != hipSuccess) return e;
+  for (int64_t r1 = batch; r1 < rows; r1 += batch) {
+    const int64_t n1 = rows - r1 < batch ? rows - r1 : batch;
+    const unsigned na = grid_of(nr), ns = grid_of(n1);
+    e = launch_kernel(&norm_split_apply_stats_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(na + ns),
+                      dim3(T), s, xi, ri, static_cast<const Ts*>(p1), static_cast<const Ts*>(p2),
+                      yo, ro, mean, rstd, cols, SEG, nseg, part, eps, r0, nr, r1, n1, na);
     if (e != hipSuccess) return e;
-    e = launch_kernel(&norm_split_apply_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid), dim3(T), s,
-                      xi + e0, ri ? ri + e0 : nullptr, static_cast<const Ts*>(p1),
-                      static_cast<const Ts*>(p2), yo + e0, ro ? ro + e0 : nullptr,
-                      mean ? mean + r0 : nullptr, rstd ? rstd + r0 : nullptr, nr, cols, SEG, nseg,
-                      static_cast<const float4*>(part + r0 * nseg), eps);
-    if (e != hipSuccess) return e;
+    r0 = r1;
+    nr = n1;
   }
-  return hipSuccess;
+  const int64_t e0 = r0 * cols;
+  return launch_kernel(&norm_split_apply_kernel<Ts, T, NV, EPV, OCC, RMS>, dim3(grid_of(nr)),
+                       dim3(T), s, xi + e0, ri ? ri + e0 : nullptr, static_cast<const Ts*>(p1),
+                       static_cast<const Ts*>(p2), yo + e0, ro ? ro + e0 : nullptr,
+                       mean ? mean + r0 : nullptr, rstd ? rstd + r0 : nullptr, nr, cols, SEG, nseg,
+                       static_cast<const float4*>(part + r0 * nseg), eps);
 }
 
 #define FR_NS(TS, T, NV, EPV, R) {T, NV, EPV, &launch_norm_split<TS, T, NV, EPV, 4, R>}

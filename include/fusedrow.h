@@ -214,9 +214,11 @@ FR_API int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols);
  * x, y as for fr_softmax_fwd (y may equal x); 1 <= cols <= FR_SPLIT_MAX_COLS.
  * workspace: device memory of >= fr_split_workspace_bytes(rows, cols) bytes,
  * 16-byte aligned, not overlapping any other buffer; contents on entry do not
- * matter. Two kernels on `stream` per batch of rows (both passes run over
- * one batch of rows, at most 256 MiB of input, before the next, so the second
- * read can come from the last-level cache; fr_debug_set_split_batch_bytes).
+ * matter. Both passes run over one batch of rows, at most 256 MiB of input,
+ * before the next, so that the second read can come from the last-level cache
+ * (fr_debug_set_split_batch_bytes): on `stream`, pass 1 of the first batch,
+ * one kernel per further batch running pass 2 of the batch before together
+ * with pass 1 of this one, then pass 2 of the last (batches + 1 kernels).
  * Results are bitwise reproducible. */
 FR_API fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t cols,
                                  fr_dtype_t x_dtype, fr_dtype_t y_dtype, void* workspace,

@@ -16,7 +16,10 @@
 // by a second pass. Logits are read twice and the outputs written once;
 // pass 1 uses ordinary (cached) loads and the launcher runs both passes over
 // one batch of rows at a time, so that the second read of a segment can come
-// from the last-level cache.
+// from the last-level cache: pass 1 of the first batch, then for each further
+// batch one launch with pass 2 of the batch before and pass 1 of this one
+// (split_apply_stats_kernel; they touch different rows), then pass 2 of the
+// last.
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 

@@ -412,7 +412,7 @@ void xent_kernel(const Tin* x,
         for (int k = 0; k < EPV; ++k) v[i][k] = 0.f;
       xe = 0.f;
     } else if constexpr (LOG2) {
-      // One factor f = g 2^n per lane and one fma per element. With the 2^8
+      // One factor f = g 2^n per wave and one fma per element. With the 2^8
       // bias every e_j <= 2^8, so where f is subnormal its rounding (at most
       // 2^-150) moves p_j by at most 2^-142, a 2^-9 fraction of the finest
       // bf16 step; where f is normal, f = g 2^n exactly and the fma rounds

@@ -37,7 +37,8 @@ RMSNorm backward (bf16 [2048, 32768], hidden size beyond the one-pass
 backward); they are
 reported under "backward" and "variants" and are not part of `value`; so is the
 attention forward (bf16 B=4 H=16 S=4096 D=128, causal and not), reported
-under "attention" in matrix TFLOP/s against the bf16 peak. Their per-row inputs from the
+under "attention" in matrix TFLOP/s against the bf16 peak and against the
+matrix-core probe's rate measured in the same run. Their per-row inputs from the
 forward (p, mean, rstd) are produced by the forward kernels before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -273,9 +274,39 @@ def launch_stats(w, us):
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
+MFMA_PROBE_ITERS = 2048
+
+
+def mfma_ceiling(torch, np, fr, dev, K):
+    """The matrix-core probe (fr_mfma_probe): bf16 32x32x16 matrix
+    instructions with no operand traffic and no vector work, three workgroups
+    of four wavefronts per compute unit (three wavefronts per SIMD, as the
+    attention kernel runs); TFLOP/s from the median of K event-timed calls,
+    with pseudo-random operands (full mantissas, as real data: the ceiling)
+    and with constant ones (less switching, a higher clock held)."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wg = 3 * cus
+    sink = torch.empty(wg * 256, device=dev)
+    runs = [lambda: fr.fr_mfma_probe(wg, MFMA_PROBE_ITERS, sink, pattern=1),
+            lambda: fr.fr_mfma_probe(wg, MFMA_PROBE_ITERS, sink, pattern=0)]
+    for r in runs:
+        for _ in range(3):
+            r()
+    torch.cuda.synchronize()
+    us = [float(np.median(u)) for u in time_calls(torch, np, runs, max(5, min(K, 20)))]
+    flops = wg * 4.0 * MFMA_PROBE_ITERS * 8 * 32768
+    tf = [flops / (u * 1e-6) / 1e12 for u in us]
+    return {"tflops": round(tf[0], 1), "median_us": round(us[0], 2),
+            "frac_of_bf16_peak": round(tf[0] / PEAK_BF16_TFLOPS, 4),
+            "constant_operands_tflops": round(tf[1], 1),
+            "constant_operands_frac_of_bf16_peak": round(tf[1] / PEAK_BF16_TFLOPS, 4),
+            "workgroups": wg, "iters": MFMA_PROBE_ITERS, "flops": flops}
+
+
 def attention_stats(torch, np, fr, workloads, dev, K):
     """Attention forward, bf16, B=4 H=16 S=4096 D=128, causal and not: per
-    call duration (HIP events) and matrix TFLOP/s against the bf16 peak.
+    call duration (HIP events) and matrix TFLOP/s against the bf16 peak and
+    against the matrix-core probe's rate measured in the same run.
     Flops: 4 B H Sq Sk D (two products), half of that when causal."""
     w = workloads.make_attention(4, 16, 4096, 4096, 128)
 
@@ -292,14 +323,16 @@ def attention_stats(torch, np, fr, workloads, dev, K):
             r()
     torch.cuda.synchronize()
     us = time_calls(torch, np, runs, max(5, min(K, 20)))
-    out = {}
+    ceil = mfma_ceiling(torch, np, fr, dev, K)
+    out = {"mfma_ceiling": ceil}
     flops = 4.0 * 64 * 4096 * 4096 * 128
     for name, u, f in (("attention_bf16_b4h16s4096d128", us[0], flops),
                        ("attention_bf16_b4h16s4096d128_causal", us[1], flops / 2)):
         med = float(np.median(u))
         tf = f / (med * 1e-6) / 1e12
         out[name] = {"median_us": round(med, 2), "tflops": round(tf, 1),
-                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": f,
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "frac_of_mfma_ceiling": round(tf / ceil["tflops"], 4), "flops": f,
                      "input_sha256": w.digest()[:16]}
     return out
 

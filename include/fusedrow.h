@@ -479,6 +479,25 @@ FR_API fr_status_t fr_stream_probe(fr_probe_t kind, const void* src, void* dst, 
                                    int64_t row_bytes, uint32_t value, uint32_t* sink, int threads,
                                    int vecs, int policy, void* stream);
 
+/* Matrix-core probe: what the bf16 matrix cores sustain when nothing else
+ * competes for the issue slots (no operand loads, no vector work) — the
+ * ceiling the attention forward's flop rate is compared with beside the
+ * published dense peak, which assumes the top clock ("Engineering a CUDA
+ * Machine Learning Framework from Scratch", §6.4 Multi-Head Attention &
+ * FlashAttention-2 Extension: attention's two matrix products). Runs
+ * `workgroups` workgroups of 256 lanes (1 .. 2^20); each wavefront issues
+ * `iters` (1 .. 2^19) rounds of 8 v_mfma_f32_32x32x16_bf16 on four
+ * independent accumulators, 2^15 flops each, so a call is
+ * workgroups * 4 * iters * 8 * 32768 flops. The rate depends on the operand
+ * data (the clock the chip holds does): pattern 0 takes every operand
+ * element 1/8, and each lane's sum of its accumulators, written to sink, is
+ * exactly 32 * iters; pattern 1 takes pseudo-random bf16 elements in [-1, 1)
+ * (full mantissas, as real data), the same in every wavefront, and every
+ * wavefront writes the same 64 sums. sink: workgroups * 256 floats, 4-byte
+ * aligned, caller-owned device memory. FR_E_SHAPE for counts out of range,
+ * FR_E_VALUE for another pattern, FR_E_NULL / FR_E_ALIGN for sink. */
+FR_API fr_status_t fr_mfma_probe(int workgroups, int iters, int pattern, float* sink,
+                                 void* stream);
 
 /* Force the kernel variant used by later calls of `op`: `threads` lanes per
  * row (64 = one wavefront per row, 256..1024 = one workgroup per row) and

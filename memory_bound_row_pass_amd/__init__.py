@@ -18,7 +18,7 @@ import os
 __all__ = [
     "F32", "BF16", "FR_MAX_COLS", "FusedRowError", "lib", "status_str", "version",
     "fr_softmax_fwd", "fr_layernorm_fwd", "fr_add_rmsnorm_fwd", "fr_softmax_xent_fwd_bwd",
-    "fr_stream_copy", "fr_stream_read", "fr_stream_write", "fr_stream_probe",
+    "fr_stream_copy", "fr_stream_read", "fr_stream_write", "fr_stream_probe", "fr_mfma_probe",
     "fr_stream_probe_rows", "PROBE_READ", "PROBE_WRITE", "PROBE_COPY", "PROBE_NT_LOADS",
     "PROBE_NT_STORES", "fr_debug_force_variant", "fr_debug_select_variant",
     "fr_debug_select_variant_for",
@@ -93,6 +93,7 @@ def _load() -> ctypes.CDLL:
         "fr_stream_copy": [P, P, I64, P],
         "fr_stream_read": [P, I64, P, P],
         "fr_stream_write": [P, I64, ctypes.c_uint32, P],
+        "fr_mfma_probe": [I32, I32, I32, P, P],
         "fr_stream_probe": [I32, P, P, I64, I64, ctypes.c_uint32, P, I32, I32, I32, P],
         "fr_softmax_bwd": [P, P, P, I64, I64, I32, P],
         "fr_softmax_xent_ex": [P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(XentOptions), P],
@@ -606,6 +607,19 @@ def fr_stream_write(dst, value: int, nbytes: int | None = None, stream=None) -> 
         raise ValueError("write larger than the buffer")
     _check(lib.fr_stream_write(_ptr(dst), n, ctypes.c_uint32(value & 0xFFFFFFFF),
                                _stream(stream, dst)), "fr_stream_write")
+
+
+def fr_mfma_probe(workgroups: int, iters: int, sink, pattern: int = 0, stream=None) -> None:
+    """Matrix-core probe (C: fr_mfma_probe): `workgroups` x 256 lanes, each
+    wavefront `iters` rounds of 8 bf16 32x32x16 matrix instructions on
+    constant (pattern 0: every sink element 32 * iters) or pseudo-random
+    (pattern 1) operands; sink is a float32 device tensor of at least
+    workgroups * 256 elements."""
+    _need_cuda(sink)
+    if sink.dtype != _torch().float32 or sink.numel() < int(workgroups) * 256:
+        raise ValueError("sink: float32, at least workgroups * 256 elements")
+    _check(lib.fr_mfma_probe(int(workgroups), int(iters), int(pattern), _ptr(sink),
+                             _stream(stream, sink)), "fr_mfma_probe")
 
 
 def fr_debug_force_variant(op: int, threads: int = 0, vecs: int = 0) -> None:

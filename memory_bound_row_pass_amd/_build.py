@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfusedrow.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["softmax.hip", "xent.hip", "norms.hip", "backward.hip", "split.hip", "split_norm.hip",
-           "attention.hip", "copy.hip", "noalloc.hip", "api.cpp"]
+           "attention.hip", "copy.hip", "noalloc.hip", "mfma_probe.hip", "api.cpp"]
 ARCH = os.environ.get("FR_OFFLOAD_ARCH", "gfx950")
 
 CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

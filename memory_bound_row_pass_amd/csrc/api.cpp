@@ -966,6 +966,15 @@ fr_status_t fr_stream_read(const void* src, int64_t bytes, uint32_t* sink, void*
                          FR_STREAM_VECS, FR_STREAM_POLICY, stream);
 }
 
+fr_status_t fr_mfma_probe(int workgroups, int iters, int pattern, float* sink, void* stream) {
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 19)) return FR_E_SHAPE;
+  if (pattern != 0 && pattern != 1) return FR_E_VALUE;
+  if (!sink) return FR_E_NULL;
+  if (!aligned(sink, 4)) return FR_E_ALIGN;
+  return launch_status(
+      fr::launch_mfma_probe(workgroups, iters, pattern, sink, static_cast<hipStream_t>(stream)));
+}
+
 fr_status_t fr_stream_write(void* dst, int64_t bytes, uint32_t value, void* stream) {
   return fr_stream_probe(FR_PROBE_WRITE, nullptr, dst, bytes, 0, value, nullptr,
                          FR_STREAM_THREADS, FR_STREAM_VECS, FR_STREAM_POLICY, stream);

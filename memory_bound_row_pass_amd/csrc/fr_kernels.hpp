@@ -205,6 +205,12 @@ hipError_t launch_stream_probe(int mode, const void* src, void* dst, int64_t byt
                                int64_t row_bytes, int threads, int vecs, int policy,
                                uint32_t value, uint32_t* sink, hipStream_t s);
 
+// Matrix-core probe (mfma_probe.hip): `workgroups` workgroups of 256 lanes,
+// each wavefront `iters` rounds of 8 bf16 32x32x16 matrix instructions on
+// operands of `pattern` (0 constant, 1 pseudo-random); sink: workgroups * 256
+// floats.
+hipError_t launch_mfma_probe(int workgroups, int iters, int pattern, float* sink, hipStream_t s);
+
 // Attention forward, bf16, head dim D in {64, 128}; BH = batch * heads.
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int64_t BH, int Sq, int Sk, int D, int causal, float scale,

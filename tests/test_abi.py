@@ -438,6 +438,18 @@ def test_stream_probe_validation():
     assert fr.lib.fr_stream_probe_rows(16, 24) == -1
 
 
+def test_mfma_probe_validation():
+    f = fr.lib.fr_mfma_probe
+    assert f(0, 1, 0, P(A), None) == E_SHAPE
+    assert f((1 << 20) + 1, 1, 0, P(A), None) == E_SHAPE
+    assert f(1, 0, 1, P(A), None) == E_SHAPE
+    assert f(1, (1 << 19) + 1, 1, P(A), None) == E_SHAPE
+    assert f(1, 1, 2, P(A), None) == E_VALUE
+    assert f(1, 1, -1, P(A), None) == E_VALUE
+    assert f(1, 1, 0, None, None) == E_NULL
+    assert f(1, 1, 1, P(A + 2), None) == E_ALIGN
+
+
 def test_variant_selection():
     # one wavefront per row for short rows, a workgroup per row for long ones
     assert fr.fr_debug_select_variant(fr.OP_SOFTMAX, 1000, fr.F32) == (64, 4, 4)

@@ -2,7 +2,8 @@
 they are timed for, in every compiled shape and both cache policies, through
 the C ABI: the read probe's per-row XOR words match the buffer, the write
 probe sets every word, the copy reproduces its source; nothing outside the
-target range is written (guard words around each buffer)."""
+target range is written (guard words around each buffer). The matrix-core
+probe runs every instruction it is timed for (an exact per-lane sum)."""
 import numpy as np
 import pytest
 import torch
@@ -99,3 +100,62 @@ def test_default_shape_entry_points():
                           row_xor(src_np, fr.STREAM_THREADS * fr.STREAM_VECS * 4))
     assert bool(torch.all(dst == np.int32(np.uint32(0xDEADBEEF).view(np.int32))))
     assert torch.equal(cdst, src)
+
+
+@pytest.mark.parametrize("workgroups,iters", [(1, 1), (7, 3), (768, 64)])
+def test_mfma_probe_runs_every_instruction(workgroups, iters):
+    """Constant operands (1/8): every lane's accumulator sum is exactly
+    32 * iters (each instruction adds 16 / 64 to each of the 16 elements of
+    each accumulator a lane holds, 2 iters instructions per accumulator);
+    the sink past the last workgroup is not written."""
+    n = workgroups * 256
+    buf = torch.full((n + 2 * GUARD,), -1.0, dtype=torch.float32, device=DEV)
+    body = buf[GUARD:GUARD + n]
+    fr.fr_mfma_probe(workgroups, iters, body, pattern=0)
+    torch.cuda.synchronize()
+    assert torch.all(body == 32.0 * iters).item()
+    assert torch.all(buf[:GUARD] == -1.0).item() and torch.all(buf[GUARD + n:] == -1.0).item()
+
+
+def probe_operands():
+    """The pseudo-random operands of the probe: element e of lane l's vector
+    s is the bf16 rounding (nearest, ties to even) of x / 2^23 - 1, with x the
+    top 24 bits of the MurmurHash3 32-bit finaliser of h + 1,
+    h = (64 s + l) * 8 + e. Returns u, w as [64 lanes, 8] float64 arrays."""
+    M = np.uint64(0xFFFFFFFF)
+    x = np.arange(1, 2 * 64 * 8 + 1, dtype=np.uint64)
+    x ^= x >> np.uint64(16)
+    x = (x * np.uint64(0x85EBCA6B)) & M
+    x ^= x >> np.uint64(13)
+    x = (x * np.uint64(0xC2B2AE35)) & M
+    x ^= x >> np.uint64(16)
+    v = ((x >> np.uint64(8)).astype(np.float64) * 2.0 ** -23 - 1.0).astype(np.float32)
+    b = v.view(np.uint32).astype(np.uint64)
+    r = ((b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    q = r.astype(np.uint32).view(np.float32).astype(np.float64).reshape(2, 64, 8)
+    return q[0], q[1]
+
+
+def test_mfma_probe_random_operands():
+    """Pseudo-random operands: every wavefront writes the same 64 sums (same
+    operands, same order), and a wavefront's total is the sum of all
+    elements of all products it formed: per instruction, sum over the
+    k-index of (column sum of A) x (row sum of B), A and B being the lane
+    vectors u and w laid out as 32 rows x 16 (lanes 32 h + i hold
+    k = 8 h .. 8 h + 7 of row i)."""
+    workgroups, iters = 7, 64
+    n = workgroups * 256
+    buf = torch.full((n + 2 * GUARD,), -1.0, dtype=torch.float32, device=DEV)
+    body = buf[GUARD:GUARD + n]
+    fr.fr_mfma_probe(workgroups, iters, body, pattern=1)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:GUARD] == -1.0).item() and torch.all(buf[GUARD + n:] == -1.0).item()
+    s = body.cpu().numpy().reshape(workgroups * 4, 64)
+    assert np.all(s.view(np.uint32) == s[0].view(np.uint32))
+    u, w = probe_operands()
+    su, sw = u.reshape(2, 32, 8).sum(axis=1), w.reshape(2, 32, 8).sum(axis=1)
+    expected = 8 * iters * float((su * sw).sum())
+    au, aw = np.abs(u).reshape(2, 32, 8).sum(axis=1), np.abs(w).reshape(2, 32, 8).sum(axis=1)
+    bound = 8 * iters * float((au * aw).sum())
+    assert abs(float(s[0].astype(np.float64).sum()) - expected) <= 1e-5 * bound
+

@@ -192,6 +192,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     kend = lim < kend ? lim : kend;
   }
   const int nblk = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // key blocks starting past mask_after reach the end of the keys or, when
+  // causal, the diagonal of the workgroup's first query (a scalar test per
+  // block)
+  int mask_after = Sk - BN;
+  if (causal) {
+    const int d = q_first + (Sk - Sq) - BN + 1;
+    mask_after = d < mask_after ? d : mask_after;
+  }
+  mask_after = __builtin_amdgcn_readfirstlane(mask_after);
 
   // tile loads: chunk c = tid + 256 i of a tile is key c / (D/8), d0 = (c % (D/8)) * 8
   // (row order), for K and V alike
@@ -282,8 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
     // online softmax for query qi over keys n0 + 32t + key(j),
     // key(j) = (j/4)*8 + 4h + j%4; t = scale_log2 * s (base-2 units)
-    const bool need_mask =
-        n0 + BN > Sk || (causal && n0 + BN - 1 > q_first + (Sk - Sq));
+    const bool need_mask = n0 > mask_after;
     const int klim = causal ? qi + (Sk - Sq) : Sk - 1;  // last visible key
     if (need_mask) {  // uniform; hidden scores take the identity of the max (or min)
 #pragma unroll

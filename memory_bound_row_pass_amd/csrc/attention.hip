@@ -12,10 +12,11 @@
 //   S^T (32 keys x 32 queries) = K_blk (A operand, from LDS) * Q^T (B operand,
 //     the wave's queries held in registers for the whole kernel);
 //   in the MFMA C layout lane l owns query l % 32 and 16 of the 32 keys (the
-//     other 16 are in lane l ^ 32), so the per-query block max takes the
-//     lane's 16 values and one exchange with lane l ^ 32 (v_permlane32_swap,
-//     no LDS round trip: 604 -> 588 us), and the rescale of
-//     the output accumulator is one per-lane factor;
+//     other 16 are in lane l ^ 32), so each lane tests the max of its own 16
+//     values against the lazy threshold, and only when the running max is
+//     raised is the query's block max formed with one exchange with lane
+//     l ^ 32 (v_permlane32_swap, no LDS round trip); the rescale of the
+//     output accumulator is one per-lane factor;
 //   O^T (D x 32 queries) += V_blk^T (A operand, from a transposed V tile in
 //     LDS) * P^T (B operand: the lane's 16 probabilities as they are). The C
 //     layout gives lane half h the keys {h*4 + 0..3, 8 + h*4 + 0..3} of each
@@ -319,14 +320,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
         for (int j = 0; j < 16; ++j) smax = s[t][j] < smax ? s[t][j] : smax;
     }
-    float tmax = smax * scale_log2;
-    {
-      const HalfPair t2 = half_pair(tmax);
-      tmax = __builtin_fmaxf(t2.lo, t2.hi);
-    }
-    // raise the running max only past the allowance (wave-uniform decision)
-    const bool raise = tmax > m_lazy;
+    // this lane's half of the query's block max (its 16 keys)
+    const float thalf = smax * scale_log2;
+    // raise the running max only past the allowance: the query's block max
+    // exceeds it iff one of its halves does, so the exchange between the
+    // halves is needed only on a raise (wave-uniform decision)
+    const bool raise = thalf > m_lazy;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const HalfPair t2 = half_pair(thalf);
+      const float tmax = __builtin_fmaxf(t2.lo, t2.hi);
       const float m_new = tmax > m_run ? tmax : m_run;
       const float alpha = m_run == kNegInf ? 0.f : exp2_hw(m_run - m_new);
       l_lane *= alpha;

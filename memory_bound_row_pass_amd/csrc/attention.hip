@@ -239,14 +239,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       vreg[i] = key < Sk ? b : u32x4{0, 0, 0, 0};
     }
   };
+  // this lane's chunk of copy i is key row tid / (D/8) + i 256 / (D/8), d
+  // (tid % (D/8)) 8: one lane offset per tile, the rest immediates
+  constexpr int RPI = 256 / (D / 8);
+  const int kst_lane = (tid / (D / 8)) * KP + (tid % (D / 8)) * 8;
+  const int vst_lane = (tid / (D / 8)) * VS + (tid % (D / 8)) * 8;
   auto store_tile = [&](int stage) {
-    bf16_t* ks = ks_st[stage];
-    bf16_t* vt = vt_st[stage];
+    bf16_t* ks = ks_st[stage] + kst_lane;
+    bf16_t* vt = vt_st[stage] + vst_lane;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(ks + (c / (D / 8)) * KP + (c % (D / 8)) * 8) = kreg[i];
-      *reinterpret_cast<u32x4*>(vt + (c / (D / 8)) * VS + (c % (D / 8)) * 8) = vreg[i];
+      *reinterpret_cast<u32x4*>(ks + RPI * i * KP) = kreg[i];
+      *reinterpret_cast<u32x4*>(vt + RPI * i * VS) = vreg[i];
     }
   };
 

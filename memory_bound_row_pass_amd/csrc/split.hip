@@ -89,9 +89,23 @@ __device__ __forceinline__ void split_stats_body(const Tin* x, int64_t rows, int
     const Tin* xs = x + row * cols + sgm.c0;
     const RowGeom<EPV> g(xs, sgm.len);
     float v[NV][EPV];
-    load_chunks<Tin, T, NV, EPV, kHeadAlign, kPass1NT>(xs, g, tid, v, kNegInf);
-    const int ec = g.extra_col(tid);
-    float xe = load_extra(xs, ec, kNegInf);
+    int ec;
+    float xe;
+    if (g.nvec == T * NV && g.head == 0 && g.tail == 0) {  // uniform: a whole segment
+      // every slot loaded, no element outside the chunks: no clamps, masks or
+      // head/tail element (the general loader's fill stores would otherwise
+      // run on this path too)
+      const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        Vec<Tin, EPV>::template load<kPass1NT>(xs + (uint32_t)(i * T * EPV) + lo, v[i]);
+      ec = -1;
+      xe = kNegInf;
+    } else {
+      load_chunks<Tin, T, NV, EPV, kHeadAlign, kPass1NT>(xs, g, tid, v, kNegInf);
+      ec = g.extra_col(tid);
+      xe = load_extra(xs, ec, kNegInf);
+    }
 
     // the wave's maximum first: exponentials relative to it, plain sums
     const float m = wave_max(lane_max<NV, EPV>(v, xe));

@@ -62,7 +62,7 @@ def expect(w, causal, scale, got, what):
     if lg is not None:
         fin = np.isfinite(lse_ref)
         assert np.array_equal(np.isneginf(lg), ~fin), what + ": -inf lse where no key is visible"
-        sabs = scale * np.einsum("bhid,bhjd->bhij", np.abs(q), np.abs(k))
+        sabs = abs(scale) * np.einsum("bhid,bhjd->bhij", np.abs(q), np.abs(k))
         sabs = np.where(vis, sabs, 0).max(-1)
         lb = 1e-5 * (np.abs(lse_ref) + sabs)
         assert np.all(np.abs(lg[fin] - lse_ref[fin]) <= lb[fin]), what + " lse"
@@ -86,8 +86,11 @@ def test_shapes(B, H, Sq, Sk, D, causal):
 
 def test_scales_in_place_and_no_lse():
     w = workloads.make_attention(1, 2, 256, 256, 128, seed=5)
-    for scale in (0.0, 0.02, 0.3):
+    # 0: every visible score equal, hidden blocks of a query at scale 0;
+    # negative: the block max is taken as the min of the raw scores
+    for scale in (0.0, 0.02, 0.3, -0.05):
         expect(w, True, scale, run(w, True, scale), f"attn scale {scale}")
+    expect(w, False, -0.05, run(w, False, -0.05), "attn scale -0.05 non-causal")
     expect(w, False, 0.0883883, run(w, False, 0.0883883, inplace=True), "attn in place (o = q)")
     ob, lg = run(w, False, 0.0883883, with_lse=False)
     assert lg is None

@@ -17,8 +17,9 @@
 //     raised is the query's block max formed with one exchange with lane
 //     l ^ 32 (v_permlane32_swap, no LDS round trip); the rescale of the
 //     output accumulator is one per-lane factor;
-//   O^T (D x 32 queries) += V_blk^T (A operand, from a transposed V tile in
-//     LDS) * P^T (B operand: the lane's 16 probabilities as they are). The C
+//   O^T (D x 32 queries) += V_blk^T (A operand, read from the row-major V
+//     tile in LDS through the transposing read ds_read_b64_tr_b16) * P^T
+//     (B operand: the lane's 16 probabilities as they are). The C
 //     layout gives lane half h the keys {h*4 + 0..3, 8 + h*4 + 0..3} of each
 //     16-key group, so the V^T operand is read with the same key order — the
 //     contraction over keys does not depend on their order.

@@ -309,6 +309,25 @@ __device__ __forceinline__ uint32_t opaque_zero() {
   return z;
 }
 
+// A whole row segment (no head or tail element, every slot in it):
+// unconditional loads, no clamps, masks or fill. The general loader's fill
+// stores for a row without whole chunks are placed by the compiler ahead of
+// its branch, so they run on every row; the split-row first passes, whose
+// segments are whole but for a row's last, take this path instead (bf16
+// cross-entropy [1024, 262144]: 263.0 -> 252.7 us per call). Used in the
+// shared loaders themselves it measured slower on the one-pass kernels, and
+// in the other split first passes (norms, softmax backward) within noise.
+template <typename Ts, int T, int NV, int EPV, bool NT = true>
+__device__ __forceinline__ void load_whole(const Ts* row, int tid, float (&v)[NV][EPV]) {
+  const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) Vec<Ts, EPV>::template load<NT>(row + (uint32_t)(i * T * EPV) + lo, v[i]);
+}
+template <int T, int NV, int EPV, int AL>
+__device__ __forceinline__ bool whole_segment(const RowGeom<EPV, AL>& g) {
+  return g.nvec == T * NV && g.head == 0 && g.tail == 0;
+}
+
 template <typename Ts, int T, int NV, int EPV, int AL, bool NT = true>
 __device__ __forceinline__ void load_chunks(const Ts* row, const RowGeom<EPV, AL>& g, int tid,
                                             float (&v)[NV][EPV], float fill) {

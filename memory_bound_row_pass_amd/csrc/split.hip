@@ -91,14 +91,8 @@ __device__ __forceinline__ void split_stats_body(const Tin* x, int64_t rows, int
     float v[NV][EPV];
     int ec;
     float xe;
-    if (g.nvec == T * NV && g.head == 0 && g.tail == 0) {  // uniform: a whole segment
-      // every slot loaded, no element outside the chunks: no clamps, masks or
-      // head/tail element (the general loader's fill stores would otherwise
-      // run on this path too)
-      const uint32_t lo = (uint32_t)tid * EPV + opaque_zero();
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        Vec<Tin, EPV>::template load<kPass1NT>(xs + (uint32_t)(i * T * EPV) + lo, v[i]);
+    if (whole_segment<T, NV>(g)) {  // uniform
+      load_whole<Tin, T, NV, EPV, kPass1NT>(xs, tid, v);
       ec = -1;
       xe = kNegInf;
     } else {

@@ -38,8 +38,9 @@
  *            then be NULL; the norm backward calls still zero their
  *            parameter gradients); 1 <= cols <= FR_MAX_COLS (less for the
  *            backward calls).
- * Threads    Entry points are re-entrant. fr_debug_force_variant and
- *            fr_debug_set_split_batch_bytes are the only global settings.
+ * Threads    Entry points are re-entrant. fr_debug_force_variant,
+ *            fr_debug_set_split_batch_bytes, fr_debug_set_split_cooperative
+ *            and fr_debug_set_coop_spin_limit are the only global settings.
  *
  * Arithmetic is fp32 throughout (bf16 inputs are widened exactly, bf16
  * outputs are rounded to nearest-even once, at the store).
@@ -199,27 +200,39 @@ FR_API fr_status_t fr_softmax_xent_ex(const void* logits, const int32_t* labels,
 #define FR_SPLIT_MIN_SEGMENT 8192
 
 /* Bytes of workspace the split entry points need for [rows, cols]:
- * rows * ceil(cols / FR_SPLIT_MIN_SEGMENT) * 16 (one 16-byte partial state
- * per row segment). -1 for an invalid shape. */
+ * rows * ceil(cols / FR_SPLIT_MIN_SEGMENT) * 16 + 16 (one 16-byte partial
+ * state per row segment, and 16 bytes more), 0 for rows = 0. -1 for an
+ * invalid shape. */
 FR_API int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols);
 
 /* Softmax for rows of any width (and for few rows: several workgroups share
  * a row). Same result definition as fr_softmax_fwd. A row is cut into
- * segments of 8192 columns (other segment shapes via fr_debug_force_variant); pass 1 writes each segment's partial state
- * (max, exponential sum) to `workspace`, pass 2 merges a row's partials in
- * segment order with the online normaliser merge and writes the segment's
- * outputs. Reads x twice, writes y once.
+ * segments, one workgroup per segment; each segment's partial state (max,
+ * exponential sum) is taken, the row's states are merged in segment order
+ * with the online normaliser merge, and each segment's outputs are written.
  *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.1:
  *    the merge of partial (max, sum) states.)
- * x, y as for fr_softmax_fwd (y may equal x); 1 <= cols <= FR_SPLIT_MAX_COLS.
- * workspace: device memory of >= fr_split_workspace_bytes(rows, cols) bytes,
- * 16-byte aligned, not overlapping any other buffer; contents on entry do not
- * matter. Both passes run over one batch of rows, at most 256 MiB of input,
- * before the next, so that the second read can come from the last-level cache
+ * One-pass form, when the rows give at least 4 segments of 32768 columns per
+ * compute unit and a row has at most 64 of them (fr_debug_set_split_cooperative):
+ * a kernel zeroing the workspace's counter and slots, then one launch in
+ * which a row's workgroups hold their segments in registers, exchange their
+ * states through the workspace (each waits for the others of its row; rows
+ * are handed out in the order workgroups start, so the waits need no more
+ * of the device than one row's workgroups) and write from the registers: x
+ * is read once. A workgroup that waits too long (fr_debug_set_coop_spin_limit;
+ * not reached in a correct run) writes NaN for its row. Otherwise two passes
+ * over segments of 8192 columns (16384 for bf16 input): pass 1 writes each
+ * segment's state to `workspace`, pass 2 merges and re-reads its segment (x
+ * read twice), over one batch of rows, at most 256 MiB of input, before the
+ * next, so that the second read can come from the last-level cache
  * (fr_debug_set_split_batch_bytes): on `stream`, pass 1 of the first batch,
  * one kernel per further batch running pass 2 of the batch before together
  * with pass 1 of this one, then pass 2 of the last (batches + 1 kernels).
- * Results are bitwise reproducible. */
+ * Other segment shapes via fr_debug_force_variant.
+ * x, y as for fr_softmax_fwd (y may equal x); 1 <= cols <= FR_SPLIT_MAX_COLS.
+ * workspace: device memory of >= fr_split_workspace_bytes(rows, cols) bytes,
+ * 16-byte aligned, not overlapping any other buffer; contents on entry do not
+ * matter. Results are bitwise reproducible for a given form and shape. */
 FR_API fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t cols,
                                  fr_dtype_t x_dtype, fr_dtype_t y_dtype, void* workspace,
                                  int64_t workspace_bytes, void* stream);
@@ -516,6 +529,26 @@ FR_API fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs);
  * not depend on it. Returns the previous setting. Process-wide setting meant
  * for tests and tuning; not synchronised with concurrent calls. */
 FR_API int64_t fr_debug_set_split_batch_bytes(int64_t bytes);
+
+/* The one-pass form of fr_softmax_fwd_split and fr_softmax_xent_split:
+ * mode 0 always runs the two passes; mode 1 (the default) takes the
+ * one-pass form where it applies and the rows give at least 4 work items
+ * per compute unit; mode 2 takes it wherever it applies (any row count, and
+ * with a forced variant, whose shape it keeps); other values mean 1.
+ * Results do not depend on it beyond rounding (both merge the same kind of
+ * segment states in segment order, the one-pass form by a fixed DPP tree).
+ * Returns the previous setting. Process-wide setting meant for tests and
+ * tuning; not synchronised with concurrent calls. */
+FR_API int fr_debug_set_split_cooperative(int mode);
+
+/* Bound on the polls a workgroup of the one-pass split form makes for the
+ * partial states of its row's other segments before it gives up and writes
+ * NaN for that row (the others always arrive in a correct run: rows are
+ * handed out in start order). polls < 0 restores the default (2^18);
+ * polls = 0 gives up whenever one poll does not find all states. Returns the
+ * previous setting. Process-wide setting meant for tests; not synchronised
+ * with concurrent calls. */
+FR_API int fr_debug_set_coop_spin_limit(int polls);
 
 /* hipError_t code of the last failed kernel launch on this thread (0 if
  * none), to explain an FR_E_LAUNCH. */

@@ -22,7 +22,8 @@ __all__ = [
     "fr_stream_probe_rows", "PROBE_READ", "PROBE_WRITE", "PROBE_COPY", "PROBE_NT_LOADS",
     "PROBE_NT_STORES", "fr_debug_force_variant", "fr_debug_select_variant",
     "fr_debug_select_variant_for",
-    "fr_debug_set_split_batch_bytes", "split_batch_bytes",
+    "fr_debug_set_split_batch_bytes", "split_batch_bytes", "fr_debug_set_split_cooperative",
+    "split_cooperative", "fr_debug_set_coop_spin_limit", "coop_spin_limit",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "fr_add_rmsnorm_bwd_noalloc", "FR_NOALLOC_SCRATCH_BYTES",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
@@ -131,6 +132,10 @@ def _load() -> ctypes.CDLL:
     L.fr_version.restype = ctypes.c_char_p
     L.fr_debug_set_split_batch_bytes.argtypes = [I64]
     L.fr_debug_set_split_batch_bytes.restype = ctypes.c_int64
+    L.fr_debug_set_split_cooperative.argtypes = [ctypes.c_int]
+    L.fr_debug_set_split_cooperative.restype = ctypes.c_int
+    L.fr_debug_set_coop_spin_limit.argtypes = [ctypes.c_int]
+    L.fr_debug_set_coop_spin_limit.restype = ctypes.c_int
     L.fr_debug_last_launch_error.argtypes = []
     L.fr_debug_last_launch_error.restype = ctypes.c_int
     return L
@@ -682,6 +687,49 @@ class split_batch_bytes:
 
     def __exit__(self, *exc):
         fr_debug_set_split_batch_bytes(self.prev)
+        return False
+
+
+def fr_debug_set_split_cooperative(mode: int) -> int:
+    """C: fr_debug_set_split_cooperative; returns the previous setting."""
+    return int(lib.fr_debug_set_split_cooperative(int(mode)))
+
+
+class split_cooperative:
+    """Context manager: the one-pass form of the split softmax and
+    cross-entropy never (0), where the rows are many enough (1, the default)
+    or wherever it applies (2); restore the previous setting after."""
+
+    def __init__(self, mode: int):
+        self.mode = mode
+
+    def __enter__(self):
+        self.prev = fr_debug_set_split_cooperative(self.mode)
+        return self
+
+    def __exit__(self, *exc):
+        fr_debug_set_split_cooperative(self.prev)
+        return False
+
+
+def fr_debug_set_coop_spin_limit(polls: int) -> int:
+    """C: fr_debug_set_coop_spin_limit; returns the previous setting."""
+    return int(lib.fr_debug_set_coop_spin_limit(int(polls)))
+
+
+class coop_spin_limit:
+    """Context manager: bound the one-pass split form's polls per wait
+    (< 0: the default); restore the previous setting after."""
+
+    def __init__(self, polls: int):
+        self.polls = polls
+
+    def __enter__(self):
+        self.prev = fr_debug_set_coop_spin_limit(self.polls)
+        return self
+
+    def __exit__(self, *exc):
+        fr_debug_set_coop_spin_limit(self.prev)
         return False
 
 

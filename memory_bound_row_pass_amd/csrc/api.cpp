@@ -129,6 +129,35 @@ const V* select_split(VariantSpan<V> sp, int op, int epv) {
   return nullptr;
 }
 
+// Split softmax / cross-entropy: shape and form. A forced (threads, vecs)
+// keeps its shape and takes the one-pass form wherever that applies (setting
+// != 0). Otherwise the one-pass shape (512 lanes x 64 elements: segments of
+// 32768 columns) in the one-pass form, for rows of at most 64 such segments
+// when (setting 1) the rows give at least 4 work items per compute unit —
+// below that, two passes over the table's first (smallest) segments measured
+// faster (fp32 [96, 131072] 39.1 against 36.9 us; [288, 131072] 77.8
+// against 81.1 us) — or (setting 2) always; else the table's first shape,
+// in two passes. rows < 0: a single row.
+struct SplitChoice {
+  const fr::SplitVariant* v;
+  bool one_pass;
+};
+SplitChoice choose_split(VariantSpan<fr::SplitVariant> sp, int op, int epv, int64_t rows,
+                         int64_t cols) {
+  const int mode = fr::split_cooperative();
+  if (g_forced[op].threads.load(std::memory_order_relaxed)) return {select_split(sp, op, epv), mode != 0};
+  if (mode != 0) {
+    const int64_t nseg = (cols + 32767) / 32768;
+    const int64_t r = rows < 0 ? 1 : rows;
+    if (nseg <= fr::kCoopMaxSegments && (mode == 2 || r * nseg >= 4 * fr::device_cu_count()))
+      for (size_t i = 0; i < sp.n; ++i) {
+        const fr::SplitVariant& v = sp.v[i];
+        if (v.epv == epv && v.threads == 512 && v.nv * v.epv == 64) return {&v, true};
+      }
+  }
+  return {select_split(sp, op, epv), mode == 2};
+}
+
 thread_local int t_last_launch_error = 0;
 
 int vec_epv(int esz) { return 16 / esz; }
@@ -137,11 +166,15 @@ int vec_epv(int esz) { return 16 / esz; }
 
 namespace {
 std::atomic<int64_t> g_split_batch_bytes{fr::kSplitBatchBytes};
+std::atomic<int> g_split_cooperative{1};
+std::atomic<int> g_coop_spin_limit{fr::kCoopSpinLimit};
 }  // namespace
 
 namespace fr {
 void note_launch_error(hipError_t e) { t_last_launch_error = static_cast<int>(e); }
 int64_t split_batch_bytes() { return g_split_batch_bytes.load(std::memory_order_relaxed); }
+int split_cooperative() { return g_split_cooperative.load(std::memory_order_relaxed); }
+int coop_spin_limit() { return g_coop_spin_limit.load(std::memory_order_relaxed); }
 int device_cu_count() {
   static std::atomic<int> cache[64];  // 0: not yet queried
   int dev = 0;
@@ -165,6 +198,14 @@ int64_t fr_debug_set_split_batch_bytes(int64_t bytes) {
   const int64_t prev = g_split_batch_bytes.load();
   g_split_batch_bytes.store(bytes < 0 ? fr::kSplitBatchBytes : bytes);
   return prev;
+}
+
+int fr_debug_set_split_cooperative(int mode) {
+  return g_split_cooperative.exchange(mode < 0 || mode > 2 ? 1 : mode);
+}
+
+int fr_debug_set_coop_spin_limit(int polls) {
+  return g_coop_spin_limit.exchange(polls < 0 ? fr::kCoopSpinLimit : polls);
 }
 
 
@@ -253,10 +294,9 @@ fr_status_t describe_variant(fr_op_t op, int64_t rows, int64_t cols, fr_dtype_t 
     }
     case FR_OP_SOFTMAX_SPLIT:
     case FR_OP_XENT_SPLIT: {
-      // the shape for a single row of `cols` (few rows: the smallest segment)
-      auto v = select_split(fr::split_variants(in_dtype == FR_BF16, out_dtype == FR_BF16,
+      auto v = choose_split(fr::split_variants(in_dtype == FR_BF16, out_dtype == FR_BF16,
                                                op == FR_OP_XENT_SPLIT),
-                            op, epv);
+                            op, epv, rows, cols).v;
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -705,7 +745,8 @@ fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* gamma, c
 int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 1 || cols > FR_SPLIT_MAX_COLS) return -1;
   if (rows > INT64_MAX / 8 / cols) return -1;
-  return rows * ((cols + FR_SPLIT_MIN_SEGMENT - 1) / FR_SPLIT_MIN_SEGMENT) * 16;
+  static_assert(FR_SPLIT_MIN_SEGMENT == fr::kSplitMinSegment, "workspace bound");
+  return fr::split_part_bytes(rows, cols);
 }
 
 namespace {
@@ -738,12 +779,13 @@ fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t c
   bool vec;
   if (xs == ys) vec = (reinterpret_cast<uintptr_t>(x) % 16) == (reinterpret_cast<uintptr_t>(y) % 16);
   else vec = aligned(x, 16) && aligned(y, 16) && cols % ve == 0;
-  const fr::SplitVariant* v =
-      select_split(fr::split_variants(x_dtype == FR_BF16, y_dtype == FR_BF16, 0),
-                   FR_OP_SOFTMAX_SPLIT, vec ? ve : 1);
-  if (!v) return FR_E_VARIANT;
-  return launch_status(v->launch(x, y, rows, (int)cols, nullptr, nullptr, nullptr, nullptr,
-                                 static_cast<float4*>(workspace), static_cast<hipStream_t>(stream)));
+  const SplitChoice c = choose_split(fr::split_variants(x_dtype == FR_BF16, y_dtype == FR_BF16, 0),
+                                     FR_OP_SOFTMAX_SPLIT, vec ? ve : 1, rows, cols);
+  if (!c.v) return FR_E_VARIANT;
+  return launch_status(c.v->launch(x, y, rows, (int)cols, nullptr, nullptr, nullptr, nullptr,
+                                   static_cast<float4*>(workspace),
+                                   fr_split_workspace_bytes(rows, cols), c.one_pass,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, float* loss,
@@ -786,17 +828,19 @@ fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, flo
   if (fr_status_t s = check_alias(bufs, 7)) return s;
   const bool vec =
       (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
-  const fr::SplitVariant* v = select_split(fr::split_variants(dtype == FR_BF16, dtype == FR_BF16, 1),
-                                           FR_OP_XENT_SPLIT, vec ? vec_epv(es) : 1);
-  if (!v) return FR_E_VARIANT;
+  const SplitChoice c = choose_split(fr::split_variants(dtype == FR_BF16, dtype == FR_BF16, 1),
+                                     FR_OP_XENT_SPLIT, vec ? vec_epv(es) : 1, rows, cols);
+  if (!c.v) return FR_E_VARIANT;
   if (count)
     if (fr_status_t s = launch_status(
             fr::launch_xent_count(labels, rows, o.use_ignore_index != 0, o.ignore_index, count, st)))
       return s;
   const fr::XentOptions ko = {o.use_ignore_index != 0, o.ignore_index, o.label_smoothing,
                               o.grad_scale, count, 0, 0, nullptr, nullptr};
-  if (fr_status_t s = launch_status(v->launch(logits, grad, rows, (int)cols, labels, loss, argmax,
-                                              &ko, static_cast<float4*>(workspace), st)))
+  if (fr_status_t s = launch_status(c.v->launch(logits, grad, rows, (int)cols, labels, loss, argmax,
+                                                &ko, static_cast<float4*>(workspace),
+                                                fr_split_workspace_bytes(rows, cols), c.one_pass,
+                                                st)))
     return s;
   if (!reduce) return FR_OK;
   return launch_status(fr::launch_xent_total(loss, rows, count, loss_total, st));

@@ -27,6 +27,35 @@ int device_cu_count();        // compute units of the current device (cached per
 // row batch stays in the last-level cache for pass 2 (with the row batches,
 // fp32 cross-entropy [2048, 131072]: 541 -> 504 us per call).
 constexpr bool kPass1NT = false;
+// The one-pass form of the split-row softmax and cross-entropy: a row's
+// segment workgroups exchange their partial states through device-scope
+// atomics in the workspace and write their outputs from the registers, so
+// the input is read once (split_cooperative(): 0 never, 1 where it applies
+// and the rows are many enough, the default; 2 wherever it applies).
+int split_cooperative();
+// Polls a workgroup makes for its row's other states before it gives up (its
+// outputs for the row are then NaN): a bound on every wait, so the kernel
+// always ends (fr_debug_set_coop_spin_limit).
+constexpr int kCoopSpinLimit = 1 << 18;
+int coop_spin_limit();
+// Most segments in one row of the one-pass form: the row's states are merged
+// by one wavefront's DPP tree, one state per lane.
+constexpr int kCoopMaxSegments = 64;
+// Workspace of the one-pass form: 16 bytes of ticket counter and abort word,
+// then two 64-bit words per (row, segment).
+inline int64_t coop_workspace_bytes(int64_t rows, int nseg) { return 16 + rows * nseg * 16; }
+// Bytes of the split workspace for [rows, cols] (fr_split_workspace_bytes):
+// one 16-byte state per segment of the smallest segment shape, and 16 bytes
+// more — room for the one-pass form of every segment shape.
+constexpr int kSplitMinSegment = 8192;
+inline int64_t split_part_bytes(int64_t rows, int64_t cols) {
+  return rows > 0 ? rows * ((cols + kSplitMinSegment - 1) / kSplitMinSegment) * 16 + 16 : 0;
+}
+inline bool coop_applies(int64_t rows, int nseg, int64_t part_bytes) {
+  return nseg <= kCoopMaxSegments && rows * nseg < (int64_t(1) << 31) &&
+         coop_workspace_bytes(rows, nseg) <= part_bytes;
+}
+
 inline int64_t split_batch_rows(int64_t rows, int64_t input_bytes_per_row) {
   const int64_t bytes = split_batch_bytes();
   if (bytes <= 0) return rows;
@@ -121,7 +150,8 @@ inline int bwd_grid(const V& v, int64_t rows) {
 // columns. labels / loss / argmax / opt: cross-entropy only (NULL otherwise).
 typedef hipError_t (*SplitLaunch)(const void* x, void* y, int64_t rows, int cols,
                                   const int32_t* labels, float* loss, int32_t* argmax,
-                                  const XentOptions* opt, float4* part, hipStream_t s);
+                                  const XentOptions* opt, float4* part, int64_t part_bytes,
+                                  bool one_pass, hipStream_t s);
 
 // Split-row LayerNorm / residual-add + RMSNorm (pass 1 partials into
 // `part`, then pass 2). LayerNorm: p1 = gamma, p2 = beta, res and res_out

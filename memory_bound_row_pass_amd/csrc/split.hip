@@ -3,23 +3,26 @@
 //
 // A row is cut into segments of `seg` columns (a multiple of 32, so every
 // segment keeps its row's address phase); workgroup (row, segment) owns one
-// segment in registers.
-//   pass 1 (split_stats_kernel): the segment's partial online-softmax state
-//     (m, s) plus the sum of its logits t and the column of its maximum,
-//     written to the workspace [rows][segments];
-//   pass 2 (split_apply_kernel): every workgroup of a row merges the row's
-//     partials in segment order (the same order, hence the same bits, in all
-//     of them), re-reads its segment and writes p (or the cross-entropy
-//     gradient, loss and argmax).
+// segment in registers. Two forms for the softmax and cross-entropy:
+//   one pass (split_coop_kernel): each workgroup takes its segment's partial
+//     online-softmax state (m, s) — plus the sum of its logits t and the
+//     column of its maximum when the options need them — posts it to the
+//     row's slots in the workspace, waits for the row's other states, merges
+//     them and writes p (or the cross-entropy gradient, loss and argmax)
+//     from its registers: the logits are read once;
+//   two passes: pass 1 (split_stats_kernel) writes each segment's state to
+//     the workspace [rows][segments]; pass 2 (split_apply_kernel) merges a
+//     row's states in segment order (the same order, hence the same bits, in
+//     every workgroup of the row), re-reads its segment and writes.
 // The merge is the online normaliser's ("Engineering a CUDA Machine Learning
-// Framework from Scratch", §3.1) applied to segment states: partials merged
-// by a second pass. Logits are read twice and the outputs written once;
-// pass 1 uses ordinary (cached) loads and the launcher runs both passes over
-// one batch of rows at a time, so that the second read of a segment can come
-// from the last-level cache: pass 1 of the first batch, then for each further
-// batch one launch with pass 2 of the batch before and pass 1 of this one
+// Framework from Scratch", §3.1) applied to segment states. In the two
+// passes the logits are read twice and the outputs written once; pass 1 uses
+// ordinary (cached) loads and the launcher runs both passes over one batch
+// of rows at a time, so that the second read of a segment can come from the
+// last-level cache: pass 1 of the first batch, then for each further batch
+// one launch with pass 2 of the batch before and pass 1 of this one
 // (split_apply_stats_kernel; they touch different rows), then pass 2 of the
-// last.
+// last. The softmax backward runs two passes (its per-row sum s = sum p dy).
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
@@ -56,6 +59,9 @@ struct Segment {
 
 // ------------------------------------------------------------------ pass 1
 
+// The state of the segment held in v (xe: the extra column of lanes with
+// ec >= 0; c0: the segment's first column), merged over the workgroup's
+// waves through the LDS slot (the alternation rule of block_merge).
 // STATS bit 1: the sum of the logits (label smoothing); bit 2: the column of
 // the maximum (argmax). Without them a segment costs a max, a subtraction, a
 // multiply and one base-2 exponential per element: the sum of exponentials
@@ -64,6 +70,64 @@ struct Segment {
 // matter), unlike an output p_j. x - m is formed first: folding m into an fma
 // with log2e would put the rounding of m * log2e (|m| * 2^-24) into every
 // term.
+template <int T, int NV, int EPV, int STATS, typename G>
+__device__ __forceinline__ SplitState segment_state(const float (&v)[NV][EPV], float xe, int ec,
+                                                    const G& g, int c0, int tid, int wave,
+                                                    int lane, float (*slot)[4]) {
+  constexpr int NW = T / 64;
+  constexpr bool WANT_T = STATS & 1;
+  constexpr bool WANT_IDX = STATS & 2;
+  // the wave's maximum first: exponentials relative to it, plain sums
+  const float m = wave_max(lane_max<NV, EPV>(v, xe));
+  float t = 0.f, best = 3.0e38f;
+  if constexpr (WANT_T) {  // masked slots hold -inf and are skipped
+    const bool full = g.nvec == T * NV;
+    float t0 = ec >= 0 ? xe : 0.f, t1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool ok = full || i * T + tid < g.nvec;
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const float a = ok ? v[i][k] : 0.f;
+        if (k & 1) t1 += a; else t0 += a;
+      }
+    }
+    t = t0 + t1;
+  }
+  if constexpr (WANT_IDX) {
+    // first slot holding the wave's max: scan backwards keeping the last
+    // match; slot order is column order within a lane
+    int c = -1;
+#pragma unroll
+    for (int i = NV - 1; i >= 0; --i)
+#pragma unroll
+      for (int k = EPV - 1; k >= 0; --k) c = v[i][k] == m ? i * EPV + k : c;
+    if (c >= 0)
+      best = (float)(c0 + g.head + ((c / EPV) * T + tid) * EPV + (c % EPV));
+    if (ec >= 0 && xe == m) {
+      const float ce = (float)(c0 + ec);
+      best = ce < best ? ce : best;
+    }
+  }
+  // sum of exp(x - m) with the hardware exponential
+  const float mr = (m == kNegInf) ? 0.f : m;
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) {
+      const float e = exp2_hw((v[i][k] - mr) * kLog2e);
+      if (k & 1) s1 += e; else s0 += e;
+    }
+  const float se = exp2_hw((xe - mr) * kLog2e);
+  const WaveSums ws = wave_reduce(WaveSums{(s0 + s1) + se, t, best}, WaveSumsMerge{});
+  SplitState st{m, ws.s, ws.t, ws.idx};
+  if constexpr (NW > 1)
+    st = block_merge_tree<NW>(st, slot, wave, lane, SplitMerge{},
+                              SplitState{kNegInf, 0.f, 0.f, 3.0e38f});
+  return st;
+}
+
 // The body: work items w0, w0 + wstride, ... of rows * nseg.
 template <typename Tin, int T, int NV, int EPV, int STATS>
 __device__ __forceinline__ void split_stats_body(const Tin* x, int64_t rows, int cols, int seg,
@@ -71,8 +135,6 @@ __device__ __forceinline__ void split_stats_body(const Tin* x, int64_t rows, int
                                                  int skip_ignored, float4* part, int64_t w0,
                                                  int64_t wstride) {
   constexpr int NW = T / 64;
-  constexpr bool WANT_T = STATS & 1;
-  constexpr bool WANT_IDX = STATS & 2;
   __shared__ float xw[2][NW][4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -101,54 +163,8 @@ __device__ __forceinline__ void split_stats_body(const Tin* x, int64_t rows, int
       xe = load_extra(xs, ec, kNegInf);
     }
 
-    // the wave's maximum first: exponentials relative to it, plain sums
-    const float m = wave_max(lane_max<NV, EPV>(v, xe));
-    float t = 0.f, best = 3.0e38f;
-    if constexpr (WANT_T) {  // masked slots hold -inf and are skipped
-      const bool full = g.nvec == T * NV;
-      float t0 = ec >= 0 ? xe : 0.f, t1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const bool ok = full || i * T + tid < g.nvec;
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          const float a = ok ? v[i][k] : 0.f;
-          if (k & 1) t1 += a; else t0 += a;
-        }
-      }
-      t = t0 + t1;
-    }
-    if constexpr (WANT_IDX) {
-      // first slot holding the wave's max: scan backwards keeping the last
-      // match; slot order is column order within a lane
-      int c = -1;
-#pragma unroll
-      for (int i = NV - 1; i >= 0; --i)
-#pragma unroll
-        for (int k = EPV - 1; k >= 0; --k) c = v[i][k] == m ? i * EPV + k : c;
-      if (c >= 0)
-        best = (float)(sgm.c0 + g.head + ((c / EPV) * T + tid) * EPV + (c % EPV));
-      if (ec >= 0 && xe == m) {
-        const float ce = (float)(sgm.c0 + ec);
-        best = ce < best ? ce : best;
-      }
-    }
-    // sum of exp(x - m) with the hardware exponential
-    const float mr = (m == kNegInf) ? 0.f : m;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const float e = exp2_hw((v[i][k] - mr) * kLog2e);
-        if (k & 1) s1 += e; else s0 += e;
-      }
-    const float se = exp2_hw((xe - mr) * kLog2e);
-    const WaveSums ws = wave_reduce(WaveSums{(s0 + s1) + se, t, best}, WaveSumsMerge{});
-    SplitState st{m, ws.s, ws.t, ws.idx};
-    if constexpr (NW > 1)
-      st = block_merge_tree<NW>(st, xw[merges++ & 1], wave, lane, SplitMerge{},
-                                SplitState{kNegInf, 0.f, 0.f, 3.0e38f});
+    const SplitState st = segment_state<T, NV, EPV, STATS>(v, xe, ec, g, sgm.c0, tid, wave, lane,
+                                                           xw[merges++ & 1]);
     if (tid == 0) part[w] = float4{st.m, st.s, st.t, st.idx};
   }
 }
@@ -193,6 +209,60 @@ __device__ __forceinline__ float split_p(float xv, float M, float fac, float b) 
     return __builtin_fmaf(e, fac, -b);
   } else {
     return __builtin_fmaf(exp_acc(xv - M), fac, -b);
+  }
+}
+
+// Writes the segment's outputs from its logits v (and xe) and the row's
+// merged state st: p, or the cross-entropy gradient with the row's loss
+// (from the lane owning the label column) and argmax (from segment 0).
+template <typename Tin, typename Tout, int T, int NV, int EPV, bool XENT, typename G>
+__device__ __forceinline__ void segment_apply(float (&v)[NV][EPV], float xe, int ec, const G& g,
+                                              const Segment& sgm, const Tin* xs, Tout* ys,
+                                              const SplitState& st, int label, float gsc,
+                                              float goff, const XentOptions& opt, float* loss,
+                                              int32_t* argmax, int64_t row, int sg, int cols,
+                                              int tid) {
+  const float inv_s = 1.f / st.s;
+  // label column handled by the lane of this segment that owns it
+  bool label_lane = false;
+  float x_label = 0.f;
+  const bool valid = XENT && label >= 0 && label < cols;
+  if constexpr (XENT) {
+    const int lc = label - sgm.c0;
+    if (valid && lc >= 0 && lc < sgm.len) {
+      const int body_end = g.head + g.nvec * EPV;
+      const int owner = lc < g.head ? lc
+                        : lc >= body_end ? g.head + (lc - body_end)
+                                         : ((lc - g.head) / EPV) % T;
+      label_lane = owner == tid;
+    }
+    if (label_lane) x_label = load1(xs + lc);
+  }
+
+  // the factor a / S (2^-8 a / S for the biased bf16 exponentials)
+  const float fac = (sizeof(Tout) == 2 ? 0x1p-8f : 1.f) * (XENT ? inv_s * gsc : inv_s);
+  const float off = XENT ? goff : 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) v[i][k] = split_p<Tout>(v[i][k], st.m, fac, off);
+  xe = split_p<Tout>(xe, st.m, fac, off);
+  store_chunks<Tout, T, NV, EPV>(ys, g, tid, v);
+  if (ec >= 0) store1(ys + ec, xe);
+
+  if constexpr (XENT) {
+    if (label_lane) {
+      const float eps = opt.smoothing;
+      const float p = exp_acc(x_label - st.m) * inv_s;
+      store1(ys + (label - sgm.c0), gsc * ((p - (1.f - eps)) - eps / (float)cols));
+      float l = st.m + logf(st.s);
+      if (eps != 1.f) l -= (1.f - eps) * x_label;
+      if (eps != 0.f) l -= eps * (st.t / (float)cols);
+      loss[row] = l;
+    } else if (!valid && sg == 0 && tid == 0) {
+      loss[row] = __builtin_nanf("");
+    }
+    if (argmax && sg == 0 && tid == 0) argmax[row] = (int32_t)st.idx;
   }
 }
 
@@ -252,53 +322,11 @@ __device__ __forceinline__ void split_apply_body(const Tin* x, Tout* y, int64_t 
     }
 
     const SplitState st = merge_row<T>(part, row, nseg, xw[merges++ & 1], wave, lane, tid);
-    const float inv_s = 1.f / st.s;
-
     float v[NV][EPV];
     load_chunks<Tin, T, NV, EPV>(xs, g, tid, v, kNegInf);
-    float xe = load_extra(xs, ec, kNegInf);
-
-    // label column handled by the lane of this segment that owns it
-    bool label_lane = false;
-    float x_label = 0.f;
-    const bool valid = XENT && label >= 0 && label < cols;
-    if constexpr (XENT) {
-      const int lc = label - sgm.c0;
-      if (valid && lc >= 0 && lc < sgm.len) {
-        const int body_end = g.head + g.nvec * EPV;
-        const int owner = lc < g.head ? lc
-                          : lc >= body_end ? g.head + (lc - body_end)
-                                           : ((lc - g.head) / EPV) % T;
-        label_lane = owner == tid;
-      }
-      if (label_lane) x_label = load1(xs + lc);
-    }
-
-    // the factor a / S (2^-8 a / S for the biased bf16 exponentials)
-    const float fac = (sizeof(Tout) == 2 ? 0x1p-8f : 1.f) * (XENT ? inv_s * gsc : inv_s);
-    const float off = XENT ? goff : 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) v[i][k] = split_p<Tout>(v[i][k], st.m, fac, off);
-    xe = split_p<Tout>(xe, st.m, fac, off);
-    store_chunks<Tout, T, NV, EPV>(ys, g, tid, v);
-    if (ec >= 0) store1(ys + ec, xe);
-
-    if constexpr (XENT) {
-      if (label_lane) {
-        const float eps = opt.smoothing;
-        const float p = exp_acc(x_label - st.m) * inv_s;
-        store1(ys + (label - sgm.c0), gsc * ((p - (1.f - eps)) - eps / (float)cols));
-        float l = st.m + logf(st.s);
-        if (eps != 1.f) l -= (1.f - eps) * x_label;
-        if (eps != 0.f) l -= eps * (st.t / (float)cols);
-        loss[row] = l;
-      } else if (!valid && sg == 0 && tid == 0) {
-        loss[row] = __builtin_nanf("");
-      }
-      if (argmax && sg == 0 && tid == 0) argmax[row] = (int32_t)st.idx;
-    }
+    const float xe = load_extra(xs, ec, kNegInf);
+    segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, label, gsc, goff, opt,
+                                              loss, argmax, row, sg, cols, tid);
   }
 }
 
@@ -335,6 +363,175 @@ void split_apply_stats_kernel(SplitBatch a, SplitBatch n, int cols, int seg, int
     split_stats_body<Tin, T, NV, EPV, STATS>(static_cast<const Tin*>(n.x), n.rows, cols, seg, nseg,
                                              n.labels, opt, skip_ignored, n.part, blockIdx.x - n_apply,
                                              gridDim.x - n_apply);
+}
+
+// ---------------------------------------------------------- one-pass form
+// One workgroup per (row, segment) work item, as in the two passes, but the
+// row's workgroups wait for each other: each loads its segment into
+// registers and takes its state as pass 1 does, posts the state, waits for
+// the states of the row's other segments, merges all nseg of them in segment
+// order (every workgroup of the row gets the same bits) and writes its
+// outputs from the registers as pass 2 does after its second read: the input
+// is read once.
+//
+// Work items are handed out in start order: a workgroup takes the next
+// ticket from a device-scope counter when it starts, and ticket w is row
+// w / nseg, segment w % nseg. So the started workgroups always hold the
+// lowest tickets, every row below the lowest unfinished one has finished,
+// and that row's missing segments only need free room on the device for
+// their workgroups (rows of at most 64 segments): the waits end however the
+// hardware orders, places or delays the workgroups.
+// Posting: the state as one or two 64-bit device-scope atomic stores, word 0
+// = {m, s}, word 1 = {t, idx + 1} (with the options that need them), into
+// the segment's slot of the row; the slots are zeroed before the launch and
+// neither word is ever zero once posted (s >= 1 when m is finite; m = -inf
+// and NaN have non-zero bits; idx + 1 >= 1). Such stores go through to the
+// level all XCDs share without the whole-L2 write-back of a device-scope
+// release fence, and a reader sees a word either unposted or whole. Waiting:
+// lane NWD j + f of wave 0 reads word f of segment j (64 / NWD segments per
+// round) with device-scope atomic loads until every word is posted.
+// Bounded: after spin_limit polls (each after a short sleep), or once
+// another wait has given up (the abort word), a workgroup takes NaN for the
+// missing states — its outputs of that row are NaN — and sets the abort
+// word; the kernel always ends.
+
+// Wave 0: waits for word f < NWD of segment j < nseg of the row's slots
+// ([nseg][2] words) and leaves segment j's state in team[j].
+template <int NWD>
+__device__ __forceinline__ void coop_wait(const uint64_t* slots, int nseg, uint32_t* abort_word,
+                                          int spin_limit, int lane, float (*team)[4]) {
+  constexpr int PER = 64 / NWD;  // segments per round
+  const int f = lane % NWD;
+  for (int j0 = 0; j0 < nseg; j0 += PER) {
+    const int j = j0 + lane / NWD;
+    const bool live = j < nseg;
+    uint64_t word = 0;
+    bool have = !live;
+    for (int spins = 0;; ++spins) {
+      if (!have) {
+        word = __hip_atomic_load(slots + (size_t)j * 2 + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        have = word != 0;
+      }
+      if (__builtin_amdgcn_ballot_w64(!have) == 0) break;
+      bool give_up = spins >= spin_limit;
+      if ((spins & 15) == 15)
+        give_up = give_up ||
+                  __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      if (__builtin_amdgcn_readfirstlane((int)give_up)) {
+        if (lane == 0) __hip_atomic_store(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (live) {
+      const float lo = have ? __builtin_bit_cast(float, (uint32_t)word) : __builtin_nanf("");
+      const float hi = have ? __builtin_bit_cast(float, (uint32_t)(word >> 32)) : __builtin_nanf("");
+      team[j][2 * f] = lo;
+      team[j][2 * f + 1] = f == 1 ? hi - 1.f : hi;  // idx + 1 -> idx (exact below 2^24)
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t coop_word(float lo, float hi) {
+  return ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32) | __builtin_bit_cast(uint32_t, lo);
+}
+
+// ctl[0]: the ticket counter, ctl[1]: the abort word; slots: [rows][nseg][2].
+template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT, int STATS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, int nseg,
+                       const int32_t* labels, float* loss, int32_t* argmax, XentOptions opt,
+                       int skip_ignored, uint64_t* slots, uint32_t* ctl, int spin_limit) {
+  constexpr int NW = T / 64;
+  constexpr int NWD = STATS ? 2 : 1;  // words posted per segment
+  __shared__ float xw[2][NW][4];
+  __shared__ float team[kCoopMaxSegments][4];
+  __shared__ uint32_t ticket;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  if (tid == 0) ticket = __hip_atomic_fetch_add(ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (NWD == 1) {  // the fields not posted
+    team[lane][2] = 0.f;
+    team[lane][3] = 3.0e38f;
+  }
+  lds_barrier();
+  const int64_t w = __builtin_amdgcn_readfirstlane(ticket);  // < rows * nseg: one per workgroup
+  const int64_t row = w / nseg;
+  const int sg = (int)(w - row * nseg);
+  const Segment sgm(sg, seg, cols);
+  const Tin* xs = x + row * cols + sgm.c0;
+  Tout* ys = y + row * cols + sgm.c0;
+  const RowGeom<EPV> g(xs, sgm.len);
+  const int ec = g.extra_col(tid);
+
+  float gsc = 1.f, goff = 0.f;
+  int label = 0;
+  bool ignored = false;
+  if constexpr (XENT) {
+    gsc = opt.grad_scale;
+    if (opt.count) gsc = gsc / (float)(*opt.count);
+    goff = gsc * (opt.smoothing / (float)cols);
+    label = __builtin_amdgcn_readfirstlane(labels[row]);
+    ignored = opt.use_ignore && label == opt.ignore_index;
+  }
+  if (ignored && skip_ignored) {  // uniform over the row: no post; a zero gradient, loss 0
+    float z[NV][EPV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) z[i][k] = 0.f;
+    store_chunks<Tout, T, NV, EPV>(ys, g, tid, z);
+    if (ec >= 0) store1(ys + ec, 0.f);
+    if (sg == 0 && tid == 0) loss[row] = 0.f;
+    return;
+  }
+
+  float v[NV][EPV];
+  float xe;
+  if (whole_segment<T, NV>(g)) {  // uniform
+    load_whole<Tin, T, NV, EPV>(xs, tid, v);
+    xe = kNegInf;
+  } else {
+    load_chunks<Tin, T, NV, EPV>(xs, g, tid, v, kNegInf);
+    xe = load_extra(xs, ec, kNegInf);
+  }
+  const SplitState mine = segment_state<T, NV, EPV, STATS>(v, xe, ec, g, sgm.c0, tid, wave, lane,
+                                                           xw[0]);
+  uint64_t* row_slots = slots + (size_t)row * nseg * 2;
+  if (tid < NWD)
+    __hip_atomic_store(row_slots + (size_t)sg * 2 + tid,
+                       tid == 0 ? coop_word(mine.m, mine.s) : coop_word(mine.t, mine.idx + 1.f),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave == 0) coop_wait<NWD>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+  lds_barrier();
+  // the row's state: lane j < nseg holds segment j's, one DPP tree (the same
+  // in every wave of every workgroup of the row)
+  SplitState st{kNegInf, 0.f, 0.f, 3.0e38f};
+  if (lane < nseg) st = SplitState{team[lane][0], team[lane][1], team[lane][2], team[lane][3]};
+  st = wave_reduce(st, SplitMerge{});
+
+  if (ignored) {  // with argmax: the row's argmax, a zero gradient, loss 0
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) v[i][k] = 0.f;
+    store_chunks<Tout, T, NV, EPV>(ys, g, tid, v);
+    if (ec >= 0) store1(ys + ec, 0.f);
+    if (sg == 0 && tid == 0) {
+      loss[row] = 0.f;
+      argmax[row] = (int32_t)st.idx;
+    }
+    return;
+  }
+  segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, label, gsc, goff, opt,
+                                            loss, argmax, row, sg, cols, tid);
+}
+
+// Zeroes n 16-byte words (the one-pass form's counter, abort word and slots).
+__global__ __launch_bounds__(256) void coop_clear_kernel(uint4* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = uint4{0u, 0u, 0u, 0u};
 }
 
 // ------------------------------------------------ softmax backward, split
@@ -450,15 +647,40 @@ static unsigned split_grid(int64_t work) {
   return (unsigned)(work < kMaxGrid ? work : kMaxGrid);
 }
 
+// The one-pass form over rows of nseg segments: its workspace (16 bytes of
+// counter and abort word, then rows * nseg * 16 bytes of slots) is zeroed,
+// then one workgroup per work item.
+template <typename Tin, typename Tout, typename K>
+static hipError_t launch_coop(K kernel, int nseg, int T, float4* part, hipStream_t s, const Tin* x,
+                              Tout* y, int64_t rows, int cols, int seg, const int32_t* labels,
+                              float* loss, int32_t* argmax, XentOptions o, int skip) {
+  const int64_t n16 = coop_workspace_bytes(rows, nseg) / 16;
+  hipError_t e = launch_kernel(&coop_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), s,
+                               reinterpret_cast<uint4*>(part), n16);
+  if (e != hipSuccess) return e;
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(part);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(part + 1);
+  return launch_kernel(kernel, dim3((unsigned)(rows * nseg)), dim3(T), s, x, y, rows, cols, seg, nseg,
+                       labels, loss, argmax, o, skip, slots, ctl, coop_spin_limit());
+}
+
 template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT>
 static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, const int32_t* labels,
                                float* loss, int32_t* argmax, const XentOptions* opt, float4* part,
-                               hipStream_t s) {
+                               int64_t part_bytes, bool one_pass, hipStream_t s) {
   constexpr int SEG = T * NV * EPV;
   const int nseg = (cols + SEG - 1) / SEG;
   const XentOptions o = opt ? *opt : XentOptions{0, 0, 0.f, 1.f, nullptr, 0, 0, nullptr, nullptr};
   const int skip = XENT && o.use_ignore && !argmax;
   const int stats = XENT ? ((o.smoothing != 0.f ? 1 : 0) | (argmax ? 2 : 0)) : 0;
+  if (one_pass && coop_applies(rows, nseg, part_bytes)) {
+    auto kc = stats == 0   ? &split_coop_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, 0>
+              : stats == 1 ? &split_coop_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, XENT ? 1 : 0>
+              : stats == 2 ? &split_coop_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, XENT ? 2 : 0>
+                           : &split_coop_kernel<Tin, Tout, T, NV, EPV, OCC, XENT, XENT ? 3 : 0>;
+    return launch_coop(kc, nseg, T, part, s, static_cast<const Tin*>(x), static_cast<Tout*>(y), rows,
+                       cols, SEG, labels, loss, argmax, o, skip);
+  }
   auto k1 = stats == 0   ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 0>
             : stats == 1 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 1>
             : stats == 2 ? &split_stats_kernel<Tin, T, NV, EPV, OCC, 2>
@@ -536,7 +758,8 @@ static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* 
 // elements; the scalar path (unaligned phases) 256 lanes x 32 elements.
 #define FR_SP_TABLE(TI, TO, E, X)                                                           \
   {FR_SP(TI, TO, 256, 8, E, 4, X),       FR_SP(TI, TO, 512, 32 / E, E, 4, X),                 \
-   FR_SP(TI, TO, 1024, 32 / E, E, 4, X), FR_SP(TI, TO, 256, 32, 1, 4, X)}
+   FR_SP(TI, TO, 1024, 32 / E, E, 4, X), FR_SP(TI, TO, 512, 64 / E, E, 4, X),                 \
+   FR_SP(TI, TO, 256, 32, 1, 4, X)}
 
 static const SplitVariant kSpF32F32[] = FR_SP_TABLE(float, float, 4, false);
 static const SplitVariant kSpBf16Bf16[] = FR_SP_TABLE(bf16_t, bf16_t, 8, false);

@@ -265,7 +265,7 @@ def test_split_validation():
     f = fr.lib.fr_softmax_fwd_split
     Y, WS = A + 0x100000, A + 0x200000
     need = fr.fr_split_workspace_bytes(4, 100000)
-    assert need == 4 * 13 * 16                        # ceil(100000 / 8192) = 13 segments per row
+    assert need == 4 * 13 * 16 + 16                   # ceil(100000 / 8192) = 13 segments per row
     assert f(P(A), P(Y), 0, 100000, 0, 0, None, 0, None) == OK
     assert f(P(A), P(Y), 4, 100000, 0, 0, P(WS), need - 1, None) == E_SHAPE
     assert f(P(A), P(Y), 4, fr.FR_SPLIT_MAX_COLS + 1, 0, 0, P(WS), 1 << 40, None) == E_SHAPE
@@ -514,6 +514,33 @@ def test_split_batch_setting():
         assert L.fr_debug_set_split_batch_bytes(-1) == default
     finally:
         L.fr_debug_set_split_batch_bytes(-1)
+
+
+def test_split_cooperative_settings():
+    # host-side settings only: each returns the previous value
+    L = fr.lib
+    assert L.fr_debug_set_split_cooperative(0) == 1          # 1 by default
+    try:
+        assert L.fr_debug_set_split_cooperative(2) == 0
+        assert L.fr_debug_set_split_cooperative(7) == 2      # out of range: 1
+        assert L.fr_debug_set_split_cooperative(-1) == 1
+        assert L.fr_debug_set_split_cooperative(1) == 1
+        with fr.split_cooperative(0):
+            assert L.fr_debug_set_split_cooperative(0) == 0
+        assert L.fr_debug_set_split_cooperative(1) == 1
+    finally:
+        L.fr_debug_set_split_cooperative(1)
+    default = 1 << 18
+    assert L.fr_debug_set_coop_spin_limit(5) == default
+    try:
+        assert L.fr_debug_set_coop_spin_limit(0) == 5
+        assert L.fr_debug_set_coop_spin_limit(-3) == 0
+        assert L.fr_debug_set_coop_spin_limit(-1) == default
+        with fr.coop_spin_limit(0):
+            assert L.fr_debug_set_coop_spin_limit(0) == 0
+        assert L.fr_debug_set_coop_spin_limit(-1) == default
+    finally:
+        L.fr_debug_set_coop_spin_limit(-1)
 
 
 def test_row_aware_selection():

@@ -2,9 +2,10 @@
 fr_softmax_xent_split) against the double-precision oracle, through the C
 ABI: widths from 1 to 2^20 (beyond the single-workgroup limit of 65,536),
 few-row shapes, every segment shape on the vector and scalar paths, mixed
-dtypes, in place, and bitwise reproducibility. The tolerances are the
-forward ones (softmax: 1e-5 relative / one bf16 ulp; cross-entropy: the rules
-of test_gpu_xent_ex)."""
+dtypes, in place, and bitwise reproducibility — the softmax and
+cross-entropy cases in both the one-pass (cooperative) and the two-pass form.
+The tolerances are the forward ones (softmax: 1e-5 relative / one bf16 ulp;
+cross-entropy: the rules of test_gpu_xent_ex)."""
 import numpy as np
 import pytest
 import torch
@@ -32,6 +33,14 @@ def softmax_input(code, R, C, seed):
 
 def workspace(R, C):
     return Guarded((max(fr.fr_split_workspace_bytes(R, C) // 4, 4),), torch.float32)
+
+
+@pytest.fixture(params=[2, 0], ids=["one-pass", "two-pass"])
+def form(request):
+    """Runs the test with the one-pass form wherever it applies (any row
+    count), then with the two passes only."""
+    with fr.split_cooperative(request.param):
+        yield request.param
 
 
 def run_softmax_split(x_np, out_code, offs=(0, 0), inplace=False):
@@ -62,13 +71,13 @@ WIDTHS = [1, 5, 1000, 8191, 8192, 8193, 32768, 50257, 65536, 65537, 100000, 2621
 
 @pytest.mark.parametrize("C", WIDTHS)
 @pytest.mark.parametrize("xin,yout", [(0, 0), (1, 1), (0, 1), (1, 0)])
-def test_softmax_split_widths(C, xin, yout):
+def test_softmax_split_widths(C, xin, yout, form):
     for R in (1, 3):
         x = softmax_input(xin, R, C, seed=C + R)
         expect_softmax(x, yout, run_softmax_split(x, yout), f"split softmax {xin}->{yout} {R}x{C}")
 
 
-def test_softmax_split_one_million_columns():
+def test_softmax_split_one_million_columns(form):
     x = softmax_input(0, 2, 1 << 20, seed=77)
     expect_softmax(x, 0, run_softmax_split(x, 0), "split softmax 2x1048576")
     x = softmax_input(1, 2, 1 << 20, seed=78)
@@ -76,10 +85,13 @@ def test_softmax_split_one_million_columns():
 
 
 SEG_SHAPES = [(1024, 8), (512, 8), (256, 8), (1024, 4), (512, 4), (256, 4), (256, 32)]
+# the softmax / cross-entropy table: 512 x 16 (fp32) and 512 x 8 (fp32 and bf16)
+# hold 64 bytes per lane; no 256 x 4
+SPLIT_SHAPES = [(1024, 8), (512, 8), (256, 8), (1024, 4), (512, 4), (512, 16), (256, 32)]
 
 
-@pytest.mark.parametrize("t,v", SEG_SHAPES)
-def test_every_segment_shape(t, v):
+@pytest.mark.parametrize("t,v", SPLIT_SHAPES)
+def test_every_segment_shape(t, v, form):
     ran = 0
     for code in (fr.F32, fr.BF16):
         for vp, offs in ((True, (0, 0)), (False, (1, 2))):
@@ -105,7 +117,7 @@ def test_every_segment_shape(t, v):
         pytest.skip(f"no split shape ({t}, {v})")
 
 
-def test_softmax_split_misaligned_and_in_place():
+def test_softmax_split_misaligned_and_in_place(form):
     for offs in ((1, 1), (3, 3), (1, 0)):
         x = softmax_input(0, 3, 70001, seed=5)
         expect_softmax(x, 0, run_softmax_split(x, 0, offs), f"split softmax offs {offs}")
@@ -113,7 +125,7 @@ def test_softmax_split_misaligned_and_in_place():
     expect_softmax(x, 1, run_softmax_split(x, 1, inplace=True), "split softmax in place")
 
 
-def test_special_rows():
+def test_special_rows(form):
     C = 100000
     rng = np.random.default_rng(9)
     x = rng.normal(0, 3, size=(4, C)).astype(np.float32)
@@ -156,14 +168,14 @@ XOPTS = [dict(), dict(ignore_index=-100, label_smoothing=0.1, reduction="mean", 
 
 @pytest.mark.parametrize("C", [1, 7, 50257, 65537, 131072, 262144])
 @pytest.mark.parametrize("code", [fr.F32, fr.BF16])
-def test_xent_split_widths(C, code):
+def test_xent_split_widths(C, code, form):
     for k, opts in enumerate(XOPTS):
         x, lab = xent_inputs(4, C, code, seed=C + k, ignore_every=3 if opts else 0)
         expect_xent(x, lab, code, opts, run_xent_split(x, lab, code, opts, argmax=k != 1),
                     f"split xent {code} 4x{C} {opts}")
 
 
-def test_xent_split_vocabulary_256k():
+def test_xent_split_vocabulary_256k(form):
     # a 256K-vocabulary batch: 128 rows (33.5M logits), fp32 and bf16
     for code in (fr.F32, fr.BF16):
         x, lab = xent_inputs(128, 262144, code, seed=1234, ignore_every=7)
@@ -171,7 +183,7 @@ def test_xent_split_vocabulary_256k():
         expect_xent(x, lab, code, opts, run_xent_split(x, lab, code, opts), f"split xent 128x256K {code}")
 
 
-def test_xent_split_in_place_and_invalid_labels():
+def test_xent_split_in_place_and_invalid_labels(form):
     C = 100003
     x, lab = xent_inputs(5, C, fr.F32, seed=12)
     lab[:] = [-100, C, 0, C - 1, 50000]
@@ -181,13 +193,69 @@ def test_xent_split_in_place_and_invalid_labels():
                 "split xent in place")
 
 
-def test_split_bitwise_determinism():
+def test_split_bitwise_determinism(form):
     x, lab = xent_inputs(64, 200000, fr.BF16, seed=13, ignore_every=5)
     outs = []
     for _ in range(3):
         r = run_xent_split(x, lab, fr.BF16, dict(ignore_index=-100, reduction="mean"))
         outs.append((r[0].tobytes(), r[1].tobytes(), r[2].tobytes(), np.float32(r[3]).tobytes()))
     assert outs[0] == outs[1] == outs[2]
+
+
+def _softmax_split_ws(x_np, ws):
+    R, C = x_np.shape
+    y = Guarded((R, C), torch.float32)
+    fr.fr_softmax_fwd_split(upload(x_np), y.t, ws.t)
+    torch.cuda.synchronize()
+    assert y.canaries_intact() and ws.canaries_intact()
+    return host(y.t)
+
+
+def test_one_pass_form_runs():
+    """White-box: the one-pass form of [64, 131072] fp32 (segments of 32768:
+    64 rows x 4 work items) leaves its ticket counter at 256 (every
+    workgroup took one), the abort word at 0, and in the slot of (row r,
+    segment j) the word {m, s} of that segment — m its maximum, s >= 1. The
+    two passes (segments of 8192) leave row 0's first segment state (max,
+    sum, ...) at the start of the workspace instead."""
+    R, C = 64, 131072
+    x = softmax_input(fr.F32, R, C, seed=41)
+    seg_max = lambda r, j, n: x[r, j * n:(j + 1) * n].max().view(np.uint32)
+    for mode in (2, 0):
+        with fr.split_cooperative(mode):
+            ws = workspace(R, C)
+            got = _softmax_split_ws(x, ws)
+        expect_softmax(x, fr.F32, got, f"split softmax {R}x{C} mode {mode}")
+        words = ws.t.cpu().numpy().view(np.uint32)
+        if mode:
+            assert (words[0], words[1]) == (R * 4, 0), words[:4]
+            for r, j in ((0, 0), (5, 3), (63, 2)):
+                k = 4 + 4 * (r * 4 + j)
+                assert words[k] == seg_max(r, j, 32768), (r, j, words[k:k + 4])
+                assert words[k + 1] >= np.float32(1.0).view(np.uint32)
+        else:
+            assert words[0] == seg_max(0, 0, 8192), words[:4]
+            assert words[1] >= np.float32(1.0).view(np.uint32)       # the exponential sum
+
+
+def test_one_pass_wait_bound():
+    """The bounded wait, forced to give up: with the poll bound at 0 a member
+    gives up whenever its first poll does not find every state of its row
+    (and every later wait gives up once one has). The launch still ends, and
+    each row is either the oracle's or holds NaN (a member that gave up);
+    the next call, with the default bound, is right throughout (its slots
+    and abort word are cleared again)."""
+    R, C = 96, 131072
+    x = softmax_input(fr.F32, R, C, seed=42)
+    with fr.split_cooperative(2):
+        with fr.coop_spin_limit(0):
+            got = _softmax_split_ws(x, workspace(R, C))
+        nan_rows = np.isnan(got).any(axis=1)
+        print(f"rows with NaN after forced give-ups: {int(nan_rows.sum())} of {R}", flush=True)
+        keep = np.flatnonzero(~nan_rows)
+        if keep.size:
+            expect_softmax(x[keep], fr.F32, got[keep], "split softmax, rows not given up")
+        expect_softmax(x, fr.F32, _softmax_split_ws(x, workspace(R, C)), "split softmax after")
 
 
 def test_convenience_routes_wide_rows():
@@ -515,8 +583,8 @@ def _bits(*arrays):
 
 @pytest.mark.parametrize("batch_rows", [1, 3, 64])
 def test_split_row_batches(batch_rows):
-    """The two-pass launches run both passes over one batch of rows at a time
-    (bounded by input bytes): batches of 1 and 3 rows (a ragged last batch of
+    """The two-pass launches (the one-pass form switched off) run both passes
+    over one batch of rows at a time (bounded by input bytes): batches of 1 and 3 rows (a ragged last batch of
     7 rows) and one batch of all of them, for every split entry point. Each
     result matches the oracle and has the same bits as the unbatched call."""
     R = 7
@@ -549,9 +617,9 @@ def test_split_row_batches(batch_rows):
                   lambda got: expect_softmax_bwd(p, dy, fr.BF16, got[0], "split softmax_bwd batches")))
     for name, row_bytes, run, expect in cases:
         print(f"row batches of {batch_rows}: {name}", flush=True)
-        with fr.split_batch_bytes(batch_rows * row_bytes):
+        with fr.split_cooperative(0), fr.split_batch_bytes(batch_rows * row_bytes):
             got = run()
-        with fr.split_batch_bytes(0):
+        with fr.split_cooperative(0), fr.split_batch_bytes(0):
             whole = run()
         expect(got)
         assert _bits(*got) == _bits(*whole), f"{name}: batched and unbatched results differ"

@@ -251,7 +251,10 @@ FR_API fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labe
  * writes each segment's exact (count, mean, M2) to `workspace`, pass 2 merges
  * a row's partials in segment order with the pairwise (Chan) merge of the
  * Welford moments and writes the segment's y (and, from the row's first
- * segment, mean and rstd). Reads x twice, writes y once.
+ * segment, mean and rstd). Reads x twice, writes y once. (The one-pass
+ * form of fr_softmax_fwd_split only with fr_debug_set_split_cooperative(2):
+ * it measured no faster here, the apply step reading gamma and beta for
+ * every row segment.)
  *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.2
  *    Welford Single-Pass Normalization: partial moments merged pairwise.)
  * Arguments and results as fr_layernorm_fwd, with 1 <= cols <=
@@ -262,10 +265,10 @@ FR_API fr_status_t fr_layernorm_fwd_split(const void* x, const void* gamma, cons
                                           void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Residual add + RMSNorm for rows of any width, split as
- * fr_softmax_fwd_split: pass 1 writes each segment's sum of h^2
- * (h = x + residual in fp32) to `workspace`, pass 2 adds a row's partials in
- * segment order, re-reads x and residual and writes residual_out and y.
- * Reads x and residual twice, writes each output once.
+ * fr_softmax_fwd_split, in one pass or two: each segment's sum of h^2
+ * (h = x + residual in fp32) is taken, a row's sums are added in segment
+ * order, and residual_out and y are written — in the one-pass form from the
+ * registers (x and residual read once), in two passes after a second read.
  *   ("NexusGrad", Core Capabilities: RMSNorm, residual blocks.)
  * Arguments and results as fr_add_rmsnorm_fwd (residual_out may equal
  * residual, y may equal x), with 1 <= cols <= FR_SPLIT_MAX_COLS, plus the
@@ -276,10 +279,11 @@ FR_API fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual,
                                             fr_dtype_t dtype, void* workspace,
                                             int64_t workspace_bytes, void* stream);
 
-/* Softmax backward for rows of any width, split as fr_softmax_fwd_split:
- * pass 1 writes each segment's sum of p * dy to `workspace`, pass 2 adds a
- * row's sums in segment order and writes dx = p (dy - s). Reads p and dy
- * twice, writes dx once.
+/* Softmax backward for rows of any width, split as fr_softmax_fwd_split,
+ * in one pass or two: each segment's sum of p * dy is taken, a row's sums
+ * are added in segment order and dx = p (dy - s) is written — in the
+ * one-pass form from the registers (p and dy read once), in two passes
+ * after a second read.
  *   ("NexusGrad", Verified VJP Operators: the softmax vector-Jacobian
  *    product.)
  * Arguments and results as fr_softmax_bwd (dx may equal p or dy), with
@@ -530,11 +534,13 @@ FR_API fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs);
  * for tests and tuning; not synchronised with concurrent calls. */
 FR_API int64_t fr_debug_set_split_batch_bytes(int64_t bytes);
 
-/* The one-pass form of fr_softmax_fwd_split and fr_softmax_xent_split:
- * mode 0 always runs the two passes; mode 1 (the default) takes the
- * one-pass form where it applies and the rows give at least 4 work items
- * per compute unit; mode 2 takes it wherever it applies (any row count, and
- * with a forced variant, whose shape it keeps); other values mean 1.
+/* The one-pass form of the split entry points (fr_softmax_fwd_split,
+ * fr_softmax_xent_split, fr_add_rmsnorm_fwd_split, fr_softmax_bwd_split;
+ * fr_layernorm_fwd_split in mode 2 only): mode 0 always runs the two
+ * passes; mode 1 (the default) takes the one-pass form where it applies and
+ * the rows give at least 4 work items per compute unit; mode 2 takes it
+ * wherever it applies (any row count, and with a forced variant, whose
+ * shape it keeps); other values mean 1.
  * Results do not depend on it beyond rounding (both merge the same kind of
  * segment states in segment order, the one-pass form by a fixed DPP tree).
  * Returns the previous setting. Process-wide setting meant for tests and

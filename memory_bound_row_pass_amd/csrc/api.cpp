@@ -129,34 +129,45 @@ const V* select_split(VariantSpan<V> sp, int op, int epv) {
   return nullptr;
 }
 
-// Split softmax / cross-entropy: shape and form. A forced (threads, vecs)
-// keeps its shape and takes the one-pass form wherever that applies (setting
-// != 0). Otherwise the one-pass shape (512 lanes x 64 elements: segments of
-// 32768 columns) in the one-pass form, for rows of at most 64 such segments
-// when (setting 1) the rows give at least 4 work items per compute unit —
-// below that, two passes over the table's first (smallest) segments measured
-// faster (fp32 [96, 131072] 39.1 against 36.9 us; [288, 131072] 77.8
-// against 81.1 us) — or (setting 2) always; else the table's first shape,
-// in two passes. rows < 0: a single row.
+// Split-row shape and form. A forced (threads, vecs) keeps its shape and
+// takes the one-pass form wherever that applies (setting != 0). Otherwise
+// the op's one-pass shape (512 lanes x `elems` elements) in the one-pass
+// form, for rows of at most 64 such segments, when (setting 1) the rows
+// give at least 4 work items per compute unit — below that, two passes over
+// the table's first (smallest) segments measured faster (cross-entropy fp32
+// [96, 131072] 39.1 against 36.9 us; [288, 131072] 77.8 against 81.1 us) —
+// or (setting 2) always; else the table's first shape, in two passes.
+// rows < 0: a single row.
+template <typename V>
 struct SplitChoice {
-  const fr::SplitVariant* v;
+  const V* v;
   bool one_pass;
 };
-SplitChoice choose_split(VariantSpan<fr::SplitVariant> sp, int op, int epv, int64_t rows,
-                         int64_t cols) {
+template <typename V>
+SplitChoice<V> choose_split(VariantSpan<V> sp, int op, int epv, int64_t rows, int64_t cols,
+                            int elems) {
   const int mode = fr::split_cooperative();
   if (g_forced[op].threads.load(std::memory_order_relaxed)) return {select_split(sp, op, epv), mode != 0};
-  if (mode != 0) {
-    const int64_t nseg = (cols + 32767) / 32768;
+  if (mode != 0 && elems > 0) {
+    const int64_t nseg = (cols + 512 * elems - 1) / (512 * elems);
     const int64_t r = rows < 0 ? 1 : rows;
     if (nseg <= fr::kCoopMaxSegments && (mode == 2 || r * nseg >= 4 * fr::device_cu_count()))
       for (size_t i = 0; i < sp.n; ++i) {
-        const fr::SplitVariant& v = sp.v[i];
-        if (v.epv == epv && v.threads == 512 && v.nv * v.epv == 64) return {&v, true};
+        const V& v = sp.v[i];
+        if (v.epv == epv && v.threads == 512 && v.nv * v.epv == elems) return {&v, true};
       }
   }
   return {select_split(sp, op, epv), mode == 2};
 }
+// Elements per lane of the one-pass shape of the softmax, cross-entropy,
+// residual-add + RMSNorm and softmax backward (measured against 32 at 512
+// lanes: RMSNorm bf16 [256, 262144] 110 against 118 us, softmax backward
+// bf16 [256, 131072] 52 against 56 us). The LayerNorm takes no one-pass
+// shape by default (elems 0): its apply step reads gamma and beta for every
+// row segment, and in one pass it measured 123 against 131 us (fp32
+// [512, 131072], 32 elements; 129 with 64) and 84 against 81 us (bf16).
+constexpr int kOnePassElems = 64;
+constexpr int kOnePassElemsLn = 0;
 
 thread_local int t_last_launch_error = 0;
 
@@ -296,19 +307,21 @@ fr_status_t describe_variant(fr_op_t op, int64_t rows, int64_t cols, fr_dtype_t 
     case FR_OP_XENT_SPLIT: {
       auto v = choose_split(fr::split_variants(in_dtype == FR_BF16, out_dtype == FR_BF16,
                                                op == FR_OP_XENT_SPLIT),
-                            op, epv, rows, cols).v;
+                            op, epv, rows, cols, kOnePassElems).v;
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
     case FR_OP_SOFTMAX_BWD_SPLIT: {
-      auto v = select_split(fr::softmax_bwd_split_variants(in_dtype == FR_BF16), op, epv);
+      auto v = choose_split(fr::softmax_bwd_split_variants(in_dtype == FR_BF16), op, epv, rows, cols,
+                            kOnePassElems).v;
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
     case FR_OP_LAYERNORM_SPLIT:
     case FR_OP_RMSNORM_SPLIT: {
-      auto v = select_split(fr::norm_split_variants(in_dtype == FR_BF16, op == FR_OP_RMSNORM_SPLIT),
-                            op, epv);
+      auto v = choose_split(fr::norm_split_variants(in_dtype == FR_BF16, op == FR_OP_RMSNORM_SPLIT),
+                            op, epv, rows, cols,
+                            op == FR_OP_RMSNORM_SPLIT ? kOnePassElems : kOnePassElemsLn).v;
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -779,8 +792,8 @@ fr_status_t fr_softmax_fwd_split(const void* x, void* y, int64_t rows, int64_t c
   bool vec;
   if (xs == ys) vec = (reinterpret_cast<uintptr_t>(x) % 16) == (reinterpret_cast<uintptr_t>(y) % 16);
   else vec = aligned(x, 16) && aligned(y, 16) && cols % ve == 0;
-  const SplitChoice c = choose_split(fr::split_variants(x_dtype == FR_BF16, y_dtype == FR_BF16, 0),
-                                     FR_OP_SOFTMAX_SPLIT, vec ? ve : 1, rows, cols);
+  const auto c = choose_split(fr::split_variants(x_dtype == FR_BF16, y_dtype == FR_BF16, 0),
+                              FR_OP_SOFTMAX_SPLIT, vec ? ve : 1, rows, cols, kOnePassElems);
   if (!c.v) return FR_E_VARIANT;
   return launch_status(c.v->launch(x, y, rows, (int)cols, nullptr, nullptr, nullptr, nullptr,
                                    static_cast<float4*>(workspace),
@@ -828,8 +841,8 @@ fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labels, flo
   if (fr_status_t s = check_alias(bufs, 7)) return s;
   const bool vec =
       (reinterpret_cast<uintptr_t>(logits) % 16) == (reinterpret_cast<uintptr_t>(grad) % 16);
-  const SplitChoice c = choose_split(fr::split_variants(dtype == FR_BF16, dtype == FR_BF16, 1),
-                                     FR_OP_XENT_SPLIT, vec ? vec_epv(es) : 1, rows, cols);
+  const auto c = choose_split(fr::split_variants(dtype == FR_BF16, dtype == FR_BF16, 1),
+                              FR_OP_XENT_SPLIT, vec ? vec_epv(es) : 1, rows, cols, kOnePassElems);
   if (!c.v) return FR_E_VARIANT;
   if (count)
     if (fr_status_t s = launch_status(
@@ -869,12 +882,13 @@ fr_status_t fr_layernorm_fwd_split(const void* x, const void* gamma, const void*
   if (fr_status_t s = check_alias(bufs, 7)) return s;
   const bool vec = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16) &&
                    (cols * es) % 16 == 0;
-  const fr::NormSplitVariant* v = select_split(fr::norm_split_variants(dtype == FR_BF16, 0),
-                                               FR_OP_LAYERNORM_SPLIT, vec ? vec_epv(es) : 1);
-  if (!v) return FR_E_VARIANT;
-  return launch_status(v->launch(x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, (int)cols,
-                                 eps, static_cast<float4*>(workspace),
-                                 static_cast<hipStream_t>(stream)));
+  const auto c = choose_split(fr::norm_split_variants(dtype == FR_BF16, 0), FR_OP_LAYERNORM_SPLIT,
+                              vec ? vec_epv(es) : 1, rows, cols, kOnePassElemsLn);
+  if (!c.v) return FR_E_VARIANT;
+  return launch_status(c.v->launch(x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, (int)cols,
+                                   eps, static_cast<float4*>(workspace),
+                                   fr_split_workspace_bytes(rows, cols), c.one_pass,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual, const void* weight,
@@ -900,12 +914,13 @@ fr_status_t fr_add_rmsnorm_fwd_split(const void* x, const void* residual, const 
   const bool vec = aligned(x, 16) && aligned(residual, 16) && aligned(weight, 16) &&
                    aligned(y, 16) && (!residual_out || aligned(residual_out, 16)) &&
                    (cols * es) % 16 == 0;
-  const fr::NormSplitVariant* v = select_split(fr::norm_split_variants(dtype == FR_BF16, 1),
-                                               FR_OP_RMSNORM_SPLIT, vec ? vec_epv(es) : 1);
-  if (!v) return FR_E_VARIANT;
-  return launch_status(v->launch(x, residual, weight, nullptr, y, residual_out, nullptr, nullptr,
-                                 rows, (int)cols, eps, static_cast<float4*>(workspace),
-                                 static_cast<hipStream_t>(stream)));
+  const auto c = choose_split(fr::norm_split_variants(dtype == FR_BF16, 1), FR_OP_RMSNORM_SPLIT,
+                              vec ? vec_epv(es) : 1, rows, cols, kOnePassElems);
+  if (!c.v) return FR_E_VARIANT;
+  return launch_status(c.v->launch(x, residual, weight, nullptr, y, residual_out, nullptr, nullptr,
+                                   rows, (int)cols, eps, static_cast<float4*>(workspace),
+                                   fr_split_workspace_bytes(rows, cols), c.one_pass,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 fr_status_t fr_softmax_bwd_split(const void* p, const void* dy, void* dx, int64_t rows,
@@ -925,11 +940,13 @@ fr_status_t fr_softmax_bwd_split(const void* p, const void* dy, void* dx, int64_
   const uintptr_t ph = reinterpret_cast<uintptr_t>(p) % 16;
   const bool vec = reinterpret_cast<uintptr_t>(dy) % 16 == ph &&
                    reinterpret_cast<uintptr_t>(dx) % 16 == ph;
-  const fr::SoftmaxBwdSplitVariant* v = select_split(
-      fr::softmax_bwd_split_variants(dtype == FR_BF16), FR_OP_SOFTMAX_BWD_SPLIT, vec ? vec_epv(es) : 1);
-  if (!v) return FR_E_VARIANT;
-  return launch_status(v->launch(p, dy, dx, rows, (int)cols, static_cast<float4*>(workspace),
-                                 static_cast<hipStream_t>(stream)));
+  const auto c = choose_split(fr::softmax_bwd_split_variants(dtype == FR_BF16),
+                              FR_OP_SOFTMAX_BWD_SPLIT, vec ? vec_epv(es) : 1, rows, cols,
+                              kOnePassElems);
+  if (!c.v) return FR_E_VARIANT;
+  return launch_status(c.v->launch(p, dy, dx, rows, (int)cols, static_cast<float4*>(workspace),
+                                   fr_split_workspace_bytes(rows, cols), c.one_pass,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 fr_status_t fr_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

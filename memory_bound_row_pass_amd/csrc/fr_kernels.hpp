@@ -159,11 +159,12 @@ typedef hipError_t (*SplitLaunch)(const void* x, void* y, int64_t rows, int cols
 typedef hipError_t (*NormSplitLaunch)(const void* x, const void* res, const void* p1,
                                       const void* p2, void* y, void* res_out, float* mean,
                                       float* rstd, int64_t rows, int cols, float eps, float4* part,
-                                      hipStream_t s);
+                                      int64_t part_bytes, bool one_pass, hipStream_t s);
 
 // Split-row softmax backward (pass 1 segment sums of p * dy into `part`).
 typedef hipError_t (*SoftmaxBwdSplitLaunch)(const void* p, const void* dy, void* dx, int64_t rows,
-                                            int cols, float4* part, hipStream_t s);
+                                            int cols, float4* part, int64_t part_bytes,
+                                            bool one_pass, hipStream_t s);
 
 typedef Variant<SoftmaxLaunch> SoftmaxVariant;
 typedef Variant<LayerNormLaunch> LayerNormVariant;

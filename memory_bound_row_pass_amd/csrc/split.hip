@@ -23,6 +23,7 @@
 // one launch with pass 2 of the batch before and pass 1 of this one
 // (split_apply_stats_kernel; they touch different rows), then pass 2 of the
 // last. The softmax backward runs two passes (its per-row sum s = sum p dy).
+#include "coop.hpp"
 #include "fr_kernels.hpp"
 #include "softmax_core.hpp"
 
@@ -213,16 +214,16 @@ __device__ __forceinline__ float split_p(float xv, float M, float fac, float b) 
 }
 
 // Writes the segment's outputs from its logits v (and xe) and the row's
-// merged state st: p, or the cross-entropy gradient with the row's loss
-// (from the lane owning the label column) and argmax (from segment 0).
+// merged state st (inv_s = 1 / st.s): p, or the cross-entropy gradient with
+// the row's loss (from the lane owning the label column) and argmax (from
+// segment 0).
 template <typename Tin, typename Tout, int T, int NV, int EPV, bool XENT, typename G>
 __device__ __forceinline__ void segment_apply(float (&v)[NV][EPV], float xe, int ec, const G& g,
                                               const Segment& sgm, const Tin* xs, Tout* ys,
-                                              const SplitState& st, int label, float gsc,
-                                              float goff, const XentOptions& opt, float* loss,
-                                              int32_t* argmax, int64_t row, int sg, int cols,
-                                              int tid) {
-  const float inv_s = 1.f / st.s;
+                                              const SplitState& st, float inv_s, int label,
+                                              float gsc, float goff, const XentOptions& opt,
+                                              float* loss, int32_t* argmax, int64_t row, int sg,
+                                              int cols, int tid) {
   // label column handled by the lane of this segment that owns it
   bool label_lane = false;
   float x_label = 0.f;
@@ -322,11 +323,12 @@ __device__ __forceinline__ void split_apply_body(const Tin* x, Tout* y, int64_t 
     }
 
     const SplitState st = merge_row<T>(part, row, nseg, xw[merges++ & 1], wave, lane, tid);
+    const float inv_s = 1.f / st.s;
     float v[NV][EPV];
     load_chunks<Tin, T, NV, EPV>(xs, g, tid, v, kNegInf);
     const float xe = load_extra(xs, ec, kNegInf);
-    segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, label, gsc, goff, opt,
-                                              loss, argmax, row, sg, cols, tid);
+    segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, inv_s, label, gsc, goff,
+                                              opt, loss, argmax, row, sg, cols, tid);
   }
 }
 
@@ -367,76 +369,16 @@ void split_apply_stats_kernel(SplitBatch a, SplitBatch n, int cols, int seg, int
 
 // ---------------------------------------------------------- one-pass form
 // One workgroup per (row, segment) work item, as in the two passes, but the
-// row's workgroups wait for each other: each loads its segment into
-// registers and takes its state as pass 1 does, posts the state, waits for
-// the states of the row's other segments, merges all nseg of them in segment
-// order (every workgroup of the row gets the same bits) and writes its
-// outputs from the registers as pass 2 does after its second read: the input
-// is read once.
-//
-// Work items are handed out in start order: a workgroup takes the next
-// ticket from a device-scope counter when it starts, and ticket w is row
-// w / nseg, segment w % nseg. So the started workgroups always hold the
-// lowest tickets, every row below the lowest unfinished one has finished,
-// and that row's missing segments only need free room on the device for
-// their workgroups (rows of at most 64 segments): the waits end however the
-// hardware orders, places or delays the workgroups.
-// Posting: the state as one or two 64-bit device-scope atomic stores, word 0
-// = {m, s}, word 1 = {t, idx + 1} (with the options that need them), into
-// the segment's slot of the row; the slots are zeroed before the launch and
-// neither word is ever zero once posted (s >= 1 when m is finite; m = -inf
-// and NaN have non-zero bits; idx + 1 >= 1). Such stores go through to the
-// level all XCDs share without the whole-L2 write-back of a device-scope
-// release fence, and a reader sees a word either unposted or whole. Waiting:
-// lane NWD j + f of wave 0 reads word f of segment j (64 / NWD segments per
-// round) with device-scope atomic loads until every word is posted.
-// Bounded: after spin_limit polls (each after a short sleep), or once
-// another wait has given up (the abort word), a workgroup takes NaN for the
-// missing states — its outputs of that row are NaN — and sets the abort
-// word; the kernel always ends.
+// row's workgroups wait for each other (the exchange of coop.hpp): each
+// loads its segment into registers and takes its state as pass 1 does,
+// posts word 0 = {m, s} and, with the options that need them, word 1 =
+// {t, idx + 1} (neither is ever zero: s >= 1 when m is finite, -inf and NaN
+// have non-zero bits, idx + 1 >= 1), waits for the row's other states,
+// merges all nseg of them in segment order (lane j holds segment j's, one
+// DPP tree: every workgroup of the row gets the same bits) and writes its
+// outputs from the registers as pass 2 does after its second read: the
+// input is read once.
 
-// Wave 0: waits for word f < NWD of segment j < nseg of the row's slots
-// ([nseg][2] words) and leaves segment j's state in team[j].
-template <int NWD>
-__device__ __forceinline__ void coop_wait(const uint64_t* slots, int nseg, uint32_t* abort_word,
-                                          int spin_limit, int lane, float (*team)[4]) {
-  constexpr int PER = 64 / NWD;  // segments per round
-  const int f = lane % NWD;
-  for (int j0 = 0; j0 < nseg; j0 += PER) {
-    const int j = j0 + lane / NWD;
-    const bool live = j < nseg;
-    uint64_t word = 0;
-    bool have = !live;
-    for (int spins = 0;; ++spins) {
-      if (!have) {
-        word = __hip_atomic_load(slots + (size_t)j * 2 + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        have = word != 0;
-      }
-      if (__builtin_amdgcn_ballot_w64(!have) == 0) break;
-      bool give_up = spins >= spin_limit;
-      if ((spins & 15) == 15)
-        give_up = give_up ||
-                  __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-      if (__builtin_amdgcn_readfirstlane((int)give_up)) {
-        if (lane == 0) __hip_atomic_store(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (live) {
-      const float lo = have ? __builtin_bit_cast(float, (uint32_t)word) : __builtin_nanf("");
-      const float hi = have ? __builtin_bit_cast(float, (uint32_t)(word >> 32)) : __builtin_nanf("");
-      team[j][2 * f] = lo;
-      team[j][2 * f + 1] = f == 1 ? hi - 1.f : hi;  // idx + 1 -> idx (exact below 2^24)
-    }
-  }
-}
-
-__device__ __forceinline__ uint64_t coop_word(float lo, float hi) {
-  return ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32) | __builtin_bit_cast(uint32_t, lo);
-}
-
-// ctl[0]: the ticket counter, ctl[1]: the abort word; slots: [rows][nseg][2].
 template <typename Tin, typename Tout, int T, int NV, int EPV, int OCC, bool XENT, int STATS>
 __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
 void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, int nseg,
@@ -450,13 +392,11 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
-  if (tid == 0) ticket = __hip_atomic_fetch_add(ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (NWD == 1) {  // the fields not posted
+  if constexpr (NWD == 1) {  // the fields not posted: t = 0, idx + 1 = 3e38
     team[lane][2] = 0.f;
     team[lane][3] = 3.0e38f;
   }
-  lds_barrier();
-  const int64_t w = __builtin_amdgcn_readfirstlane(ticket);  // < rows * nseg: one per workgroup
+  const int64_t w = coop_ticket(ctl, &ticket);  // < rows * nseg: one per workgroup
   const int64_t row = w / nseg;
   const int sg = (int)(w - row * nseg);
   const Segment sgm(sg, seg, cols);
@@ -499,16 +439,14 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
   const SplitState mine = segment_state<T, NV, EPV, STATS>(v, xe, ec, g, sgm.c0, tid, wave, lane,
                                                            xw[0]);
   uint64_t* row_slots = slots + (size_t)row * nseg * 2;
-  if (tid < NWD)
-    __hip_atomic_store(row_slots + (size_t)sg * 2 + tid,
-                       tid == 0 ? coop_word(mine.m, mine.s) : coop_word(mine.t, mine.idx + 1.f),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  coop_post<NWD>(row_slots, sg, coop_word(mine.m, mine.s), coop_word(mine.t, mine.idx + 1.f));
   if (wave == 0) coop_wait<NWD>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
   lds_barrier();
   // the row's state: lane j < nseg holds segment j's, one DPP tree (the same
-  // in every wave of every workgroup of the row)
+  // in every wave of every workgroup of the row); idx + 1 -> idx is exact
+  // below 2^24
   SplitState st{kNegInf, 0.f, 0.f, 3.0e38f};
-  if (lane < nseg) st = SplitState{team[lane][0], team[lane][1], team[lane][2], team[lane][3]};
+  if (lane < nseg) st = SplitState{team[lane][0], team[lane][1], team[lane][2], team[lane][3] - 1.f};
   st = wave_reduce(st, SplitMerge{});
 
   if (ignored) {  // with argmax: the row's argmax, a zero gradient, loss 0
@@ -524,14 +462,20 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
     }
     return;
   }
-  segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, label, gsc, goff, opt,
-                                            loss, argmax, row, sg, cols, tid);
+  segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, 1.f / st.s, label, gsc,
+                                            goff, opt, loss, argmax, row, sg, cols, tid);
 }
 
 // Zeroes n 16-byte words (the one-pass form's counter, abort word and slots).
 __global__ __launch_bounds__(256) void coop_clear_kernel(uint4* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_coop_clear(void* ws, int64_t rows, int nseg, hipStream_t s) {
+  const int64_t n16 = coop_workspace_bytes(rows, nseg) / 16;
+  return launch_kernel(&coop_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), s,
+                       static_cast<uint4*>(ws), n16);
 }
 
 // ------------------------------------------------ softmax backward, split
@@ -641,6 +585,62 @@ void softmax_bwd_split_apply_stats_kernel(const Ts* p, const Ts* dy, Ts* dx, int
                                                  blockIdx.x - n_apply, gridDim.x - n_apply);
 }
 
+// One-pass form of the softmax backward (the exchange of coop.hpp): each
+// workgroup loads its segment of p and dy into registers, posts {sum of
+// p dy over the segment, 1} (never zero), waits for the row's other sums,
+// adds them in segment order (lane j holds segment j's, one DPP tree: the
+// same bits in every workgroup of the row) and writes dx = p (dy - s) from
+// the registers. dx may be p or dy: a workgroup writes only its own segment,
+// after reading it.
+template <typename Ts, int T, int NV, int EPV, int OCC>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void softmax_bwd_split_coop_kernel(const Ts* p, const Ts* dy, Ts* dx, int64_t rows, int cols,
+                                   int seg, int nseg, uint64_t* slots, uint32_t* ctl,
+                                   int spin_limit) {
+  constexpr int NW = T / 64;
+  __shared__ float xw[2][NW][1];
+  __shared__ float team[kCoopMaxSegments][4];
+  __shared__ uint32_t ticket;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t w = coop_ticket(ctl, &ticket);  // < rows * nseg: one per workgroup
+  const int64_t row = w / nseg;
+  const int sg = (int)(w - row * nseg);
+  const Segment sgm(sg, seg, cols);
+  const int64_t off = row * cols + sgm.c0;
+  const RowGeom<EPV> g(p + off, sgm.len);
+  const int ec = g.extra_col(tid);
+  float a[NV][EPV], d[NV][EPV];
+  load_chunks2<Ts, T, NV, EPV>(p + off, dy + off, g, tid, a, d, 0.f);
+  const float ae = load_extra(p + off, ec, 0.f), de = load_extra(dy + off, ec, 0.f);
+  float s0 = ae * de, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) {
+      if (k & 1) s1 = __builtin_fmaf(a[i][k], d[i][k], s1);
+      else s0 = __builtin_fmaf(a[i][k], d[i][k], s0);
+    }
+  SumState st{s0 + s1};
+  st = wave_reduce(st, SumMerge{});
+  if constexpr (NW > 1) st = block_merge<NW>(st, xw[0], wave, lane, SumMerge{});
+  uint64_t* row_slots = slots + (size_t)row * nseg * 2;
+  coop_post<1>(row_slots, sg, coop_word(st.s, 1.f), 0);
+  if (wave == 0) coop_wait<1>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+  lds_barrier();
+  SumState tot{0.f};
+  if (lane < nseg) tot = SumState{team[lane][0]};
+  tot = wave_reduce(tot, SumMerge{});
+  const float s = tot.s;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) a[i][k] = a[i][k] * (d[i][k] - s);
+  store_chunks<Ts, T, NV, EPV>(dx + off, g, tid, a);
+  if (ec >= 0) store1(dx + off + ec, ae * (de - s));
+}
+
 // --------------------------------------------------------------- launchers
 
 static unsigned split_grid(int64_t work) {
@@ -654,9 +654,7 @@ template <typename Tin, typename Tout, typename K>
 static hipError_t launch_coop(K kernel, int nseg, int T, float4* part, hipStream_t s, const Tin* x,
                               Tout* y, int64_t rows, int cols, int seg, const int32_t* labels,
                               float* loss, int32_t* argmax, XentOptions o, int skip) {
-  const int64_t n16 = coop_workspace_bytes(rows, nseg) / 16;
-  hipError_t e = launch_kernel(&coop_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), s,
-                               reinterpret_cast<uint4*>(part), n16);
+  hipError_t e = launch_coop_clear(part, rows, nseg, s);
   if (e != hipSuccess) return e;
   uint32_t* ctl = reinterpret_cast<uint32_t*>(part);
   uint64_t* slots = reinterpret_cast<uint64_t*>(part + 1);
@@ -719,12 +717,21 @@ static hipError_t launch_split(const void* x, void* y, int64_t rows, int cols, c
 
 template <typename Ts, int T, int NV, int EPV, int OCC>
 static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* dx, int64_t rows,
-                                           int cols, float4* part, hipStream_t s) {
+                                           int cols, float4* part, int64_t part_bytes, bool one_pass,
+                                           hipStream_t s) {
   constexpr int SEG = T * NV * EPV;
   const int nseg = (cols + SEG - 1) / SEG;
   const Ts* pi = static_cast<const Ts*>(p);
   const Ts* di = static_cast<const Ts*>(dy);
   Ts* xo = static_cast<Ts*>(dx);
+  if (one_pass && coop_applies(rows, nseg, part_bytes)) {
+    hipError_t e = launch_coop_clear(part, rows, nseg, s);
+    if (e != hipSuccess) return e;
+    return launch_kernel(&softmax_bwd_split_coop_kernel<Ts, T, NV, EPV, OCC>,
+                         dim3((unsigned)(rows * nseg)), dim3(T), s, pi, di, xo, rows, cols, SEG, nseg,
+                         reinterpret_cast<uint64_t*>(part + 1), reinterpret_cast<uint32_t*>(part),
+                         coop_spin_limit());
+  }
   const int64_t batch = split_batch_rows(rows, (int64_t)cols * 2 * sizeof(Ts));
   // pass 1 of the first batch; per further batch, pass 2 of the one before
   // with pass 1 of this one; then pass 2 of the last
@@ -752,10 +759,12 @@ static hipError_t launch_softmax_bwd_split(const void* p, const void* dy, void* 
 
 #define FR_SP(TI, TO, T, NV, EPV, OCC, X) {T, NV, EPV, &launch_split<TI, TO, T, NV, EPV, OCC, X>}
 // Segment shapes: 256 lanes x 8 chunks (32 KiB segments, 8192 fp32 or 16384
-// bf16 columns, the default: several workgroups per CU overlap one segment's
-// loads with another's arithmetic; bf16 1024 x 262144 with 8 KiB-column
-// segments of 16 KiB measured 286 -> 270 us), 512 and 1024 lanes x 32
-// elements; the scalar path (unaligned phases) 256 lanes x 32 elements.
+// bf16 columns, the two passes' default: several workgroups per CU overlap
+// one segment's loads with another's arithmetic; bf16 1024 x 262144 with
+// 8 KiB-column segments of 16 KiB measured 286 -> 270 us), 512 and 1024
+// lanes x 32 elements, 512 lanes x 64 elements (32768 columns: the one-pass
+// default, the waits fewer and each workgroup's share larger); the scalar
+// path (unaligned phases) 256 lanes x 32 elements.
 #define FR_SP_TABLE(TI, TO, E, X)                                                           \
   {FR_SP(TI, TO, 256, 8, E, 4, X),       FR_SP(TI, TO, 512, 32 / E, E, 4, X),                 \
    FR_SP(TI, TO, 1024, 32 / E, E, 4, X), FR_SP(TI, TO, 512, 64 / E, E, 4, X),                 \
@@ -768,10 +777,15 @@ static const SplitVariant kSpBf16F32[] = FR_SP_TABLE(bf16_t, float, 8, false);
 static const SplitVariant kSpXeF32[] = FR_SP_TABLE(float, float, 4, true);
 static const SplitVariant kSpXeBf16[] = FR_SP_TABLE(bf16_t, bf16_t, 8, true);
 
+// Softmax backward: as above; the 512 x 64 shape (the one-pass default)
+// holds p and dy, 128 values per lane, so it is built for 256 registers
+// (two waves per SIMD: with 128 it spilled).
 #define FR_SB_SPLIT(TS, T, NV, EPV) {T, NV, EPV, &launch_softmax_bwd_split<TS, T, NV, EPV, 4>}
+#define FR_SB_SPLIT2(TS, T, NV, EPV) {T, NV, EPV, &launch_softmax_bwd_split<TS, T, NV, EPV, 2>}
 #define FR_SB_SPLIT_TABLE(TS, E)                                                      \
   {FR_SB_SPLIT(TS, 256, 32 / E, E), FR_SB_SPLIT(TS, 512, 32 / E, E),                   \
-   FR_SB_SPLIT(TS, 1024, 32 / E, E), FR_SB_SPLIT(TS, 256, 32, 1)}
+   FR_SB_SPLIT(TS, 1024, 32 / E, E), FR_SB_SPLIT2(TS, 512, 64 / E, E),                 \
+   FR_SB_SPLIT(TS, 256, 32, 1)}
 static const SoftmaxBwdSplitVariant kSbSpF32[] = FR_SB_SPLIT_TABLE(float, 4);
 static const SoftmaxBwdSplitVariant kSbSpBf16[] = FR_SB_SPLIT_TABLE(bf16_t, 8);
 

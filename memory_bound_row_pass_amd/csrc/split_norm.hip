@@ -15,9 +15,12 @@
 //     its segment and writes y (and the updated residual, and the row's mean
 //     and rstd from segment 0).
 // The updated residual is written in pass 2, after its segment's residual has
-// been re-read, so residual_out may be the residual itself.
-#include "fr_kernels.hpp"
+// been re-read, so residual_out may be the residual itself. Both also have
+// the one-pass form of split.hip (norm_split_coop_kernel: the states
+// exchanged within one launch, the segment written from the registers).
+#include "coop.hpp"
 #include "fr_device.hpp"
+#include "fr_kernels.hpp"
 
 namespace fr {
 
@@ -256,18 +259,134 @@ void norm_split_apply_stats_kernel(const Ts* x, const Ts* res, const Ts* p1, con
   }
 }
 
+// ---------------------------------------------------------- one-pass form
+// One workgroup per (row, segment) work item exchanging its segment's state
+// with the row's others (coop.hpp) instead of a second read: it loads its
+// segment (and residual) into registers, takes the state as pass 1 does,
+// posts it — LayerNorm: word 0 = {mean, count} (count >= 1: never zero),
+// word 1 = {M2, 1}; RMSNorm: {sum of h^2, 1} — waits for the row's others,
+// merges them in segment order (lane j holds segment j's, one DPP tree: the
+// same bits in every workgroup of the row) and writes y (and the updated
+// residual, and the row's mean and rstd from segment 0) from the registers.
+// Each workgroup writes only its own segment, after reading it: y may be x
+// and residual_out the residual.
+template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(OCC)))
+void norm_split_coop_kernel(const Ts* x, const Ts* res, const Ts* p1, const Ts* p2, Ts* y,
+                            Ts* res_out, float* mean, float* rstd, int64_t rows, int cols, int seg,
+                            int nseg, float eps, uint64_t* slots, uint32_t* ctl, int spin_limit) {
+  constexpr int NW = T / 64;
+  constexpr int NWD = RMS ? 1 : 2;  // words posted per segment
+  __shared__ float xw[2][NW][RMS ? 1 : 3];
+  __shared__ float team[kCoopMaxSegments][4];
+  __shared__ uint32_t ticket;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t w = coop_ticket(ctl, &ticket);  // < rows * nseg: one per workgroup
+  const int64_t row = w / nseg;
+  const int sg = (int)(w - row * nseg);
+  const NormSegment sgm(sg, seg, cols);
+  const int64_t off = row * cols + sgm.c0;
+  const RowGeom<EPV> g(x + off, sgm.len);
+  const int ec = g.extra_col(tid);
+  const Ts* q1 = p1 + sgm.c0;
+  uint64_t* row_slots = slots + (size_t)row * nseg * 2;
+  float v[NV][EPV];
+  if constexpr (RMS) {
+    float r[NV][EPV];
+    load_chunks2<Ts, T, NV, EPV>(x + off, res + off, g, tid, v, r, 0.f);
+    const float he = load_extra(x + off, ec, 0.f) + load_extra(res + off, ec, 0.f);
+    float s0 = he * he, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        v[i][k] += r[i][k];  // h, in fp32
+        if (k & 1) s1 = __builtin_fmaf(v[i][k], v[i][k], s1);
+        else s0 = __builtin_fmaf(v[i][k], v[i][k], s0);
+      }
+    SumState st{s0 + s1};
+    st = wave_reduce(st, SumMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[0], wave, lane, SumMerge{});
+    coop_post<NWD>(row_slots, sg, coop_word(st.s, 1.f), 0);
+    if (wave == 0) coop_wait<NWD>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+    lds_barrier();
+    SumState tot{0.f};
+    if (lane < nseg) tot = SumState{team[lane][0]};
+    tot = wave_reduce(tot, SumMerge{});
+    const float rs = 1.f / __builtin_sqrtf(tot.s / (float)cols + eps);
+    if (res_out) {  // updated residual, rounded once at the store
+      store_chunks<Ts, T, NV, EPV>(res_out + off, g, tid, v);
+      if (ec >= 0) store1(res_out + off + ec, he);
+    }
+    if (g.nvec > 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float wt[EPV];
+        load_param_slot<Ts, T, EPV>(q1, g, tid, i, wt);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) v[i][k] = v[i][k] * rs * wt[k];
+      }
+      store_chunks<Ts, T, NV, EPV>(y + off, g, tid, v);
+    }
+    if (ec >= 0) store1(y + off + ec, he * rs * load1(q1 + ec));
+  } else {
+    load_chunks<Ts, T, NV, EPV>(x + off, g, tid, v, 0.f);
+    const float xe = load_extra(x + off, ec, 0.f);
+    WelfordState st = lane_moments<T, NV, EPV>(v, xe, ec, g, tid);
+    st = wave_reduce(st, WelfordMerge{});
+    if constexpr (NW > 1) st = block_merge<NW>(st, xw[0], wave, lane, WelfordMerge{});
+    coop_post<NWD>(row_slots, sg, coop_word(st.mu, st.n), coop_word(st.m2, 1.f));
+    if (wave == 0) coop_wait<NWD>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+    lds_barrier();
+    WelfordState tot{0.f, 0.f, 0.f};
+    if (lane < nseg) tot = WelfordState{team[lane][1], team[lane][0], team[lane][2]};
+    tot = wave_reduce(tot, WelfordMerge{});
+    const float mu = tot.mu;
+    const float rs = 1.f / __builtin_sqrtf(tot.m2 / (float)cols + eps);
+    const Ts* q2 = p2 + sgm.c0;
+    if (g.nvec > 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float ga[EPV], be[EPV];
+        load_param_slot<Ts, T, EPV>(q1, g, tid, i, ga);
+        load_param_slot<Ts, T, EPV>(q2, g, tid, i, be);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) v[i][k] = __builtin_fmaf((v[i][k] - mu) * rs, ga[k], be[k]);
+      }
+      store_chunks<Ts, T, NV, EPV>(y + off, g, tid, v);
+    }
+    if (ec >= 0) store1(y + off + ec, __builtin_fmaf((xe - mu) * rs, load1(q1 + ec), load1(q2 + ec)));
+    if (sg == 0 && tid == 0) {
+      if (mean) mean[row] = mu;
+      if (rstd) rstd[row] = rs;
+    }
+  }
+}
+
 // --------------------------------------------------------------- launchers
 
 template <typename Ts, int T, int NV, int EPV, int OCC, bool RMS>
 static hipError_t launch_norm_split(const void* x, const void* res, const void* p1, const void* p2,
                                     void* y, void* res_out, float* mean, float* rstd, int64_t rows,
-                                    int cols, float eps, float4* part, hipStream_t s) {
+                                    int cols, float eps, float4* part, int64_t part_bytes,
+                                    bool one_pass, hipStream_t s) {
   constexpr int SEG = T * NV * EPV;
   const int nseg = (cols + SEG - 1) / SEG;
   const Ts* xi = static_cast<const Ts*>(x);
   const Ts* ri = static_cast<const Ts*>(res);
   Ts* yo = static_cast<Ts*>(y);
   Ts* ro = static_cast<Ts*>(res_out);
+  if (one_pass && coop_applies(rows, nseg, part_bytes)) {
+    hipError_t e = launch_coop_clear(part, rows, nseg, s);
+    if (e != hipSuccess) return e;
+    return launch_kernel(&norm_split_coop_kernel<Ts, T, NV, EPV, OCC, RMS>,
+                         dim3((unsigned)(rows * nseg)), dim3(T), s, xi, ri, static_cast<const Ts*>(p1),
+                         static_cast<const Ts*>(p2), yo, ro, mean, rstd, rows, cols, SEG, nseg, eps,
+                         reinterpret_cast<uint64_t*>(part + 1), reinterpret_cast<uint32_t*>(part),
+                         coop_spin_limit());
+  }
   const int64_t batch = split_batch_rows(rows, (int64_t)cols * (RMS ? 2 : 1) * sizeof(Ts));
   auto grid_of = [&](int64_t nr) {
     const int64_t work = nr * nseg;
@@ -298,11 +417,15 @@ static hipError_t launch_norm_split(const void* x, const void* res, const void* 
 }
 
 #define FR_NS(TS, T, NV, EPV, R) {T, NV, EPV, &launch_norm_split<TS, T, NV, EPV, 4, R>}
+#define FR_NS2(TS, T, NV, EPV, R) {T, NV, EPV, &launch_norm_split<TS, T, NV, EPV, 2, R>}
 // Segment shapes, 32 elements per lane as the split softmax: 256 lanes
-// (8192 columns, the default), 512 and 1024 lanes; the scalar path 256 x 32.
+// (8192 columns, the two passes' default), 512 and 1024 lanes; 512 lanes x
+// 64 elements (the RMSNorm's one-pass default; built for 256 registers, two
+// waves per SIMD: with 128 it spilled); the scalar path 256 x 32.
 #define FR_NS_TABLE(TS, E, R)                                               \
   {FR_NS(TS, 256, 32 / E, E, R), FR_NS(TS, 512, 32 / E, E, R),              \
-   FR_NS(TS, 1024, 32 / E, E, R), FR_NS(TS, 256, 32, 1, R)}
+   FR_NS(TS, 1024, 32 / E, E, R), FR_NS2(TS, 512, 64 / E, E, R),            \
+   FR_NS(TS, 256, 32, 1, R)}
 
 static const NormSplitVariant kNsLnF32[] = FR_NS_TABLE(float, 4, false);
 static const NormSplitVariant kNsLnBf16[] = FR_NS_TABLE(bf16_t, 8, false);

@@ -2,8 +2,9 @@
 fr_softmax_xent_split) against the double-precision oracle, through the C
 ABI: widths from 1 to 2^20 (beyond the single-workgroup limit of 65,536),
 few-row shapes, every segment shape on the vector and scalar paths, mixed
-dtypes, in place, and bitwise reproducibility — the softmax and
-cross-entropy cases in both the one-pass (cooperative) and the two-pass form.
+dtypes, in place, and bitwise reproducibility — the softmax,
+cross-entropy, LayerNorm, RMSNorm and softmax backward cases in both the
+one-pass and the two-pass form.
 The tolerances are the forward ones (softmax: 1e-5 relative / one bf16 ulp;
 cross-entropy: the rules of test_gpu_xent_ex)."""
 import numpy as np
@@ -84,7 +85,7 @@ def test_softmax_split_one_million_columns(form):
     expect_softmax(x, 1, run_softmax_split(x, 1), "split softmax bf16 2x1048576")
 
 
-SEG_SHAPES = [(1024, 8), (512, 8), (256, 8), (1024, 4), (512, 4), (256, 4), (256, 32)]
+SEG_SHAPES = [(1024, 8), (512, 8), (256, 8), (1024, 4), (512, 4), (256, 4), (512, 16), (256, 32)]
 # the softmax / cross-entropy table: 512 x 16 (fp32) and 512 x 8 (fp32 and bf16)
 # hold 64 bytes per lane; no 256 x 4
 SPLIT_SHAPES = [(1024, 8), (512, 8), (256, 8), (1024, 4), (512, 4), (512, 16), (256, 32)]
@@ -309,7 +310,7 @@ NORM_WIDTHS = [1, 5, 1000, 8191, 8192, 8193, 65536, 65537, 100000, 262144]
 
 @pytest.mark.parametrize("C", NORM_WIDTHS)
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_layernorm_split_widths(C, dt):
+def test_layernorm_split_widths(C, dt, form):
     for R in (1, 3):
         w = workloads.make("layernorm_f32", rows=R, cols=C, seed=C + R, dtype=dt)
         got = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps)
@@ -318,7 +319,7 @@ def test_layernorm_split_widths(C, dt):
 
 @pytest.mark.parametrize("C", NORM_WIDTHS)
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_rmsnorm_split_widths(C, dt):
+def test_rmsnorm_split_widths(C, dt, form):
     for R in (1, 3):
         w = workloads.make("add_rmsnorm_bf16", rows=R, cols=C, seed=C + R, dtype=dt)
         got = run_rms_split(w["x"], w["residual"], w["weight"], w.eps, with_res_out=R == 3)
@@ -327,7 +328,7 @@ def test_rmsnorm_split_widths(C, dt):
 
 
 @pytest.mark.parametrize("t,v", SEG_SHAPES)
-def test_norm_split_every_segment_shape(t, v):
+def test_norm_split_every_segment_shape(t, v, form):
     ran = 0
     for dt, code in (("f32", fr.F32), ("bf16", fr.BF16)):
         for vp, offs in ((True, (0, 0)), (False, (1, 3))):
@@ -359,7 +360,7 @@ def test_norm_split_every_segment_shape(t, v):
         pytest.skip(f"no split norm shape ({t}, {v})")
 
 
-def test_norm_split_in_place_and_misaligned():
+def test_norm_split_in_place_and_misaligned(form):
     for dt in ("f32", "bf16"):
         w = workloads.make("layernorm_f32", rows=4, cols=70001, seed=21, dtype=dt)
         expect_layernorm(w["x"], w["gamma"], w["beta"], w.eps,
@@ -378,7 +379,7 @@ def test_norm_split_in_place_and_misaligned():
                        f"split add_rmsnorm misaligned {dt}")
 
 
-def test_norm_split_special_rows():
+def test_norm_split_special_rows(form):
     C = 100000
     w = workloads.make("layernorm_f32", rows=3, cols=C, seed=23)
     x = w["x"].copy()
@@ -397,7 +398,7 @@ def test_norm_split_special_rows():
     assert np.all(got[0][0] == 0)
 
 
-def test_norm_split_determinism_and_convenience():
+def test_norm_split_determinism_and_convenience(form):
     w = workloads.make("layernorm_f32", rows=8, cols=200000, seed=25, dtype="bf16")
     a = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps)
     b = run_ln_split(w["x"], w["gamma"], w["beta"], w.eps)
@@ -434,13 +435,13 @@ def run_softmax_bwd_split(p, dy, offs=(0, 0, 0), inplace=None):
 
 @pytest.mark.parametrize("C", [1, 7, 8192, 8193, 16385, 65537, 262144])
 @pytest.mark.parametrize("code", [fr.F32, fr.BF16])
-def test_softmax_bwd_split_widths(C, code):
+def test_softmax_bwd_split_widths(C, code, form):
     for R in (1, 3):
         p, dy = softmax_bwd_inputs(R, C, code, seed=C + R)
         expect_softmax_bwd(p, dy, code, run_softmax_bwd_split(p, dy), f"split softmax_bwd {code} {R}x{C}")
 
 
-def test_softmax_bwd_split_shapes_in_place_misaligned():
+def test_softmax_bwd_split_shapes_in_place_misaligned(form):
     for t, v in SEG_SHAPES:
         for code in (fr.F32, fr.BF16):
             for vp, offs in ((True, (0, 0, 0)), (False, (1, 2, 0))):

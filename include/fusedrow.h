@@ -402,8 +402,9 @@ FR_API fr_status_t fr_layernorm_bwd(const void* x, const void* dy, const void* g
 
 /* Bytes of device workspace fr_add_rmsnorm_bwd_split (op FR_OP_RMSNORM_BWD)
  * or fr_layernorm_bwd_split (FR_OP_LAYERNORM_BWD) needs for [rows, cols]:
- * the per-segment row sums (rows * ceil(cols / 8192) * 16 bytes, padded to a
- * multiple of 256) plus G * cols * 4 per parameter gradient, G =
+ * the per-segment row sums (rows * ceil(cols / 8192) * 16 + 16 bytes,
+ * padded to a multiple of 256; none for rows = 0) plus G * cols * 4 per
+ * parameter gradient, G =
  * min(rows, max(1, min(512, 1024 / ceil(cols / 8192)))) partial rows. -1 for
  * another op or an invalid shape (1 <= cols <= FR_SPLIT_MAX_COLS). */
 FR_API int64_t fr_norm_bwd_split_workspace_bytes(fr_op_t op, int64_t rows, int64_t cols);
@@ -414,7 +415,12 @@ FR_API int64_t fr_norm_bwd_split_workspace_bytes(fr_op_t op, int64_t rows, int64
  * (segment, row group) over rows g, g + G, ... — adds a row's partials in
  * segment order, writes the segment's dh and accumulates its columns'
  * dweight partials, one partial row per row group; a third kernel adds the
- * G partial rows in order. Reads h, dy (and dres) twice.
+ * G partial rows in order. Reads h, dy (and dres) twice. One-pass form (fp32,
+ * rows giving at least 4 workgroups per compute unit;
+ * fr_debug_set_split_cooperative): a kernel zeroing the workspace's slots,
+ * then one launch in which the row group's segment workgroups walk their
+ * rows together, exchange each row's sums through the workspace and write
+ * dh from the registers (h, dy and dres read once), then the column sums.
  * Arguments and results as fr_add_rmsnorm_bwd, with the workspace of
  * fr_norm_bwd_split_workspace_bytes. Results are bitwise reproducible. */
 FR_API fr_status_t fr_add_rmsnorm_bwd_split(const void* h, const void* dy, const void* dres,
@@ -535,12 +541,13 @@ FR_API fr_status_t fr_debug_force_variant(fr_op_t op, int threads, int vecs);
 FR_API int64_t fr_debug_set_split_batch_bytes(int64_t bytes);
 
 /* The one-pass form of the split entry points (fr_softmax_fwd_split,
- * fr_softmax_xent_split, fr_add_rmsnorm_fwd_split, fr_softmax_bwd_split;
- * fr_layernorm_fwd_split in mode 2 only): mode 0 always runs the two
- * passes; mode 1 (the default) takes the one-pass form where it applies and
- * the rows give at least 4 work items per compute unit; mode 2 takes it
- * wherever it applies (any row count, and with a forced variant, whose
- * shape it keeps); other values mean 1.
+ * fr_softmax_xent_split, fr_add_rmsnorm_fwd_split, fr_softmax_bwd_split,
+ * fr_add_rmsnorm_bwd_split and fr_layernorm_bwd_split in fp32;
+ * fr_layernorm_fwd_split and the bf16 norm backward in mode 2 only): mode 0
+ * always runs the two passes; mode 1 (the default) takes the one-pass form
+ * where it applies and the rows give at least 4 work items per compute
+ * unit; mode 2 takes it wherever it applies (any row count, and with a
+ * forced variant, whose shape it keeps); other values mean 1.
  * Results do not depend on it beyond rounding (both merge the same kind of
  * segment states in segment order, the one-pass form by a fixed DPP tree).
  * Returns the previous setting. Process-wide setting meant for tests and

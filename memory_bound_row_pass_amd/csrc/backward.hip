@@ -25,8 +25,9 @@
 // one partial row per parameter to the workspace; colsum_kernel then adds
 // the partial rows in a fixed order. There are no atomics: results are
 // bitwise reproducible run to run.
-#include "fr_kernels.hpp"
+#include "coop.hpp"
 #include "fr_device.hpp"
+#include "fr_kernels.hpp"
 
 namespace fr {
 
@@ -759,6 +760,150 @@ void norm_bwd_split_apply_kernel(const Ts* xh, const Ts* dy, const Ts* dres, con
   }
 }
 
+// One-pass form (the exchange of coop.hpp), h, dy (and dres) read once:
+// teams of nseg workgroups — row group rg's segments, handed out in start
+// order (ticket w: rg = w / nseg, segment w % nseg) — walk rows rg, rg + RG,
+// ... together. Per row each member loads its segment, takes its two sums as
+// pass 1 does, posts {sum a, 1} and {sum b, 1} (never zero) into the row's
+// slots, waits for the row's other segments, adds them in segment order
+// (lane j holds segment j's, one DPP tree: the same bits in every workgroup
+// of the row), then writes the segment's dh / dx and accumulates its
+// columns' parameter-gradient partials as pass 2 does; at the end it writes
+// them to partial row rg, and colsum_kernel adds the partial rows. A team
+// waits only for its own members, on the same rows in the same order, and
+// lower tickets are lower teams: the lowest unfinished team needs room for
+// its own workgroups only.
+template <typename Ts, int T, int NV, int EPV, bool LN, bool DRES>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4)))
+void norm_bwd_split_coop_kernel(const Ts* xh, const Ts* dy, const Ts* dres, const Ts* w,
+                                const float* mean, const float* rstd, Ts* out, float* ws,
+                                int64_t rows, int cols, int nseg, int RG, float eps,
+                                uint64_t* slots, uint32_t* ctl, int spin_limit) {
+  constexpr int NW = T / 64;
+  constexpr int SEG = T * NV * EPV;
+  __shared__ float xw[2][NW][2];
+  __shared__ float team[kCoopMaxSegments][4];
+  __shared__ uint32_t ticket;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int64_t tk = coop_ticket(ctl, &ticket);  // < RG * nseg: one per workgroup
+  const int rg = (int)(tk / nseg);
+  const int sg = (int)(tk - (int64_t)rg * nseg);
+  const int c0 = sg * SEG;
+  const int len = cols - c0 < SEG ? cols - c0 : SEG;
+  const Slots<T, NV, EPV> sl(len, tid);
+
+  float acc[NV][EPV], acc2[LN ? NV : 1][EPV];  // dw (dgamma) and dbeta partials
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) acc[i][k] = 0.f;
+#pragma unroll
+  for (int i = 0; i < (LN ? NV : 1); ++i)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) acc2[i][k] = 0.f;
+  constexpr bool WREG = EPV > 1;  // the weight in registers on the vector path
+  float wv[WREG ? NV : 1][EPV];
+  if constexpr (WREG) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sl.param(w + c0, i, wv[i]);
+  }
+  auto weight = [&](const Ts* wp, int i, float* t) {
+    if constexpr (WREG) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) t[k] = wv[i][k];
+    } else {
+      sl.param(wp, i, t);
+    }
+  };
+
+  int merges = 0;  // cross-wave merges so far: picks the LDS slot
+  for (int64_t row = rg; row < rows; row += RG) {
+    const int64_t off = row * cols + c0;
+    float a[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
+    if constexpr (DRES) sl.load3(xh + off, dy + off, dres + off, a, d, dr);
+    else sl.load2(xh + off, dy + off, a, d);
+    float mu = 0.f, rs = 1.f;
+    if constexpr (LN) {
+      mu = mean[row];
+      rs = rstd[row];
+    }
+    const Ts* w1 = fresh(w) + c0;
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float wt[EPV];
+      weight(w1, i, wt);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const float gk = d[i][k] * wt[k];
+        if constexpr (LN) {
+          const float nk = sl.ok(i) ? (a[i][k] - mu) * rs : 0.f;
+          if (k & 1) { a1 += gk; b1 = __builtin_fmaf(gk, nk, b1); }
+          else { a0 += gk; b0 = __builtin_fmaf(gk, nk, b0); }
+        } else {
+          const float hk = a[i][k];
+          if (k & 1) { a1 = __builtin_fmaf(hk, hk, a1); b1 = __builtin_fmaf(gk, hk, b1); }
+          else { a0 = __builtin_fmaf(hk, hk, a0); b0 = __builtin_fmaf(gk, hk, b0); }
+        }
+      }
+    }
+    Sum2State mine{a0 + a1, b0 + b1};
+    mine = wave_reduce(mine, Sum2Merge{});
+    if constexpr (NW > 1) mine = block_merge<NW>(mine, xw[merges++ & 1], wave, lane, Sum2Merge{});
+    uint64_t* row_slots = slots + (size_t)row * nseg * 2;
+    coop_post<2>(row_slots, sg, coop_word(mine.a, 1.f), coop_word(mine.b, 1.f));
+    if (wave == 0) coop_wait<2>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+    lds_barrier();
+    Sum2State st{0.f, 0.f};
+    if (lane < nseg) st = Sum2State{team[lane][0], team[lane][2]};
+    st = wave_reduce(st, Sum2Merge{});
+
+    if constexpr (LN) {
+      const float mg = st.a / (float)cols, mgn = st.b / (float)cols;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float ga[EPV];
+        weight(w1, i, ga);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float nk = (a[i][k] - mu) * rs;
+          acc[i][k] = __builtin_fmaf(d[i][k], nk, acc[i][k]);
+          acc2[i][k] += d[i][k];
+          a[i][k] = rs * __builtin_fmaf(-nk, mgn, __builtin_fmaf(d[i][k], ga[k], -mg));
+        }
+      }
+    } else {
+      const float r = 1.f / __builtin_sqrtf(st.a / (float)cols + eps);
+      const float c = r * r * (st.b / (float)cols);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float wt[EPV];
+        weight(w1, i, wt);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          acc[i][k] = __builtin_fmaf(d[i][k] * a[i][k], r, acc[i][k]);
+          const float t = r * __builtin_fmaf(-a[i][k], c, wt[k] * d[i][k]);
+          if constexpr (DRES) a[i][k] = t + dr[i][k];
+          else a[i][k] = t;
+        }
+      }
+    }
+    sl.store(out + off, a);
+  }
+  float* w0 = ws + (size_t)rg * cols + c0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (sl.ok(i)) store_f32<EPV>(w0 + (i * T + tid) * EPV, acc[i]);
+  if constexpr (LN) {
+    float* w1 = ws + ((size_t)RG + rg) * cols + c0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (sl.ok(i)) store_f32<EPV>(w1 + (i * T + tid) * EPV, acc2[i]);
+  }
+}
+
 // ------------------------------------------------------------ column sums
 // out_p[c] = sum over the partial rows b = 0 .. partials-1 of ws[p][b][c],
 // parameter p = blockIdx.y. A workgroup takes a 32-column tile (one 128-byte
@@ -853,7 +998,8 @@ template <typename Ts, int NV, int EPV, bool LN>
 static hipError_t launch_norm_bwd_split_t(const void* xh, const void* dy, const void* dres,
                                           const void* w, const float* mean, const float* rstd,
                                           void* out, float* dw0, float* dw1, void* workspace,
-                                          int64_t rows, int cols, float eps, hipStream_t s) {
+                                          int64_t rows, int cols, float eps, bool one_pass,
+                                          hipStream_t s) {
   constexpr int T = 512;
   static_assert(T * NV * EPV == kBwdSplitSeg, "segment");
   const int nseg = (cols + kBwdSplitSeg - 1) / kBwdSplitSeg;
@@ -861,6 +1007,19 @@ static hipError_t launch_norm_bwd_split_t(const void* xh, const void* dy, const 
   float4* part = static_cast<float4*>(workspace);
   float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        norm_bwd_split_part_bytes(rows, cols));
+  if (one_pass && nseg <= kCoopMaxSegments) {
+    hipError_t e = launch_coop_clear(part, rows, nseg, s);
+    if (e != hipSuccess) return e;
+    auto kc = (!LN && dres) ? &norm_bwd_split_coop_kernel<Ts, T, NV, EPV, LN, true>
+                            : &norm_bwd_split_coop_kernel<Ts, T, NV, EPV, LN, false>;
+    e = launch_kernel(kc, dim3((unsigned)(nseg * RG)), dim3(T), s, static_cast<const Ts*>(xh),
+                      static_cast<const Ts*>(dy), static_cast<const Ts*>(dres),
+                      static_cast<const Ts*>(w), mean, rstd, static_cast<Ts*>(out), ws, rows, cols,
+                      nseg, RG, eps, reinterpret_cast<uint64_t*>(part + 1),
+                      reinterpret_cast<uint32_t*>(part), coop_spin_limit());
+    if (e != hipSuccess) return e;
+    return launch_colsum(ws, RG, cols, dw0, dw1, s);
+  }
   const int64_t work = rows * nseg;
   const unsigned g1 = (unsigned)(work < kMaxGrid ? work : kMaxGrid);
   hipError_t e = launch_kernel(&norm_bwd_split_sums_kernel<Ts, T, NV, EPV, LN>, dim3(g1), dim3(T), s,
@@ -881,27 +1040,23 @@ hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* x
                                  const void* dres, const void* w, const float* mean,
                                  const float* rstd, void* out, float* dw0, float* dw1,
                                  void* workspace, int64_t rows, int cols, float eps,
-                                 hipStream_t s) {
+                                 bool one_pass, hipStream_t s) {
+  auto go = [&](auto launch) {
+    return launch(xh, dy, dres, w, mean, rstd, out, dw0, dw1, workspace, rows, cols, eps, one_pass,
+                  s);
+  };
   if (layernorm) {
     if (bf16)
-      return vec ? launch_norm_bwd_split_t<bf16_t, 2, 8, true>(xh, dy, dres, w, mean, rstd, out, dw0,
-                                                               dw1, workspace, rows, cols, eps, s)
-                 : launch_norm_bwd_split_t<bf16_t, 16, 1, true>(xh, dy, dres, w, mean, rstd, out,
-                                                                dw0, dw1, workspace, rows, cols, eps, s);
-    return vec ? launch_norm_bwd_split_t<float, 4, 4, true>(xh, dy, dres, w, mean, rstd, out, dw0, dw1,
-                                                            workspace, rows, cols, eps, s)
-               : launch_norm_bwd_split_t<float, 16, 1, true>(xh, dy, dres, w, mean, rstd, out, dw0,
-                                                             dw1, workspace, rows, cols, eps, s);
+      return vec ? go(&launch_norm_bwd_split_t<bf16_t, 2, 8, true>)
+                 : go(&launch_norm_bwd_split_t<bf16_t, 16, 1, true>);
+    return vec ? go(&launch_norm_bwd_split_t<float, 4, 4, true>)
+               : go(&launch_norm_bwd_split_t<float, 16, 1, true>);
   }
   if (bf16)
-    return vec ? launch_norm_bwd_split_t<bf16_t, 2, 8, false>(xh, dy, dres, w, mean, rstd, out, dw0,
-                                                              dw1, workspace, rows, cols, eps, s)
-               : launch_norm_bwd_split_t<bf16_t, 16, 1, false>(xh, dy, dres, w, mean, rstd, out, dw0,
-                                                               dw1, workspace, rows, cols, eps, s);
-  return vec ? launch_norm_bwd_split_t<float, 4, 4, false>(xh, dy, dres, w, mean, rstd, out, dw0, dw1,
-                                                           workspace, rows, cols, eps, s)
-             : launch_norm_bwd_split_t<float, 16, 1, false>(xh, dy, dres, w, mean, rstd, out, dw0,
-                                                            dw1, workspace, rows, cols, eps, s);
+    return vec ? go(&launch_norm_bwd_split_t<bf16_t, 2, 8, false>)
+               : go(&launch_norm_bwd_split_t<bf16_t, 16, 1, false>);
+  return vec ? go(&launch_norm_bwd_split_t<float, 4, 4, false>)
+             : go(&launch_norm_bwd_split_t<float, 16, 1, false>);
 }
 
 // Norm backward shapes: (T, NV, EPV, RPB, OCC, grid_max). The default

@@ -203,14 +203,16 @@ inline int norm_bwd_split_groups(int64_t rows, int nseg) {
   g = g < 1 ? 1 : (g > kBwdGridMax ? kBwdGridMax : g);
   return (int)(rows < g ? rows : g);
 }
+// The per-(row, segment) sums of the two passes, or the one-pass form's
+// counter, abort word and slots (16 bytes more).
 inline int64_t norm_bwd_split_part_bytes(int64_t rows, int64_t cols) {
   const int64_t nseg = (cols + kBwdSplitSeg - 1) / kBwdSplitSeg;
-  return (rows * nseg * 16 + 255) / 256 * 256;
+  return rows > 0 ? (rows * nseg * 16 + 16 + 255) / 256 * 256 : 0;
 }
 hipError_t launch_norm_bwd_split(int layernorm, int bf16, int vec, const void* xh, const void* dy,
                                  const void* dres, const void* w, const float* mean,
                                  const float* rstd, void* out, float* dw0, float* dw1,
-                                 void* workspace, int64_t rows, int cols, float eps,
+                                 void* workspace, int64_t rows, int cols, float eps, bool one_pass,
                                  hipStream_t s);
 
 // Allocation-free RMSNorm backward (noalloc.hip): the partial rows go to a

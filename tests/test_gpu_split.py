@@ -3,8 +3,8 @@ fr_softmax_xent_split) against the double-precision oracle, through the C
 ABI: widths from 1 to 2^20 (beyond the single-workgroup limit of 65,536),
 few-row shapes, every segment shape on the vector and scalar paths, mixed
 dtypes, in place, and bitwise reproducibility — the softmax,
-cross-entropy, LayerNorm, RMSNorm and softmax backward cases in both the
-one-pass and the two-pass form.
+cross-entropy, LayerNorm, RMSNorm, softmax backward and norm backward
+cases in both the one-pass and the two-pass form.
 The tolerances are the forward ones (softmax: 1e-5 relative / one bf16 ulp;
 cross-entropy: the rules of test_gpu_xent_ex)."""
 import numpy as np
@@ -517,7 +517,7 @@ BWD_WIDTHS = [16385, 24576, 65537, 100000]
 
 @pytest.mark.parametrize("C", BWD_WIDTHS)
 @pytest.mark.parametrize("code", [fr.F32, fr.BF16])
-def test_rms_bwd_split_widths(C, code):
+def test_rms_bwd_split_widths(C, code, form):
     for R, dres in ((1, True), (5, False)):
         w = rms_bwd_inputs(R, C, code, seed=C + R)
         expect_rms_bwd(w, code, run_rms_bwd_split(w, code, with_dres=dres),
@@ -526,14 +526,14 @@ def test_rms_bwd_split_widths(C, code):
 
 @pytest.mark.parametrize("C", BWD_WIDTHS)
 @pytest.mark.parametrize("code", [fr.F32, fr.BF16])
-def test_ln_bwd_split_widths(C, code):
+def test_ln_bwd_split_widths(C, code, form):
     for R in (1, 5):
         w, mean, rstd = ln_bwd_inputs(R, C, code, seed=C + R)
         expect_ln_bwd(w, mean, rstd, code, run_ln_bwd_split(w, mean, rstd, code),
                       f"split ln_bwd {code} {R}x{C}")
 
 
-def test_norm_bwd_split_many_rows_in_place_misaligned():
+def test_norm_bwd_split_many_rows_in_place_misaligned(form):
     # more rows than row groups (each workgroup takes several rows), the
     # scalar path (misaligned), and outputs over their inputs
     for code in (fr.F32, fr.BF16):
@@ -555,7 +555,7 @@ def test_norm_bwd_split_many_rows_in_place_misaligned():
                           f"split ln_bwd {code} in place ({ip})")
 
 
-def test_norm_bwd_split_determinism_rows_zero_and_convenience():
+def test_norm_bwd_split_determinism_rows_zero_and_convenience(form):
     w = rms_bwd_inputs(64, 50000, fr.BF16, seed=45)
     a = run_rms_bwd_split(w, fr.BF16)
     b = run_rms_bwd_split(w, fr.BF16)

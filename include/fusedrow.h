@@ -220,7 +220,8 @@ FR_API int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols);
  * are handed out in the order workgroups start, so the waits need no more
  * of the device than one row's workgroups) and write from the registers: x
  * is read once. A workgroup that waits too long (fr_debug_set_coop_spin_limit;
- * not reached in a correct run) writes NaN for its row. Otherwise two passes
+ * not reached in a correct run) writes NaN for its row (the cross-entropy's
+ * argmax: -1). Otherwise two passes
  * over segments of 8192 columns (16384 for bf16 input): pass 1 writes each
  * segment's state to `workspace`, pass 2 merges and re-reads its segment (x
  * read twice), over one batch of rows, at most 256 MiB of input, before the

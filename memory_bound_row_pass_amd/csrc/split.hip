@@ -263,7 +263,9 @@ __device__ __forceinline__ void segment_apply(float (&v)[NV][EPV], float xe, int
     } else if (!valid && sg == 0 && tid == 0) {
       loss[row] = __builtin_nanf("");
     }
-    if (argmax && sg == 0 && tid == 0) argmax[row] = (int32_t)st.idx;
+    // the column as an integer; -1 for a NaN column (a row of the one-pass
+    // form whose states did not all arrive)
+    if (argmax && sg == 0 && tid == 0) argmax[row] = st.idx == st.idx ? (int32_t)st.idx : -1;
   }
 }
 
@@ -458,7 +460,7 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
     if (ec >= 0) store1(ys + ec, 0.f);
     if (sg == 0 && tid == 0) {
       loss[row] = 0.f;
-      argmax[row] = (int32_t)st.idx;
+      argmax[row] = st.idx == st.idx ? (int32_t)st.idx : -1;  // -1: states missing
     }
     return;
   }

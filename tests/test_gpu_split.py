@@ -576,6 +576,84 @@ def test_norm_bwd_split_determinism_rows_zero_and_convenience(form):
                   "layernorm_bwd() of a wide row")
 
 
+# ------------------------------------------- bounded waits, every one-pass kernel
+
+def _as_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _wait_bound_cases():
+    """(name, run) pairs: run() returns the call's row outputs (arrays of rows)
+    and its per-column outputs."""
+    cases = []
+    x = softmax_input(fr.F32, 96, 131072, seed=51)
+    cases.append(("softmax fp32", lambda: ((run_softmax_split(x, fr.F32),), ())))
+    xl, lab = xent_inputs(64, 262144, fr.BF16, seed=52, ignore_every=5)
+    opts = dict(ignore_index=-100, label_smoothing=0.1)
+    cases.append(("cross-entropy bf16", lambda: (lambda r: ((r[1], r[0][:, None], r[2][:, None]), ()))(
+        run_xent_split(xl, lab, fr.BF16, opts))))
+    wr = workloads.make("add_rmsnorm_bf16", rows=48, cols=262144, seed=53)
+    cases.append(("add_rmsnorm bf16", lambda: (run_rms_split(wr["x"], wr["residual"], wr["weight"],
+                                                             wr.eps), ())))
+    wl = workloads.make("layernorm_f32", rows=64, cols=131072, seed=54)
+    cases.append(("layernorm fp32", lambda: (lambda r: ((r[0], r[1][:, None], r[2][:, None]), ()))(
+        run_ln_split(wl["x"], wl["gamma"], wl["beta"], wl.eps))))
+    p, dy = softmax_bwd_inputs(96, 131072, fr.BF16, seed=55)
+    cases.append(("softmax_bwd bf16", lambda: ((run_softmax_bwd_split(p, dy),), ())))
+    wb = rms_bwd_inputs(64, 65536, fr.F32, seed=56)
+    cases.append(("add_rmsnorm_bwd fp32", lambda: (lambda r: ((r[0],), (r[1],)))(
+        run_rms_bwd_split(wb, fr.F32))))
+    wn, mean, rstd = ln_bwd_inputs(64, 65536, fr.F32, seed=57)
+    cases.append(("layernorm_bwd fp32", lambda: (lambda r: ((r[0],), (r[1], r[2])))(
+        run_ln_bwd_split(wn, mean, rstd, fr.F32))))
+    return cases
+
+
+def test_one_pass_wait_bound_every_kernel():
+    """Every one-pass kernel with its waits forced to give up (poll bound 0:
+    a workgroup gives up whenever its first poll does not find all of its
+    row's states): the launch ends, and every row of every row output is
+    either bitwise the one of a call with the default bound or holds NaN (a
+    workgroup that gave up; an ignored row of the cross-entropy, whose loss
+    and gradient are 0 regardless, shows it as argmax -1); the per-column
+    outputs (parameter gradients)
+    are bitwise the same when no row gave up. The next call, with the
+    default bound, is bitwise the same throughout."""
+    with fr.split_cooperative(2):
+        for name, run in _wait_bound_cases():
+            print(f"bounded waits: {name}", flush=True)
+            ref_rows, ref_cols = run()
+            with fr.coop_spin_limit(0):
+                got_rows, got_cols = run()
+            # a row given up: NaN in one of its float outputs, or an argmax of
+            # -1 (an ignored row's loss and gradient are 0 all the same)
+            nan_any = np.zeros(len(ref_rows[0]), dtype=bool)
+            for g in got_rows:
+                g = np.asarray(g)
+                if g.dtype == np.int32:
+                    nan_any |= (g.reshape(len(g), -1) == -1).any(axis=1)
+                else:
+                    nan_any |= np.isnan(_as_f64(g)).reshape(len(g), -1).any(axis=1)
+            for g, r in zip(got_rows, ref_rows):
+                g2 = np.ascontiguousarray(np.asarray(g).reshape(len(g), -1))
+                r2 = np.ascontiguousarray(np.asarray(r).reshape(len(r), -1))
+                same = (g2.view(np.uint8) == r2.view(np.uint8)).all(axis=1)
+                ok = same | nan_any
+                assert ok.all(), f"{name}: rows {np.flatnonzero(~ok)[:8]} neither right nor NaN"
+            if not nan_any.any():
+                for g, r in zip(got_cols, ref_cols):
+                    assert np.array_equal(g, r), f"{name}: per-column outputs differ"
+            print(f"  rows given up: {int(nan_any.sum())} of {len(nan_any)}", flush=True)
+            after_rows, after_cols = run()
+            for g, r in zip(after_rows + after_cols, ref_rows + ref_cols):
+                g2, r2 = np.ascontiguousarray(g), np.ascontiguousarray(r)
+                assert np.array_equal(g2.view(np.uint8), r2.view(np.uint8)), \
+                    f"{name}: the call after differs"
+
+
 # ------------------------------------------------------------ row batches
 
 def _bits(*arrays):

@@ -252,10 +252,10 @@ FR_API fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labe
  * writes each segment's exact (count, mean, M2) to `workspace`, pass 2 merges
  * a row's partials in segment order with the pairwise (Chan) merge of the
  * Welford moments and writes the segment's y (and, from the row's first
- * segment, mean and rstd). Reads x twice, writes y once. (The one-pass
- * form of fr_softmax_fwd_split only with fr_debug_set_split_cooperative(2):
- * it measured no faster here, the apply step reading gamma and beta for
- * every row segment.)
+ * segment, mean and rstd). Reads x twice, writes y once. fp32 also in the
+ * one-pass form of fr_softmax_fwd_split (segments of 16384 columns); bf16
+ * only with fr_debug_set_split_cooperative(2) (no faster there: the apply
+ * step reads gamma and beta for every row segment).
  *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.2
  *    Welford Single-Pass Normalization: partial moments merged pairwise.)
  * Arguments and results as fr_layernorm_fwd, with 1 <= cols <=
@@ -543,8 +543,8 @@ FR_API int64_t fr_debug_set_split_batch_bytes(int64_t bytes);
 
 /* The one-pass form of the split entry points (fr_softmax_fwd_split,
  * fr_softmax_xent_split, fr_add_rmsnorm_fwd_split, fr_softmax_bwd_split,
- * fr_add_rmsnorm_bwd_split and fr_layernorm_bwd_split in fp32;
- * fr_layernorm_fwd_split and the bf16 norm backward in mode 2 only): mode 0
+ * fr_layernorm_fwd_split, fr_add_rmsnorm_bwd_split and fr_layernorm_bwd_split
+ * in fp32; their bf16 forms in mode 2 only): mode 0
  * always runs the two passes; mode 1 (the default) takes the one-pass form
  * where it applies and the rows give at least 4 work items per compute
  * unit; mode 2 takes it wherever it applies (any row count, and with a

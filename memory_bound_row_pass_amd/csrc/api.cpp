@@ -162,12 +162,13 @@ SplitChoice<V> choose_split(VariantSpan<V> sp, int op, int epv, int64_t rows, in
 // Elements per lane of the one-pass shape of the softmax, cross-entropy,
 // residual-add + RMSNorm and softmax backward (measured against 32 at 512
 // lanes: RMSNorm bf16 [256, 262144] 110 against 118 us, softmax backward
-// bf16 [256, 131072] 52 against 56 us). The LayerNorm takes no one-pass
-// shape by default (elems 0): its apply step reads gamma and beta for every
-// row segment, and in one pass it measured 123 against 131 us (fp32
-// [512, 131072], 32 elements; 129 with 64) and 84 against 81 us (bf16).
+// bf16 [256, 131072] 52 against 56 us). The LayerNorm's apply step reads
+// gamma and beta for every row segment: in fp32 one pass at 512 x 32 pays
+// (per call against the two passes: [512, 131072] 126.9 against 131.1 us,
+// [2048, 32768] 118.1 against 129.6; 512 x 64 129 us, 1024 x 32 131-135),
+// in bf16 no shape does (512 x 32: 86-89 against 81 us), so none (0).
 constexpr int kOnePassElems = 64;
-constexpr int kOnePassElemsLn = 0;
+inline int one_pass_elems_ln(fr_dtype_t dtype) { return dtype == FR_F32 ? 32 : 0; }
 
 thread_local int t_last_launch_error = 0;
 
@@ -321,7 +322,7 @@ fr_status_t describe_variant(fr_op_t op, int64_t rows, int64_t cols, fr_dtype_t 
     case FR_OP_RMSNORM_SPLIT: {
       auto v = choose_split(fr::norm_split_variants(in_dtype == FR_BF16, op == FR_OP_RMSNORM_SPLIT),
                             op, epv, rows, cols,
-                            op == FR_OP_RMSNORM_SPLIT ? kOnePassElems : kOnePassElemsLn).v;
+                            op == FR_OP_RMSNORM_SPLIT ? kOnePassElems : one_pass_elems_ln(in_dtype)).v;
       if (v) { t = v->threads; n = v->nv; e = v->epv; }
       break;
     }
@@ -902,7 +903,7 @@ fr_status_t fr_layernorm_fwd_split(const void* x, const void* gamma, const void*
   const bool vec = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16) &&
                    (cols * es) % 16 == 0;
   const auto c = choose_split(fr::norm_split_variants(dtype == FR_BF16, 0), FR_OP_LAYERNORM_SPLIT,
-                              vec ? vec_epv(es) : 1, rows, cols, kOnePassElemsLn);
+                              vec ? vec_epv(es) : 1, rows, cols, one_pass_elems_ln(dtype));
   if (!c.v) return FR_E_VARIANT;
   return launch_status(c.v->launch(x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, (int)cols,
                                    eps, static_cast<float4*>(workspace),

@@ -52,11 +52,13 @@ __device__ __forceinline__ void coop_post(uint64_t* row_slots, int sg, uint64_t 
 // Wave 0: waits for word f < NWD of segment j < nseg of the row's slots and
 // leaves its halves in team[j][2 f] (low) and team[j][2 f + 1] (high), NaN
 // for a word that did not arrive. The caller's barrier publishes team.
+// Returns (uniformly) whether every word arrived.
 template <int NWD>
-__device__ __forceinline__ void coop_wait(const uint64_t* row_slots, int nseg, uint32_t* abort_word,
+__device__ __forceinline__ bool coop_wait(const uint64_t* row_slots, int nseg, uint32_t* abort_word,
                                           int spin_limit, int lane, float (*team)[4]) {
   constexpr int PER = 64 / NWD;  // segments per round
   const int f = lane % NWD;
+  bool all = true;
   for (int j0 = 0; j0 < nseg; j0 += PER) {
     const int j = j0 + lane / NWD;
     const bool live = j < nseg;
@@ -75,6 +77,7 @@ __device__ __forceinline__ void coop_wait(const uint64_t* row_slots, int nseg, u
                   __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
       if (__builtin_amdgcn_readfirstlane((int)give_up)) {
         if (lane == 0) __hip_atomic_store(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        all = false;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -84,6 +87,7 @@ __device__ __forceinline__ void coop_wait(const uint64_t* row_slots, int nseg, u
       team[j][2 * f + 1] = have ? __builtin_bit_cast(float, (uint32_t)(word >> 32)) : __builtin_nanf("");
     }
   }
+  return all;
 }
 
 // Zeroes the one-pass workspace of rows x nseg work items (split.hip).

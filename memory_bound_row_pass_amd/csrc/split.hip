@@ -223,7 +223,7 @@ __device__ __forceinline__ void segment_apply(float (&v)[NV][EPV], float xe, int
                                               const SplitState& st, float inv_s, int label,
                                               float gsc, float goff, const XentOptions& opt,
                                               float* loss, int32_t* argmax, int64_t row, int sg,
-                                              int cols, int tid) {
+                                              int cols, int tid, bool states_ok = true) {
   // label column handled by the lane of this segment that owns it
   bool label_lane = false;
   float x_label = 0.f;
@@ -263,9 +263,8 @@ __device__ __forceinline__ void segment_apply(float (&v)[NV][EPV], float xe, int
     } else if (!valid && sg == 0 && tid == 0) {
       loss[row] = __builtin_nanf("");
     }
-    // the column as an integer; -1 for a NaN column (a row of the one-pass
-    // form whose states did not all arrive)
-    if (argmax && sg == 0 && tid == 0) argmax[row] = st.idx == st.idx ? (int32_t)st.idx : -1;
+    // -1: a row of the one-pass form whose states did not all arrive
+    if (argmax && sg == 0 && tid == 0) argmax[row] = states_ok ? (int32_t)st.idx : -1;
   }
 }
 
@@ -391,6 +390,7 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
   __shared__ float xw[2][NW][4];
   __shared__ float team[kCoopMaxSegments][4];
   __shared__ uint32_t ticket;
+  __shared__ int team_ok;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
@@ -442,8 +442,12 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
                                                            xw[0]);
   uint64_t* row_slots = slots + (size_t)row * nseg * 2;
   coop_post<NWD>(row_slots, sg, coop_word(mine.m, mine.s), coop_word(mine.t, mine.idx + 1.f));
-  if (wave == 0) coop_wait<NWD>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+  if (wave == 0) {
+    const bool ok = coop_wait<NWD>(row_slots, nseg, ctl + 1, spin_limit, lane, team);
+    if (lane == 0) team_ok = ok;
+  }
   lds_barrier();
+  const bool states_ok = __builtin_amdgcn_readfirstlane(team_ok) != 0;
   // the row's state: lane j < nseg holds segment j's, one DPP tree (the same
   // in every wave of every workgroup of the row); idx + 1 -> idx is exact
   // below 2^24
@@ -460,12 +464,12 @@ void split_coop_kernel(const Tin* x, Tout* y, int64_t rows, int cols, int seg, i
     if (ec >= 0) store1(ys + ec, 0.f);
     if (sg == 0 && tid == 0) {
       loss[row] = 0.f;
-      argmax[row] = st.idx == st.idx ? (int32_t)st.idx : -1;  // -1: states missing
+      argmax[row] = states_ok ? (int32_t)st.idx : -1;  // -1: states missing
     }
     return;
   }
   segment_apply<Tin, Tout, T, NV, EPV, XENT>(v, xe, ec, g, sgm, xs, ys, st, 1.f / st.s, label, gsc,
-                                            goff, opt, loss, argmax, row, sg, cols, tid);
+                                            goff, opt, loss, argmax, row, sg, cols, tid, states_ok);
 }
 
 // Zeroes n 16-byte words (the one-pass form's counter, abort word and slots).

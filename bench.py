@@ -31,8 +31,8 @@ split-row cross-entropy at vocabulary widths beyond one workgroup (fp32
 [2048, 131072], bf16 [1024, 262144]), the split-row norms (LayerNorm fp32
 [512, 131072], residual-add + RMSNorm bf16 [256, 262144]), the split-row
 softmax backward (bf16 [1024, 131072]), one GPU's share of an 8-way
-row-sharded cross-entropy step (fp32 [512, 50257], one-pass and split-row
-kernels) and the split-row residual-add +
+row-sharded cross-entropy step (fp32 [512, 50257], the row kernel and the
+split-row path) and the split-row residual-add +
 RMSNorm backward (bf16 [2048, 32768], hidden size beyond the one-pass
 backward); they are
 reported under "backward" and "variants" and are not part of `value`; so is the
@@ -92,19 +92,19 @@ def bwd_algo_bytes(name, R, C):
     if name in ("xent_shard_f32", "xent_shard_split_f32"):
         return 2 * R * C * 4 + 2 * R * 4                       # logits, grad; labels, loss
     if name in ("xent_split_f32", "xent_split_bf16"):
-        # one read of the logits and one write of the gradient (the split path
-        # reads the logits twice: 1.5x these bytes move); labels, loss
+        # one read of the logits and one write of the gradient (the split path's
+        # one-pass form moves these bytes, its two passes 1.5x); labels, loss
         es = 4 if name == "xent_split_f32" else 2
         return 2 * R * C * es + 2 * R * 4
     if name == "add_rmsnorm_bwd_split_bf16":
         return 4 * R * C * 2 + C * 2 + C * 4                   # h, dy, dres, dh; w; dw
     if name == "softmax_bwd_split_bf16":
-        return 3 * R * C * 2                                   # p, dy; dx (read twice by the path)
+        return 3 * R * C * 2                                   # p, dy; dx (two passes read p, dy twice)
     if name == "layernorm_split_f32":
-        # x, y; gamma, beta; mean, rstd (the split path reads x twice)
+        # x, y; gamma, beta; mean, rstd (two passes read x twice)
         return 2 * R * C * 4 + 2 * C * 4 + 2 * R * 4
     if name == "add_rmsnorm_split_bf16":
-        # x, r, y, r_out; w (the split path reads x and r twice)
+        # x, r, y, r_out; w (two passes read x and r twice)
         return 4 * R * C * 2 + C * 2
     if name in ("xent_ex_f32", "xent_ex_bf16"):
         # logits of the rows not ignored (every 9th row is), grad of all rows;

@@ -654,6 +654,28 @@ def test_one_pass_wait_bound_every_kernel():
                     f"{name}: the call after differs"
 
 
+def test_one_pass_repeated_calls_bitwise():
+    """Each one-pass kernel called 20 times on the same inputs (a different
+    interleaving of its workgroups' posts and waits each time): every call
+    bitwise the same, and no row given up."""
+    with fr.split_cooperative(2):
+        for name, run in _wait_bound_cases():
+            print(f"repeated calls: {name}", flush=True)
+            first = run()
+            flat0 = [np.ascontiguousarray(a).view(np.uint8) for a in first[0] + first[1]]
+            for a in first[0]:
+                a = np.asarray(a)
+                if a.dtype == np.int32:
+                    assert not (a == -1).any(), f"{name}: a row given up"
+                else:
+                    assert not np.isnan(_as_f64(a)).any(), f"{name}: a row given up"
+            for k in range(19):
+                got = run()
+                flat = [np.ascontiguousarray(a).view(np.uint8) for a in got[0] + got[1]]
+                assert all(np.array_equal(x, y) for x, y in zip(flat0, flat)), \
+                    f"{name}: call {k + 2} differs from the first"
+
+
 # ------------------------------------------------------------ row batches
 
 def _bits(*arrays):

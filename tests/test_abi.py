@@ -543,6 +543,45 @@ def test_split_cooperative_settings():
         L.fr_debug_set_coop_spin_limit(-1)
 
 
+def test_split_form_selection():
+    # host-side selection only (no GPU: 256 compute units assumed): the
+    # one-pass shape (512 lanes x 64 elements; the fp32 LayerNorm 512 x 32)
+    # when the rows give at least 4 work items per compute unit, else the
+    # two passes' first shape; mode 0 never, mode 2 always (where the row
+    # has at most 64 one-pass segments)
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("compute-unit count of the host without a GPU")
+    sel = fr.fr_debug_select_variant_for
+    X, SM, LN, RN, SB = (fr.OP_XENT_SPLIT, fr.OP_SOFTMAX_SPLIT, fr.OP_LAYERNORM_SPLIT,
+                         fr.OP_RMSNORM_SPLIT, fr.OP_SOFTMAX_BWD_SPLIT)
+    cases = [  # (op, rows, cols, dtype, mode 1 shape)
+        (X, 2048, 131072, fr.F32, (512, 16, 4)),    # 2048 x 4 work items
+        (X, 96, 131072, fr.F32, (256, 8, 4)),       # 384 < 1024: two passes
+        (X, 1024, 262144, fr.BF16, (512, 8, 8)),
+        (X, 64, 262144, fr.BF16, (256, 8, 8)),
+        (X, 512, 50257, fr.F32, (512, 16, 4)),      # 512 x 2 = 1024
+        (X, 511, 50257, fr.F32, (256, 8, 4)),
+        (SM, 2048, 131072, fr.F32, (512, 16, 4)),
+        (LN, 512, 131072, fr.F32, (512, 8, 4)),     # fp32 LayerNorm: 512 x 32
+        (LN, 512, 131072, fr.BF16, (256, 4, 8)),    # bf16 LayerNorm: two passes
+        (RN, 256, 262144, fr.BF16, (512, 8, 8)),
+        (SB, 1024, 131072, fr.BF16, (512, 8, 8)),
+        (X, 4, 1 << 22, fr.F32, (256, 8, 4)),       # 128 one-pass segments > 64
+    ]
+    for op, R, C, dt, want in cases:
+        assert sel(op, R, C, dt) == want, (op, R, C, dt)
+    first = {fr.F32: (256, 8, 4), fr.BF16: (256, 8, 8)}
+    with fr.split_cooperative(0):
+        for op, R, C, dt, _ in cases:
+            want = (256, 4, 8) if (op in (LN, RN, SB) and dt == fr.BF16) else first[dt]
+            assert sel(op, R, C, dt) == want, (op, R, C, dt, "mode 0")
+    with fr.split_cooperative(2):
+        assert sel(X, 1, 131072, fr.F32) == (512, 16, 4)
+        assert sel(LN, 1, 131072, fr.BF16) == (256, 4, 8)   # no one-pass shape: the first
+        assert sel(X, 4, 1 << 22, fr.F32) == (256, 8, 4)
+
+
 def test_row_aware_selection():
     # the cross-entropy takes the 256-lane shape (two rows per compute unit)
     # when the rows fill the compute units once but not twice; without a GPU

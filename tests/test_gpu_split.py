@@ -676,6 +676,46 @@ def test_one_pass_repeated_calls_bitwise():
                     f"{name}: call {k + 2} differs from the first"
 
 
+def test_bench_split_shapes_sampled():
+    """The benchmark's split workloads at their full sizes, in the form the
+    default selection takes there (one pass for each), checked against the
+    oracle on sampled rows (the first two, two in the middle, the last two):
+    cross-entropy bf16 [1024, 262144] (every 7th row ignored, smoothing 0.1,
+    argmax), LayerNorm fp32 [512, 131072], residual-add + RMSNorm bf16
+    [256, 262144], softmax backward bf16 [1024, 131072]."""
+    def pick(R):
+        return np.array(sorted({0, 1, R // 2 - 1, R // 2, R - 2, R - 1}))
+    for op, R, C, dt in ((fr.OP_XENT_SPLIT, 1024, 262144, fr.BF16),
+                         (fr.OP_LAYERNORM_SPLIT, 512, 131072, fr.F32),
+                         (fr.OP_RMSNORM_SPLIT, 256, 262144, fr.BF16),
+                         (fr.OP_SOFTMAX_BWD_SPLIT, 1024, 131072, fr.BF16)):
+        t, v, e = fr.fr_debug_select_variant_for(op, R, C, dt)
+        assert (t, v * e) == (512, 32 if op == fr.OP_LAYERNORM_SPLIT else 64), (op, t, v, e)
+    rows = pick(1024)
+    xl, lab = xent_inputs(1024, 262144, fr.BF16, seed=61, ignore_every=7)
+    opts = dict(ignore_index=-100, label_smoothing=0.1)
+    loss, grad, am, _ = run_xent_split(xl, lab, fr.BF16, opts)
+    expect_xent(xl[rows], lab[rows], fr.BF16, opts, (loss[rows], grad[rows], am[rows], 0.0),
+                "split xent bf16 1024x262144 (sampled)")
+    del xl, grad
+    rows = pick(512)
+    wl = workloads.make("layernorm_f32", rows=512, cols=131072, seed=62)
+    y, m, r = run_ln_split(wl["x"], wl["gamma"], wl["beta"], wl.eps)
+    expect_layernorm(wl["x"][rows], wl["gamma"], wl["beta"], wl.eps, (y[rows], m[rows], r[rows]),
+                     "split layernorm fp32 512x131072 (sampled)")
+    del wl, y
+    rows = pick(256)
+    wr = workloads.make("add_rmsnorm_bf16", rows=256, cols=262144, seed=63)
+    y, ro = run_rms_split(wr["x"], wr["residual"], wr["weight"], wr.eps)
+    expect_rmsnorm(wr["x"][rows], wr["residual"][rows], wr["weight"], wr.eps, (y[rows], ro[rows]),
+                   "split add_rmsnorm bf16 256x262144 (sampled)")
+    del wr, y, ro
+    rows = pick(1024)
+    p, dy = softmax_bwd_inputs(1024, 131072, fr.BF16, seed=64)
+    dx = run_softmax_bwd_split(p, dy)
+    expect_softmax_bwd(p[rows], dy[rows], fr.BF16, dx[rows], "split softmax_bwd bf16 1024x131072 (sampled)")
+
+
 # ------------------------------------------------------------ row batches
 
 def _bits(*arrays):

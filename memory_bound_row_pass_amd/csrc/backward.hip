@@ -824,6 +824,15 @@ void norm_bwd_split_coop_kernel(const Ts* xh, const Ts* dy, const Ts* dres, cons
     float a[NV][EPV], d[NV][EPV], dr[DRES ? NV : 1][EPV];
     if constexpr (DRES) sl.load3(xh + off, dy + off, dres + off, a, d, dr);
     else sl.load2(xh + off, dy + off, a, d);
+    // slot i's operands (0 past the row end)
+    auto operands = [&](int i, float (&va)[EPV], float (&vd)[EPV], float (&vr)[EPV]) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        va[k] = a[i][k];
+        vd[k] = d[i][k];
+        if constexpr (DRES) vr[k] = dr[i][k];
+      }
+    };
     float mu = 0.f, rs = 1.f;
     if constexpr (LN) {
       mu = mean[row];
@@ -833,17 +842,18 @@ void norm_bwd_split_coop_kernel(const Ts* xh, const Ts* dy, const Ts* dres, cons
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      float wt[EPV];
+      float wt[EPV], va[EPV], vd[EPV], vr[EPV];
       weight(w1, i, wt);
+      operands(i, va, vd, vr);
 #pragma unroll
       for (int k = 0; k < EPV; ++k) {
-        const float gk = d[i][k] * wt[k];
+        const float gk = vd[k] * wt[k];
         if constexpr (LN) {
-          const float nk = sl.ok(i) ? (a[i][k] - mu) * rs : 0.f;
+          const float nk = sl.ok(i) ? (va[k] - mu) * rs : 0.f;
           if (k & 1) { a1 += gk; b1 = __builtin_fmaf(gk, nk, b1); }
           else { a0 += gk; b0 = __builtin_fmaf(gk, nk, b0); }
         } else {
-          const float hk = a[i][k];
+          const float hk = va[k];
           if (k & 1) { a1 = __builtin_fmaf(hk, hk, a1); b1 = __builtin_fmaf(gk, hk, b1); }
           else { a0 = __builtin_fmaf(hk, hk, a0); b0 = __builtin_fmaf(gk, hk, b0); }
         }
@@ -860,37 +870,30 @@ void norm_bwd_split_coop_kernel(const Ts* xh, const Ts* dy, const Ts* dres, cons
     if (lane < nseg) st = Sum2State{team[lane][0], team[lane][2]};
     st = wave_reduce(st, Sum2Merge{});
 
-    if constexpr (LN) {
-      const float mg = st.a / (float)cols, mgn = st.b / (float)cols;
+    const float mg = st.a / (float)cols, mgn = st.b / (float)cols;  // LayerNorm
+    const float r = LN ? 0.f : 1.f / __builtin_sqrtf(st.a / (float)cols + eps);  // RMSNorm
+    const float c = r * r * (st.b / (float)cols);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        float ga[EPV];
-        weight(w1, i, ga);
+    for (int i = 0; i < NV; ++i) {
+      float wt[EPV], va[EPV], vd[EPV], vr[EPV], o[EPV];
+      weight(w1, i, wt);
+      operands(i, va, vd, vr);
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          const float nk = (a[i][k] - mu) * rs;
-          acc[i][k] = __builtin_fmaf(d[i][k], nk, acc[i][k]);
-          acc2[i][k] += d[i][k];
-          a[i][k] = rs * __builtin_fmaf(-nk, mgn, __builtin_fmaf(d[i][k], ga[k], -mg));
+      for (int k = 0; k < EPV; ++k) {
+        if constexpr (LN) {
+          const float nk = (va[k] - mu) * rs;
+          acc[i][k] = __builtin_fmaf(vd[k], nk, acc[i][k]);
+          acc2[i][k] += vd[k];
+          o[k] = rs * __builtin_fmaf(-nk, mgn, __builtin_fmaf(vd[k], wt[k], -mg));
+        } else {
+          acc[i][k] = __builtin_fmaf(vd[k] * va[k], r, acc[i][k]);
+          const float t = r * __builtin_fmaf(-va[k], c, wt[k] * vd[k]);
+          if constexpr (DRES) o[k] = t + vr[k];
+          else o[k] = t;
         }
       }
-    } else {
-      const float r = 1.f / __builtin_sqrtf(st.a / (float)cols + eps);
-      const float c = r * r * (st.b / (float)cols);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        float wt[EPV];
-        weight(w1, i, wt);
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          acc[i][k] = __builtin_fmaf(d[i][k] * a[i][k], r, acc[i][k]);
-          const float t = r * __builtin_fmaf(-a[i][k], c, wt[k] * d[i][k]);
-          if constexpr (DRES) a[i][k] = t + dr[i][k];
-          else a[i][k] = t;
-        }
-      }
+      if (sl.ok(i)) Vec<Ts, EPV>::store(out + off + sl.off(i), o);
     }
-    sl.store(out + off, a);
   }
   float* w0 = ws + (size_t)rg * cols + c0;
 #pragma unroll

@@ -39,7 +39,7 @@
  *            parameter gradients); 1 <= cols <= FR_MAX_COLS (less for the
  *            backward calls).
  * Threads    Entry points are re-entrant. fr_debug_force_variant,
- *            fr_debug_set_split_batch_bytes, fr_debug_set_split_cooperative
+ *            fr_debug_set_split_batch_bytes, fr_debug_set_split_one_pass
  *            and fr_debug_set_coop_spin_limit are the only global settings.
  *
  * Arithmetic is fp32 throughout (bf16 inputs are widened exactly, bf16
@@ -213,7 +213,7 @@ FR_API int64_t fr_split_workspace_bytes(int64_t rows, int64_t cols);
  *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.1:
  *    the merge of partial (max, sum) states.)
  * One-pass form, when the rows give at least 4 segments of 32768 columns per
- * compute unit and a row has at most 64 of them (fr_debug_set_split_cooperative):
+ * compute unit and a row has at most 64 of them (fr_debug_set_split_one_pass):
  * a kernel zeroing the workspace's counter and slots, then one launch in
  * which a row's workgroups hold their segments in registers, exchange their
  * states through the workspace (each waits for the others of its row; rows
@@ -254,7 +254,7 @@ FR_API fr_status_t fr_softmax_xent_split(const void* logits, const int32_t* labe
  * Welford moments and writes the segment's y (and, from the row's first
  * segment, mean and rstd). Reads x twice, writes y once. fp32 also in the
  * one-pass form of fr_softmax_fwd_split (segments of 16384 columns); bf16
- * only with fr_debug_set_split_cooperative(2) (no faster there: the apply
+ * only with fr_debug_set_split_one_pass(2) (no faster there: the apply
  * step reads gamma and beta for every row segment).
  *   ("Engineering a CUDA Machine Learning Framework from Scratch", §3.2
  *    Welford Single-Pass Normalization: partial moments merged pairwise.)
@@ -418,7 +418,7 @@ FR_API int64_t fr_norm_bwd_split_workspace_bytes(fr_op_t op, int64_t rows, int64
  * dweight partials, one partial row per row group; a third kernel adds the
  * G partial rows in order. Reads h, dy (and dres) twice. One-pass form (fp32,
  * rows giving at least 4 workgroups per compute unit;
- * fr_debug_set_split_cooperative): a kernel zeroing the workspace's slots,
+ * fr_debug_set_split_one_pass): a kernel zeroing the workspace's slots,
  * then one launch in which the row group's segment workgroups walk their
  * rows together, exchange each row's sums through the workspace and write
  * dh from the registers (h, dy and dres read once), then the column sums.
@@ -553,7 +553,7 @@ FR_API int64_t fr_debug_set_split_batch_bytes(int64_t bytes);
  * segment states in segment order, the one-pass form by a fixed DPP tree).
  * Returns the previous setting. Process-wide setting meant for tests and
  * tuning; not synchronised with concurrent calls. */
-FR_API int fr_debug_set_split_cooperative(int mode);
+FR_API int fr_debug_set_split_one_pass(int mode);
 
 /* Bound on the polls a workgroup of the one-pass split form makes for the
  * partial states of its row's other segments before it gives up and writes

@@ -22,8 +22,8 @@ __all__ = [
     "fr_stream_probe_rows", "PROBE_READ", "PROBE_WRITE", "PROBE_COPY", "PROBE_NT_LOADS",
     "PROBE_NT_STORES", "fr_debug_force_variant", "fr_debug_select_variant",
     "fr_debug_select_variant_for",
-    "fr_debug_set_split_batch_bytes", "split_batch_bytes", "fr_debug_set_split_cooperative",
-    "split_cooperative", "fr_debug_set_coop_spin_limit", "coop_spin_limit",
+    "fr_debug_set_split_batch_bytes", "split_batch_bytes", "fr_debug_set_split_one_pass",
+    "split_one_pass", "fr_debug_set_coop_spin_limit", "coop_spin_limit",
     "fr_softmax_bwd", "fr_add_rmsnorm_bwd", "fr_layernorm_bwd", "fr_norm_bwd_workspace_bytes",
     "fr_add_rmsnorm_bwd_noalloc", "FR_NOALLOC_SCRATCH_BYTES",
     "fr_softmax_xent_ex", "XentOptions", "REDUCE_NONE", "REDUCE_SUM", "REDUCE_MEAN",
@@ -132,8 +132,8 @@ def _load() -> ctypes.CDLL:
     L.fr_version.restype = ctypes.c_char_p
     L.fr_debug_set_split_batch_bytes.argtypes = [I64]
     L.fr_debug_set_split_batch_bytes.restype = ctypes.c_int64
-    L.fr_debug_set_split_cooperative.argtypes = [ctypes.c_int]
-    L.fr_debug_set_split_cooperative.restype = ctypes.c_int
+    L.fr_debug_set_split_one_pass.argtypes = [ctypes.c_int]
+    L.fr_debug_set_split_one_pass.restype = ctypes.c_int
     L.fr_debug_set_coop_spin_limit.argtypes = [ctypes.c_int]
     L.fr_debug_set_coop_spin_limit.restype = ctypes.c_int
     L.fr_debug_last_launch_error.argtypes = []
@@ -690,12 +690,12 @@ class split_batch_bytes:
         return False
 
 
-def fr_debug_set_split_cooperative(mode: int) -> int:
-    """C: fr_debug_set_split_cooperative; returns the previous setting."""
-    return int(lib.fr_debug_set_split_cooperative(int(mode)))
+def fr_debug_set_split_one_pass(mode: int) -> int:
+    """C: fr_debug_set_split_one_pass; returns the previous setting."""
+    return int(lib.fr_debug_set_split_one_pass(int(mode)))
 
 
-class split_cooperative:
+class split_one_pass:
     """Context manager: the one-pass form of the split softmax and
     cross-entropy never (0), where the rows are many enough (1, the default)
     or wherever it applies (2); restore the previous setting after."""
@@ -704,11 +704,11 @@ class split_cooperative:
         self.mode = mode
 
     def __enter__(self):
-        self.prev = fr_debug_set_split_cooperative(self.mode)
+        self.prev = fr_debug_set_split_one_pass(self.mode)
         return self
 
     def __exit__(self, *exc):
-        fr_debug_set_split_cooperative(self.prev)
+        fr_debug_set_split_one_pass(self.prev)
         return False
 
 

@@ -146,7 +146,7 @@ struct SplitChoice {
 template <typename V>
 SplitChoice<V> choose_split(VariantSpan<V> sp, int op, int epv, int64_t rows, int64_t cols,
                             int elems) {
-  const int mode = fr::split_cooperative();
+  const int mode = fr::split_one_pass();
   if (g_forced[op].threads.load(std::memory_order_relaxed)) return {select_split(sp, op, epv), mode != 0};
   if (mode != 0 && elems > 0) {
     const int64_t nseg = (cols + 512 * elems - 1) / (512 * elems);
@@ -178,14 +178,14 @@ int vec_epv(int esz) { return 16 / esz; }
 
 namespace {
 std::atomic<int64_t> g_split_batch_bytes{fr::kSplitBatchBytes};
-std::atomic<int> g_split_cooperative{1};
+std::atomic<int> g_split_one_pass{1};
 std::atomic<int> g_coop_spin_limit{fr::kCoopSpinLimit};
 }  // namespace
 
 namespace fr {
 void note_launch_error(hipError_t e) { t_last_launch_error = static_cast<int>(e); }
 int64_t split_batch_bytes() { return g_split_batch_bytes.load(std::memory_order_relaxed); }
-int split_cooperative() { return g_split_cooperative.load(std::memory_order_relaxed); }
+int split_one_pass() { return g_split_one_pass.load(std::memory_order_relaxed); }
 int coop_spin_limit() { return g_coop_spin_limit.load(std::memory_order_relaxed); }
 int device_cu_count() {
   static std::atomic<int> cache[64];  // 0: not yet queried
@@ -212,8 +212,8 @@ int64_t fr_debug_set_split_batch_bytes(int64_t bytes) {
   return prev;
 }
 
-int fr_debug_set_split_cooperative(int mode) {
-  return g_split_cooperative.exchange(mode < 0 || mode > 2 ? 1 : mode);
+int fr_debug_set_split_one_pass(int mode) {
+  return g_split_one_pass.exchange(mode < 0 || mode > 2 ? 1 : mode);
 }
 
 int fr_debug_set_coop_spin_limit(int polls) {
@@ -635,7 +635,7 @@ namespace {
 // [2048, 32768] RMSNorm with dres 156 against 149, without 129 against 130,
 // LayerNorm 142 against 140; few rows ([256, 32768] bf16) 52 against 46.
 bool norm_bwd_one_pass(int64_t rows, int64_t cols, fr_dtype_t dtype) {
-  const int mode = fr::split_cooperative();
+  const int mode = fr::split_one_pass();
   const int nseg = (int)((cols + fr::kBwdSplitSeg - 1) / fr::kBwdSplitSeg);
   if (mode == 0 || nseg > fr::kCoopMaxSegments) return false;
   return mode == 2 || (dtype == FR_F32 && (int64_t)fr::norm_bwd_split_groups(rows, nseg) * nseg >=

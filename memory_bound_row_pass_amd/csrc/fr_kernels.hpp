@@ -30,9 +30,9 @@ constexpr bool kPass1NT = false;
 // The one-pass form of the split-row softmax and cross-entropy: a row's
 // segment workgroups exchange their partial states through device-scope
 // atomics in the workspace and write their outputs from the registers, so
-// the input is read once (split_cooperative(): 0 never, 1 where it applies
+// the input is read once (split_one_pass(): 0 never, 1 where it applies
 // and the rows are many enough, the default; 2 wherever it applies).
-int split_cooperative();
+int split_one_pass();
 // Polls a workgroup makes for its row's other states before it gives up (its
 // outputs for the row are then NaN): a bound on every wait, so the kernel
 // always ends (fr_debug_set_coop_spin_limit).

@@ -516,20 +516,20 @@ def test_split_batch_setting():
         L.fr_debug_set_split_batch_bytes(-1)
 
 
-def test_split_cooperative_settings():
+def test_split_one_pass_settings():
     # host-side settings only: each returns the previous value
     L = fr.lib
-    assert L.fr_debug_set_split_cooperative(0) == 1          # 1 by default
+    assert L.fr_debug_set_split_one_pass(0) == 1          # 1 by default
     try:
-        assert L.fr_debug_set_split_cooperative(2) == 0
-        assert L.fr_debug_set_split_cooperative(7) == 2      # out of range: 1
-        assert L.fr_debug_set_split_cooperative(-1) == 1
-        assert L.fr_debug_set_split_cooperative(1) == 1
-        with fr.split_cooperative(0):
-            assert L.fr_debug_set_split_cooperative(0) == 0
-        assert L.fr_debug_set_split_cooperative(1) == 1
+        assert L.fr_debug_set_split_one_pass(2) == 0
+        assert L.fr_debug_set_split_one_pass(7) == 2      # out of range: 1
+        assert L.fr_debug_set_split_one_pass(-1) == 1
+        assert L.fr_debug_set_split_one_pass(1) == 1
+        with fr.split_one_pass(0):
+            assert L.fr_debug_set_split_one_pass(0) == 0
+        assert L.fr_debug_set_split_one_pass(1) == 1
     finally:
-        L.fr_debug_set_split_cooperative(1)
+        L.fr_debug_set_split_one_pass(1)
     default = 1 << 18
     assert L.fr_debug_set_coop_spin_limit(5) == default
     try:
@@ -572,11 +572,11 @@ def test_split_form_selection():
     for op, R, C, dt, want in cases:
         assert sel(op, R, C, dt) == want, (op, R, C, dt)
     first = {fr.F32: (256, 8, 4), fr.BF16: (256, 8, 8)}
-    with fr.split_cooperative(0):
+    with fr.split_one_pass(0):
         for op, R, C, dt, _ in cases:
             want = (256, 4, 8) if (op in (LN, RN, SB) and dt == fr.BF16) else first[dt]
             assert sel(op, R, C, dt) == want, (op, R, C, dt, "mode 0")
-    with fr.split_cooperative(2):
+    with fr.split_one_pass(2):
         assert sel(X, 1, 131072, fr.F32) == (512, 16, 4)
         assert sel(LN, 1, 131072, fr.BF16) == (256, 4, 8)   # no one-pass shape: the first
         assert sel(X, 4, 1 << 22, fr.F32) == (256, 8, 4)

@@ -40,7 +40,7 @@ def workspace(R, C):
 def form(request):
     """Runs the test with the one-pass form wherever it applies (any row
     count), then with the two passes only."""
-    with fr.split_cooperative(request.param):
+    with fr.split_one_pass(request.param):
         yield request.param
 
 
@@ -223,7 +223,7 @@ def test_one_pass_form_runs():
     x = softmax_input(fr.F32, R, C, seed=41)
     seg_max = lambda r, j, n: x[r, j * n:(j + 1) * n].max().view(np.uint32)
     for mode in (2, 0):
-        with fr.split_cooperative(mode):
+        with fr.split_one_pass(mode):
             ws = workspace(R, C)
             got = _softmax_split_ws(x, ws)
         expect_softmax(x, fr.F32, got, f"split softmax {R}x{C} mode {mode}")
@@ -248,7 +248,7 @@ def test_one_pass_wait_bound():
     and abort word are cleared again)."""
     R, C = 96, 131072
     x = softmax_input(fr.F32, R, C, seed=42)
-    with fr.split_cooperative(2):
+    with fr.split_one_pass(2):
         with fr.coop_spin_limit(0):
             got = _softmax_split_ws(x, workspace(R, C))
         nan_rows = np.isnan(got).any(axis=1)
@@ -622,7 +622,7 @@ def test_one_pass_wait_bound_every_kernel():
     outputs (parameter gradients)
     are bitwise the same when no row gave up. The next call, with the
     default bound, is bitwise the same throughout."""
-    with fr.split_cooperative(2):
+    with fr.split_one_pass(2):
         for name, run in _wait_bound_cases():
             print(f"bounded waits: {name}", flush=True)
             ref_rows, ref_cols = run()
@@ -658,7 +658,7 @@ def test_one_pass_repeated_calls_bitwise():
     """Each one-pass kernel called 20 times on the same inputs (a different
     interleaving of its workgroups' posts and waits each time): every call
     bitwise the same, and no row given up."""
-    with fr.split_cooperative(2):
+    with fr.split_one_pass(2):
         for name, run in _wait_bound_cases():
             print(f"repeated calls: {name}", flush=True)
             first = run()
@@ -758,9 +758,9 @@ def test_split_row_batches(batch_rows):
                   lambda got: expect_softmax_bwd(p, dy, fr.BF16, got[0], "split softmax_bwd batches")))
     for name, row_bytes, run, expect in cases:
         print(f"row batches of {batch_rows}: {name}", flush=True)
-        with fr.split_cooperative(0), fr.split_batch_bytes(batch_rows * row_bytes):
+        with fr.split_one_pass(0), fr.split_batch_bytes(batch_rows * row_bytes):
             got = run()
-        with fr.split_cooperative(0), fr.split_batch_bytes(0):
+        with fr.split_one_pass(0), fr.split_batch_bytes(0):
             whole = run()
         expect(got)
         assert _bits(*got) == _bits(*whole), f"{name}: batched and unbatched results differ"
